@@ -1,0 +1,144 @@
+"""fp64 CPU oracle for the selective scan -- TEST INFRASTRUCTURE ONLY.
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may use
+this package.  The product path (the HIP library and its binding) never
+imports it, and it imports nothing from the product: the arithmetic lives in
+ssm_oracle.c (plain C, double precision, one sequential loop per channel);
+this module only marshals numpy arrays into it.
+
+  Oracle(path)             a loaded oracle library (the default is built from
+                           ssm_oracle.c next to this file)
+  .scan_f64(...)           full prefill scan, every (batch, channel)
+  .scan_channels_f64(...)  the same scan restricted to chosen (b, d) channels
+                           (channels are independent, so a subset is exact)
+  .state_update_f64(...)   one-token update of a float64 state, in place
+  .softplus_f64, .silu_f64 the scalar helpers the C oracle uses
+Module-level functions of the same names use the default oracle.
+"""
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(HERE, "ssm_oracle.c")
+LIB_PATH = os.path.join(HERE, "libssm_oracle.so")
+CFLAGS = ["-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-Wall", "-Wextra"]
+
+
+def compile_oracle(source=SOURCE, out=LIB_PATH):
+    """gcc -O2 -fopenmp: compile an oracle C source into a shared library."""
+    subprocess.run(["gcc"] + CFLAGS + ["-o", out, source, "-lm"], check=True)
+    return out
+
+
+def build():
+    """Compile ssm_oracle.c into libssm_oracle.so (always recompiles)."""
+    return compile_oracle()
+
+
+def _f64(a):
+    return None if a is None else np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+class Oracle:
+    def __init__(self, path=LIB_PATH):
+        L = ctypes.CDLL(path)
+        P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        L.oracle_scan_f64.restype = I
+        L.oracle_scan_f64.argtypes = [I64, I64, I64, I64] + [P] * 8 + [I, P, P, P]
+        L.oracle_state_update_f64.restype = I
+        L.oracle_state_update_f64.argtypes = [I64, I64, I64] + [P] * 9 + [I, P]
+        L.oracle_softplus.restype = ctypes.c_double
+        L.oracle_softplus.argtypes = [ctypes.c_double]
+        L.oracle_silu.restype = ctypes.c_double
+        L.oracle_silu.argtypes = [ctypes.c_double]
+        self.lib = L
+        self.path = path
+
+    def softplus_f64(self, x):
+        return self.lib.oracle_softplus(float(x))
+
+    def silu_f64(self, x):
+        return self.lib.oracle_silu(float(x))
+
+    def scan_f64(self, u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=False, h0=None):
+        """Returns (y, last_state) in float64.  Shapes as in ssm_oracle.c."""
+        u, delta, A, B, C, D, z, delta_bias, h0 = map(_f64, (u, delta, A, B, C, D, z, delta_bias, h0))
+        batch, dim, seqlen = u.shape
+        dstate = A.shape[1]
+        y = np.empty((batch, dim, seqlen), np.float64)
+        last = np.empty((batch, dim, dstate), np.float64)
+        rc = self.lib.oracle_scan_f64(batch, dim, dstate, seqlen, _p(u), _p(delta), _p(A), _p(B), _p(C), _p(D),
+                                      _p(z), _p(delta_bias), 1 if softplus else 0, _p(h0), _p(y), _p(last))
+        if rc != 0:
+            raise ValueError("oracle_scan_f64 rejected the arguments")
+        return y, last
+
+    def scan_channels_f64(self, channels, u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=False,
+                          h0=None):
+        """Scan only the listed (b, d) channels; returns (y[k, seqlen], last_state[k, dstate]).
+
+        Pure marshalling: each channel becomes a batch-1, dim-1 problem with its
+        own rows of u/delta/z, its batch row of B/C and its row of A/D/bias.
+        """
+        ys, hs = [], []
+        for (b, d) in channels:
+            def sl(t):
+                return None if t is None else t[b:b + 1, d:d + 1]
+            y, h = self.scan_f64(sl(u), sl(delta), A[d:d + 1], B[b:b + 1], C[b:b + 1],
+                                 None if D is None else D[d:d + 1], sl(z),
+                                 None if delta_bias is None else delta_bias[d:d + 1], softplus, sl(h0))
+            ys.append(y[0, 0])
+            hs.append(h[0, 0])
+        return np.stack(ys), np.stack(hs)
+
+    def state_update_f64(self, state, u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=False):
+        """Advance `state` (float64 (batch, dim, dstate), modified in place) by one token; returns y (batch, dim)."""
+        if state.dtype != np.float64 or not state.flags["C_CONTIGUOUS"]:
+            raise TypeError("state must be a C-contiguous float64 array (it is updated in place)")
+        u, delta, A, B, C, D, z, delta_bias = map(_f64, (u, delta, A, B, C, D, z, delta_bias))
+        batch, dim, dstate = state.shape
+        y = np.empty((batch, dim), np.float64)
+        rc = self.lib.oracle_state_update_f64(batch, dim, dstate, _p(state), _p(u), _p(delta), _p(A), _p(B),
+                                              _p(C), _p(D), _p(z), _p(delta_bias), 1 if softplus else 0, _p(y))
+        if rc != 0:
+            raise ValueError("oracle_state_update_f64 rejected the arguments")
+        return y
+
+
+_default = None
+
+
+def default():
+    global _default
+    if _default is None:
+        if not os.path.exists(LIB_PATH):
+            build()
+        _default = Oracle(LIB_PATH)
+    return _default
+
+
+def scan_f64(*args, **kw):
+    return default().scan_f64(*args, **kw)
+
+
+def scan_channels_f64(*args, **kw):
+    return default().scan_channels_f64(*args, **kw)
+
+
+def state_update_f64(*args, **kw):
+    return default().state_update_f64(*args, **kw)
+
+
+def softplus_f64(x):
+    return default().softplus_f64(x)
+
+
+def silu_f64(x):
+    return default().silu_f64(x)

@@ -1,0 +1,135 @@
+/*
+ * ssm_oracle.c -- plain, slow, obviously-correct fp64 CPU oracle for the
+ * selective state-space scan (S6) and its one-token state update.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link or call
+ * this file: only the tests, the smoke check and the benchmark's CPU-baseline
+ * leg use it.  It shares no code, header, table or constant with the HIP
+ * library, and includes nothing from it.
+ *
+ * What it computes, per (batch b, channel d), independently, in double:
+ *
+ *   h[n] <- h0[b,d,n] (or 0)
+ *   for l = 0 .. L-1:
+ *     x      <- delta[b,d,l] + bias[d]                (bias 0 when absent)
+ *     Delta  <- softplus(x) if the flag is set, else x
+ *     for n:  Abar <- exp(Delta * A[d,n])             (zero-order hold for A)
+ *             h[n] <- Abar * h[n] + Delta * B[b,n,l] * u[b,d,l]
+ *     v      <- sum_{n ascending} C[b,n,l] * h[n] + D[d] * u[b,d,l]   (D 0 when absent)
+ *     if z:   v <- v * z / (1 + exp(-z))              (silu gate)
+ *     y[b,d,l] <- v
+ *   last_state[b,d,:] <- h
+ *
+ * Sources (the pages are web articles about the Mamba selective SSM):
+ *  - state and observation equations h <- A h + B x, y = C h: the Korean
+ *    Mamba summary (dhy1.tistory.com), section "SSM의 수학적 정의";
+ *  - the scan: each state is the previous state times A-bar plus the current
+ *    input times B-bar, computed by a for loop: the Chinese explainer
+ *    (weblog-19d), section "硬件感知的设计：并行扫描";
+ *  - Delta, B and C are input dependent, A is not, and A acts per state
+ *    dimension ("represented by N numbers"): same explainer, sections on the
+ *    S4 matrix dimensions and the gating roles of Delta/B/C; the Hebrew
+ *    overview (unite.ai), section "SSM + בחירה (S6)";
+ *  - discretization by zero-order hold: the Chinese explainer, stage (1a/1b),
+ *    whose formulas did not survive extraction.
+ * Where the pages are silent or garbled this file reads them as follows:
+ *  - B is discretized as Bbar*u = Delta*B*u (the formula image is lost; A uses
+ *    the zero-order hold exp(Delta*A));
+ *  - no output lag: y_t is read from the state h_t that already includes u_t
+ *    (the Korean summary's h(t+1)/y(t) form is the textbook lagged form, while
+ *    the explainer's scan adds the *current* input);
+ *  - a D skip D[d]*u is added before the gate, the gate is silu(z);
+ *  - Delta = softplus(delta + bias) when the flag is set, else delta + bias;
+ *  - the initial state is h0 when given, else zero.
+ *
+ * Layouts (row-major, last index fastest):
+ *   u, delta, z, y : [batch][dim][seqlen]
+ *   B, C           : [batch][dstate][seqlen]
+ *   A              : [dim][dstate]
+ *   D, bias        : [dim]
+ *   h0, last_state : [batch][dim][dstate]
+ * Optional inputs (D, z, bias, h0) may be NULL; last_state may be NULL.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#define ORACLE_ABI_VERSION 1
+
+int oracle_abi_version(void) { return ORACLE_ABI_VERSION; }
+
+/* softplus(x) = log(1 + e^x), written in the overflow-free form
+ * max(x, 0) + log1p(e^{-|x|}). */
+double oracle_softplus(double x) {
+  double ax = fabs(x);
+  return (x > 0.0 ? x : 0.0) + log1p(exp(-ax));
+}
+
+/* silu(z) = z * sigmoid(z) = z / (1 + e^{-z}). */
+double oracle_silu(double z) { return z / (1.0 + exp(-z)); }
+
+/* One channel (b, d): walk the sequence once.  h has dstate entries. */
+static void scan_channel(int64_t dstate, int64_t seqlen, const double* u_row, const double* dt_row,
+                         const double* A_row, const double* B_b, const double* C_b, double Dd,
+                         const double* z_row, double bias, int softplus_flag, double* h, double* y_row) {
+  for (int64_t l = 0; l < seqlen; ++l) {
+    double x = dt_row[l] + bias;
+    double delta = softplus_flag ? oracle_softplus(x) : x;
+    double ul = u_row[l];
+    double v = 0.0;
+    for (int64_t n = 0; n < dstate; ++n) {
+      double abar = exp(delta * A_row[n]);
+      double bbar_u = delta * B_b[n * seqlen + l] * ul;
+      h[n] = abar * h[n] + bbar_u;
+      v += C_b[n * seqlen + l] * h[n];
+    }
+    v += Dd * ul;
+    if (z_row) v *= oracle_silu(z_row[l]);
+    y_row[l] = v;
+  }
+}
+
+/* Full prefill scan over every (b, d).  Parallel only across independent
+ * channels; each channel is sequential in l.  Returns 0, or -1 on bad sizes
+ * (dstate above 256 included) or a missing required pointer. */
+int oracle_scan_f64(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, const double* u,
+                    const double* delta, const double* A, const double* B, const double* C,
+                    const double* D, const double* z, const double* delta_bias, int softplus_flag,
+                    const double* h0, double* y, double* last_state) {
+  if (batch < 1 || dim < 1 || dstate < 1 || dstate > 256 || seqlen < 1) return -1;
+  if (!u || !delta || !A || !B || !C || !y) return -1;
+  int64_t nch = batch * dim;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t ch = 0; ch < nch; ++ch) {
+    int64_t b = ch / dim, d = ch % dim;
+    double h[256];
+    for (int64_t n = 0; n < dstate; ++n) h[n] = h0 ? h0[ch * dstate + n] : 0.0;
+    const double* zr = z ? z + ch * seqlen : NULL;
+    scan_channel(dstate, seqlen, u + ch * seqlen, delta + ch * seqlen, A + d * dstate,
+                 B + b * dstate * seqlen, C + b * dstate * seqlen, D ? D[d] : 0.0, zr,
+                 delta_bias ? delta_bias[d] : 0.0, softplus_flag, h, y + ch * seqlen);
+    if (last_state)
+      for (int64_t n = 0; n < dstate; ++n) last_state[ch * dstate + n] = h[n];
+  }
+  return 0;
+}
+
+/* One-token recurrent update, in place on state[batch][dim][dstate].
+ * u, delta, z, y: [batch][dim]; B, C: [batch][dstate]. */
+int oracle_state_update_f64(int64_t batch, int64_t dim, int64_t dstate, double* state, const double* u,
+                            const double* delta, const double* A, const double* B, const double* C,
+                            const double* D, const double* z, const double* delta_bias,
+                            int softplus_flag, double* y) {
+  if (batch < 1 || dim < 1 || dstate < 1 || dstate > 256) return -1;
+  if (!state || !u || !delta || !A || !B || !C || !y) return -1;
+  int64_t nch = batch * dim;
+#pragma omp parallel for schedule(static)
+  for (int64_t ch = 0; ch < nch; ++ch) {
+    int64_t b = ch / dim, d = ch % dim;
+    /* A one-token sequence: B[b,:] and C[b,:] viewed as [dstate][1]. */
+    scan_channel(dstate, 1, u + ch, delta + ch, A + d * dstate, B + b * dstate, C + b * dstate,
+                 D ? D[d] : 0.0, z ? z + ch : NULL, delta_bias ? delta_bias[d] : 0.0, softplus_flag,
+                 state + ch * dstate, y + ch);
+  }
+  return 0;
+}

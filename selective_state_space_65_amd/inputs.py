@@ -1,0 +1,178 @@
+"""Seeded synthetic inputs for the selective scan (shared by tests and bench).
+
+This module holds only the input recipe: random draws, the value
+distributions of the workloads, and bf16 storage rounding.  It contains none
+of the scan's arithmetic, so both the HIP path and the fp64 oracle can take
+their inputs from it without sharing any of the method.
+
+Recipe (every workload):
+  A[d, n]     = -(n + 1)                         (S4D-real initialisation)
+  dt[d]       = exp(U(ln 1e-3, ln 0.1))          one draw per channel
+  delta_bias  = ln(expm1(dt))                    so softplus(delta_bias) = dt
+  delta       = 0.5 * N(0, 1)                    raw step size, before bias / softplus
+  u, z, B, C  ~ N(0, 1)
+  D[d]        = 1
+Draw order from numpy.random.default_rng(seed) (PCG64): dt, u, delta, z, B, C
+(then h0 when requested).  bf16 workloads draw in fp32 and round to nearest
+even; the stored float32 arrays then hold exactly the bf16 values, so the
+oracle sees exactly what the GPU reads.
+"""
+from dataclasses import dataclass, field
+
+import numpy as np
+
+# name -> (batch, dim, dstate, seqlen, io dtype)
+SCAN_CONFIGS = {
+    0: dict(name="tiny fp32 scan", batch=1, dim=16, dstate=4, seqlen=64, io="f32"),
+    1: dict(name="Mamba-130M-layer scan fp32", batch=8, dim=1536, dstate=16, seqlen=2048, io="f32"),
+    2: dict(name="Mamba-1.4B-layer scan bf16", batch=4, dim=4096, dstate=16, seqlen=4096, io="bf16"),
+    3: dict(name="long-sequence scan fp32", batch=1, dim=2560, dstate=16, seqlen=131072, io="f32"),
+}
+DECODE_CONFIG = dict(name="recurrent decode bf16 io, fp32 state", batch=256, dim=5120, dstate=16, steps=1024,
+                     io="bf16")
+SEED_BASE = 65000
+
+
+def round_bf16(x):
+    """Round float32 values to the nearest bfloat16 (ties to even); returns float32."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    b = x.view(np.uint32)
+    bias = ((b >> np.uint32(16)) & np.uint32(1)) + np.uint32(0x7FFF)
+    r = ((b + bias) & np.uint32(0xFFFF0000)).astype(np.uint32)
+    nan = np.isnan(x)
+    if nan.any():
+        r[nan] = np.uint32(0x7FC00000)
+    return r.view(np.float32)
+
+
+def _normal(rng, shape, scale=1.0):
+    v = rng.standard_normal(size=shape, dtype=np.float32)
+    if scale != 1.0:
+        v *= np.float32(scale)
+    return v
+
+
+def _dt_bias(rng, dim):
+    dt = np.exp(rng.uniform(np.log(1e-3), np.log(0.1), size=dim))  # float64
+    return np.log(np.expm1(dt)).astype(np.float32)
+
+
+@dataclass
+class ScanInputs:
+    u: np.ndarray
+    delta: np.ndarray
+    A: np.ndarray
+    B: np.ndarray
+    C: np.ndarray
+    D: np.ndarray = None
+    z: np.ndarray = None
+    delta_bias: np.ndarray = None
+    h0: np.ndarray = None
+    io: str = "f32"
+    softplus: bool = True
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def shape(self):
+        b, d, l = self.u.shape
+        return b, d, self.A.shape[1], l
+
+
+def make_scan_inputs(batch, dim, dstate, seqlen, io="f32", seed=SEED_BASE, z=True, D=True, bias=True, softplus=True,
+                     h0=False, h0_scale=1.0):
+    """Seeded inputs with the workloads' distributions; optional pieces switch off."""
+    rng = np.random.default_rng(seed)
+    A = np.broadcast_to(-(np.arange(dstate, dtype=np.float32) + 1.0), (dim, dstate)).copy()
+    db = _dt_bias(rng, dim)
+    u = _normal(rng, (batch, dim, seqlen))
+    dlt = _normal(rng, (batch, dim, seqlen), 0.5)
+    zz = _normal(rng, (batch, dim, seqlen))
+    B = _normal(rng, (batch, dstate, seqlen))
+    C = _normal(rng, (batch, dstate, seqlen))
+    hh = _normal(rng, (batch, dim, dstate), h0_scale) if h0 else None
+    if io == "bf16":
+        u, dlt, zz, B, C = (round_bf16(t) for t in (u, dlt, zz, B, C))
+    elif io != "f32":
+        raise ValueError(io)
+    return ScanInputs(u=u, delta=dlt, A=A, B=B, C=C, D=np.ones(dim, np.float32) if D else None,
+                      z=zz if z else None, delta_bias=db if bias else None, h0=hh, io=io, softplus=softplus,
+                      meta=dict(seed=seed, batch=batch, dim=dim, dstate=dstate, seqlen=seqlen))
+
+
+def scan_config(i, **overrides):
+    """One of the four scan workloads (0 tiny, 1 Mamba-130M, 2 Mamba-1.4B bf16, 3 long sequence)."""
+    c = dict(SCAN_CONFIGS[i])
+    name = c.pop("name")
+    c["seed"] = SEED_BASE + i
+    c.update(overrides)
+    x = make_scan_inputs(**c)
+    x.meta["name"] = name
+    x.meta["config"] = i
+    return x
+
+
+@dataclass
+class DecodeInputs:
+    state0: np.ndarray  # (batch, dim, dstate) float32
+    A: np.ndarray
+    D: np.ndarray
+    delta_bias: np.ndarray
+    batch: int
+    dim: int
+    dstate: int
+    steps: int
+    io: str
+    meta: dict = field(default_factory=dict)
+
+    def step(self, s):
+        """Fresh per-token inputs of step s: dict(u, delta, z, B, C), bf16-rounded float32."""
+        rng = np.random.default_rng([SEED_BASE + 4, s])
+        b, d, n = self.batch, self.dim, self.dstate
+        u = _normal(rng, (b, d))
+        dlt = _normal(rng, (b, d), 0.5)
+        zz = _normal(rng, (b, d))
+        B = _normal(rng, (b, n))
+        C = _normal(rng, (b, n))
+        if self.io == "bf16":
+            u, dlt, zz, B, C = (round_bf16(t) for t in (u, dlt, zz, B, C))
+        return dict(u=u, delta=dlt, z=zz, B=B, C=C)
+
+
+def decode_config(batch=None, dim=None, steps=None):
+    """The recurrent-decode workload: persistent fp32 state ~ 0.1 * N(0, 1) (0.1 read as the standard deviation)."""
+    c = dict(DECODE_CONFIG)
+    batch = batch or c["batch"]
+    dim = dim or c["dim"]
+    steps = steps or c["steps"]
+    n = c["dstate"]
+    rng = np.random.default_rng(SEED_BASE + 4)
+    A = np.broadcast_to(-(np.arange(n, dtype=np.float32) + 1.0), (dim, n)).copy()
+    db = _dt_bias(rng, dim)
+    state0 = _normal(rng, (batch, dim, n), 0.1)
+    return DecodeInputs(state0=state0, A=A, D=np.ones(dim, np.float32), delta_bias=db, batch=batch, dim=dim,
+                        dstate=n, steps=steps, io=c["io"], meta=dict(seed=SEED_BASE + 4, name=c["name"]))
+
+
+def sample_channels(batch, dim, k, seed=0):
+    """k distinct (b, d) channel indices, always including the first and last channel."""
+    rng = np.random.default_rng(seed)
+    total = batch * dim
+    k = min(k, total)
+    idx = set([0, total - 1])
+    while len(idx) < k:
+        idx.add(int(rng.integers(0, total)))
+    return [(i // dim, i % dim) for i in sorted(idx)]
+
+
+def to_torch(x, device, names=None):
+    """Tensors for the binding: io arrays in float32 or bfloat16, the rest float32."""
+    import torch
+    io_dtype = torch.bfloat16 if x.io == "bf16" else torch.float32
+    out = {}
+    for k in ("u", "delta", "B", "C", "z"):
+        v = getattr(x, k)
+        out[k] = None if v is None else torch.from_numpy(v).to(device=device, dtype=io_dtype)
+    for k in ("A", "D", "delta_bias", "h0"):
+        v = getattr(x, k)
+        out[k] = None if v is None else torch.from_numpy(v).to(device=device)
+    return out

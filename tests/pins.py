@@ -1,0 +1,262 @@
+"""Pins for the fp64 oracle: checks against facts fixed by the pages and by
+the mathematics, each written independently of the oracle's loop.
+
+Every pin takes an oracle object (oracle.Oracle) and raises AssertionError on
+a mismatch, so the same pins run against the real oracle and against
+deliberately broken copies of it (tests/test_oracle_mutants.py).
+
+  worked_examples   hand-derived values (tests/golden/worked_examples.json)
+  lti_closed_form   constant Delta, B, C: the scan equals a causal convolution
+                    with kernel K_k = sum_n C_n Abar_n^k Delta B_n (the pages'
+                    recurrence-vs-global-convolution equivalence for S4, in the
+                    Chinese explainer's stage 2/3 and the Hebrew overview's
+                    linear-time-invariance section)
+  bruteforce        time-varying case, tiny L, evaluated in 50-digit mpmath
+                    from the product form h_t = (prod Abar) h0 + sum (prod Abar) Bbar u
+  single_step       L = 1 by hand formula
+  persistence       Delta = 0 leaves the state unchanged (small step: keep the
+                    state, ignore the input -- the explainer's gating section)
+  forgetting        huge Delta forgets the past (large step: reset the state)
+  split_carry       cutting the sequence and carrying last_state equals one pass
+                    (segments combine in any grouping -- the parallel scan)
+  linearity         with h0 = 0 the output is linear in u
+  softplus_silu     the scalar helpers against numpy / scipy library routines
+  decode_is_scan    the one-token update equals a one-token scan
+  channel_subset    scanning a subset of channels equals the rows of a full scan
+"""
+import json
+import math
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+GOLDEN = os.path.join(HERE, "golden", "worked_examples.json")
+
+
+def _close(got, want, rtol, atol=0.0, what=""):
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    assert got.shape == want.shape, "%s: shape %s vs %s" % (what, got.shape, want.shape)
+    err = np.abs(got - want)
+    tol = atol + rtol * np.abs(want)
+    bad = ~(err <= tol)
+    assert not bad.any(), "%s: max err %.3e at %s (got %r want %r)" % (
+        what, float(err.max()), np.unravel_index(int(np.argmax(err)), err.shape), got.flat[np.argmax(err)],
+        want.flat[np.argmax(err)])
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _random_problem(rng, batch, dim, dstate, seqlen, z=True, D=True, bias=True, h0=True):
+    A = -rng.uniform(0.2, 3.0, size=(dim, dstate))
+    return dict(
+        u=rng.standard_normal((batch, dim, seqlen)),
+        delta=0.5 * rng.standard_normal((batch, dim, seqlen)),
+        A=A,
+        B=rng.standard_normal((batch, dstate, seqlen)),
+        C=rng.standard_normal((batch, dstate, seqlen)),
+        D=rng.standard_normal(dim) if D else None,
+        z=rng.standard_normal((batch, dim, seqlen)) if z else None,
+        delta_bias=rng.uniform(-2.0, 0.5, size=dim) if bias else None,
+        h0=rng.standard_normal((batch, dim, dstate)) if h0 else None,
+    )
+
+
+# ---------------------------------------------------------------------------
+
+
+def worked_examples(o):
+    data = json.load(open(GOLDEN))
+    env = {"ln2": math.log(2.0), "ln3": math.log(3.0), "__builtins__": {}}
+
+    def ev(x):
+        if x is None:
+            return None
+        if isinstance(x, list):
+            return np.array([ev(v) for v in x], dtype=np.float64)
+        if isinstance(x, str):
+            return float(eval(x, env))
+        return float(x)
+
+    for case in data["cases"]:
+        args = {k: ev(case[k]) for k in ("u", "delta", "A", "B", "C", "D", "z", "delta_bias", "h0")}
+        y, last = o.scan_f64(softplus=case["softplus"], **args)
+        _close(y, ev(case["expected_y"]), 1e-14, 1e-14, case["name"] + " y")
+        _close(last, ev(case["expected_last_state"]), 1e-14, 1e-14, case["name"] + " last_state")
+
+
+def lti_closed_form(o):
+    rng = _rng(11)
+    batch, dim, dstate, seqlen = 2, 3, 4, 40
+    for with_h0 in (False, True):
+        p = _random_problem(rng, batch, dim, dstate, seqlen, z=True, D=True, bias=True, h0=with_h0)
+        # Time-invariant system: one raw step per channel, one B and C per batch row.
+        p["delta"] = np.repeat(0.5 * rng.standard_normal((batch, dim, 1)), seqlen, axis=2)
+        Bc = rng.standard_normal((batch, dstate, 1))
+        Cc = rng.standard_normal((batch, dstate, 1))
+        p["B"] = np.repeat(Bc, seqlen, axis=2)
+        p["C"] = np.repeat(Cc, seqlen, axis=2)
+        y, last = o.scan_f64(softplus=True, **p)
+        k = np.arange(seqlen)
+        for b in range(batch):
+            for d in range(dim):
+                step = np.logaddexp(0.0, p["delta"][b, d, 0] + p["delta_bias"][d])
+                abar = np.exp(step * p["A"][d])                             # (dstate,)
+                powers = abar[None, :] ** k[:, None]                         # (seqlen, dstate)
+                K = powers @ (Cc[b, :, 0] * step * Bc[b, :, 0])              # convolution kernel
+                conv = np.convolve(p["u"][b, d], K)[:seqlen]
+                ref = conv + p["D"][d] * p["u"][b, d]
+                if with_h0:
+                    ref = ref + (abar[None, :] ** (k[:, None] + 1)) @ (Cc[b, :, 0] * p["h0"][b, d])
+                zz = p["z"][b, d]
+                from scipy.special import expit
+                ref = ref * zz * expit(zz)
+                _close(y[b, d], ref, 1e-11, 1e-12, "LTI convolution b=%d d=%d h0=%s" % (b, d, with_h0))
+                h_ref = (abar ** seqlen) * (p["h0"][b, d] if with_h0 else 0.0) + np.array(
+                    [np.sum(abar[n] ** (seqlen - 1 - k) * step * Bc[b, n, 0] * p["u"][b, d]) for n in range(dstate)])
+                _close(last[b, d], h_ref, 1e-11, 1e-12, "LTI final state b=%d d=%d" % (b, d))
+
+
+def bruteforce(o):
+    import itertools
+    import mpmath as mp
+    mp.mp.dps = 50
+    rng = _rng(12)
+    batch, dim, dstate, seqlen = 2, 2, 3, 5
+    for flags in itertools.product([False, True], repeat=5):
+        zf, Df, bf, spf, hf = flags
+        p = _random_problem(rng, batch, dim, dstate, seqlen, z=zf, D=Df, bias=bf, h0=hf)
+        y, last = o.scan_f64(softplus=spf, **p)
+        for b in range(batch):
+            for d in range(dim):
+                steps = []
+                for t in range(seqlen):
+                    x = mp.mpf(p["delta"][b, d, t]) + (mp.mpf(p["delta_bias"][d]) if bf else 0)
+                    steps.append(mp.log(1 + mp.exp(x)) if spf else x)
+                abar = [[mp.exp(steps[t] * mp.mpf(p["A"][d, n])) for n in range(dstate)] for t in range(seqlen)]
+                for t in range(seqlen):
+                    acc = mp.mpf(0)
+                    hs = []
+                    for n in range(dstate):
+                        prod_all = mp.fprod(abar[s][n] for s in range(t + 1))
+                        h = prod_all * (mp.mpf(p["h0"][b, d, n]) if hf else 0)
+                        for s in range(t + 1):
+                            tail = mp.fprod(abar[r][n] for r in range(s + 1, t + 1))
+                            h += tail * steps[s] * mp.mpf(p["B"][b, n, s]) * mp.mpf(p["u"][b, d, s])
+                        hs.append(h)
+                        acc += mp.mpf(p["C"][b, n, t]) * h
+                    if Df:
+                        acc += mp.mpf(p["D"][d]) * mp.mpf(p["u"][b, d, t])
+                    if zf:
+                        zz = mp.mpf(p["z"][b, d, t])
+                        acc *= zz / (1 + mp.exp(-zz))
+                    _close(y[b, d, t], float(acc), 1e-13, 1e-14, "brute force y flags=%s" % (flags,))
+                    if t == seqlen - 1:
+                        _close(last[b, d], [float(v) for v in hs], 1e-13, 1e-14, "brute force h flags=%s" % (flags,))
+
+
+def single_step(o):
+    rng = _rng(13)
+    p = _random_problem(rng, 3, 4, 5, 1)
+    y, last = o.scan_f64(softplus=True, **p)
+    step = np.logaddexp(0.0, p["delta"][..., 0] + p["delta_bias"][None, :])           # (b, d)
+    abar = np.exp(step[..., None] * p["A"][None])                                     # (b, d, n)
+    h = abar * p["h0"] + step[..., None] * p["B"][:, None, :, 0] * p["u"][..., 0][..., None]
+    ref = np.einsum("bdn,bn->bd", h, p["C"][..., 0]) + p["D"][None] * p["u"][..., 0]
+    zz = p["z"][..., 0]
+    ref = ref * zz / (1.0 + np.exp(-zz))
+    _close(y[..., 0], ref, 1e-13, 1e-14, "single step y")
+    _close(last, h, 1e-13, 1e-14, "single step h")
+
+
+def persistence(o):
+    rng = _rng(14)
+    p = _random_problem(rng, 2, 3, 4, 17, z=False, bias=False, h0=True)
+    p["delta"] = np.zeros_like(p["delta"])
+    y, last = o.scan_f64(softplus=False, **p)
+    assert np.array_equal(last, p["h0"]), "zero step must leave the state unchanged"
+    ref = np.einsum("bdn,bnl->bdl", p["h0"], p["C"]) + p["D"][None, :, None] * p["u"]
+    _close(y, ref, 1e-14, 1e-14, "persistence y")
+
+
+def forgetting(o):
+    rng = _rng(15)
+    p = _random_problem(rng, 2, 3, 4, 12, bias=False, h0=True)
+    p["A"] = -rng.uniform(1.0, 4.0, size=p["A"].shape)
+    p["delta"] = np.full_like(p["delta"], 50.0)
+    y1, _ = o.scan_f64(softplus=False, **p)
+    q = dict(p)
+    for t in range(1, 12):
+        q["u"] = p["u"].copy()
+        q["u"][..., :t] += rng.standard_normal(q["u"][..., :t].shape) * 10.0
+        q["h0"] = p["h0"] + 100.0
+        y2, _ = o.scan_f64(softplus=False, **q)
+        _close(y2[..., t:], y1[..., t:], 1e-15, 1e-12, "forgetting t=%d" % t)
+        # and the past did matter before t (the perturbation is visible there)
+        assert np.abs(y2[..., :t] - y1[..., :t]).max() > 1e-3
+
+
+def split_carry(o):
+    rng = _rng(16)
+    p = _random_problem(rng, 2, 3, 4, 50)
+    y, last = o.scan_f64(softplus=True, **p)
+    for cuts in ([1], [7, 8], [13, 29, 30, 49]):
+        h = p["h0"]
+        pieces = []
+        edges = [0] + cuts + [50]
+        for a, b in zip(edges[:-1], edges[1:]):
+            q = dict(p)
+            for k in ("u", "delta", "B", "C", "z"):
+                q[k] = p[k][..., a:b]
+            q["h0"] = h
+            yy, h = o.scan_f64(softplus=True, **q)
+            pieces.append(yy)
+        _close(np.concatenate(pieces, axis=-1), y, 1e-12, 1e-13, "split %s y" % cuts)
+        _close(h, last, 1e-12, 1e-13, "split %s state" % cuts)
+
+
+def linearity(o):
+    rng = _rng(17)
+    p = _random_problem(rng, 2, 3, 4, 30, h0=False)
+    u1, u2 = p["u"], rng.standard_normal(p["u"].shape)
+    a, b = 0.75, -2.5
+    y1, h1 = o.scan_f64(softplus=True, **dict(p, u=u1))
+    y2, h2 = o.scan_f64(softplus=True, **dict(p, u=u2))
+    y3, h3 = o.scan_f64(softplus=True, **dict(p, u=a * u1 + b * u2))
+    _close(y3, a * y1 + b * y2, 1e-12, 1e-12, "linearity y")
+    _close(h3, a * h1 + b * h2, 1e-12, 1e-12, "linearity h")
+
+
+def softplus_silu(o):
+    from scipy.special import expit
+    for x in (-800.0, -60.0, -20.0, -7.0, -1e-3, 0.0, 1e-3, 1.0, 19.0, 21.0, 60.0, 800.0):
+        _close(o.softplus_f64(x), np.logaddexp(0.0, x), 1e-15, 0.0, "softplus(%g)" % x)
+        _close(o.silu_f64(x), x * expit(x), 1e-15, 1e-300, "silu(%g)" % x)
+
+
+def decode_is_scan(o):
+    rng = _rng(18)
+    p = _random_problem(rng, 3, 5, 4, 1)
+    y_scan, h_scan = o.scan_f64(softplus=True, **p)
+    state = p["h0"].copy()
+    y_dec = o.state_update_f64(state, p["u"][..., 0], p["delta"][..., 0], p["A"], p["B"][..., 0], p["C"][..., 0],
+                               p["D"], p["z"][..., 0], p["delta_bias"], softplus=True)
+    _close(y_dec, y_scan[..., 0], 1e-15, 1e-15, "decode y")
+    _close(state, h_scan, 1e-15, 1e-15, "decode state")
+
+
+def channel_subset(o):
+    rng = _rng(19)
+    p = _random_problem(rng, 3, 5, 4, 9)
+    y, last = o.scan_f64(softplus=True, **p)
+    ch = [(0, 0), (1, 3), (2, 4), (0, 2)]
+    ys, hs = o.scan_channels_f64(ch, softplus=True, **p)
+    for i, (b, d) in enumerate(ch):
+        assert np.array_equal(ys[i], y[b, d]) and np.array_equal(hs[i], last[b, d])
+
+
+ALL = [worked_examples, lti_closed_form, bruteforce, single_step, persistence, forgetting, split_carry, linearity,
+       softplus_silu, decode_is_scan, channel_subset]

@@ -1,0 +1,56 @@
+"""The pins must catch plausible mistakes in the oracle.
+
+Each mutant is a copy of oracle/ssm_oracle.c with one planted error (a dropped
+term, a wrong sign, a transposed index, an output lag, ...), compiled with the
+same flags into a temporary directory.  Every mutant must fail at least one pin
+of tests/pins.py; the real oracle passes them all (test_oracle_pins.py).
+"""
+import os
+
+import pytest
+
+import oracle
+import pins
+
+# (name, original text, replacement)
+MUTANTS = [
+    ("output_lag", "      h[n] = abar * h[n] + bbar_u;\n      v += C_b[n * seqlen + l] * h[n];",
+     "      v += C_b[n * seqlen + l] * h[n];\n      h[n] = abar * h[n] + bbar_u;"),
+    ("exp_sign", "exp(delta * A_row[n])", "exp(-delta * A_row[n])"),
+    ("dropped_D", "    v += Dd * ul;", "    v += 0.0 * Dd * ul;"),
+    ("B_transposed", "delta * B_b[n * seqlen + l] * ul", "delta * B_b[l * dstate + n] * ul"),
+    ("C_transposed", "v += C_b[n * seqlen + l] * h[n];", "v += C_b[l * dstate + n] * h[n];"),
+    ("bias_ignored", "double x = dt_row[l] + bias;", "double x = dt_row[l] + 0.0 * bias;"),
+    ("bias_after_softplus", "double delta = softplus_flag ? oracle_softplus(x) : x;",
+     "double delta = softplus_flag ? oracle_softplus(dt_row[l]) + bias : x;"),
+    ("gate_sigmoid", "if (z_row) v *= oracle_silu(z_row[l]);", "if (z_row) v *= 1.0 / (1.0 + exp(-z_row[l]));"),
+    ("h0_ignored", "h[n] = h0 ? h0[ch * dstate + n] : 0.0;", "h[n] = 0.0;"),
+    ("bbar_without_delta", "double bbar_u = delta * B_b[n * seqlen + l] * ul;",
+     "double bbar_u = B_b[n * seqlen + l] * ul;"),
+    ("softplus_negative_branch", "return (x > 0.0 ? x : 0.0) + log1p(exp(-ax));", "return x + log1p(exp(-ax));"),
+    ("A_row_of_channel_0", "delta + ch * seqlen, A + d * dstate,", "delta + ch * seqlen, A,"),
+    ("B_of_batch_0", "B + b * dstate * seqlen, C + b * dstate * seqlen,", "B, C + b * dstate * seqlen,"),
+    ("abar_linearized", "double abar = exp(delta * A_row[n]);", "double abar = 1.0 + delta * A_row[n];"),
+    ("state_not_decayed", "h[n] = abar * h[n] + bbar_u;", "h[n] = h[n] + bbar_u;"),
+]
+
+
+@pytest.fixture(scope="module")
+def source():
+    return open(oracle.SOURCE).read()
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(tmp_path, source, name, old, new):
+    assert source.count(old) == 1, "mutation site for %s not found exactly once" % name
+    src = tmp_path / ("mutant_%s.c" % name)
+    src.write_text(source.replace(old, new))
+    lib = oracle.compile_oracle(str(src), str(tmp_path / ("libmutant_%s.so" % name)))
+    o = oracle.Oracle(lib)
+    caught = []
+    for pin in pins.ALL:
+        try:
+            pin(o)
+        except AssertionError:
+            caught.append(pin.__name__)
+    assert caught, "mutant %s passed every pin" % name
