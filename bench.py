@@ -1,0 +1,202 @@
+#!/usr/bin/env python3
+"""Selective-scan benchmark on one MI355X.
+
+One step = one ssm_scan_fwd call over the Mamba-1.4B-layer workload (batch 4,
+dim 4096, dstate 16, seqlen 4096; u, delta, z, B, C, y in bf16; A, D, bias and
+the state in fp32; gate and softplus on), with inputs resident in HBM before
+the timed region.  Prints one JSON line:
+
+  value        whole-job HBM throughput, algorithmic bytes / wall time per step (GB/s)
+  roofline     the scan call against its binding roof (see below), timed with
+               HIP events on the launch stream
+  cpu_baseline the fp64 oracle on the host cores, on a bounded sample of the
+               same workload
+  decode       the one-token state update at the decode workload (batch 256,
+               dim 5120, dstate 16), per step
+
+Algorithmic bytes: read u, delta, z and write y once (4 x io bytes per
+element), read B and C once per (batch, token), read A, D and the bias once,
+write the final state once.  The (batch, dim, seqlen, dstate) expanded state
+is not counted: the method never stores it.
+
+ALU roof: each (element, state) needs one exp2 and four fp32 VALU operations
+(Delta*A, B*x, the state FMA and the C.h FMA).  On gfx950 exp2 issues at half
+the fp32 rate, so the floor is 6 VALU lane-slots per (element, state), against
+256 CU x 64 lanes x 2.4 GHz = 39.3 T lane-slots/s.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "selective-scan HBM GB/s (% of MI355X peak) + (B·D·L)/s at Mamba-1.4B shape"
+HBM_PEAK_GBS = 8000.0
+LANE_SLOTS_PEAK = 256 * 64 * 2.4e9  # fp32 VALU lane-slots per second
+SLOTS_PER_ELEM_STATE = 6            # exp2 (2 slots, half rate) + 4 fp32 ops
+
+
+def algorithmic_bytes(batch, dim, dstate, seqlen, io_bytes, has_z=True, has_h0=False):
+    streams = (4 if has_z else 3) * batch * dim * seqlen * io_bytes      # u, delta, (z) in, y out
+    bc = 2 * batch * dstate * seqlen * io_bytes
+    params = dim * dstate * 4 + 2 * dim * 4
+    state = batch * dim * dstate * 4 * (2 if has_h0 else 1)
+    return streams + bc + params + state
+
+
+def decode_bytes(batch, dim, dstate, io_bytes):
+    return (2 * batch * dim * dstate * 4 + 4 * batch * dim * io_bytes + 2 * batch * dstate * io_bytes
+            + dim * dstate * 4 + 2 * dim * 4)
+
+
+def cpu_cores():
+    env = os.environ.get("OMP_NUM_THREADS")
+    if env and env.isdigit():
+        return int(env)
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
+def cpu_baseline(x, budget_s):
+    """Time the fp64 oracle on whole batch rows of the workload until budget_s has elapsed."""
+    import numpy as np
+    import oracle
+    b, d, n, l = x.shape
+    o = oracle.default()
+    done = 0
+    spent = 0.0
+    rows = 0
+    for bi in range(b):
+        sl = slice(bi, bi + 1)
+        args = [np.ascontiguousarray(a[sl], dtype=np.float64) for a in (x.u, x.delta, x.B, x.C, x.z)]
+        t0 = time.perf_counter()
+        o.scan_f64(args[0], args[1], x.A, args[2], args[3], x.D, args[4], x.delta_bias, x.softplus, None)
+        spent += time.perf_counter() - t0
+        done += d * l
+        rows += 1
+        if spent >= budget_s:
+            break
+    gbs = algorithmic_bytes(rows, d, n, l, 2 if x.io == "bf16" else 4) / spent / 1e9
+    return dict(value=round(gbs, 3), unit="GB/s", cores=cpu_cores(), kind="oracle",
+                sample="%d of %d batch rows (%d channels x %d tokens, dstate %d), fp64, OpenMP over channels"
+                % (rows, b, rows * d, l, n), seconds=round(spent, 3), elements_per_s=round(done / spent, 1))
+
+
+def time_calls(fn, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record()
+        fn()
+        ends[i].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    return wall / steps * 1e3, sum(per) / len(per), per[len(per) // 2]
+
+
+def bench_decode(dev, steps, warmup):
+    import torch
+    from selective_state_space_65_amd import binding, inputs
+    dec = inputs.decode_config()
+    st = dec.step(0)
+    state = torch.from_numpy(dec.state0).to(dev)
+    A = torch.from_numpy(dec.A).to(dev)
+    D = torch.from_numpy(dec.D).to(dev)
+    bias = torch.from_numpy(dec.delta_bias).to(dev)
+    tt = {k: torch.from_numpy(v).to(dev, torch.bfloat16) for k, v in st.items()}
+    y = torch.empty_like(tt["u"])
+
+    def fn():
+        binding.state_update(state, tt["u"], tt["delta"], A, tt["B"], tt["C"], D=D, z=tt["z"], delta_bias=bias,
+                             delta_softplus=True, out=y)
+
+    wall_ms, avg_ms, med_ms = time_calls(fn, steps, warmup)
+    nbytes = decode_bytes(dec.batch, dec.dim, dec.dstate, 2)
+    return dict(workload="decode state update, batch %d, dim %d, dstate %d, bf16 io, fp32 state"
+                % (dec.batch, dec.dim, dec.dstate), us_per_step=round(avg_ms * 1e3, 2),
+                effective_gbs=round(nbytes / (avg_ms * 1e-3) / 1e9, 1), bytes_per_step=nbytes,
+                note="the 84 MB state can stay in the 256 MB Infinity Cache between steps, so this is an "
+                     "effective rate, not HBM traffic")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=2, help="scan workload (default 2: Mamba-1.4B layer)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: every box here has a single MI355X, and this path is not "
+              "sharded across GPUs (run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from selective_state_space_65_amd import binding, inputs
+
+    dev = "cuda:0"
+    x = inputs.scan_config(args.config)
+    b, d, n, l = x.shape
+    io_bytes = 2 if x.io == "bf16" else 4
+    t = inputs.to_torch(x, dev)
+    y = torch.empty_like(t["u"])
+    last = torch.empty((b, d, n), dtype=torch.float32, device=dev)
+
+    def step():
+        binding.scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"], delta_bias=t["delta_bias"],
+                         delta_softplus=x.softplus, h0=None, out=y, last_state=last)
+
+    wall_ms, avg_ms, med_ms = time_calls(step, args.steps, args.warmup)
+    nbytes = algorithmic_bytes(b, d, n, l, io_bytes, has_z=x.z is not None)
+    elems = b * d * l
+    gbs = nbytes / (wall_ms * 1e-3) / 1e9
+    seg, seglen, scratch = binding.scan_plan(b, d, n, l, t["u"].dtype)
+
+    call_gbs = nbytes / (avg_ms * 1e-3) / 1e9
+    slots = SLOTS_PER_ELEM_STATE * elems * n
+    alu_rate = slots / (avg_ms * 1e-3)
+    hbm_frac = call_gbs / HBM_PEAK_GBS
+    alu_frac = alu_rate / LANE_SLOTS_PEAK
+    if alu_frac >= hbm_frac:
+        roof = dict(bound="alu", achieved=round(alu_rate / 1e12, 2), peak=round(LANE_SLOTS_PEAK / 1e12, 2),
+                    unit="T lane-slots/s", frac=round(alu_frac, 4))
+    else:
+        roof = dict(bound="hbm", achieved=round(call_gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s", frac=round(hbm_frac, 4))
+    roof.update(traffic=None, kernel="ssm_scan_fwd call (%s)" % (
+        "scan_kernel" if seg == 1 else "aggregate_kernel + carry_kernel + scan_kernel"),
+        call_us_avg=round(avg_ms * 1e3, 2), call_us_median=round(med_ms * 1e3, 2),
+        hbm_gbs=round(call_gbs, 1), hbm_frac=round(hbm_frac, 4), alu_frac=round(alu_frac, 4),
+        algorithmic_bytes=nbytes, algorithmic_lane_slots=slots)
+
+    out = dict(metric=METRIC, value=round(gbs, 1), unit="GB/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
+               ms_per_step=round(wall_ms, 4), higher_is_better=True, scaling="weak", vs_baseline=None, dtype="f32",
+               data="synthetic",
+               config=dict(workload=x.meta["name"], batch=b, dim=d, dstate=n, seqlen=l, io=x.io, gate=True,
+                           softplus=True, segments=seg, segment_len=seglen),
+               hbm_frac_of_peak=round(gbs / HBM_PEAK_GBS, 4), elements_per_s=round(elems / (wall_ms * 1e-3), 1),
+               roofline=roof)
+    if not args.no_decode:
+        out["decode"] = bench_decode(dev, 50, 5)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(x, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

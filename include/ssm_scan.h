@@ -1,0 +1,158 @@
+/*
+ * ssm_scan.h -- C ABI of the MI355X (gfx950) selective state-space scan (S6).
+ *
+ * Two operations, both on device memory, both asynchronous on the caller's
+ * HIP stream:
+ *
+ *   ssm_scan_fwd      prefill: run the selective scan over a whole sequence;
+ *   ssm_state_update  decode: advance a persistent state by one token.
+ *
+ * What is computed (for every batch row b and channel d independently):
+ *
+ *   Delta_l = softplus(delta[b,d,l] + bias[d])   (or delta + bias, flag off)
+ *   Abar    = exp(Delta_l * A[d,n])              zero-order hold of A
+ *   h[n]    = Abar * h[n] + Delta_l * B[b,n,l] * u[b,d,l]
+ *   y[b,d,l]= (sum_n C[b,n,l] * h[n] + D[d] * u[b,d,l]) * silu(z[b,d,l])
+ *
+ * The state recurrence h <- A h + B x and read-out y = C h are the equations
+ * of the Korean Mamba summary ("Mamba: Linear-Time Sequence Modeling with
+ * Selective State Spaces", section on the SSM's mathematical definition).  The
+ * scan (previous state times A-bar plus current input times B-bar) is the
+ * Chinese Mamba explainer's "hardware-aware design: parallel scan" section;
+ * the input dependence of Delta, B and C (A fixed and diagonal, N numbers per
+ * channel) is from the same explainer's S4-to-S6 sections and the Hebrew
+ * overview's "SSM + selection (S6)" section; zero-order hold is named in the
+ * explainer's discretization stage (1a/1b).  The pages lost the formulas; the
+ * readings taken for the silent points are: Bbar*u = Delta*B*u, no output lag
+ * (y_l uses h_l, which already holds u_l), D skip before the gate, silu gate,
+ * softplus applied to delta + bias, zero initial state unless h0 is given.
+ *
+ * Conventions shared by both entry points
+ *  - Every pointer is a DEVICE pointer to contiguous, row-major memory (last
+ *    index fastest).  The caller owns every buffer; the library never keeps a
+ *    pointer after the call returns.
+ *  - io dtype (SSM_F32 or SSM_BF16) applies to u, delta, z, B, C and y.  A, D,
+ *    delta_bias, h0, last_state and state are always fp32.  All arithmetic is
+ *    fp32; bf16 inputs are widened exactly, y is rounded to nearest-even.
+ *  - Optional pointers (D, z, delta_bias, h0, last_state) may be NULL:
+ *    D = NULL means D = 0, delta_bias = NULL means 0, z = NULL means no gate,
+ *    h0 = NULL means a zero initial state, last_state = NULL means not written.
+ *  - Sizes: batch, dim, seqlen >= 1 and 1 <= dstate <= 16.
+ *  - stream is a hipStream_t (NULL = the default stream).  The call only
+ *    enqueues work; device-side faults surface at the caller's next
+ *    synchronisation.  The library prints nothing and never aborts.
+ *  - Validation (NULL pointers, sizes, dtype, element alignment, overlap of an
+ *    output with an input) happens on the host before any HIP call, so an
+ *    invalid call returns an error code without touching the device.
+ *  - NaN and Inf propagate; nothing is clamped.
+ *  - The library may take stream-ordered scratch memory from a pool of its
+ *    own during ssm_scan_fwd (per-segment carries of long sequences); it is
+ *    released on the same stream before the call returns.  Calls on different
+ *    streams are independent; the library is re-entrant.
+ */
+#ifndef SSM_SCAN_H
+#define SSM_SCAN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSM_ABI_VERSION 1
+
+struct ihipStream_t; /* the same incomplete type as HIP's hipStream_t */
+
+typedef enum {
+  SSM_F32 = 0,  /* 32-bit IEEE float */
+  SSM_BF16 = 1  /* bfloat16 (upper half of an fp32) */
+} ssm_dtype_t;
+
+typedef enum {
+  SSM_OK = 0,
+  SSM_ERR_NULL = 1,                 /* a required pointer is NULL            */
+  SSM_ERR_SHAPE = 2,                /* a size < 1, or a size product overflows */
+  SSM_ERR_DSTATE_UNSUPPORTED = 3,   /* dstate > 16                           */
+  SSM_ERR_DTYPE = 4,                /* unknown io dtype                      */
+  SSM_ERR_ALIGN = 5,                /* a pointer is not element-aligned      */
+  SSM_ERR_ALIAS = 6,                /* an output overlaps an input           */
+  SSM_ERR_HIP = 7                   /* a HIP runtime call failed             */
+} ssm_status_t;
+
+/*
+ * ssm_scan_fwd -- prefill selective scan over seqlen tokens.
+ *
+ *   u          [batch, dim, seqlen]     io     input sequence x
+ *   delta      [batch, dim, seqlen]     io     raw step size (before bias / softplus)
+ *   A          [dim, dstate]            fp32   diagonal state matrix (one row per channel)
+ *   B          [batch, dstate, seqlen]  io     input matrix, per token, shared by all channels
+ *   C          [batch, dstate, seqlen]  io     output matrix, per token, shared by all channels
+ *   D          [dim]                    fp32   skip weight, may be NULL
+ *   z          [batch, dim, seqlen]     io     gate input, may be NULL
+ *   delta_bias [dim]                    fp32   added to delta, may be NULL
+ *   softplus_flag                              nonzero: Delta = softplus(delta + bias)
+ *   h0         [batch, dim, dstate]     fp32   initial state, may be NULL; may be the
+ *                                              same pointer as last_state (the state is
+ *                                              then carried in place); any other overlap
+ *                                              with an output is SSM_ERR_ALIAS
+ *   y          [batch, dim, seqlen]     io     output, written
+ *   last_state [batch, dim, dstate]     fp32   state after the last token, may be NULL
+ *
+ * y must not overlap any input.  The expanded (batch, dim, seqlen, dstate)
+ * state is never written to memory: each channel's dstate values live in
+ * registers for the whole scan.
+ */
+ssm_status_t ssm_scan_fwd(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, ssm_dtype_t io,
+                          const void* u, const void* delta, const float* A, const void* B,
+                          const void* C, const float* D, const void* z, const float* delta_bias,
+                          int softplus_flag, const float* h0, void* y, float* last_state,
+                          struct ihipStream_t* stream);
+
+/*
+ * ssm_state_update -- one decode step: the recurrence of ssm_scan_fwd for a
+ * single token (seqlen = 1), updating the state in place.  This is the
+ * recurrent ("RNN") mode the Chinese explainer describes for autoregressive
+ * inference: constant work per token because the state has a fixed size.
+ *
+ *   state      [batch, dim, dstate]     fp32   read, then overwritten with the new state
+ *   u, delta   [batch, dim]             io
+ *   A          [dim, dstate]            fp32
+ *   B, C       [batch, dstate]          io
+ *   D          [dim]                    fp32   may be NULL
+ *   z          [batch, dim]             io     may be NULL
+ *   delta_bias [dim]                    fp32   may be NULL
+ *   y          [batch, dim]             io     written; must not overlap any input or state
+ *
+ * The result equals ssm_scan_fwd with seqlen = 1, h0 = last_state = state.
+ */
+ssm_status_t ssm_state_update(int64_t batch, int64_t dim, int64_t dstate, ssm_dtype_t io, float* state,
+                              const void* u, const void* delta, const float* A, const void* B,
+                              const void* C, const float* D, const void* z,
+                              const float* delta_bias, int softplus_flag, void* y,
+                              struct ihipStream_t* stream);
+
+/*
+ * ssm_scan_fwd_plan -- how ssm_scan_fwd would split a problem of this shape:
+ * the number of sequence segments scanned in parallel per channel, the
+ * segment length in tokens, and the scratch bytes the call takes from the
+ * library's pool.  Pure host arithmetic; any output pointer may be NULL.
+ * Returns the same status ssm_scan_fwd would return for these sizes.
+ */
+ssm_status_t ssm_scan_fwd_plan(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
+                               ssm_dtype_t io, int64_t* segments, int64_t* segment_len,
+                               int64_t* scratch_bytes);
+
+/* Static English text for a status code (never NULL). */
+const char* ssm_status_string(ssm_status_t status);
+
+/* The HIP error code behind the calling thread's last SSM_ERR_HIP (0 if none). */
+int ssm_last_hip_error(void);
+
+/* SSM_ABI_VERSION of the built library. */
+int ssm_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSM_SCAN_H */

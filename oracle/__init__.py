@@ -12,6 +12,7 @@ this module only marshals numpy arrays into it.
   .scan_channels_f64(...)  the same scan restricted to chosen (b, d) channels
                            (channels are independent, so a subset is exact)
   .state_update_f64(...)   one-token update of a float64 state, in place
+  .state_update_channels_f64(...)  the same for chosen (b, d) channels
   .softplus_f64, .silu_f64 the scalar helpers the C oracle uses
 Module-level functions of the same names use the default oracle.
 """
@@ -98,6 +99,22 @@ class Oracle:
             hs.append(h[0, 0])
         return np.stack(ys), np.stack(hs)
 
+    def state_update_channels_f64(self, channels, state_rows, u, delta, A, B, C, D=None, z=None, delta_bias=None,
+                                  softplus=False):
+        """One-token update of chosen (b, d) channels only.
+
+        state_rows: float64 (k, dstate), row i belongs to channels[i], updated in
+        place; u, delta, z: (batch, dim); B, C: (batch, dstate).  Returns y (k,).
+        """
+        y = np.empty(len(channels), np.float64)
+        for i, (b, d) in enumerate(channels):
+            st = state_rows[i:i + 1].reshape(1, 1, -1)  # a view: updated in place
+            y[i] = self.state_update_f64(st, u[b:b + 1, d:d + 1], delta[b:b + 1, d:d + 1], A[d:d + 1], B[b:b + 1],
+                                         C[b:b + 1], None if D is None else D[d:d + 1],
+                                         None if z is None else z[b:b + 1, d:d + 1],
+                                         None if delta_bias is None else delta_bias[d:d + 1], softplus)[0, 0]
+        return y
+
     def state_update_f64(self, state, u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=False):
         """Advance `state` (float64 (batch, dim, dstate), modified in place) by one token; returns y (batch, dim)."""
         if state.dtype != np.float64 or not state.flags["C_CONTIGUOUS"]:
@@ -134,6 +151,10 @@ def scan_channels_f64(*args, **kw):
 
 def state_update_f64(*args, **kw):
     return default().state_update_f64(*args, **kw)
+
+
+def state_update_channels_f64(*args, **kw):
+    return default().state_update_channels_f64(*args, **kw)
 
 
 def softplus_f64(x):

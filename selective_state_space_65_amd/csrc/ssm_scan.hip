@@ -1,0 +1,919 @@
+// ssm_scan.hip -- selective state-space scan (S6) for MI355X / gfx950.
+//
+// Prefill (ssm_scan_fwd) and one-token decode (ssm_state_update) behind the C
+// ABI declared in include/ssm_scan.h.  Everything on the path runs in the
+// kernels below; the host code only validates, plans and launches.
+//
+// Mathematics (see the header for the sources on the pages):
+//   Delta = softplus(delta + bias)          (or delta + bias)
+//   Abar  = exp(Delta * A)                  zero-order hold of the diagonal A
+//   h     = Abar * h + Delta * B * u        the scan ("previous state times
+//                                           A-bar plus current input times B-bar")
+//   y     = (C . h + D * u) * silu(z)
+//
+// Layout of the work on the chip
+//   * One lane owns one channel d; a wave owns 64 consecutive channels of one
+//     batch row.  All 64 lanes therefore sit on the same token l, so B[b,:,l]
+//     and C[b,:,l] are wave-uniform: they are fetched with scalar loads into
+//     SGPRs and used directly as VALU operands.  No LDS or VGPR traffic is
+//     spent on B and C, and the dstate-wide state h of each channel stays in
+//     VGPRs for the whole sequence (the (batch, dim, seqlen, dstate) expanded
+//     state never exists in memory).
+//   * u, delta, z and y are streamed along l in chunks of 8 tokens per lane
+//     (one 16-byte load per row for bf16, two for fp32), prefetched one chunk
+//     ahead.
+//   * When batch*ceil(dim/64) waves cannot fill the 256 compute units, the
+//     sequence is cut into P segments scanned in parallel.  The scan is an
+//     associative composition of affine maps h -> a*h + b with
+//     (a1, b1) o (a2, b2) = (a1*a2, a2*b1 + b2) (the explainer's parallel
+//     scan: segments are computed separately and combined because the order
+//     of combination does not matter).  Three launches:
+//       1. aggregate: each segment but the last scans from a zero state and
+//          stores its end state b and sum(Delta) (a = exp(A * sum Delta));
+//       2. carry: one thread per (channel, state) folds the segment
+//          aggregates in order, starting from h0, into each segment's
+//          carry-in;
+//       3. scan: each segment rescans from its carry-in and writes y; the
+//          last segment writes last_state.
+//     With P = 1 only launch 3 runs, reading h0 directly.
+//   * The decode kernel gives each channel dstate/4 lanes (four states per
+//     lane) so that the fp32 state rows are read and written with fully
+//     coalesced 16-byte accesses; the dot product with C is finished with a
+//     lane shuffle.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+
+#include "ssm_scan.h"
+
+namespace {
+
+// ----------------------------------------------------------------------------
+// Device helpers
+// ----------------------------------------------------------------------------
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kChunk = 8;           // tokens per lane per inner iteration
+constexpr int kWaveThreads = 64;
+constexpr int kBlockThreads = 256;  // 4 independent waves per block
+constexpr int kWavesPerBlock = kBlockThreads / kWaveThreads;
+
+typedef uint16_t bf16_t;  // bit pattern of a bfloat16
+
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float log2_hw(float x) { return __builtin_amdgcn_logf(x); }
+__device__ __forceinline__ float rcp_hw(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// softplus(x) = log(1 + e^x).  e^x via the hardware exp2; log1p(e) via the
+// hardware log2 with Kahan's correction for the rounding of w = 1 + e
+// (log1p(e) = log(w) * e / (w - 1), D. Goldberg, "What every computer
+// scientist should know about floating-point arithmetic", 1991).  Above 20 the
+// result equals x to within 2e-9 and e^x may overflow, so x is returned.
+__device__ __forceinline__ float softplus_f32(float x) {
+  float e = exp2_hw(x * kLog2e);
+  float w = 1.0f + e;
+  float lg = log2_hw(w) * kLn2;
+  float r = (w == 1.0f) ? e : lg * (e * rcp_hw(w - 1.0f));
+  return x > 20.0f ? x : r;
+}
+
+// silu(z) = z * sigmoid(z) = z / (1 + e^-z)
+__device__ __forceinline__ float silu_f32(float z) { return z * rcp_hw(1.0f + exp2_hw(-z * kLog2e)); }
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+template <typename IoT>
+struct Io;
+
+template <>
+struct Io<float> {
+  __device__ static __forceinline__ float load1(const float* p) { return *p; }
+  __device__ static __forceinline__ void store1(float* p, float v) { *p = v; }
+  // 8 consecutive elements; p is 16-byte aligned.
+  __device__ static __forceinline__ void load8(const float* p, float out[8]) {
+    float4 a = reinterpret_cast<const float4*>(p)[0];
+    float4 b = reinterpret_cast<const float4*>(p)[1];
+    out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
+    out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
+  }
+  __device__ static __forceinline__ void store8(float* p, const float v[8]) {
+    reinterpret_cast<float4*>(p)[0] = make_float4(v[0], v[1], v[2], v[3]);
+    reinterpret_cast<float4*>(p)[1] = make_float4(v[4], v[5], v[6], v[7]);
+  }
+  // 4 consecutive elements; p is 16-byte aligned.
+  __device__ static __forceinline__ void load4(const float* p, float out[4]) {
+    float4 a = *reinterpret_cast<const float4*>(p);
+    out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
+  }
+};
+
+template <>
+struct Io<bf16_t> {
+  __device__ static __forceinline__ float load1(const bf16_t* p) { return __uint_as_float((uint32_t)*p << 16); }
+  __device__ static __forceinline__ void store1(bf16_t* p, float v) {
+    __bf16 r = (__bf16)v;  // round to nearest even (v_cvt_pk_bf16_f32)
+    *p = __builtin_bit_cast(bf16_t, r);
+  }
+  __device__ static __forceinline__ void load8(const bf16_t* p, float out[8]) {
+    uint4 w = *reinterpret_cast<const uint4*>(p);
+    out[0] = bf16_lo(w.x); out[1] = bf16_hi(w.x); out[2] = bf16_lo(w.y); out[3] = bf16_hi(w.y);
+    out[4] = bf16_lo(w.z); out[5] = bf16_hi(w.z); out[6] = bf16_lo(w.w); out[7] = bf16_hi(w.w);
+  }
+  __device__ static __forceinline__ uint32_t pack2(float lo, float hi) {
+    uint32_t a = __builtin_bit_cast(bf16_t, (__bf16)lo);
+    uint32_t b = __builtin_bit_cast(bf16_t, (__bf16)hi);
+    return a | (b << 16);
+  }
+  __device__ static __forceinline__ void store8(bf16_t* p, const float v[8]) {
+    uint4 w;
+    w.x = pack2(v[0], v[1]); w.y = pack2(v[2], v[3]); w.z = pack2(v[4], v[5]); w.w = pack2(v[6], v[7]);
+    *reinterpret_cast<uint4*>(p) = w;
+  }
+  // 4 consecutive elements; p is 8-byte aligned.
+  __device__ static __forceinline__ void load4(const bf16_t* p, float out[4]) {
+    uint2 w = *reinterpret_cast<const uint2*>(p);
+    out[0] = bf16_lo(w.x); out[1] = bf16_hi(w.x); out[2] = bf16_lo(w.y); out[3] = bf16_hi(w.y);
+  }
+};
+
+// Wave-uniform loads through the scalar data cache.  Reading through the
+// constant address space tells the compiler the memory is not written by this
+// kernel, so a uniform address becomes an s_load into SGPRs (bf16 pairs are
+// widened with scalar shifts) instead of a vector load plus VALU unpacking.
+template <typename T>
+using const_as4 = const __attribute__((address_space(4))) T*;
+
+template <typename IoT>
+struct Uni;
+
+template <>
+struct Uni<float> {
+  // 8 consecutive elements at base + byte_off (4-byte aligned, wave-uniform).
+  __device__ static __forceinline__ void load8(const float* base, uint32_t byte_off, float out[8]) {
+    const_as4<float> q = (const_as4<float>)((const_as4<char>)base + byte_off);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) out[t] = q[t];
+  }
+};
+
+template <>
+struct Uni<bf16_t> {
+  // 8 consecutive elements at base + byte_off (4-byte aligned, wave-uniform).
+  __device__ static __forceinline__ void load8(const bf16_t* base, uint32_t byte_off, float out[8]) {
+    const_as4<uint32_t> q = (const_as4<uint32_t>)((const_as4<char>)base + byte_off);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      uint32_t w = q[t];
+      out[2 * t] = bf16_lo(w);
+      out[2 * t + 1] = bf16_hi(w);
+    }
+  }
+};
+
+// ----------------------------------------------------------------------------
+// Prefill kernels
+// ----------------------------------------------------------------------------
+
+struct ScanArgs {
+  const void* u;
+  const void* delta;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* D;  // may be null
+  const void* z;   // may be null
+  const float* bias;  // may be null
+  const float* h0;    // may be null
+  void* y;
+  float* last_state;  // may be null
+  float* agg_sum;     // [P-1][batch*dim]            scratch, P > 1
+  float* agg_h;       // [P-1][batch*dim][dstate]    scratch, P > 1
+  float* carry;       // [P][batch*dim][dstate]      scratch, P > 1
+  int64_t batch, dim, dstate, seqlen;
+  int64_t groups;    // ceil(dim / 64)
+  int64_t segments;  // P
+  int64_t seg_len;   // tokens per segment, a multiple of kChunk
+};
+
+// Wave-uniform decomposition of a wave index into (segment, batch row, group).
+struct WaveCoord {
+  int64_t s, b, g;
+};
+
+__device__ __forceinline__ int64_t wave_index() {
+  // readfirstlane makes the wave id provably uniform, so everything derived
+  // from it stays in SGPRs and loads indexed by it become scalar loads.
+  int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  return (int64_t)blockIdx.x * kWavesPerBlock + w;
+}
+
+__device__ __forceinline__ WaveCoord decompose(int64_t wave, const ScanArgs& a) {
+  WaveCoord c;
+  c.g = wave % a.groups;
+  int64_t rest = wave / a.groups;
+  c.b = rest % a.batch;
+  c.s = rest / a.batch;
+  return c;
+}
+
+// Per-channel constants loaded once per wave.
+template <int N>
+struct Channel {
+  float A2[N];  // A * log2(e): Abar = exp2(Delta * A2)
+  float Dd;
+  float bias;
+};
+
+template <int N>
+__device__ __forceinline__ void load_channel(const ScanArgs& a, int64_t d, Channel<N>& c) {
+#pragma unroll
+  for (int n = 0; n < N; ++n) c.A2[n] = (n < a.dstate) ? a.A[d * a.dstate + n] * kLog2e : 0.0f;
+  c.Dd = a.D ? a.D[d] : 0.0f;
+  c.bias = a.bias ? a.bias[d] : 0.0f;
+}
+
+template <bool kSoftplus>
+__device__ __forceinline__ float discretize_delta(float raw, float bias) {
+  float v = raw + bias;
+  return kSoftplus ? softplus_f32(v) : v;
+}
+
+// One full chunk of kChunk tokens for every state (dstate == N exactly): h
+// advances, and (kEmit) y accumulates C.h.  Bb/Cb are the batch row's B and C
+// ([dstate][seqlen]); l is the chunk's first token; row_bytes = seqlen * size.
+template <typename IoT, int N, bool kEmit>
+__device__ __forceinline__ void chunk_states(const IoT* __restrict__ Bb, const IoT* __restrict__ Cb,
+                                             uint32_t row_bytes, uint32_t l_bytes, const float A2[N],
+                                             const float dl[kChunk], const float xl[kChunk], float h[N],
+                                             float yv[kChunk]) {
+  // B/C of state n+1 are fetched while state n computes; the scheduling
+  // barriers keep the compiler from hoisting all 2*N scalar loads at once
+  // (which would spill SGPRs), so SGPR pressure stays at two states.
+  float Bc[kChunk], Cc[kChunk], Bn[kChunk], Cn[kChunk];
+  Uni<IoT>::load8(Bb, l_bytes, Bc);
+  if (kEmit) Uni<IoT>::load8(Cb, l_bytes, Cc);
+#pragma unroll
+  for (int n = 0; n < N; ++n) {
+    if (n + 1 < N) {
+      const uint32_t off = (uint32_t)(n + 1) * row_bytes + l_bytes;
+      Uni<IoT>::load8(Bb, off, Bn);
+      if (kEmit) Uni<IoT>::load8(Cb, off, Cn);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    float hn = h[n];
+#pragma unroll
+    for (int t = 0; t < kChunk; ++t) {
+      float abar = exp2_hw(A2[n] * dl[t]);
+      hn = __builtin_fmaf(abar, hn, Bc[t] * xl[t]);
+      if (kEmit) yv[t] = __builtin_fmaf(Cc[t], hn, yv[t]);
+    }
+    h[n] = hn;
+    // Empty register constraints: the state's results must exist here, so the
+    // compiler cannot sink the C.h accumulation below later states (which
+    // would keep all N*kChunk intermediate states alive in VGPRs).
+    asm volatile("" : "+v"(h[n]));
+    if (kEmit) {
+#pragma unroll
+      for (int t = 0; t < kChunk; ++t) asm volatile("" : "+v"(yv[t]));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < kChunk; ++t) {
+      Bc[t] = Bn[t];
+      if (kEmit) Cc[t] = Cn[t];
+    }
+  }
+}
+
+// One token with scalar loads (tails, unaligned shapes).
+template <typename IoT, int N, bool kEmit>
+__device__ __forceinline__ float token_states(const IoT* __restrict__ Bb, const IoT* __restrict__ Cb, int64_t L,
+                                              int64_t dstate, const float A2[N], float dl, float xl, float h[N]) {
+  float yv = 0.0f;
+#pragma unroll
+  for (int n = 0; n < N; ++n) {
+    if (n < dstate) {
+      float abar = exp2_hw(A2[n] * dl);
+      float bv = Io<IoT>::load1(Bb + n * L);
+      h[n] = __builtin_fmaf(abar, h[n], bv * xl);
+      if (kEmit) yv = __builtin_fmaf(Io<IoT>::load1(Cb + n * L), h[n], yv);
+    }
+  }
+  return yv;
+}
+
+template <bool kZ>
+__device__ __forceinline__ float epilogue(float acc, float Dd, float uv, float zv) {
+  float v = __builtin_fmaf(Dd, uv, acc);
+  if (kZ) v *= silu_f32(zv);
+  return v;
+}
+
+// Raw (not yet widened) chunk of u, delta, z for one lane.
+template <typename IoT, bool kZ>
+struct RawChunk {
+  float u[kChunk], dt[kChunk], z[kChunk];
+};
+
+template <typename IoT, bool kZ>
+__device__ __forceinline__ void load_raw(const IoT* ur, const IoT* dr, const IoT* zr, int64_t l,
+                                         RawChunk<IoT, kZ>& c) {
+  Io<IoT>::load8(ur + l, c.u);
+  Io<IoT>::load8(dr + l, c.dt);
+  if (kZ) Io<IoT>::load8(zr + l, c.z);
+}
+
+// Launch 3 (and the only launch when P == 1): scan one segment of 64
+// channels from its carry-in, write y, and (last segment) last_state.
+//   kVec: dstate == N, rows are 16-byte aligned and seqlen % kChunk == 0, so
+//         every chunk is a full vector chunk with B/C in SGPRs.  Otherwise
+//         (N = 16 then bounds a runtime dstate) every token goes through the
+//         scalar path.
+template <typename IoT, int N, bool kZ, bool kSoftplus, bool kVec>
+__global__ __launch_bounds__(kBlockThreads) void scan_kernel(ScanArgs a, int64_t total_waves) {
+  const int64_t wave = wave_index();
+  if (wave >= total_waves) return;
+  const WaveCoord wc = decompose(wave, a);
+  const int lane = threadIdx.x & 63;
+  const int64_t d_raw = wc.g * kWaveThreads + lane;
+  const bool active = d_raw < a.dim;
+  const int64_t d = active ? d_raw : a.dim - 1;  // idle lanes shadow a valid channel, write nothing
+  const int64_t L = a.seqlen;
+  const int64_t bd = a.batch * a.dim;
+  const int64_t ch = wc.b * a.dim + d;
+  const int64_t l0 = wc.s * a.seg_len;
+  const int64_t l1 = min(l0 + a.seg_len, L);
+
+  Channel<N> c;
+  load_channel<N>(a, d, c);
+
+  float h[N];
+  const float* cin = (a.segments > 1) ? a.carry + (wc.s * bd + ch) * a.dstate
+                                      : (a.h0 ? a.h0 + ch * a.dstate : nullptr);
+#pragma unroll
+  for (int n = 0; n < N; ++n) h[n] = (cin && n < a.dstate) ? cin[n] : 0.0f;
+
+  const IoT* ur = static_cast<const IoT*>(a.u) + ch * L;
+  const IoT* dr = static_cast<const IoT*>(a.delta) + ch * L;
+  const IoT* zr = kZ ? static_cast<const IoT*>(a.z) + ch * L : nullptr;
+  IoT* yr = static_cast<IoT*>(a.y) + ch * L;
+  const IoT* Bb = static_cast<const IoT*>(a.B) + wc.b * a.dstate * L;
+  const IoT* Cb = static_cast<const IoT*>(a.C) + wc.b * a.dstate * L;
+  const uint32_t row_bytes = (uint32_t)(L * sizeof(IoT));
+
+  int64_t l = l0;
+  if constexpr (kVec) {
+    RawChunk<IoT, kZ> cur, nxt;
+    if (l < l1) load_raw<IoT, kZ>(ur, dr, zr, l, cur);
+    for (; l < l1; l += kChunk) {
+      if (l + kChunk < l1) load_raw<IoT, kZ>(ur, dr, zr, l + kChunk, nxt);
+      float dl[kChunk], xl[kChunk], yv[kChunk];
+#pragma unroll
+      for (int t = 0; t < kChunk; ++t) {
+        dl[t] = discretize_delta<kSoftplus>(cur.dt[t], c.bias);
+        xl[t] = dl[t] * cur.u[t];
+        yv[t] = 0.0f;
+      }
+      chunk_states<IoT, N, true>(Bb, Cb, row_bytes, (uint32_t)(l * sizeof(IoT)), c.A2, dl, xl, h, yv);
+#pragma unroll
+      for (int t = 0; t < kChunk; ++t) yv[t] = epilogue<kZ>(yv[t], c.Dd, cur.u[t], kZ ? cur.z[t] : 0.0f);
+      if (active) Io<IoT>::store8(yr + l, yv);
+      cur = nxt;
+    }
+  } else {
+    for (; l < l1; ++l) {
+      float uv = Io<IoT>::load1(ur + l);
+      float dl = discretize_delta<kSoftplus>(Io<IoT>::load1(dr + l), c.bias);
+      float acc = token_states<IoT, N, true>(Bb + l, Cb + l, L, a.dstate, c.A2, dl, dl * uv, h);
+      float v = epilogue<kZ>(acc, c.Dd, uv, kZ ? Io<IoT>::load1(zr + l) : 0.0f);
+      if (active) Io<IoT>::store1(yr + l, v);
+    }
+  }
+
+  if (a.last_state && active && wc.s == a.segments - 1) {
+#pragma unroll
+    for (int n = 0; n < N; ++n)
+      if (n < a.dstate) a.last_state[ch * a.dstate + n] = h[n];
+  }
+}
+
+// Launch 1: every segment but the last scans from a zero state and records
+// (sum of Delta, end state).  The segment's decay is a = exp(A * sum Delta).
+template <typename IoT, int N, bool kSoftplus, bool kVec>
+__global__ __launch_bounds__(kBlockThreads) void aggregate_kernel(ScanArgs a, int64_t total_waves) {
+  const int64_t wave = wave_index();
+  if (wave >= total_waves) return;
+  const WaveCoord wc = decompose(wave, a);
+  const int lane = threadIdx.x & 63;
+  const int64_t d_raw = wc.g * kWaveThreads + lane;
+  const bool active = d_raw < a.dim;
+  const int64_t d = active ? d_raw : a.dim - 1;
+  const int64_t L = a.seqlen;
+  const int64_t bd = a.batch * a.dim;
+  const int64_t ch = wc.b * a.dim + d;
+  const int64_t l0 = wc.s * a.seg_len;
+  const int64_t l1 = min(l0 + a.seg_len, L);
+
+  Channel<N> c;
+  load_channel<N>(a, d, c);
+  float h[N];
+#pragma unroll
+  for (int n = 0; n < N; ++n) h[n] = 0.0f;
+  float dsum = 0.0f;
+
+  const IoT* ur = static_cast<const IoT*>(a.u) + ch * L;
+  const IoT* dr = static_cast<const IoT*>(a.delta) + ch * L;
+  const IoT* Bb = static_cast<const IoT*>(a.B) + wc.b * a.dstate * L;
+  const uint32_t row_bytes = (uint32_t)(L * sizeof(IoT));
+
+  int64_t l = l0;
+  if constexpr (kVec) {
+    RawChunk<IoT, false> cur, nxt;
+    if (l < l1) load_raw<IoT, false>(ur, dr, nullptr, l, cur);
+    for (; l < l1; l += kChunk) {
+      if (l + kChunk < l1) load_raw<IoT, false>(ur, dr, nullptr, l + kChunk, nxt);
+      float dl[kChunk], xl[kChunk], unused[kChunk];
+#pragma unroll
+      for (int t = 0; t < kChunk; ++t) {
+        dl[t] = discretize_delta<kSoftplus>(cur.dt[t], c.bias);
+        xl[t] = dl[t] * cur.u[t];
+        dsum += dl[t];
+      }
+      chunk_states<IoT, N, false>(Bb, nullptr, row_bytes, (uint32_t)(l * sizeof(IoT)), c.A2, dl, xl, h, unused);
+      cur = nxt;
+    }
+  } else {
+    for (; l < l1; ++l) {
+      float uv = Io<IoT>::load1(ur + l);
+      float dl = discretize_delta<kSoftplus>(Io<IoT>::load1(dr + l), c.bias);
+      dsum += dl;
+      token_states<IoT, N, false>(Bb + l, nullptr, L, a.dstate, c.A2, dl, dl * uv, h);
+    }
+  }
+
+  if (active) {
+    a.agg_sum[wc.s * bd + ch] = dsum;
+#pragma unroll
+    for (int n = 0; n < N; ++n)
+      if (n < a.dstate) a.agg_h[(wc.s * bd + ch) * a.dstate + n] = h[n];
+  }
+}
+
+// Launch 2: one thread per (channel, state) folds the segment aggregates in
+// sequence order: carry[0] = h0, carry[s+1] = a_s * carry[s] + b_s.
+__global__ __launch_bounds__(kBlockThreads) void carry_kernel(ScanArgs a) {
+  const int64_t bd = a.batch * a.dim;
+  const int64_t idx = (int64_t)blockIdx.x * kBlockThreads + threadIdx.x;
+  if (idx >= bd * a.dstate) return;
+  const int64_t ch = idx / a.dstate;
+  const int64_t n = idx % a.dstate;
+  const int64_t d = ch % a.dim;
+  const float A2 = a.A[d * a.dstate + n] * kLog2e;
+  float h = a.h0 ? a.h0[idx] : 0.0f;
+  const int64_t P = a.segments;
+  int64_t s = 0;
+  // Aggregates do not depend on the running carry: fetch 8 segments ahead.
+  for (; s + 8 <= P - 1; s += 8) {
+    float sums[8], hs[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      sums[j] = a.agg_sum[(s + j) * bd + ch];
+      hs[j] = a.agg_h[(s + j) * bd * a.dstate + idx];
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      a.carry[(s + j) * bd * a.dstate + idx] = h;
+      h = __builtin_fmaf(exp2_hw(A2 * sums[j]), h, hs[j]);
+    }
+  }
+  for (; s < P - 1; ++s) {
+    a.carry[s * bd * a.dstate + idx] = h;
+    h = __builtin_fmaf(exp2_hw(A2 * a.agg_sum[s * bd + ch]), h, a.agg_h[s * bd * a.dstate + idx]);
+  }
+  a.carry[(P - 1) * bd * a.dstate + idx] = h;
+}
+
+// ----------------------------------------------------------------------------
+// Decode kernel
+// ----------------------------------------------------------------------------
+
+struct UpdateArgs {
+  float* state;
+  const void* u;
+  const void* delta;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* D;
+  const void* z;
+  const float* bias;
+  void* y;
+  int64_t batch, dim, dstate;
+};
+
+// N in {4, 8, 16}: N/4 lanes per channel, four states per lane.  Groups of
+// N/4 lanes are aligned inside the wave, so the shuffle stays in the group.
+template <typename IoT, int N, bool kZ, bool kSoftplus>
+__global__ __launch_bounds__(kBlockThreads) void state_update_kernel(UpdateArgs a) {
+  constexpr int kLanes = N / 4;
+  const int64_t bd = a.batch * a.dim;
+  const int64_t tid = (int64_t)blockIdx.x * kBlockThreads + threadIdx.x;
+  const int64_t ch_raw = tid / kLanes;
+  const int q = (int)(tid % kLanes);
+  const bool active = ch_raw < bd;
+  const int64_t ch = active ? ch_raw : bd - 1;
+  const int64_t b = ch / a.dim, d = ch % a.dim;
+
+  float h[4], A4[4], B4[4], C4[4];
+  Io<float>::load4(a.state + ch * N + 4 * q, h);
+  Io<float>::load4(a.A + d * N + 4 * q, A4);
+  Io<IoT>::load4(static_cast<const IoT*>(a.B) + b * N + 4 * q, B4);
+  Io<IoT>::load4(static_cast<const IoT*>(a.C) + b * N + 4 * q, C4);
+  const float uv = Io<IoT>::load1(static_cast<const IoT*>(a.u) + ch);
+  const float dl = discretize_delta<kSoftplus>(Io<IoT>::load1(static_cast<const IoT*>(a.delta) + ch),
+                                               a.bias ? a.bias[d] : 0.0f);
+  const float xl = dl * uv;
+  float acc = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    float abar = exp2_hw(A4[j] * kLog2e * dl);
+    h[j] = __builtin_fmaf(abar, h[j], B4[j] * xl);
+    acc = __builtin_fmaf(C4[j], h[j], acc);
+  }
+#pragma unroll
+  for (int off = 1; off < kLanes; off <<= 1) acc += __shfl_xor(acc, off, kLanes);
+  if (active) {
+    *reinterpret_cast<float4*>(a.state + ch * N + 4 * q) = make_float4(h[0], h[1], h[2], h[3]);
+    if (q == 0) {
+      float zv = kZ ? Io<IoT>::load1(static_cast<const IoT*>(a.z) + ch) : 0.0f;
+      Io<IoT>::store1(static_cast<IoT*>(a.y) + ch, epilogue<kZ>(acc, a.D ? a.D[d] : 0.0f, uv, zv));
+    }
+  }
+}
+
+// Any dstate <= 16 and any alignment: one lane per channel, scalar loads.
+template <typename IoT, bool kZ, bool kSoftplus>
+__global__ __launch_bounds__(kBlockThreads) void state_update_generic_kernel(UpdateArgs a) {
+  const int64_t bd = a.batch * a.dim;
+  const int64_t ch = (int64_t)blockIdx.x * kBlockThreads + threadIdx.x;
+  if (ch >= bd) return;
+  const int64_t b = ch / a.dim, d = ch % a.dim;
+  const float uv = Io<IoT>::load1(static_cast<const IoT*>(a.u) + ch);
+  const float dl = discretize_delta<kSoftplus>(Io<IoT>::load1(static_cast<const IoT*>(a.delta) + ch),
+                                               a.bias ? a.bias[d] : 0.0f);
+  const float xl = dl * uv;
+  float acc = 0.0f;
+  for (int64_t n = 0; n < a.dstate; ++n) {
+    float abar = exp2_hw(a.A[d * a.dstate + n] * kLog2e * dl);
+    float hn = a.state[ch * a.dstate + n];
+    hn = __builtin_fmaf(abar, hn, Io<IoT>::load1(static_cast<const IoT*>(a.B) + b * a.dstate + n) * xl);
+    a.state[ch * a.dstate + n] = hn;
+    acc = __builtin_fmaf(Io<IoT>::load1(static_cast<const IoT*>(a.C) + b * a.dstate + n), hn, acc);
+  }
+  float zv = kZ ? Io<IoT>::load1(static_cast<const IoT*>(a.z) + ch) : 0.0f;
+  Io<IoT>::store1(static_cast<IoT*>(a.y) + ch, epilogue<kZ>(acc, a.D ? a.D[d] : 0.0f, uv, zv));
+}
+
+// ----------------------------------------------------------------------------
+// Host side: validation, planning, dispatch
+// ----------------------------------------------------------------------------
+
+thread_local int g_last_hip_error = 0;
+
+ssm_status_t hip_fail(hipError_t e) {
+  g_last_hip_error = (int)e;
+  return SSM_ERR_HIP;
+}
+
+bool mul_ok(int64_t a, int64_t b, int64_t* out) { return !__builtin_mul_overflow(a, b, out); }
+
+size_t io_size(ssm_dtype_t io) { return io == SSM_BF16 ? 2 : 4; }
+
+bool aligned(const void* p, size_t k) { return (reinterpret_cast<uintptr_t>(p) % k) == 0; }
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range span(const void* p, int64_t bytes) {
+  uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  return Range{lo, lo + (uintptr_t)bytes};
+}
+
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+// Sizes of one call in elements.
+struct Shape {
+  int64_t bd, bdl, bnl, dn, bdn;
+};
+
+ssm_status_t shape_of(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, ssm_dtype_t io, Shape* s) {
+  if (io != SSM_F32 && io != SSM_BF16) return SSM_ERR_DTYPE;
+  if (batch < 1 || dim < 1 || dstate < 1 || seqlen < 1) return SSM_ERR_SHAPE;
+  if (dstate > 16) return SSM_ERR_DSTATE_UNSUPPORTED;
+  int64_t bn, bytes;
+  if (!mul_ok(batch, dim, &s->bd) || !mul_ok(s->bd, seqlen, &s->bdl) || !mul_ok(batch, dstate, &bn) ||
+      !mul_ok(bn, seqlen, &s->bnl) || !mul_ok(dim, dstate, &s->dn) || !mul_ok(s->bd, dstate, &s->bdn) ||
+      !mul_ok(s->bdl, 8, &bytes) || !mul_ok(s->bnl, 8, &bytes) || !mul_ok(s->bdn, 64, &bytes))
+    return SSM_ERR_SHAPE;
+  return SSM_OK;
+}
+
+struct Plan {
+  int64_t groups, segments, seg_len;
+  int64_t scratch_bytes;
+};
+
+constexpr int64_t kTargetWaves = 2048;  // two waves per SIMD on 256 CUs
+constexpr int64_t kMinSegment = 256;    // tokens; keeps the aggregate pass amortised
+
+Plan make_plan(const Shape& s, int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen) {
+  Plan p;
+  p.groups = (dim + kWaveThreads - 1) / kWaveThreads;
+  int64_t base = batch * p.groups;
+  int64_t want = (kTargetWaves + base - 1) / base;
+  int64_t seg = (seqlen + want - 1) / want;
+  seg = ((seg + kChunk - 1) / kChunk) * kChunk;
+  seg = std::max(seg, kMinSegment);
+  if (seg >= seqlen) {
+    p.segments = 1;
+    p.seg_len = seqlen;
+  } else {
+    p.segments = (seqlen + seg - 1) / seg;
+    p.seg_len = seg;
+  }
+  if (p.segments > 1) {
+    int64_t P = p.segments;
+    p.scratch_bytes = 4 * ((P - 1) * s.bd + (P - 1) * s.bdn + P * s.bdn);
+  } else {
+    p.scratch_bytes = 0;
+  }
+  (void)dstate;
+  return p;
+}
+
+// Per-device pool for the scratch memory of segmented scans (stream ordered,
+// kept warm between calls).
+struct PoolCache {
+  std::mutex mu;
+  hipMemPool_t pools[64] = {};
+};
+
+PoolCache& pool_cache() {
+  static PoolCache c;
+  return c;
+}
+
+hipError_t get_pool(hipMemPool_t* out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  PoolCache& c = pool_cache();
+  std::lock_guard<std::mutex> lock(c.mu);
+  if (!c.pools[dev]) {
+    hipMemPoolProps props;
+    std::memset(&props, 0, sizeof(props));
+    props.allocType = hipMemAllocationTypePinned;
+    props.location.type = hipMemLocationTypeDevice;
+    props.location.id = dev;
+    hipMemPool_t pool;
+    e = hipMemPoolCreate(&pool, &props);
+    if (e != hipSuccess) return e;
+    uint64_t keep = UINT64_MAX;
+    e = hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep);
+    if (e != hipSuccess) return e;
+    c.pools[dev] = pool;
+  }
+  *out = c.pools[dev];
+  return hipSuccess;
+}
+
+template <typename IoT, int N, bool kZ, bool kSp, bool kVec>
+hipError_t launch_scan_t(const ScanArgs& a, const Plan& p, hipStream_t st) {
+  int64_t waves_scan = a.batch * p.groups * p.segments;
+  if (p.segments > 1) {
+    int64_t waves_agg = a.batch * p.groups * (p.segments - 1);
+    int64_t blocks = (waves_agg + kWavesPerBlock - 1) / kWavesPerBlock;
+    hipLaunchKernelGGL((aggregate_kernel<IoT, N, kSp, kVec>), dim3((unsigned)blocks), dim3(kBlockThreads), 0, st, a,
+                       waves_agg);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    int64_t threads = a.batch * a.dim * a.dstate;
+    hipLaunchKernelGGL(carry_kernel, dim3((unsigned)((threads + kBlockThreads - 1) / kBlockThreads)),
+                       dim3(kBlockThreads), 0, st, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  int64_t blocks = (waves_scan + kWavesPerBlock - 1) / kWavesPerBlock;
+  hipLaunchKernelGGL((scan_kernel<IoT, N, kZ, kSp, kVec>), dim3((unsigned)blocks), dim3(kBlockThreads), 0, st, a,
+                     waves_scan);
+  return hipGetLastError();
+}
+
+template <typename IoT, int N, bool kVec>
+hipError_t launch_scan_f(const ScanArgs& a, const Plan& p, hipStream_t st, bool sp) {
+  if (a.z) return sp ? launch_scan_t<IoT, N, true, true, kVec>(a, p, st) : launch_scan_t<IoT, N, true, false, kVec>(a, p, st);
+  return sp ? launch_scan_t<IoT, N, false, true, kVec>(a, p, st) : launch_scan_t<IoT, N, false, false, kVec>(a, p, st);
+}
+
+// Vector kernels exist for dstate in {4, 8, 16}; every other case runs the
+// scalar-token kernel instantiated for up to 16 states.
+template <typename IoT>
+hipError_t launch_scan(const ScanArgs& a, const Plan& p, hipStream_t st, bool vec, bool sp) {
+  if (vec) {
+    if (a.dstate == 4) return launch_scan_f<IoT, 4, true>(a, p, st, sp);
+    if (a.dstate == 8) return launch_scan_f<IoT, 8, true>(a, p, st, sp);
+    if (a.dstate == 16) return launch_scan_f<IoT, 16, true>(a, p, st, sp);
+  }
+  return launch_scan_f<IoT, 16, false>(a, p, st, sp);
+}
+
+template <typename IoT, int N, bool kZ, bool kSp>
+hipError_t launch_update_t(const UpdateArgs& a, hipStream_t st, bool generic) {
+  const int64_t bd = a.batch * a.dim;
+  if (generic) {
+    int64_t blocks = (bd + kBlockThreads - 1) / kBlockThreads;
+    hipLaunchKernelGGL((state_update_generic_kernel<IoT, kZ, kSp>), dim3((unsigned)blocks), dim3(kBlockThreads), 0,
+                       st, a);
+  } else {
+    int64_t threads = bd * (N / 4);
+    int64_t blocks = (threads + kBlockThreads - 1) / kBlockThreads;
+    hipLaunchKernelGGL((state_update_kernel<IoT, N, kZ, kSp>), dim3((unsigned)blocks), dim3(kBlockThreads), 0, st,
+                       a);
+  }
+  return hipGetLastError();
+}
+
+template <typename IoT, int N>
+hipError_t launch_update_n(const UpdateArgs& a, hipStream_t st, bool generic, bool sp) {
+  if (a.z) return sp ? launch_update_t<IoT, N, true, true>(a, st, generic) : launch_update_t<IoT, N, true, false>(a, st, generic);
+  return sp ? launch_update_t<IoT, N, false, true>(a, st, generic) : launch_update_t<IoT, N, false, false>(a, st, generic);
+}
+
+template <typename IoT>
+hipError_t launch_update(const UpdateArgs& a, hipStream_t st, bool generic, bool sp) {
+  switch (a.dstate) {
+    case 4: return launch_update_n<IoT, 4>(a, st, generic, sp);
+    case 8: return launch_update_n<IoT, 8>(a, st, generic, sp);
+    case 16: return launch_update_n<IoT, 16>(a, st, generic, sp);
+    default: return launch_update_n<IoT, 4>(a, st, true, sp);
+  }
+}
+
+}  // namespace
+
+// ----------------------------------------------------------------------------
+// C ABI
+// ----------------------------------------------------------------------------
+
+extern "C" {
+
+int ssm_abi_version(void) { return SSM_ABI_VERSION; }
+
+int ssm_last_hip_error(void) { return g_last_hip_error; }
+
+const char* ssm_status_string(ssm_status_t s) {
+  switch (s) {
+    case SSM_OK: return "ok";
+    case SSM_ERR_NULL: return "a required pointer is NULL";
+    case SSM_ERR_SHAPE: return "invalid size (batch, dim, seqlen and dstate must be >= 1 and their products must fit in 64 bits)";
+    case SSM_ERR_DSTATE_UNSUPPORTED: return "dstate above 16 is not supported";
+    case SSM_ERR_DTYPE: return "unknown io dtype";
+    case SSM_ERR_ALIGN: return "a pointer is not aligned to its element size";
+    case SSM_ERR_ALIAS: return "an output buffer overlaps an input buffer";
+    case SSM_ERR_HIP: return "a HIP runtime call failed (see ssm_last_hip_error)";
+  }
+  return "unknown status";
+}
+
+ssm_status_t ssm_scan_fwd_plan(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, ssm_dtype_t io,
+                               int64_t* segments, int64_t* segment_len, int64_t* scratch_bytes) {
+  Shape sh;
+  ssm_status_t st = shape_of(batch, dim, dstate, seqlen, io, &sh);
+  if (st != SSM_OK) return st;
+  Plan p = make_plan(sh, batch, dim, dstate, seqlen);
+  if (segments) *segments = p.segments;
+  if (segment_len) *segment_len = p.seg_len;
+  if (scratch_bytes) *scratch_bytes = p.scratch_bytes;
+  return SSM_OK;
+}
+
+ssm_status_t ssm_scan_fwd(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, ssm_dtype_t io, const void* u,
+                          const void* delta, const float* A, const void* B, const void* C, const float* D,
+                          const void* z, const float* delta_bias, int softplus_flag, const float* h0, void* y,
+                          float* last_state, struct ihipStream_t* stream) {
+  Shape sh;
+  ssm_status_t st = shape_of(batch, dim, dstate, seqlen, io, &sh);
+  if (st != SSM_OK) return st;
+  if (!u || !delta || !A || !B || !C || !y) return SSM_ERR_NULL;
+  const size_t es = io_size(io);
+  const void* io_ptrs[] = {u, delta, B, C, z, y};
+  for (const void* p : io_ptrs)
+    if (p && !aligned(p, es)) return SSM_ERR_ALIGN;
+  const void* f_ptrs[] = {A, D, delta_bias, h0, last_state};
+  for (const void* p : f_ptrs)
+    if (p && !aligned(p, 4)) return SSM_ERR_ALIGN;
+
+  // Outputs must not overlap inputs; h0 may be exactly last_state.
+  const Range ry = span(y, sh.bdl * (int64_t)es);
+  const Range ins[] = {span(u, sh.bdl * (int64_t)es), span(delta, sh.bdl * (int64_t)es),
+                       span(B, sh.bnl * (int64_t)es), span(C, sh.bnl * (int64_t)es),
+                       z ? span(z, sh.bdl * (int64_t)es) : Range{0, 0}, span(A, sh.dn * 4),
+                       D ? span(D, dim * 4) : Range{0, 0}, delta_bias ? span(delta_bias, dim * 4) : Range{0, 0},
+                       h0 ? span(h0, sh.bdn * 4) : Range{0, 0}};
+  for (const Range& r : ins)
+    if (r.hi > r.lo && overlap(ry, r)) return SSM_ERR_ALIAS;
+  if (last_state) {
+    const Range rl = span(last_state, sh.bdn * 4);
+    if (overlap(rl, ry)) return SSM_ERR_ALIAS;
+    for (int i = 0; i < 8; ++i)
+      if (ins[i].hi > ins[i].lo && overlap(rl, ins[i])) return SSM_ERR_ALIAS;
+    if (h0 && h0 != last_state && overlap(rl, ins[8])) return SSM_ERR_ALIAS;
+  }
+
+  const Plan plan = make_plan(sh, batch, dim, dstate, seqlen);
+  // Vector path: whole 16-byte chunks on every row, and B/C batch slabs
+  // addressable with 32-bit byte offsets.
+  const bool vec = (seqlen % kChunk == 0) && aligned(u, 16) && aligned(delta, 16) && aligned(y, 16) &&
+                   (!z || aligned(z, 16)) && aligned(B, 16) && aligned(C, 16) &&
+                   dstate * seqlen * (int64_t)es < ((int64_t)1 << 31);
+
+  ScanArgs a;
+  a.u = u; a.delta = delta; a.A = A; a.B = B; a.C = C; a.D = D; a.z = z; a.bias = delta_bias; a.h0 = h0;
+  a.y = y; a.last_state = last_state; a.agg_sum = nullptr; a.agg_h = nullptr; a.carry = nullptr;
+  a.batch = batch; a.dim = dim; a.dstate = dstate; a.seqlen = seqlen;
+  a.groups = plan.groups; a.segments = plan.segments; a.seg_len = plan.seg_len;
+
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  void* scratch = nullptr;
+  if (plan.scratch_bytes > 0) {
+    hipMemPool_t pool;
+    hipError_t e = get_pool(&pool);
+    if (e != hipSuccess) return hip_fail(e);
+    e = hipMallocFromPoolAsync(&scratch, (size_t)plan.scratch_bytes, pool, hs);
+    if (e != hipSuccess) return hip_fail(e);
+    float* f = static_cast<float*>(scratch);
+    const int64_t P = plan.segments;
+    a.agg_sum = f;
+    a.agg_h = f + (P - 1) * sh.bd;
+    a.carry = a.agg_h + (P - 1) * sh.bdn;
+  }
+  const bool sp = softplus_flag != 0;
+  hipError_t e = (io == SSM_BF16) ? launch_scan<bf16_t>(a, plan, hs, vec, sp)
+                                  : launch_scan<float>(a, plan, hs, vec, sp);
+  if (scratch) {
+    hipError_t ef = hipFreeAsync(scratch, hs);
+    if (e == hipSuccess) e = ef;
+  }
+  if (e != hipSuccess) return hip_fail(e);
+  return SSM_OK;
+}
+
+ssm_status_t ssm_state_update(int64_t batch, int64_t dim, int64_t dstate, ssm_dtype_t io, float* state, const void* u,
+                              const void* delta, const float* A, const void* B, const void* C, const float* D,
+                              const void* z, const float* delta_bias, int softplus_flag, void* y,
+                              struct ihipStream_t* stream) {
+  Shape sh;
+  ssm_status_t st = shape_of(batch, dim, dstate, 1, io, &sh);
+  if (st != SSM_OK) return st;
+  if (!state || !u || !delta || !A || !B || !C || !y) return SSM_ERR_NULL;
+  const size_t es = io_size(io);
+  const void* io_ptrs[] = {u, delta, B, C, z, y};
+  for (const void* p : io_ptrs)
+    if (p && !aligned(p, es)) return SSM_ERR_ALIGN;
+  const void* f_ptrs[] = {state, A, D, delta_bias};
+  for (const void* p : f_ptrs)
+    if (p && !aligned(p, 4)) return SSM_ERR_ALIGN;
+
+  const Range ry = span(y, sh.bd * (int64_t)es);
+  const Range rs = span(state, sh.bdn * 4);
+  const Range ins[] = {span(u, sh.bd * (int64_t)es), span(delta, sh.bd * (int64_t)es),
+                       span(B, batch * dstate * (int64_t)es), span(C, batch * dstate * (int64_t)es),
+                       z ? span(z, sh.bd * (int64_t)es) : Range{0, 0}, span(A, sh.dn * 4),
+                       D ? span(D, dim * 4) : Range{0, 0}, delta_bias ? span(delta_bias, dim * 4) : Range{0, 0}};
+  if (overlap(ry, rs)) return SSM_ERR_ALIAS;
+  for (const Range& r : ins) {
+    if (r.hi <= r.lo) continue;
+    if (overlap(ry, r) || overlap(rs, r)) return SSM_ERR_ALIAS;
+  }
+
+  UpdateArgs a;
+  a.state = state; a.u = u; a.delta = delta; a.A = A; a.B = B; a.C = C; a.D = D; a.z = z; a.bias = delta_bias;
+  a.y = y; a.batch = batch; a.dim = dim; a.dstate = dstate;
+  const size_t bc_align = (io == SSM_BF16) ? 8 : 16;
+  const bool generic = !(dstate == 4 || dstate == 8 || dstate == 16) || !aligned(state, 16) || !aligned(A, 16) ||
+                       !aligned(B, bc_align) || !aligned(C, bc_align);
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  const bool sp = softplus_flag != 0;
+  hipError_t e = (io == SSM_BF16) ? launch_update<bf16_t>(a, hs, generic, sp) : launch_update<float>(a, hs, generic, sp);
+  if (e != hipSuccess) return hip_fail(e);
+  return SSM_OK;
+}
+
+}  // extern "C"
