@@ -151,27 +151,30 @@ using const_as4 = const __attribute__((address_space(4))) T*;
 template <typename IoT>
 struct Uni;
 
+// Raw words of 8 consecutive elements: 8 fp32 values or 4 packed bf16 pairs.
+// They stay packed in SGPRs until the compute loop widens them (elem), so a
+// prefetched group of bf16 rows costs half the SGPRs.
 template <>
 struct Uni<float> {
-  // 8 consecutive elements at base + byte_off (4-byte aligned, wave-uniform).
-  __device__ static __forceinline__ void load8(const float* base, uint32_t byte_off, float out[8]) {
-    const_as4<float> q = (const_as4<float>)((const_as4<char>)base + byte_off);
+  static constexpr int kWords = 8;
+  __device__ static __forceinline__ void load8(const float* base, uint32_t byte_off, uint32_t w[kWords]) {
+    const_as4<uint32_t> q = (const_as4<uint32_t>)((const_as4<char>)base + byte_off);
 #pragma unroll
-    for (int t = 0; t < 8; ++t) out[t] = q[t];
+    for (int t = 0; t < kWords; ++t) w[t] = q[t];
   }
+  __device__ static __forceinline__ float elem(const uint32_t w[kWords], int t) { return __uint_as_float(w[t]); }
 };
 
 template <>
 struct Uni<bf16_t> {
-  // 8 consecutive elements at base + byte_off (4-byte aligned, wave-uniform).
-  __device__ static __forceinline__ void load8(const bf16_t* base, uint32_t byte_off, float out[8]) {
+  static constexpr int kWords = 4;
+  __device__ static __forceinline__ void load8(const bf16_t* base, uint32_t byte_off, uint32_t w[kWords]) {
     const_as4<uint32_t> q = (const_as4<uint32_t>)((const_as4<char>)base + byte_off);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      uint32_t w = q[t];
-      out[2 * t] = bf16_lo(w);
-      out[2 * t + 1] = bf16_hi(w);
-    }
+    for (int t = 0; t < kWords; ++t) w[t] = q[t];
+  }
+  __device__ static __forceinline__ float elem(const uint32_t w[kWords], int t) {
+    return (t & 1) ? bf16_hi(w[t >> 1]) : bf16_lo(w[t >> 1]);
   }
 };
 
@@ -251,42 +254,61 @@ __device__ __forceinline__ void chunk_states(const IoT* __restrict__ Bb, const I
                                              uint32_t row_bytes, uint32_t l_bytes, const float A2[N],
                                              const float dl[kChunk], const float xl[kChunk], float h[N],
                                              float yv[kChunk]) {
-  // B/C of state n+1 are fetched while state n computes; the scheduling
-  // barriers keep the compiler from hoisting all 2*N scalar loads at once
-  // (which would spill SGPRs), so SGPR pressure stays at two states.
-  float Bc[kChunk], Cc[kChunk], Bn[kChunk], Cn[kChunk];
-  Uni<IoT>::load8(Bb, l_bytes, Bc);
-  if (kEmit) Uni<IoT>::load8(Cb, l_bytes, Cc);
+  // States are processed in groups of G; the B/C rows of group g+1 are
+  // fetched (scalar loads into SGPRs) while group g computes, so a scalar
+  // cache miss has a whole group of work to hide behind.  The scheduling
+  // barriers stop the compiler from hoisting every load of the chunk at once
+  // (which would spill SGPRs).  G keeps two groups within the SGPR budget:
+  // bf16 rows are 4 packed SGPRs per 8 tokens, fp32 rows 8.
+  constexpr int G = (sizeof(IoT) == 2) ? 4 : 2;
+  constexpr int W = Uni<IoT>::kWords;
+  static_assert(N % G == 0, "state count must be a multiple of the group size");
+  uint32_t Bc[G][W], Cc[G][W], Bn[G][W], Cn[G][W];
 #pragma unroll
-  for (int n = 0; n < N; ++n) {
-    if (n + 1 < N) {
-      const uint32_t off = (uint32_t)(n + 1) * row_bytes + l_bytes;
-      Uni<IoT>::load8(Bb, off, Bn);
-      if (kEmit) Uni<IoT>::load8(Cb, off, Cn);
+  for (int j = 0; j < G; ++j) {
+    const uint32_t off = (uint32_t)j * row_bytes + l_bytes;
+    Uni<IoT>::load8(Bb, off, Bc[j]);
+    if (kEmit) Uni<IoT>::load8(Cb, off, Cc[j]);
+  }
+#pragma unroll
+  for (int g = 0; g < N; g += G) {
+    if (g + G < N) {
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        const uint32_t off = (uint32_t)(g + G + j) * row_bytes + l_bytes;
+        Uni<IoT>::load8(Bb, off, Bn[j]);
+        if (kEmit) Uni<IoT>::load8(Cb, off, Cn[j]);
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
-    float hn = h[n];
 #pragma unroll
-    for (int t = 0; t < kChunk; ++t) {
-      float abar = exp2_hw(A2[n] * dl[t]);
-      hn = __builtin_fmaf(abar, hn, Bc[t] * xl[t]);
-      if (kEmit) yv[t] = __builtin_fmaf(Cc[t], hn, yv[t]);
+    for (int j = 0; j < G; ++j) {
+      const int n = g + j;
+      float hn = h[n];
+#pragma unroll
+      for (int t = 0; t < kChunk; ++t) {
+        float abar = exp2_hw(A2[n] * dl[t]);
+        hn = __builtin_fmaf(abar, hn, Uni<IoT>::elem(Bc[j], t) * xl[t]);
+        if (kEmit) yv[t] = __builtin_fmaf(Uni<IoT>::elem(Cc[j], t), hn, yv[t]);
+      }
+      h[n] = hn;
+      // Empty register constraints: the group's results must exist here, so
+      // the compiler cannot sink the C.h accumulation below later groups
+      // (which would keep N*kChunk intermediate states alive in VGPRs).
+      asm volatile("" : "+v"(h[n]));
     }
-    h[n] = hn;
-    // Empty register constraints: the state's results must exist here, so the
-    // compiler cannot sink the C.h accumulation below later states (which
-    // would keep all N*kChunk intermediate states alive in VGPRs).
-    asm volatile("" : "+v"(h[n]));
     if (kEmit) {
 #pragma unroll
       for (int t = 0; t < kChunk; ++t) asm volatile("" : "+v"(yv[t]));
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int t = 0; t < kChunk; ++t) {
-      Bc[t] = Bn[t];
-      if (kEmit) Cc[t] = Cn[t];
-    }
+    for (int j = 0; j < G; ++j)
+#pragma unroll
+      for (int t = 0; t < W; ++t) {
+        Bc[j][t] = Bn[j][t];
+        if (kEmit) Cc[j][t] = Cn[j][t];
+      }
   }
 }
 
@@ -314,18 +336,122 @@ __device__ __forceinline__ float epilogue(float acc, float Dd, float uv, float z
   return v;
 }
 
-// Raw (not yet widened) chunk of u, delta, z for one lane.
-template <typename IoT, bool kZ>
-struct RawChunk {
-  float u[kChunk], dt[kChunk], z[kChunk];
+// One 128-byte line of one row per lane, as 32 raw words (32 fp32 tokens or
+// 64 bf16 tokens).  A lane always fetches or writes a whole line at once, so
+// each L2 line is requested once: consuming a row 16 bytes at a time across
+// many iterations lets the line be evicted between visits and refetched.
+// The line is consumed in 8-token sub-chunks with static register indices;
+// bf16 lines take two passes of four sub-chunks with a register rotation in
+// between, which keeps the loop body at four sub-chunks of code.
+template <typename IoT>
+struct Line {
+  static constexpr int kTokens = 128 / (int)sizeof(IoT);                 // 32 fp32, 64 bf16
+  static constexpr int kWordsPerChunk = kChunk * (int)sizeof(IoT) / 4;  // 8 fp32, 4 bf16
+  static constexpr int kChunksPerPass = 4;
+  static constexpr int kPasses = kTokens / (kChunk * kChunksPerPass);     // 1 fp32, 2 bf16
+  static constexpr int kPassWords = kChunksPerPass * kWordsPerChunk;      // 32 fp32, 16 bf16
+  static constexpr int kPiecesPerChunk = kChunk * (int)sizeof(IoT) / 16;  // 16-byte pieces: 2 fp32, 1 bf16
+
+  // The first `pieces` 16-byte pieces of the line at p (16-byte aligned); the
+  // rest are left as zero and never read from memory.
+  __device__ static __forceinline__ void load(const IoT* p, int pieces, uint32_t w[32]) {
+    const uint4* q = reinterpret_cast<const uint4*>(p);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (j < pieces) v = q[j];
+      w[4 * j] = v.x; w[4 * j + 1] = v.y; w[4 * j + 2] = v.z; w[4 * j + 3] = v.w;
+    }
+  }
+  __device__ static __forceinline__ void store(IoT* p, int pieces, const uint32_t w[32]) {
+    uint4* q = reinterpret_cast<uint4*>(p);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (j < pieces) q[j] = make_uint4(w[4 * j], w[4 * j + 1], w[4 * j + 2], w[4 * j + 3]);
+  }
+  // Widen the 8 tokens whose words start at w.
+  __device__ static __forceinline__ void unpack(const uint32_t* w, float out[kChunk]) {
+    if constexpr (sizeof(IoT) == 4) {
+#pragma unroll
+      for (int t = 0; t < kChunk; ++t) out[t] = __uint_as_float(w[t]);
+    } else {
+#pragma unroll
+      for (int t = 0; t < kChunk / 2; ++t) {
+        out[2 * t] = bf16_lo(w[t]);
+        out[2 * t + 1] = bf16_hi(w[t]);
+      }
+    }
+  }
+  __device__ static __forceinline__ float elem(const uint32_t* w, int t) {
+    if constexpr (sizeof(IoT) == 4) return __uint_as_float(w[t]);
+    else return (t & 1) ? bf16_hi(w[t >> 1]) : bf16_lo(w[t >> 1]);
+  }
+  __device__ static __forceinline__ void pack(const float v[kChunk], uint32_t* w) {
+    if constexpr (sizeof(IoT) == 4) {
+#pragma unroll
+      for (int t = 0; t < kChunk; ++t) w[t] = __float_as_uint(v[t]);
+    } else {
+#pragma unroll
+      for (int t = 0; t < kChunk / 2; ++t) w[t] = Io<bf16_t>::pack2(v[2 * t], v[2 * t + 1]);
+    }
+  }
+  // Move the unread upper words down by one pass.
+  __device__ static __forceinline__ void rotate(uint32_t w[32]) {
+#pragma unroll
+    for (int i = 0; i + kPassWords < 32; ++i) w[i] = w[i + kPassWords];
+  }
 };
 
-template <typename IoT, bool kZ>
-__device__ __forceinline__ void load_raw(const IoT* ur, const IoT* dr, const IoT* zr, int64_t l,
-                                         RawChunk<IoT, kZ>& c) {
-  Io<IoT>::load8(ur + l, c.u);
-  Io<IoT>::load8(dr + l, c.dt);
-  if (kZ) Io<IoT>::load8(zr + l, c.z);
+// Scan [l0, l1) of one lane's channel row in line tiles (l0 line-aligned,
+// l1 - l0 a multiple of kChunk): h advances; with kEmit, y is written.
+template <typename IoT, int N, bool kEmit, bool kZ, bool kSoftplus>
+__device__ __forceinline__ void scan_lines(const IoT* ur, const IoT* dr, const IoT* zr, IoT* yr, bool active,
+                                           const IoT* Bb, const IoT* Cb, uint32_t row_bytes, int64_t l0,
+                                           int64_t l1, const Channel<N>& c, float h[N], float* dsum) {
+  using LI = Line<IoT>;
+  for (int64_t l = l0; l < l1; l += LI::kTokens) {
+    const int valid = (int)min((int64_t)LI::kTokens, l1 - l);  // a multiple of kChunk
+    const int pieces = valid / kChunk * LI::kPiecesPerChunk;
+    uint32_t ru[32], rd[32], rz[kZ ? 32 : 1], yw[kEmit ? 32 : 1];
+    LI::load(ur + l, pieces, ru);
+    LI::load(dr + l, pieces, rd);
+    if constexpr (kZ) LI::load(zr + l, pieces, rz);
+#pragma unroll 1
+    for (int pass = 0; pass < LI::kPasses; ++pass) {
+#pragma unroll
+      for (int k = 0; k < LI::kChunksPerPass; ++k) {
+        const int t0 = (pass * LI::kChunksPerPass + k) * kChunk;
+        if (t0 < valid) {
+          const uint32_t* uw = ru + k * LI::kWordsPerChunk;
+          float dl[kChunk], xl[kChunk], yv[kChunk];
+          LI::unpack(rd + k * LI::kWordsPerChunk, dl);
+#pragma unroll
+          for (int t = 0; t < kChunk; ++t) {
+            dl[t] = discretize_delta<kSoftplus>(dl[t], c.bias);
+            xl[t] = dl[t] * LI::elem(uw, t);
+            yv[t] = 0.0f;
+            if (!kEmit) *dsum += dl[t];
+          }
+          chunk_states<IoT, N, kEmit>(Bb, Cb, row_bytes, (uint32_t)((l + t0) * sizeof(IoT)), c.A2, dl, xl, h, yv);
+          if constexpr (kEmit) {
+#pragma unroll
+            for (int t = 0; t < kChunk; ++t)
+              yv[t] = epilogue<kZ>(yv[t], c.Dd, LI::elem(uw, t),
+                                   kZ ? LI::elem(rz + k * LI::kWordsPerChunk, t) : 0.0f);
+            LI::pack(yv, yw + (32 - LI::kPassWords) + k * LI::kWordsPerChunk);
+          }
+        }
+      }
+      if (pass + 1 < LI::kPasses) {
+        LI::rotate(ru);
+        LI::rotate(rd);
+        if constexpr (kZ) LI::rotate(rz);
+        if constexpr (kEmit) LI::rotate(yw);
+      }
+    }
+    if constexpr (kEmit)
+      if (active) LI::store(yr + l, pieces, yw);
+  }
 }
 
 // Launch 3 (and the only launch when P == 1): scan one segment of 64
@@ -368,23 +494,7 @@ __global__ __launch_bounds__(kBlockThreads) void scan_kernel(ScanArgs a, int64_t
 
   int64_t l = l0;
   if constexpr (kVec) {
-    RawChunk<IoT, kZ> cur, nxt;
-    if (l < l1) load_raw<IoT, kZ>(ur, dr, zr, l, cur);
-    for (; l < l1; l += kChunk) {
-      if (l + kChunk < l1) load_raw<IoT, kZ>(ur, dr, zr, l + kChunk, nxt);
-      float dl[kChunk], xl[kChunk], yv[kChunk];
-#pragma unroll
-      for (int t = 0; t < kChunk; ++t) {
-        dl[t] = discretize_delta<kSoftplus>(cur.dt[t], c.bias);
-        xl[t] = dl[t] * cur.u[t];
-        yv[t] = 0.0f;
-      }
-      chunk_states<IoT, N, true>(Bb, Cb, row_bytes, (uint32_t)(l * sizeof(IoT)), c.A2, dl, xl, h, yv);
-#pragma unroll
-      for (int t = 0; t < kChunk; ++t) yv[t] = epilogue<kZ>(yv[t], c.Dd, cur.u[t], kZ ? cur.z[t] : 0.0f);
-      if (active) Io<IoT>::store8(yr + l, yv);
-      cur = nxt;
-    }
+    scan_lines<IoT, N, true, kZ, kSoftplus>(ur, dr, zr, yr, active, Bb, Cb, row_bytes, l, l1, c, h, nullptr);
   } else {
     for (; l < l1; ++l) {
       float uv = Io<IoT>::load1(ur + l);
@@ -433,20 +543,8 @@ __global__ __launch_bounds__(kBlockThreads) void aggregate_kernel(ScanArgs a, in
 
   int64_t l = l0;
   if constexpr (kVec) {
-    RawChunk<IoT, false> cur, nxt;
-    if (l < l1) load_raw<IoT, false>(ur, dr, nullptr, l, cur);
-    for (; l < l1; l += kChunk) {
-      if (l + kChunk < l1) load_raw<IoT, false>(ur, dr, nullptr, l + kChunk, nxt);
-      float dl[kChunk], xl[kChunk], unused[kChunk];
-#pragma unroll
-      for (int t = 0; t < kChunk; ++t) {
-        dl[t] = discretize_delta<kSoftplus>(cur.dt[t], c.bias);
-        xl[t] = dl[t] * cur.u[t];
-        dsum += dl[t];
-      }
-      chunk_states<IoT, N, false>(Bb, nullptr, row_bytes, (uint32_t)(l * sizeof(IoT)), c.A2, dl, xl, h, unused);
-      cur = nxt;
-    }
+    scan_lines<IoT, N, false, false, kSoftplus>(ur, dr, nullptr, nullptr, active, Bb, nullptr, row_bytes, l, l1, c, h,
+                                                &dsum);
   } else {
     for (; l < l1; ++l) {
       float uv = Io<IoT>::load1(ur + l);
@@ -630,6 +728,7 @@ struct Plan {
 };
 
 constexpr int64_t kTargetWaves = 2048;  // two waves per SIMD on 256 CUs
+constexpr int64_t kSegAlign = 64;       // segments start on a 128-byte line for bf16 and fp32 rows
 constexpr int64_t kMinSegment = 256;    // tokens; keeps the aggregate pass amortised
 
 Plan make_plan(const Shape& s, int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen) {
@@ -638,7 +737,7 @@ Plan make_plan(const Shape& s, int64_t batch, int64_t dim, int64_t dstate, int64
   int64_t base = batch * p.groups;
   int64_t want = (kTargetWaves + base - 1) / base;
   int64_t seg = (seqlen + want - 1) / want;
-  seg = ((seg + kChunk - 1) / kChunk) * kChunk;
+  seg = ((seg + kSegAlign - 1) / kSegAlign) * kSegAlign;
   seg = std::max(seg, kMinSegment);
   if (seg >= seqlen) {
     p.segments = 1;
