@@ -35,6 +35,17 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "selective-scan HBM GB/s (% of MI355X peak) + (B·D·L)/s at Mamba-1.4B shape"
+
+# HBM bytes per call of the Mamba-1.4B-layer scan measured with rocprofv3
+# (FETCH_SIZE x 2 + WRITE_SIZE x 1, the factors a 1 GiB copy gives these
+# counters), valid only for the kernel source they were measured on: when
+# csrc/ssm_scan.hip changes, the figure is reported as null until re-measured.
+MEASURED_TRAFFIC = {
+    "source_sha256": "654683c1c20de0fb54c935bd56224bbee53f8e273e71d9cd7d4ac10ebe51aa7e",
+    "config": 2,
+    "read_bytes": 474_302_208,
+    "write_bytes": 208_454_728,
+}
 HBM_PEAK_GBS = 8000.0
 LANE_SLOTS_PEAK = 256 * 64 * 2.4e9  # fp32 VALU lane-slots per second
 SLOTS_PER_ELEM_STATE = 6            # exp2 (2 slots, half rate) + 4 fp32 ops
@@ -51,6 +62,17 @@ def algorithmic_bytes(batch, dim, dstate, seqlen, io_bytes, has_z=True, has_h0=F
 def decode_bytes(batch, dim, dstate, io_bytes):
     return (2 * batch * dim * dstate * 4 + 4 * batch * dim * io_bytes + 2 * batch * dstate * io_bytes
             + dim * dstate * 4 + 2 * dim * 4)
+
+
+def measured_traffic(config):
+    """Counter-measured HBM bytes per call, or None if the kernel changed since."""
+    import hashlib
+    src = os.path.join(ROOT, "selective_state_space_65_amd", "csrc", "ssm_scan.hip")
+    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    m = MEASURED_TRAFFIC
+    if digest != m["source_sha256"] or config != m["config"]:
+        return None
+    return m["read_bytes"] + m["write_bytes"]
 
 
 def cpu_cores():
@@ -141,6 +163,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only copy 1 GiB three times (reference kernel for rocprofv3 FETCH_SIZE/WRITE_SIZE)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: every box here has a single MI355X, and this path is not "
@@ -151,6 +175,17 @@ def main():
     from selective_state_space_65_amd import binding, inputs
 
     dev = "cuda:0"
+    if args.copy_calibration:
+        # A plain device copy of known size: 1 GiB read + 1 GiB written per
+        # launch.  Profiled with the same counters as the scan, it gives the
+        # factor between FETCH_SIZE / WRITE_SIZE and the true bytes.
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps(dict(copy_bytes_per_launch=src.numel() * 4, launches=3)))
+        return
     x = inputs.scan_config(args.config)
     b, d, n, l = x.shape
     io_bytes = 2 if x.io == "bf16" else 4
@@ -166,7 +201,7 @@ def main():
     nbytes = algorithmic_bytes(b, d, n, l, io_bytes, has_z=x.z is not None)
     elems = b * d * l
     gbs = nbytes / (wall_ms * 1e-3) / 1e9
-    seg, seglen, scratch = binding.scan_plan(b, d, n, l, t["u"].dtype)
+    path, seg, seglen, scratch = binding.scan_plan(b, d, n, l, t["u"].dtype, with_path=True)
 
     call_gbs = nbytes / (avg_ms * 1e-3) / 1e9
     slots = SLOTS_PER_ELEM_STATE * elems * n
@@ -178,8 +213,9 @@ def main():
                     unit="T lane-slots/s", frac=round(alu_frac, 4))
     else:
         roof = dict(bound="hbm", achieved=round(call_gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s", frac=round(hbm_frac, 4))
-    roof.update(traffic=None, kernel="ssm_scan_fwd call (%s)" % (
-        "scan_kernel" if seg == 1 else "aggregate_kernel + carry_kernel + scan_kernel"),
+    kernels = {"split": "scan_split_kernel", "segmented": "aggregate_kernel + carry_kernel + scan_kernel",
+               "generic": "scan_kernel (per-token)"}
+    roof.update(traffic=measured_traffic(args.config), kernel="ssm_scan_fwd call: %s" % kernels[path],
         call_us_avg=round(avg_ms * 1e3, 2), call_us_median=round(med_ms * 1e3, 2),
         hbm_gbs=round(call_gbs, 1), hbm_frac=round(hbm_frac, 4), alu_frac=round(alu_frac, 4),
         algorithmic_bytes=nbytes, algorithmic_lane_slots=slots)
@@ -188,7 +224,7 @@ def main():
                ms_per_step=round(wall_ms, 4), higher_is_better=True, scaling="weak", vs_baseline=None, dtype="f32",
                data="synthetic",
                config=dict(workload=x.meta["name"], batch=b, dim=d, dstate=n, seqlen=l, io=x.io, gate=True,
-                           softplus=True, segments=seg, segment_len=seglen),
+                           softplus=True, kernel_path=path, segments=seg, segment_len=seglen),
                hbm_frac_of_peak=round(gbs / HBM_PEAK_GBS, 4), elements_per_s=round(elems / (wall_ms * 1e-3), 1),
                roofline=roof)
     if not args.no_decode:

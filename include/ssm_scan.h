@@ -131,15 +131,26 @@ ssm_status_t ssm_state_update(int64_t batch, int64_t dim, int64_t dstate, ssm_dt
                               const float* delta_bias, int softplus_flag, void* y,
                               struct ihipStream_t* stream);
 
+/* Kernel paths of ssm_scan_fwd (reported by ssm_scan_fwd_plan). */
+typedef enum {
+  SSM_PATH_SPLIT = 0,     /* one pass; a block owns 64 channels, its waves split the states */
+  SSM_PATH_SEGMENTED = 1, /* the sequence is cut into segments scanned in parallel, then
+                             combined (segment aggregates -> carries -> rescan)            */
+  SSM_PATH_GENERIC = 2    /* one token at a time with scalar loads: any dstate <= 16, any
+                             seqlen, any element-aligned pointers                          */
+} ssm_path_t;
+
 /*
- * ssm_scan_fwd_plan -- how ssm_scan_fwd would split a problem of this shape:
- * the number of sequence segments scanned in parallel per channel, the
- * segment length in tokens, and the scratch bytes the call takes from the
- * library's pool.  Pure host arithmetic; any output pointer may be NULL.
- * Returns the same status ssm_scan_fwd would return for these sizes.
+ * ssm_scan_fwd_plan -- how ssm_scan_fwd would run a problem of this shape,
+ * assuming 16-byte aligned buffers (misaligned rows fall back to
+ * SSM_PATH_GENERIC at call time): the kernel path, the number of sequence
+ * segments scanned in parallel per channel, the segment length in tokens, and
+ * the scratch bytes the call takes from the library's pool.  Pure host
+ * arithmetic; any output pointer may be NULL.  Returns the same status
+ * ssm_scan_fwd would return for these sizes.
  */
 ssm_status_t ssm_scan_fwd_plan(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
-                               ssm_dtype_t io, int64_t* segments, int64_t* segment_len,
+                               ssm_dtype_t io, int* path, int64_t* segments, int64_t* segment_len,
                                int64_t* scratch_bytes);
 
 /* Static English text for a status code (never NULL). */

@@ -35,8 +35,8 @@ _I = ctypes.c_int
 SIGNATURES = {
     "ssm_scan_fwd": (_I, [_I64, _I64, _I64, _I64, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P]),
     "ssm_state_update": (_I, [_I64, _I64, _I64, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P]),
-    "ssm_scan_fwd_plan": (_I, [_I64, _I64, _I64, _I64, _I, ctypes.POINTER(_I64), ctypes.POINTER(_I64),
-                              ctypes.POINTER(_I64)]),
+    "ssm_scan_fwd_plan": (_I, [_I64, _I64, _I64, _I64, _I, ctypes.POINTER(_I), ctypes.POINTER(_I64),
+                              ctypes.POINTER(_I64), ctypes.POINTER(_I64)]),
     "ssm_status_string": (ctypes.c_char_p, [_I]),
     "ssm_last_hip_error": (_I, []),
     "ssm_abi_version": (_I, []),
@@ -59,10 +59,12 @@ class SsmError(RuntimeError):
 _lib = None
 
 
-def load_library(path=LIB_PATH):
-    """Load libssm_scan.so once and attach the ctypes signatures."""
+def load_library(path=None):
+    """Load libssm_scan.so (LIB_PATH unless another path is given) and attach the ctypes signatures."""
     global _lib
-    if _lib is not None and path == LIB_PATH:
+    default = path is None or path == LIB_PATH
+    path = LIB_PATH if path is None else path
+    if _lib is not None and default:
         return _lib
     if not os.path.exists(path):
         raise ImportError(
@@ -73,7 +75,7 @@ def load_library(path=LIB_PATH):
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args
-    if path == LIB_PATH:
+    if default:
         _lib = lib
     return lib
 
@@ -114,13 +116,22 @@ def _stream(device, stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def scan_plan(batch, dim, dstate, seqlen, io_dtype):
-    """(segments, segment_len, scratch_bytes) the library uses for this shape."""
+PATH_NAMES = {0: "split", 1: "segmented", 2: "generic"}
+
+
+def scan_plan(batch, dim, dstate, seqlen, io_dtype, with_path=False):
+    """(segments, segment_len, scratch_bytes) the library uses for this shape.
+
+    With with_path=True the kernel path name ("split", "segmented" or
+    "generic") is prepended to the tuple.
+    """
     lib = load_library()
-    seg, seglen, scratch = _I64(), _I64(), _I64()
-    st = lib.ssm_scan_fwd_plan(batch, dim, dstate, seqlen, _io_code(io_dtype), ctypes.byref(seg),
+    path, seg, seglen, scratch = _I(), _I64(), _I64(), _I64()
+    st = lib.ssm_scan_fwd_plan(batch, dim, dstate, seqlen, _io_code(io_dtype), ctypes.byref(path), ctypes.byref(seg),
                                ctypes.byref(seglen), ctypes.byref(scratch))
     _check("ssm_scan_fwd_plan", st)
+    if with_path:
+        return PATH_NAMES[path.value], seg.value, seglen.value, scratch.value
     return seg.value, seglen.value, scratch.value
 
 

@@ -148,6 +148,29 @@ struct Io<bf16_t> {
 template <typename T>
 using const_as4 = const __attribute__((address_space(4))) T*;
 
+// Scalar loads can complete out of order, so the only wait available for
+// one of them is "all outstanding scalar/LDS operations done".  A prefetch
+// must therefore be issued only after the data it replaces has been waited
+// for; these empty asm statements consume the current words in SGPRs at a
+// chosen point, which makes the compiler place that wait there.
+template <int K>
+__device__ __forceinline__ void settle_sgprs(const uint32_t (&w)[K]) {
+#pragma unroll
+  for (int i = 0; i < K; ++i) asm volatile("" : : "s"(w[i]));
+}
+
+// Pin VGPR values: they must be computed (and their loads waited for) here.
+template <int K>
+__device__ __forceinline__ void settle_vgprs(float (&v)[K]) {
+#pragma unroll
+  for (int i = 0; i < K; ++i) asm volatile("" : "+v"(v[i]));
+}
+template <int K>
+__device__ __forceinline__ void settle_vgprs(uint32_t (&v)[K]) {
+#pragma unroll
+  for (int i = 0; i < K; ++i) asm volatile("" : "+v"(v[i]));
+}
+
 template <typename IoT>
 struct Uni;
 
@@ -246,71 +269,82 @@ __device__ __forceinline__ float discretize_delta(float raw, float bias) {
   return kSoftplus ? softplus_f32(v) : v;
 }
 
-// One full chunk of kChunk tokens for every state (dstate == N exactly): h
-// advances, and (kEmit) y accumulates C.h.  Bb/Cb are the batch row's B and C
-// ([dstate][seqlen]); l is the chunk's first token; row_bytes = seqlen * size.
-template <typename IoT, int N, bool kEmit>
-__device__ __forceinline__ void chunk_states(const IoT* __restrict__ Bb, const IoT* __restrict__ Cb,
-                                             uint32_t row_bytes, uint32_t l_bytes, const float A2[N],
-                                             const float dl[kChunk], const float xl[kChunk], float h[N],
-                                             float yv[kChunk]) {
-  // States are processed in groups of G; the B/C rows of group g+1 are
-  // fetched (scalar loads into SGPRs) while group g computes, so a scalar
-  // cache miss has a whole group of work to hide behind.  The scheduling
-  // barriers stop the compiler from hoisting every load of the chunk at once
-  // (which would spill SGPRs).  G keeps two groups within the SGPR budget:
-  // bf16 rows are 4 packed SGPRs per 8 tokens, fp32 rows 8.
-  constexpr int G = (sizeof(IoT) == 2) ? 4 : 2;
-  constexpr int W = Uni<IoT>::kWords;
-  static_assert(N % G == 0, "state count must be a multiple of the group size");
+// B/C rows of NST consecutive states (n0 .. n0+NST-1) streamed through SGPRs
+// in groups of G states.  The rows of the next group -- the next group of
+// this chunk, or the first group of the next chunk -- are fetched while the
+// current group computes; each group's wait is forced (settle_sgprs) before
+// the next fetch is issued.  G keeps two groups within the SGPR budget: bf16
+// rows are 4 packed SGPRs per 8 tokens, fp32 rows 8.
+template <typename IoT, int NST, bool kEmit>
+struct BCPipe {
+  static constexpr int G = (sizeof(IoT) == 2) ? (NST < 4 ? NST : 4) : (NST < 2 ? NST : 2);
+  static constexpr int W = Uni<IoT>::kWords;
+  static_assert(NST % G == 0, "state count must be a multiple of the group size");
+  const IoT* Bb;
+  const IoT* Cb;
+  uint32_t row_bytes;
+  int n0;
   uint32_t Bc[G][W], Cc[G][W], Bn[G][W], Cn[G][W];
-#pragma unroll
-  for (int j = 0; j < G; ++j) {
-    const uint32_t off = (uint32_t)j * row_bytes + l_bytes;
-    Uni<IoT>::load8(Bb, off, Bc[j]);
-    if (kEmit) Uni<IoT>::load8(Cb, off, Cc[j]);
-  }
-#pragma unroll
-  for (int g = 0; g < N; g += G) {
-    if (g + G < N) {
-#pragma unroll
-      for (int j = 0; j < G; ++j) {
-        const uint32_t off = (uint32_t)(g + G + j) * row_bytes + l_bytes;
-        Uni<IoT>::load8(Bb, off, Bn[j]);
-        if (kEmit) Uni<IoT>::load8(Cb, off, Cn[j]);
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
+
+  __device__ __forceinline__ void fetch(int first_state, uint32_t l_bytes, uint32_t (&Bd)[G][W],
+                                        uint32_t (&Cd)[G][W]) const {
 #pragma unroll
     for (int j = 0; j < G; ++j) {
-      const int n = g + j;
-      float hn = h[n];
-#pragma unroll
-      for (int t = 0; t < kChunk; ++t) {
-        float abar = exp2_hw(A2[n] * dl[t]);
-        hn = __builtin_fmaf(abar, hn, Uni<IoT>::elem(Bc[j], t) * xl[t]);
-        if (kEmit) yv[t] = __builtin_fmaf(Uni<IoT>::elem(Cc[j], t), hn, yv[t]);
-      }
-      h[n] = hn;
-      // Empty register constraints: the group's results must exist here, so
-      // the compiler cannot sink the C.h accumulation below later groups
-      // (which would keep N*kChunk intermediate states alive in VGPRs).
-      asm volatile("" : "+v"(h[n]));
+      const uint32_t off = (uint32_t)(n0 + first_state + j) * row_bytes + l_bytes;
+      Uni<IoT>::load8(Bb, off, Bd[j]);
+      if (kEmit) Uni<IoT>::load8(Cb, off, Cd[j]);
     }
-    if (kEmit) {
-#pragma unroll
-      for (int t = 0; t < kChunk; ++t) asm volatile("" : "+v"(yv[t]));
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int j = 0; j < G; ++j)
-#pragma unroll
-      for (int t = 0; t < W; ++t) {
-        Bc[j][t] = Bn[j][t];
-        if (kEmit) Cc[j][t] = Cn[j][t];
-      }
   }
-}
+  // Fetch the first group of the chunk starting at byte offset l_bytes.
+  __device__ __forceinline__ void prime(uint32_t l_bytes) { fetch(0, l_bytes, Bc, Cc); }
+
+  // One chunk of kChunk tokens for all NST states: h advances, and (kEmit)
+  // y accumulates C.h.  has_next / next_l_bytes name the following chunk.
+  __device__ __forceinline__ void chunk(uint32_t l_bytes, bool has_next, uint32_t next_l_bytes,
+                                        const float A2[NST], const float dl[kChunk], const float xl[kChunk],
+                                        float h[NST], float yv[kChunk]) {
+#pragma unroll
+    for (int g = 0; g < NST; g += G) {
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        settle_sgprs(Bc[j]);
+        if (kEmit) settle_sgprs(Cc[j]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (g + G < NST) fetch(g + G, l_bytes, Bn, Cn);
+      else if (has_next) fetch(0, next_l_bytes, Bn, Cn);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        const int n = g + j;
+        float hn = h[n];
+#pragma unroll
+        for (int t = 0; t < kChunk; ++t) {
+          float abar = exp2_hw(A2[n] * dl[t]);
+          hn = __builtin_fmaf(abar, hn, Uni<IoT>::elem(Bc[j], t) * xl[t]);
+          if (kEmit) yv[t] = __builtin_fmaf(Uni<IoT>::elem(Cc[j], t), hn, yv[t]);
+        }
+        h[n] = hn;
+        // Empty register constraints: the group's results must exist here, so
+        // the compiler cannot sink the C.h accumulation below later groups
+        // (which would keep NST*kChunk intermediate states alive in VGPRs).
+        asm volatile("" : "+v"(h[n]));
+      }
+      if (kEmit) {
+#pragma unroll
+        for (int t = 0; t < kChunk; ++t) asm volatile("" : "+v"(yv[t]));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < G; ++j)
+#pragma unroll
+        for (int q = 0; q < W; ++q) {
+          Bc[j][q] = Bn[j][q];
+          if (kEmit) Cc[j][q] = Cn[j][q];
+        }
+    }
+  }
+};
 
 // One token with scalar loads (tails, unaligned shapes).
 template <typename IoT, int N, bool kEmit>
@@ -409,6 +443,12 @@ __device__ __forceinline__ void scan_lines(const IoT* ur, const IoT* dr, const I
                                            const IoT* Bb, const IoT* Cb, uint32_t row_bytes, int64_t l0,
                                            int64_t l1, const Channel<N>& c, float h[N], float* dsum) {
   using LI = Line<IoT>;
+  BCPipe<IoT, N, kEmit> bc;
+  bc.Bb = Bb;
+  bc.Cb = Cb;
+  bc.row_bytes = row_bytes;
+  bc.n0 = 0;
+  if (l0 < l1) bc.prime((uint32_t)(l0 * sizeof(IoT)));
   for (int64_t l = l0; l < l1; l += LI::kTokens) {
     const int valid = (int)min((int64_t)LI::kTokens, l1 - l);  // a multiple of kChunk
     const int pieces = valid / kChunk * LI::kPiecesPerChunk;
@@ -432,7 +472,9 @@ __device__ __forceinline__ void scan_lines(const IoT* ur, const IoT* dr, const I
             yv[t] = 0.0f;
             if (!kEmit) *dsum += dl[t];
           }
-          chunk_states<IoT, N, kEmit>(Bb, Cb, row_bytes, (uint32_t)((l + t0) * sizeof(IoT)), c.A2, dl, xl, h, yv);
+          const int64_t lt = l + t0;
+          bc.chunk((uint32_t)(lt * sizeof(IoT)), lt + kChunk < l1, (uint32_t)((lt + kChunk) * sizeof(IoT)), c.A2,
+                   dl, xl, h, yv);
           if constexpr (kEmit) {
 #pragma unroll
             for (int t = 0; t < kChunk; ++t)
@@ -509,6 +551,245 @@ __global__ __launch_bounds__(kBlockThreads) void scan_kernel(ScanArgs a, int64_t
 #pragma unroll
     for (int n = 0; n < N; ++n)
       if (n < a.dstate) a.last_state[ch * a.dstate + n] = h[n];
+  }
+}
+
+// ----------------------------------------------------------------------------
+// Single-pass prefill: the states of a channel are split across the waves
+// of a block (used when there are enough 64-channel groups to fill the chip)
+// ----------------------------------------------------------------------------
+//
+// A block owns 64 channels (one per lane) of one batch row and walks the
+// whole sequence once, in tiles of T = S * TS tokens.  Its S waves split the
+// N states: wave w owns states [w*NS, (w+1)*NS).  Per tile:
+//   A. wave w widens tokens [w*TS, (w+1)*TS) of the tile (Delta = softplus(
+//      delta + bias), x = Delta * u) and publishes (Delta, x) in LDS;
+//   B. every wave runs its NS states over all T tokens (B/C rows are wave-
+//      uniform scalar loads, prefetched one state group ahead across
+//      sub-chunks and tiles) and publishes its partial C.h sums in LDS;
+//   C. wave w adds the S partials of its TS tokens in wave order (so the
+//      result is deterministic), applies the D skip and the silu gate and
+//      stores y.
+// Each state is therefore updated exactly once per token: no segment
+// aggregates, no rescans.  Two barriers per tile; single LDS buffers are safe
+// because a wave can only reach phase A (or B) of the next tile after every
+// wave has passed the barrier that follows phase B (or A).
+template <typename IoT, int N, int S, int TS>
+struct Split {
+  static constexpr int NS = N / S;
+  static constexpr int T = S * TS;
+  static constexpr int KT = T / kChunk;
+  static constexpr int G = (sizeof(IoT) == 2) ? (NS < 4 ? NS : 4) : (NS < 2 ? NS : 2);
+  static constexpr int NG = NS / G;
+  static constexpr int W = Uni<IoT>::kWords;
+  static constexpr int kDxFloat4 = (T / 2) * 64;      // [T/2][64] of (Delta_t, x_t, Delta_t+1, x_t+1)
+  static constexpr int kYpFloat4 = S * (T / 4) * 64;  // [S][T/4][64] of 4 partial sums
+  static constexpr int kLdsBytes = 2 * 16 * (kDxFloat4 + kYpFloat4);  // double-buffered
+  static_assert(kLdsBytes <= 160 * 1024, "LDS budget of a gfx950 workgroup");
+  static_assert(N % S == 0 && NS % G == 0, "state split");
+  static_assert(TS % 4 == 0 && T % kChunk == 0, "tile shape");
+};
+
+// TS tokens of one row starting at p (TS * sizeof(IoT) bytes, aligned to that).
+template <typename IoT, int TS>
+struct Piece {
+  static constexpr int kWords = TS * (int)sizeof(IoT) / 4;
+  __device__ static __forceinline__ void load(const IoT* p, uint32_t w[kWords]) {
+    if constexpr (kWords == 2) {
+      uint2 v = *reinterpret_cast<const uint2*>(p);
+      w[0] = v.x; w[1] = v.y;
+    } else {
+#pragma unroll
+      for (int j = 0; j < kWords / 4; ++j) {
+        uint4 v = reinterpret_cast<const uint4*>(p)[j];
+        w[4 * j] = v.x; w[4 * j + 1] = v.y; w[4 * j + 2] = v.z; w[4 * j + 3] = v.w;
+      }
+    }
+  }
+  __device__ static __forceinline__ void store(IoT* p, const uint32_t w[kWords]) {
+    if constexpr (kWords == 2) {
+      *reinterpret_cast<uint2*>(p) = make_uint2(w[0], w[1]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < kWords / 4; ++j)
+        reinterpret_cast<uint4*>(p)[j] = make_uint4(w[4 * j], w[4 * j + 1], w[4 * j + 2], w[4 * j + 3]);
+    }
+  }
+};
+
+template <typename IoT, int N, int S, int TS, bool kZ, bool kSoftplus>
+__global__ __launch_bounds__(64 * S) void scan_split_kernel(ScanArgs a) {
+  using C = Split<IoT, N, S, TS>;
+  using LI = Line<IoT>;
+  using PI = Piece<IoT, TS>;
+  constexpr int NS = C::NS, T = C::T, KT = C::KT, PW = PI::kWords;
+  // Double-buffered by tile parity: one barrier per tile (see below).
+  __shared__ float4 dx[2][C::kDxFloat4];
+  __shared__ float4 yp[2][C::kYpFloat4];
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int64_t g = blockIdx.x % a.groups;
+  const int64_t b = blockIdx.x / a.groups;
+  const int64_t d_raw = g * kWaveThreads + lane;
+  const bool active = d_raw < a.dim;
+  const int64_t d = active ? d_raw : a.dim - 1;
+  const int64_t L = a.seqlen;
+  const int64_t ch = b * a.dim + d;
+
+  float A2[NS], h[NS];
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+    const int n = w * NS + j;
+    A2[j] = a.A[d * N + n] * kLog2e;
+    h[j] = a.h0 ? a.h0[ch * N + n] : 0.0f;
+  }
+  const float Dd = a.D ? a.D[d] : 0.0f;
+  const float bias = a.bias ? a.bias[d] : 0.0f;
+
+  const IoT* ur = static_cast<const IoT*>(a.u) + ch * L;
+  const IoT* dr = static_cast<const IoT*>(a.delta) + ch * L;
+  const IoT* zr = kZ ? static_cast<const IoT*>(a.z) + ch * L : nullptr;
+  IoT* yr = static_cast<IoT*>(a.y) + ch * L;
+
+  BCPipe<IoT, NS, true> bc;
+  bc.Bb = static_cast<const IoT*>(a.B) + b * N * L;
+  bc.Cb = static_cast<const IoT*>(a.C) + b * N * L;
+  bc.row_bytes = (uint32_t)(L * sizeof(IoT));
+  bc.n0 = w * NS;
+  bc.prime(0);
+
+  // This wave's TS-token pieces of u, delta, z for three tiles in flight:
+  //   c*: tile i   (u, z needed by phase C of tile i)
+  //   a*: tile i+1 (widened by phase A of tile i+1)
+  //   n*: tile i+2 (fetched during phase A of tile i+1)
+  uint32_t cu[PW], cz[kZ ? PW : 1], au[PW], ad[PW], az[kZ ? PW : 1], nu[PW], nd[PW], nz[kZ ? PW : 1];
+  auto fetch = [&](int64_t l, uint32_t (&pu)[PW], uint32_t (&pd)[PW], uint32_t (&pz)[kZ ? PW : 1]) {
+    PI::load(ur + l + w * TS, pu);
+    PI::load(dr + l + w * TS, pd);
+    if constexpr (kZ) PI::load(zr + l + w * TS, pz);
+  };
+  // Phase A: widen this wave's tokens of tile l and publish (Delta, x).
+  auto widen = [&](int buf, const uint32_t (&pu)[PW], const uint32_t (&pd)[PW]) {
+#pragma unroll
+    for (int t = 0; t < TS; t += 2) {
+      float d0 = discretize_delta<kSoftplus>(LI::elem(pd, t), bias);
+      float d1 = discretize_delta<kSoftplus>(LI::elem(pd, t + 1), bias);
+      dx[buf][((w * TS + t) / 2) * 64 + lane] = make_float4(d0, d0 * LI::elem(pu, t), d1, d1 * LI::elem(pu, t + 1));
+    }
+  };
+  // A wave's share of a tile is all-or-nothing: tiles hold a multiple of
+  // kChunk tokens and TS divides kChunk.
+  auto owns = [&](int64_t l) { return l < L && l + w * TS < L; };
+
+  if (owns(0)) {
+    fetch(0, au, ad, az);
+    if (owns(T)) fetch(T, nu, nd, nz);
+    widen(0, au, ad);
+#pragma unroll
+    for (int q = 0; q < PW; ++q) {
+      cu[q] = au[q];
+      if constexpr (kZ) cz[q] = az[q];
+      au[q] = nu[q];
+      ad[q] = nd[q];
+      if constexpr (kZ) az[q] = nz[q];
+    }
+  }
+  __syncthreads();
+
+  // Per tile i:  B(i) reads dx[i%2], writes yp[i%2];  A(i+1) writes
+  // dx[(i+1)%2];  barrier;  C(i) reads yp[i%2].  The barrier orders every
+  // cross-wave hand-off: B(i+1) needs all of A(i+1); C(i) needs all of B(i);
+  // A(i+1) overwrites dx[(i+1)%2], last read by B(i-1) before barrier i-1;
+  // B(i) overwrites yp[i%2], last read by C(i-2) before barrier i-1.
+  int buf = 0;
+  for (int64_t l = 0; l < L; l += T, buf ^= 1) {
+    const int valid = (int)min((int64_t)T, L - l);  // a multiple of kChunk
+    // ---- B: this wave's states over the whole tile.  The tile's (Delta, x)
+    // are read and waited for first and the partial sums written after the
+    // loop, so inside it the scalar B/C pipeline is the only traffic on the
+    // shared LDS/scalar wait counter.
+    float dl[KT][kChunk], xl[KT][kChunk], yv[KT][kChunk];
+#pragma unroll
+    for (int k = 0; k < KT; ++k)
+#pragma unroll
+      for (int i = 0; i < kChunk / 2; ++i) {
+        float4 v = dx[buf][(k * kChunk / 2 + i) * 64 + lane];
+        dl[k][2 * i] = v.x; xl[k][2 * i] = v.y; dl[k][2 * i + 1] = v.z; xl[k][2 * i + 1] = v.w;
+      }
+#pragma unroll
+    for (int k = 0; k < KT; ++k) {
+      settle_vgprs(dl[k]);
+      settle_vgprs(xl[k]);
+    }
+#pragma unroll
+    for (int k = 0; k < KT; ++k) {
+#pragma unroll
+      for (int t = 0; t < kChunk; ++t) yv[k][t] = 0.0f;
+      if (k * kChunk < valid) {
+        const int64_t lt = l + k * kChunk;
+        const bool in_tile = (k + 1) * kChunk < valid;
+        const bool has_next = in_tile || l + T < L;
+        const int64_t nl = in_tile ? lt + kChunk : l + T;
+        bc.chunk((uint32_t)(lt * sizeof(IoT)), has_next, (uint32_t)(nl * sizeof(IoT)), A2, dl[k], xl[k], h, yv[k]);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < KT; ++k) {
+      yp[buf][(w * (T / 4) + 2 * k) * 64 + lane] = make_float4(yv[k][0], yv[k][1], yv[k][2], yv[k][3]);
+      yp[buf][(w * (T / 4) + 2 * k + 1) * 64 + lane] = make_float4(yv[k][4], yv[k][5], yv[k][6], yv[k][7]);
+    }
+    // ---- A of the next tile
+    if (owns(l + T)) {
+      if (owns(l + 2 * T)) fetch(l + 2 * T, nu, nd, nz);
+      widen(buf ^ 1, au, ad);
+    }
+    __syncthreads();
+    // ---- C: reduce the partial sums of this wave's tokens, gate, store
+    if (owns(l)) {
+      float yo[TS];
+#pragma unroll
+      for (int q = 0; q < TS / 4; ++q) {
+        float4 acc = yp[buf][((w * TS) / 4 + q) * 64 + lane];
+#pragma unroll
+        for (int s2 = 1; s2 < S; ++s2) {
+          float4 v = yp[buf][(s2 * (T / 4) + (w * TS) / 4 + q) * 64 + lane];
+          acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+        }
+        yo[4 * q] = acc.x; yo[4 * q + 1] = acc.y; yo[4 * q + 2] = acc.z; yo[4 * q + 3] = acc.w;
+      }
+#pragma unroll
+      for (int t = 0; t < TS; ++t)
+        yo[t] = epilogue<kZ>(yo[t], Dd, LI::elem(cu, t), kZ ? LI::elem(cz, t) : 0.0f);
+      uint32_t yw[PW];
+      if constexpr (sizeof(IoT) == 4) {
+#pragma unroll
+        for (int t = 0; t < TS; ++t) yw[t] = __float_as_uint(yo[t]);
+      } else {
+#pragma unroll
+        for (int t = 0; t < TS / 2; ++t) yw[t] = Io<bf16_t>::pack2(yo[2 * t], yo[2 * t + 1]);
+      }
+      if (active) PI::store(yr + l + w * TS, yw);
+    }
+    // Rotate the pieces: tile i+1 becomes current, tile i+2 becomes next to
+    // widen.  The pins keep the compiler from deferring the copies (and the
+    // wait on the tile i+2 fetch) into the next iteration's phase A.
+#pragma unroll
+    for (int q = 0; q < PW; ++q) {
+      cu[q] = au[q];
+      if constexpr (kZ) cz[q] = az[q];
+      au[q] = nu[q];
+      ad[q] = nd[q];
+      if constexpr (kZ) az[q] = nz[q];
+    }
+    settle_vgprs(au);
+    settle_vgprs(ad);
+    if constexpr (kZ) settle_vgprs(az);
+  }
+
+  if (a.last_state && active) {
+#pragma unroll
+    for (int j = 0; j < NS; ++j) a.last_state[ch * N + w * NS + j] = h[j];
   }
 }
 
@@ -725,16 +1006,34 @@ ssm_status_t shape_of(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen
 struct Plan {
   int64_t groups, segments, seg_len;
   int64_t scratch_bytes;
+  bool split;  // single-pass state-split kernel
 };
 
 constexpr int64_t kTargetWaves = 2048;  // two waves per SIMD on 256 CUs
 constexpr int64_t kSegAlign = 64;       // segments start on a 128-byte line for bf16 and fp32 rows
 constexpr int64_t kMinSegment = 256;    // tokens; keeps the aggregate pass amortised
+#ifndef SSM_SPLIT_MIN_BLOCKS
+#define SSM_SPLIT_MIN_BLOCKS 192
+#endif
+#ifndef SSM_SPLIT_WAVES
+#define SSM_SPLIT_WAVES 8
+#endif
+// The single-pass kernel runs one block per 64-channel group; it is chosen
+// when those blocks cover most of the 256 compute units.  Otherwise the
+// sequence is segmented so that every CU has work.
+constexpr int64_t kSplitMinBlocks = SSM_SPLIT_MIN_BLOCKS;
 
 Plan make_plan(const Shape& s, int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen) {
   Plan p;
   p.groups = (dim + kWaveThreads - 1) / kWaveThreads;
   int64_t base = batch * p.groups;
+  p.split = base >= kSplitMinBlocks && (dstate == 4 || dstate == 8 || dstate == 16) && seqlen % kChunk == 0;
+  if (p.split) {
+    p.segments = 1;
+    p.seg_len = seqlen;
+    p.scratch_bytes = 0;
+    return p;
+  }
   int64_t want = (kTargetWaves + base - 1) / base;
   int64_t seg = (seqlen + want - 1) / want;
   seg = ((seg + kSegAlign - 1) / kSegAlign) * kSegAlign;
@@ -752,7 +1051,6 @@ Plan make_plan(const Shape& s, int64_t batch, int64_t dim, int64_t dstate, int64
   } else {
     p.scratch_bytes = 0;
   }
-  (void)dstate;
   return p;
 }
 
@@ -821,10 +1119,30 @@ hipError_t launch_scan_f(const ScanArgs& a, const Plan& p, hipStream_t st, bool 
   return sp ? launch_scan_t<IoT, N, false, true, kVec>(a, p, st) : launch_scan_t<IoT, N, false, false, kVec>(a, p, st);
 }
 
+template <typename IoT, int N, int S, int TS, bool kZ, bool kSp>
+hipError_t launch_split_t(const ScanArgs& a, const Plan& p, hipStream_t st) {
+  hipLaunchKernelGGL((scan_split_kernel<IoT, N, S, TS, kZ, kSp>), dim3((unsigned)(a.batch * p.groups)), dim3(64 * S),
+                     0, st, a);
+  return hipGetLastError();
+}
+
+template <typename IoT, int N>
+hipError_t launch_split(const ScanArgs& a, const Plan& p, hipStream_t st, bool sp) {
+  constexpr int S = (N >= SSM_SPLIT_WAVES) ? SSM_SPLIT_WAVES : N;
+  constexpr int TS = 32 / S;  // 32-token tiles
+  if (a.z) return sp ? launch_split_t<IoT, N, S, TS, true, true>(a, p, st) : launch_split_t<IoT, N, S, TS, true, false>(a, p, st);
+  return sp ? launch_split_t<IoT, N, S, TS, false, true>(a, p, st) : launch_split_t<IoT, N, S, TS, false, false>(a, p, st);
+}
+
 // Vector kernels exist for dstate in {4, 8, 16}; every other case runs the
 // scalar-token kernel instantiated for up to 16 states.
 template <typename IoT>
 hipError_t launch_scan(const ScanArgs& a, const Plan& p, hipStream_t st, bool vec, bool sp) {
+  if (vec && p.split) {
+    if (a.dstate == 4) return launch_split<IoT, 4>(a, p, st, sp);
+    if (a.dstate == 8) return launch_split<IoT, 8>(a, p, st, sp);
+    return launch_split<IoT, 16>(a, p, st, sp);
+  }
   if (vec) {
     if (a.dstate == 4) return launch_scan_f<IoT, 4, true>(a, p, st, sp);
     if (a.dstate == 8) return launch_scan_f<IoT, 8, true>(a, p, st, sp);
@@ -892,11 +1210,14 @@ const char* ssm_status_string(ssm_status_t s) {
 }
 
 ssm_status_t ssm_scan_fwd_plan(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, ssm_dtype_t io,
-                               int64_t* segments, int64_t* segment_len, int64_t* scratch_bytes) {
+                               int* path, int64_t* segments, int64_t* segment_len, int64_t* scratch_bytes) {
   Shape sh;
   ssm_status_t st = shape_of(batch, dim, dstate, seqlen, io, &sh);
   if (st != SSM_OK) return st;
   Plan p = make_plan(sh, batch, dim, dstate, seqlen);
+  const bool vec = seqlen % kChunk == 0 && (dstate == 4 || dstate == 8 || dstate == 16) &&
+                   dstate * seqlen * (int64_t)io_size(io) < ((int64_t)1 << 31);
+  if (path) *path = p.split && vec ? SSM_PATH_SPLIT : (vec ? SSM_PATH_SEGMENTED : SSM_PATH_GENERIC);
   if (segments) *segments = p.segments;
   if (segment_len) *segment_len = p.seg_len;
   if (scratch_bytes) *scratch_bytes = p.scratch_bytes;

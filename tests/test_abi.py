@@ -123,13 +123,16 @@ def test_update_validation(lib):
 
 
 def test_plan(lib):
-    seg, seglen, scratch = binding.scan_plan(4, 4096, 16, 4096, __import__("torch").bfloat16)
-    assert seg >= 1 and seglen % 8 == 0 and seg * seglen >= 4096
-    assert (seg == 1) == (scratch == 0)
-    seg, seglen, scratch = binding.scan_plan(1, 16, 4, 64, __import__("torch").float32)
-    assert (seg, seglen, scratch) == (1, 64, 0)
-    seg, seglen, scratch = binding.scan_plan(1, 2560, 16, 131072, __import__("torch").float32)
-    assert seg > 1 and (seg - 1) * seglen < 131072 <= seg * seglen
+    import torch
+    path, seg, seglen, scratch = binding.scan_plan(4, 4096, 16, 4096, torch.bfloat16, with_path=True)
+    assert (path, seg, seglen, scratch) == ("split", 1, 4096, 0)          # Mamba-1.4B layer: single pass
+    path, seg, seglen, scratch = binding.scan_plan(1, 2560, 16, 131072, torch.float32, with_path=True)
+    assert path == "segmented" and seg > 1 and (seg - 1) * seglen < 131072 <= seg * seglen and scratch > 0
+    assert seglen % 64 == 0
+    assert binding.scan_plan(1, 16, 4, 64, torch.float32, with_path=True) == ("segmented", 1, 64, 0)
+    assert binding.scan_plan(1, 16, 4, 63, torch.float32, with_path=True)[0] == "generic"
+    assert binding.scan_plan(256, 64, 5, 64, torch.float32, with_path=True)[0] == "generic"
+    assert binding.scan_plan(2, 8, 16, 16, torch.float32) == (1, 16, 0)
 
 
 def test_product_never_uses_the_oracle():

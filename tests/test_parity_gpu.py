@@ -294,3 +294,44 @@ def test_binding_rejects_aliasing():
     with pytest.raises(binding.SsmError) as e:
         binding.scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], out=t["u"])
     assert e.value.name == "SSM_ERR_ALIAS"
+
+
+# Shapes with at least 192 channel groups take the single-pass state-split
+# kernel; keep them small in seqlen so the full oracle stays cheap.
+SPLIT_SHAPES = [(192, 64, 16, 72), (96, 130, 16, 40), (200, 64, 8, 24), (256, 33, 4, 8), (192, 64, 16, 256)]
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", SPLIT_SHAPES, ids=["%dx%dx%dx%d" % s for s in SPLIT_SHAPES])
+def test_split_path(io, shape):
+    b, d, n, l = shape
+    seg, seglen, scratch = binding.scan_plan(b, d, n, l, torch.float32 if io == "f32" else torch.bfloat16)
+    assert seg == 1 and scratch == 0
+    for mask in (0, 31, 5, 26):
+        z, D, bias, sp, h0 = [(mask >> i) & 1 == 1 for i in range(5)]
+        x = inputs.make_scan_inputs(b, d, n, l, io=io, seed=300 + mask, z=z, D=D, bias=bias, softplus=sp, h0=h0)
+        if not sp:
+            x.delta = inputs.round_bf16(np.abs(x.delta) * np.float32(0.2)) if io == "bf16" else \
+                np.abs(x.delta) * np.float32(0.2)
+            if bias:
+                x.delta_bias = np.full(d, 0.01, np.float32)
+        say("split path shape=%s io=%s mask=%d" % (shape, io, mask))
+        y, last = gpu_scan(x)
+        yr, hr = oracle_full(x)
+        check(np64(y), yr, io, "y mask=%d" % mask)
+        check(np64(last), hr, "f32", "last_state mask=%d" % mask)
+
+
+def test_split_path_determinism_and_alias():
+    b, d, n, l = 192, 64, 16, 128
+    x = inputs.make_scan_inputs(b, d, n, l, io="bf16", seed=400, h0=True)
+    t = inputs.to_torch(x, DEV)
+    say("split path determinism + in-place state")
+    y1, h1 = gpu_scan(x)
+    y2, h2 = gpu_scan(x)
+    assert torch.equal(y1, y2) and torch.equal(h1, h2)
+    state = t["h0"].clone()
+    y3, _ = binding.scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
+                             delta_bias=t["delta_bias"], delta_softplus=True, h0=state, last_state=state)
+    torch.cuda.synchronize()
+    assert torch.equal(y3, y1) and torch.equal(state, h1)
