@@ -147,6 +147,7 @@ struct Io<bf16_t> {
 // widened with scalar shifts) instead of a vector load plus VALU unpacking.
 template <typename T>
 using const_as4 = const __attribute__((address_space(4))) T*;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // Scalar loads can complete out of order, so the only wait available for
 // one of them is "all outstanding scalar/LDS operations done".  A prefetch
@@ -171,6 +172,15 @@ __device__ __forceinline__ void settle_vgprs(uint32_t (&v)[K]) {
   for (int i = 0; i < K; ++i) asm volatile("" : "+v"(v[i]));
 }
 
+// Workgroup barrier that orders LDS only: the LDS writes before it are
+// visible to every wave after it, while global loads and stores stay in
+// flight (a full __syncthreads would also wait for those).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 template <typename IoT>
 struct Uni;
 
@@ -180,10 +190,13 @@ struct Uni;
 template <>
 struct Uni<float> {
   static constexpr int kWords = 8;
+  // base + byte_off is 16-byte aligned: the typed vector loads let the
+  // compiler emit whole s_load_dwordx8 / x4 instructions.
   __device__ static __forceinline__ void load8(const float* base, uint32_t byte_off, uint32_t w[kWords]) {
-    const_as4<uint32_t> q = (const_as4<uint32_t>)((const_as4<char>)base + byte_off);
-#pragma unroll
-    for (int t = 0; t < kWords; ++t) w[t] = q[t];
+    const_as4<u32x4> q = (const_as4<u32x4>)((const_as4<char>)base + byte_off);
+    const u32x4 a = q[0], b = q[1];
+    w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+    w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
   }
   __device__ static __forceinline__ float elem(const uint32_t w[kWords], int t) { return __uint_as_float(w[t]); }
 };
@@ -191,10 +204,10 @@ struct Uni<float> {
 template <>
 struct Uni<bf16_t> {
   static constexpr int kWords = 4;
+  // base + byte_off is 16-byte aligned (one s_load_dwordx4).
   __device__ static __forceinline__ void load8(const bf16_t* base, uint32_t byte_off, uint32_t w[kWords]) {
-    const_as4<uint32_t> q = (const_as4<uint32_t>)((const_as4<char>)base + byte_off);
-#pragma unroll
-    for (int t = 0; t < kWords; ++t) w[t] = q[t];
+    const u32x4 a = *(const_as4<u32x4>)((const_as4<char>)base + byte_off);
+    w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
   }
   __device__ static __forceinline__ float elem(const uint32_t w[kWords], int t) {
     return (t & 1) ? bf16_hi(w[t >> 1]) : bf16_lo(w[t >> 1]);
@@ -273,56 +286,60 @@ __device__ __forceinline__ float discretize_delta(float raw, float bias) {
 // in groups of G states.  The rows of the next group -- the next group of
 // this chunk, or the first group of the next chunk -- are fetched while the
 // current group computes; each group's wait is forced (settle_sgprs) before
-// the next fetch is issued.  G keeps two groups within the SGPR budget: bf16
-// rows are 4 packed SGPRs per 8 tokens, fp32 rows 8.
+// the next fetch is issued.  Two buffers alternate by the parity of the group
+// count, which the caller passes as a compile-time constant (P0: parity of the
+// chunk's first group), so no SGPR copies are needed.  G keeps both buffers
+// within the SGPR budget: bf16 rows are 4 packed SGPRs per 8 tokens, fp32 8.
 template <typename IoT, int NST, bool kEmit>
 struct BCPipe {
   static constexpr int G = (sizeof(IoT) == 2) ? (NST < 4 ? NST : 4) : (NST < 2 ? NST : 2);
+  static constexpr int NG = NST / G;
   static constexpr int W = Uni<IoT>::kWords;
   static_assert(NST % G == 0, "state count must be a multiple of the group size");
   const IoT* Bb;
   const IoT* Cb;
   uint32_t row_bytes;
   int n0;
-  uint32_t Bc[G][W], Cc[G][W], Bn[G][W], Cn[G][W];
+  uint32_t Bx[2][G][W], Cx[2][G][W];
 
-  __device__ __forceinline__ void fetch(int first_state, uint32_t l_bytes, uint32_t (&Bd)[G][W],
-                                        uint32_t (&Cd)[G][W]) const {
+  __device__ __forceinline__ void fetch(int buf, int first_state, uint32_t l_bytes) {
 #pragma unroll
     for (int j = 0; j < G; ++j) {
       const uint32_t off = (uint32_t)(n0 + first_state + j) * row_bytes + l_bytes;
-      Uni<IoT>::load8(Bb, off, Bd[j]);
-      if (kEmit) Uni<IoT>::load8(Cb, off, Cd[j]);
+      Uni<IoT>::load8(Bb, off, Bx[buf][j]);
+      if (kEmit) Uni<IoT>::load8(Cb, off, Cx[buf][j]);
     }
   }
-  // Fetch the first group of the chunk starting at byte offset l_bytes.
-  __device__ __forceinline__ void prime(uint32_t l_bytes) { fetch(0, l_bytes, Bc, Cc); }
+  // Fetch the first group of the first chunk (starting at byte offset l_bytes).
+  __device__ __forceinline__ void prime(uint32_t l_bytes) { fetch(0, 0, l_bytes); }
 
   // One chunk of kChunk tokens for all NST states: h advances, and (kEmit)
   // y accumulates C.h.  has_next / next_l_bytes name the following chunk.
+  template <int P0>
   __device__ __forceinline__ void chunk(uint32_t l_bytes, bool has_next, uint32_t next_l_bytes,
                                         const float A2[NST], const float dl[kChunk], const float xl[kChunk],
                                         float h[NST], float yv[kChunk]) {
 #pragma unroll
-    for (int g = 0; g < NST; g += G) {
+    for (int gi = 0; gi < NG; ++gi) {
+      const int cur = (P0 + gi) & 1;
 #pragma unroll
       for (int j = 0; j < G; ++j) {
-        settle_sgprs(Bc[j]);
-        if (kEmit) settle_sgprs(Cc[j]);
+        settle_sgprs(Bx[cur][j]);
+        if (kEmit) settle_sgprs(Cx[cur][j]);
       }
       __builtin_amdgcn_sched_barrier(0);
-      if (g + G < NST) fetch(g + G, l_bytes, Bn, Cn);
-      else if (has_next) fetch(0, next_l_bytes, Bn, Cn);
+      if (gi + 1 < NG) fetch(cur ^ 1, (gi + 1) * G, l_bytes);
+      else if (has_next) fetch(cur ^ 1, 0, next_l_bytes);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int j = 0; j < G; ++j) {
-        const int n = g + j;
+        const int n = gi * G + j;
         float hn = h[n];
 #pragma unroll
         for (int t = 0; t < kChunk; ++t) {
           float abar = exp2_hw(A2[n] * dl[t]);
-          hn = __builtin_fmaf(abar, hn, Uni<IoT>::elem(Bc[j], t) * xl[t]);
-          if (kEmit) yv[t] = __builtin_fmaf(Uni<IoT>::elem(Cc[j], t), hn, yv[t]);
+          hn = __builtin_fmaf(abar, hn, Uni<IoT>::elem(Bx[cur][j], t) * xl[t]);
+          if (kEmit) yv[t] = __builtin_fmaf(Uni<IoT>::elem(Cx[cur][j], t), hn, yv[t]);
         }
         h[n] = hn;
         // Empty register constraints: the group's results must exist here, so
@@ -335,13 +352,6 @@ struct BCPipe {
         for (int t = 0; t < kChunk; ++t) asm volatile("" : "+v"(yv[t]));
       }
       __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int j = 0; j < G; ++j)
-#pragma unroll
-        for (int q = 0; q < W; ++q) {
-          Bc[j][q] = Bn[j][q];
-          if (kEmit) Cc[j][q] = Cn[j][q];
-        }
     }
   }
 };
@@ -381,7 +391,7 @@ template <typename IoT>
 struct Line {
   static constexpr int kTokens = 128 / (int)sizeof(IoT);                 // 32 fp32, 64 bf16
   static constexpr int kWordsPerChunk = kChunk * (int)sizeof(IoT) / 4;  // 8 fp32, 4 bf16
-  static constexpr int kChunksPerPass = 4;
+  static constexpr int kChunksPerPass = 4;  // even: keeps the B/C buffer parity fixed per pass
   static constexpr int kPasses = kTokens / (kChunk * kChunksPerPass);     // 1 fp32, 2 bf16
   static constexpr int kPassWords = kChunksPerPass * kWordsPerChunk;      // 32 fp32, 16 bf16
   static constexpr int kPiecesPerChunk = kChunk * (int)sizeof(IoT) / 16;  // 16-byte pieces: 2 fp32, 1 bf16
@@ -473,8 +483,14 @@ __device__ __forceinline__ void scan_lines(const IoT* ur, const IoT* dr, const I
             if (!kEmit) *dsum += dl[t];
           }
           const int64_t lt = l + t0;
-          bc.chunk((uint32_t)(lt * sizeof(IoT)), lt + kChunk < l1, (uint32_t)((lt + kChunk) * sizeof(IoT)), c.A2,
-                   dl, xl, h, yv);
+          // Each pass runs kChunksPerPass (even) chunks, so the buffer parity
+          // of chunk k's first group is (k * NG) mod 2 on every pass and tile.
+          // (The branch folds away once the chunk loop is unrolled.)
+          const uint32_t lb = (uint32_t)(lt * sizeof(IoT)), nb = (uint32_t)((lt + kChunk) * sizeof(IoT));
+          if (((k * BCPipe<IoT, N, kEmit>::NG) & 1) == 0)
+            bc.template chunk<0>(lb, lt + kChunk < l1, nb, c.A2, dl, xl, h, yv);
+          else
+            bc.template chunk<1>(lb, lt + kChunk < l1, nb, c.A2, dl, xl, h, yv);
           if constexpr (kEmit) {
 #pragma unroll
             for (int t = 0; t < kChunk; ++t)
@@ -561,33 +577,28 @@ __global__ __launch_bounds__(kBlockThreads) void scan_kernel(ScanArgs a, int64_t
 //
 // A block owns 64 channels (one per lane) of one batch row and walks the
 // whole sequence once, in tiles of T = S * TS tokens.  Its S waves split the
-// N states: wave w owns states [w*NS, (w+1)*NS).  Per tile:
+// N states: wave w owns states [w*NS, (w+1)*NS).  The work on a tile:
 //   A. wave w widens tokens [w*TS, (w+1)*TS) of the tile (Delta = softplus(
 //      delta + bias), x = Delta * u) and publishes (Delta, x) in LDS;
 //   B. every wave runs its NS states over all T tokens (B/C rows are wave-
-//      uniform scalar loads, prefetched one state group ahead across
-//      sub-chunks and tiles) and publishes its partial C.h sums in LDS;
+//      uniform scalar loads) and publishes its partial C.h sums in LDS;
 //   C. wave w adds the S partials of its TS tokens in wave order (so the
 //      result is deterministic), applies the D skip and the silu gate and
 //      stores y.
 // Each state is therefore updated exactly once per token: no segment
-// aggregates, no rescans.  Two barriers per tile; single LDS buffers are safe
-// because a wave can only reach phase A (or B) of the next tile after every
-// wave has passed the barrier that follows phase B (or A).
+// aggregates, no rescans.
 template <typename IoT, int N, int S, int TS>
 struct Split {
   static constexpr int NS = N / S;
   static constexpr int T = S * TS;
   static constexpr int KT = T / kChunk;
-  static constexpr int G = (sizeof(IoT) == 2) ? (NS < 4 ? NS : 4) : (NS < 2 ? NS : 2);
-  static constexpr int NG = NS / G;
-  static constexpr int W = Uni<IoT>::kWords;
   static constexpr int kDxFloat4 = (T / 2) * 64;      // [T/2][64] of (Delta_t, x_t, Delta_t+1, x_t+1)
   static constexpr int kYpFloat4 = S * (T / 4) * 64;  // [S][T/4][64] of 4 partial sums
   static constexpr int kLdsBytes = 2 * 16 * (kDxFloat4 + kYpFloat4);  // double-buffered
   static_assert(kLdsBytes <= 160 * 1024, "LDS budget of a gfx950 workgroup");
-  static_assert(N % S == 0 && NS % G == 0, "state split");
-  static_assert(TS % 4 == 0 && T % kChunk == 0, "tile shape");
+  static_assert(N % S == 0 && NS <= 2, "state split: at most two states per wave");
+  static_assert(TS % 4 == 0 && kChunk % TS == 0 && T % kChunk == 0, "tile shape");
+  static_assert(KT % 2 == 0, "an even number of sub-chunks per tile: sub-chunk k uses B/C buffer k % 2");
 };
 
 // TS tokens of one row starting at p (TS * sizeof(IoT) bytes, aligned to that).
@@ -622,7 +633,8 @@ __global__ __launch_bounds__(64 * S) void scan_split_kernel(ScanArgs a) {
   using C = Split<IoT, N, S, TS>;
   using LI = Line<IoT>;
   using PI = Piece<IoT, TS>;
-  constexpr int NS = C::NS, T = C::T, KT = C::KT, PW = PI::kWords;
+  using U = Uni<IoT>;
+  constexpr int NS = C::NS, T = C::T, KT = C::KT, PW = PI::kWords, ZW = kZ ? PI::kWords : 1, W = U::kWords;
   // Double-buffered by tile parity: one barrier per tile (see below).
   __shared__ float4 dx[2][C::kDxFloat4];
   __shared__ float4 yp[2][C::kYpFloat4];
@@ -652,31 +664,85 @@ __global__ __launch_bounds__(64 * S) void scan_split_kernel(ScanArgs a) {
   const IoT* zr = kZ ? static_cast<const IoT*>(a.z) + ch * L : nullptr;
   IoT* yr = static_cast<IoT*>(a.y) + ch * L;
 
-  BCPipe<IoT, NS, true> bc;
-  bc.Bb = static_cast<const IoT*>(a.B) + b * N * L;
-  bc.Cb = static_cast<const IoT*>(a.C) + b * N * L;
-  bc.row_bytes = (uint32_t)(L * sizeof(IoT));
-  bc.n0 = w * NS;
-  bc.prime(0);
+  // B/C words of this wave's states for one sub-chunk of kChunk tokens, in
+  // two buffers: sub-chunk k of a tile uses buffer k % 2, and the next sub-
+  // chunk's rows are fetched while the current one computes (each fetch is
+  // issued only after the buffer it overwrites has been waited for).
+  const IoT* Bb = static_cast<const IoT*>(a.B) + b * N * L;
+  const IoT* Cb = static_cast<const IoT*>(a.C) + b * N * L;
+  const uint32_t row_bytes = (uint32_t)(L * sizeof(IoT));
+  uint32_t Bx[2][NS][W], Cx[2][NS][W];
+  auto fetch_bc = [&](int s, int64_t lt) {
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      uint32_t off = (uint32_t)(w * NS + j) * row_bytes + (uint32_t)(lt * sizeof(IoT));
+      // Materialise the offset here: an address computed in another block
+      // is not merged into whole-row s_load_dwordx4/x8 loads.
+      asm volatile("" : "+s"(off));
+      U::load8(Bb, off, Bx[s][j]);
+      U::load8(Cb, off, Cx[s][j]);
+    }
+  };
+  // (Delta, x) of sub-chunk k of the tile in dx[buf].
+  auto read_dx = [&](int buf, int k, float (&dl)[kChunk], float (&xl)[kChunk]) {
+#pragma unroll
+    for (int i = 0; i < kChunk / 2; ++i) {
+      float4 v = dx[buf][(k * kChunk / 2 + i) * 64 + lane];
+      dl[2 * i] = v.x; xl[2 * i] = v.y; dl[2 * i + 1] = v.z; xl[2 * i + 1] = v.w;
+    }
+  };
+  // The S partial sums of this wave's TS tokens of the tile in yp[buf].
+  auto read_partials = [&](int buf, float4 (&part)[TS / 4][S]) {
+#pragma unroll
+    for (int q = 0; q < TS / 4; ++q)
+#pragma unroll
+      for (int s2 = 0; s2 < S; ++s2) part[q][s2] = yp[buf][(s2 * (T / 4) + (w * TS) / 4 + q) * 64 + lane];
+  };
 
-  // This wave's TS-token pieces of u, delta, z for three tiles in flight:
-  //   c*: tile i   (u, z needed by phase C of tile i)
+  // This wave's TS-token pieces of u, delta, z, four tiles in flight:
+  //   p*: tile i-1 (u, z for phase C of tile i-1)
+  //   c*: tile i   (u, z kept for phase C of tile i)
   //   a*: tile i+1 (widened by phase A of tile i+1)
   //   n*: tile i+2 (fetched during phase A of tile i+1)
-  uint32_t cu[PW], cz[kZ ? PW : 1], au[PW], ad[PW], az[kZ ? PW : 1], nu[PW], nd[PW], nz[kZ ? PW : 1];
-  auto fetch = [&](int64_t l, uint32_t (&pu)[PW], uint32_t (&pd)[PW], uint32_t (&pz)[kZ ? PW : 1]) {
-    PI::load(ur + l + w * TS, pu);
-    PI::load(dr + l + w * TS, pd);
-    if constexpr (kZ) PI::load(zr + l + w * TS, pz);
+  uint32_t pu[PW], pz[ZW], cu[PW], cz[ZW], au[PW], ad[PW], az[ZW], nu[PW], nd[PW], nz[ZW];
+  auto fetch = [&](int64_t l, uint32_t (&qu)[PW], uint32_t (&qd)[PW], uint32_t (&qz)[ZW]) {
+    PI::load(ur + l + w * TS, qu);
+    PI::load(dr + l + w * TS, qd);
+    if constexpr (kZ) PI::load(zr + l + w * TS, qz);
   };
-  // Phase A: widen this wave's tokens of tile l and publish (Delta, x).
-  auto widen = [&](int buf, const uint32_t (&pu)[PW], const uint32_t (&pd)[PW]) {
+  // Phase A: widen this wave's tokens of a tile and publish (Delta, x).
+  auto widen = [&](int buf, const uint32_t (&qu)[PW], const uint32_t (&qd)[PW]) {
 #pragma unroll
     for (int t = 0; t < TS; t += 2) {
-      float d0 = discretize_delta<kSoftplus>(LI::elem(pd, t), bias);
-      float d1 = discretize_delta<kSoftplus>(LI::elem(pd, t + 1), bias);
-      dx[buf][((w * TS + t) / 2) * 64 + lane] = make_float4(d0, d0 * LI::elem(pu, t), d1, d1 * LI::elem(pu, t + 1));
+      float d0 = discretize_delta<kSoftplus>(LI::elem(qd, t), bias);
+      float d1 = discretize_delta<kSoftplus>(LI::elem(qd, t + 1), bias);
+      dx[buf][((w * TS + t) / 2) * 64 + lane] = make_float4(d0, d0 * LI::elem(qu, t), d1, d1 * LI::elem(qu, t + 1));
     }
+  };
+  // Phase C: sum the partials in wave order, gate, store the tile at lc.
+  auto finish = [&](const float4 (&part)[TS / 4][S], int64_t lc, const uint32_t (&qu)[PW],
+                    const uint32_t (&qz)[ZW]) {
+    float yo[TS];
+#pragma unroll
+    for (int q = 0; q < TS / 4; ++q) {
+      float4 acc = part[q][0];
+#pragma unroll
+      for (int s2 = 1; s2 < S; ++s2) {
+        acc.x += part[q][s2].x; acc.y += part[q][s2].y; acc.z += part[q][s2].z; acc.w += part[q][s2].w;
+      }
+      yo[4 * q] = acc.x; yo[4 * q + 1] = acc.y; yo[4 * q + 2] = acc.z; yo[4 * q + 3] = acc.w;
+    }
+#pragma unroll
+    for (int t = 0; t < TS; ++t) yo[t] = epilogue<kZ>(yo[t], Dd, LI::elem(qu, t), kZ ? LI::elem(qz, t) : 0.0f);
+    uint32_t yw[PW];
+    if constexpr (sizeof(IoT) == 4) {
+#pragma unroll
+      for (int t = 0; t < TS; ++t) yw[t] = __float_as_uint(yo[t]);
+    } else {
+#pragma unroll
+      for (int t = 0; t < TS / 2; ++t) yw[t] = Io<bf16_t>::pack2(yo[2 * t], yo[2 * t + 1]);
+    }
+    if (active) PI::store(yr + lc + w * TS, yw);
   };
   // A wave's share of a tile is all-or-nothing: tiles hold a multiple of
   // kChunk tokens and TS divides kChunk.
@@ -697,85 +763,87 @@ __global__ __launch_bounds__(64 * S) void scan_split_kernel(ScanArgs a) {
   }
   __syncthreads();
 
-  // Per tile i:  B(i) reads dx[i%2], writes yp[i%2];  A(i+1) writes
-  // dx[(i+1)%2];  barrier;  C(i) reads yp[i%2].  The barrier orders every
-  // cross-wave hand-off: B(i+1) needs all of A(i+1); C(i) needs all of B(i);
-  // A(i+1) overwrites dx[(i+1)%2], last read by B(i-1) before barrier i-1;
-  // B(i) overwrites yp[i%2], last read by C(i-2) before barrier i-1.
+  // Iteration i (tile i at l, buf = i % 2):
+  //   issue the B/C scalar loads and the dx[buf] LDS reads of sub-chunk 0,
+  //   and the LDS reads of the partials of tile i-1 in yp[buf^1];  A(i+1)
+  //   writes dx[buf^1];  C(i-1) consumes the partials;  B(i) reads dx[buf]
+  //   and B/C one sub-chunk ahead and writes yp[buf];  LDS barrier.
+  // The single barrier orders every cross-wave hand-off: B(i) needs all of
+  // A(i) (written before barrier i-1); C(i-1) needs all of B(i-1) (before
+  // barrier i-1); A(i+1) overwrites dx[buf^1], last read by B(i-1) before
+  // barrier i-1; B(i) overwrites yp[buf], last read at the start of
+  // iteration i-1, before barrier i-1.  Issuing the reads first lets phase A's
+  // arithmetic cover their latency instead of every wave stalling on them at
+  // once after the barrier.
   int buf = 0;
   for (int64_t l = 0; l < L; l += T, buf ^= 1) {
     const int valid = (int)min((int64_t)T, L - l);  // a multiple of kChunk
-    // ---- B: this wave's states over the whole tile.  The tile's (Delta, x)
-    // are read and waited for first and the partial sums written after the
-    // loop, so inside it the scalar B/C pipeline is the only traffic on the
-    // shared LDS/scalar wait counter.
-    float dl[KT][kChunk], xl[KT][kChunk], yv[KT][kChunk];
-#pragma unroll
-    for (int k = 0; k < KT; ++k)
-#pragma unroll
-      for (int i = 0; i < kChunk / 2; ++i) {
-        float4 v = dx[buf][(k * kChunk / 2 + i) * 64 + lane];
-        dl[k][2 * i] = v.x; xl[k][2 * i] = v.y; dl[k][2 * i + 1] = v.z; xl[k][2 * i + 1] = v.w;
-      }
-#pragma unroll
-    for (int k = 0; k < KT; ++k) {
-      settle_vgprs(dl[k]);
-      settle_vgprs(xl[k]);
-    }
-#pragma unroll
-    for (int k = 0; k < KT; ++k) {
-#pragma unroll
-      for (int t = 0; t < kChunk; ++t) yv[k][t] = 0.0f;
-      if (k * kChunk < valid) {
-        const int64_t lt = l + k * kChunk;
-        const bool in_tile = (k + 1) * kChunk < valid;
-        const bool has_next = in_tile || l + T < L;
-        const int64_t nl = in_tile ? lt + kChunk : l + T;
-        bc.chunk((uint32_t)(lt * sizeof(IoT)), has_next, (uint32_t)(nl * sizeof(IoT)), A2, dl[k], xl[k], h, yv[k]);
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < KT; ++k) {
-      yp[buf][(w * (T / 4) + 2 * k) * 64 + lane] = make_float4(yv[k][0], yv[k][1], yv[k][2], yv[k][3]);
-      yp[buf][(w * (T / 4) + 2 * k + 1) * 64 + lane] = make_float4(yv[k][4], yv[k][5], yv[k][6], yv[k][7]);
-    }
+    float dl[KT][kChunk], xl[KT][kChunk];
+    float4 part[TS / 4][S];
+    const bool prev = l > 0 && owns(l - T);
+    fetch_bc(0, l);
+    read_dx(buf, 0, dl[0], xl[0]);
+    if (prev) read_partials(buf ^ 1, part);
+    __builtin_amdgcn_sched_barrier(0);
     // ---- A of the next tile
     if (owns(l + T)) {
       if (owns(l + 2 * T)) fetch(l + 2 * T, nu, nd, nz);
       widen(buf ^ 1, au, ad);
     }
-    __syncthreads();
-    // ---- C: reduce the partial sums of this wave's tokens, gate, store
-    if (owns(l)) {
-      float yo[TS];
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- C of the previous tile
+    if (prev) finish(part, l - T, pu, pz);
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- B: this wave's states over the tile, one sub-chunk at a time.
 #pragma unroll
-      for (int q = 0; q < TS / 4; ++q) {
-        float4 acc = yp[buf][((w * TS) / 4 + q) * 64 + lane];
+    for (int k = 0; k < KT; ++k) {
+      if (k * kChunk < valid) {
+        const int s = k & 1;
+        // One wait covers this sub-chunk's (Delta, x) and B/C words.
+        settle_vgprs(dl[k]);
+        settle_vgprs(xl[k]);
 #pragma unroll
-        for (int s2 = 1; s2 < S; ++s2) {
-          float4 v = yp[buf][(s2 * (T / 4) + (w * TS) / 4 + q) * 64 + lane];
-          acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+        for (int j = 0; j < NS; ++j) {
+          settle_sgprs(Bx[s][j]);
+          settle_sgprs(Cx[s][j]);
         }
-        yo[4 * q] = acc.x; yo[4 * q + 1] = acc.y; yo[4 * q + 2] = acc.z; yo[4 * q + 3] = acc.w;
+        __builtin_amdgcn_sched_barrier(0);
+        // Prefetch the next sub-chunk of this tile.  (The first sub-chunk of
+        // the next tile is fetched after the barrier: a scalar load in flight
+        // would hold up the LDS wait in front of it.)
+        if (k + 1 < KT && (k + 1) * kChunk < valid) {
+          const int kn = (k + 1 < KT) ? k + 1 : k;  // (the clamp only keeps the index static)
+          read_dx(buf, kn, dl[kn], xl[kn]);
+          fetch_bc(s ^ 1, l + (k + 1) * kChunk);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        float yv[kChunk];
+#pragma unroll
+        for (int j = 0; j < NS; ++j) {
+          float hn = h[j];
+#pragma unroll
+          for (int t = 0; t < kChunk; ++t) {
+            float abar = exp2_hw(A2[j] * dl[k][t]);
+            hn = __builtin_fmaf(abar, hn, U::elem(Bx[s][j], t) * xl[k][t]);
+            const float cv = U::elem(Cx[s][j], t);
+            yv[t] = (j == 0) ? cv * hn : __builtin_fmaf(cv, hn, yv[t]);
+          }
+          h[j] = hn;
+          // The state's results must exist here: the compiler may not sink
+          // the C.h accumulation below the next state's work.
+          asm volatile("" : "+v"(h[j]));
+        }
+        yp[buf][(w * (T / 4) + 2 * k) * 64 + lane] = make_float4(yv[0], yv[1], yv[2], yv[3]);
+        yp[buf][(w * (T / 4) + 2 * k + 1) * 64 + lane] = make_float4(yv[4], yv[5], yv[6], yv[7]);
+        __builtin_amdgcn_sched_barrier(0);
       }
-#pragma unroll
-      for (int t = 0; t < TS; ++t)
-        yo[t] = epilogue<kZ>(yo[t], Dd, LI::elem(cu, t), kZ ? LI::elem(cz, t) : 0.0f);
-      uint32_t yw[PW];
-      if constexpr (sizeof(IoT) == 4) {
-#pragma unroll
-        for (int t = 0; t < TS; ++t) yw[t] = __float_as_uint(yo[t]);
-      } else {
-#pragma unroll
-        for (int t = 0; t < TS / 2; ++t) yw[t] = Io<bf16_t>::pack2(yo[2 * t], yo[2 * t + 1]);
-      }
-      if (active) PI::store(yr + l + w * TS, yw);
     }
-    // Rotate the pieces: tile i+1 becomes current, tile i+2 becomes next to
-    // widen.  The pins keep the compiler from deferring the copies (and the
-    // wait on the tile i+2 fetch) into the next iteration's phase A.
+    // Rotate the pieces.  The pins keep the compiler from deferring the
+    // copies (and the wait on the tile i+2 fetch) into the next phase A.
 #pragma unroll
     for (int q = 0; q < PW; ++q) {
+      pu[q] = cu[q];
+      if constexpr (kZ) pz[q] = cz[q];
       cu[q] = au[q];
       if constexpr (kZ) cz[q] = az[q];
       au[q] = nu[q];
@@ -785,6 +853,14 @@ __global__ __launch_bounds__(64 * S) void scan_split_kernel(ScanArgs a) {
     settle_vgprs(au);
     settle_vgprs(ad);
     if constexpr (kZ) settle_vgprs(az);
+    lds_barrier();
+  }
+  // ---- C of the last tile (its partials are in yp[buf^1]).
+  const int64_t l_last = ((L - 1) / T) * T;
+  if (owns(l_last)) {
+    float4 part[TS / 4][S];
+    read_partials(buf ^ 1, part);
+    finish(part, l_last, pu, pz);
   }
 
   if (a.last_state && active) {
@@ -1018,12 +1094,13 @@ constexpr int64_t kMinSegment = 256;    // tokens; keeps the aggregate pass amor
 #ifndef SSM_SPLIT_WAVES
 #define SSM_SPLIT_WAVES 8
 #endif
+
 // The single-pass kernel runs one block per 64-channel group; it is chosen
 // when those blocks cover most of the 256 compute units.  Otherwise the
 // sequence is segmented so that every CU has work.
 constexpr int64_t kSplitMinBlocks = SSM_SPLIT_MIN_BLOCKS;
 
-Plan make_plan(const Shape& s, int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen) {
+Plan make_plan(const Shape& s, int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, ssm_dtype_t io) {
   Plan p;
   p.groups = (dim + kWaveThreads - 1) / kWaveThreads;
   int64_t base = batch * p.groups;
@@ -1214,7 +1291,7 @@ ssm_status_t ssm_scan_fwd_plan(int64_t batch, int64_t dim, int64_t dstate, int64
   Shape sh;
   ssm_status_t st = shape_of(batch, dim, dstate, seqlen, io, &sh);
   if (st != SSM_OK) return st;
-  Plan p = make_plan(sh, batch, dim, dstate, seqlen);
+  Plan p = make_plan(sh, batch, dim, dstate, seqlen, io);
   const bool vec = seqlen % kChunk == 0 && (dstate == 4 || dstate == 8 || dstate == 16) &&
                    dstate * seqlen * (int64_t)io_size(io) < ((int64_t)1 << 31);
   if (path) *path = p.split && vec ? SSM_PATH_SPLIT : (vec ? SSM_PATH_SEGMENTED : SSM_PATH_GENERIC);
@@ -1257,7 +1334,7 @@ ssm_status_t ssm_scan_fwd(int64_t batch, int64_t dim, int64_t dstate, int64_t se
     if (h0 && h0 != last_state && overlap(rl, ins[8])) return SSM_ERR_ALIAS;
   }
 
-  const Plan plan = make_plan(sh, batch, dim, dstate, seqlen);
+  const Plan plan = make_plan(sh, batch, dim, dstate, seqlen, io);
   // Vector path: whole 16-byte chunks on every row, and B/C batch slabs
   // addressable with 32-bit byte offsets.
   const bool vec = (seqlen % kChunk == 0) && aligned(u, 16) && aligned(delta, 16) && aligned(y, 16) &&

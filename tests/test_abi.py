@@ -126,6 +126,7 @@ def test_plan(lib):
     import torch
     path, seg, seglen, scratch = binding.scan_plan(4, 4096, 16, 4096, torch.bfloat16, with_path=True)
     assert (path, seg, seglen, scratch) == ("split", 1, 4096, 0)          # Mamba-1.4B layer: single pass
+    assert binding.scan_plan(8, 1536, 16, 2048, torch.float32, with_path=True) == ("split", 1, 2048, 0)
     path, seg, seglen, scratch = binding.scan_plan(1, 2560, 16, 131072, torch.float32, with_path=True)
     assert path == "segmented" and seg > 1 and (seg - 1) * seglen < 131072 <= seg * seglen and scratch > 0
     assert seglen % 64 == 0

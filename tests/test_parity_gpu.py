@@ -305,8 +305,9 @@ SPLIT_SHAPES = [(192, 64, 16, 72), (96, 130, 16, 40), (200, 64, 8, 24), (256, 33
 @pytest.mark.parametrize("shape", SPLIT_SHAPES, ids=["%dx%dx%dx%d" % s for s in SPLIT_SHAPES])
 def test_split_path(io, shape):
     b, d, n, l = shape
-    seg, seglen, scratch = binding.scan_plan(b, d, n, l, torch.float32 if io == "f32" else torch.bfloat16)
-    assert seg == 1 and scratch == 0
+    path, seg, seglen, scratch = binding.scan_plan(b, d, n, l, torch.float32 if io == "f32" else torch.bfloat16,
+                                                   with_path=True)
+    assert path == "split" and seg == 1
     for mask in (0, 31, 5, 26):
         z, D, bias, sp, h0 = [(mask >> i) & 1 == 1 for i in range(5)]
         x = inputs.make_scan_inputs(b, d, n, l, io=io, seed=300 + mask, z=z, D=D, bias=bias, softplus=sp, h0=h0)
