@@ -41,10 +41,10 @@ METRIC = "selective-scan HBM GB/s (% of MI355X peak) + (B·D·L)/s at Mamba-1.4B
 # counters), valid only for the kernel source they were measured on: when
 # csrc/ssm_scan.hip changes, the figure is reported as null until re-measured.
 MEASURED_TRAFFIC = {
-    "source_sha256": "654683c1c20de0fb54c935bd56224bbee53f8e273e71d9cd7d4ac10ebe51aa7e",
+    "source_sha256": "4c807a501994bfa132c3e1f6e713b5888fff8fca057accbbcf41ba353cae3853",
     "config": 2,
-    "read_bytes": 474_302_208,
-    "write_bytes": 208_454_728,
+    "read_bytes": 464_276_890,
+    "write_bytes": 311_755_488,
 }
 HBM_PEAK_GBS = 8000.0
 LANE_SLOTS_PEAK = 256 * 64 * 2.4e9  # fp32 VALU lane-slots per second
@@ -150,8 +150,8 @@ def bench_decode(dev, steps, warmup):
     return dict(workload="decode state update, batch %d, dim %d, dstate %d, bf16 io, fp32 state"
                 % (dec.batch, dec.dim, dec.dstate), us_per_step=round(avg_ms * 1e3, 2),
                 effective_gbs=round(nbytes / (avg_ms * 1e-3) / 1e9, 1), bytes_per_step=nbytes,
-                note="the 84 MB state can stay in the 256 MB Infinity Cache between steps, so this is an "
-                     "effective rate, not HBM traffic")
+                note="algorithmic bytes per step / step time; the 84 MB state fits in the 256 MB Infinity "
+                     "Cache, which sits behind the L2 and may serve part of it, so this is not pure HBM traffic")
 
 
 def main():
