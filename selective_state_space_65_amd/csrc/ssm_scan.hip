@@ -68,17 +68,21 @@ __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2
 __device__ __forceinline__ float log2_hw(float x) { return __builtin_amdgcn_logf(x); }
 __device__ __forceinline__ float rcp_hw(float x) { return __builtin_amdgcn_rcpf(x); }
 
-// softplus(x) = log(1 + e^x).  e^x via the hardware exp2; log1p(e) via the
-// hardware log2 with Kahan's correction for the rounding of w = 1 + e
-// (log1p(e) = log(w) * e / (w - 1), D. Goldberg, "What every computer
-// scientist should know about floating-point arithmetic", 1991).  Above 20 the
-// result equals x to within 2e-9 and e^x may overflow, so x is returned.
+// softplus(x) = log(1 + e^x) = max(x, 0) + log1p(e), e = e^-|x| in (0, 1].
+// w = 1 + e is rounded, but for w in [1, 2] its rounding error c = (w - 1) - e
+// is exact (w - 1 is exact there, and so is the difference of two nearby
+// floats), and log1p(e) = log(w) - c / w + O(c^2).  Using c for c / w errs by
+// at most c / 2 <= 2^-25 absolute, which is below the rounding of the result
+// except where the result is below 2^-24 -- and there (w == 1, so c = -e)
+// the formula returns e itself.  Emulated in fp32 with correctly rounded
+// exp2/log2 over x in [-40, 40] it stays within 2e-6 relative of the fp64
+// log1p(exp(x)), like the Kahan form log(w) * e / (w - 1), with one
+// transcendental and four VALU ops fewer.
 __device__ __forceinline__ float softplus_f32(float x) {
-  float e = exp2_hw(x * kLog2e);
-  float w = 1.0f + e;
-  float lg = log2_hw(w) * kLn2;
-  float r = (w == 1.0f) ? e : lg * (e * rcp_hw(w - 1.0f));
-  return x > 20.0f ? x : r;
+  const float e = exp2_hw(-__builtin_fabsf(x) * kLog2e);  // in (0, 1]
+  const float w = 1.0f + e;                               // in [1, 2]
+  const float c = (w - 1.0f) - e;                         // rounding error of w, exact
+  return __builtin_fmaf(log2_hw(w), kLn2, __builtin_fmaxf(x, 0.0f) - c);
 }
 
 // silu(z) = z * sigmoid(z) = z / (1 + e^-z)
@@ -576,28 +580,34 @@ __global__ __launch_bounds__(kBlockThreads) void scan_kernel(ScanArgs a, int64_t
 // ----------------------------------------------------------------------------
 //
 // A block owns 64 channels (one per lane) of one batch row and walks the
-// whole sequence once, in tiles of T = S * TS tokens.  Its S waves split the
-// N states: wave w owns states [w*NS, (w+1)*NS).  The work on a tile:
-//   A. wave w widens tokens [w*TS, (w+1)*TS) of the tile (Delta = softplus(
-//      delta + bias), x = Delta * u) and publishes (Delta, x) in LDS;
+// whole sequence once, in tiles of T = 32 tokens.  Its S waves split the N
+// states: wave w owns states [w*NS, (w+1)*NS).  The work on a tile:
+//   A. each of the first SA waves widens TS = T / SA tokens of the tile
+//      (Delta = softplus(delta + bias), x = Delta * u): wave w < SA owns
+//      tokens [w*TS, (w+1)*TS), and publishes (Delta, x) in LDS;
 //   B. every wave runs its NS states over all T tokens (B/C rows are wave-
 //      uniform scalar loads) and publishes its partial C.h sums in LDS;
-//   C. wave w adds the S partials of its TS tokens in wave order (so the
+//   C. wave w < SA adds the S partials of its TS tokens in wave order (so the
 //      result is deterministic), applies the D skip and the silu gate and
 //      stores y.
 // Each state is therefore updated exactly once per token: no segment
-// aggregates, no rescans.
-template <typename IoT, int N, int S, int TS>
+// aggregates, no rescans.  With two waves per SIMD (S = 8) phases A and C go
+// to the first four waves only: waves w and w + 4 share a SIMD and the older
+// one is issued first, so it finishes the common phase B early; giving it
+// the short, latency-bound softplus/silu chains lets them overlap the
+// partner's state arithmetic instead of leaving the partner to run alone.
+template <typename IoT, int N, int S, int SA>
 struct Split {
   static constexpr int NS = N / S;
-  static constexpr int T = S * TS;
+  static constexpr int T = 32;
+  static constexpr int TS = T / SA;
   static constexpr int KT = T / kChunk;
   static constexpr int kDxFloat4 = (T / 2) * 64;      // [T/2][64] of (Delta_t, x_t, Delta_t+1, x_t+1)
   static constexpr int kYpFloat4 = S * (T / 4) * 64;  // [S][T/4][64] of 4 partial sums
   static constexpr int kLdsBytes = 2 * 16 * (kDxFloat4 + kYpFloat4);  // double-buffered
   static_assert(kLdsBytes <= 160 * 1024, "LDS budget of a gfx950 workgroup");
   static_assert(N % S == 0 && NS <= 2, "state split: at most two states per wave");
-  static_assert(TS % 4 == 0 && kChunk % TS == 0 && T % kChunk == 0, "tile shape");
+  static_assert(SA <= S && T % SA == 0 && TS % 4 == 0 && kChunk % TS == 0 && T % kChunk == 0, "tile shape");
   static_assert(KT % 2 == 0, "an even number of sub-chunks per tile: sub-chunk k uses B/C buffer k % 2");
 };
 
@@ -628,9 +638,10 @@ struct Piece {
   }
 };
 
-template <typename IoT, int N, int S, int TS, bool kZ, bool kSoftplus>
+template <typename IoT, int N, int S, int SA, bool kZ, bool kSoftplus>
 __global__ __launch_bounds__(64 * S) void scan_split_kernel(ScanArgs a) {
-  using C = Split<IoT, N, S, TS>;
+  using C = Split<IoT, N, S, SA>;
+  constexpr int TS = C::TS;
   using LI = Line<IoT>;
   using PI = Piece<IoT, TS>;
   using U = Uni<IoT>;
@@ -745,8 +756,8 @@ __global__ __launch_bounds__(64 * S) void scan_split_kernel(ScanArgs a) {
     if (active) PI::store(yr + lc + w * TS, yw);
   };
   // A wave's share of a tile is all-or-nothing: tiles hold a multiple of
-  // kChunk tokens and TS divides kChunk.
-  auto owns = [&](int64_t l) { return l < L && l + w * TS < L; };
+  // kChunk tokens and TS divides kChunk.  Waves w >= SA own no tokens.
+  auto owns = [&](int64_t l) { return w < SA && l < L && l + w * TS < L; };
 
   if (owns(0)) {
     fetch(0, au, ad, az);
@@ -1196,9 +1207,9 @@ hipError_t launch_scan_f(const ScanArgs& a, const Plan& p, hipStream_t st, bool 
   return sp ? launch_scan_t<IoT, N, false, true, kVec>(a, p, st) : launch_scan_t<IoT, N, false, false, kVec>(a, p, st);
 }
 
-template <typename IoT, int N, int S, int TS, bool kZ, bool kSp>
+template <typename IoT, int N, int S, int SA, bool kZ, bool kSp>
 hipError_t launch_split_t(const ScanArgs& a, const Plan& p, hipStream_t st) {
-  hipLaunchKernelGGL((scan_split_kernel<IoT, N, S, TS, kZ, kSp>), dim3((unsigned)(a.batch * p.groups)), dim3(64 * S),
+  hipLaunchKernelGGL((scan_split_kernel<IoT, N, S, SA, kZ, kSp>), dim3((unsigned)(a.batch * p.groups)), dim3(64 * S),
                      0, st, a);
   return hipGetLastError();
 }
@@ -1206,9 +1217,10 @@ hipError_t launch_split_t(const ScanArgs& a, const Plan& p, hipStream_t st) {
 template <typename IoT, int N>
 hipError_t launch_split(const ScanArgs& a, const Plan& p, hipStream_t st, bool sp) {
   constexpr int S = (N >= SSM_SPLIT_WAVES) ? SSM_SPLIT_WAVES : N;
-  constexpr int TS = 32 / S;  // 32-token tiles
-  if (a.z) return sp ? launch_split_t<IoT, N, S, TS, true, true>(a, p, st) : launch_split_t<IoT, N, S, TS, true, false>(a, p, st);
-  return sp ? launch_split_t<IoT, N, S, TS, false, true>(a, p, st) : launch_split_t<IoT, N, S, TS, false, false>(a, p, st);
+  // Phases A and C run on one wave per SIMD (the first four waves).
+  constexpr int SA = (S > 4) ? 4 : S;
+  if (a.z) return sp ? launch_split_t<IoT, N, S, SA, true, true>(a, p, st) : launch_split_t<IoT, N, S, SA, true, false>(a, p, st);
+  return sp ? launch_split_t<IoT, N, S, SA, false, true>(a, p, st) : launch_split_t<IoT, N, S, SA, false, false>(a, p, st);
 }
 
 // Vector kernels exist for dstate in {4, 8, 16}; every other case runs the
