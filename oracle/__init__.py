@@ -13,6 +13,7 @@ this module only marshals numpy arrays into it.
                            (channels are independent, so a subset is exact)
   .state_update_f64(...)   one-token update of a float64 state, in place
   .state_update_channels_f64(...)  the same for chosen (b, d) channels
+  .conv1d_f64(...)         the causal depthwise conv (+ silu) in front of the scan
   .softplus_f64, .silu_f64 the scalar helpers the C oracle uses
 Module-level functions of the same names use the default oracle.
 """
@@ -55,6 +56,8 @@ class Oracle:
         L.oracle_scan_f64.argtypes = [I64, I64, I64, I64] + [P] * 8 + [I, P, P, P]
         L.oracle_state_update_f64.restype = I
         L.oracle_state_update_f64.argtypes = [I64, I64, I64] + [P] * 9 + [I, P]
+        L.oracle_conv1d_f64.restype = I
+        L.oracle_conv1d_f64.argtypes = [I64, I64, I64, I64, P, P, P, P, I, P]
         L.oracle_softplus.restype = ctypes.c_double
         L.oracle_softplus.argtypes = [ctypes.c_double]
         L.oracle_silu.restype = ctypes.c_double
@@ -80,6 +83,20 @@ class Oracle:
         if rc != 0:
             raise ValueError("oracle_scan_f64 rejected the arguments")
         return y, last
+
+    def conv1d_f64(self, x, weight, bias=None, x_prev=None, silu=True):
+        """u = act(causal depthwise conv of x).  x: (batch, dim, seqlen); weight: (dim, K), K in 1..4;
+        bias: (dim,); x_prev: (batch, dim, K-1), the inputs before token 0.  Returns u in float64."""
+        x, weight, bias = _f64(x), _f64(weight), _f64(bias)
+        batch, dim, seqlen = x.shape
+        width = weight.shape[1]
+        xp = None if x_prev is None or width == 1 else _f64(x_prev)
+        u = np.empty((batch, dim, seqlen), np.float64)
+        rc = self.lib.oracle_conv1d_f64(batch, dim, seqlen, width, _p(x), _p(weight), _p(bias), _p(xp),
+                                        1 if silu else 0, _p(u))
+        if rc != 0:
+            raise ValueError("oracle_conv1d_f64 rejected the arguments")
+        return u
 
     def scan_channels_f64(self, channels, u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=False,
                           h0=None):
@@ -155,6 +172,10 @@ def state_update_f64(*args, **kw):
 
 def state_update_channels_f64(*args, **kw):
     return default().state_update_channels_f64(*args, **kw)
+
+
+def conv1d_f64(*args, **kw):
+    return default().conv1d_f64(*args, **kw)
 
 
 def softplus_f64(x):

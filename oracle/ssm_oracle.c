@@ -42,13 +42,25 @@
  *  - Delta = softplus(delta + bias) when the flag is set, else delta + bias;
  *  - the initial state is h0 when given, else zero.
  *
+ * The Mamba block puts a causal Conv1d in front of the SSM (the Hebrew
+ * overview, "תחילת העבודה עם Mamba"; the Chinese explainer's section on why a
+ * convolution precedes the SSM: each token is first mixed with its neighbours
+ * so that it is not processed alone).  oracle_conv1d_f64 computes it, read as:
+ *  - depthwise (one filter per channel), causal, width K (1..4):
+ *      u[b,d,l] = act(cb[d] + sum_{k<K} w[d,k] * x[b,d,l-(K-1)+k]),
+ *    so w[d,K-1] multiplies the current token;
+ *  - before token 0 the input is x_prev[b,d,0..K-2] (the K-1 inputs that
+ *    preceded this piece of the sequence) when given, else zero;
+ *  - act is silu when the flag is set, else the identity; cb is 0 when absent.
+ *
  * Layouts (row-major, last index fastest):
  *   u, delta, z, y : [batch][dim][seqlen]
  *   B, C           : [batch][dstate][seqlen]
  *   A              : [dim][dstate]
  *   D, bias        : [dim]
  *   h0, last_state : [batch][dim][dstate]
- * Optional inputs (D, z, bias, h0) may be NULL; last_state may be NULL.
+ *   x, u (conv)    : [batch][dim][seqlen]; w: [dim][K]; cb: [dim]; x_prev: [batch][dim][K-1]
+ * Optional inputs (D, z, bias, h0, cb, x_prev) may be NULL; last_state may be NULL.
  */
 #include <math.h>
 #include <stddef.h>
@@ -130,6 +142,33 @@ int oracle_state_update_f64(int64_t batch, int64_t dim, int64_t dstate, double* 
     scan_channel(dstate, 1, u + ch, delta + ch, A + d * dstate, B + b * dstate, C + b * dstate,
                  D ? D[d] : 0.0, z ? z + ch : NULL, delta_bias ? delta_bias[d] : 0.0, softplus_flag,
                  state + ch * dstate, y + ch);
+  }
+  return 0;
+}
+
+/* Causal depthwise convolution of every (b, d) row, then silu if the flag is
+ * set.  Returns 0, or -1 on bad sizes or a missing required pointer. */
+int oracle_conv1d_f64(int64_t batch, int64_t dim, int64_t seqlen, int64_t width, const double* x,
+                      const double* w, const double* cb, const double* x_prev, int silu_flag, double* u) {
+  if (batch < 1 || dim < 1 || seqlen < 1 || width < 1 || width > 4) return -1;
+  if (!x || !w || !u) return -1;
+  int64_t nch = batch * dim;
+#pragma omp parallel for schedule(static)
+  for (int64_t ch = 0; ch < nch; ++ch) {
+    int64_t d = ch % dim;
+    for (int64_t l = 0; l < seqlen; ++l) {
+      double acc = cb ? cb[d] : 0.0;
+      for (int64_t k = 0; k < width; ++k) {
+        int64_t src = l - (width - 1) + k; /* position of the input this tap reads */
+        double v;
+        if (src >= 0)
+          v = x[ch * seqlen + src];
+        else
+          v = x_prev ? x_prev[ch * (width - 1) + (width - 1) + src] : 0.0;
+        acc += w[d * width + k] * v;
+      }
+      u[ch * seqlen + l] = silu_flag ? oracle_silu(acc) : acc;
+    }
   }
   return 0;
 }

@@ -23,6 +23,13 @@ deliberately broken copies of it (tests/test_oracle_mutants.py).
   softplus_silu     the scalar helpers against numpy / scipy library routines
   decode_is_scan    the one-token update equals a one-token scan
   channel_subset    scanning a subset of channels equals the rows of a full scan
+  conv_library      the causal depthwise conv (+ silu) in front of the scan against
+                    numpy's correlate over [x_prev, x] and scipy's logistic
+  conv_taps         a filter that keeps only the current tap returns x; one that
+                    keeps only the oldest tap shifts x by K-1, fed by x_prev
+  conv_causality    changing x at position p changes exactly u[p .. p+K-1]
+  conv_split_carry  convolving in two pieces, the second fed the first's last K-1
+                    inputs as x_prev, equals one pass
 """
 import json
 import math
@@ -258,5 +265,77 @@ def channel_subset(o):
         assert np.array_equal(ys[i], y[b, d]) and np.array_equal(hs[i], last[b, d])
 
 
+def _conv_problem(rng, batch, dim, seqlen, width):
+    return dict(x=rng.standard_normal((batch, dim, seqlen)), weight=rng.standard_normal((dim, width)),
+                bias=rng.standard_normal(dim), x_prev=rng.standard_normal((batch, dim, width - 1)))
+
+
+def conv_library(o):
+    from scipy.special import expit
+    rng = _rng(20)
+    batch, dim, seqlen = 2, 3, 23
+    for width in (1, 2, 3, 4):
+        for silu in (False, True):
+            for with_prev in (False, True):
+                for with_bias in (False, True):
+                    p = _conv_problem(rng, batch, dim, seqlen, width)
+                    u = o.conv1d_f64(p["x"], p["weight"], p["bias"] if with_bias else None,
+                                     p["x_prev"] if with_prev else None, silu=silu)
+                    for b in range(batch):
+                        for d in range(dim):
+                            head = p["x_prev"][b, d] if with_prev else np.zeros(width - 1)
+                            ref = np.correlate(np.concatenate([head, p["x"][b, d]]), p["weight"][d], mode="valid")
+                            if with_bias:
+                                ref = ref + p["bias"][d]
+                            if silu:
+                                ref = ref * expit(ref)
+                            _close(u[b, d], ref, 1e-13, 1e-14,
+                                   "conv K=%d silu=%s prev=%s bias=%s" % (width, silu, with_prev, with_bias))
+
+
+def conv_taps(o):
+    rng = _rng(21)
+    x = rng.standard_normal((2, 3, 17))
+    for width in (1, 2, 3, 4):
+        keep_current = np.zeros((3, width))
+        keep_current[:, width - 1] = 1.0
+        assert np.array_equal(o.conv1d_f64(x, keep_current, silu=False), x), "current tap must return x (K=%d)" % width
+        keep_oldest = np.zeros((3, width))
+        keep_oldest[:, 0] = 1.0
+        prev = rng.standard_normal((2, 3, width - 1))
+        u = o.conv1d_f64(x, keep_oldest, x_prev=prev, silu=False)
+        assert np.array_equal(u[..., width - 1:], x[..., :17 - (width - 1)]), "oldest tap must shift (K=%d)" % width
+        assert np.array_equal(u[..., :width - 1], prev), "oldest tap must read x_prev first (K=%d)" % width
+        u0 = o.conv1d_f64(x, keep_oldest, silu=False)
+        assert not u0[..., :width - 1].any(), "no x_prev means zero history (K=%d)" % width
+
+
+def conv_causality(o):
+    rng = _rng(22)
+    for width in (2, 4):
+        p = _conv_problem(rng, 1, 2, 20, width)
+        u = o.conv1d_f64(p["x"], p["weight"], p["bias"], p["x_prev"], silu=True)
+        for pos in (0, 7, 19):
+            x2 = p["x"].copy()
+            x2[..., pos] += 3.0
+            u2 = o.conv1d_f64(x2, p["weight"], p["bias"], p["x_prev"], silu=True)
+            changed = np.abs(u2 - u).max(axis=(0, 1)) > 0
+            want = np.zeros(20, bool)
+            want[pos:pos + width] = True
+            assert np.array_equal(changed, want), "K=%d pos=%d changed %s" % (width, pos, np.nonzero(changed)[0])
+
+
+def conv_split_carry(o):
+    rng = _rng(23)
+    for width in (2, 3, 4):
+        p = _conv_problem(rng, 2, 3, 30, width)
+        u = o.conv1d_f64(p["x"], p["weight"], p["bias"], p["x_prev"], silu=True)
+        for cut in (width - 1, 11, 29):
+            u1 = o.conv1d_f64(p["x"][..., :cut], p["weight"], p["bias"], p["x_prev"], silu=True)
+            tail = np.concatenate([p["x_prev"], p["x"][..., :cut]], axis=-1)[..., -(width - 1):]
+            u2 = o.conv1d_f64(p["x"][..., cut:], p["weight"], p["bias"], tail, silu=True)
+            _close(np.concatenate([u1, u2], axis=-1), u, 1e-15, 1e-15, "conv split K=%d cut=%d" % (width, cut))
+
+
 ALL = [worked_examples, lti_closed_form, bruteforce, single_step, persistence, forgetting, split_carry, linearity,
-       softplus_silu, decode_is_scan, channel_subset]
+       softplus_silu, decode_is_scan, channel_subset, conv_library, conv_taps, conv_causality, conv_split_carry]

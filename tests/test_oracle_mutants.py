@@ -32,6 +32,12 @@ MUTANTS = [
     ("B_of_batch_0", "B + b * dstate * seqlen, C + b * dstate * seqlen,", "B, C + b * dstate * seqlen,"),
     ("abar_linearized", "double abar = exp(delta * A_row[n]);", "double abar = 1.0 + delta * A_row[n];"),
     ("state_not_decayed", "h[n] = abar * h[n] + bbar_u;", "h[n] = h[n] + bbar_u;"),
+    ("conv_taps_reversed", "acc += w[d * width + k] * v;", "acc += w[d * width + (width - 1 - k)] * v;"),
+    ("conv_off_by_one", "int64_t src = l - (width - 1) + k;", "int64_t src = l - width + k;"),
+    ("conv_prev_ignored", "v = x_prev ? x_prev[ch * (width - 1) + (width - 1) + src] : 0.0;", "v = 0.0;"),
+    ("conv_prev_reversed", "x_prev[ch * (width - 1) + (width - 1) + src]", "x_prev[ch * (width - 1) - 1 - src]"),
+    ("conv_bias_dropped", "double acc = cb ? cb[d] : 0.0;", "double acc = 0.0;"),
+    ("conv_silu_dropped", "u[ch * seqlen + l] = silu_flag ? oracle_silu(acc) : acc;", "u[ch * seqlen + l] = acc;"),
 ]
 
 
