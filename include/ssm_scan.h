@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 1
+#define SSM_ABI_VERSION 2
 
 struct ihipStream_t; /* the same incomplete type as HIP's hipStream_t */
 
@@ -130,6 +130,44 @@ ssm_status_t ssm_state_update(int64_t batch, int64_t dim, int64_t dstate, ssm_dt
                               const void* C, const float* D, const void* z,
                               const float* delta_bias, int softplus_flag, void* y,
                               struct ihipStream_t* stream);
+
+/*
+ * ssm_conv_scan_fwd -- the Mamba block's causal Conv1d fused in front of the
+ * scan.  The Hebrew overview ("תחילת העבודה עם Mamba") says the Mamba block
+ * runs a causal Conv1d before the selective SSM; the Chinese explainer's
+ * section on why a convolution precedes the SSM says it mixes each token
+ * with its neighbours first.  Read here as a depthwise (per-channel) causal
+ * filter of width K = conv_width (1..4) with an optional bias and silu:
+ *
+ *   u[b,d,l] = act(conv_bias[d] + sum_{k<K} conv_weight[d,k] * x[b,d,l-(K-1)+k])
+ *
+ * where x before token 0 is x_prev (the K-1 inputs that preceded this piece
+ * of the sequence) or zero, and act is silu when conv_silu is nonzero.  u is
+ * rounded to the io dtype, as if it had been stored, and then the scan of
+ * ssm_scan_fwd runs on it.  The result equals the conv written to memory
+ * followed by ssm_scan_fwd on it; where the single-pass path applies, u never
+ * touches memory (it is computed in the scan's prologue) unless u_out asks
+ * for it.
+ *
+ *   x            [batch, dim, seqlen]         io    conv input
+ *   conv_weight  [dim, conv_width]            fp32  conv_weight[d, K-1] multiplies the current token
+ *   conv_bias    [dim]                        fp32  may be NULL (0)
+ *   x_prev       [batch, dim, conv_width-1]   io    may be NULL (zero history); unused when conv_width == 1
+ *   conv_silu    nonzero: u = silu(conv + bias)
+ *   u_out        [batch, dim, seqlen]         io    the u the scan consumed, may be NULL
+ *   delta .. last_state, stream: as ssm_scan_fwd (y must not overlap any input,
+ *                                u_out must not overlap any input or output)
+ *
+ * Errors as ssm_scan_fwd, plus SSM_ERR_SHAPE for conv_width outside 1..4.
+ * Shapes that do not take the single-pass path run a separate conv kernel
+ * into u_out or into stream-ordered scratch from the library's pool.
+ */
+ssm_status_t ssm_conv_scan_fwd(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int64_t conv_width,
+                               ssm_dtype_t io, const void* x, const float* conv_weight, const float* conv_bias,
+                               const void* x_prev, int conv_silu, const void* delta, const float* A,
+                               const void* B, const void* C, const float* D, const void* z,
+                               const float* delta_bias, int softplus_flag, const float* h0, void* y,
+                               float* last_state, void* u_out, struct ihipStream_t* stream);
 
 /* Kernel paths of ssm_scan_fwd (reported by ssm_scan_fwd_plan). */
 typedef enum {

@@ -35,6 +35,8 @@ _I = ctypes.c_int
 SIGNATURES = {
     "ssm_scan_fwd": (_I, [_I64, _I64, _I64, _I64, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P]),
     "ssm_state_update": (_I, [_I64, _I64, _I64, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P]),
+    "ssm_conv_scan_fwd": (_I, [_I64, _I64, _I64, _I64, _I64, _I, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _I, _P,
+                               _P, _P, _P, _P]),
     "ssm_scan_fwd_plan": (_I, [_I64, _I64, _I64, _I64, _I, ctypes.POINTER(_I), ctypes.POINTER(_I64),
                               ctypes.POINTER(_I64), ctypes.POINTER(_I64)]),
     "ssm_status_string": (ctypes.c_char_p, [_I]),
@@ -178,6 +180,67 @@ def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=
                           _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias), 1 if delta_softplus else 0, _ptr(h0),
                           _ptr(out), _ptr(last_state), _stream(dev, stream))
     _check("ssm_scan_fwd", st)
+    return out, last_state
+
+
+def conv_scan_fwd(x, conv_weight, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=False,
+                  conv_bias=None, x_prev=None, conv_silu=True, h0=None, out=None, last_state=None, u_out=None,
+                  return_last_state=True, stream=None):
+    """Causal depthwise conv (+ silu) fused in front of the scan; returns (y, last_state).
+
+    x: (batch, dim, seqlen) in the io dtype; conv_weight: (dim, K) float32 with
+    K in 1..4 (conv_weight[:, K-1] multiplies the current token); conv_bias:
+    (dim,) float32; x_prev: (batch, dim, K-1) in the io dtype, the inputs before
+    token 0.  u = act(conv(x)) is rounded to the io dtype and scanned as
+    scan_fwd would scan it; u_out, when given, receives it.  The other
+    arguments are scan_fwd's.
+    """
+    import torch
+    if x.dim() != 3:
+        raise ValueError("x must be (batch, dim, seqlen)")
+    batch, dim, seqlen = x.shape
+    dstate = A.shape[-1]
+    dev = x.device
+    io = x.dtype
+    if conv_weight.dim() != 2:
+        raise ValueError("conv_weight must be (dim, K)")
+    width = conv_weight.shape[1]
+    _need(x, "x", (batch, dim, seqlen), io, dev)
+    _need(conv_weight, "conv_weight", (dim, width), torch.float32, dev)
+    if conv_bias is not None:
+        _need(conv_bias, "conv_bias", (dim,), torch.float32, dev)
+    if x_prev is not None and width > 1:
+        _need(x_prev, "x_prev", (batch, dim, width - 1), io, dev)
+    elif width == 1:
+        x_prev = None
+    _need(delta, "delta", (batch, dim, seqlen), io, dev)
+    _need(A, "A", (dim, dstate), torch.float32, dev)
+    _need(B, "B", (batch, dstate, seqlen), io, dev)
+    _need(C, "C", (batch, dstate, seqlen), io, dev)
+    if D is not None:
+        _need(D, "D", (dim,), torch.float32, dev)
+    if z is not None:
+        _need(z, "z", (batch, dim, seqlen), io, dev)
+    if delta_bias is not None:
+        _need(delta_bias, "delta_bias", (dim,), torch.float32, dev)
+    if h0 is not None:
+        _need(h0, "h0", (batch, dim, dstate), torch.float32, dev)
+    if out is None:
+        out = torch.empty((batch, dim, seqlen), dtype=io, device=dev)
+    else:
+        _need(out, "out", (batch, dim, seqlen), io, dev)
+    if last_state is None and return_last_state:
+        last_state = torch.empty((batch, dim, dstate), dtype=torch.float32, device=dev)
+    elif last_state is not None:
+        _need(last_state, "last_state", (batch, dim, dstate), torch.float32, dev)
+    if u_out is not None:
+        _need(u_out, "u_out", (batch, dim, seqlen), io, dev)
+    lib = load_library()
+    st = lib.ssm_conv_scan_fwd(batch, dim, dstate, seqlen, width, _io_code(io), _ptr(x), _ptr(conv_weight),
+                               _ptr(conv_bias), _ptr(x_prev), 1 if conv_silu else 0, _ptr(delta), _ptr(A), _ptr(B),
+                               _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias), 1 if delta_softplus else 0, _ptr(h0),
+                               _ptr(out), _ptr(last_state), _ptr(u_out), _stream(dev, stream))
+    _check("ssm_conv_scan_fwd", st)
     return out, last_state
 
 

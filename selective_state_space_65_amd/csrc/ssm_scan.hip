@@ -241,7 +241,28 @@ struct ScanArgs {
   int64_t groups;    // ceil(dim / 64)
   int64_t segments;  // P
   int64_t seg_len;   // tokens per segment, a multiple of kChunk
+  // Fused causal conv in front of the scan (single-pass kernel only): u
+  // then holds the conv input x.
+  const float* conv_w;  // [dim][conv_width]
+  const float* conv_b;  // [dim], may be null
+  const void* x_prev;   // [batch][dim][conv_width - 1], may be null
+  void* u_out;          // [batch][dim][seqlen], may be null
+  int conv_width;       // 1..4
+  int conv_silu;
 };
+
+// The causal depthwise conv of one token: acc = bias, then one FMA per tap
+// from the oldest input (xs[4 - K]) to the current one (xs[3]); taps a
+// narrower filter does not have are skipped, not multiplied by zero, so a
+// non-finite input reaches exactly the K outputs that read it.  The standalone
+// conv kernel and the fused prologue both use this, so they agree bitwise.
+template <int K>
+__device__ __forceinline__ float conv_taps(const float* xs, const float* w, float bias) {
+  float acc = bias;
+#pragma unroll
+  for (int k = 0; k < K; ++k) acc = __builtin_fmaf(w[k], xs[4 - K + k], acc);
+  return acc;
+}
 
 // Wave-uniform decomposition of a wave index into (segment, batch row, group).
 struct WaveCoord {
@@ -638,12 +659,14 @@ struct Piece {
   }
 };
 
-template <typename IoT, int N, int S, int SA, bool kZ, bool kSoftplus>
+template <typename IoT, int N, int S, int SA, bool kZ, bool kSoftplus, bool kConv>
 __global__ __launch_bounds__(64 * S) void scan_split_kernel(ScanArgs a) {
   using C = Split<IoT, N, S, SA>;
   constexpr int TS = C::TS;
   using LI = Line<IoT>;
   using PI = Piece<IoT, TS>;
+  using HI = Piece<IoT, 4>;          // the 4 inputs in front of a piece (conv history)
+  constexpr int HW = HI::kWords;
   using U = Uni<IoT>;
   constexpr int NS = C::NS, T = C::T, KT = C::KT, PW = PI::kWords, ZW = kZ ? PI::kWords : 1, W = U::kWords;
   // Double-buffered by tile parity: one barrier per tile (see below).
@@ -669,8 +692,19 @@ __global__ __launch_bounds__(64 * S) void scan_split_kernel(ScanArgs a) {
   }
   const float Dd = a.D ? a.D[d] : 0.0f;
   const float bias = a.bias ? a.bias[d] : 0.0f;
+  // Fused conv: the channel's filter taps, oldest first.
+  float cw[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  float cbias = 0.0f;
+  const int K = kConv ? a.conv_width : 1;
+  if constexpr (kConv) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (k < K) cw[k] = a.conv_w[d * K + k];
+    cbias = a.conv_b ? a.conv_b[d] : 0.0f;
+  }
 
-  const IoT* ur = static_cast<const IoT*>(a.u) + ch * L;
+  const IoT* ur = static_cast<const IoT*>(a.u) + ch * L;  // x when the conv is fused
+  IoT* uo = kConv && a.u_out ? static_cast<IoT*>(a.u_out) + ch * L : nullptr;
   const IoT* dr = static_cast<const IoT*>(a.delta) + ch * L;
   const IoT* zr = kZ ? static_cast<const IoT*>(a.z) + ch * L : nullptr;
   IoT* yr = static_cast<IoT*>(a.y) + ch * L;
@@ -715,11 +749,85 @@ __global__ __launch_bounds__(64 * S) void scan_split_kernel(ScanArgs a) {
   //   c*: tile i   (u, z kept for phase C of tile i)
   //   a*: tile i+1 (widened by phase A of tile i+1)
   //   n*: tile i+2 (fetched during phase A of tile i+1)
+  // With the conv fused, the a* and n* pieces hold x (plus the four inputs in
+  // front of the piece, ah/nh) until phase A turns them into u.
   uint32_t pu[PW], pz[ZW], cu[PW], cz[ZW], au[PW], ad[PW], az[ZW], nu[PW], nd[PW], nz[ZW];
-  auto fetch = [&](int64_t l, uint32_t (&qu)[PW], uint32_t (&qd)[PW], uint32_t (&qz)[ZW]) {
-    PI::load(ur + l + w * TS, qu);
-    PI::load(dr + l + w * TS, qd);
-    if constexpr (kZ) PI::load(zr + l + w * TS, qz);
+  uint32_t ah[HW], nh[HW];
+  auto fetch = [&](int64_t l, uint32_t (&qu)[PW], uint32_t (&qd)[PW], uint32_t (&qz)[ZW], uint32_t (&qh)[HW]) {
+    const int64_t p0 = l + w * TS;
+    PI::load(ur + p0, qu);
+    PI::load(dr + p0, qd);
+    if constexpr (kZ) PI::load(zr + p0, qz);
+    if constexpr (kConv) {
+      if (p0 > 0) {
+        HI::load(ur + p0 - 4, qh);
+      } else {
+        // Token 0: the history is x_prev (the last K-1 of its slots), else zero.
+        float hv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int idx = (K - 1) - 4 + i;  // x_prev slot of position i - 4
+          hv[i] = (a.x_prev && idx >= 0)
+                      ? Io<IoT>::load1(static_cast<const IoT*>(a.x_prev) + ch * (K - 1) + idx)
+                      : 0.0f;
+        }
+        if constexpr (sizeof(IoT) == 4) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) qh[i] = __float_as_uint(hv[i]);
+        } else {
+          // bf16 values widen exactly, so their upper halves are the raw bits.
+#pragma unroll
+          for (int i = 0; i < 2; ++i) qh[i] = (__float_as_uint(hv[2 * i]) >> 16) | (__float_as_uint(hv[2 * i + 1]) & 0xffff0000u);
+        }
+      }
+    }
+  };
+  // The conv of one piece: x words (and their history) in, u words out,
+  // rounded to the io dtype exactly as a stored u would be.
+  auto conv_piece = [&](uint32_t (&q)[PW], const uint32_t (&qh)[HW]) {
+    float xs[TS + 4];  // xs[i] = input at position i - 4 relative to the piece
+#pragma unroll
+    for (int i = 0; i < 4; ++i) xs[i] = LI::elem(qh, i);
+#pragma unroll
+    for (int t = 0; t < TS; ++t) xs[4 + t] = LI::elem(q, t);
+    float uv[TS];
+    switch (K) {
+      case 1:
+#pragma unroll
+        for (int t = 0; t < TS; ++t) uv[t] = conv_taps<1>(xs + t + 1, cw, cbias);
+        break;
+      case 2:
+#pragma unroll
+        for (int t = 0; t < TS; ++t) uv[t] = conv_taps<2>(xs + t + 1, cw, cbias);
+        break;
+      case 3:
+#pragma unroll
+        for (int t = 0; t < TS; ++t) uv[t] = conv_taps<3>(xs + t + 1, cw, cbias);
+        break;
+      default:
+#pragma unroll
+        for (int t = 0; t < TS; ++t) uv[t] = conv_taps<4>(xs + t + 1, cw, cbias);
+        break;
+    }
+    if (a.conv_silu) {
+#pragma unroll
+      for (int t = 0; t < TS; ++t) uv[t] = silu_f32(uv[t]);
+    }
+    if constexpr (sizeof(IoT) == 4) {
+#pragma unroll
+      for (int t = 0; t < TS; ++t) q[t] = __float_as_uint(uv[t]);
+    } else {
+#pragma unroll
+      for (int t = 0; t < TS / 2; ++t) q[t] = Io<bf16_t>::pack2(uv[2 * t], uv[2 * t + 1]);
+    }
+  };
+  // Phase A prologue for the piece of the tile at lt: with the conv fused,
+  // x becomes u (stored to u_out when asked).
+  auto make_u = [&](int64_t lt) {
+    if constexpr (kConv) {
+      conv_piece(au, ah);
+      if (uo && active) PI::store(uo + lt + w * TS, au);
+    }
   };
   // Phase A: widen this wave's tokens of a tile and publish (Delta, x).
   auto widen = [&](int buf, const uint32_t (&qu)[PW], const uint32_t (&qd)[PW]) {
@@ -760,8 +868,9 @@ __global__ __launch_bounds__(64 * S) void scan_split_kernel(ScanArgs a) {
   auto owns = [&](int64_t l) { return w < SA && l < L && l + w * TS < L; };
 
   if (owns(0)) {
-    fetch(0, au, ad, az);
-    if (owns(T)) fetch(T, nu, nd, nz);
+    fetch(0, au, ad, az, ah);
+    if (owns(T)) fetch(T, nu, nd, nz, nh);
+    make_u(0);
     widen(0, au, ad);
 #pragma unroll
     for (int q = 0; q < PW; ++q) {
@@ -770,6 +879,10 @@ __global__ __launch_bounds__(64 * S) void scan_split_kernel(ScanArgs a) {
       au[q] = nu[q];
       ad[q] = nd[q];
       if constexpr (kZ) az[q] = nz[q];
+    }
+    if constexpr (kConv) {
+#pragma unroll
+      for (int q = 0; q < HW; ++q) ah[q] = nh[q];
     }
   }
   __syncthreads();
@@ -798,7 +911,8 @@ __global__ __launch_bounds__(64 * S) void scan_split_kernel(ScanArgs a) {
     __builtin_amdgcn_sched_barrier(0);
     // ---- A of the next tile
     if (owns(l + T)) {
-      if (owns(l + 2 * T)) fetch(l + 2 * T, nu, nd, nz);
+      if (owns(l + 2 * T)) fetch(l + 2 * T, nu, nd, nz, nh);
+      make_u(l + T);
       widen(buf ^ 1, au, ad);
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -860,6 +974,11 @@ __global__ __launch_bounds__(64 * S) void scan_split_kernel(ScanArgs a) {
       au[q] = nu[q];
       ad[q] = nd[q];
       if constexpr (kZ) az[q] = nz[q];
+    }
+    if constexpr (kConv) {
+#pragma unroll
+      for (int q = 0; q < HW; ++q) ah[q] = nh[q];
+      settle_vgprs(ah);
     }
     settle_vgprs(au);
     settle_vgprs(ad);
@@ -1207,30 +1326,78 @@ hipError_t launch_scan_f(const ScanArgs& a, const Plan& p, hipStream_t st, bool 
   return sp ? launch_scan_t<IoT, N, false, true, kVec>(a, p, st) : launch_scan_t<IoT, N, false, false, kVec>(a, p, st);
 }
 
-template <typename IoT, int N, int S, int SA, bool kZ, bool kSp>
+template <typename IoT, int N, int S, int SA, bool kZ, bool kSp, bool kConv>
 hipError_t launch_split_t(const ScanArgs& a, const Plan& p, hipStream_t st) {
-  hipLaunchKernelGGL((scan_split_kernel<IoT, N, S, SA, kZ, kSp>), dim3((unsigned)(a.batch * p.groups)), dim3(64 * S),
-                     0, st, a);
+  hipLaunchKernelGGL((scan_split_kernel<IoT, N, S, SA, kZ, kSp, kConv>), dim3((unsigned)(a.batch * p.groups)),
+                     dim3(64 * S), 0, st, a);
   return hipGetLastError();
 }
 
-template <typename IoT, int N>
+template <typename IoT, int N, bool kConv>
 hipError_t launch_split(const ScanArgs& a, const Plan& p, hipStream_t st, bool sp) {
   constexpr int S = (N >= SSM_SPLIT_WAVES) ? SSM_SPLIT_WAVES : N;
   // Phases A and C run on one wave per SIMD (the first four waves).
   constexpr int SA = (S > 4) ? 4 : S;
-  if (a.z) return sp ? launch_split_t<IoT, N, S, SA, true, true>(a, p, st) : launch_split_t<IoT, N, S, SA, true, false>(a, p, st);
-  return sp ? launch_split_t<IoT, N, S, SA, false, true>(a, p, st) : launch_split_t<IoT, N, S, SA, false, false>(a, p, st);
+  if (a.z)
+    return sp ? launch_split_t<IoT, N, S, SA, true, true, kConv>(a, p, st)
+              : launch_split_t<IoT, N, S, SA, true, false, kConv>(a, p, st);
+  return sp ? launch_split_t<IoT, N, S, SA, false, true, kConv>(a, p, st)
+            : launch_split_t<IoT, N, S, SA, false, false, kConv>(a, p, st);
+}
+
+template <typename IoT, int N>
+hipError_t launch_split_c(const ScanArgs& a, const Plan& p, hipStream_t st, bool sp, bool conv) {
+  return conv ? launch_split<IoT, N, true>(a, p, st, sp) : launch_split<IoT, N, false>(a, p, st, sp);
+}
+
+// The causal depthwise conv as a kernel of its own (shapes the single-pass
+// kernel does not take): one thread per output element, u rounded to IoT.
+template <typename IoT>
+__global__ __launch_bounds__(kBlockThreads) void conv1d_kernel(ScanArgs a, IoT* u) {
+  const int64_t i = (int64_t)blockIdx.x * kBlockThreads + threadIdx.x;
+  const int64_t L = a.seqlen;
+  if (i >= a.batch * a.dim * L) return;
+  const int64_t ch = i / L, l = i % L, d = ch % a.dim;
+  const int K = a.conv_width;
+  const IoT* x = static_cast<const IoT*>(a.u) + ch * L;
+  const IoT* xp = static_cast<const IoT*>(a.x_prev);
+  float w[4], xs[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) w[k] = k < K ? a.conv_w[d * K + k] : 0.0f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {  // xs[j] = input at position l - 3 + j
+    const int64_t pos = l - 3 + j;
+    const int64_t slot = (K - 1) + pos;  // x_prev slot of a negative position
+    xs[j] = pos >= 0 ? Io<IoT>::load1(x + pos) : ((xp && slot >= 0) ? Io<IoT>::load1(xp + ch * (K - 1) + slot) : 0.0f);
+  }
+  const float cb = a.conv_b ? a.conv_b[d] : 0.0f;
+  float acc;
+  switch (K) {
+    case 1: acc = conv_taps<1>(xs, w, cb); break;
+    case 2: acc = conv_taps<2>(xs, w, cb); break;
+    case 3: acc = conv_taps<3>(xs, w, cb); break;
+    default: acc = conv_taps<4>(xs, w, cb); break;
+  }
+  if (a.conv_silu) acc = silu_f32(acc);
+  Io<IoT>::store1(u + i, acc);
+}
+
+template <typename IoT>
+hipError_t launch_conv(const ScanArgs& a, void* u, hipStream_t st) {
+  const int64_t total = a.batch * a.dim * a.seqlen;
+  const int64_t blocks = (total + kBlockThreads - 1) / kBlockThreads;
+  hipLaunchKernelGGL((conv1d_kernel<IoT>), dim3((unsigned)blocks), dim3(kBlockThreads), 0, st, a, static_cast<IoT*>(u));
+  return hipGetLastError();
 }
 
 // Vector kernels exist for dstate in {4, 8, 16}; every other case runs the
 // scalar-token kernel instantiated for up to 16 states.
 template <typename IoT>
-hipError_t launch_scan(const ScanArgs& a, const Plan& p, hipStream_t st, bool vec, bool sp) {
+hipError_t launch_scan(const ScanArgs& a, const Plan& p, hipStream_t st, bool vec, bool sp, bool conv = false) {
   if (vec && p.split) {
-    if (a.dstate == 4) return launch_split<IoT, 4>(a, p, st, sp);
-    if (a.dstate == 8) return launch_split<IoT, 8>(a, p, st, sp);
-    return launch_split<IoT, 16>(a, p, st, sp);
+    if (a.dstate == 4) return launch_split_c<IoT, 4>(a, p, st, sp, conv);
+    if (a.dstate == 8) return launch_split_c<IoT, 8>(a, p, st, sp, conv);
+    return launch_split_c<IoT, 16>(a, p, st, sp, conv);
   }
   if (vec) {
     if (a.dstate == 4) return launch_scan_f<IoT, 4, true>(a, p, st, sp);
@@ -1278,6 +1445,98 @@ hipError_t launch_update(const UpdateArgs& a, hipStream_t st, bool generic, bool
 // C ABI
 // ----------------------------------------------------------------------------
 
+// Host-side checks shared by the prefill entry points: element alignment,
+// and no output overlapping an input or another output (h0 may be exactly
+// last_state).  extra: further input ranges (the conv's); u_out: an extra
+// output of bdl io elements, or null.
+ssm_status_t check_scan_buffers(const Shape& sh, int64_t dim, ssm_dtype_t io, const void* u, const void* delta,
+                                const float* A, const void* B, const void* C, const float* D, const void* z,
+                                const float* delta_bias, const float* h0, const void* y, const float* last_state,
+                                const Range* extra, int n_extra, const void* u_out) {
+  const size_t es = io_size(io);
+  const void* io_ptrs[] = {u, delta, B, C, z, y, u_out};
+  for (const void* p : io_ptrs)
+    if (p && !aligned(p, es)) return SSM_ERR_ALIGN;
+  const void* f_ptrs[] = {A, D, delta_bias, h0, last_state};
+  for (const void* p : f_ptrs)
+    if (p && !aligned(p, 4)) return SSM_ERR_ALIGN;
+  Range ins[12];
+  int n = 0;
+  ins[n++] = span(u, sh.bdl * (int64_t)es);
+  ins[n++] = span(delta, sh.bdl * (int64_t)es);
+  ins[n++] = span(B, sh.bnl * (int64_t)es);
+  ins[n++] = span(C, sh.bnl * (int64_t)es);
+  ins[n++] = z ? span(z, sh.bdl * (int64_t)es) : Range{0, 0};
+  ins[n++] = span(A, sh.dn * 4);
+  ins[n++] = D ? span(D, dim * 4) : Range{0, 0};
+  ins[n++] = delta_bias ? span(delta_bias, dim * 4) : Range{0, 0};
+  for (int i = 0; i < n_extra; ++i) ins[n++] = extra[i];
+  const Range rh0 = h0 ? span(h0, sh.bdn * 4) : Range{0, 0};
+  const Range outs[] = {span(y, sh.bdl * (int64_t)es), last_state ? span(last_state, sh.bdn * 4) : Range{0, 0},
+                        u_out ? span(u_out, sh.bdl * (int64_t)es) : Range{0, 0}};
+  for (int o = 0; o < 3; ++o) {
+    if (outs[o].hi <= outs[o].lo) continue;
+    for (int i = 0; i < n; ++i)
+      if (ins[i].hi > ins[i].lo && overlap(outs[o], ins[i])) return SSM_ERR_ALIAS;
+    // h0 is an input too, except that last_state may be the very same buffer.
+    if (rh0.hi > rh0.lo && overlap(outs[o], rh0) && !(o == 1 && h0 == last_state)) return SSM_ERR_ALIAS;
+    for (int q = o + 1; q < 3; ++q)
+      if (outs[q].hi > outs[q].lo && overlap(outs[o], outs[q])) return SSM_ERR_ALIAS;
+  }
+  return SSM_OK;
+}
+
+// Vector path: whole 16-byte chunks on every row, and B/C batch slabs
+// addressable with 32-bit byte offsets.
+bool vec_rows(const Shape&, int64_t dstate, int64_t seqlen, ssm_dtype_t io, const void* u, const void* delta,
+              const void* B, const void* C, const void* z, const void* y) {
+  return (seqlen % kChunk == 0) && aligned(u, 16) && aligned(delta, 16) && aligned(y, 16) && (!z || aligned(z, 16)) &&
+         aligned(B, 16) && aligned(C, 16) && dstate * seqlen * (int64_t)io_size(io) < ((int64_t)1 << 31);
+}
+
+ScanArgs scan_args(const Shape&, int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, ssm_dtype_t io,
+                   const void* u, const void* delta, const float* A, const void* B, const void* C, const float* D,
+                   const void* z, const float* delta_bias, const float* h0, void* y, float* last_state) {
+  (void)io;
+  ScanArgs a;
+  a.u = u; a.delta = delta; a.A = A; a.B = B; a.C = C; a.D = D; a.z = z; a.bias = delta_bias; a.h0 = h0;
+  a.y = y; a.last_state = last_state; a.agg_sum = nullptr; a.agg_h = nullptr; a.carry = nullptr;
+  a.batch = batch; a.dim = dim; a.dstate = dstate; a.seqlen = seqlen;
+  a.groups = 0; a.segments = 0; a.seg_len = 0;
+  a.conv_w = nullptr; a.conv_b = nullptr; a.x_prev = nullptr; a.u_out = nullptr; a.conv_width = 1; a.conv_silu = 0;
+  return a;
+}
+
+// Plans and launches the scan of a validated call, with the segment scratch
+// (if the plan needs it) taken from the pool and released on the stream.
+// conv: the conv is fused (a.u holds x); only the single-pass vector path
+// takes it, which the caller has checked.
+ssm_status_t run_scan(ScanArgs& a, const Shape& sh, ssm_dtype_t io, bool vec, bool sp, bool conv, hipStream_t hs) {
+  const Plan plan = make_plan(sh, a.batch, a.dim, a.dstate, a.seqlen, io);
+  a.groups = plan.groups; a.segments = plan.segments; a.seg_len = plan.seg_len;
+  void* scratch = nullptr;
+  if (plan.scratch_bytes > 0) {
+    hipMemPool_t pool;
+    hipError_t e = get_pool(&pool);
+    if (e != hipSuccess) return hip_fail(e);
+    e = hipMallocFromPoolAsync(&scratch, (size_t)plan.scratch_bytes, pool, hs);
+    if (e != hipSuccess) return hip_fail(e);
+    float* f = static_cast<float*>(scratch);
+    const int64_t P = plan.segments;
+    a.agg_sum = f;
+    a.agg_h = f + (P - 1) * sh.bd;
+    a.carry = a.agg_h + (P - 1) * sh.bdn;
+  }
+  hipError_t e = (io == SSM_BF16) ? launch_scan<bf16_t>(a, plan, hs, vec, sp, conv)
+                                  : launch_scan<float>(a, plan, hs, vec, sp, conv);
+  if (scratch) {
+    hipError_t ef = hipFreeAsync(scratch, hs);
+    if (e == hipSuccess) e = ef;
+  }
+  if (e != hipSuccess) return hip_fail(e);
+  return SSM_OK;
+}
+
 extern "C" {
 
 int ssm_abi_version(void) { return SSM_ABI_VERSION; }
@@ -1321,67 +1580,68 @@ ssm_status_t ssm_scan_fwd(int64_t batch, int64_t dim, int64_t dstate, int64_t se
   ssm_status_t st = shape_of(batch, dim, dstate, seqlen, io, &sh);
   if (st != SSM_OK) return st;
   if (!u || !delta || !A || !B || !C || !y) return SSM_ERR_NULL;
+  st = check_scan_buffers(sh, dim, io, u, delta, A, B, C, D, z, delta_bias, h0, y, last_state, nullptr, 0, nullptr);
+  if (st != SSM_OK) return st;
+  ScanArgs a = scan_args(sh, batch, dim, dstate, seqlen, io, u, delta, A, B, C, D, z, delta_bias, h0, y, last_state);
+  return run_scan(a, sh, io, vec_rows(sh, dstate, seqlen, io, u, delta, B, C, z, y), softplus_flag != 0, false,
+                  reinterpret_cast<hipStream_t>(stream));
+}
+
+ssm_status_t ssm_conv_scan_fwd(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int64_t conv_width,
+                               ssm_dtype_t io, const void* x, const float* conv_weight, const float* conv_bias,
+                               const void* x_prev, int conv_silu, const void* delta, const float* A,
+                               const void* B, const void* C, const float* D, const void* z,
+                               const float* delta_bias, int softplus_flag, const float* h0, void* y,
+                               float* last_state, void* u_out, struct ihipStream_t* stream) {
+  Shape sh;
+  ssm_status_t st = shape_of(batch, dim, dstate, seqlen, io, &sh);
+  if (st != SSM_OK) return st;
+  if (conv_width < 1 || conv_width > 4) return SSM_ERR_SHAPE;
+  if (!x || !conv_weight || !delta || !A || !B || !C || !y) return SSM_ERR_NULL;
+  if (conv_width == 1) x_prev = nullptr;  // no history to read
   const size_t es = io_size(io);
-  const void* io_ptrs[] = {u, delta, B, C, z, y};
-  for (const void* p : io_ptrs)
-    if (p && !aligned(p, es)) return SSM_ERR_ALIGN;
-  const void* f_ptrs[] = {A, D, delta_bias, h0, last_state};
-  for (const void* p : f_ptrs)
-    if (p && !aligned(p, 4)) return SSM_ERR_ALIGN;
-
-  // Outputs must not overlap inputs; h0 may be exactly last_state.
-  const Range ry = span(y, sh.bdl * (int64_t)es);
-  const Range ins[] = {span(u, sh.bdl * (int64_t)es), span(delta, sh.bdl * (int64_t)es),
-                       span(B, sh.bnl * (int64_t)es), span(C, sh.bnl * (int64_t)es),
-                       z ? span(z, sh.bdl * (int64_t)es) : Range{0, 0}, span(A, sh.dn * 4),
-                       D ? span(D, dim * 4) : Range{0, 0}, delta_bias ? span(delta_bias, dim * 4) : Range{0, 0},
-                       h0 ? span(h0, sh.bdn * 4) : Range{0, 0}};
-  for (const Range& r : ins)
-    if (r.hi > r.lo && overlap(ry, r)) return SSM_ERR_ALIAS;
-  if (last_state) {
-    const Range rl = span(last_state, sh.bdn * 4);
-    if (overlap(rl, ry)) return SSM_ERR_ALIAS;
-    for (int i = 0; i < 8; ++i)
-      if (ins[i].hi > ins[i].lo && overlap(rl, ins[i])) return SSM_ERR_ALIAS;
-    if (h0 && h0 != last_state && overlap(rl, ins[8])) return SSM_ERR_ALIAS;
-  }
-
-  const Plan plan = make_plan(sh, batch, dim, dstate, seqlen, io);
-  // Vector path: whole 16-byte chunks on every row, and B/C batch slabs
-  // addressable with 32-bit byte offsets.
-  const bool vec = (seqlen % kChunk == 0) && aligned(u, 16) && aligned(delta, 16) && aligned(y, 16) &&
-                   (!z || aligned(z, 16)) && aligned(B, 16) && aligned(C, 16) &&
-                   dstate * seqlen * (int64_t)es < ((int64_t)1 << 31);
-
-  ScanArgs a;
-  a.u = u; a.delta = delta; a.A = A; a.B = B; a.C = C; a.D = D; a.z = z; a.bias = delta_bias; a.h0 = h0;
-  a.y = y; a.last_state = last_state; a.agg_sum = nullptr; a.agg_h = nullptr; a.carry = nullptr;
-  a.batch = batch; a.dim = dim; a.dstate = dstate; a.seqlen = seqlen;
-  a.groups = plan.groups; a.segments = plan.segments; a.seg_len = plan.seg_len;
+  if (x_prev && !aligned(x_prev, es)) return SSM_ERR_ALIGN;
+  if (!aligned(conv_weight, 4) || (conv_bias && !aligned(conv_bias, 4))) return SSM_ERR_ALIGN;
+  const Range conv_ins[] = {span(conv_weight, dim * conv_width * 4), conv_bias ? span(conv_bias, dim * 4) : Range{0, 0},
+                            x_prev ? span(x_prev, sh.bd * (conv_width - 1) * (int64_t)es) : Range{0, 0}};
+  st = check_scan_buffers(sh, dim, io, x, delta, A, B, C, D, z, delta_bias, h0, y, last_state, conv_ins, 3, u_out);
+  if (st != SSM_OK) return st;
 
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-  void* scratch = nullptr;
-  if (plan.scratch_bytes > 0) {
+  ScanArgs a = scan_args(sh, batch, dim, dstate, seqlen, io, x, delta, A, B, C, D, z, delta_bias, h0, y, last_state);
+  a.conv_w = conv_weight; a.conv_b = conv_bias; a.x_prev = x_prev; a.u_out = u_out;
+  a.conv_width = (int)conv_width; a.conv_silu = conv_silu != 0;
+  const Plan plan = make_plan(sh, batch, dim, dstate, seqlen, io);
+  const bool sp = softplus_flag != 0;
+  // Fused: the single-pass kernel computes u in its prologue.  Its u_out
+  // stores are whole 16- or 32-byte pieces, so they need 16-byte rows too.
+  if (plan.split && vec_rows(sh, dstate, seqlen, io, x, delta, B, C, z, y) && (!u_out || aligned(u_out, 16)))
+    return run_scan(a, sh, io, true, sp, true, hs);
+
+  // Otherwise the conv writes u (to u_out, else to pool scratch) and the
+  // plain scan reads it.
+  void* ubuf = u_out;
+  if (!ubuf) {
     hipMemPool_t pool;
     hipError_t e = get_pool(&pool);
     if (e != hipSuccess) return hip_fail(e);
-    e = hipMallocFromPoolAsync(&scratch, (size_t)plan.scratch_bytes, pool, hs);
+    e = hipMallocFromPoolAsync(&ubuf, (size_t)(sh.bdl * (int64_t)es), pool, hs);
     if (e != hipSuccess) return hip_fail(e);
-    float* f = static_cast<float*>(scratch);
-    const int64_t P = plan.segments;
-    a.agg_sum = f;
-    a.agg_h = f + (P - 1) * sh.bd;
-    a.carry = a.agg_h + (P - 1) * sh.bdn;
   }
-  const bool sp = softplus_flag != 0;
-  hipError_t e = (io == SSM_BF16) ? launch_scan<bf16_t>(a, plan, hs, vec, sp)
-                                  : launch_scan<float>(a, plan, hs, vec, sp);
-  if (scratch) {
-    hipError_t ef = hipFreeAsync(scratch, hs);
-    if (e == hipSuccess) e = ef;
+  hipError_t e = (io == SSM_BF16) ? launch_conv<bf16_t>(a, ubuf, hs) : launch_conv<float>(a, ubuf, hs);
+  ssm_status_t out = SSM_OK;
+  if (e != hipSuccess) {
+    out = hip_fail(e);
+  } else {
+    a.u = ubuf;
+    a.conv_w = nullptr; a.conv_b = nullptr; a.x_prev = nullptr; a.u_out = nullptr;
+    out = run_scan(a, sh, io, vec_rows(sh, dstate, seqlen, io, ubuf, delta, B, C, z, y), sp, false, hs);
   }
-  if (e != hipSuccess) return hip_fail(e);
-  return SSM_OK;
+  if (!u_out) {
+    hipError_t ef = hipFreeAsync(ubuf, hs);
+    if (out == SSM_OK && ef != hipSuccess) out = hip_fail(ef);
+  }
+  return out;
 }
 
 ssm_status_t ssm_state_update(int64_t batch, int64_t dim, int64_t dstate, ssm_dtype_t io, float* state, const void* u,

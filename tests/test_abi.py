@@ -122,6 +122,38 @@ def test_update_validation(lib):
     assert upd(lib, state=addr(2)) == 6             # state on u
 
 
+def cfwd(lib, batch=2, dim=8, dstate=4, seqlen=16, width=4, io=0, **over):
+    args = dict(x=addr(1), w=addr(12), cb=addr(13), xp=addr(14), silu=1, delta=addr(2), A=addr(3), B=addr(4),
+                C=addr(5), D=addr(6), z=addr(7), bias=addr(8), sp=1, h0=addr(9), y=addr(10), last=addr(11),
+                uo=addr(15))
+    args.update(over)
+    return lib.ssm_conv_scan_fwd(batch, dim, dstate, seqlen, width, io, args["x"], args["w"], args["cb"], args["xp"],
+                                 args["silu"], args["delta"], args["A"], args["B"], args["C"], args["D"], args["z"],
+                                 args["bias"], args["sp"], args["h0"], args["y"], args["last"], args["uo"], None)
+
+
+@pytest.mark.parametrize("field", ["x", "w", "delta", "A", "B", "C", "y"])
+def test_conv_scan_null_required(lib, field):
+    assert cfwd(lib, **{field: None}) == 1
+
+
+@pytest.mark.parametrize("width", [0, 5, -1])
+def test_conv_scan_bad_width(lib, width):
+    assert cfwd(lib, width=width) == 2
+
+
+def test_conv_scan_misaligned_and_aliasing(lib):
+    assert cfwd(lib, xp=addr(14) + 2) == 5          # fp32 x_prev needs 4-byte alignment
+    assert cfwd(lib, w=addr(12) + 2) == 5
+    assert cfwd(lib, io=1, uo=addr(15) + 1) == 5    # bf16 u_out needs 2-byte alignment
+    assert cfwd(lib, uo=addr(1)) == 6               # u_out on x
+    assert cfwd(lib, uo=addr(10)) == 6              # u_out on y
+    assert cfwd(lib, uo=addr(11)) == 6              # u_out on last_state
+    assert cfwd(lib, y=addr(12)) == 6               # y on the conv weights
+    assert cfwd(lib, y=addr(14)) == 6               # y on x_prev
+    assert cfwd(lib, last=addr(13)) == 6            # last_state on the conv bias
+
+
 def test_plan(lib):
     import torch
     path, seg, seglen, scratch = binding.scan_plan(4, 4096, 16, 4096, torch.bfloat16, with_path=True)
