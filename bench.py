@@ -13,6 +13,8 @@ the timed region.  Prints one JSON line:
                same workload
   decode       the one-token state update at the decode workload (batch 256,
                dim 5120, dstate 16), per step
+  conv_scan    ssm_conv_scan_fwd (causal conv of width 4 fused in front of the
+               scan) on the same workload
 
 Algorithmic bytes: read u, delta, z and write y once (4 x io bytes per
 element), read B and C once per (batch, token), read A, D and the bias once,
@@ -154,6 +156,30 @@ def bench_decode(dev, steps, warmup):
                      "Cache, which sits behind the L2 and may serve part of it, so this is not pure HBM traffic")
 
 
+def bench_conv_scan(dev, x, t, steps, warmup):
+    """ssm_conv_scan_fwd on the same workload with u replaced by the conv input x
+    (width 4, bias and silu on, no history): the conv rides in the scan's prologue."""
+    import torch
+    from selective_state_space_65_amd import binding, inputs
+    b, d, n, l = x.shape
+    w, cb = inputs.conv_params(d, 4)
+    wt, cbt = torch.from_numpy(w).to(dev), torch.from_numpy(cb).to(dev)
+    y = torch.empty_like(t["u"])
+    last = torch.empty((b, d, n), dtype=torch.float32, device=dev)
+
+    def fn():
+        binding.conv_scan_fwd(t["u"], wt, t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
+                              delta_bias=t["delta_bias"], delta_softplus=x.softplus, conv_bias=cbt, conv_silu=True,
+                              out=y, last_state=last)
+
+    wall_ms, avg_ms, med_ms = time_calls(fn, steps, warmup)
+    io_bytes = 2 if x.io == "bf16" else 4
+    nbytes = algorithmic_bytes(b, d, n, l, io_bytes, has_z=x.z is not None) + d * 4 * 4 + d * 4
+    return dict(workload="causal conv (width 4, bias, silu) fused in front of the scan, same shape",
+                us_per_call=round(avg_ms * 1e3, 2), us_median=round(med_ms * 1e3, 2),
+                algorithmic_gbs=round(nbytes / (avg_ms * 1e-3) / 1e9, 1), algorithmic_bytes=nbytes)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -163,6 +189,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-conv", action="store_true", help="skip the fused conv + scan line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy 1 GiB three times (reference kernel for rocprofv3 FETCH_SIZE/WRITE_SIZE)")
     args = ap.parse_args()
@@ -229,6 +256,8 @@ def main():
                roofline=roof)
     if not args.no_decode:
         out["decode"] = bench_decode(dev, 50, 5)
+    if not args.no_conv:
+        out["conv_scan"] = bench_conv_scan(dev, x, t, args.steps, args.warmup)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(x, args.cpu_seconds)
     print(json.dumps(out), flush=True)

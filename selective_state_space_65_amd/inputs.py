@@ -111,6 +111,15 @@ def scan_config(i, **overrides):
     return x
 
 
+def conv_params(dim, width=4, seed=SEED_BASE + 10):
+    """Depthwise causal conv filter (dim, width) and bias (dim,), float32, for the
+    conv fused in front of the scan: taps ~ N(0, 1/width), bias ~ N(0, 0.1^2)."""
+    rng = np.random.default_rng(seed)
+    w = _normal(rng, (dim, width), 1.0 / np.sqrt(width))
+    cb = _normal(rng, (dim,), 0.1)
+    return w, cb
+
+
 @dataclass
 class DecodeInputs:
     state0: np.ndarray  # (batch, dim, dstate) float32
