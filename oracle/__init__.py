@@ -13,6 +13,7 @@ this module only marshals numpy arrays into it.
                            (channels are independent, so a subset is exact)
   .state_update_f64(...)   one-token update of a float64 state, in place
   .state_update_channels_f64(...)  the same for chosen (b, d) channels
+  .scan_bwd_f64(...)       gradients of the scan (reverse mode, written out by hand)
   .conv1d_f64(...)         the causal depthwise conv (+ silu) in front of the scan
   .softplus_f64, .silu_f64 the scalar helpers the C oracle uses
 Module-level functions of the same names use the default oracle.
@@ -56,6 +57,8 @@ class Oracle:
         L.oracle_scan_f64.argtypes = [I64, I64, I64, I64] + [P] * 8 + [I, P, P, P]
         L.oracle_state_update_f64.restype = I
         L.oracle_state_update_f64.argtypes = [I64, I64, I64] + [P] * 9 + [I, P]
+        L.oracle_scan_bwd_f64.restype = I
+        L.oracle_scan_bwd_f64.argtypes = [I64, I64, I64, I64] + [P] * 8 + [I] + [P] * 12
         L.oracle_conv1d_f64.restype = I
         L.oracle_conv1d_f64.argtypes = [I64, I64, I64, I64, P, P, P, P, I, P]
         L.oracle_softplus.restype = ctypes.c_double
@@ -83,6 +86,32 @@ class Oracle:
         if rc != 0:
             raise ValueError("oracle_scan_f64 rejected the arguments")
         return y, last
+
+    def scan_bwd_f64(self, u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=False, h0=None, dy=None,
+                     dlast=None):
+        """Gradients of sum(dy * y) + sum(dlast * last_state) with respect to every input.
+
+        Returns a dict with du, ddelta (batch, dim, seqlen), dA (dim, dstate),
+        dB, dC (batch, dstate, seqlen), and dD (dim,), dz, ddelta_bias (dim,),
+        dh0 (batch, dim, dstate) for the inputs that are given (else None).
+        """
+        u, delta, A, B, C, D, z, delta_bias, h0, dy, dlast = map(_f64, (u, delta, A, B, C, D, z, delta_bias, h0, dy,
+                                                                       dlast))
+        batch, dim, seqlen = u.shape
+        dstate = A.shape[1]
+        out = dict(du=np.empty_like(u), ddelta=np.empty_like(u), dA=np.empty_like(A), dB=np.empty_like(B),
+                   dC=np.empty_like(C), dD=None if D is None else np.empty_like(D),
+                   dz=None if z is None else np.empty_like(z),
+                   ddelta_bias=None if delta_bias is None else np.empty_like(delta_bias),
+                   dh0=np.empty((batch, dim, dstate), np.float64))
+        rc = self.lib.oracle_scan_bwd_f64(batch, dim, dstate, seqlen, _p(u), _p(delta), _p(A), _p(B), _p(C), _p(D),
+                                          _p(z), _p(delta_bias), 1 if softplus else 0, _p(h0), _p(dy), _p(dlast),
+                                          _p(out["du"]), _p(out["ddelta"]), _p(out["dA"]), _p(out["dB"]),
+                                          _p(out["dC"]), _p(out["dD"]), _p(out["dz"]), _p(out["ddelta_bias"]),
+                                          _p(out["dh0"]))
+        if rc != 0:
+            raise ValueError("oracle_scan_bwd_f64 rejected the arguments")
+        return out
 
     def conv1d_f64(self, x, weight, bias=None, x_prev=None, silu=True):
         """u = act(causal depthwise conv of x).  x: (batch, dim, seqlen); weight: (dim, K), K in 1..4;
@@ -172,6 +201,10 @@ def state_update_f64(*args, **kw):
 
 def state_update_channels_f64(*args, **kw):
     return default().state_update_channels_f64(*args, **kw)
+
+
+def scan_bwd_f64(*args, **kw):
+    return default().scan_bwd_f64(*args, **kw)
 
 
 def conv1d_f64(*args, **kw):

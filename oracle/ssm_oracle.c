@@ -65,6 +65,8 @@
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
 
 #define ORACLE_ABI_VERSION 1
 
@@ -171,4 +173,125 @@ int oracle_conv1d_f64(int64_t batch, int64_t dim, int64_t seqlen, int64_t width,
     }
   }
   return 0;
+}
+
+/* Gradients of the scan for a scalar loss with dL/dy = dy and dL/dlast_state
+ * = dlast (NULL: 0), by reverse-mode differentiation of the loop above (the
+ * chain rule written out by hand; no formula for it is on the pages):
+ *
+ *   g_t        = dy_t * silu(z_t) (dy_t without a gate)       dL/d(pre-gate output)
+ *   dz_t       = dy_t * s_t * silu'(z_t),  s_t = sum_n C h + D u
+ *   lambda_t,n = dL/dh_t,n = g_t C_t,n + Abar_{t+1},n lambda_{t+1},n   (+ dlast at t = L-1)
+ *   dC[b,n,t] += g_t h_t,n                 dB[b,n,t] += lambda Delta_t u_t
+ *   du_t       = g_t D + sum_n lambda Delta_t B_t,n
+ *   dDelta_t   = sum_n lambda (A_n Abar_t,n h_{t-1},n + B_t,n u_t)
+ *   dA[d,n]   += lambda Delta_t Abar_t,n h_{t-1},n
+ *   ddelta_t   = dDelta_t * sigmoid(delta_t + bias) with softplus, else dDelta_t
+ *   dD[d] += g_t u_t;  dbias[d] += ddelta_t;  dh0 = Abar_0 lambda_0
+ *
+ * dB and dC sum over the channels of a batch row, dA, dD and dbias over the
+ * batch rows as well.  Parallel over batch rows only, with per-row partial
+ * sums of dA/dD/dbias added in row order afterwards, so the result does not
+ * depend on the thread count.  Outputs for absent inputs (dD, dz, ddelta_bias,
+ * dh0) may be NULL.  Returns 0, or -1 on bad sizes, a missing pointer or
+ * allocation failure. */
+int oracle_scan_bwd_f64(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, const double* u,
+                        const double* delta, const double* A, const double* B, const double* C,
+                        const double* D, const double* z, const double* delta_bias, int softplus_flag,
+                        const double* h0, const double* dy, const double* dlast, double* du, double* ddelta,
+                        double* dA, double* dB, double* dC, double* dD, double* dz, double* ddelta_bias,
+                        double* dh0) {
+  if (batch < 1 || dim < 1 || dstate < 1 || dstate > 256 || seqlen < 1) return -1;
+  if (!u || !delta || !A || !B || !C || !dy || !du || !ddelta || !dA || !dB || !dC) return -1;
+  double* partA = calloc((size_t)(batch * dim * dstate), sizeof(double));
+  double* partD = calloc((size_t)(batch * dim), sizeof(double));
+  double* partBias = calloc((size_t)(batch * dim), sizeof(double));
+  int fail = !partA || !partD || !partBias;
+  memset(dB, 0, sizeof(double) * (size_t)(batch * dstate * seqlen));
+  memset(dC, 0, sizeof(double) * (size_t)(batch * dstate * seqlen));
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : fail)
+  for (int64_t b = 0; b < batch; ++b) {
+    if (fail) continue;
+    double* hs = malloc(sizeof(double) * (size_t)((seqlen + 1) * dstate)); /* hs[t+1] = h_t, hs[0] = h0 */
+    double* steps = malloc(sizeof(double) * (size_t)seqlen);
+    double* pre = malloc(sizeof(double) * (size_t)seqlen);
+    if (!hs || !steps || !pre) {
+      fail = 1;
+      free(hs); free(steps); free(pre);
+      continue;
+    }
+    const double* Bb = B + b * dstate * seqlen;
+    const double* Cb = C + b * dstate * seqlen;
+    for (int64_t d = 0; d < dim; ++d) {
+      const int64_t ch = b * dim + d;
+      const double* Ar = A + d * dstate;
+      const double Dd = D ? D[d] : 0.0;
+      const double bias = delta_bias ? delta_bias[d] : 0.0;
+      /* forward, keeping every state, step and pre-gate output */
+      for (int64_t n = 0; n < dstate; ++n) hs[n] = h0 ? h0[ch * dstate + n] : 0.0;
+      for (int64_t t = 0; t < seqlen; ++t) {
+        double x = delta[ch * seqlen + t] + bias;
+        double step = softplus_flag ? oracle_softplus(x) : x;
+        double ut = u[ch * seqlen + t];
+        double v = 0.0;
+        steps[t] = step;
+        for (int64_t n = 0; n < dstate; ++n) {
+          double h = exp(step * Ar[n]) * hs[t * dstate + n] + step * Bb[n * seqlen + t] * ut;
+          hs[(t + 1) * dstate + n] = h;
+          v += Cb[n * seqlen + t] * h;
+        }
+        pre[t] = v + Dd * ut;
+      }
+      /* backward */
+      double lam[256];
+      for (int64_t n = 0; n < dstate; ++n) lam[n] = dlast ? dlast[ch * dstate + n] : 0.0;
+      for (int64_t t = seqlen - 1; t >= 0; --t) {
+        const double ut = u[ch * seqlen + t], step = steps[t];
+        double g = dy[ch * seqlen + t];
+        if (z) {
+          const double zt = z[ch * seqlen + t];
+          const double sg = 1.0 / (1.0 + exp(-zt));
+          if (dz) dz[ch * seqlen + t] = g * pre[t] * sg * (1.0 + zt * (1.0 - sg));
+          g *= zt * sg;
+        }
+        partD[ch] += g * ut;
+        double du_t = g * Dd, dstep = 0.0;
+        for (int64_t n = 0; n < dstate; ++n) {
+          const double bt = Bb[n * seqlen + t];
+          const double hprev = hs[t * dstate + n];
+          const double abar = exp(step * Ar[n]);
+          lam[n] += g * Cb[n * seqlen + t];
+          dC[(b * dstate + n) * seqlen + t] += g * hs[(t + 1) * dstate + n];
+          dB[(b * dstate + n) * seqlen + t] += lam[n] * step * ut;
+          du_t += lam[n] * step * bt;
+          dstep += lam[n] * (Ar[n] * abar * hprev + bt * ut);
+          partA[ch * dstate + n] += lam[n] * step * abar * hprev;
+          lam[n] *= abar;
+        }
+        du[ch * seqlen + t] = du_t;
+        const double x = delta[ch * seqlen + t] + bias;
+        const double dd = softplus_flag ? dstep / (1.0 + exp(-x)) : dstep;
+        ddelta[ch * seqlen + t] = dd;
+        partBias[ch] += dd;
+      }
+      if (dh0)
+        for (int64_t n = 0; n < dstate; ++n) dh0[ch * dstate + n] = lam[n];
+    }
+    free(hs); free(steps); free(pre);
+  }
+  if (!fail) {
+    for (int64_t i = 0; i < dim * dstate; ++i) dA[i] = 0.0;
+    for (int64_t d = 0; d < dim; ++d) {
+      if (dD) dD[d] = 0.0;
+      if (ddelta_bias) ddelta_bias[d] = 0.0;
+    }
+    for (int64_t b = 0; b < batch; ++b)
+      for (int64_t d = 0; d < dim; ++d) {
+        for (int64_t n = 0; n < dstate; ++n) dA[d * dstate + n] += partA[(b * dim + d) * dstate + n];
+        if (dD) dD[d] += partD[b * dim + d];
+        if (ddelta_bias) ddelta_bias[d] += partBias[b * dim + d];
+      }
+  }
+  free(partA); free(partD); free(partBias);
+  return fail ? -1 : 0;
 }

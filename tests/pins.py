@@ -30,6 +30,10 @@ deliberately broken copies of it (tests/test_oracle_mutants.py).
   conv_causality    changing x at position p changes exactly u[p .. p+K-1]
   conv_split_carry  convolving in two pieces, the second fed the first's last K-1
                     inputs as x_prev, equals one pass
+  bwd_finite_diff   the hand-written reverse-mode gradients against central finite
+                    differences of the forward oracle, every input, every flag
+  bwd_autograd      the same gradients against torch autograd (fp64, CPU) through an
+                    independently written vectorised forward
 """
 import json
 import math
@@ -337,5 +341,90 @@ def conv_split_carry(o):
             _close(np.concatenate([u1, u2], axis=-1), u, 1e-15, 1e-15, "conv split K=%d cut=%d" % (width, cut))
 
 
+GRAD_OF = dict(u="du", delta="ddelta", A="dA", B="dB", C="dC", D="dD", z="dz", delta_bias="ddelta_bias", h0="dh0")
+
+
+def bwd_finite_diff(o):
+    rng = _rng(24)
+    batch, dim, dstate, seqlen = 2, 2, 3, 9
+    eps = 1e-6
+    for zf, Df, bf, spf, hf, dlf in ((True, True, True, True, True, True), (False, False, False, False, False, False),
+                                     (True, False, True, False, True, False), (False, True, False, True, False, True)):
+        p = _random_problem(rng, batch, dim, dstate, seqlen, z=zf, D=Df, bias=bf, h0=hf)
+        dy = rng.standard_normal((batch, dim, seqlen))
+        dlast = rng.standard_normal((batch, dim, dstate)) if dlf else None
+        g = o.scan_bwd_f64(softplus=spf, dy=dy, dlast=dlast, **p)
+
+        def loss(q):
+            y, h = o.scan_f64(softplus=spf, **q)
+            return float((dy * y).sum() + ((dlast * h).sum() if dlf else 0.0))
+
+        for name, key in GRAD_OF.items():
+            if p.get(name) is None:
+                continue
+            base = p[name]
+            num = np.empty_like(base)
+            for i in range(base.size):
+                up, dn = base.copy(), base.copy()
+                up.flat[i] += eps
+                dn.flat[i] -= eps
+                num.flat[i] = (loss(dict(p, **{name: up})) - loss(dict(p, **{name: dn}))) / (2 * eps)
+            if name == "h0" and not hf:
+                continue
+            scale = max(float(np.abs(num).max()), 1e-12)
+            _close(g[key] / scale, num / scale, 0.0, 1e-6, "d/d%s flags=%s" % (name, (zf, Df, bf, spf, hf, dlf)))
+        if not hf:  # without h0 the state starts at zero; dh0 is still the gradient at that zero state
+            zero = np.zeros((batch, dim, dstate))
+            num = np.empty_like(zero)
+            for i in range(zero.size):
+                up, dn = zero.copy(), zero.copy()
+                up.flat[i] += eps
+                dn.flat[i] -= eps
+                num.flat[i] = (loss(dict(p, h0=up)) - loss(dict(p, h0=dn))) / (2 * eps)
+            _close(g["dh0"], num, 1e-6, 1e-9, "dh0 at a zero state")
+
+
+def _torch_loss(p, softplus, dy, dlast):
+    import torch
+    t = {k: (None if v is None else torch.tensor(v, dtype=torch.float64, requires_grad=True)) for k, v in p.items()}
+    x = t["delta"] + (t["delta_bias"][None, :, None] if t["delta_bias"] is not None else 0.0)
+    step = torch.logaddexp(x, torch.zeros_like(x)) if softplus else x
+    batch, dim, seqlen = t["u"].shape
+    dstate = t["A"].shape[1]
+    h = t["h0"] if t["h0"] is not None else torch.zeros(batch, dim, dstate, dtype=torch.float64)
+    loss = 0.0
+    for l in range(seqlen):
+        abar = torch.exp(step[:, :, l, None] * t["A"][None])
+        h = abar * h + step[:, :, l, None] * t["B"][:, None, :, l] * t["u"][:, :, l, None]
+        s = (t["C"][:, None, :, l] * h).sum(-1)
+        if t["D"] is not None:
+            s = s + t["D"][None] * t["u"][:, :, l]
+        if t["z"] is not None:
+            zz = t["z"][:, :, l]
+            s = s * zz * torch.sigmoid(zz)
+        loss = loss + (torch.tensor(dy[:, :, l]) * s).sum()
+    if dlast is not None:
+        loss = loss + (torch.tensor(dlast) * h).sum()
+    loss.backward()
+    return {k: (None if v is None else v.grad.numpy()) for k, v in t.items()}
+
+
+def bwd_autograd(o):
+    rng = _rng(25)
+    batch, dim, dstate, seqlen = 3, 4, 5, 17
+    for flags in ((True, True, True, True, True), (False, True, False, True, False), (True, False, True, False, True)):
+        zf, Df, bf, spf, hf = flags
+        p = _random_problem(rng, batch, dim, dstate, seqlen, z=zf, D=Df, bias=bf, h0=hf)
+        dy = rng.standard_normal((batch, dim, seqlen))
+        dlast = rng.standard_normal((batch, dim, dstate))
+        g = o.scan_bwd_f64(softplus=spf, dy=dy, dlast=dlast, **p)
+        ref = _torch_loss(p, spf, dy, dlast)
+        for name, key in GRAD_OF.items():
+            if p.get(name) is None:
+                continue
+            _close(g[key], ref[name], 1e-11, 1e-12, "autograd d/d%s flags=%s" % (name, flags))
+
+
 ALL = [worked_examples, lti_closed_form, bruteforce, single_step, persistence, forgetting, split_carry, linearity,
-       softplus_silu, decode_is_scan, channel_subset, conv_library, conv_taps, conv_causality, conv_split_carry]
+       softplus_silu, decode_is_scan, channel_subset, conv_library, conv_taps, conv_causality, conv_split_carry,
+       bwd_finite_diff, bwd_autograd]

@@ -38,6 +38,13 @@ MUTANTS = [
     ("conv_prev_reversed", "x_prev[ch * (width - 1) + (width - 1) + src]", "x_prev[ch * (width - 1) - 1 - src]"),
     ("conv_bias_dropped", "double acc = cb ? cb[d] : 0.0;", "double acc = 0.0;"),
     ("conv_silu_dropped", "u[ch * seqlen + l] = silu_flag ? oracle_silu(acc) : acc;", "u[ch * seqlen + l] = acc;"),
+    ("bwd_lambda_not_decayed", "          lam[n] *= abar;", "          lam[n] *= 1.0;"),
+    ("bwd_hprev_is_h", "const double hprev = hs[t * dstate + n];", "const double hprev = hs[(t + 1) * dstate + n];"),
+    ("bwd_softplus_grad_dropped", "softplus_flag ? dstep / (1.0 + exp(-x)) : dstep", "softplus_flag ? dstep : dstep"),
+    ("bwd_dz_sign", "(1.0 + zt * (1.0 - sg))", "(1.0 - zt * (1.0 - sg))"),
+    ("bwd_dB_missing_step", "+= lam[n] * step * ut;", "+= lam[n] * ut;"),
+    ("bwd_dC_uses_hprev", "g * hs[(t + 1) * dstate + n];", "g * hs[t * dstate + n];"),
+    ("bwd_dD_after_gate", "        partD[ch] += g * ut;", "        partD[ch] += dy[ch * seqlen + t] * ut;"),
 ]
 
 
