@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 2
+#define SSM_ABI_VERSION 3
 
 struct ihipStream_t; /* the same incomplete type as HIP's hipStream_t */
 
@@ -76,7 +76,8 @@ typedef enum {
   SSM_ERR_DTYPE = 4,                /* unknown io dtype                      */
   SSM_ERR_ALIGN = 5,                /* a pointer is not element-aligned      */
   SSM_ERR_ALIAS = 6,                /* an output overlaps an input           */
-  SSM_ERR_HIP = 7                   /* a HIP runtime call failed             */
+  SSM_ERR_HIP = 7,                  /* a HIP runtime call failed             */
+  SSM_ERR_UNSUPPORTED = 8           /* valid, but outside what this entry point implements */
 } ssm_status_t;
 
 /*
@@ -168,6 +169,47 @@ ssm_status_t ssm_conv_scan_fwd(int64_t batch, int64_t dim, int64_t dstate, int64
                                const void* B, const void* C, const float* D, const void* z,
                                const float* delta_bias, int softplus_flag, const float* h0, void* y,
                                float* last_state, void* u_out, struct ihipStream_t* stream);
+
+/*
+ * ssm_scan_bwd -- gradients of the scan for training: given dy = dL/dy and
+ * (optionally) dlast = dL/dlast_state, the gradients of L with respect to
+ * every input of ssm_scan_fwd.  The pages state the training-efficiency aim of
+ * the hardware-aware scan (the Chinese explainer's "硬件感知的设计" and S4/S6
+ * comparison sections: parallel training without materialising the expanded
+ * state); the gradient formulas are the chain rule through the recurrence:
+ *
+ *   g_t    = dy_t silu(z_t) (dy_t without z);  lambda_t = g_t C_t + Abar_{t+1} lambda_{t+1} (+ dlast at the end)
+ *   du     = g D + Delta sum_n lambda B;        dDelta = sum_n lambda (A Abar h_{t-1} + B u)
+ *   ddelta = dDelta sigmoid(delta + bias) with softplus, else dDelta
+ *   dA[d,n] = sum_{b,t} lambda Delta Abar h_{t-1};  dB[b,n,t] = sum_d lambda Delta u;  dC[b,n,t] = sum_d g h
+ *   dD[d] = sum_{b,t} g u;  ddelta_bias[d] = sum_{b,t} ddelta;  dz = dy (C.h + D u) silu'(z);  dh0 = Abar_0 lambda_0
+ *
+ * The expanded state is never stored: a forward pass writes the state every
+ * 16 tokens (stream-ordered scratch from the library's pool, about a 16th of
+ * the expanded state) and the backward recomputes each 16-token tile from it.
+ *
+ *   inputs u .. h0      as ssm_scan_fwd (io dtype for u, delta, z, B, C)
+ *   dy          [batch, dim, seqlen]    io
+ *   dlast       [batch, dim, dstate]    fp32   may be NULL (0)
+ *   du, ddelta  [batch, dim, seqlen]    io     written
+ *   dA          [dim, dstate]           fp32   written
+ *   dB, dC      [batch, dstate, seqlen] fp32   written (sums over all channels: kept in fp32)
+ *   dD, ddelta_bias [dim]               fp32   written when not NULL (the gradient at D = 0 / bias = 0
+ *                                              when D / delta_bias is NULL)
+ *   dz          [batch, dim, seqlen]    io     written when z and dz are not NULL
+ *   dh0         [batch, dim, dstate]    fp32   written when not NULL (the gradient at h0 = 0 when h0 is NULL)
+ *
+ * Outputs must not overlap inputs or each other.  Supported: dstate in
+ * {4, 8, 16}, seqlen a multiple of 8, and every (batch, dim, seqlen) and
+ * (batch, dstate, seqlen) buffer 16-byte aligned; anything else returns
+ * SSM_ERR_UNSUPPORTED.  Deterministic: partial sums are added in a fixed order.
+ */
+ssm_status_t ssm_scan_bwd(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, ssm_dtype_t io,
+                          const void* u, const void* delta, const float* A, const void* B, const void* C,
+                          const float* D, const void* z, const float* delta_bias, int softplus_flag,
+                          const float* h0, const void* dy, const float* dlast, void* du, void* ddelta,
+                          float* dA, float* dB, float* dC, float* dD, void* dz, float* ddelta_bias, float* dh0,
+                          struct ihipStream_t* stream);
 
 /* Kernel paths of ssm_scan_fwd (reported by ssm_scan_fwd_plan). */
 typedef enum {

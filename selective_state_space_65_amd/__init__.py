@@ -1,13 +1,13 @@
 """MI355X (gfx950) selective state-space scan (S6).
 
 The compute lives in libssm_scan.so (HIP kernels behind a C ABI, see
-include/ssm_scan.h); `scan_fwd`, `conv_scan_fwd` and `state_update` are the
-ctypes wrappers.
+include/ssm_scan.h); `scan_fwd`, `conv_scan_fwd`, `scan_bwd` and `state_update`
+are the ctypes wrappers.
 The binding is imported lazily so that `inputs` (the seeded synthetic-input
 generators) can be used without the library.
 """
 
-__all__ = ["scan_fwd", "conv_scan_fwd", "state_update", "scan_plan", "SsmError"]
+__all__ = ["scan_fwd", "conv_scan_fwd", "scan_bwd", "state_update", "scan_plan", "SsmError"]
 
 
 def __getattr__(name):

@@ -26,6 +26,7 @@ STATUS_NAMES = {
     5: "SSM_ERR_ALIGN",
     6: "SSM_ERR_ALIAS",
     7: "SSM_ERR_HIP",
+    8: "SSM_ERR_UNSUPPORTED",
 }
 
 # Every symbol the header declares, with its ctypes signature.
@@ -37,6 +38,8 @@ SIGNATURES = {
     "ssm_state_update": (_I, [_I64, _I64, _I64, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P]),
     "ssm_conv_scan_fwd": (_I, [_I64, _I64, _I64, _I64, _I64, _I, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _I, _P,
                                _P, _P, _P, _P]),
+    "ssm_scan_bwd": (_I, [_I64, _I64, _I64, _I64, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P,
+                          _P, _P, _P, _P, _P]),
     "ssm_scan_fwd_plan": (_I, [_I64, _I64, _I64, _I64, _I, ctypes.POINTER(_I), ctypes.POINTER(_I64),
                               ctypes.POINTER(_I64), ctypes.POINTER(_I64)]),
     "ssm_status_string": (ctypes.c_char_p, [_I]),
@@ -242,6 +245,55 @@ def conv_scan_fwd(x, conv_weight, delta, A, B, C, D=None, z=None, delta_bias=Non
                                _ptr(out), _ptr(last_state), _ptr(u_out), _stream(dev, stream))
     _check("ssm_conv_scan_fwd", st)
     return out, last_state
+
+
+def scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, delta_softplus=False, h0=None, dlast=None,
+             need=("dD", "dz", "ddelta_bias", "dh0"), stream=None):
+    """Gradients of sum(dy * y) + sum(dlast * last_state) for the scan of scan_fwd.
+
+    Returns a dict: du, ddelta (io dtype, like u); dA (dim, dstate), dB, dC
+    (batch, dstate, seqlen) in float32; and, when named in `need`, dD and
+    ddelta_bias (dim,) float32, dz (io dtype, only with z) and dh0 (batch, dim,
+    dstate) float32.
+    """
+    import torch
+    if u.dim() != 3:
+        raise ValueError("u must be (batch, dim, seqlen)")
+    batch, dim, seqlen = u.shape
+    dstate = A.shape[-1]
+    dev = u.device
+    io = u.dtype
+    f32 = torch.float32
+    _need(u, "u", (batch, dim, seqlen), io, dev)
+    _need(delta, "delta", (batch, dim, seqlen), io, dev)
+    _need(A, "A", (dim, dstate), f32, dev)
+    _need(B, "B", (batch, dstate, seqlen), io, dev)
+    _need(C, "C", (batch, dstate, seqlen), io, dev)
+    _need(dy, "dy", (batch, dim, seqlen), io, dev)
+    if D is not None:
+        _need(D, "D", (dim,), f32, dev)
+    if z is not None:
+        _need(z, "z", (batch, dim, seqlen), io, dev)
+    if delta_bias is not None:
+        _need(delta_bias, "delta_bias", (dim,), f32, dev)
+    if h0 is not None:
+        _need(h0, "h0", (batch, dim, dstate), f32, dev)
+    if dlast is not None:
+        _need(dlast, "dlast", (batch, dim, dstate), f32, dev)
+    g = dict(du=torch.empty_like(u), ddelta=torch.empty_like(u), dA=torch.empty((dim, dstate), dtype=f32, device=dev),
+             dB=torch.empty((batch, dstate, seqlen), dtype=f32, device=dev),
+             dC=torch.empty((batch, dstate, seqlen), dtype=f32, device=dev),
+             dD=torch.empty(dim, dtype=f32, device=dev) if "dD" in need else None,
+             dz=torch.empty_like(u) if ("dz" in need and z is not None) else None,
+             ddelta_bias=torch.empty(dim, dtype=f32, device=dev) if "ddelta_bias" in need else None,
+             dh0=torch.empty((batch, dim, dstate), dtype=f32, device=dev) if "dh0" in need else None)
+    lib = load_library()
+    st = lib.ssm_scan_bwd(batch, dim, dstate, seqlen, _io_code(io), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
+                          _ptr(D), _ptr(z), _ptr(delta_bias), 1 if delta_softplus else 0, _ptr(h0), _ptr(dy),
+                          _ptr(dlast), _ptr(g["du"]), _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]),
+                          _ptr(g["dD"]), _ptr(g["dz"]), _ptr(g["ddelta_bias"]), _ptr(g["dh0"]), _stream(dev, stream))
+    _check("ssm_scan_bwd", st)
+    return g
 
 
 def state_update(state, u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=False, out=None,

@@ -249,7 +249,12 @@ struct ScanArgs {
   void* u_out;          // [batch][dim][seqlen], may be null
   int conv_width;       // 1..4
   int conv_silu;
+  // Backward support (single-pass kernel only): when set, the state before
+  // every 16th token is written here, [seqlen/16 rounded up][batch][N][dim].
+  float* ckpt;
 };
+
+constexpr int kCkptTokens = 16;  // tokens between backward checkpoints (one backward tile)
 
 // The causal depthwise conv of one token: acc = bias, then one FMA per tap
 // from the oldest input (xs[4 - K]) to the current one (xs[3]); taps a
@@ -942,6 +947,13 @@ __global__ __launch_bounds__(64 * S) void scan_split_kernel(ScanArgs a) {
           fetch_bc(s ^ 1, l + (k + 1) * kChunk);
         }
         __builtin_amdgcn_sched_barrier(0);
+        if (a.ckpt && (k * kChunk) % kCkptTokens == 0) {
+          // The state before token l + k*kChunk, for the backward's recompute.
+          const int64_t c = (l + k * kChunk) / kCkptTokens;
+#pragma unroll
+          for (int j = 0; j < NS; ++j)
+            if (active) a.ckpt[((c * a.batch + b) * N + w * NS + j) * a.dim + d] = h[j];
+        }
         float yv[kChunk];
 #pragma unroll
         for (int j = 0; j < NS; ++j) {
@@ -996,6 +1008,357 @@ __global__ __launch_bounds__(64 * S) void scan_split_kernel(ScanArgs a) {
   if (a.last_state && active) {
 #pragma unroll
     for (int j = 0; j < NS; ++j) a.last_state[ch * N + w * NS + j] = h[j];
+  }
+}
+
+// ----------------------------------------------------------------------------
+// Backward of the scan (gradients for training)
+// ----------------------------------------------------------------------------
+//
+// The adjoint of the recurrence runs the sequence in reverse:
+//   lambda_t = g_t C_t + Abar_{t+1} lambda_{t+1}   (lambda = dL/dh, g = dL/d(pre-gate y))
+// and needs h_{t-1} at every token.  The forward states are not stored: the
+// single-pass forward kernel writes each wave's states every 16 tokens
+// (checkpoints, 1/16 of the expanded state for N = 16 ... and a 16th of the
+// tokens), and the backward recomputes a 16-token tile of states from its
+// checkpoint in registers before walking it backwards.  Same layout as the
+// forward: a block owns 64 channels of one batch row, its S waves split the
+// states, and the first SA waves (one per SIMD) handle the per-token work.
+// Per tile, in reverse order:
+//   P0  the first SA waves stage (Delta, x = Delta u) of their TS tokens in LDS;
+//   P1  every wave recomputes its states over the tile from the checkpoint and
+//       publishes its partial C.h sums;
+//   P2  the first SA waves sum the partials (wave order) into the pre-gate
+//       output s_t = C.h + D u and form g_t, dz_t and dD; g_t goes to LDS;
+//   P3  every wave walks its states backwards: lambda, dA in registers, the
+//       partial sums over its states of lambda B and lambda A (h_t - B x_t)
+//       (= lambda A Abar h_{t-1}) to LDS, and the per-lane products lambda x
+//       (dB) and g h (dC) summed over the wave's 64 channels;
+//   P4  the first SA waves sum the partials into du_t = g D + Delta sum(lambda B)
+//       and dDelta_t = sum(lambda A Abar h_{t-1}) + u sum(lambda B), and
+//       ddelta_t = dDelta_t sigmoid(delta_t + bias) with softplus.
+// dB and dC are per-(group, batch row) partial sums over 64 channels, dA per
+// batch row, dD and dbias per (batch row, wave); bwd_reduce_kernel adds them
+// up in a fixed order, so the gradients are deterministic (no atomics).
+struct BwdArgs {
+  const void* u;
+  const void* delta;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* D;      // may be null
+  const void* z;       // may be null
+  const float* bias;   // may be null
+  const void* dy;
+  const float* dlast;  // may be null
+  const float* ckpt;   // [ceil(seqlen/16)][batch][N][dim]
+  void* du;
+  void* ddelta;
+  void* dz;            // written when z is given and this is not null
+  float* dh0;          // may be null
+  float* dB_part;      // [groups][batch][N][seqlen]
+  float* dC_part;      // [groups][batch][N][seqlen]
+  float* dA_part;      // [batch][dim][N]
+  float* dD_part;      // [batch][SA][dim]
+  float* dbias_part;   // [batch][SA][dim]
+  int64_t batch, dim, seqlen, groups;
+};
+
+__device__ __forceinline__ float sigmoid_f32(float x) { return rcp_hw(1.0f + exp2_hw(-x * kLog2e)); }
+
+// Sum of NV values over the 64 lanes of a wave, all at once: after log2(NV)
+// exchange-and-add halvings (each lane keeps the half of the values its lane
+// bit selects and adds its partner's copy of that half), lane i holds the sum
+// over the wave of value i mod NV.  NV is a power of two up to 64.
+template <int NV>
+__device__ __forceinline__ float wave_sum_spread(float (&v)[NV], int lane) {
+#pragma unroll
+  for (int m = NV / 2; m >= 1; m >>= 1) {
+    const bool hi = (lane & m) != 0;
+#pragma unroll
+    for (int i = 0; i < m; ++i) {
+      const float send = hi ? v[i] : v[m + i];
+      const float keep = hi ? v[m + i] : v[i];
+      v[i] = keep + __shfl_xor(send, m);
+    }
+  }
+  float r = v[0];
+#pragma unroll
+  for (int m = NV; m < 64; m <<= 1) r += __shfl_xor(r, m);
+  return r;
+}
+
+template <typename IoT, int N, int S, int SA, bool kZ, bool kSoftplus>
+__global__ __launch_bounds__(64 * S) void scan_bwd_kernel(BwdArgs a) {
+  constexpr int NS = N / S;
+  constexpr int T = kCkptTokens;
+  constexpr int KT = T / kChunk;
+  constexpr int TS = T / SA;
+  constexpr int NV = 2 * NS * T;  // per-lane products summed over the wave per tile: dB, then dC
+  using LI = Line<IoT>;
+  using PI = Piece<IoT, TS>;
+  using U = Uni<IoT>;
+  constexpr int PW = PI::kWords, ZW = kZ ? PI::kWords : 1, W = U::kWords;
+  static_assert(N % S == 0 && NS <= 2 && S % SA == 0 && TS % 2 == 0 && kChunk % TS == 0, "backward tile shape");
+  static_assert(NV <= 64 && (NV & (NV - 1)) == 0, "one wave-wide sum per tile");
+  __shared__ float4 dxs[T / 2][64];  // (Delta_t, x_t, Delta_t+1, x_t+1)
+  __shared__ float2 part[S][T][64];  // per-wave partials: P1 .x = C.h; P3 .x = sum lambda A q, .y = sum lambda B
+  __shared__ float gs[T][64];        // g_t
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int64_t grp = blockIdx.x % a.groups;
+  const int64_t b = blockIdx.x / a.groups;
+  const int64_t d_raw = grp * kWaveThreads + lane;
+  const bool active = d_raw < a.dim;
+  const int64_t d = active ? d_raw : a.dim - 1;
+  const int64_t L = a.seqlen;
+  const int64_t ch = b * a.dim + d;
+
+  float Af[NS], A2[NS], carry[NS], dA_acc[NS];
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+    const int n = w * NS + j;
+    Af[j] = a.A[d * N + n];
+    A2[j] = Af[j] * kLog2e;
+    carry[j] = a.dlast ? a.dlast[ch * N + n] : 0.0f;  // Abar_{t+1} lambda_{t+1} past the last token
+    dA_acc[j] = 0.0f;
+  }
+  const float Dd = a.D ? a.D[d] : 0.0f;
+  const float bias = a.bias ? a.bias[d] : 0.0f;
+  float dD_acc = 0.0f, dbias_acc = 0.0f;
+
+  const IoT* ur = static_cast<const IoT*>(a.u) + ch * L;
+  const IoT* dr = static_cast<const IoT*>(a.delta) + ch * L;
+  const IoT* zr = kZ ? static_cast<const IoT*>(a.z) + ch * L : nullptr;
+  const IoT* yr = static_cast<const IoT*>(a.dy) + ch * L;
+  IoT* dur = static_cast<IoT*>(a.du) + ch * L;
+  IoT* ddr = static_cast<IoT*>(a.ddelta) + ch * L;
+  IoT* dzr = (kZ && a.dz) ? static_cast<IoT*>(a.dz) + ch * L : nullptr;
+  const IoT* Bb = static_cast<const IoT*>(a.B) + b * N * L;
+  const IoT* Cb = static_cast<const IoT*>(a.C) + b * N * L;
+  const uint32_t row_bytes = (uint32_t)(L * sizeof(IoT));
+
+  const int64_t ntiles = (L + T - 1) / T;
+  for (int64_t c = ntiles - 1; c >= 0; --c) {
+    const int64_t l = c * T;
+    const int valid = (int)min((int64_t)T, L - l);  // a multiple of kChunk
+    const bool acw = w < SA && w * TS < valid;       // this wave's per-token share exists
+    // ---- P0
+    uint32_t qu[PW], qd[PW], qz[ZW], qy[PW];
+    float dlv4[TS], sgd4[TS], g4[TS];
+    if (acw) {
+      PI::load(ur + l + w * TS, qu);
+      PI::load(dr + l + w * TS, qd);
+      if constexpr (kZ) PI::load(zr + l + w * TS, qz);
+      PI::load(yr + l + w * TS, qy);
+#pragma unroll
+      for (int t = 0; t < TS; t += 2) {
+        float dd[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const float raw = LI::elem(qd, t + e) + bias;
+          dd[e] = kSoftplus ? softplus_f32(raw) : raw;
+          dlv4[t + e] = dd[e];
+          sgd4[t + e] = kSoftplus ? sigmoid_f32(raw) : 1.0f;
+        }
+        dxs[(w * TS + t) / 2][lane] =
+            make_float4(dd[0], dd[0] * LI::elem(qu, t), dd[1], dd[1] * LI::elem(qu, t + 1));
+      }
+    }
+    lds_barrier();
+    // ---- P1: the tile's states from its checkpoint (B/C rows of this wave's states as scalar words)
+    uint32_t Bt[NS][KT][W], Ct[NS][KT][W];
+#pragma unroll
+    for (int j = 0; j < NS; ++j)
+#pragma unroll
+      for (int k = 0; k < KT; ++k)
+        if (k * kChunk < valid) {
+          uint32_t off = (uint32_t)(w * NS + j) * row_bytes + (uint32_t)((l + k * kChunk) * sizeof(IoT));
+          asm volatile("" : "+s"(off));
+          U::load8(Bb, off, Bt[j][k]);
+          U::load8(Cb, off, Ct[j][k]);
+        }
+    float dlv[T], xv[T];
+#pragma unroll
+    for (int i = 0; i < T / 2; ++i)
+      if (2 * i < valid) {
+        const float4 v = dxs[i][lane];
+        dlv[2 * i] = v.x; xv[2 * i] = v.y; dlv[2 * i + 1] = v.z; xv[2 * i + 1] = v.w;
+      }
+    float hs[NS][T], ab[NS][T];
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      float hc = a.ckpt[((c * a.batch + b) * N + w * NS + j) * a.dim + d];
+#pragma unroll
+      for (int t = 0; t < T; ++t)
+        if (t < valid) {
+          ab[j][t] = exp2_hw(A2[j] * dlv[t]);
+          hc = __builtin_fmaf(ab[j][t], hc, U::elem(Bt[j][t / kChunk], t % kChunk) * xv[t]);
+          hs[j][t] = hc;
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+      if (t < valid) {
+        float ps = U::elem(Ct[0][t / kChunk], t % kChunk) * hs[0][t];
+#pragma unroll
+        for (int j = 1; j < NS; ++j) ps = __builtin_fmaf(U::elem(Ct[j][t / kChunk], t % kChunk), hs[j][t], ps);
+        part[w][t][lane] = make_float2(ps, 0.0f);
+      }
+    lds_barrier();
+    // ---- P2
+    if (acw) {
+      uint32_t zw[PW];
+#pragma unroll
+      for (int t = 0; t < TS; ++t) {
+        const int tt = w * TS + t;
+        float sv = part[0][tt][lane].x;
+#pragma unroll
+        for (int s2 = 1; s2 < S; ++s2) sv += part[s2][tt][lane].x;
+        const float ut = LI::elem(qu, t);
+        sv = __builtin_fmaf(Dd, ut, sv);
+        const float dyv = LI::elem(qy, t);
+        float g = dyv;
+        if constexpr (kZ) {
+          const float zt = LI::elem(qz, t);
+          const float sg = sigmoid_f32(zt);
+          const float dzt = dyv * sv * sg * (1.0f + zt * (1.0f - sg));
+          g = dyv * (zt * sg);
+          if constexpr (sizeof(IoT) == 4) {
+            zw[t] = __float_as_uint(dzt);
+          } else if (t & 1) {
+            zw[t / 2] = Io<bf16_t>::pack2(__uint_as_float(zw[t / 2]), dzt);
+          } else {
+            zw[t / 2] = __float_as_uint(dzt);
+          }
+        }
+        dD_acc = __builtin_fmaf(g, ut, dD_acc);
+        g4[t] = g;
+        gs[tt][lane] = g;
+      }
+      if (kZ && dzr && active) PI::store(dzr + l + w * TS, zw);
+    }
+    lds_barrier();
+    // ---- P3
+    float gv[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+      if (t < valid) gv[t] = gs[t][lane];
+    float pv[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) pv[i] = 0.0f;
+#pragma unroll
+    for (int t = T - 1; t >= 0; --t)
+      if (t < valid) {
+        float sA = 0.0f, sB = 0.0f;
+#pragma unroll
+        for (int j = 0; j < NS; ++j) {
+          const float cv = U::elem(Ct[j][t / kChunk], t % kChunk);
+          const float bv = U::elem(Bt[j][t / kChunk], t % kChunk);
+          const float lam = __builtin_fmaf(gv[t], cv, carry[j]);
+          pv[j * T + t] = lam * xv[t];
+          pv[NS * T + j * T + t] = gv[t] * hs[j][t];
+          const float q = __builtin_fmaf(-bv, xv[t], hs[j][t]);  // Abar_t h_{t-1}
+          sB = __builtin_fmaf(lam, bv, sB);
+          sA = __builtin_fmaf(lam * Af[j], q, sA);
+          dA_acc[j] = __builtin_fmaf(lam * dlv[t], q, dA_acc[j]);
+          carry[j] = ab[j][t] * lam;
+        }
+        part[w][t][lane] = make_float2(sA, sB);
+      }
+    {
+      // Lanes past the last channel run on a copy of it; they must add nothing.
+      if (!active) {
+#pragma unroll
+        for (int i = 0; i < NV; ++i) pv[i] = 0.0f;
+      }
+      const float tot = wave_sum_spread<NV>(pv, lane);
+      const int i = lane % NV;
+      const int which = i / (NS * T), jj = (i % (NS * T)) / T, t = i % T;
+      if (lane < NV && t < valid) {
+        float* dst = which ? a.dC_part : a.dB_part;
+        dst[((grp * a.batch + b) * N + w * NS + jj) * L + l + t] = tot;
+      }
+    }
+    lds_barrier();
+    // ---- P4
+    if (acw) {
+      uint32_t uw[PW], dw[PW];
+#pragma unroll
+      for (int t = 0; t < TS; ++t) {
+        const int tt = w * TS + t;
+        float2 acc = part[0][tt][lane];
+#pragma unroll
+        for (int s2 = 1; s2 < S; ++s2) {
+          const float2 v = part[s2][tt][lane];
+          acc.x += v.x;
+          acc.y += v.y;
+        }
+        const float ut = LI::elem(qu, t);
+        const float dstep = __builtin_fmaf(ut, acc.y, acc.x);
+        const float duv = __builtin_fmaf(dlv4[t], acc.y, g4[t] * Dd);
+        const float ddv = dstep * sgd4[t];
+        dbias_acc += ddv;
+        if constexpr (sizeof(IoT) == 4) {
+          uw[t] = __float_as_uint(duv);
+          dw[t] = __float_as_uint(ddv);
+        } else if (t & 1) {
+          uw[t / 2] = Io<bf16_t>::pack2(__uint_as_float(uw[t / 2]), duv);
+          dw[t / 2] = Io<bf16_t>::pack2(__uint_as_float(dw[t / 2]), ddv);
+        } else {
+          uw[t / 2] = __float_as_uint(duv);
+          dw[t / 2] = __float_as_uint(ddv);
+        }
+      }
+      if (active) {
+        PI::store(dur + l + w * TS, uw);
+        PI::store(ddr + l + w * TS, dw);
+      }
+    }
+  }
+  if (active) {
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      if (a.dh0) a.dh0[ch * N + w * NS + j] = carry[j];
+      a.dA_part[ch * N + w * NS + j] = dA_acc[j];
+    }
+    if (w < SA) {
+      a.dD_part[(b * SA + w) * a.dim + d] = dD_acc;
+      a.dbias_part[(b * SA + w) * a.dim + d] = dbias_acc;
+    }
+  }
+}
+
+// Adds the backward's partial sums in a fixed order: dB, dC over channel
+// groups; dA over batch rows; dD and dbias over batch rows and waves.
+__global__ __launch_bounds__(kBlockThreads) void bwd_reduce_kernel(BwdArgs a, int N, int SA, float* dB, float* dC,
+                                                                   float* dA, float* dD, float* dbias) {
+  const int64_t i = (int64_t)blockIdx.x * kBlockThreads + threadIdx.x;
+  const int64_t bnl = a.batch * N * a.seqlen;
+  if (i < bnl) {
+    float sb = 0.0f, sc = 0.0f;
+    for (int64_t g = 0; g < a.groups; ++g) {
+      sb += a.dB_part[g * bnl + i];
+      sc += a.dC_part[g * bnl + i];
+    }
+    dB[i] = sb;
+    dC[i] = sc;
+  }
+  if (i < a.dim * N) {
+    float s = 0.0f;
+    for (int64_t b = 0; b < a.batch; ++b) s += a.dA_part[b * a.dim * N + i];
+    dA[i] = s;
+  }
+  if (i < a.dim) {
+    float sd = 0.0f, sb = 0.0f;
+    for (int64_t b = 0; b < a.batch; ++b)
+      for (int w = 0; w < SA; ++w) {
+        sd += a.dD_part[(b * SA + w) * a.dim + i];
+        sb += a.dbias_part[(b * SA + w) * a.dim + i];
+      }
+    if (dD) dD[i] = sd;
+    if (dbias) dbias[i] = sb;
   }
 }
 
@@ -1390,6 +1753,34 @@ hipError_t launch_conv(const ScanArgs& a, void* u, hipStream_t st) {
   return hipGetLastError();
 }
 
+template <typename IoT, int N, bool kZ, bool kSp>
+hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
+  constexpr int S = (N >= SSM_SPLIT_WAVES) ? SSM_SPLIT_WAVES : N;
+  constexpr int SA = (S > 4) ? 4 : S;
+  hipLaunchKernelGGL((scan_bwd_kernel<IoT, N, S, SA, kZ, kSp>), dim3((unsigned)(a.batch * a.groups)), dim3(64 * S), 0,
+                     st, a);
+  return hipGetLastError();
+}
+
+template <typename IoT, int N>
+hipError_t launch_bwd_n(const BwdArgs& a, hipStream_t st, bool sp) {
+  if (a.z) return sp ? launch_bwd_t<IoT, N, true, true>(a, st) : launch_bwd_t<IoT, N, true, false>(a, st);
+  return sp ? launch_bwd_t<IoT, N, false, true>(a, st) : launch_bwd_t<IoT, N, false, false>(a, st);
+}
+
+template <typename IoT>
+hipError_t launch_bwd(const BwdArgs& a, int N, hipStream_t st, bool sp) {
+  if (N == 4) return launch_bwd_n<IoT, 4>(a, st, sp);
+  if (N == 8) return launch_bwd_n<IoT, 8>(a, st, sp);
+  return launch_bwd_n<IoT, 16>(a, st, sp);
+}
+
+// Waves of the backward (and forward) blocks that do the per-token work.
+int bwd_token_waves(int64_t dstate) {
+  const int S = dstate >= SSM_SPLIT_WAVES ? SSM_SPLIT_WAVES : (int)dstate;
+  return S > 4 ? 4 : S;
+}
+
 // Vector kernels exist for dstate in {4, 8, 16}; every other case runs the
 // scalar-token kernel instantiated for up to 16 states.
 template <typename IoT>
@@ -1504,6 +1895,7 @@ ScanArgs scan_args(const Shape&, int64_t batch, int64_t dim, int64_t dstate, int
   a.batch = batch; a.dim = dim; a.dstate = dstate; a.seqlen = seqlen;
   a.groups = 0; a.segments = 0; a.seg_len = 0;
   a.conv_w = nullptr; a.conv_b = nullptr; a.x_prev = nullptr; a.u_out = nullptr; a.conv_width = 1; a.conv_silu = 0;
+  a.ckpt = nullptr;
   return a;
 }
 
@@ -1553,6 +1945,7 @@ const char* ssm_status_string(ssm_status_t s) {
     case SSM_ERR_ALIGN: return "a pointer is not aligned to its element size";
     case SSM_ERR_ALIAS: return "an output buffer overlaps an input buffer";
     case SSM_ERR_HIP: return "a HIP runtime call failed (see ssm_last_hip_error)";
+    case SSM_ERR_UNSUPPORTED: return "valid arguments outside what this entry point implements (see the header)";
   }
   return "unknown status";
 }
@@ -1642,6 +2035,97 @@ ssm_status_t ssm_conv_scan_fwd(int64_t batch, int64_t dim, int64_t dstate, int64
     if (out == SSM_OK && ef != hipSuccess) out = hip_fail(ef);
   }
   return out;
+}
+
+ssm_status_t ssm_scan_bwd(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, ssm_dtype_t io,
+                          const void* u, const void* delta, const float* A, const void* B, const void* C,
+                          const float* D, const void* z, const float* delta_bias, int softplus_flag,
+                          const float* h0, const void* dy, const float* dlast, void* du, void* ddelta,
+                          float* dA, float* dB, float* dC, float* dD, void* dz, float* ddelta_bias, float* dh0,
+                          struct ihipStream_t* stream) {
+  Shape sh;
+  ssm_status_t st = shape_of(batch, dim, dstate, seqlen, io, &sh);
+  if (st != SSM_OK) return st;
+  if (!u || !delta || !A || !B || !C || !dy || !du || !ddelta || !dA || !dB || !dC) return SSM_ERR_NULL;
+  if (!z) dz = nullptr;
+  const size_t es = io_size(io);
+  const void* io_ptrs[] = {u, delta, B, C, z, dy, du, ddelta, dz};
+  for (const void* p : io_ptrs)
+    if (p && !aligned(p, es)) return SSM_ERR_ALIGN;
+  const void* f_ptrs[] = {A, D, delta_bias, h0, dlast, dA, dB, dC, dD, ddelta_bias, dh0};
+  for (const void* p : f_ptrs)
+    if (p && !aligned(p, 4)) return SSM_ERR_ALIGN;
+  const int64_t bdl = sh.bdl * (int64_t)es, bnl = sh.bnl * (int64_t)es;
+  const Range ins[] = {span(u, bdl), span(delta, bdl), span(A, sh.dn * 4), span(B, bnl), span(C, bnl),
+                       D ? span(D, dim * 4) : Range{0, 0}, z ? span(z, bdl) : Range{0, 0},
+                       delta_bias ? span(delta_bias, dim * 4) : Range{0, 0}, h0 ? span(h0, sh.bdn * 4) : Range{0, 0},
+                       span(dy, bdl), dlast ? span(dlast, sh.bdn * 4) : Range{0, 0}};
+  const Range outs[] = {span(du, bdl), span(ddelta, bdl), span(dA, sh.dn * 4), span(dB, sh.bnl * 4),
+                        span(dC, sh.bnl * 4), dD ? span(dD, dim * 4) : Range{0, 0}, dz ? span(dz, bdl) : Range{0, 0},
+                        ddelta_bias ? span(ddelta_bias, dim * 4) : Range{0, 0},
+                        dh0 ? span(dh0, sh.bdn * 4) : Range{0, 0}};
+  for (int o = 0; o < 9; ++o) {
+    if (outs[o].hi <= outs[o].lo) continue;
+    for (const Range& r : ins)
+      if (r.hi > r.lo && overlap(outs[o], r)) return SSM_ERR_ALIAS;
+    for (int q = o + 1; q < 9; ++q)
+      if (outs[q].hi > outs[q].lo && overlap(outs[o], outs[q])) return SSM_ERR_ALIAS;
+  }
+  if (!(dstate == 4 || dstate == 8 || dstate == 16)) return SSM_ERR_UNSUPPORTED;
+  if (!vec_rows(sh, dstate, seqlen, io, u, delta, B, C, z, dy) || !aligned(du, 16) || !aligned(ddelta, 16) ||
+      (dz && !aligned(dz, 16)))
+    return SSM_ERR_UNSUPPORTED;
+
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  const Plan plan = make_plan(sh, batch, dim, dstate, seqlen, io);
+  const int64_t groups = plan.groups;
+  const int64_t ntiles = (seqlen + kCkptTokens - 1) / kCkptTokens;
+  const int SA = bwd_token_waves(dstate);
+  // Scratch: checkpoints, per-group dB/dC partials, per-batch dA, dD, dbias partials.
+  const int64_t n_ckpt = ntiles * sh.bdn;
+  const int64_t n_part = groups * sh.bnl;
+  const int64_t n_small = sh.bdn + 2 * batch * SA * dim;
+  const int64_t scratch_floats = n_ckpt + 2 * n_part + n_small;
+  hipMemPool_t pool;
+  hipError_t e = get_pool(&pool);
+  if (e != hipSuccess) return hip_fail(e);
+  void* scratch = nullptr;
+  e = hipMallocFromPoolAsync(&scratch, (size_t)scratch_floats * 4, pool, hs);
+  if (e != hipSuccess) return hip_fail(e);
+  float* f = static_cast<float*>(scratch);
+
+  // 1. Forward with checkpoints (single-pass kernel; y goes to du, overwritten below).
+  ScanArgs fa = scan_args(sh, batch, dim, dstate, seqlen, io, u, delta, A, B, C, D, z, delta_bias, h0, du, nullptr);
+  fa.groups = groups; fa.segments = 1; fa.seg_len = seqlen;
+  fa.ckpt = f;
+  Plan fp = plan;
+  fp.split = true; fp.segments = 1; fp.seg_len = seqlen; fp.scratch_bytes = 0;
+  const bool sp = softplus_flag != 0;
+  e = (io == SSM_BF16) ? launch_scan<bf16_t>(fa, fp, hs, true, sp) : launch_scan<float>(fa, fp, hs, true, sp);
+  // 2. Backward over the tiles in reverse.
+  BwdArgs ba;
+  ba.u = u; ba.delta = delta; ba.A = A; ba.B = B; ba.C = C; ba.D = D; ba.z = z; ba.bias = delta_bias; ba.dy = dy;
+  ba.dlast = dlast; ba.ckpt = f; ba.du = du; ba.ddelta = ddelta; ba.dz = dz; ba.dh0 = dh0;
+  ba.dB_part = f + n_ckpt;
+  ba.dC_part = ba.dB_part + n_part;
+  ba.dA_part = ba.dC_part + n_part;
+  ba.dD_part = ba.dA_part + sh.bdn;
+  ba.dbias_part = ba.dD_part + batch * SA * dim;
+  ba.batch = batch; ba.dim = dim; ba.seqlen = seqlen; ba.groups = groups;
+  if (e == hipSuccess)
+    e = (io == SSM_BF16) ? launch_bwd<bf16_t>(ba, (int)dstate, hs, sp) : launch_bwd<float>(ba, (int)dstate, hs, sp);
+  // 3. Fixed-order sums of the partials.
+  if (e == hipSuccess) {
+    const int64_t n = std::max(sh.bnl, std::max(sh.dn, dim));
+    const int64_t blocks = (n + kBlockThreads - 1) / kBlockThreads;
+    hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)blocks), dim3(kBlockThreads), 0, hs, ba, (int)dstate, SA, dB,
+                       dC, dA, dD, ddelta_bias);
+    e = hipGetLastError();
+  }
+  hipError_t ef = hipFreeAsync(scratch, hs);
+  if (e == hipSuccess) e = ef;
+  if (e != hipSuccess) return hip_fail(e);
+  return SSM_OK;
 }
 
 ssm_status_t ssm_state_update(int64_t batch, int64_t dim, int64_t dstate, ssm_dtype_t io, float* state, const void* u,

@@ -42,7 +42,7 @@ def test_abi_version(lib):
 
 
 def test_status_strings(lib):
-    for code in range(8):
+    for code in range(9):
         s = lib.ssm_status_string(code)
         assert s and s != b"unknown status"
     assert lib.ssm_status_string(99) == b"unknown status"
@@ -152,6 +152,37 @@ def test_conv_scan_misaligned_and_aliasing(lib):
     assert cfwd(lib, y=addr(12)) == 6               # y on the conv weights
     assert cfwd(lib, y=addr(14)) == 6               # y on x_prev
     assert cfwd(lib, last=addr(13)) == 6            # last_state on the conv bias
+
+
+def bwd(lib, batch=2, dim=8, dstate=4, seqlen=16, io=0, **over):
+    args = dict(u=addr(1), delta=addr(2), A=addr(3), B=addr(4), C=addr(5), D=addr(6), z=addr(7), bias=addr(8), sp=1,
+                h0=addr(9), dy=addr(10), dlast=addr(11), du=addr(20), ddelta=addr(21), dA=addr(22), dB=addr(23),
+                dC=addr(24), dD=addr(25), dz=addr(26), dbias=addr(27), dh0=addr(28))
+    args.update(over)
+    return lib.ssm_scan_bwd(batch, dim, dstate, seqlen, io, args["u"], args["delta"], args["A"], args["B"], args["C"],
+                            args["D"], args["z"], args["bias"], args["sp"], args["h0"], args["dy"], args["dlast"],
+                            args["du"], args["ddelta"], args["dA"], args["dB"], args["dC"], args["dD"], args["dz"],
+                            args["dbias"], args["dh0"], None)
+
+
+@pytest.mark.parametrize("field", ["u", "delta", "A", "B", "C", "dy", "du", "ddelta", "dA", "dB", "dC"])
+def test_bwd_null_required(lib, field):
+    assert bwd(lib, **{field: None}) == 1
+
+
+def test_bwd_validation(lib):
+    assert bwd(lib, dstate=0) == 2
+    assert bwd(lib, dstate=17) == 3
+    assert bwd(lib, io=3) == 4
+    assert bwd(lib, dy=addr(10) + 2) == 5             # fp32 dy needs 4-byte alignment
+    assert bwd(lib, dB=addr(23) + 1) == 5
+    assert bwd(lib, du=addr(1)) == 6                  # du on u
+    assert bwd(lib, dA=addr(3) + 4) == 6              # dA overlapping A
+    assert bwd(lib, dz=addr(20)) == 6                 # two outputs on one buffer
+    assert bwd(lib, dh0=addr(11)) == 6                # dh0 on dlast
+    assert bwd(lib, dstate=5) == 8                    # valid, but the backward takes dstate 4, 8, 16 only
+    assert bwd(lib, seqlen=20) == 8                   # ... and seqlen a multiple of 8
+    assert bwd(lib, u=addr(1) + 4) == 8               # ... and 16-byte aligned rows
 
 
 def test_plan(lib):
