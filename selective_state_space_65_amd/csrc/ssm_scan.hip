@@ -41,6 +41,7 @@
 //     coalesced 16-byte accesses; the dot product with C is finished with a
 //     lane shuffle.
 #include <hip/hip_runtime.h>
+#include <type_traits>
 
 #include <algorithm>
 #include <cstdint>
@@ -1066,25 +1067,70 @@ struct BwdArgs {
 
 __device__ __forceinline__ float sigmoid_f32(float x) { return rcp_hw(1.0f + exp2_hw(-x * kLog2e)); }
 
-// Sum of NV values over the 64 lanes of a wave, all at once: after log2(NV)
-// exchange-and-add halvings (each lane keeps the half of the values its lane
-// bit selects and adds its partner's copy of that half), lane i holds the sum
-// over the wave of value i mod NV.  NV is a power of two up to 64.
+// Sum of NV values over the 64 lanes of a wave, all at once: log2(NV)
+// exchange-and-add halvings.  At the halving of distance m every lane keeps
+// the half of its values selected by lane bit m and adds the partner lane's
+// copy of that half; the partner differs in bit m (and, for the mirror
+// patterns, in lower bits only), so after the last halving lane i holds the
+// sum over the wave of value i mod NV.  Distances 32 and 16 are one
+// v_permlane32/16_swap per pair of registers (whichever order the pair comes
+// back in, lo + hi is the pair sum in each half); 8 and 4 are the DPP
+// row_mirror / row_half_mirror patterns, 2 and 1 quad permutes, each fused
+// into an add (both halves are added, the lane keeps one).  NV is 16, 32 or
+// 64.
+__device__ __forceinline__ float dpp_pair(float send, int ctrl_id) {
+  const uint32_t s = __float_as_uint(send);
+  uint32_t r;
+  switch (ctrl_id) {
+    case 8: r = __builtin_amdgcn_update_dpp(0u, s, 0x140, 0xF, 0xF, false); break;  // row_mirror
+    case 4: r = __builtin_amdgcn_update_dpp(0u, s, 0x141, 0xF, 0xF, false); break;  // row_half_mirror
+    case 2: r = __builtin_amdgcn_update_dpp(0u, s, 0x4E, 0xF, 0xF, false); break;   // quad_perm [2,3,0,1]
+    default: r = __builtin_amdgcn_update_dpp(0u, s, 0xB1, 0xF, 0xF, false); break;  // quad_perm [1,0,3,2]
+  }
+  return __uint_as_float(r);
+}
+
 template <int NV>
 __device__ __forceinline__ float wave_sum_spread(float (&v)[NV], int lane) {
+  constexpr int kStages = NV == 64 ? 6 : (NV == 32 ? 5 : 4);
+  // (Counted loops: a shift-stepped loop is not fully unrolled, and a
+  // run-time m would turn every v[] access into a select chain.)
 #pragma unroll
-  for (int m = NV / 2; m >= 1; m >>= 1) {
-    const bool hi = (lane & m) != 0;
+  for (int st = 0; st < kStages; ++st) {
+    const int m = NV >> (st + 1);
+    if (m >= 16) {
 #pragma unroll
-    for (int i = 0; i < m; ++i) {
-      const float send = hi ? v[i] : v[m + i];
-      const float keep = hi ? v[m + i] : v[i];
-      v[i] = keep + __shfl_xor(send, m);
+      for (int i = 0; i < m; ++i) {
+        const auto r = (m == 32) ? __builtin_amdgcn_permlane32_swap(__float_as_uint(v[i]), __float_as_uint(v[m + i]),
+                                                                    false, false)
+                                 : __builtin_amdgcn_permlane16_swap(__float_as_uint(v[i]), __float_as_uint(v[m + i]),
+                                                                    false, false);
+        v[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+      }
+    } else {
+      // Both halves are summed with the partner and the lane keeps one: a
+      // select between two loaded values would be folded into one load at a
+      // lane-dependent index, which cannot stay in registers.
+      const bool hi = (lane & m) != 0;
+#pragma unroll
+      for (int i = 0; i < m; ++i) {
+        const float lo_sum = v[i] + dpp_pair(v[i], m);
+        const float hi_sum = v[m + i] + dpp_pair(v[m + i], m);
+        v[i] = hi ? hi_sum : lo_sum;
+      }
     }
   }
+  static_assert(NV >= 16 && NV <= 64 && (NV & (NV - 1)) == 0, "16, 32 or 64 values");
+  // Below 64 values each 16- or 32-lane part of the wave holds sums over
+  // itself only: add the parts (a register swapped with itself).
   float r = v[0];
 #pragma unroll
-  for (int m = NV; m < 64; m <<= 1) r += __shfl_xor(r, m);
+  for (int st = kStages; st < 6; ++st) {
+    const int m = 1 << st;
+    const auto p = (m == 32) ? __builtin_amdgcn_permlane32_swap(__float_as_uint(r), __float_as_uint(r), false, false)
+                             : __builtin_amdgcn_permlane16_swap(__float_as_uint(r), __float_as_uint(r), false, false);
+    r = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  }
   return r;
 }
 
@@ -1094,13 +1140,13 @@ __global__ __launch_bounds__(64 * S) void scan_bwd_kernel(BwdArgs a) {
   constexpr int T = kCkptTokens;
   constexpr int KT = T / kChunk;
   constexpr int TS = T / SA;
-  constexpr int NV = 2 * NS * T;  // per-lane products summed over the wave per tile: dB, then dC
+  constexpr int NV = 2 * NS * kChunk;  // per-lane products summed over the wave per sub-chunk: dB, then dC
   using LI = Line<IoT>;
   using PI = Piece<IoT, TS>;
   using U = Uni<IoT>;
   constexpr int PW = PI::kWords, ZW = kZ ? PI::kWords : 1, W = U::kWords;
-  static_assert(N % S == 0 && NS <= 2 && S % SA == 0 && TS % 2 == 0 && kChunk % TS == 0, "backward tile shape");
-  static_assert(NV <= 64 && (NV & (NV - 1)) == 0, "one wave-wide sum per tile");
+  static_assert(N % S == 0 && NS <= 2 && S % SA == 0 && TS % 2 == 0 && kChunk % TS == 0 && KT == 2,
+                "backward tile shape");
   __shared__ float4 dxs[T / 2][64];  // (Delta_t, x_t, Delta_t+1, x_t+1)
   __shared__ float2 part[S][T][64];  // per-wave partials: P1 .x = C.h; P3 .x = sum lambda A q, .y = sum lambda B
   __shared__ float gs[T][64];        // g_t
@@ -1139,11 +1185,13 @@ __global__ __launch_bounds__(64 * S) void scan_bwd_kernel(BwdArgs a) {
   const IoT* Cb = static_cast<const IoT*>(a.C) + b * N * L;
   const uint32_t row_bytes = (uint32_t)(L * sizeof(IoT));
 
-  const int64_t ntiles = (L + T - 1) / T;
-  for (int64_t c = ntiles - 1; c >= 0; --c) {
+  // One tile of KV sub-chunks of kChunk tokens (KV = KT, or 1 for a last
+  // tile of 8 tokens), so that every loop below has a static trip count.
+  auto tile = [&](int64_t c, auto kv_tag) {
+    constexpr int KV = decltype(kv_tag)::value;
+    constexpr int VT = KV * kChunk;
     const int64_t l = c * T;
-    const int valid = (int)min((int64_t)T, L - l);  // a multiple of kChunk
-    const bool acw = w < SA && w * TS < valid;       // this wave's per-token share exists
+    const bool acw = w < SA && w * TS < VT;  // this wave's per-token share exists
     // ---- P0
     uint32_t qu[PW], qd[PW], qz[ZW], qy[PW];
     float dlv4[TS], sgd4[TS], g4[TS];
@@ -1168,44 +1216,40 @@ __global__ __launch_bounds__(64 * S) void scan_bwd_kernel(BwdArgs a) {
     }
     lds_barrier();
     // ---- P1: the tile's states from its checkpoint (B/C rows of this wave's states as scalar words)
-    uint32_t Bt[NS][KT][W], Ct[NS][KT][W];
+    uint32_t Bt[NS][KV][W], Ct[NS][KV][W];
 #pragma unroll
     for (int j = 0; j < NS; ++j)
 #pragma unroll
-      for (int k = 0; k < KT; ++k)
-        if (k * kChunk < valid) {
-          uint32_t off = (uint32_t)(w * NS + j) * row_bytes + (uint32_t)((l + k * kChunk) * sizeof(IoT));
-          asm volatile("" : "+s"(off));
-          U::load8(Bb, off, Bt[j][k]);
-          U::load8(Cb, off, Ct[j][k]);
-        }
-    float dlv[T], xv[T];
-#pragma unroll
-    for (int i = 0; i < T / 2; ++i)
-      if (2 * i < valid) {
-        const float4 v = dxs[i][lane];
-        dlv[2 * i] = v.x; xv[2 * i] = v.y; dlv[2 * i + 1] = v.z; xv[2 * i + 1] = v.w;
+      for (int k = 0; k < KV; ++k) {
+        uint32_t off = (uint32_t)(w * NS + j) * row_bytes + (uint32_t)((l + k * kChunk) * sizeof(IoT));
+        asm volatile("" : "+s"(off));
+        U::load8(Bb, off, Bt[j][k]);
+        U::load8(Cb, off, Ct[j][k]);
       }
-    float hs[NS][T], ab[NS][T];
+    float dlv[VT], xv[VT];
+#pragma unroll
+    for (int i = 0; i < VT / 2; ++i) {
+      const float4 v = dxs[i][lane];
+      dlv[2 * i] = v.x; xv[2 * i] = v.y; dlv[2 * i + 1] = v.z; xv[2 * i + 1] = v.w;
+    }
+    float hs[NS][VT], ab[NS][VT];
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
       float hc = a.ckpt[((c * a.batch + b) * N + w * NS + j) * a.dim + d];
 #pragma unroll
-      for (int t = 0; t < T; ++t)
-        if (t < valid) {
-          ab[j][t] = exp2_hw(A2[j] * dlv[t]);
-          hc = __builtin_fmaf(ab[j][t], hc, U::elem(Bt[j][t / kChunk], t % kChunk) * xv[t]);
-          hs[j][t] = hc;
-        }
+      for (int t = 0; t < VT; ++t) {
+        ab[j][t] = exp2_hw(A2[j] * dlv[t]);
+        hc = __builtin_fmaf(ab[j][t], hc, U::elem(Bt[j][t / kChunk], t % kChunk) * xv[t]);
+        hs[j][t] = hc;
+      }
     }
 #pragma unroll
-    for (int t = 0; t < T; ++t)
-      if (t < valid) {
-        float ps = U::elem(Ct[0][t / kChunk], t % kChunk) * hs[0][t];
+    for (int t = 0; t < VT; ++t) {
+      float ps = U::elem(Ct[0][t / kChunk], t % kChunk) * hs[0][t];
 #pragma unroll
-        for (int j = 1; j < NS; ++j) ps = __builtin_fmaf(U::elem(Ct[j][t / kChunk], t % kChunk), hs[j][t], ps);
-        part[w][t][lane] = make_float2(ps, 0.0f);
-      }
+      for (int j = 1; j < NS; ++j) ps = __builtin_fmaf(U::elem(Ct[j][t / kChunk], t % kChunk), hs[j][t], ps);
+      part[w][t][lane] = make_float2(ps, 0.0f);
+    }
     lds_barrier();
     // ---- P2
     if (acw) {
@@ -1240,45 +1284,40 @@ __global__ __launch_bounds__(64 * S) void scan_bwd_kernel(BwdArgs a) {
       if (kZ && dzr && active) PI::store(dzr + l + w * TS, zw);
     }
     lds_barrier();
-    // ---- P3
-    float gv[T];
+    // ---- P3: this wave's states backwards over the tile, one sub-chunk at a time
+    float gv[VT];
 #pragma unroll
-    for (int t = 0; t < T; ++t)
-      if (t < valid) gv[t] = gs[t][lane];
-    float pv[NV];
+    for (int t = 0; t < VT; ++t) gv[t] = gs[t][lane];
 #pragma unroll
-    for (int i = 0; i < NV; ++i) pv[i] = 0.0f;
+    for (int k = KV - 1; k >= 0; --k) {
+      float pv[NV];
 #pragma unroll
-    for (int t = T - 1; t >= 0; --t)
-      if (t < valid) {
+      for (int t = kChunk - 1; t >= 0; --t) {
+        const int tt = k * kChunk + t;
         float sA = 0.0f, sB = 0.0f;
 #pragma unroll
         for (int j = 0; j < NS; ++j) {
-          const float cv = U::elem(Ct[j][t / kChunk], t % kChunk);
-          const float bv = U::elem(Bt[j][t / kChunk], t % kChunk);
-          const float lam = __builtin_fmaf(gv[t], cv, carry[j]);
-          pv[j * T + t] = lam * xv[t];
-          pv[NS * T + j * T + t] = gv[t] * hs[j][t];
-          const float q = __builtin_fmaf(-bv, xv[t], hs[j][t]);  // Abar_t h_{t-1}
+          const float cv = U::elem(Ct[j][k], t);
+          const float bv = U::elem(Bt[j][k], t);
+          const float lam = __builtin_fmaf(gv[tt], cv, carry[j]);
+          pv[j * kChunk + t] = active ? lam * xv[tt] : 0.0f;
+          pv[NS * kChunk + j * kChunk + t] = active ? gv[tt] * hs[j][tt] : 0.0f;
+          const float q = __builtin_fmaf(-bv, xv[tt], hs[j][tt]);  // Abar_t h_{t-1}
           sB = __builtin_fmaf(lam, bv, sB);
           sA = __builtin_fmaf(lam * Af[j], q, sA);
-          dA_acc[j] = __builtin_fmaf(lam * dlv[t], q, dA_acc[j]);
-          carry[j] = ab[j][t] * lam;
+          dA_acc[j] = __builtin_fmaf(lam * dlv[tt], q, dA_acc[j]);
+          carry[j] = ab[j][tt] * lam;
         }
-        part[w][t][lane] = make_float2(sA, sB);
+        part[w][tt][lane] = make_float2(sA, sB);
       }
-    {
-      // Lanes past the last channel run on a copy of it; they must add nothing.
-      if (!active) {
-#pragma unroll
-        for (int i = 0; i < NV; ++i) pv[i] = 0.0f;
-      }
+      // Sum the products over the wave's 64 channels (lanes past the last
+      // channel run on a copy of it and contribute zero).
       const float tot = wave_sum_spread<NV>(pv, lane);
       const int i = lane % NV;
-      const int which = i / (NS * T), jj = (i % (NS * T)) / T, t = i % T;
-      if (lane < NV && t < valid) {
+      const int which = i / (NS * kChunk), jj = (i % (NS * kChunk)) / kChunk, t = i % kChunk;
+      if (lane < NV) {
         float* dst = which ? a.dC_part : a.dB_part;
-        dst[((grp * a.batch + b) * N + w * NS + jj) * L + l + t] = tot;
+        dst[((grp * a.batch + b) * N + w * NS + jj) * L + l + k * kChunk + t] = tot;
       }
     }
     lds_barrier();
@@ -1316,6 +1355,14 @@ __global__ __launch_bounds__(64 * S) void scan_bwd_kernel(BwdArgs a) {
         PI::store(ddr + l + w * TS, dw);
       }
     }
+  };
+
+  const int64_t ntiles = (L + T - 1) / T;
+  for (int64_t c = ntiles - 1; c >= 0; --c) {
+    if (L - c * T >= T)
+      tile(c, std::integral_constant<int, KT>{});
+    else
+      tile(c, std::integral_constant<int, 1>{});  // a last tile of kChunk tokens
   }
   if (active) {
 #pragma unroll
