@@ -15,6 +15,7 @@ the timed region.  Prints one JSON line:
                dim 5120, dstate 16), per step
   conv_scan    ssm_conv_scan_fwd (causal conv of width 4 fused in front of the
                scan) on the same workload
+  backward     ssm_scan_bwd (every gradient) on the same workload
 
 Algorithmic bytes: read u, delta, z and write y once (4 x io bytes per
 element), read B and C once per (batch, token), read A, D and the bias once,
@@ -180,6 +181,34 @@ def bench_conv_scan(dev, x, t, steps, warmup):
                 algorithmic_gbs=round(nbytes / (avg_ms * 1e-3) / 1e9, 1), algorithmic_bytes=nbytes)
 
 
+BWD_SLOTS_PER_ELEM_STATE = 20  # 6 for the checkpointing forward + 14 for the adjoint walk
+
+
+def bench_backward(dev, x, t, steps, warmup):
+    """ssm_scan_bwd on the same workload: every gradient of sum(dy * y)."""
+    import torch
+    from selective_state_space_65_amd import binding, inputs
+    b, d, n, l = x.shape
+    dy = torch.from_numpy(inputs.grad_output(x)).to(dev, t["u"].dtype)
+
+    def fn():
+        binding.scan_bwd(t["u"], t["delta"], t["A"], t["B"], t["C"], dy, D=t["D"], z=t["z"], delta_bias=t["delta_bias"],
+                         delta_softplus=x.softplus, h0=None)
+
+    wall_ms, avg_ms, med_ms = time_calls(fn, steps, warmup)
+    io_bytes = 2 if x.io == "bf16" else 4
+    el = b * d * l
+    # read u, delta, z, dy, B, C (+ A, D, bias); write du, ddelta, dz, dB, dC (fp32), dA, dD, dbias
+    nbytes = 4 * el * io_bytes + 2 * b * n * l * io_bytes + d * n * 4 + 2 * d * 4 + 3 * el * io_bytes \
+        + 2 * b * n * l * 4 + d * n * 4 + 2 * d * 4
+    slots = BWD_SLOTS_PER_ELEM_STATE * el * n
+    return dict(workload="ssm_scan_bwd (every gradient), same shape and flags", us_per_call=round(avg_ms * 1e3, 2),
+                us_median=round(med_ms * 1e3, 2), algorithmic_gbs=round(nbytes / (avg_ms * 1e-3) / 1e9, 1),
+                algorithmic_bytes=nbytes, alu_frac=round(slots / (avg_ms * 1e-3) / LANE_SLOTS_PEAK, 4),
+                lane_slots_per_elem_state=BWD_SLOTS_PER_ELEM_STATE,
+                vs_forward=None)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -190,6 +219,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-conv", action="store_true", help="skip the fused conv + scan line")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy 1 GiB three times (reference kernel for rocprofv3 FETCH_SIZE/WRITE_SIZE)")
     args = ap.parse_args()
@@ -258,6 +288,10 @@ def main():
         out["decode"] = bench_decode(dev, 50, 5)
     if not args.no_conv:
         out["conv_scan"] = bench_conv_scan(dev, x, t, args.steps, args.warmup)
+    if not args.no_backward:
+        bw = bench_backward(dev, x, t, max(3, args.steps // 4), 2)
+        bw["vs_forward"] = round(bw["us_per_call"] / (avg_ms * 1e3), 2)
+        out["backward"] = bw
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(x, args.cpu_seconds)
     print(json.dumps(out), flush=True)

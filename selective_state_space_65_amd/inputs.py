@@ -120,6 +120,13 @@ def conv_params(dim, width=4, seed=SEED_BASE + 10):
     return w, cb
 
 
+def grad_output(x, seed=SEED_BASE + 20):
+    """dL/dy for the backward, (batch, dim, seqlen) ~ N(0, 1), bf16-rounded for bf16 io."""
+    rng = np.random.default_rng(seed)
+    dy = _normal(rng, x.u.shape)
+    return round_bf16(dy) if x.io == "bf16" else dy
+
+
 @dataclass
 class DecodeInputs:
     state0: np.ndarray  # (batch, dim, dstate) float32
