@@ -1,11 +1,15 @@
 /*
  * ssm_scan.h -- C ABI of the MI355X (gfx950) selective state-space scan (S6).
  *
- * Two operations, both on device memory, both asynchronous on the caller's
+ * Four operations, all on device memory, all asynchronous on the caller's
  * HIP stream:
  *
- *   ssm_scan_fwd      prefill: run the selective scan over a whole sequence;
- *   ssm_state_update  decode: advance a persistent state by one token.
+ *   ssm_scan_fwd       prefill: run the selective scan over a whole sequence;
+ *   ssm_state_update   decode: advance a persistent state by one token;
+ *   ssm_conv_scan_fwd  prefill with the block's short causal depthwise
+ *                      convolution (and its silu) fused in front of the scan;
+ *   ssm_scan_bwd       training: every gradient of a scalar loss through
+ *                      ssm_scan_fwd, given dL/dy (and optionally dL/dh_L).
  *
  * What is computed (for every batch row b and channel d independently):
  *
@@ -27,7 +31,7 @@
  * (y_l uses h_l, which already holds u_l), D skip before the gate, silu gate,
  * softplus applied to delta + bias, zero initial state unless h0 is given.
  *
- * Conventions shared by both entry points
+ * Conventions shared by the entry points
  *  - Every pointer is a DEVICE pointer to contiguous, row-major memory (last
  *    index fastest).  The caller owns every buffer; the library never keeps a
  *    pointer after the call returns.
