@@ -8,7 +8,8 @@ this module only marshals numpy arrays into it.
 
   Oracle(path)             a loaded oracle library (the default is built from
                            ssm_oracle.c next to this file)
-  .scan_f64(...)           full prefill scan, every (batch, channel)
+  .scan_f64(...)           full prefill scan, every (batch, channel); zoh=True
+                           discretizes B by exact zero-order hold
   .scan_channels_f64(...)  the same scan restricted to chosen (b, d) channels
                            (channels are independent, so a subset is exact)
   .state_update_f64(...)   one-token update of a float64 state, in place
@@ -53,10 +54,12 @@ class Oracle:
     def __init__(self, path=LIB_PATH):
         L = ctypes.CDLL(path)
         P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
-        L.oracle_scan_f64.restype = I
-        L.oracle_scan_f64.argtypes = [I64, I64, I64, I64] + [P] * 8 + [I, P, P, P]
-        L.oracle_state_update_f64.restype = I
-        L.oracle_state_update_f64.argtypes = [I64, I64, I64] + [P] * 9 + [I, P]
+        L.oracle_scan_ex_f64.restype = I
+        L.oracle_scan_ex_f64.argtypes = [I64, I64, I64, I64, I] + [P] * 8 + [I, P, P, P]
+        L.oracle_state_update_ex_f64.restype = I
+        L.oracle_state_update_ex_f64.argtypes = [I64, I64, I64, I] + [P] * 9 + [I, P]
+        L.oracle_zoh_b.restype = ctypes.c_double
+        L.oracle_zoh_b.argtypes = [ctypes.c_double, ctypes.c_double]
         L.oracle_scan_bwd_f64.restype = I
         L.oracle_scan_bwd_f64.argtypes = [I64, I64, I64, I64] + [P] * 8 + [I] + [P] * 12
         L.oracle_conv1d_f64.restype = I
@@ -74,15 +77,19 @@ class Oracle:
     def silu_f64(self, x):
         return self.lib.oracle_silu(float(x))
 
-    def scan_f64(self, u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=False, h0=None):
+    def zoh_b_f64(self, delta, a):
+        return self.lib.oracle_zoh_b(float(delta), float(a))
+
+    def scan_f64(self, u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=False, h0=None, zoh=False):
         """Returns (y, last_state) in float64.  Shapes as in ssm_oracle.c."""
         u, delta, A, B, C, D, z, delta_bias, h0 = map(_f64, (u, delta, A, B, C, D, z, delta_bias, h0))
         batch, dim, seqlen = u.shape
         dstate = A.shape[1]
         y = np.empty((batch, dim, seqlen), np.float64)
         last = np.empty((batch, dim, dstate), np.float64)
-        rc = self.lib.oracle_scan_f64(batch, dim, dstate, seqlen, _p(u), _p(delta), _p(A), _p(B), _p(C), _p(D),
-                                      _p(z), _p(delta_bias), 1 if softplus else 0, _p(h0), _p(y), _p(last))
+        rc = self.lib.oracle_scan_ex_f64(batch, dim, dstate, seqlen, 1 if zoh else 0, _p(u), _p(delta), _p(A), _p(B),
+                                         _p(C), _p(D), _p(z), _p(delta_bias), 1 if softplus else 0, _p(h0), _p(y),
+                                         _p(last))
         if rc != 0:
             raise ValueError("oracle_scan_f64 rejected the arguments")
         return y, last
@@ -128,7 +135,7 @@ class Oracle:
         return u
 
     def scan_channels_f64(self, channels, u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=False,
-                          h0=None):
+                          h0=None, zoh=False):
         """Scan only the listed (b, d) channels; returns (y[k, seqlen], last_state[k, dstate]).
 
         Pure marshalling: each channel becomes a batch-1, dim-1 problem with its
@@ -140,13 +147,13 @@ class Oracle:
                 return None if t is None else t[b:b + 1, d:d + 1]
             y, h = self.scan_f64(sl(u), sl(delta), A[d:d + 1], B[b:b + 1], C[b:b + 1],
                                  None if D is None else D[d:d + 1], sl(z),
-                                 None if delta_bias is None else delta_bias[d:d + 1], softplus, sl(h0))
+                                 None if delta_bias is None else delta_bias[d:d + 1], softplus, sl(h0), zoh=zoh)
             ys.append(y[0, 0])
             hs.append(h[0, 0])
         return np.stack(ys), np.stack(hs)
 
     def state_update_channels_f64(self, channels, state_rows, u, delta, A, B, C, D=None, z=None, delta_bias=None,
-                                  softplus=False):
+                                  softplus=False, zoh=False):
         """One-token update of chosen (b, d) channels only.
 
         state_rows: float64 (k, dstate), row i belongs to channels[i], updated in
@@ -158,18 +165,19 @@ class Oracle:
             y[i] = self.state_update_f64(st, u[b:b + 1, d:d + 1], delta[b:b + 1, d:d + 1], A[d:d + 1], B[b:b + 1],
                                          C[b:b + 1], None if D is None else D[d:d + 1],
                                          None if z is None else z[b:b + 1, d:d + 1],
-                                         None if delta_bias is None else delta_bias[d:d + 1], softplus)[0, 0]
+                                         None if delta_bias is None else delta_bias[d:d + 1], softplus, zoh=zoh)[0, 0]
         return y
 
-    def state_update_f64(self, state, u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=False):
+    def state_update_f64(self, state, u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=False, zoh=False):
         """Advance `state` (float64 (batch, dim, dstate), modified in place) by one token; returns y (batch, dim)."""
         if state.dtype != np.float64 or not state.flags["C_CONTIGUOUS"]:
             raise TypeError("state must be a C-contiguous float64 array (it is updated in place)")
         u, delta, A, B, C, D, z, delta_bias = map(_f64, (u, delta, A, B, C, D, z, delta_bias))
         batch, dim, dstate = state.shape
         y = np.empty((batch, dim), np.float64)
-        rc = self.lib.oracle_state_update_f64(batch, dim, dstate, _p(state), _p(u), _p(delta), _p(A), _p(B),
-                                              _p(C), _p(D), _p(z), _p(delta_bias), 1 if softplus else 0, _p(y))
+        rc = self.lib.oracle_state_update_ex_f64(batch, dim, dstate, 1 if zoh else 0, _p(state), _p(u), _p(delta),
+                                                 _p(A), _p(B), _p(C), _p(D), _p(z), _p(delta_bias),
+                                                 1 if softplus else 0, _p(y))
         if rc != 0:
             raise ValueError("oracle_state_update_f64 rejected the arguments")
         return y
@@ -209,6 +217,10 @@ def scan_bwd_f64(*args, **kw):
 
 def conv1d_f64(*args, **kw):
     return default().conv1d_f64(*args, **kw)
+
+
+def zoh_b_f64(delta, a):
+    return default().zoh_b_f64(delta, a)
 
 
 def softplus_f64(x):

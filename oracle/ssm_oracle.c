@@ -42,6 +42,14 @@
  *  - Delta = softplus(delta + bias) when the flag is set, else delta + bias;
  *  - the initial state is h0 when given, else zero.
  *
+ * Exact zero-order hold for B (the _ex entry points with zoh = 1).  The
+ * explainer's stage (1a/1b) names zero-order hold as one of several
+ * discretization rules.  Holding u constant over a step of length Delta and
+ * solving dh/dt = A h + B u exactly gives, per state of a diagonal A,
+ *   h(Delta) = exp(Delta A) h(0) + (exp(Delta A) - 1) / A * B * u,
+ * so Bbar = (exp(Delta A) - 1) / A * B, whose limit at A = 0 is Delta * B
+ * (oracle_zoh_b).  Abar is the same exp(Delta A) in both rules.
+ *
  * The Mamba block puts a causal Conv1d in front of the SSM (the Hebrew
  * overview, "תחילת העבודה עם Mamba"; the Chinese explainer's section on why a
  * convolution precedes the SSM: each token is first mixed with its neighbours
@@ -68,7 +76,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-#define ORACLE_ABI_VERSION 1
+#define ORACLE_ABI_VERSION 2
 
 int oracle_abi_version(void) { return ORACLE_ABI_VERSION; }
 
@@ -82,10 +90,15 @@ double oracle_softplus(double x) {
 /* silu(z) = z * sigmoid(z) = z / (1 + e^{-z}). */
 double oracle_silu(double z) { return z / (1.0 + exp(-z)); }
 
+/* The zero-order-hold factor of B for one state: (e^{delta a} - 1) / a,
+ * written with expm1 (no cancellation for small |delta a|); delta at a = 0. */
+double oracle_zoh_b(double delta, double a) { return a != 0.0 ? expm1(delta * a) / a : delta; }
+
 /* One channel (b, d): walk the sequence once.  h has dstate entries. */
 static void scan_channel(int64_t dstate, int64_t seqlen, const double* u_row, const double* dt_row,
                          const double* A_row, const double* B_b, const double* C_b, double Dd,
-                         const double* z_row, double bias, int softplus_flag, double* h, double* y_row) {
+                         const double* z_row, double bias, int softplus_flag, int zoh, double* h,
+                         double* y_row) {
   for (int64_t l = 0; l < seqlen; ++l) {
     double x = dt_row[l] + bias;
     double delta = softplus_flag ? oracle_softplus(x) : x;
@@ -94,6 +107,7 @@ static void scan_channel(int64_t dstate, int64_t seqlen, const double* u_row, co
     for (int64_t n = 0; n < dstate; ++n) {
       double abar = exp(delta * A_row[n]);
       double bbar_u = delta * B_b[n * seqlen + l] * ul;
+      if (zoh) bbar_u = oracle_zoh_b(delta, A_row[n]) * B_b[n * seqlen + l] * ul;
       h[n] = abar * h[n] + bbar_u;
       v += C_b[n * seqlen + l] * h[n];
     }
@@ -103,14 +117,15 @@ static void scan_channel(int64_t dstate, int64_t seqlen, const double* u_row, co
   }
 }
 
-/* Full prefill scan over every (b, d).  Parallel only across independent
+/* Full prefill scan over every (b, d), B discretized as Delta*B (zoh = 0) or
+ * by exact zero-order hold (zoh = 1).  Parallel only across independent
  * channels; each channel is sequential in l.  Returns 0, or -1 on bad sizes
- * (dstate above 256 included) or a missing required pointer. */
-int oracle_scan_f64(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, const double* u,
-                    const double* delta, const double* A, const double* B, const double* C,
-                    const double* D, const double* z, const double* delta_bias, int softplus_flag,
-                    const double* h0, double* y, double* last_state) {
-  if (batch < 1 || dim < 1 || dstate < 1 || dstate > 256 || seqlen < 1) return -1;
+ * (dstate above 256 included), a bad zoh value or a missing required pointer. */
+int oracle_scan_ex_f64(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int zoh, const double* u,
+                       const double* delta, const double* A, const double* B, const double* C,
+                       const double* D, const double* z, const double* delta_bias, int softplus_flag,
+                       const double* h0, double* y, double* last_state) {
+  if (batch < 1 || dim < 1 || dstate < 1 || dstate > 256 || seqlen < 1 || (zoh != 0 && zoh != 1)) return -1;
   if (!u || !delta || !A || !B || !C || !y) return -1;
   int64_t nch = batch * dim;
 #pragma omp parallel for schedule(dynamic, 1)
@@ -121,20 +136,29 @@ int oracle_scan_f64(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, 
     const double* zr = z ? z + ch * seqlen : NULL;
     scan_channel(dstate, seqlen, u + ch * seqlen, delta + ch * seqlen, A + d * dstate,
                  B + b * dstate * seqlen, C + b * dstate * seqlen, D ? D[d] : 0.0, zr,
-                 delta_bias ? delta_bias[d] : 0.0, softplus_flag, h, y + ch * seqlen);
+                 delta_bias ? delta_bias[d] : 0.0, softplus_flag, zoh, h, y + ch * seqlen);
     if (last_state)
       for (int64_t n = 0; n < dstate; ++n) last_state[ch * dstate + n] = h[n];
   }
   return 0;
 }
 
+/* The prefill scan with B discretized as Delta*B. */
+int oracle_scan_f64(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, const double* u,
+                    const double* delta, const double* A, const double* B, const double* C,
+                    const double* D, const double* z, const double* delta_bias, int softplus_flag,
+                    const double* h0, double* y, double* last_state) {
+  return oracle_scan_ex_f64(batch, dim, dstate, seqlen, 0, u, delta, A, B, C, D, z, delta_bias, softplus_flag, h0,
+                            y, last_state);
+}
+
 /* One-token recurrent update, in place on state[batch][dim][dstate].
- * u, delta, z, y: [batch][dim]; B, C: [batch][dstate]. */
-int oracle_state_update_f64(int64_t batch, int64_t dim, int64_t dstate, double* state, const double* u,
-                            const double* delta, const double* A, const double* B, const double* C,
-                            const double* D, const double* z, const double* delta_bias,
-                            int softplus_flag, double* y) {
-  if (batch < 1 || dim < 1 || dstate < 1 || dstate > 256) return -1;
+ * u, delta, z, y: [batch][dim]; B, C: [batch][dstate]; zoh as above. */
+int oracle_state_update_ex_f64(int64_t batch, int64_t dim, int64_t dstate, int zoh, double* state,
+                               const double* u, const double* delta, const double* A, const double* B,
+                               const double* C, const double* D, const double* z, const double* delta_bias,
+                               int softplus_flag, double* y) {
+  if (batch < 1 || dim < 1 || dstate < 1 || dstate > 256 || (zoh != 0 && zoh != 1)) return -1;
   if (!state || !u || !delta || !A || !B || !C || !y) return -1;
   int64_t nch = batch * dim;
 #pragma omp parallel for schedule(static)
@@ -142,10 +166,18 @@ int oracle_state_update_f64(int64_t batch, int64_t dim, int64_t dstate, double* 
     int64_t b = ch / dim, d = ch % dim;
     /* A one-token sequence: B[b,:] and C[b,:] viewed as [dstate][1]. */
     scan_channel(dstate, 1, u + ch, delta + ch, A + d * dstate, B + b * dstate, C + b * dstate,
-                 D ? D[d] : 0.0, z ? z + ch : NULL, delta_bias ? delta_bias[d] : 0.0, softplus_flag,
+                 D ? D[d] : 0.0, z ? z + ch : NULL, delta_bias ? delta_bias[d] : 0.0, softplus_flag, zoh,
                  state + ch * dstate, y + ch);
   }
   return 0;
+}
+
+int oracle_state_update_f64(int64_t batch, int64_t dim, int64_t dstate, double* state, const double* u,
+                            const double* delta, const double* A, const double* B, const double* C,
+                            const double* D, const double* z, const double* delta_bias,
+                            int softplus_flag, double* y) {
+  return oracle_state_update_ex_f64(batch, dim, dstate, 0, state, u, delta, A, B, C, D, z, delta_bias,
+                                    softplus_flag, y);
 }
 
 /* Causal depthwise convolution of every (b, d) row, then silu if the flag is

@@ -34,6 +34,14 @@ deliberately broken copies of it (tests/test_oracle_mutants.py).
                     differences of the forward oracle, every input, every flag
   bwd_autograd      the same gradients against torch autograd (fp64, CPU) through an
                     independently written vectorised forward
+  zoh_van_loan      exact zero-order hold for B: every step equals the block matrix
+                    exponential expm([[a, b u], [0, 0]] Delta) per state (scipy), which
+                    holds Abar and Bbar u of the held-input ODE; A with zeros included
+  zoh_fixed_point   constant input: the ZOH state converges to -B u / A whatever
+                    Delta is (the ODE's equilibrium), the Delta*B rule's does not
+  zoh_limits        at A = 0 ZOH equals the Delta*B rule, and for small |Delta A|
+                    its factor follows the series Delta (1 + Delta A / 2 + ...)
+  zoh_decode        the one-token ZOH update equals a one-token ZOH scan
 """
 import json
 import math
@@ -94,7 +102,7 @@ def worked_examples(o):
 
     for case in data["cases"]:
         args = {k: ev(case[k]) for k in ("u", "delta", "A", "B", "C", "D", "z", "delta_bias", "h0")}
-        y, last = o.scan_f64(softplus=case["softplus"], **args)
+        y, last = o.scan_f64(softplus=case["softplus"], zoh=case.get("zoh", False), **args)
         _close(y, ev(case["expected_y"]), 1e-14, 1e-14, case["name"] + " y")
         _close(last, ev(case["expected_last_state"]), 1e-14, 1e-14, case["name"] + " last_state")
 
@@ -425,6 +433,81 @@ def bwd_autograd(o):
             _close(g[key], ref[name], 1e-11, 1e-12, "autograd d/d%s flags=%s" % (name, flags))
 
 
+def zoh_van_loan(o):
+    from scipy.linalg import expm
+    rng = _rng(30)
+    batch, dim, dstate, seqlen = 2, 3, 4, 7
+    for flags in ((True, True, True, True, True), (False, False, False, False, False), (True, False, True, True, False)):
+        zf, Df, bf, spf, hf = flags
+        p = _random_problem(rng, batch, dim, dstate, seqlen, z=zf, D=Df, bias=bf, h0=hf)
+        p["A"][0, 1] = 0.0         # a non-decaying state
+        p["A"][2, 3] = -1e-9       # nearly non-decaying
+        y, last = o.scan_f64(softplus=spf, zoh=True, **p)
+        x = p["delta"] + (p["delta_bias"][None, :, None] if bf else 0.0)
+        step = np.logaddexp(x, 0.0) if spf else x
+        for b in range(batch):
+            for d in range(dim):
+                h = p["h0"][b, d].copy() if hf else np.zeros(dstate)
+                for t in range(seqlen):
+                    # A is diagonal, so the (N+1)-square block exponential splits
+                    # into one 2 x 2 block per state (scipy's expm of the whole
+                    # block matrix loses ~1e-8 when its diagonal spans 1e-9..3).
+                    for n in range(dstate):
+                        m = np.array([[p["A"][d, n], p["B"][b, n, t] * p["u"][b, d, t]], [0.0, 0.0]])
+                        e = expm(m * step[b, d, t])
+                        h[n] = e[0, 0] * h[n] + e[0, 1]
+                    v = float(p["C"][b, :, t] @ h) + (p["D"][d] * p["u"][b, d, t] if Df else 0.0)
+                    if zf:
+                        zz = p["z"][b, d, t]
+                        v *= zz / (1.0 + math.exp(-zz))
+                    _close(y[b, d, t], v, 1e-11, 1e-13, "zoh van loan y b=%d d=%d t=%d" % (b, d, t))
+                _close(last[b, d], h, 1e-11, 1e-13, "zoh van loan state b=%d d=%d" % (b, d))
+
+
+def zoh_fixed_point(o):
+    dim, dstate, seqlen = 3, 4, 400
+    A = -np.array([[0.5, 1.0, 2.0, 3.0], [1.0, 1.5, 2.5, 4.0], [0.7, 0.9, 1.1, 5.0]])
+    Bc = np.array([1.0, -2.0, 0.5, 3.0])
+    for dt in (0.25, 1.0, 3.0):
+        u = np.full((1, dim, seqlen), 1.5)
+        delta = np.full((1, dim, seqlen), dt)
+        B = np.repeat(Bc[None, :, None], seqlen, axis=2)
+        C = np.ones((1, dstate, seqlen))
+        _, last = o.scan_f64(u, delta, A, B, C, zoh=True)
+        want = -Bc[None, :] * 1.5 / A
+        _close(last[0], want, 1e-12, 1e-14, "zoh fixed point dt=%g" % dt)
+
+
+def zoh_limits(o):
+    rng = _rng(31)
+    p = _random_problem(rng, 2, 3, 4, 9)
+    p["A"][:, 0] = 0.0
+    ys, ls = o.scan_f64(softplus=True, zoh=False, **dict(p, A=p["A"][:, :1], B=p["B"][:, :1], C=p["C"][:, :1]))
+    yz, lz = o.scan_f64(softplus=True, zoh=True, **dict(p, A=p["A"][:, :1], B=p["B"][:, :1], C=p["C"][:, :1]))
+    _close(yz, ys, 1e-15, 1e-15, "zoh at A = 0 is the Delta*B rule (y)")
+    _close(lz, ls, 1e-15, 1e-15, "zoh at A = 0 is the Delta*B rule (state)")
+    for dt in (1e-3, 0.1, 1.0):
+        for a in (-1e-12, -1e-6, 1e-6, -1e-3):
+            x = dt * a
+            series = dt * (1.0 + x / 2.0 + x * x / 6.0 + x ** 3 / 24.0)
+            _close(o.zoh_b_f64(dt, a), series, 1e-14, 0.0, "zoh factor series dt=%g a=%g" % (dt, a))
+        assert o.zoh_b_f64(dt, 0.0) == dt, "zoh factor at a = 0"
+        for a in (-0.5, -4.0, 2.0):
+            _close(o.zoh_b_f64(dt, a), (math.exp(dt * a) - 1.0) / a, 1e-13, 0.0, "zoh factor dt=%g a=%g" % (dt, a))
+
+
+def zoh_decode(o):
+    rng = _rng(32)
+    p = _random_problem(rng, 3, 5, 4, 1)
+    p["A"][1, 2] = 0.0
+    y_scan, last_scan = o.scan_f64(softplus=True, zoh=True, **p)
+    st = p["h0"].copy()
+    y_dec = o.state_update_f64(st, p["u"][..., 0], p["delta"][..., 0], p["A"], p["B"][..., 0], p["C"][..., 0],
+                               p["D"], p["z"][..., 0], p["delta_bias"], softplus=True, zoh=True)
+    _close(y_dec, y_scan[..., 0], 1e-15, 1e-15, "zoh decode y")
+    _close(st, last_scan, 1e-15, 1e-15, "zoh decode state")
+
+
 ALL = [worked_examples, lti_closed_form, bruteforce, single_step, persistence, forgetting, split_carry, linearity,
        softplus_silu, decode_is_scan, channel_subset, conv_library, conv_taps, conv_causality, conv_split_carry,
-       bwd_finite_diff, bwd_autograd]
+       bwd_finite_diff, bwd_autograd, zoh_van_loan, zoh_fixed_point, zoh_limits, zoh_decode]

@@ -44,6 +44,12 @@ MUTANTS = [
     ("bwd_dz_sign", "(1.0 + zt * (1.0 - sg))", "(1.0 - zt * (1.0 - sg))"),
     ("bwd_dB_missing_step", "+= lam[n] * step * ut;", "+= lam[n] * ut;"),
     ("bwd_dC_uses_hprev", "g * hs[(t + 1) * dstate + n];", "g * hs[t * dstate + n];"),
+    ("zoh_missing_divide", "expm1(delta * a) / a : delta", "expm1(delta * a) : delta"),
+    ("zoh_exp_not_expm1", "expm1(delta * a) / a : delta", "exp(delta * a) / a : delta"),
+    ("zoh_zero_limit", "expm1(delta * a) / a : delta", "expm1(delta * a) / a : 0.0"),
+    ("zoh_ignored", "      if (zoh) bbar_u = ", "      if (0) bbar_u = "),
+    ("zoh_sign", "expm1(delta * a) / a : delta", "expm1(-delta * a) / a : delta"),
+    ("zoh_without_B", "oracle_zoh_b(delta, A_row[n]) * B_b[n * seqlen + l] * ul", "oracle_zoh_b(delta, A_row[n]) * ul"),
     ("bwd_dD_after_gate", "        partD[ch] += g * ut;", "        partD[ch] += dy[ch * seqlen + t] * ut;"),
 ]
 
