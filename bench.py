@@ -15,6 +15,7 @@ the timed region.  Prints one JSON line:
                dim 5120, dstate 16), per step
   conv_scan    ssm_conv_scan_fwd (causal conv of width 4 fused in front of the
                scan) on the same workload
+  zoh          ssm_scan_fwd_ex with exact zero-order hold for B, same workload
   backward     ssm_scan_bwd (every gradient) on the same workload
 
 Algorithmic bytes: read u, delta, z and write y once (4 x io bytes per
@@ -181,6 +182,32 @@ def bench_conv_scan(dev, x, t, steps, warmup):
                 algorithmic_gbs=round(nbytes / (avg_ms * 1e-3) / 1e9, 1), algorithmic_bytes=nbytes)
 
 
+ZOH_SLOTS_PER_ELEM_STATE = 14  # the 6 of the Delta*B rule + u/A, the series (3 FMAs, 1 mul), e*iu - iu, select (2)
+
+
+def bench_zoh(dev, x, t, steps, warmup):
+    """ssm_scan_fwd_ex with exact zero-order hold for B on the same workload."""
+    import torch
+    from selective_state_space_65_amd import binding
+    b, d, n, l = x.shape
+    y = torch.empty_like(t["u"])
+    last = torch.empty((b, d, n), dtype=torch.float32, device=dev)
+
+    def fn():
+        binding.scan_fwd_ex(t["u"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"], delta_bias=t["delta_bias"],
+                            delta_softplus=x.softplus, disc="zoh", out=y, last_state=last)
+
+    wall_ms, avg_ms, med_ms = time_calls(fn, steps, warmup)
+    io_bytes = 2 if x.io == "bf16" else 4
+    nbytes = algorithmic_bytes(b, d, n, l, io_bytes, has_z=x.z is not None)
+    slots = ZOH_SLOTS_PER_ELEM_STATE * b * d * l * n
+    return dict(workload="exact zero-order hold for B (ssm_scan_fwd_ex), same shape and flags",
+                us_per_call=round(avg_ms * 1e3, 2), us_median=round(med_ms * 1e3, 2),
+                algorithmic_gbs=round(nbytes / (avg_ms * 1e-3) / 1e9, 1),
+                alu_frac=round(slots / (avg_ms * 1e-3) / LANE_SLOTS_PEAK, 4),
+                lane_slots_per_elem_state=ZOH_SLOTS_PER_ELEM_STATE)
+
+
 BWD_SLOTS_PER_ELEM_STATE = 20  # 6 for the checkpointing forward + 14 for the adjoint walk
 
 
@@ -220,6 +247,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-conv", action="store_true", help="skip the fused conv + scan line")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward line")
+    ap.add_argument("--no-zoh", action="store_true", help="skip the zero-order-hold line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy 1 GiB three times (reference kernel for rocprofv3 FETCH_SIZE/WRITE_SIZE)")
     args = ap.parse_args()
@@ -288,6 +316,8 @@ def main():
         out["decode"] = bench_decode(dev, 50, 5)
     if not args.no_conv:
         out["conv_scan"] = bench_conv_scan(dev, x, t, args.steps, args.warmup)
+    if not args.no_zoh:
+        out["zoh"] = bench_zoh(dev, x, t, args.steps, args.warmup)
     if not args.no_backward:
         bw = bench_backward(dev, x, t, max(3, args.steps // 4), 2)
         bw["vs_forward"] = round(bw["us_per_call"] / (avg_ms * 1e3), 2)

@@ -11,6 +11,9 @@
  *   ssm_scan_bwd       training: every gradient of a scalar loss through
  *                      ssm_scan_fwd, given dL/dy (and optionally dL/dh_L).
  *
+ * ssm_scan_fwd_ex and ssm_state_update_ex are the first two with a choice of
+ * how B is discretized (Delta * B, or exact zero-order hold).
+ *
  * What is computed (for every batch row b and channel d independently):
  *
  *   Delta_l = softplus(delta[b,d,l] + bias[d])   (or delta + bias, flag off)
@@ -63,7 +66,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 3
+#define SSM_ABI_VERSION 4
 
 struct ihipStream_t; /* the same incomplete type as HIP's hipStream_t */
 
@@ -214,6 +217,45 @@ ssm_status_t ssm_scan_bwd(int64_t batch, int64_t dim, int64_t dstate, int64_t se
                           const float* h0, const void* dy, const float* dlast, void* du, void* ddelta,
                           float* dA, float* dB, float* dC, float* dD, void* dz, float* ddelta_bias, float* dh0,
                           struct ihipStream_t* stream);
+
+/* How B is discretized (the _ex entry points).  Abar = exp(Delta * A) in both. */
+typedef enum {
+  SSM_DISC_DELTA_B = 0, /* Bbar * u = Delta * B * u (what every other entry point computes) */
+  SSM_DISC_ZOH = 1      /* exact zero-order hold: Bbar * u = (exp(Delta * A) - 1) / A * B * u,
+                           Delta * B * u where A = 0                                          */
+} ssm_disc_t;
+
+/*
+ * ssm_scan_fwd_ex -- ssm_scan_fwd with a choice of discretization for B.
+ * The Chinese explainer's discretization stage (1a/1b) turns the continuous
+ * parameters into discrete ones by a fixed rule and names zero-order hold as
+ * one such rule (its formulas did not survive).  Holding u constant over a
+ * step of length Delta and solving dh/dt = A h + B u exactly gives, per state
+ * of a diagonal A, Abar = exp(Delta A) and Bbar = (exp(Delta A) - 1) / A * B
+ * (SSM_DISC_ZOH); SSM_DISC_DELTA_B keeps Abar and takes Bbar = Delta * B, the
+ * form every other entry point uses.  Arguments, layouts, ownership and
+ * errors are those of ssm_scan_fwd, plus SSM_ERR_UNSUPPORTED for a disc value
+ * outside ssm_disc_t.  With SSM_DISC_DELTA_B the result is bitwise that of
+ * ssm_scan_fwd.  fp32 evaluation: where |Delta A| < 1/16 the zero-order-hold
+ * factor is taken from its series (exp(x) - 1 cancels there), elsewhere from
+ * exp(Delta A) - 1; both are within about 1e-6 relative of the exact factor.
+ */
+ssm_status_t ssm_scan_fwd_ex(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, ssm_dtype_t io,
+                             ssm_disc_t disc, const void* u, const void* delta, const float* A, const void* B,
+                             const void* C, const float* D, const void* z, const float* delta_bias,
+                             int softplus_flag, const float* h0, void* y, float* last_state,
+                             struct ihipStream_t* stream);
+
+/*
+ * ssm_state_update_ex -- ssm_state_update with a choice of discretization for
+ * B (as ssm_scan_fwd_ex).  Equals ssm_scan_fwd_ex with seqlen = 1 and
+ * h0 = last_state = state.  Errors as ssm_state_update, plus
+ * SSM_ERR_UNSUPPORTED for a disc value outside ssm_disc_t.
+ */
+ssm_status_t ssm_state_update_ex(int64_t batch, int64_t dim, int64_t dstate, ssm_dtype_t io, ssm_disc_t disc,
+                                 float* state, const void* u, const void* delta, const float* A, const void* B,
+                                 const void* C, const float* D, const void* z, const float* delta_bias,
+                                 int softplus_flag, void* y, struct ihipStream_t* stream);
 
 /* Kernel paths of ssm_scan_fwd (reported by ssm_scan_fwd_plan). */
 typedef enum {

@@ -17,6 +17,9 @@ SSM_F32 = 0
 SSM_BF16 = 1
 SSM_OK = 0
 
+# ssm_disc_t: how B is discretized by the _ex entry points.
+DISC_CODES = {"delta_b": 0, "zoh": 1}
+
 STATUS_NAMES = {
     0: "SSM_OK",
     1: "SSM_ERR_NULL",
@@ -36,6 +39,8 @@ _I = ctypes.c_int
 SIGNATURES = {
     "ssm_scan_fwd": (_I, [_I64, _I64, _I64, _I64, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P]),
     "ssm_state_update": (_I, [_I64, _I64, _I64, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P]),
+    "ssm_scan_fwd_ex": (_I, [_I64, _I64, _I64, _I64, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P]),
+    "ssm_state_update_ex": (_I, [_I64, _I64, _I64, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P]),
     "ssm_conv_scan_fwd": (_I, [_I64, _I64, _I64, _I64, _I64, _I, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _I, _P,
                                _P, _P, _P, _P]),
     "ssm_scan_bwd": (_I, [_I64, _I64, _I64, _I64, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P,
@@ -142,7 +147,7 @@ def scan_plan(batch, dim, dstate, seqlen, io_dtype, with_path=False):
 
 def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=False, h0=None,
              out=None, last_state=None, return_last_state=True, stream=None):
-    """Selective scan over the sequence; returns (y, last_state).
+    """Selective scan over the sequence (ssm_scan_fwd); returns (y, last_state).
 
     u, delta, z: (batch, dim, seqlen); B, C: (batch, dstate, seqlen), all in
     one io dtype (float32 or bfloat16).  A: (dim, dstate), D and delta_bias:
@@ -150,6 +155,25 @@ def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=
     last_state is float32 (None when return_last_state is False).  h0 may be
     the same tensor as last_state to carry the state in place.
     """
+    return _scan_fwd(None, u, delta, A, B, C, D, z, delta_bias, delta_softplus, h0, out, last_state,
+                     return_last_state, stream)
+
+
+def scan_fwd_ex(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=False, h0=None, disc="zoh",
+                out=None, last_state=None, return_last_state=True, stream=None):
+    """scan_fwd with a choice of discretization for B (ssm_scan_fwd_ex).
+
+    disc: "zoh" (exact zero-order hold, Bbar = (exp(Delta A) - 1) / A * B) or
+    "delta_b" (Bbar = Delta * B, as scan_fwd).  Everything else as scan_fwd.
+    """
+    if disc not in DISC_CODES:
+        raise ValueError("disc must be one of %s" % sorted(DISC_CODES))
+    return _scan_fwd(DISC_CODES[disc], u, delta, A, B, C, D, z, delta_bias, delta_softplus, h0, out, last_state,
+                     return_last_state, stream)
+
+
+def _scan_fwd(disc, u, delta, A, B, C, D, z, delta_bias, delta_softplus, h0, out, last_state, return_last_state,
+              stream):
     import torch
     if u.dim() != 3:
         raise ValueError("u must be (batch, dim, seqlen)")
@@ -179,10 +203,12 @@ def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=
     elif last_state is not None:
         _need(last_state, "last_state", (batch, dim, dstate), torch.float32, dev)
     lib = load_library()
-    st = lib.ssm_scan_fwd(batch, dim, dstate, seqlen, _io_code(io), _ptr(u), _ptr(delta), _ptr(A), _ptr(B),
-                          _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias), 1 if delta_softplus else 0, _ptr(h0),
-                          _ptr(out), _ptr(last_state), _stream(dev, stream))
-    _check("ssm_scan_fwd", st)
+    tail = (_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+            1 if delta_softplus else 0, _ptr(h0), _ptr(out), _ptr(last_state), _stream(dev, stream))
+    if disc is None:
+        _check("ssm_scan_fwd", lib.ssm_scan_fwd(batch, dim, dstate, seqlen, _io_code(io), *tail))
+    else:
+        _check("ssm_scan_fwd_ex", lib.ssm_scan_fwd_ex(batch, dim, dstate, seqlen, _io_code(io), disc, *tail))
     return out, last_state
 
 
@@ -298,10 +324,22 @@ def scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, delta_softp
 
 def state_update(state, u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=False, out=None,
                  stream=None):
-    """One decode step, updating state (batch, dim, dstate) float32 in place; returns y (batch, dim).
+    """One decode step (ssm_state_update), updating state (batch, dim, dstate) float32 in place; returns y (batch, dim).
 
     u, delta, z: (batch, dim); B, C: (batch, dstate) in the io dtype.
     """
+    return _state_update(None, state, u, delta, A, B, C, D, z, delta_bias, delta_softplus, out, stream)
+
+
+def state_update_ex(state, u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=False, disc="zoh",
+                    out=None, stream=None):
+    """state_update with a choice of discretization for B (ssm_state_update_ex); disc as scan_fwd_ex."""
+    if disc not in DISC_CODES:
+        raise ValueError("disc must be one of %s" % sorted(DISC_CODES))
+    return _state_update(DISC_CODES[disc], state, u, delta, A, B, C, D, z, delta_bias, delta_softplus, out, stream)
+
+
+def _state_update(disc, state, u, delta, A, B, C, D, z, delta_bias, delta_softplus, out, stream):
     import torch
     if state.dim() != 3:
         raise ValueError("state must be (batch, dim, dstate)")
@@ -325,8 +363,10 @@ def state_update(state, u, delta, A, B, C, D=None, z=None, delta_bias=None, delt
     else:
         _need(out, "out", (batch, dim), io, dev)
     lib = load_library()
-    st = lib.ssm_state_update(batch, dim, dstate, _io_code(io), _ptr(state), _ptr(u), _ptr(delta), _ptr(A),
-                              _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias), 1 if delta_softplus else 0,
-                              _ptr(out), _stream(dev, stream))
-    _check("ssm_state_update", st)
+    tail = (_ptr(state), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+            1 if delta_softplus else 0, _ptr(out), _stream(dev, stream))
+    if disc is None:
+        _check("ssm_state_update", lib.ssm_state_update(batch, dim, dstate, _io_code(io), *tail))
+    else:
+        _check("ssm_state_update_ex", lib.ssm_state_update_ex(batch, dim, dstate, _io_code(io), disc, *tail))
     return out

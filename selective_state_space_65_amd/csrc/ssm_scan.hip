@@ -89,6 +89,26 @@ __device__ __forceinline__ float softplus_f32(float x) {
 // silu(z) = z * sigmoid(z) = z / (1 + e^-z)
 __device__ __forceinline__ float silu_f32(float z) { return z * rcp_hw(1.0f + exp2_hw(-z * kLog2e)); }
 
+// Exact zero-order hold for B.  Holding u over a step of length Delta and
+// solving dh/dt = a h + B u exactly gives the input term (e^{Delta a} - 1)/a * u
+// per state (times B).  t = Delta a log2(e) is the exp2 argument, e = exp2(t)
+// is Abar, du = Delta u and iu = u / a.  Where |Delta a| >= 1/16 the term is
+// (e - 1) iu: the rounding of e (about 6e-8 near 1) is then at most 1e-6 of
+// e - 1.  Below that, e - 1 would cancel, and the term is
+// du (1 + x/2 + x^2/6 + x^3/24), x = Delta a, whose first dropped term is
+// under 1.3e-7 of the sum.  At a = 0 (iu infinite, the other side not taken)
+// it is exactly du.
+constexpr float kZohSeriesT = 0.0625f * kLog2e;  // |t| below this: the series
+__device__ __forceinline__ float zoh_input(float t, float e, float du, float iu) {
+  constexpr float c1 = kLn2 / 2.0f, c2 = kLn2 * kLn2 / 6.0f, c3 = kLn2 * kLn2 * kLn2 / 24.0f;
+  float q = __builtin_fmaf(t, c3, c2);
+  q = __builtin_fmaf(t, q, c1);
+  q = __builtin_fmaf(t, q, 1.0f);
+  const float series = du * q;
+  const float held = __builtin_fmaf(e, iu, -iu);
+  return __builtin_fabsf(t) < kZohSeriesT ? series : held;
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
@@ -253,6 +273,7 @@ struct ScanArgs {
   // Backward support (single-pass kernel only): when set, the state before
   // every 16th token is written here, [seqlen/16 rounded up][batch][N][dim].
   float* ckpt;
+  int zoh;  // B discretized by exact zero-order hold instead of Delta * B
 };
 
 constexpr int kCkptTokens = 16;  // tokens between backward checkpoints (one backward tile)
@@ -294,7 +315,8 @@ __device__ __forceinline__ WaveCoord decompose(int64_t wave, const ScanArgs& a) 
 // Per-channel constants loaded once per wave.
 template <int N>
 struct Channel {
-  float A2[N];  // A * log2(e): Abar = exp2(Delta * A2)
+  float A2[N];    // A * log2(e): Abar = exp2(Delta * A2)
+  float inva[N];  // 1 / A (zero-order hold only)
   float Dd;
   float bias;
 };
@@ -302,7 +324,11 @@ struct Channel {
 template <int N>
 __device__ __forceinline__ void load_channel(const ScanArgs& a, int64_t d, Channel<N>& c) {
 #pragma unroll
-  for (int n = 0; n < N; ++n) c.A2[n] = (n < a.dstate) ? a.A[d * a.dstate + n] * kLog2e : 0.0f;
+  for (int n = 0; n < N; ++n) {
+    const float an = (n < a.dstate) ? a.A[d * a.dstate + n] : 0.0f;
+    c.A2[n] = an * kLog2e;
+    c.inva[n] = 1.0f / an;
+  }
   c.Dd = a.D ? a.D[d] : 0.0f;
   c.bias = a.bias ? a.bias[d] : 0.0f;
 }
@@ -346,10 +372,16 @@ struct BCPipe {
 
   // One chunk of kChunk tokens for all NST states: h advances, and (kEmit)
   // y accumulates C.h.  has_next / next_l_bytes name the following chunk.
-  template <int P0>
+  // xl is Delta * u, or u itself with kZoh (then inva holds 1 / A).
+  template <int P0, bool kZoh>
   __device__ __forceinline__ void chunk(uint32_t l_bytes, bool has_next, uint32_t next_l_bytes,
-                                        const float A2[NST], const float dl[kChunk], const float xl[kChunk],
-                                        float h[NST], float yv[kChunk]) {
+                                        const float A2[NST], const float inva[NST], const float dl[kChunk],
+                                        const float xl[kChunk], float h[NST], float yv[kChunk]) {
+    float du[kChunk];
+    if constexpr (kZoh) {
+#pragma unroll
+      for (int t = 0; t < kChunk; ++t) du[t] = dl[t] * xl[t];
+    }
 #pragma unroll
     for (int gi = 0; gi < NG; ++gi) {
       const int cur = (P0 + gi) & 1;
@@ -368,8 +400,10 @@ struct BCPipe {
         float hn = h[n];
 #pragma unroll
         for (int t = 0; t < kChunk; ++t) {
-          float abar = exp2_hw(A2[n] * dl[t]);
-          hn = __builtin_fmaf(abar, hn, Uni<IoT>::elem(Bx[cur][j], t) * xl[t]);
+          const float ta = A2[n] * dl[t];
+          const float abar = exp2_hw(ta);
+          const float bu = kZoh ? zoh_input(ta, abar, du[t], xl[t] * inva[n]) : xl[t];
+          hn = __builtin_fmaf(abar, hn, Uni<IoT>::elem(Bx[cur][j], t) * bu);
           if (kEmit) yv[t] = __builtin_fmaf(Uni<IoT>::elem(Cx[cur][j], t), hn, yv[t]);
         }
         h[n] = hn;
@@ -388,16 +422,20 @@ struct BCPipe {
 };
 
 // One token with scalar loads (tails, unaligned shapes).
-template <typename IoT, int N, bool kEmit>
+// uv is u; the input term is Delta * u, or its zero-order-hold form (kZoh).
+template <typename IoT, int N, bool kEmit, bool kZoh>
 __device__ __forceinline__ float token_states(const IoT* __restrict__ Bb, const IoT* __restrict__ Cb, int64_t L,
-                                              int64_t dstate, const float A2[N], float dl, float xl, float h[N]) {
+                                              int64_t dstate, const Channel<N>& c, float dl, float uv, float h[N]) {
   float yv = 0.0f;
+  const float xl = dl * uv;
 #pragma unroll
   for (int n = 0; n < N; ++n) {
     if (n < dstate) {
-      float abar = exp2_hw(A2[n] * dl);
+      const float ta = c.A2[n] * dl;
+      const float abar = exp2_hw(ta);
+      const float bu = kZoh ? zoh_input(ta, abar, xl, uv * c.inva[n]) : xl;
       float bv = Io<IoT>::load1(Bb + n * L);
-      h[n] = __builtin_fmaf(abar, h[n], bv * xl);
+      h[n] = __builtin_fmaf(abar, h[n], bv * bu);
       if (kEmit) yv = __builtin_fmaf(Io<IoT>::load1(Cb + n * L), h[n], yv);
     }
   }
@@ -479,7 +517,7 @@ struct Line {
 
 // Scan [l0, l1) of one lane's channel row in line tiles (l0 line-aligned,
 // l1 - l0 a multiple of kChunk): h advances; with kEmit, y is written.
-template <typename IoT, int N, bool kEmit, bool kZ, bool kSoftplus>
+template <typename IoT, int N, bool kEmit, bool kZ, bool kSoftplus, bool kZoh>
 __device__ __forceinline__ void scan_lines(const IoT* ur, const IoT* dr, const IoT* zr, IoT* yr, bool active,
                                            const IoT* Bb, const IoT* Cb, uint32_t row_bytes, int64_t l0,
                                            int64_t l1, const Channel<N>& c, float h[N], float* dsum) {
@@ -509,7 +547,7 @@ __device__ __forceinline__ void scan_lines(const IoT* ur, const IoT* dr, const I
 #pragma unroll
           for (int t = 0; t < kChunk; ++t) {
             dl[t] = discretize_delta<kSoftplus>(dl[t], c.bias);
-            xl[t] = dl[t] * LI::elem(uw, t);
+            xl[t] = kZoh ? LI::elem(uw, t) : dl[t] * LI::elem(uw, t);
             yv[t] = 0.0f;
             if (!kEmit) *dsum += dl[t];
           }
@@ -519,9 +557,9 @@ __device__ __forceinline__ void scan_lines(const IoT* ur, const IoT* dr, const I
           // (The branch folds away once the chunk loop is unrolled.)
           const uint32_t lb = (uint32_t)(lt * sizeof(IoT)), nb = (uint32_t)((lt + kChunk) * sizeof(IoT));
           if (((k * BCPipe<IoT, N, kEmit>::NG) & 1) == 0)
-            bc.template chunk<0>(lb, lt + kChunk < l1, nb, c.A2, dl, xl, h, yv);
+            bc.template chunk<0, kZoh>(lb, lt + kChunk < l1, nb, c.A2, c.inva, dl, xl, h, yv);
           else
-            bc.template chunk<1>(lb, lt + kChunk < l1, nb, c.A2, dl, xl, h, yv);
+            bc.template chunk<1, kZoh>(lb, lt + kChunk < l1, nb, c.A2, c.inva, dl, xl, h, yv);
           if constexpr (kEmit) {
 #pragma unroll
             for (int t = 0; t < kChunk; ++t)
@@ -549,7 +587,7 @@ __device__ __forceinline__ void scan_lines(const IoT* ur, const IoT* dr, const I
 //         every chunk is a full vector chunk with B/C in SGPRs.  Otherwise
 //         (N = 16 then bounds a runtime dstate) every token goes through the
 //         scalar path.
-template <typename IoT, int N, bool kZ, bool kSoftplus, bool kVec>
+template <typename IoT, int N, bool kZ, bool kSoftplus, bool kVec, bool kZoh>
 __global__ __launch_bounds__(kBlockThreads) void scan_kernel(ScanArgs a, int64_t total_waves) {
   const int64_t wave = wave_index();
   if (wave >= total_waves) return;
@@ -583,12 +621,12 @@ __global__ __launch_bounds__(kBlockThreads) void scan_kernel(ScanArgs a, int64_t
 
   int64_t l = l0;
   if constexpr (kVec) {
-    scan_lines<IoT, N, true, kZ, kSoftplus>(ur, dr, zr, yr, active, Bb, Cb, row_bytes, l, l1, c, h, nullptr);
+    scan_lines<IoT, N, true, kZ, kSoftplus, kZoh>(ur, dr, zr, yr, active, Bb, Cb, row_bytes, l, l1, c, h, nullptr);
   } else {
     for (; l < l1; ++l) {
       float uv = Io<IoT>::load1(ur + l);
       float dl = discretize_delta<kSoftplus>(Io<IoT>::load1(dr + l), c.bias);
-      float acc = token_states<IoT, N, true>(Bb + l, Cb + l, L, a.dstate, c.A2, dl, dl * uv, h);
+      float acc = token_states<IoT, N, true, kZoh>(Bb + l, Cb + l, L, a.dstate, c, dl, uv, h);
       float v = epilogue<kZ>(acc, c.Dd, uv, kZ ? Io<IoT>::load1(zr + l) : 0.0f);
       if (active) Io<IoT>::store1(yr + l, v);
     }
@@ -665,7 +703,7 @@ struct Piece {
   }
 };
 
-template <typename IoT, int N, int S, int SA, bool kZ, bool kSoftplus, bool kConv>
+template <typename IoT, int N, int S, int SA, bool kZ, bool kSoftplus, bool kConv, bool kZoh>
 __global__ __launch_bounds__(64 * S) void scan_split_kernel(ScanArgs a) {
   using C = Split<IoT, N, S, SA>;
   constexpr int TS = C::TS;
@@ -689,11 +727,13 @@ __global__ __launch_bounds__(64 * S) void scan_split_kernel(ScanArgs a) {
   const int64_t L = a.seqlen;
   const int64_t ch = b * a.dim + d;
 
-  float A2[NS], h[NS];
+  float A2[NS], inva[NS], h[NS];
 #pragma unroll
   for (int j = 0; j < NS; ++j) {
     const int n = w * NS + j;
-    A2[j] = a.A[d * N + n] * kLog2e;
+    const float an = a.A[d * N + n];
+    A2[j] = an * kLog2e;
+    inva[j] = 1.0f / an;
     h[j] = a.h0 ? a.h0[ch * N + n] : 0.0f;
   }
   const float Dd = a.D ? a.D[d] : 0.0f;
@@ -835,13 +875,16 @@ __global__ __launch_bounds__(64 * S) void scan_split_kernel(ScanArgs a) {
       if (uo && active) PI::store(uo + lt + w * TS, au);
     }
   };
-  // Phase A: widen this wave's tokens of a tile and publish (Delta, x).
+  // Phase A: widen this wave's tokens of a tile and publish (Delta, x):
+  // x = Delta * u, or u itself under zero-order hold.
   auto widen = [&](int buf, const uint32_t (&qu)[PW], const uint32_t (&qd)[PW]) {
 #pragma unroll
     for (int t = 0; t < TS; t += 2) {
       float d0 = discretize_delta<kSoftplus>(LI::elem(qd, t), bias);
       float d1 = discretize_delta<kSoftplus>(LI::elem(qd, t + 1), bias);
-      dx[buf][((w * TS + t) / 2) * 64 + lane] = make_float4(d0, d0 * LI::elem(qu, t), d1, d1 * LI::elem(qu, t + 1));
+      const float u0 = LI::elem(qu, t), u1 = LI::elem(qu, t + 1);
+      dx[buf][((w * TS + t) / 2) * 64 + lane] =
+          kZoh ? make_float4(d0, u0, d1, u1) : make_float4(d0, d0 * u0, d1, d1 * u1);
     }
   };
   // Phase C: sum the partials in wave order, gate, store the tile at lc.
@@ -955,14 +998,20 @@ __global__ __launch_bounds__(64 * S) void scan_split_kernel(ScanArgs a) {
           for (int j = 0; j < NS; ++j)
             if (active) a.ckpt[((c * a.batch + b) * N + w * NS + j) * a.dim + d] = h[j];
         }
-        float yv[kChunk];
+        float yv[kChunk], du[kChunk];
+        if constexpr (kZoh) {
+#pragma unroll
+          for (int t = 0; t < kChunk; ++t) du[t] = dl[k][t] * xl[k][t];
+        }
 #pragma unroll
         for (int j = 0; j < NS; ++j) {
           float hn = h[j];
 #pragma unroll
           for (int t = 0; t < kChunk; ++t) {
-            float abar = exp2_hw(A2[j] * dl[k][t]);
-            hn = __builtin_fmaf(abar, hn, U::elem(Bx[s][j], t) * xl[k][t]);
+            const float ta = A2[j] * dl[k][t];
+            const float abar = exp2_hw(ta);
+            const float bu = kZoh ? zoh_input(ta, abar, du[t], xl[k][t] * inva[j]) : xl[k][t];
+            hn = __builtin_fmaf(abar, hn, U::elem(Bx[s][j], t) * bu);
             const float cv = U::elem(Cx[s][j], t);
             yv[t] = (j == 0) ? cv * hn : __builtin_fmaf(cv, hn, yv[t]);
           }
@@ -1411,7 +1460,7 @@ __global__ __launch_bounds__(kBlockThreads) void bwd_reduce_kernel(BwdArgs a, in
 
 // Launch 1: every segment but the last scans from a zero state and records
 // (sum of Delta, end state).  The segment's decay is a = exp(A * sum Delta).
-template <typename IoT, int N, bool kSoftplus, bool kVec>
+template <typename IoT, int N, bool kSoftplus, bool kVec, bool kZoh>
 __global__ __launch_bounds__(kBlockThreads) void aggregate_kernel(ScanArgs a, int64_t total_waves) {
   const int64_t wave = wave_index();
   if (wave >= total_waves) return;
@@ -1440,14 +1489,14 @@ __global__ __launch_bounds__(kBlockThreads) void aggregate_kernel(ScanArgs a, in
 
   int64_t l = l0;
   if constexpr (kVec) {
-    scan_lines<IoT, N, false, false, kSoftplus>(ur, dr, nullptr, nullptr, active, Bb, nullptr, row_bytes, l, l1, c, h,
-                                                &dsum);
+    scan_lines<IoT, N, false, false, kSoftplus, kZoh>(ur, dr, nullptr, nullptr, active, Bb, nullptr, row_bytes, l, l1,
+                                                      c, h, &dsum);
   } else {
     for (; l < l1; ++l) {
       float uv = Io<IoT>::load1(ur + l);
       float dl = discretize_delta<kSoftplus>(Io<IoT>::load1(dr + l), c.bias);
       dsum += dl;
-      token_states<IoT, N, false>(Bb + l, nullptr, L, a.dstate, c.A2, dl, dl * uv, h);
+      token_states<IoT, N, false, kZoh>(Bb + l, nullptr, L, a.dstate, c, dl, uv, h);
     }
   }
 
@@ -1509,11 +1558,12 @@ struct UpdateArgs {
   const float* bias;
   void* y;
   int64_t batch, dim, dstate;
+  int zoh;  // B discretized by exact zero-order hold instead of Delta * B
 };
 
 // N in {4, 8, 16}: N/4 lanes per channel, four states per lane.  Groups of
 // N/4 lanes are aligned inside the wave, so the shuffle stays in the group.
-template <typename IoT, int N, bool kZ, bool kSoftplus>
+template <typename IoT, int N, bool kZ, bool kSoftplus, bool kZoh>
 __global__ __launch_bounds__(kBlockThreads) void state_update_kernel(UpdateArgs a) {
   constexpr int kLanes = N / 4;
   const int64_t bd = a.batch * a.dim;
@@ -1536,8 +1586,10 @@ __global__ __launch_bounds__(kBlockThreads) void state_update_kernel(UpdateArgs 
   float acc = 0.0f;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    float abar = exp2_hw(A4[j] * kLog2e * dl);
-    h[j] = __builtin_fmaf(abar, h[j], B4[j] * xl);
+    const float ta = A4[j] * kLog2e * dl;
+    const float abar = exp2_hw(ta);
+    const float bu = kZoh ? zoh_input(ta, abar, xl, uv * (1.0f / A4[j])) : xl;
+    h[j] = __builtin_fmaf(abar, h[j], B4[j] * bu);
     acc = __builtin_fmaf(C4[j], h[j], acc);
   }
 #pragma unroll
@@ -1552,7 +1604,7 @@ __global__ __launch_bounds__(kBlockThreads) void state_update_kernel(UpdateArgs 
 }
 
 // Any dstate <= 16 and any alignment: one lane per channel, scalar loads.
-template <typename IoT, bool kZ, bool kSoftplus>
+template <typename IoT, bool kZ, bool kSoftplus, bool kZoh>
 __global__ __launch_bounds__(kBlockThreads) void state_update_generic_kernel(UpdateArgs a) {
   const int64_t bd = a.batch * a.dim;
   const int64_t ch = (int64_t)blockIdx.x * kBlockThreads + threadIdx.x;
@@ -1564,9 +1616,12 @@ __global__ __launch_bounds__(kBlockThreads) void state_update_generic_kernel(Upd
   const float xl = dl * uv;
   float acc = 0.0f;
   for (int64_t n = 0; n < a.dstate; ++n) {
-    float abar = exp2_hw(a.A[d * a.dstate + n] * kLog2e * dl);
+    const float an = a.A[d * a.dstate + n];
+    const float ta = an * kLog2e * dl;
+    const float abar = exp2_hw(ta);
+    const float bu = kZoh ? zoh_input(ta, abar, xl, uv * (1.0f / an)) : xl;
     float hn = a.state[ch * a.dstate + n];
-    hn = __builtin_fmaf(abar, hn, Io<IoT>::load1(static_cast<const IoT*>(a.B) + b * a.dstate + n) * xl);
+    hn = __builtin_fmaf(abar, hn, Io<IoT>::load1(static_cast<const IoT*>(a.B) + b * a.dstate + n) * bu);
     a.state[ch * a.dstate + n] = hn;
     acc = __builtin_fmaf(Io<IoT>::load1(static_cast<const IoT*>(a.C) + b * a.dstate + n), hn, acc);
   }
@@ -1708,14 +1763,14 @@ hipError_t get_pool(hipMemPool_t* out) {
   return hipSuccess;
 }
 
-template <typename IoT, int N, bool kZ, bool kSp, bool kVec>
+template <typename IoT, int N, bool kZ, bool kSp, bool kVec, bool kZoh>
 hipError_t launch_scan_t(const ScanArgs& a, const Plan& p, hipStream_t st) {
   int64_t waves_scan = a.batch * p.groups * p.segments;
   if (p.segments > 1) {
     int64_t waves_agg = a.batch * p.groups * (p.segments - 1);
     int64_t blocks = (waves_agg + kWavesPerBlock - 1) / kWavesPerBlock;
-    hipLaunchKernelGGL((aggregate_kernel<IoT, N, kSp, kVec>), dim3((unsigned)blocks), dim3(kBlockThreads), 0, st, a,
-                       waves_agg);
+    hipLaunchKernelGGL((aggregate_kernel<IoT, N, kSp, kVec, kZoh>), dim3((unsigned)blocks), dim3(kBlockThreads), 0, st,
+                       a, waves_agg);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     int64_t threads = a.batch * a.dim * a.dstate;
@@ -1725,39 +1780,50 @@ hipError_t launch_scan_t(const ScanArgs& a, const Plan& p, hipStream_t st) {
     if (e != hipSuccess) return e;
   }
   int64_t blocks = (waves_scan + kWavesPerBlock - 1) / kWavesPerBlock;
-  hipLaunchKernelGGL((scan_kernel<IoT, N, kZ, kSp, kVec>), dim3((unsigned)blocks), dim3(kBlockThreads), 0, st, a,
+  hipLaunchKernelGGL((scan_kernel<IoT, N, kZ, kSp, kVec, kZoh>), dim3((unsigned)blocks), dim3(kBlockThreads), 0, st, a,
                      waves_scan);
   return hipGetLastError();
 }
 
-template <typename IoT, int N, bool kVec>
-hipError_t launch_scan_f(const ScanArgs& a, const Plan& p, hipStream_t st, bool sp) {
-  if (a.z) return sp ? launch_scan_t<IoT, N, true, true, kVec>(a, p, st) : launch_scan_t<IoT, N, true, false, kVec>(a, p, st);
-  return sp ? launch_scan_t<IoT, N, false, true, kVec>(a, p, st) : launch_scan_t<IoT, N, false, false, kVec>(a, p, st);
+template <typename IoT, int N, bool kVec, bool kZoh>
+hipError_t launch_scan_z(const ScanArgs& a, const Plan& p, hipStream_t st, bool sp) {
+  if (a.z)
+    return sp ? launch_scan_t<IoT, N, true, true, kVec, kZoh>(a, p, st)
+              : launch_scan_t<IoT, N, true, false, kVec, kZoh>(a, p, st);
+  return sp ? launch_scan_t<IoT, N, false, true, kVec, kZoh>(a, p, st)
+            : launch_scan_t<IoT, N, false, false, kVec, kZoh>(a, p, st);
 }
 
-template <typename IoT, int N, int S, int SA, bool kZ, bool kSp, bool kConv>
+template <typename IoT, int N, bool kVec>
+hipError_t launch_scan_f(const ScanArgs& a, const Plan& p, hipStream_t st, bool sp) {
+  return a.zoh ? launch_scan_z<IoT, N, kVec, true>(a, p, st, sp) : launch_scan_z<IoT, N, kVec, false>(a, p, st, sp);
+}
+
+template <typename IoT, int N, int S, int SA, bool kZ, bool kSp, bool kConv, bool kZoh>
 hipError_t launch_split_t(const ScanArgs& a, const Plan& p, hipStream_t st) {
-  hipLaunchKernelGGL((scan_split_kernel<IoT, N, S, SA, kZ, kSp, kConv>), dim3((unsigned)(a.batch * p.groups)),
+  hipLaunchKernelGGL((scan_split_kernel<IoT, N, S, SA, kZ, kSp, kConv, kZoh>), dim3((unsigned)(a.batch * p.groups)),
                      dim3(64 * S), 0, st, a);
   return hipGetLastError();
 }
 
-template <typename IoT, int N, bool kConv>
+template <typename IoT, int N, bool kConv, bool kZoh>
 hipError_t launch_split(const ScanArgs& a, const Plan& p, hipStream_t st, bool sp) {
   constexpr int S = (N >= SSM_SPLIT_WAVES) ? SSM_SPLIT_WAVES : N;
   // Phases A and C run on one wave per SIMD (the first four waves).
   constexpr int SA = (S > 4) ? 4 : S;
   if (a.z)
-    return sp ? launch_split_t<IoT, N, S, SA, true, true, kConv>(a, p, st)
-              : launch_split_t<IoT, N, S, SA, true, false, kConv>(a, p, st);
-  return sp ? launch_split_t<IoT, N, S, SA, false, true, kConv>(a, p, st)
-            : launch_split_t<IoT, N, S, SA, false, false, kConv>(a, p, st);
+    return sp ? launch_split_t<IoT, N, S, SA, true, true, kConv, kZoh>(a, p, st)
+              : launch_split_t<IoT, N, S, SA, true, false, kConv, kZoh>(a, p, st);
+  return sp ? launch_split_t<IoT, N, S, SA, false, true, kConv, kZoh>(a, p, st)
+            : launch_split_t<IoT, N, S, SA, false, false, kConv, kZoh>(a, p, st);
 }
 
+// The fused conv runs with the Delta * B rule only (its entry point has no
+// discretization argument).
 template <typename IoT, int N>
 hipError_t launch_split_c(const ScanArgs& a, const Plan& p, hipStream_t st, bool sp, bool conv) {
-  return conv ? launch_split<IoT, N, true>(a, p, st, sp) : launch_split<IoT, N, false>(a, p, st, sp);
+  if (conv) return launch_split<IoT, N, true, false>(a, p, st, sp);
+  return a.zoh ? launch_split<IoT, N, false, true>(a, p, st, sp) : launch_split<IoT, N, false, false>(a, p, st, sp);
 }
 
 // The causal depthwise conv as a kernel of its own (shapes the single-pass
@@ -1845,26 +1911,34 @@ hipError_t launch_scan(const ScanArgs& a, const Plan& p, hipStream_t st, bool ve
   return launch_scan_f<IoT, 16, false>(a, p, st, sp);
 }
 
-template <typename IoT, int N, bool kZ, bool kSp>
+template <typename IoT, int N, bool kZ, bool kSp, bool kZoh>
 hipError_t launch_update_t(const UpdateArgs& a, hipStream_t st, bool generic) {
   const int64_t bd = a.batch * a.dim;
   if (generic) {
     int64_t blocks = (bd + kBlockThreads - 1) / kBlockThreads;
-    hipLaunchKernelGGL((state_update_generic_kernel<IoT, kZ, kSp>), dim3((unsigned)blocks), dim3(kBlockThreads), 0,
-                       st, a);
+    hipLaunchKernelGGL((state_update_generic_kernel<IoT, kZ, kSp, kZoh>), dim3((unsigned)blocks), dim3(kBlockThreads),
+                       0, st, a);
   } else {
     int64_t threads = bd * (N / 4);
     int64_t blocks = (threads + kBlockThreads - 1) / kBlockThreads;
-    hipLaunchKernelGGL((state_update_kernel<IoT, N, kZ, kSp>), dim3((unsigned)blocks), dim3(kBlockThreads), 0, st,
-                       a);
+    hipLaunchKernelGGL((state_update_kernel<IoT, N, kZ, kSp, kZoh>), dim3((unsigned)blocks), dim3(kBlockThreads), 0,
+                       st, a);
   }
   return hipGetLastError();
 }
 
+template <typename IoT, int N, bool kZoh>
+hipError_t launch_update_z(const UpdateArgs& a, hipStream_t st, bool generic, bool sp) {
+  if (a.z)
+    return sp ? launch_update_t<IoT, N, true, true, kZoh>(a, st, generic)
+              : launch_update_t<IoT, N, true, false, kZoh>(a, st, generic);
+  return sp ? launch_update_t<IoT, N, false, true, kZoh>(a, st, generic)
+            : launch_update_t<IoT, N, false, false, kZoh>(a, st, generic);
+}
+
 template <typename IoT, int N>
 hipError_t launch_update_n(const UpdateArgs& a, hipStream_t st, bool generic, bool sp) {
-  if (a.z) return sp ? launch_update_t<IoT, N, true, true>(a, st, generic) : launch_update_t<IoT, N, true, false>(a, st, generic);
-  return sp ? launch_update_t<IoT, N, false, true>(a, st, generic) : launch_update_t<IoT, N, false, false>(a, st, generic);
+  return a.zoh ? launch_update_z<IoT, N, true>(a, st, generic, sp) : launch_update_z<IoT, N, false>(a, st, generic, sp);
 }
 
 template <typename IoT>
@@ -1943,6 +2017,7 @@ ScanArgs scan_args(const Shape&, int64_t batch, int64_t dim, int64_t dstate, int
   a.groups = 0; a.segments = 0; a.seg_len = 0;
   a.conv_w = nullptr; a.conv_b = nullptr; a.x_prev = nullptr; a.u_out = nullptr; a.conv_width = 1; a.conv_silu = 0;
   a.ckpt = nullptr;
+  a.zoh = 0;
   return a;
 }
 
@@ -2012,19 +2087,30 @@ ssm_status_t ssm_scan_fwd_plan(int64_t batch, int64_t dim, int64_t dstate, int64
   return SSM_OK;
 }
 
-ssm_status_t ssm_scan_fwd(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, ssm_dtype_t io, const void* u,
-                          const void* delta, const float* A, const void* B, const void* C, const float* D,
-                          const void* z, const float* delta_bias, int softplus_flag, const float* h0, void* y,
-                          float* last_state, struct ihipStream_t* stream) {
+ssm_status_t ssm_scan_fwd_ex(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, ssm_dtype_t io,
+                             ssm_disc_t disc, const void* u, const void* delta, const float* A, const void* B,
+                             const void* C, const float* D, const void* z, const float* delta_bias,
+                             int softplus_flag, const float* h0, void* y, float* last_state,
+                             struct ihipStream_t* stream) {
   Shape sh;
   ssm_status_t st = shape_of(batch, dim, dstate, seqlen, io, &sh);
   if (st != SSM_OK) return st;
   if (!u || !delta || !A || !B || !C || !y) return SSM_ERR_NULL;
   st = check_scan_buffers(sh, dim, io, u, delta, A, B, C, D, z, delta_bias, h0, y, last_state, nullptr, 0, nullptr);
   if (st != SSM_OK) return st;
+  if (disc != SSM_DISC_DELTA_B && disc != SSM_DISC_ZOH) return SSM_ERR_UNSUPPORTED;
   ScanArgs a = scan_args(sh, batch, dim, dstate, seqlen, io, u, delta, A, B, C, D, z, delta_bias, h0, y, last_state);
+  a.zoh = disc == SSM_DISC_ZOH;
   return run_scan(a, sh, io, vec_rows(sh, dstate, seqlen, io, u, delta, B, C, z, y), softplus_flag != 0, false,
                   reinterpret_cast<hipStream_t>(stream));
+}
+
+ssm_status_t ssm_scan_fwd(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, ssm_dtype_t io, const void* u,
+                          const void* delta, const float* A, const void* B, const void* C, const float* D,
+                          const void* z, const float* delta_bias, int softplus_flag, const float* h0, void* y,
+                          float* last_state, struct ihipStream_t* stream) {
+  return ssm_scan_fwd_ex(batch, dim, dstate, seqlen, io, SSM_DISC_DELTA_B, u, delta, A, B, C, D, z, delta_bias,
+                         softplus_flag, h0, y, last_state, stream);
 }
 
 ssm_status_t ssm_conv_scan_fwd(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int64_t conv_width,
@@ -2175,10 +2261,10 @@ ssm_status_t ssm_scan_bwd(int64_t batch, int64_t dim, int64_t dstate, int64_t se
   return SSM_OK;
 }
 
-ssm_status_t ssm_state_update(int64_t batch, int64_t dim, int64_t dstate, ssm_dtype_t io, float* state, const void* u,
-                              const void* delta, const float* A, const void* B, const void* C, const float* D,
-                              const void* z, const float* delta_bias, int softplus_flag, void* y,
-                              struct ihipStream_t* stream) {
+ssm_status_t ssm_state_update_ex(int64_t batch, int64_t dim, int64_t dstate, ssm_dtype_t io, ssm_disc_t disc,
+                                 float* state, const void* u, const void* delta, const float* A, const void* B,
+                                 const void* C, const float* D, const void* z, const float* delta_bias,
+                                 int softplus_flag, void* y, struct ihipStream_t* stream) {
   Shape sh;
   ssm_status_t st = shape_of(batch, dim, dstate, 1, io, &sh);
   if (st != SSM_OK) return st;
@@ -2203,9 +2289,10 @@ ssm_status_t ssm_state_update(int64_t batch, int64_t dim, int64_t dstate, ssm_dt
     if (overlap(ry, r) || overlap(rs, r)) return SSM_ERR_ALIAS;
   }
 
+  if (disc != SSM_DISC_DELTA_B && disc != SSM_DISC_ZOH) return SSM_ERR_UNSUPPORTED;
   UpdateArgs a;
   a.state = state; a.u = u; a.delta = delta; a.A = A; a.B = B; a.C = C; a.D = D; a.z = z; a.bias = delta_bias;
-  a.y = y; a.batch = batch; a.dim = dim; a.dstate = dstate;
+  a.y = y; a.batch = batch; a.dim = dim; a.dstate = dstate; a.zoh = disc == SSM_DISC_ZOH;
   const size_t bc_align = (io == SSM_BF16) ? 8 : 16;
   const bool generic = !(dstate == 4 || dstate == 8 || dstate == 16) || !aligned(state, 16) || !aligned(A, 16) ||
                        !aligned(B, bc_align) || !aligned(C, bc_align);
@@ -2214,6 +2301,14 @@ ssm_status_t ssm_state_update(int64_t batch, int64_t dim, int64_t dstate, ssm_dt
   hipError_t e = (io == SSM_BF16) ? launch_update<bf16_t>(a, hs, generic, sp) : launch_update<float>(a, hs, generic, sp);
   if (e != hipSuccess) return hip_fail(e);
   return SSM_OK;
+}
+
+ssm_status_t ssm_state_update(int64_t batch, int64_t dim, int64_t dstate, ssm_dtype_t io, float* state, const void* u,
+                              const void* delta, const float* A, const void* B, const void* C, const float* D,
+                              const void* z, const float* delta_bias, int softplus_flag, void* y,
+                              struct ihipStream_t* stream) {
+  return ssm_state_update_ex(batch, dim, dstate, io, SSM_DISC_DELTA_B, state, u, delta, A, B, C, D, z, delta_bias,
+                             softplus_flag, y, stream);
 }
 
 }  // extern "C"

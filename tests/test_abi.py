@@ -122,6 +122,40 @@ def test_update_validation(lib):
     assert upd(lib, state=addr(2)) == 6             # state on u
 
 
+def fwd_ex(lib, disc, batch=2, dim=8, dstate=4, seqlen=16, io=0, **over):
+    args = dict(u=addr(1), delta=addr(2), A=addr(3), B=addr(4), C=addr(5), D=addr(6), z=addr(7), bias=addr(8),
+                sp=1, h0=addr(9), y=addr(10), last=addr(11))
+    args.update(over)
+    return lib.ssm_scan_fwd_ex(batch, dim, dstate, seqlen, io, disc, args["u"], args["delta"], args["A"], args["B"],
+                               args["C"], args["D"], args["z"], args["bias"], args["sp"], args["h0"], args["y"],
+                               args["last"], None)
+
+
+def upd_ex(lib, disc, batch=2, dim=8, dstate=4, io=0, **over):
+    args = dict(state=addr(1), u=addr(2), delta=addr(3), A=addr(4), B=addr(5), C=addr(6), D=addr(7), z=addr(8),
+                bias=addr(9), sp=1, y=addr(10))
+    args.update(over)
+    return lib.ssm_state_update_ex(batch, dim, dstate, io, disc, args["state"], args["u"], args["delta"], args["A"],
+                                   args["B"], args["C"], args["D"], args["z"], args["bias"], args["sp"], args["y"],
+                                   None)
+
+
+def test_ex_validation(lib):
+    for disc in (0, 1):
+        assert fwd_ex(lib, disc, u=None) == 1
+        assert fwd_ex(lib, disc, seqlen=0) == 2
+        assert fwd_ex(lib, disc, dstate=17) == 3
+        assert fwd_ex(lib, disc, io=3) == 4
+        assert fwd_ex(lib, disc, A=addr(3) + 2) == 5
+        assert fwd_ex(lib, disc, y=addr(5)) == 6
+        assert upd_ex(lib, disc, state=None) == 1
+        assert upd_ex(lib, disc, dstate=20) == 3
+        assert upd_ex(lib, disc, y=addr(1)) == 6
+    for disc in (2, -1, 99):   # not an ssm_disc_t value; otherwise valid calls
+        assert fwd_ex(lib, disc) == 8
+        assert upd_ex(lib, disc) == 8
+
+
 def cfwd(lib, batch=2, dim=8, dstate=4, seqlen=16, width=4, io=0, **over):
     args = dict(x=addr(1), w=addr(12), cb=addr(13), xp=addr(14), silu=1, delta=addr(2), A=addr(3), B=addr(4),
                 C=addr(5), D=addr(6), z=addr(7), bias=addr(8), sp=1, h0=addr(9), y=addr(10), last=addr(11),
