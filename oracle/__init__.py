@@ -15,6 +15,7 @@ this module only marshals numpy arrays into it.
   .state_update_f64(...)   one-token update of a float64 state, in place
   .state_update_channels_f64(...)  the same for chosen (b, d) channels
   .scan_bwd_f64(...)       gradients of the scan (reverse mode, written out by hand)
+  .scan_complex_f64(...)   the scan with complex diagonal A (complex B, C, state)
   .conv1d_f64(...)         the causal depthwise conv (+ silu) in front of the scan
   .softplus_f64, .silu_f64 the scalar helpers the C oracle uses
 Module-level functions of the same names use the default oracle.
@@ -62,6 +63,8 @@ class Oracle:
         L.oracle_zoh_b.argtypes = [ctypes.c_double, ctypes.c_double]
         L.oracle_scan_bwd_f64.restype = I
         L.oracle_scan_bwd_f64.argtypes = [I64, I64, I64, I64] + [P] * 8 + [I] + [P] * 12
+        L.oracle_scan_complex_f64.restype = I
+        L.oracle_scan_complex_f64.argtypes = [I64, I64, I64, I64] + [P] * 8 + [I, P, P, P]
         L.oracle_conv1d_f64.restype = I
         L.oracle_conv1d_f64.argtypes = [I64, I64, I64, I64, P, P, P, P, I, P]
         L.oracle_softplus.restype = ctypes.c_double
@@ -93,6 +96,39 @@ class Oracle:
         if rc != 0:
             raise ValueError("oracle_scan_f64 rejected the arguments")
         return y, last
+
+    def scan_complex_f64(self, u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=False, h0=None):
+        """The scan with complex A (dim, dstate), B and C (batch, dstate, seqlen) and h0 (batch, dim, dstate),
+        given as numpy complex arrays; u, delta, z (batch, dim, seqlen), D and delta_bias (dim,) are real.
+        Returns (y real (batch, dim, seqlen), last_state complex (batch, dim, dstate))."""
+        def ri(a):
+            return None if a is None else np.ascontiguousarray(np.stack([np.real(a), np.imag(a)], -1), np.float64)
+        u, delta, D, z, delta_bias = map(_f64, (u, delta, D, z, delta_bias))
+        A, B, C, h0 = map(ri, (A, B, C, h0))
+        batch, dim, seqlen = u.shape
+        dstate = A.shape[1]
+        y = np.empty((batch, dim, seqlen), np.float64)
+        last = np.empty((batch, dim, dstate, 2), np.float64)
+        rc = self.lib.oracle_scan_complex_f64(batch, dim, dstate, seqlen, _p(u), _p(delta), _p(A), _p(B), _p(C),
+                                              _p(D), _p(z), _p(delta_bias), 1 if softplus else 0, _p(h0), _p(y),
+                                              _p(last))
+        if rc != 0:
+            raise ValueError("oracle_scan_complex_f64 rejected the arguments")
+        return y, last[..., 0] + 1j * last[..., 1]
+
+    def scan_complex_channels_f64(self, channels, u, delta, A, B, C, D=None, z=None, delta_bias=None,
+                                  softplus=False, h0=None):
+        """scan_complex_f64 restricted to the listed (b, d) channels (marshalling only)."""
+        ys, hs = [], []
+        for (b, d) in channels:
+            def sl(t):
+                return None if t is None else t[b:b + 1, d:d + 1]
+            y, h = self.scan_complex_f64(sl(u), sl(delta), A[d:d + 1], B[b:b + 1], C[b:b + 1],
+                                         None if D is None else D[d:d + 1], sl(z),
+                                         None if delta_bias is None else delta_bias[d:d + 1], softplus, sl(h0))
+            ys.append(y[0, 0])
+            hs.append(h[0, 0])
+        return np.stack(ys), np.stack(hs)
 
     def scan_bwd_f64(self, u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=False, h0=None, dy=None,
                      dlast=None):
@@ -213,6 +249,14 @@ def state_update_channels_f64(*args, **kw):
 
 def scan_bwd_f64(*args, **kw):
     return default().scan_bwd_f64(*args, **kw)
+
+
+def scan_complex_f64(*args, **kw):
+    return default().scan_complex_f64(*args, **kw)
+
+
+def scan_complex_channels_f64(*args, **kw):
+    return default().scan_complex_channels_f64(*args, **kw)
 
 
 def conv1d_f64(*args, **kw):

@@ -50,6 +50,17 @@
  * so Bbar = (exp(Delta A) - 1) / A * B, whose limit at A = 0 is Delta * B
  * (oracle_zoh_b).  Abar is the same exp(Delta A) in both rules.
  *
+ * Complex diagonal A (oracle_scan_complex_f64).  The pages give A as real
+ * (the explainer's section on the S4 matrix dimensions: N numbers per
+ * channel); the S4 family also uses a complex diagonal A, read here as
+ * follows.  A real system whose state matrix has complex-conjugate
+ * eigenvalue pairs is stored as one state of each pair: A[d,n], B[b,n,l],
+ * C[b,n,l] and h are complex, the recurrence is the same one,
+ *   h[n] <- exp(Delta A[d,n]) h[n] + Delta B[b,n,l] u[b,d,l],
+ * and the output adds each state's conjugate partner, conj(C h):
+ *   y = (2 Re(sum_n C h) + D u) * silu(z).
+ * Delta, u, z, D and the bias stay real.
+ *
  * The Mamba block puts a causal Conv1d in front of the SSM (the Hebrew
  * overview, "תחילת העבודה עם Mamba"; the Chinese explainer's section on why a
  * convolution precedes the SSM: each token is first mixed with its neighbours
@@ -70,13 +81,14 @@
  *   x, u (conv)    : [batch][dim][seqlen]; w: [dim][K]; cb: [dim]; x_prev: [batch][dim][K-1]
  * Optional inputs (D, z, bias, h0, cb, x_prev) may be NULL; last_state may be NULL.
  */
+#include <complex.h>
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
 
-#define ORACLE_ABI_VERSION 2
+#define ORACLE_ABI_VERSION 3
 
 int oracle_abi_version(void) { return ORACLE_ABI_VERSION; }
 
@@ -178,6 +190,52 @@ int oracle_state_update_f64(int64_t batch, int64_t dim, int64_t dstate, double* 
                             int softplus_flag, double* y) {
   return oracle_state_update_ex_f64(batch, dim, dstate, 0, state, u, delta, A, B, C, D, z, delta_bias,
                                     softplus_flag, y);
+}
+
+/* The scan with complex A, B, C and state (see the top of the file).  Complex
+ * arrays hold (re, im) pairs in their last index:
+ *   A [dim][dstate][2], B and C [batch][dstate][seqlen][2],
+ *   h0 and last_state [batch][dim][dstate][2];
+ * u, delta, z, y, D and delta_bias are real, as in oracle_scan_f64.
+ * Returns 0, or -1 on bad sizes or a missing required pointer. */
+int oracle_scan_complex_f64(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, const double* u,
+                            const double* delta, const double* A, const double* B, const double* C,
+                            const double* D, const double* z, const double* delta_bias, int softplus_flag,
+                            const double* h0, double* y, double* last_state) {
+  if (batch < 1 || dim < 1 || dstate < 1 || dstate > 256 || seqlen < 1) return -1;
+  if (!u || !delta || !A || !B || !C || !y) return -1;
+  int64_t nch = batch * dim;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t ch = 0; ch < nch; ++ch) {
+    int64_t b = ch / dim, d = ch % dim;
+    double complex h[256];
+    for (int64_t n = 0; n < dstate; ++n)
+      h[n] = h0 ? h0[(ch * dstate + n) * 2] + I * h0[(ch * dstate + n) * 2 + 1] : 0.0;
+    double bias = delta_bias ? delta_bias[d] : 0.0;
+    for (int64_t l = 0; l < seqlen; ++l) {
+      double x = delta[ch * seqlen + l] + bias;
+      double step = softplus_flag ? oracle_softplus(x) : x;
+      double ul = u[ch * seqlen + l];
+      double complex acc = 0.0;
+      for (int64_t n = 0; n < dstate; ++n) {
+        const double* a = A + (d * dstate + n) * 2;
+        const double* bb = B + ((b * dstate + n) * seqlen + l) * 2;
+        const double* cc = C + ((b * dstate + n) * seqlen + l) * 2;
+        double complex abar = cexp(step * (a[0] + I * a[1]));
+        h[n] = abar * h[n] + step * (bb[0] + I * bb[1]) * ul;
+        acc += (cc[0] + I * cc[1]) * h[n];
+      }
+      double v = 2.0 * creal(acc) + (D ? D[d] : 0.0) * ul;
+      if (z) v *= oracle_silu(z[ch * seqlen + l]);
+      y[ch * seqlen + l] = v;
+    }
+    if (last_state)
+      for (int64_t n = 0; n < dstate; ++n) {
+        last_state[(ch * dstate + n) * 2] = creal(h[n]);
+        last_state[(ch * dstate + n) * 2 + 1] = cimag(h[n]);
+      }
+  }
+  return 0;
 }
 
 /* Causal depthwise convolution of every (b, d) row, then silu if the flag is

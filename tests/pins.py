@@ -42,6 +42,13 @@ deliberately broken copies of it (tests/test_oracle_mutants.py).
   zoh_limits        at A = 0 ZOH equals the Delta*B rule, and for small |Delta A|
                     its factor follows the series Delta (1 + Delta A / 2 + ...)
   zoh_decode        the one-token ZOH update equals a one-token ZOH scan
+  complex_real_limit   complex A, B, C, h0 with zero imaginary parts equal the real
+                    scan with C doubled (a real state and its conjugate partner)
+  complex_block_expm   each complex state a + ib is the real two-state system with
+                    block [[a, -b], [b, a]]: stepped with scipy's expm of that block,
+                    input (Re B, Im B) u and output 2 (Re C, -Im C)
+  complex_lti       constant Delta, B, C: y = 2 Re(sum_k K_k u_{t-k}) + D u with
+                    K_k = sum_n C_n Abar_n^k Delta B_n (numpy complex powers, np.convolve)
 """
 import json
 import math
@@ -508,6 +515,87 @@ def zoh_decode(o):
     _close(st, last_scan, 1e-15, 1e-15, "zoh decode state")
 
 
+def _complex_problem(rng, batch, dim, dstate, seqlen, h0=True):
+    p = _random_problem(rng, batch, dim, dstate, seqlen, h0=False)
+    p["A"] = p["A"] + 1j * rng.uniform(-6.0, 6.0, size=(dim, dstate))
+    p["B"] = p["B"] + 1j * rng.standard_normal((batch, dstate, seqlen))
+    p["C"] = p["C"] + 1j * rng.standard_normal((batch, dstate, seqlen))
+    p["h0"] = (rng.standard_normal((batch, dim, dstate)) + 1j * rng.standard_normal((batch, dim, dstate))) if h0 else None
+    return p
+
+
+def complex_real_limit(o):
+    rng = _rng(40)
+    p = _random_problem(rng, 2, 3, 4, 11, h0=True)
+    y, last = o.scan_f64(softplus=True, **dict(p, C=2.0 * p["C"]))
+    q = dict(p, A=p["A"] + 0j, B=p["B"] + 0j, C=p["C"] + 0j, h0=p["h0"] + 0j)
+    yc, lc = o.scan_complex_f64(softplus=True, **q)
+    _close(yc, y, 1e-13, 1e-14, "complex with real parameters: y")
+    _close(lc.real, last, 1e-13, 1e-14, "complex with real parameters: state")
+    assert not lc.imag.any(), "imaginary state from real parameters"
+
+
+def complex_block_expm(o):
+    from scipy.linalg import expm
+    rng = _rng(41)
+    batch, dim, dstate, seqlen = 2, 2, 3, 6
+    for flags in ((True, True, True, True, True), (False, False, False, False, False)):
+        zf, Df, bf, spf, hf = flags
+        p = _complex_problem(rng, batch, dim, dstate, seqlen, h0=hf)
+        if not zf:
+            p["z"] = None
+        if not Df:
+            p["D"] = None
+        if not bf:
+            p["delta_bias"] = None
+        y, last = o.scan_complex_f64(softplus=spf, **p)
+        x = p["delta"] + (p["delta_bias"][None, :, None] if bf else 0.0)
+        step = np.logaddexp(x, 0.0) if spf else x
+        for b in range(batch):
+            for d in range(dim):
+                h = np.zeros((dstate, 2))
+                if hf:
+                    h[:, 0], h[:, 1] = p["h0"][b, d].real, p["h0"][b, d].imag
+                for t in range(seqlen):
+                    v = 0.0
+                    for n in range(dstate):
+                        a, w = p["A"][d, n].real, p["A"][d, n].imag
+                        e = expm(np.array([[a, -w], [w, a]]) * step[b, d, t])
+                        bv = np.array([p["B"][b, n, t].real, p["B"][b, n, t].imag])
+                        h[n] = e @ h[n] + step[b, d, t] * bv * p["u"][b, d, t]
+                        v += 2.0 * (p["C"][b, n, t].real * h[n, 0] - p["C"][b, n, t].imag * h[n, 1])
+                    if Df:
+                        v += p["D"][d] * p["u"][b, d, t]
+                    if zf:
+                        zz = p["z"][b, d, t]
+                        v *= zz / (1.0 + math.exp(-zz))
+                    _close(y[b, d, t], v, 1e-11, 1e-13, "complex block y b=%d d=%d t=%d" % (b, d, t))
+                _close(last[b, d].real, h[:, 0], 1e-11, 1e-13, "complex block state re")
+                _close(last[b, d].imag, h[:, 1], 1e-11, 1e-13, "complex block state im")
+
+
+def complex_lti(o):
+    rng = _rng(42)
+    dim, dstate, seqlen = 3, 4, 40
+    A = -rng.uniform(0.1, 1.0, size=(dim, dstate)) + 1j * rng.uniform(-3.0, 3.0, size=(dim, dstate))
+    Bc = rng.standard_normal(dstate) + 1j * rng.standard_normal(dstate)
+    Cc = rng.standard_normal(dstate) + 1j * rng.standard_normal(dstate)
+    u = rng.standard_normal((1, dim, seqlen))
+    dt = 0.3
+    delta = np.full((1, dim, seqlen), dt)
+    B = np.repeat(Bc[None, :, None], seqlen, axis=2)
+    C = np.repeat(Cc[None, :, None], seqlen, axis=2)
+    D = rng.standard_normal(dim)
+    y, _ = o.scan_complex_f64(u, delta, A, B, C, D=D)
+    k = np.arange(seqlen)
+    for d in range(dim):
+        abar = np.exp(dt * A[d])
+        K = (Cc[None, :] * abar[None, :] ** k[:, None] * dt * Bc[None, :]).sum(axis=1)
+        want = 2.0 * np.convolve(K, u[0, d])[:seqlen].real + D[d] * u[0, d]
+        _close(y[0, d], want, 1e-11, 1e-12, "complex LTI d=%d" % d)
+
+
 ALL = [worked_examples, lti_closed_form, bruteforce, single_step, persistence, forgetting, split_carry, linearity,
        softplus_silu, decode_is_scan, channel_subset, conv_library, conv_taps, conv_causality, conv_split_carry,
-       bwd_finite_diff, bwd_autograd, zoh_van_loan, zoh_fixed_point, zoh_limits, zoh_decode]
+       bwd_finite_diff, bwd_autograd, zoh_van_loan, zoh_fixed_point, zoh_limits, zoh_decode, complex_real_limit,
+       complex_block_expm, complex_lti]

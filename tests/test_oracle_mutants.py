@@ -50,6 +50,14 @@ MUTANTS = [
     ("zoh_ignored", "      if (zoh) bbar_u = ", "      if (0) bbar_u = "),
     ("zoh_sign", "expm1(delta * a) / a : delta", "expm1(-delta * a) / a : delta"),
     ("zoh_without_B", "oracle_zoh_b(delta, A_row[n]) * B_b[n * seqlen + l] * ul", "oracle_zoh_b(delta, A_row[n]) * ul"),
+    ("cplx_no_factor_two", "double v = 2.0 * creal(acc)", "double v = creal(acc)"),
+    ("cplx_imag_part_out", "double v = 2.0 * creal(acc)", "double v = 2.0 * cimag(acc)"),
+    ("cplx_A_imag_dropped", "cexp(step * (a[0] + I * a[1]))", "cexp(step * (a[0] + 0.0 * I * a[1]))"),
+    ("cplx_A_conjugated", "cexp(step * (a[0] + I * a[1]))", "cexp(step * (a[0] - I * a[1]))"),
+    ("cplx_B_imag_dropped", "step * (bb[0] + I * bb[1]) * ul", "step * (bb[0] + 0.0 * I * bb[1]) * ul"),
+    ("cplx_C_conjugated", "acc += (cc[0] + I * cc[1]) * h[n];", "acc += (cc[0] - I * cc[1]) * h[n];"),
+    ("cplx_h0_imag_dropped", "h0[(ch * dstate + n) * 2] + I * h0[(ch * dstate + n) * 2 + 1]",
+     "h0[(ch * dstate + n) * 2] + 0.0 * I * h0[(ch * dstate + n) * 2 + 1]"),
     ("bwd_dD_after_gate", "        partD[ch] += g * ut;", "        partD[ch] += dy[ch * seqlen + t] * ut;"),
 ]
 
