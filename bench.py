@@ -16,6 +16,7 @@ the timed region.  Prints one JSON line:
   conv_scan    ssm_conv_scan_fwd (causal conv of width 4 fused in front of the
                scan) on the same workload
   zoh          ssm_scan_fwd_ex with exact zero-order hold for B, same workload
+  complex      ssm_scan_fwd_complex, 8 complex states (16 real numbers per channel)
   backward     ssm_scan_bwd (every gradient) on the same workload
 
 Algorithmic bytes: read u, delta, z and write y once (4 x io bytes per
@@ -208,6 +209,45 @@ def bench_zoh(dev, x, t, steps, warmup):
                 lane_slots_per_elem_state=ZOH_SLOTS_PER_ELEM_STATE)
 
 
+# Per (element, complex state): Delta Re A, exp2 (2), Delta Im A, fract, cos (2), sin (2), the two Abar
+# products, Delta u times Re B and Im B, four FMAs of the complex update, two for Re(C h).
+CPLX_SLOTS_PER_ELEM_STATE = 19
+
+
+def bench_complex(dev, x, t, steps, warmup):
+    """ssm_scan_fwd_complex on the same shape with 8 complex states (16 real numbers per channel, as the
+    real workload's 16 states): A = -1/2 + i pi n, B and C with N(0, 1) real and imaginary parts."""
+    import numpy as np
+    import torch
+    from selective_state_space_65_amd import binding, inputs
+    b, d, n, l = x.shape
+    nc = n // 2
+    rng = np.random.default_rng(inputs.SEED_BASE + 30)
+    k = np.arange(nc, dtype=np.float32)
+    A = np.stack([np.full((d, nc), -0.5, np.float32), np.broadcast_to(np.float32(np.pi) * k, (d, nc))], -1)
+    B = rng.standard_normal((b, nc, l, 2)).astype(np.float32)
+    C = rng.standard_normal((b, nc, l, 2)).astype(np.float32)
+    At = torch.from_numpy(np.ascontiguousarray(A)).to(dev)
+    Bt = torch.from_numpy(B).to(dev, t["u"].dtype)
+    Ct = torch.from_numpy(C).to(dev, t["u"].dtype)
+    y = torch.empty_like(t["u"])
+    last = torch.empty((b, d, nc, 2), dtype=torch.float32, device=dev)
+
+    def fn():
+        binding.scan_fwd_complex(t["u"], t["delta"], At, Bt, Ct, D=t["D"], z=t["z"], delta_bias=t["delta_bias"],
+                                 delta_softplus=x.softplus, out=y, last_state=last)
+
+    wall_ms, avg_ms, med_ms = time_calls(fn, steps, warmup)
+    io_bytes = 2 if x.io == "bf16" else 4
+    nbytes = algorithmic_bytes(b, d, n, l, io_bytes, has_z=x.z is not None) + d * n * 4  # A holds 2 numbers per state
+    slots = CPLX_SLOTS_PER_ELEM_STATE * b * d * l * nc
+    return dict(workload="complex diagonal A (ssm_scan_fwd_complex), 8 complex states, same shape and flags",
+                us_per_call=round(avg_ms * 1e3, 2), us_median=round(med_ms * 1e3, 2),
+                algorithmic_gbs=round(nbytes / (avg_ms * 1e-3) / 1e9, 1),
+                alu_frac=round(slots / (avg_ms * 1e-3) / LANE_SLOTS_PEAK, 4),
+                lane_slots_per_elem_complex_state=CPLX_SLOTS_PER_ELEM_STATE)
+
+
 BWD_SLOTS_PER_ELEM_STATE = 20  # 6 for the checkpointing forward + 14 for the adjoint walk
 
 
@@ -248,6 +288,7 @@ def main():
     ap.add_argument("--no-conv", action="store_true", help="skip the fused conv + scan line")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward line")
     ap.add_argument("--no-zoh", action="store_true", help="skip the zero-order-hold line")
+    ap.add_argument("--no-complex", action="store_true", help="skip the complex-A line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy 1 GiB three times (reference kernel for rocprofv3 FETCH_SIZE/WRITE_SIZE)")
     args = ap.parse_args()
@@ -318,6 +359,12 @@ def main():
         out["conv_scan"] = bench_conv_scan(dev, x, t, args.steps, args.warmup)
     if not args.no_zoh:
         out["zoh"] = bench_zoh(dev, x, t, args.steps, args.warmup)
+    if not args.no_complex:
+        from selective_state_space_65_amd import binding as _b
+        try:
+            out["complex"] = bench_complex(dev, x, t, args.steps, args.warmup)
+        except _b.SsmError as e:  # complex A runs on the single-pass kernel only
+            out["complex"] = dict(skipped=str(e))
     if not args.no_backward:
         bw = bench_backward(dev, x, t, max(3, args.steps // 4), 2)
         bw["vs_forward"] = round(bw["us_per_call"] / (avg_ms * 1e3), 2)

@@ -12,7 +12,8 @@
  *                      ssm_scan_fwd, given dL/dy (and optionally dL/dh_L).
  *
  * ssm_scan_fwd_ex and ssm_state_update_ex are the first two with a choice of
- * how B is discretized (Delta * B, or exact zero-order hold).
+ * how B is discretized (Delta * B, or exact zero-order hold), and
+ * ssm_scan_fwd_complex is the prefill scan with a complex diagonal A.
  *
  * What is computed (for every batch row b and channel d independently):
  *
@@ -66,7 +67,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 4
+#define SSM_ABI_VERSION 5
 
 struct ihipStream_t; /* the same incomplete type as HIP's hipStream_t */
 
@@ -256,6 +257,37 @@ ssm_status_t ssm_state_update_ex(int64_t batch, int64_t dim, int64_t dstate, ssm
                                  float* state, const void* u, const void* delta, const float* A, const void* B,
                                  const void* C, const float* D, const void* z, const float* delta_bias,
                                  int softplus_flag, void* y, struct ihipStream_t* stream);
+
+/*
+ * ssm_scan_fwd_complex -- the prefill scan with a complex diagonal A.  The
+ * pages give A as real (the Chinese explainer's section on the S4 matrix
+ * dimensions: N numbers per channel); models of the S4 family also use a
+ * complex diagonal A.  Read here as a real system whose state matrix has
+ * complex-conjugate eigenvalue pairs, one state of each pair stored:
+ *
+ *   h[n]     = exp(Delta A[d,n]) h[n] + Delta B[b,n,l] u[b,d,l]      (complex A, B, h)
+ *   y[b,d,l] = (2 Re(sum_n C[b,n,l] h[n]) + D[d] u[b,d,l]) * silu(z[b,d,l])
+ *
+ * (the 2 Re adds each state's conjugate partner).  Delta, u, z, D and the
+ * bias are real and as in ssm_scan_fwd.  dstate counts complex states.
+ * Complex arrays hold (re, im) pairs in their last index:
+ *
+ *   A          [dim, dstate, 2]          fp32
+ *   B, C       [batch, dstate, seqlen, 2] io
+ *   h0         [batch, dim, dstate, 2]   fp32   may be NULL (zero); may equal last_state
+ *   last_state [batch, dim, dstate, 2]   fp32   may be NULL
+ *   u, delta, z, y, D, delta_bias: as ssm_scan_fwd.
+ *
+ * Errors as ssm_scan_fwd (dstate above 8, i.e. above 16 real numbers per
+ * channel, is SSM_ERR_DSTATE_UNSUPPORTED), plus SSM_ERR_UNSUPPORTED outside
+ * the single-pass kernel: dstate must be 4 or 8, seqlen a multiple of 8, every
+ * (batch, dim, seqlen) and B/C buffer 16-byte aligned, and batch *
+ * ceil(dim / 64) at least 192 (enough 64-channel groups to fill the chip).
+ */
+ssm_status_t ssm_scan_fwd_complex(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, ssm_dtype_t io,
+                                  const void* u, const void* delta, const float* A, const void* B, const void* C,
+                                  const float* D, const void* z, const float* delta_bias, int softplus_flag,
+                                  const float* h0, void* y, float* last_state, struct ihipStream_t* stream);
 
 /* Kernel paths of ssm_scan_fwd (reported by ssm_scan_fwd_plan). */
 typedef enum {

@@ -41,6 +41,7 @@ SIGNATURES = {
     "ssm_state_update": (_I, [_I64, _I64, _I64, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P]),
     "ssm_scan_fwd_ex": (_I, [_I64, _I64, _I64, _I64, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P]),
     "ssm_state_update_ex": (_I, [_I64, _I64, _I64, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P]),
+    "ssm_scan_fwd_complex": (_I, [_I64, _I64, _I64, _I64, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P]),
     "ssm_conv_scan_fwd": (_I, [_I64, _I64, _I64, _I64, _I64, _I, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _I, _P,
                                _P, _P, _P, _P]),
     "ssm_scan_bwd": (_I, [_I64, _I64, _I64, _I64, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P,
@@ -209,6 +210,53 @@ def _scan_fwd(disc, u, delta, A, B, C, D, z, delta_bias, delta_softplus, h0, out
         _check("ssm_scan_fwd", lib.ssm_scan_fwd(batch, dim, dstate, seqlen, _io_code(io), *tail))
     else:
         _check("ssm_scan_fwd_ex", lib.ssm_scan_fwd_ex(batch, dim, dstate, seqlen, _io_code(io), disc, *tail))
+    return out, last_state
+
+
+def scan_fwd_complex(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=False, h0=None,
+                     out=None, last_state=None, return_last_state=True, stream=None):
+    """Selective scan with a complex diagonal A (ssm_scan_fwd_complex); returns (y, last_state).
+
+    Complex arrays are real tensors whose last dimension holds (re, im):
+    A (dim, dstate, 2) float32; B, C (batch, dstate, seqlen, 2) in the io dtype;
+    h0 and last_state (batch, dim, dstate, 2) float32.  u, delta, z, D,
+    delta_bias and y are as in scan_fwd.  dstate counts complex states.
+    """
+    import torch
+    if u.dim() != 3:
+        raise ValueError("u must be (batch, dim, seqlen)")
+    batch, dim, seqlen = u.shape
+    if A.dim() != 3 or A.shape[-1] != 2:
+        raise ValueError("A must be (dim, dstate, 2)")
+    dstate = A.shape[1]
+    dev = u.device
+    io = u.dtype
+    _need(u, "u", (batch, dim, seqlen), io, dev)
+    _need(delta, "delta", (batch, dim, seqlen), io, dev)
+    _need(A, "A", (dim, dstate, 2), torch.float32, dev)
+    _need(B, "B", (batch, dstate, seqlen, 2), io, dev)
+    _need(C, "C", (batch, dstate, seqlen, 2), io, dev)
+    if D is not None:
+        _need(D, "D", (dim,), torch.float32, dev)
+    if z is not None:
+        _need(z, "z", (batch, dim, seqlen), io, dev)
+    if delta_bias is not None:
+        _need(delta_bias, "delta_bias", (dim,), torch.float32, dev)
+    if h0 is not None:
+        _need(h0, "h0", (batch, dim, dstate, 2), torch.float32, dev)
+    if out is None:
+        out = torch.empty((batch, dim, seqlen), dtype=io, device=dev)
+    else:
+        _need(out, "out", (batch, dim, seqlen), io, dev)
+    if last_state is None and return_last_state:
+        last_state = torch.empty((batch, dim, dstate, 2), dtype=torch.float32, device=dev)
+    elif last_state is not None:
+        _need(last_state, "last_state", (batch, dim, dstate, 2), torch.float32, dev)
+    lib = load_library()
+    st = lib.ssm_scan_fwd_complex(batch, dim, dstate, seqlen, _io_code(io), _ptr(u), _ptr(delta), _ptr(A), _ptr(B),
+                                  _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias), 1 if delta_softplus else 0, _ptr(h0),
+                                  _ptr(out), _ptr(last_state), _stream(dev, stream))
+    _check("ssm_scan_fwd_complex", st)
     return out, last_state
 
 

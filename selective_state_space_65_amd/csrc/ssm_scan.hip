@@ -58,6 +58,7 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kInv2Pi = 0.15915494309189535f;  // 1 / (2 pi): radians to turns
 constexpr int kChunk = 8;           // tokens per lane per inner iteration
 constexpr int kWaveThreads = 64;
 constexpr int kBlockThreads = 256;  // 4 independent waves per block
@@ -703,9 +704,15 @@ struct Piece {
   }
 };
 
-template <typename IoT, int N, int S, int SA, bool kZ, bool kSoftplus, bool kConv, bool kZoh>
+// kCplx: complex diagonal A.  The N slots of a channel hold N/2 complex
+// states as (re, im) pairs (A, h0, last_state), and each wave owns one
+// complex state (NS = 2 slots); B and C rows are (re, im)-interleaved
+// [batch][N/2][seqlen][2], and the output is 2 Re(sum C h) + D u (each
+// stored state stands for a conjugate pair).
+template <typename IoT, int N, int S, int SA, bool kZ, bool kSoftplus, bool kConv, bool kZoh, bool kCplx = false>
 __global__ __launch_bounds__(64 * S) void scan_split_kernel(ScanArgs a) {
   using C = Split<IoT, N, S, SA>;
+  static_assert(!kCplx || (C::NS == 2 && !kConv && !kZoh), "one complex state per wave, Delta * B rule, no conv");
   constexpr int TS = C::TS;
   using LI = Line<IoT>;
   using PI = Piece<IoT, TS>;
@@ -732,7 +739,9 @@ __global__ __launch_bounds__(64 * S) void scan_split_kernel(ScanArgs a) {
   for (int j = 0; j < NS; ++j) {
     const int n = w * NS + j;
     const float an = a.A[d * N + n];
-    A2[j] = an * kLog2e;
+    // Complex: A2 = (Re A log2(e), Im A / 2 pi), the exp2 argument and the
+    // rotation in turns per unit of Delta.
+    A2[j] = (kCplx && j == 1) ? an * kInv2Pi : an * kLog2e;
     inva[j] = 1.0f / an;
     h[j] = a.h0 ? a.h0[ch * N + n] : 0.0f;
   }
@@ -766,7 +775,9 @@ __global__ __launch_bounds__(64 * S) void scan_split_kernel(ScanArgs a) {
   auto fetch_bc = [&](int s, int64_t lt) {
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
-      uint32_t off = (uint32_t)(w * NS + j) * row_bytes + (uint32_t)(lt * sizeof(IoT));
+      // Complex rows are twice as long; slot j holds tokens [4j, 4j + 4) as (re, im) pairs.
+      uint32_t off = kCplx ? (uint32_t)(w * NS) * row_bytes + (uint32_t)((2 * lt + 8 * j) * sizeof(IoT))
+                           : (uint32_t)(w * NS + j) * row_bytes + (uint32_t)(lt * sizeof(IoT));
       // Materialise the offset here: an address computed in another block
       // is not merged into whole-row s_load_dwordx4/x8 loads.
       asm volatile("" : "+s"(off));
@@ -898,6 +909,9 @@ __global__ __launch_bounds__(64 * S) void scan_split_kernel(ScanArgs a) {
       for (int s2 = 1; s2 < S; ++s2) {
         acc.x += part[q][s2].x; acc.y += part[q][s2].y; acc.z += part[q][s2].z; acc.w += part[q][s2].w;
       }
+      if constexpr (kCplx) {  // each state and its conjugate partner
+        acc.x *= 2.0f; acc.y *= 2.0f; acc.z *= 2.0f; acc.w *= 2.0f;
+      }
       yo[4 * q] = acc.x; yo[4 * q + 1] = acc.y; yo[4 * q + 2] = acc.z; yo[4 * q + 3] = acc.w;
     }
 #pragma unroll
@@ -991,7 +1005,7 @@ __global__ __launch_bounds__(64 * S) void scan_split_kernel(ScanArgs a) {
           fetch_bc(s ^ 1, l + (k + 1) * kChunk);
         }
         __builtin_amdgcn_sched_barrier(0);
-        if (a.ckpt && (k * kChunk) % kCkptTokens == 0) {
+        if (!kCplx && a.ckpt && (k * kChunk) % kCkptTokens == 0) {
           // The state before token l + k*kChunk, for the backward's recompute.
           const int64_t c = (l + k * kChunk) / kCkptTokens;
 #pragma unroll
@@ -1003,6 +1017,27 @@ __global__ __launch_bounds__(64 * S) void scan_split_kernel(ScanArgs a) {
 #pragma unroll
           for (int t = 0; t < kChunk; ++t) du[t] = dl[k][t] * xl[k][t];
         }
+        if constexpr (kCplx) {
+          // h <- exp(Delta A) h + Delta B u in complex arithmetic; the partial
+          // is Re(C h) = Re C Re h - Im C Im h.
+          float hr = h[0], hi = h[1];
+#pragma unroll
+          for (int t = 0; t < kChunk; ++t) {
+            const int jj = t >> 2, q = 2 * (t & 3);
+            const float mag = exp2_hw(A2[0] * dl[k][t]);
+            const float turn = __builtin_amdgcn_fractf(A2[1] * dl[k][t]);
+            const float pr = mag * __builtin_amdgcn_cosf(turn), pi = mag * __builtin_amdgcn_sinf(turn);
+            const float x = xl[k][t];
+            const float nr = __builtin_fmaf(pr, hr, __builtin_fmaf(-pi, hi, U::elem(Bx[s][jj], q) * x));
+            const float ni = __builtin_fmaf(pr, hi, __builtin_fmaf(pi, hr, U::elem(Bx[s][jj], q + 1) * x));
+            hr = nr;
+            hi = ni;
+            yv[t] = __builtin_fmaf(U::elem(Cx[s][jj], q), hr, -(U::elem(Cx[s][jj], q + 1) * hi));
+          }
+          h[0] = hr;
+          h[1] = hi;
+          asm volatile("" : "+v"(h[0]), "+v"(h[1]));
+        } else {
 #pragma unroll
         for (int j = 0; j < NS; ++j) {
           float hn = h[j];
@@ -1019,6 +1054,7 @@ __global__ __launch_bounds__(64 * S) void scan_split_kernel(ScanArgs a) {
           // The state's results must exist here: the compiler may not sink
           // the C.h accumulation below the next state's work.
           asm volatile("" : "+v"(h[j]));
+        }
         }
         yp[buf][(w * (T / 4) + 2 * k) * 64 + lane] = make_float4(yv[0], yv[1], yv[2], yv[3]);
         yp[buf][(w * (T / 4) + 2 * k + 1) * 64 + lane] = make_float4(yv[4], yv[5], yv[6], yv[7]);
@@ -1799,11 +1835,22 @@ hipError_t launch_scan_f(const ScanArgs& a, const Plan& p, hipStream_t st, bool 
   return a.zoh ? launch_scan_z<IoT, N, kVec, true>(a, p, st, sp) : launch_scan_z<IoT, N, kVec, false>(a, p, st, sp);
 }
 
-template <typename IoT, int N, int S, int SA, bool kZ, bool kSp, bool kConv, bool kZoh>
+template <typename IoT, int N, int S, int SA, bool kZ, bool kSp, bool kConv, bool kZoh, bool kCplx = false>
 hipError_t launch_split_t(const ScanArgs& a, const Plan& p, hipStream_t st) {
-  hipLaunchKernelGGL((scan_split_kernel<IoT, N, S, SA, kZ, kSp, kConv, kZoh>), dim3((unsigned)(a.batch * p.groups)),
-                     dim3(64 * S), 0, st, a);
+  hipLaunchKernelGGL((scan_split_kernel<IoT, N, S, SA, kZ, kSp, kConv, kZoh, kCplx>),
+                     dim3((unsigned)(a.batch * p.groups)), dim3(64 * S), 0, st, a);
   return hipGetLastError();
+}
+
+// Complex A: NC complex states (2 NC slots), one per wave.
+template <typename IoT, int NC>
+hipError_t launch_split_cplx(const ScanArgs& a, const Plan& p, hipStream_t st, bool sp) {
+  constexpr int N = 2 * NC, S = NC, SA = 4;
+  if (a.z)
+    return sp ? launch_split_t<IoT, N, S, SA, true, true, false, false, true>(a, p, st)
+              : launch_split_t<IoT, N, S, SA, true, false, false, false, true>(a, p, st);
+  return sp ? launch_split_t<IoT, N, S, SA, false, true, false, false, true>(a, p, st)
+            : launch_split_t<IoT, N, S, SA, false, false, false, false, true>(a, p, st);
 }
 
 template <typename IoT, int N, bool kConv, bool kZoh>
@@ -2111,6 +2158,35 @@ ssm_status_t ssm_scan_fwd(int64_t batch, int64_t dim, int64_t dstate, int64_t se
                           float* last_state, struct ihipStream_t* stream) {
   return ssm_scan_fwd_ex(batch, dim, dstate, seqlen, io, SSM_DISC_DELTA_B, u, delta, A, B, C, D, z, delta_bias,
                          softplus_flag, h0, y, last_state, stream);
+}
+
+ssm_status_t ssm_scan_fwd_complex(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, ssm_dtype_t io,
+                                  const void* u, const void* delta, const float* A, const void* B, const void* C,
+                                  const float* D, const void* z, const float* delta_bias, int softplus_flag,
+                                  const float* h0, void* y, float* last_state, struct ihipStream_t* stream) {
+  // The checks of ssm_scan_fwd on the real slots (two per complex state);
+  // more than 8 complex states is more than 16 slots.
+  const int64_t slots = dstate < 1 ? dstate : (dstate > 8 ? 17 : 2 * dstate);
+  Shape sh;
+  ssm_status_t st = shape_of(batch, dim, slots, seqlen, io, &sh);
+  if (st != SSM_OK) return st;
+  if (!u || !delta || !A || !B || !C || !y) return SSM_ERR_NULL;
+  st = check_scan_buffers(sh, dim, io, u, delta, A, B, C, D, z, delta_bias, h0, y, last_state, nullptr, 0, nullptr);
+  if (st != SSM_OK) return st;
+  Plan plan = make_plan(sh, batch, dim, slots, seqlen, io);
+  if (!(dstate == 4 || dstate == 8) || !plan.split || !vec_rows(sh, slots, seqlen, io, u, delta, B, C, z, y))
+    return SSM_ERR_UNSUPPORTED;
+  ScanArgs a = scan_args(sh, batch, dim, slots, seqlen, io, u, delta, A, B, C, D, z, delta_bias, h0, y, last_state);
+  a.groups = plan.groups; a.segments = 1; a.seg_len = seqlen;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  const bool sp = softplus_flag != 0;
+  hipError_t e;
+  if (io == SSM_BF16)
+    e = dstate == 4 ? launch_split_cplx<bf16_t, 4>(a, plan, hs, sp) : launch_split_cplx<bf16_t, 8>(a, plan, hs, sp);
+  else
+    e = dstate == 4 ? launch_split_cplx<float, 4>(a, plan, hs, sp) : launch_split_cplx<float, 8>(a, plan, hs, sp);
+  if (e != hipSuccess) return hip_fail(e);
+  return SSM_OK;
 }
 
 ssm_status_t ssm_conv_scan_fwd(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int64_t conv_width,

@@ -156,6 +156,31 @@ def test_ex_validation(lib):
         assert upd_ex(lib, disc) == 8
 
 
+def cplx(lib, batch=2, dim=8, dstate=4, seqlen=16, io=0, **over):
+    args = dict(u=addr(1), delta=addr(2), A=addr(3), B=addr(4), C=addr(5), D=addr(6), z=addr(7), bias=addr(8),
+                sp=1, h0=addr(9), y=addr(10), last=addr(11))
+    args.update(over)
+    return lib.ssm_scan_fwd_complex(batch, dim, dstate, seqlen, io, args["u"], args["delta"], args["A"], args["B"],
+                                    args["C"], args["D"], args["z"], args["bias"], args["sp"], args["h0"], args["y"],
+                                    args["last"], None)
+
+
+def test_complex_validation(lib):
+    assert cplx(lib, u=None) == 1
+    assert cplx(lib, dstate=0) == 2
+    assert cplx(lib, dstate=9) == 3            # above 16 real numbers per channel
+    assert cplx(lib, dstate=1 << 62) == 3
+    assert cplx(lib, io=9) == 4
+    assert cplx(lib, B=addr(4) + 2) == 5
+    assert cplx(lib, y=addr(2) + 8) == 6
+    # A is (dim, dstate, 2): last_state overlapping A's second half is an alias.
+    assert cplx(lib, last=addr(3) + 8 * 4 * 4) == 6
+    # Valid calls outside the single-pass kernel are refused before any launch.
+    assert cplx(lib) == 8                      # 2 x 1 groups of 64 channels: too few blocks
+    assert cplx(lib, batch=192, dim=64, dstate=2) == 8
+    assert cplx(lib, batch=192, dim=64, seqlen=12) == 8
+
+
 def cfwd(lib, batch=2, dim=8, dstate=4, seqlen=16, width=4, io=0, **over):
     args = dict(x=addr(1), w=addr(12), cb=addr(13), xp=addr(14), silu=1, delta=addr(2), A=addr(3), B=addr(4),
                 C=addr(5), D=addr(6), z=addr(7), bias=addr(8), sp=1, h0=addr(9), y=addr(10), last=addr(11),

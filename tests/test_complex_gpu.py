@@ -1,0 +1,171 @@
+"""Complex diagonal A (ssm_scan_fwd_complex) against the fp64 oracle, through
+the C ABI (needs an MI355X).
+
+Bar as for the real scan: max|got - want| <= tol * max|want|, tol = 1e-4 for
+fp32 io and 2e-2 for bf16 io; states (complex, compared as (re, im) pairs) at
+1e-4 for both.  Inputs: A = -1/2 + i pi n (a decaying rotation per state,
+n = 0 .. dstate-1), Delta from the workloads' recipe, B and C with standard
+normal real and imaginary parts, complex h0.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from selective_state_space_65_amd import binding, inputs
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def say(msg):
+    print("[gpu-case] " + msg, flush=True)
+
+
+def check(got, want, tol, what):
+    got = np.asarray(got, np.float64)
+    want = np.asarray(want, np.float64)
+    assert got.shape == want.shape, what
+    assert np.isfinite(got).all(), "%s: non-finite output" % what
+    scale = float(np.max(np.abs(want)))
+    err = float(np.max(np.abs(got - want)))
+    assert err <= tol * scale + 1e-30, "%s: max err %.3e > %.1e * %.3e" % (what, err, tol, scale)
+
+
+def np64(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def complex_inputs(batch, dim, dstate, seqlen, io, seed, z=True, D=True, bias=True, softplus=True, h0=True):
+    """Real parts from the workload recipe; (re, im) float32 arrays, bf16-rounded for bf16 io."""
+    x = inputs.make_scan_inputs(batch, dim, dstate, seqlen, io=io, seed=seed, z=z, D=D, bias=bias,
+                                softplus=softplus)
+    rng = np.random.default_rng([seed, 7])
+    n = np.arange(dstate, dtype=np.float32)
+    A = np.stack([np.full((dim, dstate), -0.5, np.float32), np.broadcast_to(np.float32(np.pi) * n, (dim, dstate))],
+                 -1).astype(np.float32)
+    B = rng.standard_normal((batch, dstate, seqlen, 2)).astype(np.float32)
+    C = rng.standard_normal((batch, dstate, seqlen, 2)).astype(np.float32)
+    if io == "bf16":
+        B, C = inputs.round_bf16(B), inputs.round_bf16(C)
+    hh = rng.standard_normal((batch, dim, dstate, 2)).astype(np.float32) if h0 else None
+    return x, A, B, C, hh
+
+
+def cplx(a):
+    return None if a is None else a[..., 0].astype(np.float64) + 1j * a[..., 1].astype(np.float64)
+
+
+def run(x, A, B, C, hh, **kw):
+    t = inputs.to_torch(x, DEV)
+    dt = t["u"].dtype
+    At = torch.from_numpy(A).to(DEV)
+    Bt = torch.from_numpy(B).to(DEV, dt)
+    Ct = torch.from_numpy(C).to(DEV, dt)
+    ht = None if hh is None else torch.from_numpy(hh).to(DEV)
+    y, last = binding.scan_fwd_complex(t["u"], t["delta"], At, Bt, Ct, D=t["D"], z=t["z"], delta_bias=t["delta_bias"],
+                                       delta_softplus=x.softplus, h0=ht, **kw)
+    torch.cuda.synchronize()
+    return y, last
+
+
+def reference(x, A, B, C, hh):
+    return oracle.scan_complex_f64(x.u, x.delta, cplx(A), cplx(B), cplx(C), x.D, x.z, x.delta_bias, x.softplus,
+                                   cplx(hh))
+
+
+SHAPES = [(192, 64, 8, 64), (200, 64, 4, 40), (256, 33, 8, 24), (192, 130, 4, 16)]
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", SHAPES, ids=["%dx%dx%dx%d" % s for s in SHAPES])
+def test_complex_matches_oracle(io, shape):
+    b, d, n, l = shape
+    for mask in (31, 0, 21, 10):
+        zf, Df, bf, spf, hf = [(mask >> i) & 1 == 1 for i in range(5)]
+        say("complex shape=%s io=%s mask=%d" % (shape, io, mask))
+        x, A, B, C, hh = complex_inputs(b, d, n, l, io, 4000 + mask, z=zf, D=Df, bias=bf, softplus=spf, h0=hf)
+        if not spf:  # keep Delta positive (a negative step makes the state grow without bound)
+            x.delta = inputs.round_bf16(np.abs(x.delta) * np.float32(0.2)) if io == "bf16" else \
+                np.abs(x.delta) * np.float32(0.2)
+            if bf:
+                x.delta_bias = np.full(d, 0.01, np.float32)
+        y, last = run(x, A, B, C, hh)
+        yr, hr = reference(x, A, B, C, hh)
+        check(np64(y), yr, TOL[io], "y mask=%d" % mask)
+        check(np64(last), np.stack([hr.real, hr.imag], -1), TOL["f32"], "last_state mask=%d" % mask)
+
+
+def test_complex_large_rotations():
+    """Im(A) Delta of tens of turns: the rotation is reduced to one turn before sin/cos."""
+    x, A, B, C, hh = complex_inputs(192, 64, 8, 32, "f32", 4100)
+    A[..., 1] = np.float32(300.0) * (np.arange(8, dtype=np.float32) - 3.5)
+    y, last = run(x, A, B, C, hh)
+    yr, hr = reference(x, A, B, C, hh)
+    check(np64(y), yr, TOL["f32"], "y")
+    check(np64(last), np.stack([hr.real, hr.imag], -1), TOL["f32"], "last_state")
+
+
+def test_complex_state_carry_in_place():
+    """h0 == last_state carries the state across two calls; equals one call over both halves."""
+    x, A, B, C, hh = complex_inputs(192, 64, 8, 64, "f32", 4200)
+    y_all, last_all = run(x, A, B, C, hh)
+    st = torch.from_numpy(hh).to(DEV)
+    halves = []
+    for lo, hi in ((0, 32), (32, 64)):
+        xs = inputs.ScanInputs(u=np.ascontiguousarray(x.u[..., lo:hi]), delta=np.ascontiguousarray(x.delta[..., lo:hi]),
+                               A=x.A, B=x.B, C=x.C, D=x.D, z=np.ascontiguousarray(x.z[..., lo:hi]),
+                               delta_bias=x.delta_bias, io="f32", softplus=True)
+        t = inputs.to_torch(xs, DEV)
+        y, _ = binding.scan_fwd_complex(t["u"], t["delta"], torch.from_numpy(A).to(DEV),
+                                        torch.from_numpy(np.ascontiguousarray(B[:, :, lo:hi])).to(DEV),
+                                        torch.from_numpy(np.ascontiguousarray(C[:, :, lo:hi])).to(DEV), D=t["D"],
+                                        z=t["z"], delta_bias=t["delta_bias"], delta_softplus=True, h0=st, last_state=st)
+        halves.append(y)
+    torch.cuda.synchronize()
+    check(np64(torch.cat(halves, -1)), np64(y_all), 1e-5, "y in two calls")
+    check(np64(st), np64(last_all), 1e-5, "carried state")
+
+
+def test_complex_real_parameters_equal_real_scan():
+    """Zero imaginary parts: the complex kernel equals the real scan with C doubled."""
+    x, A, B, C, hh = complex_inputs(192, 64, 8, 64, "f32", 4300)
+    A[..., 0] = -(np.arange(8, dtype=np.float32) + 1.0)
+    A[..., 1] = 0.0
+    B[..., 1] = 0.0
+    C[..., 1] = 0.0
+    hh[..., 1] = 0.0
+    y, last = run(x, A, B, C, hh)
+    t = inputs.to_torch(x, DEV)
+    yr, lr = binding.scan_fwd(t["u"], t["delta"], torch.from_numpy(A[..., 0].copy()).to(DEV),
+                              torch.from_numpy(np.ascontiguousarray(B[..., 0])).to(DEV),
+                              torch.from_numpy(np.ascontiguousarray(2.0 * C[..., 0])).to(DEV), D=t["D"], z=t["z"],
+                              delta_bias=t["delta_bias"], delta_softplus=True,
+                              h0=torch.from_numpy(np.ascontiguousarray(hh[..., 0])).to(DEV))
+    torch.cuda.synchronize()
+    check(np64(y), np64(yr), 1e-5, "y")
+    check(np64(last)[..., 0], np64(lr), 1e-5, "state")
+    assert not np64(last)[..., 1].any()
+
+
+def test_complex_mamba1p4b_shape_sampled():
+    """The Mamba-1.4B layer shape with 8 complex states (16 real numbers per channel), bf16."""
+    b, d, n, l = 4, 4096, 8, 4096
+    x, A, B, C, hh = complex_inputs(b, d, n, l, "bf16", 4400, h0=False)
+    say("complex 4x4096x8cx4096 bf16, sampled channels")
+    y, last = run(x, A, B, C, hh)
+    ch = inputs.sample_channels(b, d, 16, seed=9)
+    yr, hr = oracle.scan_complex_channels_f64(ch, x.u, x.delta, cplx(A), cplx(B), cplx(C), x.D, x.z, x.delta_bias,
+                                              x.softplus, None)
+    yg, hg = np64(y), np64(last)
+    check(np.stack([yg[bb, dd] for bb, dd in ch]), yr, TOL["bf16"], "y")
+    check(np.stack([hg[bb, dd] for bb, dd in ch]), np.stack([hr.real, hr.imag], -1), TOL["f32"], "last_state")
+
+
+def test_complex_unsupported_shapes():
+    for shape in ((2, 64, 8, 64), (192, 64, 2, 64), (192, 64, 8, 60)):
+        x, A, B, C, hh = complex_inputs(*shape, "f32", 4500)
+        with pytest.raises(binding.SsmError) as e:
+            run(x, A, B, C, hh)
+        assert e.value.name == "SSM_ERR_UNSUPPORTED"
