@@ -1061,26 +1061,29 @@ __global__ __launch_bounds__(64 * S) void scan_split_kernel(ScanArgs a) {
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    // Rotate the pieces.  The pins keep the compiler from deferring the
-    // copies (and the wait on the tile i+2 fetch) into the next phase A.
+    // Rotate the pieces (only the waves that own tokens hold any).  The pins
+    // keep the compiler from deferring the copies (and the wait on the tile
+    // i+2 fetch) into the next phase A.
+    if (w < SA) {
 #pragma unroll
-    for (int q = 0; q < PW; ++q) {
-      pu[q] = cu[q];
-      if constexpr (kZ) pz[q] = cz[q];
-      cu[q] = au[q];
-      if constexpr (kZ) cz[q] = az[q];
-      au[q] = nu[q];
-      ad[q] = nd[q];
-      if constexpr (kZ) az[q] = nz[q];
-    }
-    if constexpr (kConv) {
+      for (int q = 0; q < PW; ++q) {
+        pu[q] = cu[q];
+        if constexpr (kZ) pz[q] = cz[q];
+        cu[q] = au[q];
+        if constexpr (kZ) cz[q] = az[q];
+        au[q] = nu[q];
+        ad[q] = nd[q];
+        if constexpr (kZ) az[q] = nz[q];
+      }
+      if constexpr (kConv) {
 #pragma unroll
-      for (int q = 0; q < HW; ++q) ah[q] = nh[q];
-      settle_vgprs(ah);
+        for (int q = 0; q < HW; ++q) ah[q] = nh[q];
+        settle_vgprs(ah);
+      }
+      settle_vgprs(au);
+      settle_vgprs(ad);
+      if constexpr (kZ) settle_vgprs(az);
     }
-    settle_vgprs(au);
-    settle_vgprs(ad);
-    if constexpr (kZ) settle_vgprs(az);
     lds_barrier();
   }
   // ---- C of the last tile (its partials are in yp[buf^1]).
