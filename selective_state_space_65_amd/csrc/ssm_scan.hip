@@ -1113,19 +1113,23 @@ __global__ __launch_bounds__(64 * S) void scan_split_kernel(ScanArgs a) {
 // checkpoint in registers before walking it backwards.  Same layout as the
 // forward: a block owns 64 channels of one batch row, its S waves split the
 // states, and the first SA waves (one per SIMD) handle the per-token work.
-// Per tile, in reverse order:
-//   P0  the first SA waves stage (Delta, x = Delta u) of their TS tokens in LDS;
+// Per tile, in reverse order, with two barriers:
+//   P0  the first SA waves stage (Delta, x = Delta u) and g_t = dy_t silu(z_t)
+//       of their TS tokens in LDS (g does not depend on the state) and add
+//       g u into dD;                                              -- barrier
 //   P1  every wave recomputes its states over the tile from the checkpoint and
 //       publishes its partial C.h sums;
-//   P2  the first SA waves sum the partials (wave order) into the pre-gate
-//       output s_t = C.h + D u and form g_t, dz_t and dD; g_t goes to LDS;
-//   P3  every wave walks its states backwards: lambda, dA in registers, the
-//       partial sums over its states of lambda B and lambda A (h_t - B x_t)
+//   P2  then walks its states backwards: lambda, dA in registers, the partial
+//       sums over its states of lambda B and lambda A (h_t - B x_t)
 //       (= lambda A Abar h_{t-1}) to LDS, and the per-lane products lambda x
-//       (dB) and g h (dC) summed over the wave's 64 channels;
-//   P4  the first SA waves sum the partials into du_t = g D + Delta sum(lambda B)
-//       and dDelta_t = sum(lambda A Abar h_{t-1}) + u sum(lambda B), and
-//       ddelta_t = dDelta_t sigmoid(delta_t + bias) with softplus.
+//       (dB) and g h (dC) summed over the wave's 64 channels;    -- barrier
+//   P3  the first SA waves sum the partials in wave order into the pre-gate
+//       output s_t = C.h + D u (for dz_t), du_t = g D + Delta sum(lambda B) and
+//       dDelta_t = sum(lambda A Abar h_{t-1}) + u sum(lambda B), with
+//       ddelta_t = dDelta_t sigmoid(delta_t + bias) under softplus.
+// The next tile's P0 follows P3 directly: every LDS buffer it writes was last
+// read before the second barrier, and every buffer P3 reads is next written
+// after the next tile's first barrier.
 // dB and dC are per-(group, batch row) partial sums over 64 channels, dA per
 // batch row, dD and dbias per (batch row, wave); bwd_reduce_kernel adds them
 // up in a fixed order, so the gradients are deterministic (no atomics).
@@ -1236,7 +1240,8 @@ __global__ __launch_bounds__(64 * S) void scan_bwd_kernel(BwdArgs a) {
   static_assert(N % S == 0 && NS <= 2 && S % SA == 0 && TS % 2 == 0 && kChunk % TS == 0 && KT == 2,
                 "backward tile shape");
   __shared__ float4 dxs[T / 2][64];  // (Delta_t, x_t, Delta_t+1, x_t+1)
-  __shared__ float2 part[S][T][64];  // per-wave partials: P1 .x = C.h; P3 .x = sum lambda A q, .y = sum lambda B
+  __shared__ float pch[S][T][64];    // per-wave partials of P1: C.h
+  __shared__ float2 part[S][T][64];  // per-wave partials of P2: .x = sum lambda A q, .y = sum lambda B
   __shared__ float gs[T][64];        // g_t
 
   const int lane = threadIdx.x & 63;
@@ -1273,6 +1278,23 @@ __global__ __launch_bounds__(64 * S) void scan_bwd_kernel(BwdArgs a) {
   const IoT* Cb = static_cast<const IoT*>(a.C) + b * N * L;
   const uint32_t row_bytes = (uint32_t)(L * sizeof(IoT));
 
+  // Inputs of a tile, loaded one tile ahead: the per-token pieces of the
+  // first SA waves and every wave's checkpointed states.
+  uint32_t qu[PW], qd[PW], qz[ZW], qy[PW], nqu[PW], nqd[PW], nqz[ZW], nqy[PW];
+  float hck[NS], nhck[NS];
+  auto load_tile = [&](int64_t c, uint32_t (&u_)[PW], uint32_t (&d_)[PW], uint32_t (&z_)[ZW], uint32_t (&y_)[PW],
+                       float (&h_)[NS]) {
+    const int64_t l = c * T;
+    if (w < SA && l + w * TS < L) {
+      PI::load(ur + l + w * TS, u_);
+      PI::load(dr + l + w * TS, d_);
+      if constexpr (kZ) PI::load(zr + l + w * TS, z_);
+      PI::load(yr + l + w * TS, y_);
+    }
+#pragma unroll
+    for (int j = 0; j < NS; ++j) h_[j] = a.ckpt[((c * a.batch + b) * N + w * NS + j) * a.dim + d];
+  };
+
   // One tile of KV sub-chunks of kChunk tokens (KV = KT, or 1 for a last
   // tile of 8 tokens), so that every loop below has a static trip count.
   auto tile = [&](int64_t c, auto kv_tag) {
@@ -1280,14 +1302,25 @@ __global__ __launch_bounds__(64 * S) void scan_bwd_kernel(BwdArgs a) {
     constexpr int VT = KV * kChunk;
     const int64_t l = c * T;
     const bool acw = w < SA && w * TS < VT;  // this wave's per-token share exists
-    // ---- P0
-    uint32_t qu[PW], qd[PW], qz[ZW], qy[PW];
-    float dlv4[TS], sgd4[TS], g4[TS];
+    // The B/C rows of this wave's states (scalar words), issued first so that
+    // P0 covers their latency.
+    uint32_t Bt[NS][KV][W], Ct[NS][KV][W];
+#pragma unroll
+    for (int j = 0; j < NS; ++j)
+#pragma unroll
+      for (int k = 0; k < KV; ++k) {
+        uint32_t off = (uint32_t)(w * NS + j) * row_bytes + (uint32_t)((l + k * kChunk) * sizeof(IoT));
+        asm volatile("" : "+s"(off));
+        U::load8(Bb, off, Bt[j][k]);
+        U::load8(Cb, off, Ct[j][k]);
+      }
+    // The next tile's inputs (tiles run in reverse; every tile but the last is full).
+    if (c > 0) load_tile(c - 1, nqu, nqd, nqz, nqy, nhck);
+    // ---- P0: (Delta, x = Delta u) and g = dL/d(pre-gate output) of this
+    // wave's tokens.  g = dy silu(z) does not depend on the state, so every
+    // wave can start on the adjoint right after recomputing its states.
+    float dlv4[TS], sgd4[TS], g4[TS], sgz4[TS];
     if (acw) {
-      PI::load(ur + l + w * TS, qu);
-      PI::load(dr + l + w * TS, qd);
-      if constexpr (kZ) PI::load(zr + l + w * TS, qz);
-      PI::load(yr + l + w * TS, qy);
 #pragma unroll
       for (int t = 0; t < TS; t += 2) {
         float dd[2];
@@ -1301,29 +1334,35 @@ __global__ __launch_bounds__(64 * S) void scan_bwd_kernel(BwdArgs a) {
         dxs[(w * TS + t) / 2][lane] =
             make_float4(dd[0], dd[0] * LI::elem(qu, t), dd[1], dd[1] * LI::elem(qu, t + 1));
       }
+#pragma unroll
+      for (int t = 0; t < TS; ++t) {
+        float g = LI::elem(qy, t);
+        if constexpr (kZ) {
+          const float zt = LI::elem(qz, t);
+          sgz4[t] = sigmoid_f32(zt);
+          g *= zt * sgz4[t];
+        }
+        dD_acc = __builtin_fmaf(g, LI::elem(qu, t), dD_acc);
+        g4[t] = g;
+        gs[w * TS + t][lane] = g;
+      }
     }
     lds_barrier();
-    // ---- P1: the tile's states from its checkpoint (B/C rows of this wave's states as scalar words)
-    uint32_t Bt[NS][KV][W], Ct[NS][KV][W];
-#pragma unroll
-    for (int j = 0; j < NS; ++j)
-#pragma unroll
-      for (int k = 0; k < KV; ++k) {
-        uint32_t off = (uint32_t)(w * NS + j) * row_bytes + (uint32_t)((l + k * kChunk) * sizeof(IoT));
-        asm volatile("" : "+s"(off));
-        U::load8(Bb, off, Bt[j][k]);
-        U::load8(Cb, off, Ct[j][k]);
-      }
-    float dlv[VT], xv[VT];
+    // ---- P1: the tile's states from its checkpoint
+    float dlv[VT], xv[VT], gv[VT];
 #pragma unroll
     for (int i = 0; i < VT / 2; ++i) {
       const float4 v = dxs[i][lane];
       dlv[2 * i] = v.x; xv[2 * i] = v.y; dlv[2 * i + 1] = v.z; xv[2 * i + 1] = v.w;
     }
+    // Lanes past the last channel run on a copy of it; a zero g (and x in
+    // the products) keeps them out of the lane sums of dB and dC.
+#pragma unroll
+    for (int t = 0; t < VT; ++t) gv[t] = active ? gs[t][lane] : 0.0f;
     float hs[NS][VT], ab[NS][VT];
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
-      float hc = a.ckpt[((c * a.batch + b) * N + w * NS + j) * a.dim + d];
+      float hc = hck[j];
 #pragma unroll
       for (int t = 0; t < VT; ++t) {
         ab[j][t] = exp2_hw(A2[j] * dlv[t]);
@@ -1336,46 +1375,11 @@ __global__ __launch_bounds__(64 * S) void scan_bwd_kernel(BwdArgs a) {
       float ps = U::elem(Ct[0][t / kChunk], t % kChunk) * hs[0][t];
 #pragma unroll
       for (int j = 1; j < NS; ++j) ps = __builtin_fmaf(U::elem(Ct[j][t / kChunk], t % kChunk), hs[j][t], ps);
-      part[w][t][lane] = make_float2(ps, 0.0f);
+      pch[w][t][lane] = ps;
     }
-    lds_barrier();
-    // ---- P2
-    if (acw) {
-      uint32_t zw[PW];
 #pragma unroll
-      for (int t = 0; t < TS; ++t) {
-        const int tt = w * TS + t;
-        float sv = part[0][tt][lane].x;
-#pragma unroll
-        for (int s2 = 1; s2 < S; ++s2) sv += part[s2][tt][lane].x;
-        const float ut = LI::elem(qu, t);
-        sv = __builtin_fmaf(Dd, ut, sv);
-        const float dyv = LI::elem(qy, t);
-        float g = dyv;
-        if constexpr (kZ) {
-          const float zt = LI::elem(qz, t);
-          const float sg = sigmoid_f32(zt);
-          const float dzt = dyv * sv * sg * (1.0f + zt * (1.0f - sg));
-          g = dyv * (zt * sg);
-          if constexpr (sizeof(IoT) == 4) {
-            zw[t] = __float_as_uint(dzt);
-          } else if (t & 1) {
-            zw[t / 2] = Io<bf16_t>::pack2(__uint_as_float(zw[t / 2]), dzt);
-          } else {
-            zw[t / 2] = __float_as_uint(dzt);
-          }
-        }
-        dD_acc = __builtin_fmaf(g, ut, dD_acc);
-        g4[t] = g;
-        gs[tt][lane] = g;
-      }
-      if (kZ && dzr && active) PI::store(dzr + l + w * TS, zw);
-    }
-    lds_barrier();
-    // ---- P3: this wave's states backwards over the tile, one sub-chunk at a time
-    float gv[VT];
-#pragma unroll
-    for (int t = 0; t < VT; ++t) gv[t] = gs[t][lane];
+    for (int t = 0; t < VT; ++t) xv[t] = active ? xv[t] : 0.0f;
+    // ---- P2: this wave's states backwards over the tile, one sub-chunk at a time
 #pragma unroll
     for (int k = KV - 1; k >= 0; --k) {
       float pv[NV];
@@ -1388,18 +1392,18 @@ __global__ __launch_bounds__(64 * S) void scan_bwd_kernel(BwdArgs a) {
           const float cv = U::elem(Ct[j][k], t);
           const float bv = U::elem(Bt[j][k], t);
           const float lam = __builtin_fmaf(gv[tt], cv, carry[j]);
-          pv[j * kChunk + t] = active ? lam * xv[tt] : 0.0f;
-          pv[NS * kChunk + j * kChunk + t] = active ? gv[tt] * hs[j][tt] : 0.0f;
-          const float q = __builtin_fmaf(-bv, xv[tt], hs[j][tt]);  // Abar_t h_{t-1}
+          pv[j * kChunk + t] = lam * xv[tt];
+          pv[NS * kChunk + j * kChunk + t] = gv[tt] * hs[j][tt];
+          const float q = __builtin_fmaf(-bv, xv[tt], hs[j][tt]);  // Abar_t h_{t-1} (active lanes)
+          const float m = lam * q;
           sB = __builtin_fmaf(lam, bv, sB);
-          sA = __builtin_fmaf(lam * Af[j], q, sA);
-          dA_acc[j] = __builtin_fmaf(lam * dlv[tt], q, dA_acc[j]);
+          sA = __builtin_fmaf(m, Af[j], sA);
+          dA_acc[j] = __builtin_fmaf(m, dlv[tt], dA_acc[j]);
           carry[j] = ab[j][tt] * lam;
         }
         part[w][tt][lane] = make_float2(sA, sB);
       }
-      // Sum the products over the wave's 64 channels (lanes past the last
-      // channel run on a copy of it and contribute zero).
+      // Sum the products over the wave's 64 channels.
       const float tot = wave_sum_spread<NV>(pv, lane);
       const int i = lane % NV;
       const int which = i / (NS * kChunk), jj = (i % (NS * kChunk)) / kChunk, t = i % kChunk;
@@ -1409,15 +1413,18 @@ __global__ __launch_bounds__(64 * S) void scan_bwd_kernel(BwdArgs a) {
       }
     }
     lds_barrier();
-    // ---- P4
+    // ---- P3: the pre-gate output (for dz) and the partials of P2 (for du,
+    // ddelta), summed over the waves in order.
     if (acw) {
-      uint32_t uw[PW], dw[PW];
+      uint32_t uw[PW], dw[PW], zw[PW];
 #pragma unroll
       for (int t = 0; t < TS; ++t) {
         const int tt = w * TS + t;
+        float sv = pch[0][tt][lane];
         float2 acc = part[0][tt][lane];
 #pragma unroll
         for (int s2 = 1; s2 < S; ++s2) {
+          sv += pch[s2][tt][lane];
           const float2 v = part[s2][tt][lane];
           acc.x += v.x;
           acc.y += v.y;
@@ -1427,25 +1434,46 @@ __global__ __launch_bounds__(64 * S) void scan_bwd_kernel(BwdArgs a) {
         const float duv = __builtin_fmaf(dlv4[t], acc.y, g4[t] * Dd);
         const float ddv = dstep * sgd4[t];
         dbias_acc += ddv;
+        float dzt = 0.0f;
+        if constexpr (kZ) {
+          sv = __builtin_fmaf(Dd, ut, sv);
+          const float zt = LI::elem(qz, t), sg = sgz4[t];
+          dzt = LI::elem(qy, t) * sv * sg * (1.0f + zt * (1.0f - sg));
+        }
         if constexpr (sizeof(IoT) == 4) {
           uw[t] = __float_as_uint(duv);
           dw[t] = __float_as_uint(ddv);
+          zw[t] = __float_as_uint(dzt);
         } else if (t & 1) {
           uw[t / 2] = Io<bf16_t>::pack2(__uint_as_float(uw[t / 2]), duv);
           dw[t / 2] = Io<bf16_t>::pack2(__uint_as_float(dw[t / 2]), ddv);
+          zw[t / 2] = Io<bf16_t>::pack2(__uint_as_float(zw[t / 2]), dzt);
         } else {
           uw[t / 2] = __float_as_uint(duv);
           dw[t / 2] = __float_as_uint(ddv);
+          zw[t / 2] = __float_as_uint(dzt);
         }
       }
       if (active) {
         PI::store(dur + l + w * TS, uw);
         PI::store(ddr + l + w * TS, dw);
+        if (kZ && dzr) PI::store(dzr + l + w * TS, zw);
       }
     }
+    // The prefetched inputs become the current ones.
+#pragma unroll
+    for (int q = 0; q < PW; ++q) {
+      qu[q] = nqu[q];
+      qd[q] = nqd[q];
+      if constexpr (kZ) qz[q] = nqz[q];
+      qy[q] = nqy[q];
+    }
+#pragma unroll
+    for (int j = 0; j < NS; ++j) hck[j] = nhck[j];
   };
 
   const int64_t ntiles = (L + T - 1) / T;
+  load_tile(ntiles - 1, qu, qd, qz, qy, hck);
   for (int64_t c = ntiles - 1; c >= 0; --c) {
     if (L - c * T >= T)
       tile(c, std::integral_constant<int, KT>{});
