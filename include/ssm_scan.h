@@ -13,7 +13,8 @@
  *
  * ssm_scan_fwd_ex and ssm_state_update_ex are the first two with a choice of
  * how B is discretized (Delta * B, or exact zero-order hold), and
- * ssm_scan_fwd_complex is the prefill scan with a complex diagonal A.
+ * ssm_scan_fwd_complex and ssm_state_update_complex are the prefill scan and
+ * the decode step with a complex diagonal A.
  *
  * What is computed (for every batch row b and channel d independently):
  *
@@ -67,7 +68,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 5
+#define SSM_ABI_VERSION 6
 
 struct ihipStream_t; /* the same incomplete type as HIP's hipStream_t */
 
@@ -288,6 +289,28 @@ ssm_status_t ssm_scan_fwd_complex(int64_t batch, int64_t dim, int64_t dstate, in
                                   const void* u, const void* delta, const float* A, const void* B, const void* C,
                                   const float* D, const void* z, const float* delta_bias, int softplus_flag,
                                   const float* h0, void* y, float* last_state, struct ihipStream_t* stream);
+
+/*
+ * ssm_state_update_complex -- one decode step with a complex diagonal A: the
+ * recurrence of ssm_scan_fwd_complex for a single token, the state updated in
+ * place.  Equals ssm_scan_fwd_complex with seqlen = 1 and h0 = last_state =
+ * state.
+ *
+ *   state      [batch, dim, dstate, 2]  fp32   read, then overwritten
+ *   u, delta   [batch, dim]             io
+ *   A          [dim, dstate, 2]         fp32
+ *   B, C       [batch, dstate, 2]       io
+ *   D, z, delta_bias, y: as ssm_state_update
+ *
+ * dstate counts complex states, 1..8 (above 8 is SSM_ERR_DSTATE_UNSUPPORTED).
+ * Errors as ssm_state_update.  Any dstate and element alignment runs; 2, 4
+ * and 8 with 16-byte aligned state and A (8-byte B and C in bf16, 16-byte in
+ * fp32) take the vector kernel.
+ */
+ssm_status_t ssm_state_update_complex(int64_t batch, int64_t dim, int64_t dstate, ssm_dtype_t io, float* state,
+                                      const void* u, const void* delta, const float* A, const void* B, const void* C,
+                                      const float* D, const void* z, const float* delta_bias, int softplus_flag,
+                                      void* y, struct ihipStream_t* stream);
 
 /* Kernel paths of ssm_scan_fwd (reported by ssm_scan_fwd_plan). */
 typedef enum {

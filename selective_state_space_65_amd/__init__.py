@@ -7,8 +7,8 @@ The binding is imported lazily so that `inputs` (the seeded synthetic-input
 generators) can be used without the library.
 """
 
-__all__ = ["scan_fwd", "scan_fwd_ex", "scan_fwd_complex", "conv_scan_fwd", "scan_bwd", "state_update", "state_update_ex", "scan_plan",
-           "SsmError"]
+__all__ = ["scan_fwd", "scan_fwd_ex", "scan_fwd_complex", "conv_scan_fwd", "scan_bwd", "state_update", "state_update_ex",
+           "state_update_complex", "scan_plan", "SsmError"]
 
 
 def __getattr__(name):

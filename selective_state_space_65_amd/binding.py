@@ -42,6 +42,7 @@ SIGNATURES = {
     "ssm_scan_fwd_ex": (_I, [_I64, _I64, _I64, _I64, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P]),
     "ssm_state_update_ex": (_I, [_I64, _I64, _I64, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P]),
     "ssm_scan_fwd_complex": (_I, [_I64, _I64, _I64, _I64, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P]),
+    "ssm_state_update_complex": (_I, [_I64, _I64, _I64, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P]),
     "ssm_conv_scan_fwd": (_I, [_I64, _I64, _I64, _I64, _I64, _I, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _I, _P,
                                _P, _P, _P, _P]),
     "ssm_scan_bwd": (_I, [_I64, _I64, _I64, _I64, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P,
@@ -258,6 +259,43 @@ def scan_fwd_complex(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_s
                                   _ptr(out), _ptr(last_state), _stream(dev, stream))
     _check("ssm_scan_fwd_complex", st)
     return out, last_state
+
+
+def state_update_complex(state, u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=False, out=None,
+                         stream=None):
+    """One decode step with complex A (ssm_state_update_complex), state updated in place; returns y (batch, dim).
+
+    state (batch, dim, dstate, 2) float32; A (dim, dstate, 2) float32; B, C
+    (batch, dstate, 2) in the io dtype; u, delta, z (batch, dim).
+    """
+    import torch
+    if state.dim() != 4 or state.shape[-1] != 2:
+        raise ValueError("state must be (batch, dim, dstate, 2)")
+    batch, dim, dstate, _ = state.shape
+    dev = state.device
+    io = u.dtype
+    _need(state, "state", (batch, dim, dstate, 2), torch.float32, dev)
+    _need(u, "u", (batch, dim), io, dev)
+    _need(delta, "delta", (batch, dim), io, dev)
+    _need(A, "A", (dim, dstate, 2), torch.float32, dev)
+    _need(B, "B", (batch, dstate, 2), io, dev)
+    _need(C, "C", (batch, dstate, 2), io, dev)
+    if D is not None:
+        _need(D, "D", (dim,), torch.float32, dev)
+    if z is not None:
+        _need(z, "z", (batch, dim), io, dev)
+    if delta_bias is not None:
+        _need(delta_bias, "delta_bias", (dim,), torch.float32, dev)
+    if out is None:
+        out = torch.empty((batch, dim), dtype=io, device=dev)
+    else:
+        _need(out, "out", (batch, dim), io, dev)
+    lib = load_library()
+    st = lib.ssm_state_update_complex(batch, dim, dstate, _io_code(io), _ptr(state), _ptr(u), _ptr(delta), _ptr(A),
+                                      _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias), 1 if delta_softplus else 0,
+                                      _ptr(out), _stream(dev, stream))
+    _check("ssm_state_update_complex", st)
+    return out
 
 
 def conv_scan_fwd(x, conv_weight, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=False,

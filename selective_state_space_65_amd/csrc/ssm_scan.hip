@@ -1696,6 +1696,88 @@ __global__ __launch_bounds__(kBlockThreads) void state_update_generic_kernel(Upd
   Io<IoT>::store1(static_cast<IoT*>(a.y) + ch, epilogue<kZ>(acc, a.D ? a.D[d] : 0.0f, uv, zv));
 }
 
+// Complex A, one decode step (the recurrence of the single-pass kernel's
+// complex variant for one token): NC/2 lanes per channel, two complex states
+// (four floats, (re, im) pairs) per lane, so state, A, B and C rows are read
+// and written as whole vectors.  y = 2 Re(sum C h) + D u, gated.
+template <typename IoT, int NC, bool kZ, bool kSoftplus>
+__global__ __launch_bounds__(kBlockThreads) void state_update_complex_kernel(UpdateArgs a) {
+  constexpr int kLanes = NC / 2;
+  constexpr int N = 2 * NC;  // floats per channel
+  const int64_t bd = a.batch * a.dim;
+  const int64_t tid = (int64_t)blockIdx.x * kBlockThreads + threadIdx.x;
+  const int64_t ch_raw = tid / kLanes;
+  const int q = (int)(tid % kLanes);
+  const bool active = ch_raw < bd;
+  const int64_t ch = active ? ch_raw : bd - 1;
+  const int64_t b = ch / a.dim, d = ch % a.dim;
+
+  float h[4], A4[4], B4[4], C4[4];
+  Io<float>::load4(a.state + ch * N + 4 * q, h);
+  Io<float>::load4(a.A + d * N + 4 * q, A4);
+  Io<IoT>::load4(static_cast<const IoT*>(a.B) + b * N + 4 * q, B4);
+  Io<IoT>::load4(static_cast<const IoT*>(a.C) + b * N + 4 * q, C4);
+  const float uv = Io<IoT>::load1(static_cast<const IoT*>(a.u) + ch);
+  const float dl = discretize_delta<kSoftplus>(Io<IoT>::load1(static_cast<const IoT*>(a.delta) + ch),
+                                               a.bias ? a.bias[d] : 0.0f);
+  const float xl = dl * uv;
+  float acc = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const float mag = exp2_hw(A4[2 * j] * kLog2e * dl);
+    const float turn = __builtin_amdgcn_fractf(A4[2 * j + 1] * kInv2Pi * dl);
+    const float pr = mag * __builtin_amdgcn_cosf(turn), pi = mag * __builtin_amdgcn_sinf(turn);
+    const float hr = h[2 * j], hi = h[2 * j + 1];
+    const float nr = __builtin_fmaf(pr, hr, __builtin_fmaf(-pi, hi, B4[2 * j] * xl));
+    const float ni = __builtin_fmaf(pr, hi, __builtin_fmaf(pi, hr, B4[2 * j + 1] * xl));
+    h[2 * j] = nr;
+    h[2 * j + 1] = ni;
+    acc = __builtin_fmaf(C4[2 * j], nr, __builtin_fmaf(-C4[2 * j + 1], ni, acc));
+  }
+#pragma unroll
+  for (int off = 1; off < kLanes; off <<= 1) acc += __shfl_xor(acc, off, kLanes);
+  if (active) {
+    *reinterpret_cast<float4*>(a.state + ch * N + 4 * q) = make_float4(h[0], h[1], h[2], h[3]);
+    if (q == 0) {
+      float zv = kZ ? Io<IoT>::load1(static_cast<const IoT*>(a.z) + ch) : 0.0f;
+      Io<IoT>::store1(static_cast<IoT*>(a.y) + ch, epilogue<kZ>(2.0f * acc, a.D ? a.D[d] : 0.0f, uv, zv));
+    }
+  }
+}
+
+// Complex A, any number of complex states up to 8 and any element alignment:
+// one lane per channel, scalar loads.
+template <typename IoT, bool kZ, bool kSoftplus>
+__global__ __launch_bounds__(kBlockThreads) void state_update_complex_generic_kernel(UpdateArgs a, int64_t nc) {
+  const int64_t bd = a.batch * a.dim;
+  const int64_t ch = (int64_t)blockIdx.x * kBlockThreads + threadIdx.x;
+  if (ch >= bd) return;
+  const int64_t b = ch / a.dim, d = ch % a.dim;
+  const IoT* Bp = static_cast<const IoT*>(a.B) + b * 2 * nc;
+  const IoT* Cp = static_cast<const IoT*>(a.C) + b * 2 * nc;
+  const float uv = Io<IoT>::load1(static_cast<const IoT*>(a.u) + ch);
+  const float dl = discretize_delta<kSoftplus>(Io<IoT>::load1(static_cast<const IoT*>(a.delta) + ch),
+                                               a.bias ? a.bias[d] : 0.0f);
+  const float xl = dl * uv;
+  float acc = 0.0f;
+  for (int64_t n = 0; n < nc; ++n) {
+    const float ar = a.A[(d * nc + n) * 2], ai = a.A[(d * nc + n) * 2 + 1];
+    const float mag = exp2_hw(ar * kLog2e * dl);
+    const float turn = __builtin_amdgcn_fractf(ai * kInv2Pi * dl);
+    const float pr = mag * __builtin_amdgcn_cosf(turn), pi = mag * __builtin_amdgcn_sinf(turn);
+    float* hp = a.state + (ch * nc + n) * 2;
+    const float hr = hp[0], hi = hp[1];
+    const float br = Io<IoT>::load1(Bp + 2 * n), bi = Io<IoT>::load1(Bp + 2 * n + 1);
+    const float nr = __builtin_fmaf(pr, hr, __builtin_fmaf(-pi, hi, br * xl));
+    const float ni = __builtin_fmaf(pr, hi, __builtin_fmaf(pi, hr, bi * xl));
+    hp[0] = nr;
+    hp[1] = ni;
+    acc = __builtin_fmaf(Io<IoT>::load1(Cp + 2 * n), nr, __builtin_fmaf(-Io<IoT>::load1(Cp + 2 * n + 1), ni, acc));
+  }
+  float zv = kZ ? Io<IoT>::load1(static_cast<const IoT*>(a.z) + ch) : 0.0f;
+  Io<IoT>::store1(static_cast<IoT*>(a.y) + ch, epilogue<kZ>(2.0f * acc, a.D ? a.D[d] : 0.0f, uv, zv));
+}
+
 // ----------------------------------------------------------------------------
 // Host side: validation, planning, dispatch
 // ----------------------------------------------------------------------------
@@ -2027,6 +2109,31 @@ hipError_t launch_update(const UpdateArgs& a, hipStream_t st, bool generic, bool
     case 16: return launch_update_n<IoT, 16>(a, st, generic, sp);
     default: return launch_update_n<IoT, 4>(a, st, true, sp);
   }
+}
+
+template <typename IoT, bool kZ, bool kSp>
+hipError_t launch_update_cplx_t(const UpdateArgs& a, int64_t nc, hipStream_t st, bool generic) {
+  const int64_t bd = a.batch * a.dim;
+  if (generic) {
+    hipLaunchKernelGGL((state_update_complex_generic_kernel<IoT, kZ, kSp>),
+                       dim3((unsigned)((bd + kBlockThreads - 1) / kBlockThreads)), dim3(kBlockThreads), 0, st, a, nc);
+    return hipGetLastError();
+  }
+  const int64_t threads = bd * (nc / 2);
+  const dim3 grid((unsigned)((threads + kBlockThreads - 1) / kBlockThreads));
+  if (nc == 2) hipLaunchKernelGGL((state_update_complex_kernel<IoT, 2, kZ, kSp>), grid, dim3(kBlockThreads), 0, st, a);
+  else if (nc == 4) hipLaunchKernelGGL((state_update_complex_kernel<IoT, 4, kZ, kSp>), grid, dim3(kBlockThreads), 0, st, a);
+  else hipLaunchKernelGGL((state_update_complex_kernel<IoT, 8, kZ, kSp>), grid, dim3(kBlockThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+template <typename IoT>
+hipError_t launch_update_cplx(const UpdateArgs& a, int64_t nc, hipStream_t st, bool generic, bool sp) {
+  if (a.z)
+    return sp ? launch_update_cplx_t<IoT, true, true>(a, nc, st, generic)
+              : launch_update_cplx_t<IoT, true, false>(a, nc, st, generic);
+  return sp ? launch_update_cplx_t<IoT, false, true>(a, nc, st, generic)
+            : launch_update_cplx_t<IoT, false, false>(a, nc, st, generic);
 }
 
 }  // namespace
@@ -2368,14 +2475,17 @@ ssm_status_t ssm_scan_bwd(int64_t batch, int64_t dim, int64_t dstate, int64_t se
   return SSM_OK;
 }
 
-ssm_status_t ssm_state_update_ex(int64_t batch, int64_t dim, int64_t dstate, ssm_dtype_t io, ssm_disc_t disc,
-                                 float* state, const void* u, const void* delta, const float* A, const void* B,
+// Host-side checks shared by the decode entry points (slots: floats of state
+// per channel, dstate or twice the complex dstate).
+static ssm_status_t check_update(int64_t batch, int64_t dim, int64_t slots, ssm_dtype_t io, Shape* out,
+                                 const float* state, const void* u, const void* delta, const float* A, const void* B,
                                  const void* C, const float* D, const void* z, const float* delta_bias,
-                                 int softplus_flag, void* y, struct ihipStream_t* stream) {
-  Shape sh;
-  ssm_status_t st = shape_of(batch, dim, dstate, 1, io, &sh);
+                                 const void* y) {
+  Shape& sh = *out;
+  ssm_status_t st = shape_of(batch, dim, slots, 1, io, &sh);
   if (st != SSM_OK) return st;
   if (!state || !u || !delta || !A || !B || !C || !y) return SSM_ERR_NULL;
+  const int64_t dstate = slots;
   const size_t es = io_size(io);
   const void* io_ptrs[] = {u, delta, B, C, z, y};
   for (const void* p : io_ptrs)
@@ -2395,7 +2505,16 @@ ssm_status_t ssm_state_update_ex(int64_t batch, int64_t dim, int64_t dstate, ssm
     if (r.hi <= r.lo) continue;
     if (overlap(ry, r) || overlap(rs, r)) return SSM_ERR_ALIAS;
   }
+  return SSM_OK;
+}
 
+ssm_status_t ssm_state_update_ex(int64_t batch, int64_t dim, int64_t dstate, ssm_dtype_t io, ssm_disc_t disc,
+                                 float* state, const void* u, const void* delta, const float* A, const void* B,
+                                 const void* C, const float* D, const void* z, const float* delta_bias,
+                                 int softplus_flag, void* y, struct ihipStream_t* stream) {
+  Shape sh;
+  ssm_status_t st = check_update(batch, dim, dstate, io, &sh, state, u, delta, A, B, C, D, z, delta_bias, y);
+  if (st != SSM_OK) return st;
   if (disc != SSM_DISC_DELTA_B && disc != SSM_DISC_ZOH) return SSM_ERR_UNSUPPORTED;
   UpdateArgs a;
   a.state = state; a.u = u; a.delta = delta; a.A = A; a.B = B; a.C = C; a.D = D; a.z = z; a.bias = delta_bias;
@@ -2406,6 +2525,28 @@ ssm_status_t ssm_state_update_ex(int64_t batch, int64_t dim, int64_t dstate, ssm
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   const bool sp = softplus_flag != 0;
   hipError_t e = (io == SSM_BF16) ? launch_update<bf16_t>(a, hs, generic, sp) : launch_update<float>(a, hs, generic, sp);
+  if (e != hipSuccess) return hip_fail(e);
+  return SSM_OK;
+}
+
+ssm_status_t ssm_state_update_complex(int64_t batch, int64_t dim, int64_t dstate, ssm_dtype_t io, float* state,
+                                      const void* u, const void* delta, const float* A, const void* B, const void* C,
+                                      const float* D, const void* z, const float* delta_bias, int softplus_flag,
+                                      void* y, struct ihipStream_t* stream) {
+  const int64_t slots = dstate < 1 ? dstate : (dstate > 8 ? 17 : 2 * dstate);
+  Shape sh;
+  ssm_status_t st = check_update(batch, dim, slots, io, &sh, state, u, delta, A, B, C, D, z, delta_bias, y);
+  if (st != SSM_OK) return st;
+  UpdateArgs a;
+  a.state = state; a.u = u; a.delta = delta; a.A = A; a.B = B; a.C = C; a.D = D; a.z = z; a.bias = delta_bias;
+  a.y = y; a.batch = batch; a.dim = dim; a.dstate = slots; a.zoh = 0;
+  const size_t bc_align = (io == SSM_BF16) ? 8 : 16;
+  const bool generic = !(dstate == 2 || dstate == 4 || dstate == 8) || !aligned(state, 16) || !aligned(A, 16) ||
+                       !aligned(B, bc_align) || !aligned(C, bc_align);
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  const bool sp = softplus_flag != 0;
+  hipError_t e = (io == SSM_BF16) ? launch_update_cplx<bf16_t>(a, dstate, hs, generic, sp)
+                                  : launch_update_cplx<float>(a, dstate, hs, generic, sp);
   if (e != hipSuccess) return hip_fail(e);
   return SSM_OK;
 }

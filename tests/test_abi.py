@@ -181,6 +181,25 @@ def test_complex_validation(lib):
     assert cplx(lib, batch=192, dim=64, seqlen=12) == 8
 
 
+def cupd(lib, batch=2, dim=8, dstate=4, io=0, **over):
+    args = dict(state=addr(1), u=addr(2), delta=addr(3), A=addr(4), B=addr(5), C=addr(6), D=addr(7), z=addr(8),
+                bias=addr(9), sp=1, y=addr(10))
+    args.update(over)
+    return lib.ssm_state_update_complex(batch, dim, dstate, io, args["state"], args["u"], args["delta"], args["A"],
+                                        args["B"], args["C"], args["D"], args["z"], args["bias"], args["sp"], args["y"],
+                                        None)
+
+
+def test_complex_update_validation(lib):
+    assert cupd(lib, state=None) == 1
+    assert cupd(lib, dim=0) == 2
+    assert cupd(lib, dstate=9) == 3
+    assert cupd(lib, io=4) == 4
+    assert cupd(lib, A=addr(4) + 1) == 5
+    assert cupd(lib, y=addr(1) + 64) == 6            # y inside the state (2 x 8 x 4 x 2 floats)
+    assert cupd(lib, u=addr(1) + 2 * 8 * 4 * 2 * 4 - 4) == 6   # u overlapping the state's last float
+
+
 def cfwd(lib, batch=2, dim=8, dstate=4, seqlen=16, width=4, io=0, **over):
     args = dict(x=addr(1), w=addr(12), cb=addr(13), xp=addr(14), silu=1, delta=addr(2), A=addr(3), B=addr(4),
                 C=addr(5), D=addr(6), z=addr(7), bias=addr(8), sp=1, h0=addr(9), y=addr(10), last=addr(11),

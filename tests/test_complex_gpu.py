@@ -169,3 +169,58 @@ def test_complex_unsupported_shapes():
         with pytest.raises(binding.SsmError) as e:
             run(x, A, B, C, hh)
         assert e.value.name == "SSM_ERR_UNSUPPORTED"
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("dstate", [8, 2, 3])
+def test_complex_decode(io, dstate):
+    """ssm_state_update_complex over 5 steps against the oracle's one-token complex scan
+    (dstate 3 takes the generic kernel)."""
+    batch, dim, steps = 8, 96, 5
+    rng = np.random.default_rng(4600 + dstate)
+    x, A, _, _, _ = complex_inputs(batch, dim, dstate, 8, io, 4600 + dstate)
+    state = (0.1 * rng.standard_normal((batch, dim, dstate, 2))).astype(np.float32)
+    st_gpu = torch.from_numpy(state).to(DEV)
+    st_ref = cplx(state)
+    dt = torch.float32 if io == "f32" else torch.bfloat16
+    At = torch.from_numpy(A).to(DEV)
+    Dt = torch.from_numpy(x.D).to(DEV)
+    bt = torch.from_numpy(x.delta_bias).to(DEV)
+    for s in range(steps):
+        say("complex decode io=%s dstate=%d step=%d" % (io, dstate, s))
+        r = np.random.default_rng([4601, dstate, s])
+        f = dict(u=r.standard_normal((batch, dim)), delta=0.5 * r.standard_normal((batch, dim)),
+                 z=r.standard_normal((batch, dim)), B=r.standard_normal((batch, dstate, 2)),
+                 C=r.standard_normal((batch, dstate, 2)))
+        f = {k: v.astype(np.float32) for k, v in f.items()}
+        if io == "bf16":
+            f = {k: inputs.round_bf16(v) for k, v in f.items()}
+        tt = {k: torch.from_numpy(v).to(DEV, dt) for k, v in f.items()}
+        y = binding.state_update_complex(st_gpu, tt["u"], tt["delta"], At, tt["B"], tt["C"], D=Dt, z=tt["z"],
+                                         delta_bias=bt, delta_softplus=True)
+        torch.cuda.synchronize()
+        yr, hr = oracle.scan_complex_f64(f["u"][..., None], f["delta"][..., None], cplx(A), cplx(f["B"])[..., None],
+                                         cplx(f["C"])[..., None], x.D, f["z"][..., None], x.delta_bias, True, st_ref)
+        st_ref = hr
+        check(np64(y), yr[..., 0], TOL[io], "y step %d" % s)
+        check(np64(st_gpu), np.stack([hr.real, hr.imag], -1), TOL["f32"], "state step %d" % s)
+
+
+def test_complex_decode_steps_equal_scan():
+    """Eight decode steps equal an eight-token complex scan (single-pass kernel) on the same inputs."""
+    b, d, n, l = 192, 64, 8, 8
+    x, A, B, C, hh = complex_inputs(b, d, n, l, "f32", 4700)
+    y_scan, last = run(x, A, B, C, hh)
+    st = torch.from_numpy(hh).to(DEV)
+    t = inputs.to_torch(x, DEV)
+    At = torch.from_numpy(A).to(DEV)
+    ys = []
+    for s in range(l):
+        ys.append(binding.state_update_complex(st, t["u"][..., s].contiguous(), t["delta"][..., s].contiguous(), At,
+                                               torch.from_numpy(np.ascontiguousarray(B[:, :, s])).to(DEV),
+                                               torch.from_numpy(np.ascontiguousarray(C[:, :, s])).to(DEV), D=t["D"],
+                                               z=t["z"][..., s].contiguous(), delta_bias=t["delta_bias"],
+                                               delta_softplus=True))
+    torch.cuda.synchronize()
+    check(np64(torch.stack(ys, -1)), np64(y_scan), 1e-5, "y")
+    check(np64(st), np64(last), 1e-5, "state")
