@@ -269,11 +269,35 @@ def bench_backward(dev, x, t, steps, warmup):
     nbytes = 4 * el * io_bytes + 2 * b * n * l * io_bytes + d * n * 4 + 2 * d * 4 + 3 * el * io_bytes \
         + 2 * b * n * l * 4 + d * n * 4 + 2 * d * 4
     slots = BWD_SLOTS_PER_ELEM_STATE * el * n
-    return dict(workload="ssm_scan_bwd (every gradient), same shape and flags", us_per_call=round(avg_ms * 1e3, 2),
-                us_median=round(med_ms * 1e3, 2), algorithmic_gbs=round(nbytes / (avg_ms * 1e-3) / 1e9, 1),
-                algorithmic_bytes=nbytes, alu_frac=round(slots / (avg_ms * 1e-3) / LANE_SLOTS_PEAK, 4),
-                lane_slots_per_elem_state=BWD_SLOTS_PER_ELEM_STATE,
-                vs_forward=None)
+    out = dict(workload="ssm_scan_bwd (every gradient), same shape and flags", us_per_call=round(avg_ms * 1e3, 2),
+               us_median=round(med_ms * 1e3, 2), algorithmic_gbs=round(nbytes / (avg_ms * 1e-3) / 1e9, 1),
+               algorithmic_bytes=nbytes, alu_frac=round(slots / (avg_ms * 1e-3) / LANE_SLOTS_PEAK, 4),
+               lane_slots_per_elem_state=BWD_SLOTS_PER_ELEM_STATE,
+               vs_forward=None)
+    # A training step with the forward's checkpoints kept for the backward:
+    # ssm_scan_fwd_save, then ssm_scan_bwd_saved (no recompute pass).
+    from selective_state_space_65_amd import binding as _b
+    try:
+        y = torch.empty_like(t["u"])
+        last = torch.empty((b, d, n), dtype=torch.float32, device=dev)
+        ck = torch.empty(_b.ckpt_shape(b, d, n, l), dtype=torch.float32, device=dev)
+
+        def fwd_save():
+            binding.scan_fwd_save(t["u"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
+                                  delta_bias=t["delta_bias"], delta_softplus=x.softplus, out=y, last_state=last, ckpt=ck)
+
+        def bwd_saved():
+            binding.scan_bwd_saved(t["u"], t["delta"], t["A"], t["B"], t["C"], dy, ck, D=t["D"], z=t["z"],
+                                   delta_bias=t["delta_bias"], delta_softplus=x.softplus)
+
+        _, fs_ms, _ = time_calls(fwd_save, steps, warmup)
+        _, bs_ms, _ = time_calls(bwd_saved, steps, warmup)
+        out["saved_checkpoints"] = dict(fwd_save_us=round(fs_ms * 1e3, 2), bwd_saved_us=round(bs_ms * 1e3, 2),
+                                        training_step_us=round((fs_ms + bs_ms) * 1e3, 2),
+                                        checkpoint_mb=round(ck.numel() * 4 / 1e6, 1))
+    except _b.SsmError as e:
+        out["saved_checkpoints"] = dict(skipped=str(e))
+    return out
 
 
 def main():
@@ -368,6 +392,9 @@ def main():
     if not args.no_backward:
         bw = bench_backward(dev, x, t, max(3, args.steps // 4), 2)
         bw["vs_forward"] = round(bw["us_per_call"] / (avg_ms * 1e3), 2)
+        sc = bw.get("saved_checkpoints", {})
+        if "training_step_us" in sc:
+            sc["recompute_training_step_us"] = round(avg_ms * 1e3 + bw["us_per_call"], 2)
         out["backward"] = bw
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(x, args.cpu_seconds)

@@ -68,7 +68,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 6
+#define SSM_ABI_VERSION 7
 
 struct ihipStream_t; /* the same incomplete type as HIP's hipStream_t */
 
@@ -311,6 +311,44 @@ ssm_status_t ssm_state_update_complex(int64_t batch, int64_t dim, int64_t dstate
                                       const void* u, const void* delta, const float* A, const void* B, const void* C,
                                       const float* D, const void* z, const float* delta_bias, int softplus_flag,
                                       void* y, struct ihipStream_t* stream);
+
+/*
+ * Training without the backward's forward pass.  ssm_scan_bwd recomputes the
+ * forward to obtain the states at every 16th token (its checkpoints).  A
+ * training step runs the forward anyway: ssm_scan_fwd_save is ssm_scan_fwd
+ * that also writes those checkpoints, and ssm_scan_bwd_saved is ssm_scan_bwd
+ * that reads them instead of recomputing them.  The checkpoints hold fp32
+ * states laid out [ceil(seqlen/16)][batch][dstate][dim] (the state before
+ * tokens 0, 16, 32, ...), ssm_scan_ckpt_bytes bytes; the caller owns the
+ * buffer and must pass the same u, delta, A, B, C, D, z, delta_bias, flags and
+ * h0 to both calls (ssm_scan_bwd_saved does not read h0: the checkpoints
+ * carry it).  Results equal ssm_scan_fwd and ssm_scan_bwd bit for bit on
+ * shapes where ssm_scan_fwd takes the single-pass kernel.
+ *
+ * ssm_scan_ckpt_bytes: bytes of the checkpoint buffer; errors as ssm_scan_fwd's
+ *   size checks.  bytes may be NULL.
+ * ssm_scan_fwd_save: arguments of ssm_scan_fwd plus ckpt (written; may overlap
+ *   no input or output).  Supported shapes are those of ssm_scan_bwd (dstate in
+ *   {4, 8, 16}, seqlen a multiple of 8, 16-byte aligned rows, y included);
+ *   others return SSM_ERR_UNSUPPORTED.  It always runs the single-pass kernel.
+ * ssm_scan_bwd_saved: arguments of ssm_scan_bwd with ckpt (read) in place of
+ *   h0; errors as ssm_scan_bwd, SSM_ERR_NULL for a NULL ckpt.
+ */
+ssm_status_t ssm_scan_ckpt_bytes(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, ssm_dtype_t io,
+                                 int64_t* bytes);
+
+ssm_status_t ssm_scan_fwd_save(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, ssm_dtype_t io,
+                               const void* u, const void* delta, const float* A, const void* B, const void* C,
+                               const float* D, const void* z, const float* delta_bias, int softplus_flag,
+                               const float* h0, void* y, float* last_state, float* ckpt,
+                               struct ihipStream_t* stream);
+
+ssm_status_t ssm_scan_bwd_saved(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, ssm_dtype_t io,
+                                const void* u, const void* delta, const float* A, const void* B, const void* C,
+                                const float* D, const void* z, const float* delta_bias, int softplus_flag,
+                                const float* ckpt, const void* dy, const float* dlast, void* du, void* ddelta,
+                                float* dA, float* dB, float* dC, float* dD, void* dz, float* ddelta_bias, float* dh0,
+                                struct ihipStream_t* stream);
 
 /* Kernel paths of ssm_scan_fwd (reported by ssm_scan_fwd_plan). */
 typedef enum {

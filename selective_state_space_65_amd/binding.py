@@ -47,6 +47,10 @@ SIGNATURES = {
                                _P, _P, _P, _P]),
     "ssm_scan_bwd": (_I, [_I64, _I64, _I64, _I64, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P,
                           _P, _P, _P, _P, _P]),
+    "ssm_scan_ckpt_bytes": (_I, [_I64, _I64, _I64, _I64, _I, ctypes.POINTER(_I64)]),
+    "ssm_scan_fwd_save": (_I, [_I64, _I64, _I64, _I64, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P]),
+    "ssm_scan_bwd_saved": (_I, [_I64, _I64, _I64, _I64, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P,
+                                _P, _P, _P, _P, _P, _P, _P]),
     "ssm_scan_fwd_plan": (_I, [_I64, _I64, _I64, _I64, _I, ctypes.POINTER(_I), ctypes.POINTER(_I64),
                               ctypes.POINTER(_I64), ctypes.POINTER(_I64)]),
     "ssm_status_string": (ctypes.c_char_p, [_I]),
@@ -361,13 +365,73 @@ def conv_scan_fwd(x, conv_weight, delta, A, B, C, D=None, z=None, delta_bias=Non
 
 def scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, delta_softplus=False, h0=None, dlast=None,
              need=("dD", "dz", "ddelta_bias", "dh0"), stream=None):
-    """Gradients of sum(dy * y) + sum(dlast * last_state) for the scan of scan_fwd.
+    """Gradients of sum(dy * y) + sum(dlast * last_state) for the scan of scan_fwd (ssm_scan_bwd).
 
     Returns a dict: du, ddelta (io dtype, like u); dA (dim, dstate), dB, dC
     (batch, dstate, seqlen) in float32; and, when named in `need`, dD and
     ddelta_bias (dim,) float32, dz (io dtype, only with z) and dh0 (batch, dim,
     dstate) float32.
     """
+    return _scan_bwd(None, u, delta, A, B, C, dy, D, z, delta_bias, delta_softplus, h0, dlast, need, stream)
+
+
+def scan_bwd_saved(u, delta, A, B, C, dy, ckpt, D=None, z=None, delta_bias=None, delta_softplus=False, dlast=None,
+                   need=("dD", "dz", "ddelta_bias", "dh0"), stream=None):
+    """scan_bwd reading the checkpoints scan_fwd_save wrote instead of re-running the forward (ssm_scan_bwd_saved)."""
+    return _scan_bwd(ckpt, u, delta, A, B, C, dy, D, z, delta_bias, delta_softplus, None, dlast, need, stream)
+
+
+def ckpt_shape(batch, dim, dstate, seqlen):
+    """Shape of the float32 checkpoint tensor of scan_fwd_save / scan_bwd_saved."""
+    return ((seqlen + 15) // 16, batch, dstate, dim)
+
+
+def scan_fwd_save(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=False, h0=None, out=None,
+                  last_state=None, ckpt=None, stream=None):
+    """scan_fwd that also writes the backward's checkpoints (ssm_scan_fwd_save); returns (y, last_state, ckpt)."""
+    import torch
+    if u.dim() != 3:
+        raise ValueError("u must be (batch, dim, seqlen)")
+    batch, dim, seqlen = u.shape
+    dstate = A.shape[-1]
+    dev = u.device
+    io = u.dtype
+    f32 = torch.float32
+    _need(u, "u", (batch, dim, seqlen), io, dev)
+    _need(delta, "delta", (batch, dim, seqlen), io, dev)
+    _need(A, "A", (dim, dstate), f32, dev)
+    _need(B, "B", (batch, dstate, seqlen), io, dev)
+    _need(C, "C", (batch, dstate, seqlen), io, dev)
+    if D is not None:
+        _need(D, "D", (dim,), f32, dev)
+    if z is not None:
+        _need(z, "z", (batch, dim, seqlen), io, dev)
+    if delta_bias is not None:
+        _need(delta_bias, "delta_bias", (dim,), f32, dev)
+    if h0 is not None:
+        _need(h0, "h0", (batch, dim, dstate), f32, dev)
+    if out is None:
+        out = torch.empty((batch, dim, seqlen), dtype=io, device=dev)
+    else:
+        _need(out, "out", (batch, dim, seqlen), io, dev)
+    if last_state is None:
+        last_state = torch.empty((batch, dim, dstate), dtype=f32, device=dev)
+    else:
+        _need(last_state, "last_state", (batch, dim, dstate), f32, dev)
+    cs = ckpt_shape(batch, dim, dstate, seqlen)
+    if ckpt is None:
+        ckpt = torch.empty(cs, dtype=f32, device=dev)
+    else:
+        _need(ckpt, "ckpt", cs, f32, dev)
+    lib = load_library()
+    st = lib.ssm_scan_fwd_save(batch, dim, dstate, seqlen, _io_code(io), _ptr(u), _ptr(delta), _ptr(A), _ptr(B),
+                               _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias), 1 if delta_softplus else 0, _ptr(h0),
+                               _ptr(out), _ptr(last_state), _ptr(ckpt), _stream(dev, stream))
+    _check("ssm_scan_fwd_save", st)
+    return out, last_state, ckpt
+
+
+def _scan_bwd(ckpt, u, delta, A, B, C, dy, D, z, delta_bias, delta_softplus, h0, dlast, need, stream):
     import torch
     if u.dim() != 3:
         raise ValueError("u must be (batch, dim, seqlen)")
@@ -392,6 +456,8 @@ def scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, delta_softp
         _need(h0, "h0", (batch, dim, dstate), f32, dev)
     if dlast is not None:
         _need(dlast, "dlast", (batch, dim, dstate), f32, dev)
+    if ckpt is not None:
+        _need(ckpt, "ckpt", ckpt_shape(batch, dim, dstate, seqlen), f32, dev)
     g = dict(du=torch.empty_like(u), ddelta=torch.empty_like(u), dA=torch.empty((dim, dstate), dtype=f32, device=dev),
              dB=torch.empty((batch, dstate, seqlen), dtype=f32, device=dev),
              dC=torch.empty((batch, dstate, seqlen), dtype=f32, device=dev),
@@ -400,11 +466,14 @@ def scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, delta_softp
              ddelta_bias=torch.empty(dim, dtype=f32, device=dev) if "ddelta_bias" in need else None,
              dh0=torch.empty((batch, dim, dstate), dtype=f32, device=dev) if "dh0" in need else None)
     lib = load_library()
-    st = lib.ssm_scan_bwd(batch, dim, dstate, seqlen, _io_code(io), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
-                          _ptr(D), _ptr(z), _ptr(delta_bias), 1 if delta_softplus else 0, _ptr(h0), _ptr(dy),
-                          _ptr(dlast), _ptr(g["du"]), _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]),
-                          _ptr(g["dD"]), _ptr(g["dz"]), _ptr(g["ddelta_bias"]), _ptr(g["dh0"]), _stream(dev, stream))
-    _check("ssm_scan_bwd", st)
+    head = (batch, dim, dstate, seqlen, _io_code(io), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+            _ptr(delta_bias), 1 if delta_softplus else 0)
+    tail = (_ptr(dy), _ptr(dlast), _ptr(g["du"]), _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]),
+            _ptr(g["dD"]), _ptr(g["dz"]), _ptr(g["ddelta_bias"]), _ptr(g["dh0"]), _stream(dev, stream))
+    if ckpt is None:
+        _check("ssm_scan_bwd", lib.ssm_scan_bwd(*head, _ptr(h0), *tail))
+    else:
+        _check("ssm_scan_bwd_saved", lib.ssm_scan_bwd_saved(*head, _ptr(ckpt), *tail))
     return g
 
 

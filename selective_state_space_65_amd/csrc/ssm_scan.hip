@@ -2384,12 +2384,14 @@ ssm_status_t ssm_conv_scan_fwd(int64_t batch, int64_t dim, int64_t dstate, int64
   return out;
 }
 
-ssm_status_t ssm_scan_bwd(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, ssm_dtype_t io,
-                          const void* u, const void* delta, const float* A, const void* B, const void* C,
-                          const float* D, const void* z, const float* delta_bias, int softplus_flag,
-                          const float* h0, const void* dy, const float* dlast, void* du, void* ddelta,
-                          float* dA, float* dB, float* dC, float* dD, void* dz, float* ddelta_bias, float* dh0,
-                          struct ihipStream_t* stream) {
+// The backward, with the checkpoints either saved by ssm_scan_fwd_save
+// (saved != null) or written by a forward pass run here first.
+static ssm_status_t scan_bwd_impl(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, ssm_dtype_t io,
+                                  const void* u, const void* delta, const float* A, const void* B, const void* C,
+                                  const float* D, const void* z, const float* delta_bias, int softplus_flag,
+                                  const float* h0, const float* saved, const void* dy, const float* dlast, void* du,
+                                  void* ddelta, float* dA, float* dB, float* dC, float* dD, void* dz,
+                                  float* ddelta_bias, float* dh0, hipStream_t hs) {
   Shape sh;
   ssm_status_t st = shape_of(batch, dim, dstate, seqlen, io, &sh);
   if (st != SSM_OK) return st;
@@ -2399,14 +2401,19 @@ ssm_status_t ssm_scan_bwd(int64_t batch, int64_t dim, int64_t dstate, int64_t se
   const void* io_ptrs[] = {u, delta, B, C, z, dy, du, ddelta, dz};
   for (const void* p : io_ptrs)
     if (p && !aligned(p, es)) return SSM_ERR_ALIGN;
-  const void* f_ptrs[] = {A, D, delta_bias, h0, dlast, dA, dB, dC, dD, ddelta_bias, dh0};
+  const void* f_ptrs[] = {A, D, delta_bias, h0, saved, dlast, dA, dB, dC, dD, ddelta_bias, dh0};
   for (const void* p : f_ptrs)
     if (p && !aligned(p, 4)) return SSM_ERR_ALIGN;
+  const int64_t ntiles = (seqlen + kCkptTokens - 1) / kCkptTokens;
+  int64_t n_ckpt;
+  if (!mul_ok(ntiles, sh.bdn, &n_ckpt) || !mul_ok(n_ckpt, 4, &n_ckpt)) return SSM_ERR_SHAPE;
+  n_ckpt /= 4;
   const int64_t bdl = sh.bdl * (int64_t)es, bnl = sh.bnl * (int64_t)es;
   const Range ins[] = {span(u, bdl), span(delta, bdl), span(A, sh.dn * 4), span(B, bnl), span(C, bnl),
                        D ? span(D, dim * 4) : Range{0, 0}, z ? span(z, bdl) : Range{0, 0},
                        delta_bias ? span(delta_bias, dim * 4) : Range{0, 0}, h0 ? span(h0, sh.bdn * 4) : Range{0, 0},
-                       span(dy, bdl), dlast ? span(dlast, sh.bdn * 4) : Range{0, 0}};
+                       span(dy, bdl), dlast ? span(dlast, sh.bdn * 4) : Range{0, 0},
+                       saved ? span(saved, n_ckpt * 4) : Range{0, 0}};
   const Range outs[] = {span(du, bdl), span(ddelta, bdl), span(dA, sh.dn * 4), span(dB, sh.bnl * 4),
                         span(dC, sh.bnl * 4), dD ? span(dD, dim * 4) : Range{0, 0}, dz ? span(dz, bdl) : Range{0, 0},
                         ddelta_bias ? span(ddelta_bias, dim * 4) : Range{0, 0},
@@ -2423,16 +2430,15 @@ ssm_status_t ssm_scan_bwd(int64_t batch, int64_t dim, int64_t dstate, int64_t se
       (dz && !aligned(dz, 16)))
     return SSM_ERR_UNSUPPORTED;
 
-  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   const Plan plan = make_plan(sh, batch, dim, dstate, seqlen, io);
   const int64_t groups = plan.groups;
-  const int64_t ntiles = (seqlen + kCkptTokens - 1) / kCkptTokens;
   const int SA = bwd_token_waves(dstate);
-  // Scratch: checkpoints, per-group dB/dC partials, per-batch dA, dD, dbias partials.
-  const int64_t n_ckpt = ntiles * sh.bdn;
+  // Scratch: checkpoints (unless saved), per-group dB/dC partials, per-batch
+  // dA, dD, dbias partials.
+  const int64_t n_own = saved ? 0 : n_ckpt;
   const int64_t n_part = groups * sh.bnl;
   const int64_t n_small = sh.bdn + 2 * batch * SA * dim;
-  const int64_t scratch_floats = n_ckpt + 2 * n_part + n_small;
+  const int64_t scratch_floats = n_own + 2 * n_part + n_small;
   hipMemPool_t pool;
   hipError_t e = get_pool(&pool);
   if (e != hipSuccess) return hip_fail(e);
@@ -2441,19 +2447,22 @@ ssm_status_t ssm_scan_bwd(int64_t batch, int64_t dim, int64_t dstate, int64_t se
   if (e != hipSuccess) return hip_fail(e);
   float* f = static_cast<float*>(scratch);
 
-  // 1. Forward with checkpoints (single-pass kernel; y goes to du, overwritten below).
-  ScanArgs fa = scan_args(sh, batch, dim, dstate, seqlen, io, u, delta, A, B, C, D, z, delta_bias, h0, du, nullptr);
-  fa.groups = groups; fa.segments = 1; fa.seg_len = seqlen;
-  fa.ckpt = f;
-  Plan fp = plan;
-  fp.split = true; fp.segments = 1; fp.seg_len = seqlen; fp.scratch_bytes = 0;
   const bool sp = softplus_flag != 0;
-  e = (io == SSM_BF16) ? launch_scan<bf16_t>(fa, fp, hs, true, sp) : launch_scan<float>(fa, fp, hs, true, sp);
+  // 1. Unless saved: the forward with checkpoints (single-pass kernel; y goes
+  //    to du, overwritten below).
+  if (!saved) {
+    ScanArgs fa = scan_args(sh, batch, dim, dstate, seqlen, io, u, delta, A, B, C, D, z, delta_bias, h0, du, nullptr);
+    fa.groups = groups; fa.segments = 1; fa.seg_len = seqlen;
+    fa.ckpt = f;
+    Plan fp = plan;
+    fp.split = true; fp.segments = 1; fp.seg_len = seqlen; fp.scratch_bytes = 0;
+    e = (io == SSM_BF16) ? launch_scan<bf16_t>(fa, fp, hs, true, sp) : launch_scan<float>(fa, fp, hs, true, sp);
+  }
   // 2. Backward over the tiles in reverse.
   BwdArgs ba;
   ba.u = u; ba.delta = delta; ba.A = A; ba.B = B; ba.C = C; ba.D = D; ba.z = z; ba.bias = delta_bias; ba.dy = dy;
-  ba.dlast = dlast; ba.ckpt = f; ba.du = du; ba.ddelta = ddelta; ba.dz = dz; ba.dh0 = dh0;
-  ba.dB_part = f + n_ckpt;
+  ba.dlast = dlast; ba.ckpt = saved ? saved : f; ba.du = du; ba.ddelta = ddelta; ba.dz = dz; ba.dh0 = dh0;
+  ba.dB_part = f + n_own;
   ba.dC_part = ba.dB_part + n_part;
   ba.dA_part = ba.dC_part + n_part;
   ba.dD_part = ba.dA_part + sh.bdn;
@@ -2471,6 +2480,83 @@ ssm_status_t ssm_scan_bwd(int64_t batch, int64_t dim, int64_t dstate, int64_t se
   }
   hipError_t ef = hipFreeAsync(scratch, hs);
   if (e == hipSuccess) e = ef;
+  if (e != hipSuccess) return hip_fail(e);
+  return SSM_OK;
+}
+
+ssm_status_t ssm_scan_bwd(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, ssm_dtype_t io,
+                          const void* u, const void* delta, const float* A, const void* B, const void* C,
+                          const float* D, const void* z, const float* delta_bias, int softplus_flag,
+                          const float* h0, const void* dy, const float* dlast, void* du, void* ddelta,
+                          float* dA, float* dB, float* dC, float* dD, void* dz, float* ddelta_bias, float* dh0,
+                          struct ihipStream_t* stream) {
+  return scan_bwd_impl(batch, dim, dstate, seqlen, io, u, delta, A, B, C, D, z, delta_bias, softplus_flag, h0, nullptr,
+                       dy, dlast, du, ddelta, dA, dB, dC, dD, dz, ddelta_bias, dh0,
+                       reinterpret_cast<hipStream_t>(stream));
+}
+
+ssm_status_t ssm_scan_bwd_saved(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, ssm_dtype_t io,
+                                const void* u, const void* delta, const float* A, const void* B, const void* C,
+                                const float* D, const void* z, const float* delta_bias, int softplus_flag,
+                                const float* ckpt, const void* dy, const float* dlast, void* du, void* ddelta,
+                                float* dA, float* dB, float* dC, float* dD, void* dz, float* ddelta_bias, float* dh0,
+                                struct ihipStream_t* stream) {
+  if (!ckpt) {
+    Shape sh;
+    ssm_status_t st = shape_of(batch, dim, dstate, seqlen, io, &sh);
+    return st != SSM_OK ? st : SSM_ERR_NULL;
+  }
+  return scan_bwd_impl(batch, dim, dstate, seqlen, io, u, delta, A, B, C, D, z, delta_bias, softplus_flag, nullptr,
+                       ckpt, dy, dlast, du, ddelta, dA, dB, dC, dD, dz, ddelta_bias, dh0,
+                       reinterpret_cast<hipStream_t>(stream));
+}
+
+ssm_status_t ssm_scan_ckpt_bytes(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, ssm_dtype_t io,
+                                 int64_t* bytes) {
+  Shape sh;
+  ssm_status_t st = shape_of(batch, dim, dstate, seqlen, io, &sh);
+  if (st != SSM_OK) return st;
+  int64_t n;
+  if (!mul_ok((seqlen + kCkptTokens - 1) / kCkptTokens, sh.bdn, &n) || !mul_ok(n, 4, &n)) return SSM_ERR_SHAPE;
+  if (bytes) *bytes = n;
+  return SSM_OK;
+}
+
+ssm_status_t ssm_scan_fwd_save(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, ssm_dtype_t io,
+                               const void* u, const void* delta, const float* A, const void* B, const void* C,
+                               const float* D, const void* z, const float* delta_bias, int softplus_flag,
+                               const float* h0, void* y, float* last_state, float* ckpt,
+                               struct ihipStream_t* stream) {
+  Shape sh;
+  ssm_status_t st = shape_of(batch, dim, dstate, seqlen, io, &sh);
+  if (st != SSM_OK) return st;
+  if (!u || !delta || !A || !B || !C || !y || !ckpt) return SSM_ERR_NULL;
+  if (!aligned(ckpt, 4)) return SSM_ERR_ALIGN;
+  int64_t ck_bytes = 0;
+  st = ssm_scan_ckpt_bytes(batch, dim, dstate, seqlen, io, &ck_bytes);
+  if (st != SSM_OK) return st;
+  // The checkpoints are an output: they may overlap no input and no other
+  // output (passing them as an extra range checks them against y and
+  // last_state; the inputs are checked here).
+  const Range ck = span(ckpt, ck_bytes);
+  st = check_scan_buffers(sh, dim, io, u, delta, A, B, C, D, z, delta_bias, h0, y, last_state, &ck, 1, nullptr);
+  if (st != SSM_OK) return st;
+  const int64_t bdl = sh.bdl * (int64_t)io_size(io), bnl = sh.bnl * (int64_t)io_size(io);
+  const Range ins[] = {span(u, bdl), span(delta, bdl), span(A, sh.dn * 4), span(B, bnl), span(C, bnl),
+                       D ? span(D, dim * 4) : Range{0, 0}, z ? span(z, bdl) : Range{0, 0},
+                       delta_bias ? span(delta_bias, dim * 4) : Range{0, 0}, h0 ? span(h0, sh.bdn * 4) : Range{0, 0}};
+  for (const Range& r : ins)
+    if (r.hi > r.lo && overlap(ck, r)) return SSM_ERR_ALIAS;
+  if (!(dstate == 4 || dstate == 8 || dstate == 16) || !vec_rows(sh, dstate, seqlen, io, u, delta, B, C, z, y))
+    return SSM_ERR_UNSUPPORTED;
+  ScanArgs a = scan_args(sh, batch, dim, dstate, seqlen, io, u, delta, A, B, C, D, z, delta_bias, h0, y, last_state);
+  Plan p = make_plan(sh, batch, dim, dstate, seqlen, io);
+  a.groups = p.groups; a.segments = 1; a.seg_len = seqlen;
+  a.ckpt = ckpt;
+  p.split = true; p.segments = 1; p.seg_len = seqlen; p.scratch_bytes = 0;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  const bool sp = softplus_flag != 0;
+  hipError_t e = (io == SSM_BF16) ? launch_scan<bf16_t>(a, p, hs, true, sp) : launch_scan<float>(a, p, hs, true, sp);
   if (e != hipSuccess) return hip_fail(e);
   return SSM_OK;
 }

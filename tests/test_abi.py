@@ -200,6 +200,38 @@ def test_complex_update_validation(lib):
     assert cupd(lib, u=addr(1) + 2 * 8 * 4 * 2 * 4 - 4) == 6   # u overlapping the state's last float
 
 
+def test_saved_checkpoint_validation(lib):
+    nb = ctypes.c_int64(0)
+    assert lib.ssm_scan_ckpt_bytes(2, 8, 4, 33, 0, ctypes.byref(nb)) == 0
+    assert nb.value == 3 * 2 * 4 * 8 * 4                      # ceil(33/16) tiles x batch x dstate x dim floats
+    assert lib.ssm_scan_ckpt_bytes(2, 8, 17, 33, 0, None) == 3
+    assert lib.ssm_scan_ckpt_bytes(0, 8, 4, 33, 0, None) == 2
+
+    def save(**over):
+        args = dict(u=addr(1), delta=addr(2), A=addr(3), B=addr(4), C=addr(5), D=addr(6), z=addr(7), bias=addr(8),
+                    h0=None, y=addr(10), last=addr(11), ck=addr(12), seqlen=16, dstate=4)
+        args.update(over)
+        return lib.ssm_scan_fwd_save(2, 8, args["dstate"], args["seqlen"], 0, args["u"], args["delta"], args["A"],
+                                     args["B"], args["C"], args["D"], args["z"], args["bias"], 1, args["h0"], args["y"],
+                                     args["last"], args["ck"], None)
+    assert save(ck=None) == 1
+    assert save(ck=addr(12) + 2) == 5
+    assert save(ck=addr(1) + 16) == 6          # checkpoints inside u
+    assert save(ck=addr(10)) == 6              # checkpoints on y
+    assert save(dstate=5) == 8                 # outside the single-pass kernel
+    assert save(seqlen=12) == 8
+
+    def saved(**over):
+        args = dict(ck=addr(12), dy=addr(13), du=addr(14), dd=addr(15), dA=addr(16), dB=addr(17), dC=addr(18))
+        args.update(over)
+        return lib.ssm_scan_bwd_saved(2, 8, 4, 16, 0, addr(1), addr(2), addr(3), addr(4), addr(5), None, None, None, 1,
+                                      args["ck"], args["dy"], None, args["du"], args["dd"], args["dA"], args["dB"],
+                                      args["dC"], None, None, None, None, None)
+    assert saved(ck=None) == 1
+    assert saved(ck=addr(12) + 1) == 5
+    assert saved(du=addr(12)) == 6             # an output on the checkpoints
+
+
 def cfwd(lib, batch=2, dim=8, dstate=4, seqlen=16, width=4, io=0, **over):
     args = dict(x=addr(1), w=addr(12), cb=addr(13), xp=addr(14), silu=1, delta=addr(2), A=addr(3), B=addr(4),
                 C=addr(5), D=addr(6), z=addr(7), bias=addr(8), sp=1, h0=addr(9), y=addr(10), last=addr(11),

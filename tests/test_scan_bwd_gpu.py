@@ -139,3 +139,35 @@ def test_bwd_deterministic_and_unsupported():
         with pytest.raises(binding.SsmError) as e:
             gpu_bwd(y, dy2, None)
         assert e.value.name == "SSM_ERR_UNSUPPORTED"
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_saved_checkpoints_match_recompute(io):
+    """scan_fwd_save + scan_bwd_saved equal scan_fwd + scan_bwd bit for bit (single-pass shapes), on a split
+    shape and on one that scan_fwd runs segmented (y then matches to the usual bar)."""
+    for shape in ((192, 64, 16, 64), (1, 64, 8, 2048)):
+        b, d, n, l = shape
+        say("saved checkpoints shape=%s io=%s" % (shape, io))
+        x = inputs.make_scan_inputs(b, d, n, l, io=io, seed=1700, h0=True)
+        dy, dlast = grads_inputs(x, 1700)
+        t = inputs.to_torch(x, DEV)
+        dyt = torch.from_numpy(dy).to(DEV, t["u"].dtype)
+        dlt = torch.from_numpy(dlast).to(DEV)
+        y1, h1, ck = binding.scan_fwd_save(t["u"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
+                                           delta_bias=t["delta_bias"], delta_softplus=True, h0=t["h0"])
+        y2, h2 = binding.scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
+                                  delta_bias=t["delta_bias"], delta_softplus=True, h0=t["h0"])
+        g1 = binding.scan_bwd_saved(t["u"], t["delta"], t["A"], t["B"], t["C"], dyt, ck, D=t["D"], z=t["z"],
+                                    delta_bias=t["delta_bias"], delta_softplus=True, dlast=dlt)
+        g2 = binding.scan_bwd(t["u"], t["delta"], t["A"], t["B"], t["C"], dyt, D=t["D"], z=t["z"],
+                              delta_bias=t["delta_bias"], delta_softplus=True, h0=t["h0"], dlast=dlt)
+        torch.cuda.synchronize()
+        split = binding.scan_plan(b, d, n, l, t["u"].dtype, with_path=True)[0] == "split"
+        if split:
+            assert torch.equal(y1, y2) and torch.equal(h1, h2)
+        else:
+            check(np64(y1), np64(y2), IO_TOL[io], "y (segmented scan_fwd)")
+            check(np64(h1), np64(h2), F32_TOL, "last_state (segmented scan_fwd)")
+        for k in g2:
+            if g2[k] is not None:
+                assert torch.equal(g1[k], g2[k]), k
