@@ -61,8 +61,10 @@ class Oracle:
         L.oracle_state_update_ex_f64.argtypes = [I64, I64, I64, I] + [P] * 9 + [I, P]
         L.oracle_zoh_b.restype = ctypes.c_double
         L.oracle_zoh_b.argtypes = [ctypes.c_double, ctypes.c_double]
-        L.oracle_scan_bwd_f64.restype = I
-        L.oracle_scan_bwd_f64.argtypes = [I64, I64, I64, I64] + [P] * 8 + [I] + [P] * 12
+        L.oracle_scan_bwd_ex_f64.restype = I
+        L.oracle_scan_bwd_ex_f64.argtypes = [I64, I64, I64, I64, I] + [P] * 8 + [I] + [P] * 12
+        L.oracle_zoh_b_da.restype = ctypes.c_double
+        L.oracle_zoh_b_da.argtypes = [ctypes.c_double, ctypes.c_double]
         L.oracle_scan_complex_f64.restype = I
         L.oracle_scan_complex_f64.argtypes = [I64, I64, I64, I64] + [P] * 8 + [I, P, P, P]
         L.oracle_conv1d_f64.restype = I
@@ -130,9 +132,13 @@ class Oracle:
             hs.append(h[0, 0])
         return np.stack(ys), np.stack(hs)
 
+    def zoh_b_da_f64(self, delta, a):
+        return self.lib.oracle_zoh_b_da(float(delta), float(a))
+
     def scan_bwd_f64(self, u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=False, h0=None, dy=None,
-                     dlast=None):
-        """Gradients of sum(dy * y) + sum(dlast * last_state) with respect to every input.
+                     dlast=None, zoh=False):
+        """Gradients of sum(dy * y) + sum(dlast * last_state) with respect to every input (zoh: B by exact
+        zero-order hold, as scan_f64).
 
         Returns a dict with du, ddelta (batch, dim, seqlen), dA (dim, dstate),
         dB, dC (batch, dstate, seqlen), and dD (dim,), dz, ddelta_bias (dim,),
@@ -147,11 +153,11 @@ class Oracle:
                    dz=None if z is None else np.empty_like(z),
                    ddelta_bias=None if delta_bias is None else np.empty_like(delta_bias),
                    dh0=np.empty((batch, dim, dstate), np.float64))
-        rc = self.lib.oracle_scan_bwd_f64(batch, dim, dstate, seqlen, _p(u), _p(delta), _p(A), _p(B), _p(C), _p(D),
-                                          _p(z), _p(delta_bias), 1 if softplus else 0, _p(h0), _p(dy), _p(dlast),
-                                          _p(out["du"]), _p(out["ddelta"]), _p(out["dA"]), _p(out["dB"]),
-                                          _p(out["dC"]), _p(out["dD"]), _p(out["dz"]), _p(out["ddelta_bias"]),
-                                          _p(out["dh0"]))
+        rc = self.lib.oracle_scan_bwd_ex_f64(batch, dim, dstate, seqlen, 1 if zoh else 0, _p(u), _p(delta), _p(A),
+                                             _p(B), _p(C), _p(D), _p(z), _p(delta_bias), 1 if softplus else 0, _p(h0),
+                                             _p(dy), _p(dlast), _p(out["du"]), _p(out["ddelta"]), _p(out["dA"]),
+                                             _p(out["dB"]), _p(out["dC"]), _p(out["dD"]), _p(out["dz"]),
+                                             _p(out["ddelta_bias"]), _p(out["dh0"]))
         if rc != 0:
             raise ValueError("oracle_scan_bwd_f64 rejected the arguments")
         return out

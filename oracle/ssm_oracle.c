@@ -88,7 +88,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-#define ORACLE_ABI_VERSION 3
+#define ORACLE_ABI_VERSION 4
 
 int oracle_abi_version(void) { return ORACLE_ABI_VERSION; }
 
@@ -105,6 +105,24 @@ double oracle_silu(double z) { return z / (1.0 + exp(-z)); }
 /* The zero-order-hold factor of B for one state: (e^{delta a} - 1) / a,
  * written with expm1 (no cancellation for small |delta a|); delta at a = 0. */
 double oracle_zoh_b(double delta, double a) { return a != 0.0 ? expm1(delta * a) / a : delta; }
+
+/* d/da of the zero-order-hold factor (e^{delta a} - 1) / a, which is
+ * (delta e^{delta a} - (e^{delta a} - 1)/a) / a.  With x = delta a that is
+ * delta^2 (x e^x - e^x + 1) / x^2 = delta^2 sum_{k>=0} x^k (k+1)/(k+2)!; the
+ * series (summed to convergence) is used where |x| < 1/2, where the closed
+ * form would cancel, and gives delta^2 / 2 at a = 0. */
+double oracle_zoh_b_da(double delta, double a) {
+  const double x = delta * a;
+  if (fabs(x) < 0.5) {
+    double term = 0.5, sum = 0.0; /* term_k = x^k (k+1)/(k+2)! */
+    for (int k = 0; k < 40; ++k) {
+      sum += term;
+      term *= x * (double)(k + 2) / ((double)(k + 1) * (double)(k + 3));
+    }
+    return delta * delta * sum;
+  }
+  return (delta * exp(x) - expm1(x) / a) / a;
+}
 
 /* One channel (b, d): walk the sequence once.  h has dstate entries. */
 static void scan_channel(int64_t dstate, int64_t seqlen, const double* u_row, const double* dt_row,
@@ -285,13 +303,13 @@ int oracle_conv1d_f64(int64_t batch, int64_t dim, int64_t seqlen, int64_t width,
  * depend on the thread count.  Outputs for absent inputs (dD, dz, ddelta_bias,
  * dh0) may be NULL.  Returns 0, or -1 on bad sizes, a missing pointer or
  * allocation failure. */
-int oracle_scan_bwd_f64(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, const double* u,
-                        const double* delta, const double* A, const double* B, const double* C,
-                        const double* D, const double* z, const double* delta_bias, int softplus_flag,
-                        const double* h0, const double* dy, const double* dlast, double* du, double* ddelta,
-                        double* dA, double* dB, double* dC, double* dD, double* dz, double* ddelta_bias,
-                        double* dh0) {
-  if (batch < 1 || dim < 1 || dstate < 1 || dstate > 256 || seqlen < 1) return -1;
+int oracle_scan_bwd_ex_f64(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int zoh, const double* u,
+                           const double* delta, const double* A, const double* B, const double* C,
+                           const double* D, const double* z, const double* delta_bias, int softplus_flag,
+                           const double* h0, const double* dy, const double* dlast, double* du, double* ddelta,
+                           double* dA, double* dB, double* dC, double* dD, double* dz, double* ddelta_bias,
+                           double* dh0) {
+  if (batch < 1 || dim < 1 || dstate < 1 || dstate > 256 || seqlen < 1 || (zoh != 0 && zoh != 1)) return -1;
   if (!u || !delta || !A || !B || !C || !dy || !du || !ddelta || !dA || !dB || !dC) return -1;
   double* partA = calloc((size_t)(batch * dim * dstate), sizeof(double));
   double* partD = calloc((size_t)(batch * dim), sizeof(double));
@@ -326,7 +344,8 @@ int oracle_scan_bwd_f64(int64_t batch, int64_t dim, int64_t dstate, int64_t seql
         double v = 0.0;
         steps[t] = step;
         for (int64_t n = 0; n < dstate; ++n) {
-          double h = exp(step * Ar[n]) * hs[t * dstate + n] + step * Bb[n * seqlen + t] * ut;
+          double phi = zoh ? oracle_zoh_b(step, Ar[n]) : step; /* Bbar = phi * B */
+          double h = exp(step * Ar[n]) * hs[t * dstate + n] + phi * Bb[n * seqlen + t] * ut;
           hs[(t + 1) * dstate + n] = h;
           v += Cb[n * seqlen + t] * h;
         }
@@ -350,12 +369,17 @@ int oracle_scan_bwd_f64(int64_t batch, int64_t dim, int64_t dstate, int64_t seql
           const double bt = Bb[n * seqlen + t];
           const double hprev = hs[t * dstate + n];
           const double abar = exp(step * Ar[n]);
+          const double phi = zoh ? oracle_zoh_b(step, Ar[n]) : step;
+          /* d phi / d step is abar under zero-order hold, 1 for the Delta*B rule;
+           * d phi / d A is oracle_zoh_b_da, 0 for the Delta*B rule. */
+          const double dphi_dstep = zoh ? abar : 1.0;
+          const double dphi_da = zoh ? oracle_zoh_b_da(step, Ar[n]) : 0.0;
           lam[n] += g * Cb[n * seqlen + t];
           dC[(b * dstate + n) * seqlen + t] += g * hs[(t + 1) * dstate + n];
-          dB[(b * dstate + n) * seqlen + t] += lam[n] * step * ut;
-          du_t += lam[n] * step * bt;
-          dstep += lam[n] * (Ar[n] * abar * hprev + bt * ut);
-          partA[ch * dstate + n] += lam[n] * step * abar * hprev;
+          dB[(b * dstate + n) * seqlen + t] += lam[n] * phi * ut;
+          du_t += lam[n] * phi * bt;
+          dstep += lam[n] * (Ar[n] * abar * hprev + dphi_dstep * bt * ut);
+          partA[ch * dstate + n] += lam[n] * (step * abar * hprev + dphi_da * bt * ut);
           lam[n] *= abar;
         }
         du[ch * seqlen + t] = du_t;
@@ -384,4 +408,14 @@ int oracle_scan_bwd_f64(int64_t batch, int64_t dim, int64_t dstate, int64_t seql
   }
   free(partA); free(partD); free(partBias);
   return fail ? -1 : 0;
+}
+
+int oracle_scan_bwd_f64(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, const double* u,
+                        const double* delta, const double* A, const double* B, const double* C,
+                        const double* D, const double* z, const double* delta_bias, int softplus_flag,
+                        const double* h0, const double* dy, const double* dlast, double* du, double* ddelta,
+                        double* dA, double* dB, double* dC, double* dD, double* dz, double* ddelta_bias,
+                        double* dh0) {
+  return oracle_scan_bwd_ex_f64(batch, dim, dstate, seqlen, 0, u, delta, A, B, C, D, z, delta_bias, softplus_flag, h0,
+                                dy, dlast, du, ddelta, dA, dB, dC, dD, dz, ddelta_bias, dh0);
 }

@@ -42,6 +42,8 @@ deliberately broken copies of it (tests/test_oracle_mutants.py).
   zoh_limits        at A = 0 ZOH equals the Delta*B rule, and for small |Delta A|
                     its factor follows the series Delta (1 + Delta A / 2 + ...)
   zoh_decode        the one-token ZOH update equals a one-token ZOH scan
+  zoh_bwd           the ZOH backward against finite differences (A with zero and tiny
+                    entries) and torch autograd through expm1(Delta A) / A
   complex_real_limit   complex A, B, C, h0 with zero imaginary parts equal the real
                     scan with C doubled (a real state and its conjugate partner)
   complex_block_expm   each complex state a + ib is the real two-state system with
@@ -399,7 +401,7 @@ def bwd_finite_diff(o):
             _close(g["dh0"], num, 1e-6, 1e-9, "dh0 at a zero state")
 
 
-def _torch_loss(p, softplus, dy, dlast):
+def _torch_loss(p, softplus, dy, dlast, zoh=False):
     import torch
     t = {k: (None if v is None else torch.tensor(v, dtype=torch.float64, requires_grad=True)) for k, v in p.items()}
     x = t["delta"] + (t["delta_bias"][None, :, None] if t["delta_bias"] is not None else 0.0)
@@ -410,7 +412,8 @@ def _torch_loss(p, softplus, dy, dlast):
     loss = 0.0
     for l in range(seqlen):
         abar = torch.exp(step[:, :, l, None] * t["A"][None])
-        h = abar * h + step[:, :, l, None] * t["B"][:, None, :, l] * t["u"][:, :, l, None]
+        phi = torch.expm1(step[:, :, l, None] * t["A"][None]) / t["A"][None] if zoh else step[:, :, l, None]
+        h = abar * h + phi * t["B"][:, None, :, l] * t["u"][:, :, l, None]
         s = (t["C"][:, None, :, l] * h).sum(-1)
         if t["D"] is not None:
             s = s + t["D"][None] * t["u"][:, :, l]
@@ -501,6 +504,49 @@ def zoh_limits(o):
         assert o.zoh_b_f64(dt, 0.0) == dt, "zoh factor at a = 0"
         for a in (-0.5, -4.0, 2.0):
             _close(o.zoh_b_f64(dt, a), (math.exp(dt * a) - 1.0) / a, 1e-13, 0.0, "zoh factor dt=%g a=%g" % (dt, a))
+
+
+def zoh_bwd(o):
+    """The zero-order-hold backward: finite differences (A with a zero and a tiny entry, where the
+    factor's A-derivative comes from its series) and torch autograd through expm1(Delta A) / A."""
+    rng = _rng(33)
+    batch, dim, dstate, seqlen = 2, 2, 3, 8
+    eps = 1e-6
+    p = _random_problem(rng, batch, dim, dstate, seqlen)
+    p["A"][0, 0] = 0.0
+    p["A"][1, 2] = -1e-7
+    dy = rng.standard_normal((batch, dim, seqlen))
+    dlast = rng.standard_normal((batch, dim, dstate))
+    g = o.scan_bwd_f64(softplus=True, dy=dy, dlast=dlast, zoh=True, **p)
+
+    def loss(q):
+        y, h = o.scan_f64(softplus=True, zoh=True, **q)
+        return float((dy * y).sum() + (dlast * h).sum())
+
+    for name, key in GRAD_OF.items():
+        base = p[name]
+        num = np.empty_like(base)
+        for i in range(base.size):
+            up, dn = base.copy(), base.copy()
+            up.flat[i] += eps
+            dn.flat[i] -= eps
+            num.flat[i] = (loss(dict(p, **{name: up})) - loss(dict(p, **{name: dn}))) / (2 * eps)
+        scale = max(float(np.abs(num).max()), 1e-12)
+        _close(g[key] / scale, num / scale, 0.0, 1e-6, "zoh d/d%s" % name)
+    q = _random_problem(rng, 3, 4, 5, 13)
+    dy = rng.standard_normal((3, 4, 13))
+    dlast = rng.standard_normal((3, 4, 5))
+    g = o.scan_bwd_f64(softplus=True, dy=dy, dlast=dlast, zoh=True, **q)
+    ref = _torch_loss(q, True, dy, dlast, zoh=True)
+    for name, key in GRAD_OF.items():
+        _close(g[key], ref[name], 1e-11, 1e-12, "zoh autograd d/d%s" % name)
+    # the factor's A-derivative: its series at small |Delta A|, the closed form elsewhere, Delta^2/2 at A = 0
+    for dt in (1e-3, 0.3, 2.0):
+        assert abs(o.zoh_b_da_f64(dt, 0.0) - dt * dt / 2) <= 1e-16 * dt * dt
+        for a in (-3.0, -0.4, -1e-5, 1e-5, 0.7):
+            h = 1e-4  # central difference: truncation ~ h^2 dt^4, rounding ~ 1e-16 dt / h
+            num = (o.zoh_b_f64(dt, a + h) - o.zoh_b_f64(dt, a - h)) / (2 * h)
+            _close(o.zoh_b_da_f64(dt, a), num, 1e-7, 1e-13, "d phi / dA at dt=%g a=%g" % (dt, a))
 
 
 def zoh_decode(o):
@@ -597,5 +643,5 @@ def complex_lti(o):
 
 ALL = [worked_examples, lti_closed_form, bruteforce, single_step, persistence, forgetting, split_carry, linearity,
        softplus_silu, decode_is_scan, channel_subset, conv_library, conv_taps, conv_causality, conv_split_carry,
-       bwd_finite_diff, bwd_autograd, zoh_van_loan, zoh_fixed_point, zoh_limits, zoh_decode, complex_real_limit,
+       bwd_finite_diff, bwd_autograd, zoh_van_loan, zoh_fixed_point, zoh_limits, zoh_decode, zoh_bwd, complex_real_limit,
        complex_block_expm, complex_lti]

@@ -42,7 +42,13 @@ MUTANTS = [
     ("bwd_hprev_is_h", "const double hprev = hs[t * dstate + n];", "const double hprev = hs[(t + 1) * dstate + n];"),
     ("bwd_softplus_grad_dropped", "softplus_flag ? dstep / (1.0 + exp(-x)) : dstep", "softplus_flag ? dstep : dstep"),
     ("bwd_dz_sign", "(1.0 + zt * (1.0 - sg))", "(1.0 - zt * (1.0 - sg))"),
-    ("bwd_dB_missing_step", "+= lam[n] * step * ut;", "+= lam[n] * ut;"),
+    ("bwd_dB_missing_step", "+= lam[n] * phi * ut;", "+= lam[n] * ut;"),
+    ("bwd_zoh_dphi_dstep", "const double dphi_dstep = zoh ? abar : 1.0;", "const double dphi_dstep = 1.0;"),
+    ("bwd_zoh_dphi_da_dropped", "const double dphi_da = zoh ? oracle_zoh_b_da(step, Ar[n]) : 0.0;",
+     "const double dphi_da = 0.0;"),
+    ("bwd_zoh_series_term", "term *= x * (double)(k + 2) / ((double)(k + 1) * (double)(k + 3));",
+     "term *= x / (double)(k + 3);"),
+    ("bwd_zoh_closed_form_sign", "return (delta * exp(x) - expm1(x) / a) / a;", "return (delta * exp(x) + expm1(x) / a) / a;"),
     ("bwd_dC_uses_hprev", "g * hs[(t + 1) * dstate + n];", "g * hs[t * dstate + n];"),
     ("zoh_missing_divide", "expm1(delta * a) / a : delta", "expm1(delta * a) : delta"),
     ("zoh_exp_not_expm1", "expm1(delta * a) / a : delta", "exp(delta * a) / a : delta"),
