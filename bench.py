@@ -297,6 +297,13 @@ def bench_backward(dev, x, t, steps, warmup):
                                         checkpoint_mb=round(ck.numel() * 4 / 1e6, 1))
     except _b.SsmError as e:
         out["saved_checkpoints"] = dict(skipped=str(e))
+
+    def bwd_zoh():
+        binding.scan_bwd_ex(t["u"], t["delta"], t["A"], t["B"], t["C"], dy, D=t["D"], z=t["z"],
+                            delta_bias=t["delta_bias"], delta_softplus=x.softplus, disc="zoh")
+
+    _, z_ms, _ = time_calls(bwd_zoh, steps, warmup)
+    out["zoh_us_per_call"] = round(z_ms * 1e3, 2)
     return out
 
 

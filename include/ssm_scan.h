@@ -68,7 +68,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 7
+#define SSM_ABI_VERSION 8
 
 struct ihipStream_t; /* the same incomplete type as HIP's hipStream_t */
 
@@ -349,6 +349,25 @@ ssm_status_t ssm_scan_bwd_saved(int64_t batch, int64_t dim, int64_t dstate, int6
                                 const float* ckpt, const void* dy, const float* dlast, void* du, void* ddelta,
                                 float* dA, float* dB, float* dC, float* dD, void* dz, float* ddelta_bias, float* dh0,
                                 struct ihipStream_t* stream);
+
+/*
+ * ssm_scan_bwd_ex -- ssm_scan_bwd for either discretization of B (see
+ * ssm_scan_fwd_ex): the gradients of ssm_scan_fwd_ex with the same disc.
+ * Under zero-order hold, with phi = (exp(Delta A) - 1) / A per state,
+ *   du += sum_n lambda B phi,  dB += lambda phi u,
+ *   dDelta = sum_n lambda (A Abar h_{t-1} + Abar B u)      (d phi / d Delta = Abar)
+ *   dA += lambda (Delta Abar h_{t-1} + B u d phi / d A),
+ *   d phi / d A = (Delta Abar - phi) / A = Delta^2 (x e^x - e^x + 1) / x^2, x = Delta A
+ * (its series where |x| < 1/4, Delta^2 / 2 at A = 0).  Arguments, layouts and
+ * errors as ssm_scan_bwd, plus SSM_ERR_UNSUPPORTED for a disc value outside
+ * ssm_disc_t.  SSM_DISC_DELTA_B gives ssm_scan_bwd's results bit for bit.
+ */
+ssm_status_t ssm_scan_bwd_ex(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, ssm_dtype_t io,
+                             ssm_disc_t disc, const void* u, const void* delta, const float* A, const void* B,
+                             const void* C, const float* D, const void* z, const float* delta_bias,
+                             int softplus_flag, const float* h0, const void* dy, const float* dlast, void* du,
+                             void* ddelta, float* dA, float* dB, float* dC, float* dD, void* dz, float* ddelta_bias,
+                             float* dh0, struct ihipStream_t* stream);
 
 /* Kernel paths of ssm_scan_fwd (reported by ssm_scan_fwd_plan). */
 typedef enum {

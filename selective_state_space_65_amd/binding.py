@@ -47,6 +47,8 @@ SIGNATURES = {
                                _P, _P, _P, _P]),
     "ssm_scan_bwd": (_I, [_I64, _I64, _I64, _I64, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P,
                           _P, _P, _P, _P, _P]),
+    "ssm_scan_bwd_ex": (_I, [_I64, _I64, _I64, _I64, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P,
+                             _P, _P, _P, _P, _P, _P, _P]),
     "ssm_scan_ckpt_bytes": (_I, [_I64, _I64, _I64, _I64, _I, ctypes.POINTER(_I64)]),
     "ssm_scan_fwd_save": (_I, [_I64, _I64, _I64, _I64, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P]),
     "ssm_scan_bwd_saved": (_I, [_I64, _I64, _I64, _I64, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P,
@@ -375,6 +377,15 @@ def scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, delta_softp
     return _scan_bwd(None, u, delta, A, B, C, dy, D, z, delta_bias, delta_softplus, h0, dlast, need, stream)
 
 
+def scan_bwd_ex(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, delta_softplus=False, h0=None, dlast=None,
+                disc="zoh", need=("dD", "dz", "ddelta_bias", "dh0"), stream=None):
+    """scan_bwd for either discretization of B (ssm_scan_bwd_ex): the gradients of scan_fwd_ex with the same disc."""
+    if disc not in DISC_CODES:
+        raise ValueError("disc must be one of %s" % sorted(DISC_CODES))
+    return _scan_bwd(None, u, delta, A, B, C, dy, D, z, delta_bias, delta_softplus, h0, dlast, need, stream,
+                     disc=DISC_CODES[disc])
+
+
 def scan_bwd_saved(u, delta, A, B, C, dy, ckpt, D=None, z=None, delta_bias=None, delta_softplus=False, dlast=None,
                    need=("dD", "dz", "ddelta_bias", "dh0"), stream=None):
     """scan_bwd reading the checkpoints scan_fwd_save wrote instead of re-running the forward (ssm_scan_bwd_saved)."""
@@ -431,7 +442,7 @@ def scan_fwd_save(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_soft
     return out, last_state, ckpt
 
 
-def _scan_bwd(ckpt, u, delta, A, B, C, dy, D, z, delta_bias, delta_softplus, h0, dlast, need, stream):
+def _scan_bwd(ckpt, u, delta, A, B, C, dy, D, z, delta_bias, delta_softplus, h0, dlast, need, stream, disc=None):
     import torch
     if u.dim() != 3:
         raise ValueError("u must be (batch, dim, seqlen)")
@@ -470,7 +481,9 @@ def _scan_bwd(ckpt, u, delta, A, B, C, dy, D, z, delta_bias, delta_softplus, h0,
             _ptr(delta_bias), 1 if delta_softplus else 0)
     tail = (_ptr(dy), _ptr(dlast), _ptr(g["du"]), _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]),
             _ptr(g["dD"]), _ptr(g["dz"]), _ptr(g["ddelta_bias"]), _ptr(g["dh0"]), _stream(dev, stream))
-    if ckpt is None:
+    if disc is not None:
+        _check("ssm_scan_bwd_ex", lib.ssm_scan_bwd_ex(*head[:5], disc, *head[5:], _ptr(h0), *tail))
+    elif ckpt is None:
         _check("ssm_scan_bwd", lib.ssm_scan_bwd(*head, _ptr(h0), *tail))
     else:
         _check("ssm_scan_bwd_saved", lib.ssm_scan_bwd_saved(*head, _ptr(ckpt), *tail))

@@ -110,6 +110,35 @@ __device__ __forceinline__ float zoh_input(float t, float e, float du, float iu)
   return __builtin_fabsf(t) < kZohSeriesT ? series : held;
 }
 
+// The zero-order-hold factor alone, phi = (e^{Delta a} - 1) / a (zoh_input
+// without u): t, e as there, dl = Delta, inva = 1 / a.
+__device__ __forceinline__ float zoh_factor(float t, float e, float dl, float inva) {
+  constexpr float c1 = kLn2 / 2.0f, c2 = kLn2 * kLn2 / 6.0f, c3 = kLn2 * kLn2 * kLn2 / 24.0f;
+  float q = __builtin_fmaf(t, c3, c2);
+  q = __builtin_fmaf(t, q, c1);
+  q = __builtin_fmaf(t, q, 1.0f);
+  const float series = dl * q;
+  const float held = __builtin_fmaf(e, inva, -inva);
+  return __builtin_fabsf(t) < kZohSeriesT ? series : held;
+}
+
+// d phi / d a = (Delta e - phi) / a = Delta^2 psi(x), x = Delta a, with
+// psi(x) = (x e^x - e^x + 1) / x^2 = sum_k x^k (k+1)/(k+2)!.  Where |x| < 1/4
+// the closed form would cancel, and the series to x^5 is used (the first
+// dropped term is under 1e-7 of psi); psi(0) = 1/2.  t = x log2(e).
+constexpr float kZohDaSeriesT = 0.25f * kLog2e;
+__device__ __forceinline__ float zoh_factor_da(float t, float e, float dl, float phi, float inva) {
+  const float x = t * kLn2;
+  float q = __builtin_fmaf(x, 6.0f / 5040.0f, 5.0f / 720.0f);  // coefficients (k+1)/(k+2)!, k = 5 .. 0
+  q = __builtin_fmaf(x, q, 4.0f / 120.0f);
+  q = __builtin_fmaf(x, q, 3.0f / 24.0f);
+  q = __builtin_fmaf(x, q, 2.0f / 6.0f);
+  q = __builtin_fmaf(x, q, 0.5f);
+  const float series = dl * dl * q;
+  const float closed = __builtin_fmaf(dl, e, -phi) * inva;
+  return __builtin_fabsf(t) < kZohDaSeriesT ? series : closed;
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
@@ -1226,7 +1255,8 @@ __device__ __forceinline__ float wave_sum_spread(float (&v)[NV], int lane) {
   return r;
 }
 
-template <typename IoT, int N, int S, int SA, bool kZ, bool kSoftplus>
+// kZoh: B discretized by exact zero-order hold; the staged x is then u itself.
+template <typename IoT, int N, int S, int SA, bool kZ, bool kSoftplus, bool kZoh = false>
 __global__ __launch_bounds__(64 * S) void scan_bwd_kernel(BwdArgs a) {
   constexpr int NS = N / S;
   constexpr int T = kCkptTokens;
@@ -1254,12 +1284,13 @@ __global__ __launch_bounds__(64 * S) void scan_bwd_kernel(BwdArgs a) {
   const int64_t L = a.seqlen;
   const int64_t ch = b * a.dim + d;
 
-  float Af[NS], A2[NS], carry[NS], dA_acc[NS];
+  float Af[NS], A2[NS], inva[NS], carry[NS], dA_acc[NS];
 #pragma unroll
   for (int j = 0; j < NS; ++j) {
     const int n = w * NS + j;
     Af[j] = a.A[d * N + n];
     A2[j] = Af[j] * kLog2e;
+    inva[j] = 1.0f / Af[j];
     carry[j] = a.dlast ? a.dlast[ch * N + n] : 0.0f;  // Abar_{t+1} lambda_{t+1} past the last token
     dA_acc[j] = 0.0f;
   }
@@ -1331,8 +1362,8 @@ __global__ __launch_bounds__(64 * S) void scan_bwd_kernel(BwdArgs a) {
           dlv4[t + e] = dd[e];
           sgd4[t + e] = kSoftplus ? sigmoid_f32(raw) : 1.0f;
         }
-        dxs[(w * TS + t) / 2][lane] =
-            make_float4(dd[0], dd[0] * LI::elem(qu, t), dd[1], dd[1] * LI::elem(qu, t + 1));
+        const float u0 = LI::elem(qu, t), u1 = LI::elem(qu, t + 1);
+        dxs[(w * TS + t) / 2][lane] = kZoh ? make_float4(dd[0], u0, dd[1], u1) : make_float4(dd[0], dd[0] * u0, dd[1], dd[1] * u1);
       }
 #pragma unroll
       for (int t = 0; t < TS; ++t) {
@@ -1365,8 +1396,10 @@ __global__ __launch_bounds__(64 * S) void scan_bwd_kernel(BwdArgs a) {
       float hc = hck[j];
 #pragma unroll
       for (int t = 0; t < VT; ++t) {
-        ab[j][t] = exp2_hw(A2[j] * dlv[t]);
-        hc = __builtin_fmaf(ab[j][t], hc, U::elem(Bt[j][t / kChunk], t % kChunk) * xv[t]);
+        const float ta = A2[j] * dlv[t];
+        ab[j][t] = exp2_hw(ta);
+        const float bu = kZoh ? zoh_input(ta, ab[j][t], dlv[t] * xv[t], xv[t] * inva[j]) : xv[t];
+        hc = __builtin_fmaf(ab[j][t], hc, U::elem(Bt[j][t / kChunk], t % kChunk) * bu);
         hs[j][t] = hc;
       }
     }
@@ -1392,13 +1425,30 @@ __global__ __launch_bounds__(64 * S) void scan_bwd_kernel(BwdArgs a) {
           const float cv = U::elem(Ct[j][k], t);
           const float bv = U::elem(Bt[j][k], t);
           const float lam = __builtin_fmaf(gv[tt], cv, carry[j]);
-          pv[j * kChunk + t] = lam * xv[tt];
           pv[NS * kChunk + j * kChunk + t] = gv[tt] * hs[j][tt];
-          const float q = __builtin_fmaf(-bv, xv[tt], hs[j][tt]);  // Abar_t h_{t-1} (active lanes)
-          const float m = lam * q;
-          sB = __builtin_fmaf(lam, bv, sB);
-          sA = __builtin_fmaf(m, Af[j], sA);
-          dA_acc[j] = __builtin_fmaf(m, dlv[tt], dA_acc[j]);
+          if constexpr (kZoh) {
+            // Bbar u = phi u: dB gets lambda phi u, du lambda B phi, dDelta
+            // lambda (A Abar h_{t-1} + Abar B u) (d phi / d Delta = Abar), dA
+            // lambda (Delta Abar h_{t-1} + B u d phi / d A).  xv holds u.
+            const float ta = A2[j] * dlv[tt];
+            const float phi = zoh_factor(ta, ab[j][tt], dlv[tt], inva[j]);
+            const float bu = phi * xv[tt];
+            pv[j * kChunk + t] = lam * bu;
+            const float q = __builtin_fmaf(-bv, bu, hs[j][tt]);  // Abar_t h_{t-1}
+            const float m = lam * q;
+            const float lb = lam * bv, lbu = lb * xv[tt];
+            sB = __builtin_fmaf(lb, phi, sB);
+            sA = __builtin_fmaf(m, Af[j], __builtin_fmaf(lbu, ab[j][tt], sA));
+            dA_acc[j] = __builtin_fmaf(m, dlv[tt], __builtin_fmaf(lbu, zoh_factor_da(ta, ab[j][tt], dlv[tt], phi, inva[j]),
+                                                                  dA_acc[j]));
+          } else {
+            pv[j * kChunk + t] = lam * xv[tt];
+            const float q = __builtin_fmaf(-bv, xv[tt], hs[j][tt]);  // Abar_t h_{t-1} (active lanes)
+            const float m = lam * q;
+            sB = __builtin_fmaf(lam, bv, sB);
+            sA = __builtin_fmaf(m, Af[j], sA);
+            dA_acc[j] = __builtin_fmaf(m, dlv[tt], dA_acc[j]);
+          }
           carry[j] = ab[j][tt] * lam;
         }
         part[w][tt][lane] = make_float2(sA, sB);
@@ -1430,8 +1480,10 @@ __global__ __launch_bounds__(64 * S) void scan_bwd_kernel(BwdArgs a) {
           acc.y += v.y;
         }
         const float ut = LI::elem(qu, t);
-        const float dstep = __builtin_fmaf(ut, acc.y, acc.x);
-        const float duv = __builtin_fmaf(dlv4[t], acc.y, g4[t] * Dd);
+        // Under zero-order hold the partials already are the dDelta terms
+        // (.x) and sum lambda B phi (.y).
+        const float dstep = kZoh ? acc.x : __builtin_fmaf(ut, acc.y, acc.x);
+        const float duv = kZoh ? __builtin_fmaf(g4[t], Dd, acc.y) : __builtin_fmaf(dlv4[t], acc.y, g4[t] * Dd);
         const float ddv = dstep * sgd4[t];
         dbias_acc += ddv;
         float dzt = 0.0f;
@@ -2026,26 +2078,32 @@ hipError_t launch_conv(const ScanArgs& a, void* u, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <typename IoT, int N, bool kZ, bool kSp>
+template <typename IoT, int N, bool kZ, bool kSp, bool kZoh>
 hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
   constexpr int S = (N >= SSM_SPLIT_WAVES) ? SSM_SPLIT_WAVES : N;
   constexpr int SA = (S > 4) ? 4 : S;
-  hipLaunchKernelGGL((scan_bwd_kernel<IoT, N, S, SA, kZ, kSp>), dim3((unsigned)(a.batch * a.groups)), dim3(64 * S), 0,
-                     st, a);
+  hipLaunchKernelGGL((scan_bwd_kernel<IoT, N, S, SA, kZ, kSp, kZoh>), dim3((unsigned)(a.batch * a.groups)),
+                     dim3(64 * S), 0, st, a);
   return hipGetLastError();
 }
 
+template <typename IoT, int N, bool kZoh>
+hipError_t launch_bwd_z(const BwdArgs& a, hipStream_t st, bool sp) {
+  if (a.z)
+    return sp ? launch_bwd_t<IoT, N, true, true, kZoh>(a, st) : launch_bwd_t<IoT, N, true, false, kZoh>(a, st);
+  return sp ? launch_bwd_t<IoT, N, false, true, kZoh>(a, st) : launch_bwd_t<IoT, N, false, false, kZoh>(a, st);
+}
+
 template <typename IoT, int N>
-hipError_t launch_bwd_n(const BwdArgs& a, hipStream_t st, bool sp) {
-  if (a.z) return sp ? launch_bwd_t<IoT, N, true, true>(a, st) : launch_bwd_t<IoT, N, true, false>(a, st);
-  return sp ? launch_bwd_t<IoT, N, false, true>(a, st) : launch_bwd_t<IoT, N, false, false>(a, st);
+hipError_t launch_bwd_n(const BwdArgs& a, hipStream_t st, bool sp, bool zoh) {
+  return zoh ? launch_bwd_z<IoT, N, true>(a, st, sp) : launch_bwd_z<IoT, N, false>(a, st, sp);
 }
 
 template <typename IoT>
-hipError_t launch_bwd(const BwdArgs& a, int N, hipStream_t st, bool sp) {
-  if (N == 4) return launch_bwd_n<IoT, 4>(a, st, sp);
-  if (N == 8) return launch_bwd_n<IoT, 8>(a, st, sp);
-  return launch_bwd_n<IoT, 16>(a, st, sp);
+hipError_t launch_bwd(const BwdArgs& a, int N, hipStream_t st, bool sp, bool zoh) {
+  if (N == 4) return launch_bwd_n<IoT, 4>(a, st, sp, zoh);
+  if (N == 8) return launch_bwd_n<IoT, 8>(a, st, sp, zoh);
+  return launch_bwd_n<IoT, 16>(a, st, sp, zoh);
 }
 
 // Waves of the backward (and forward) blocks that do the per-token work.
@@ -2391,7 +2449,7 @@ static ssm_status_t scan_bwd_impl(int64_t batch, int64_t dim, int64_t dstate, in
                                   const float* D, const void* z, const float* delta_bias, int softplus_flag,
                                   const float* h0, const float* saved, const void* dy, const float* dlast, void* du,
                                   void* ddelta, float* dA, float* dB, float* dC, float* dD, void* dz,
-                                  float* ddelta_bias, float* dh0, hipStream_t hs) {
+                                  float* ddelta_bias, float* dh0, hipStream_t hs, bool zoh) {
   Shape sh;
   ssm_status_t st = shape_of(batch, dim, dstate, seqlen, io, &sh);
   if (st != SSM_OK) return st;
@@ -2454,6 +2512,7 @@ static ssm_status_t scan_bwd_impl(int64_t batch, int64_t dim, int64_t dstate, in
     ScanArgs fa = scan_args(sh, batch, dim, dstate, seqlen, io, u, delta, A, B, C, D, z, delta_bias, h0, du, nullptr);
     fa.groups = groups; fa.segments = 1; fa.seg_len = seqlen;
     fa.ckpt = f;
+    fa.zoh = zoh;
     Plan fp = plan;
     fp.split = true; fp.segments = 1; fp.seg_len = seqlen; fp.scratch_bytes = 0;
     e = (io == SSM_BF16) ? launch_scan<bf16_t>(fa, fp, hs, true, sp) : launch_scan<float>(fa, fp, hs, true, sp);
@@ -2469,7 +2528,8 @@ static ssm_status_t scan_bwd_impl(int64_t batch, int64_t dim, int64_t dstate, in
   ba.dbias_part = ba.dD_part + batch * SA * dim;
   ba.batch = batch; ba.dim = dim; ba.seqlen = seqlen; ba.groups = groups;
   if (e == hipSuccess)
-    e = (io == SSM_BF16) ? launch_bwd<bf16_t>(ba, (int)dstate, hs, sp) : launch_bwd<float>(ba, (int)dstate, hs, sp);
+    e = (io == SSM_BF16) ? launch_bwd<bf16_t>(ba, (int)dstate, hs, sp, zoh)
+                         : launch_bwd<float>(ba, (int)dstate, hs, sp, zoh);
   // 3. Fixed-order sums of the partials.
   if (e == hipSuccess) {
     const int64_t n = std::max(sh.bnl, std::max(sh.dn, dim));
@@ -2492,7 +2552,23 @@ ssm_status_t ssm_scan_bwd(int64_t batch, int64_t dim, int64_t dstate, int64_t se
                           struct ihipStream_t* stream) {
   return scan_bwd_impl(batch, dim, dstate, seqlen, io, u, delta, A, B, C, D, z, delta_bias, softplus_flag, h0, nullptr,
                        dy, dlast, du, ddelta, dA, dB, dC, dD, dz, ddelta_bias, dh0,
-                       reinterpret_cast<hipStream_t>(stream));
+                       reinterpret_cast<hipStream_t>(stream), false);
+}
+
+ssm_status_t ssm_scan_bwd_ex(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, ssm_dtype_t io,
+                             ssm_disc_t disc, const void* u, const void* delta, const float* A, const void* B,
+                             const void* C, const float* D, const void* z, const float* delta_bias,
+                             int softplus_flag, const float* h0, const void* dy, const float* dlast, void* du,
+                             void* ddelta, float* dA, float* dB, float* dC, float* dD, void* dz, float* ddelta_bias,
+                             float* dh0, struct ihipStream_t* stream) {
+  if (disc != SSM_DISC_DELTA_B && disc != SSM_DISC_ZOH) {
+    Shape sh;
+    ssm_status_t st = shape_of(batch, dim, dstate, seqlen, io, &sh);
+    return st != SSM_OK ? st : SSM_ERR_UNSUPPORTED;
+  }
+  return scan_bwd_impl(batch, dim, dstate, seqlen, io, u, delta, A, B, C, D, z, delta_bias, softplus_flag, h0, nullptr,
+                       dy, dlast, du, ddelta, dA, dB, dC, dD, dz, ddelta_bias, dh0,
+                       reinterpret_cast<hipStream_t>(stream), disc == SSM_DISC_ZOH);
 }
 
 ssm_status_t ssm_scan_bwd_saved(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, ssm_dtype_t io,
@@ -2508,7 +2584,7 @@ ssm_status_t ssm_scan_bwd_saved(int64_t batch, int64_t dim, int64_t dstate, int6
   }
   return scan_bwd_impl(batch, dim, dstate, seqlen, io, u, delta, A, B, C, D, z, delta_bias, softplus_flag, nullptr,
                        ckpt, dy, dlast, du, ddelta, dA, dB, dC, dD, dz, ddelta_bias, dh0,
-                       reinterpret_cast<hipStream_t>(stream));
+                       reinterpret_cast<hipStream_t>(stream), false);
 }
 
 ssm_status_t ssm_scan_ckpt_bytes(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, ssm_dtype_t io,

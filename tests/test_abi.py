@@ -232,6 +232,19 @@ def test_saved_checkpoint_validation(lib):
     assert saved(du=addr(12)) == 6             # an output on the checkpoints
 
 
+def test_bwd_ex_validation(lib):
+    def call(disc, **over):
+        args = dict(u=addr(1), dy=addr(13), du=addr(14), dd=addr(15), dA=addr(16), dB=addr(17), dC=addr(18))
+        args.update(over)
+        return lib.ssm_scan_bwd_ex(2, 8, 4, 16, 0, disc, args["u"], addr(2), addr(3), addr(4), addr(5), None, None, None,
+                                   1, None, args["dy"], None, args["du"], args["dd"], args["dA"], args["dB"],
+                                   args["dC"], None, None, None, None, None)
+    assert call(1, u=None) == 1
+    assert call(1, du=addr(1)) == 6
+    for disc in (2, -1):
+        assert call(disc) == 8
+
+
 def cfwd(lib, batch=2, dim=8, dstate=4, seqlen=16, width=4, io=0, **over):
     args = dict(x=addr(1), w=addr(12), cb=addr(13), xp=addr(14), silu=1, delta=addr(2), A=addr(3), B=addr(4),
                 C=addr(5), D=addr(6), z=addr(7), bias=addr(8), sp=1, h0=addr(9), y=addr(10), last=addr(11),

@@ -171,3 +171,50 @@ def test_saved_checkpoints_match_recompute(io):
         for k in g2:
             if g2[k] is not None:
                 assert torch.equal(g1[k], g2[k]), k
+
+
+ZOH_SHAPES = [(192, 64, 16, 64), (256, 33, 4, 16), (2, 8, 16, 40), (3, 130, 8, 24)]
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", ZOH_SHAPES, ids=["%dx%dx%dx%d" % s for s in ZOH_SHAPES])
+def test_bwd_zoh_matches_oracle(io, shape):
+    """Gradients under exact zero-order hold (ssm_scan_bwd_ex), with A holding a zero and a tiny entry."""
+    b, d, n, l = shape
+    for mask in (31, 10):
+        z, D, bias, sp, h0 = [(mask >> i) & 1 == 1 for i in range(5)]
+        x = inputs.make_scan_inputs(b, d, n, l, io=io, seed=1800 + mask, z=z, D=D, bias=bias, softplus=sp, h0=h0)
+        x.A = x.A.copy()
+        x.A[::5, 0] = 0.0
+        x.A[1::5, n - 1] = -1e-6
+        if not sp:
+            x.delta = inputs.round_bf16(np.abs(x.delta) * np.float32(0.2)) if io == "bf16" else \
+                np.abs(x.delta) * np.float32(0.2)
+            if bias:
+                x.delta_bias = np.full(d, 0.01, np.float32)
+        dy, dlast = grads_inputs(x, 1800 + mask)
+        say("bwd zoh shape=%s io=%s mask=%d" % (shape, io, mask))
+        t = inputs.to_torch(x, DEV)
+        g = binding.scan_bwd_ex(t["u"], t["delta"], t["A"], t["B"], t["C"],
+                                torch.from_numpy(dy).to(DEV, t["u"].dtype), D=t["D"], z=t["z"],
+                                delta_bias=t["delta_bias"], delta_softplus=sp, h0=t["h0"],
+                                dlast=torch.from_numpy(dlast).to(DEV), disc="zoh")
+        torch.cuda.synchronize()
+        r = oracle.scan_bwd_f64(x.u, x.delta, x.A, x.B, x.C, x.D, x.z, x.delta_bias, x.softplus, x.h0, dy=dy,
+                                dlast=dlast, zoh=True)
+        compare(g, r, io, x, "zoh mask=%d" % mask)
+
+
+def test_bwd_ex_delta_b_is_scan_bwd_bitwise():
+    x = inputs.make_scan_inputs(192, 64, 16, 64, io="bf16", seed=1900, h0=True)
+    dy, dlast = grads_inputs(x, 1900)
+    t = inputs.to_torch(x, DEV)
+    dyt = torch.from_numpy(dy).to(DEV, t["u"].dtype)
+    dlt = torch.from_numpy(dlast).to(DEV)
+    kw = dict(D=t["D"], z=t["z"], delta_bias=t["delta_bias"], delta_softplus=True, h0=t["h0"], dlast=dlt)
+    g1 = binding.scan_bwd_ex(t["u"], t["delta"], t["A"], t["B"], t["C"], dyt, disc="delta_b", **kw)
+    g2 = binding.scan_bwd(t["u"], t["delta"], t["A"], t["B"], t["C"], dyt, **kw)
+    torch.cuda.synchronize()
+    for k in g2:
+        if g2[k] is not None:
+            assert torch.equal(g1[k], g2[k]), k
