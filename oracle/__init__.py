@@ -67,6 +67,8 @@ class Oracle:
         L.oracle_zoh_b_da.argtypes = [ctypes.c_double, ctypes.c_double]
         L.oracle_scan_complex_f64.restype = I
         L.oracle_scan_complex_f64.argtypes = [I64, I64, I64, I64] + [P] * 8 + [I, P, P, P]
+        L.oracle_scan_complex_bwd_f64.restype = I
+        L.oracle_scan_complex_bwd_f64.argtypes = [I64, I64, I64, I64] + [P] * 8 + [I] + [P] * 12
         L.oracle_conv1d_f64.restype = I
         L.oracle_conv1d_f64.argtypes = [I64, I64, I64, I64, P, P, P, P, I, P]
         L.oracle_softplus.restype = ctypes.c_double
@@ -117,6 +119,32 @@ class Oracle:
         if rc != 0:
             raise ValueError("oracle_scan_complex_f64 rejected the arguments")
         return y, last[..., 0] + 1j * last[..., 1]
+
+    def scan_complex_bwd_f64(self, u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=False, h0=None,
+                             dy=None, dlast=None):
+        """Gradients of sum(dy * y) + sum(Re(conj(dlast) last_state)) for scan_complex_f64 (complex arrays as
+        numpy complex).  Returns a dict like scan_bwd_f64; dA, dB, dC, dh0 complex (d/dRe + i d/dIm)."""
+        def ri(a):
+            return None if a is None else np.ascontiguousarray(np.stack([np.real(a), np.imag(a)], -1), np.float64)
+        u, delta, D, z, delta_bias, dy = map(_f64, (u, delta, D, z, delta_bias, dy))
+        A, B, C, h0, dlast = map(ri, (A, B, C, h0, dlast))
+        batch, dim, seqlen = u.shape
+        dstate = A.shape[1]
+        out = dict(du=np.empty_like(u), ddelta=np.empty_like(u), dA=np.empty((dim, dstate, 2)),
+                   dB=np.empty((batch, dstate, seqlen, 2)), dC=np.empty((batch, dstate, seqlen, 2)),
+                   dD=None if D is None else np.empty_like(D), dz=None if z is None else np.empty_like(z),
+                   ddelta_bias=None if delta_bias is None else np.empty_like(delta_bias),
+                   dh0=np.empty((batch, dim, dstate, 2)))
+        rc = self.lib.oracle_scan_complex_bwd_f64(batch, dim, dstate, seqlen, _p(u), _p(delta), _p(A), _p(B), _p(C),
+                                                  _p(D), _p(z), _p(delta_bias), 1 if softplus else 0, _p(h0), _p(dy),
+                                                  _p(dlast), _p(out["du"]), _p(out["ddelta"]), _p(out["dA"]),
+                                                  _p(out["dB"]), _p(out["dC"]), _p(out["dD"]), _p(out["dz"]),
+                                                  _p(out["ddelta_bias"]), _p(out["dh0"]))
+        if rc != 0:
+            raise ValueError("oracle_scan_complex_bwd_f64 rejected the arguments")
+        for k in ("dA", "dB", "dC", "dh0"):
+            out[k] = out[k][..., 0] + 1j * out[k][..., 1]
+        return out
 
     def scan_complex_channels_f64(self, channels, u, delta, A, B, C, D=None, z=None, delta_bias=None,
                                   softplus=False, h0=None):
@@ -259,6 +287,10 @@ def scan_bwd_f64(*args, **kw):
 
 def scan_complex_f64(*args, **kw):
     return default().scan_complex_f64(*args, **kw)
+
+
+def scan_complex_bwd_f64(*args, **kw):
+    return default().scan_complex_bwd_f64(*args, **kw)
 
 
 def scan_complex_channels_f64(*args, **kw):

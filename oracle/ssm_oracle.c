@@ -88,7 +88,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-#define ORACLE_ABI_VERSION 4
+#define ORACLE_ABI_VERSION 5
 
 int oracle_abi_version(void) { return ORACLE_ABI_VERSION; }
 
@@ -254,6 +254,137 @@ int oracle_scan_complex_f64(int64_t batch, int64_t dim, int64_t dstate, int64_t 
       }
   }
   return 0;
+}
+
+/* Gradients of the complex-A scan for a real loss with dL/dy = dy and
+ * dL/dlast_state = dlast ((re, im) pairs; NULL: 0).  A complex number w
+ * stands for its real pair (Re w, Im w); the gradient of the loss with respect
+ * to such a pair is written as the complex number dRe + i dIm.  Multiplying a
+ * state by Abar maps the gradient of the result to conj(Abar) times it, so
+ * the adjoint runs
+ *   lambda_t = 2 g_t conj(C_t) + conj(Abar_{t+1}) lambda_{t+1}   (+ dlast at the end)
+ * and, with q = Abar_t h_{t-1}:
+ *   dC[b,n,t] += 2 g conj(h_t)        dB[b,n,t] += lambda Delta u
+ *   du_t = g D + Delta sum_n Re(lambda conj(B))
+ *   dDelta_t = sum_n Re(lambda conj(A q + B u))
+ *   dA[d,n] += lambda conj(Delta q)   dh0 = conj(Abar_0) lambda_0
+ * with g, dz, dD, dbias as in oracle_scan_bwd_f64.  Layouts as
+ * oracle_scan_complex_f64; dA [dim][dstate][2], dB and dC
+ * [batch][dstate][seqlen][2], dh0 [batch][dim][dstate][2].  Parallel over
+ * batch rows with per-row partial sums added in row order.  Returns 0, or -1
+ * on bad sizes, a missing pointer or allocation failure. */
+int oracle_scan_complex_bwd_f64(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, const double* u,
+                                const double* delta, const double* A, const double* B, const double* C,
+                                const double* D, const double* z, const double* delta_bias, int softplus_flag,
+                                const double* h0, const double* dy, const double* dlast, double* du,
+                                double* ddelta, double* dA, double* dB, double* dC, double* dD, double* dz,
+                                double* ddelta_bias, double* dh0) {
+  if (batch < 1 || dim < 1 || dstate < 1 || dstate > 256 || seqlen < 1) return -1;
+  if (!u || !delta || !A || !B || !C || !dy || !du || !ddelta || !dA || !dB || !dC) return -1;
+  double complex* partA = calloc((size_t)(batch * dim * dstate), sizeof(double complex));
+  double* partD = calloc((size_t)(batch * dim), sizeof(double));
+  double* partBias = calloc((size_t)(batch * dim), sizeof(double));
+  int fail = !partA || !partD || !partBias;
+  memset(dB, 0, sizeof(double) * (size_t)(batch * dstate * seqlen * 2));
+  memset(dC, 0, sizeof(double) * (size_t)(batch * dstate * seqlen * 2));
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : fail)
+  for (int64_t b = 0; b < batch; ++b) {
+    if (fail) continue;
+    double complex* hs = malloc(sizeof(double complex) * (size_t)((seqlen + 1) * dstate)); /* hs[t+1] = h_t */
+    double* steps = malloc(sizeof(double) * (size_t)seqlen);
+    double* pre = malloc(sizeof(double) * (size_t)seqlen);
+    if (!hs || !steps || !pre) {
+      fail = 1;
+      free(hs); free(steps); free(pre);
+      continue;
+    }
+    for (int64_t d = 0; d < dim; ++d) {
+      const int64_t ch = b * dim + d;
+      const double Dd = D ? D[d] : 0.0;
+      const double bias = delta_bias ? delta_bias[d] : 0.0;
+      /* forward, keeping every state, step and pre-gate output */
+      for (int64_t n = 0; n < dstate; ++n)
+        hs[n] = h0 ? h0[(ch * dstate + n) * 2] + I * h0[(ch * dstate + n) * 2 + 1] : 0.0;
+      for (int64_t t = 0; t < seqlen; ++t) {
+        const double x = delta[ch * seqlen + t] + bias;
+        const double step = softplus_flag ? oracle_softplus(x) : x;
+        const double ut = u[ch * seqlen + t];
+        double complex acc = 0.0;
+        steps[t] = step;
+        for (int64_t n = 0; n < dstate; ++n) {
+          const double complex an = A[(d * dstate + n) * 2] + I * A[(d * dstate + n) * 2 + 1];
+          const int64_t k = ((b * dstate + n) * seqlen + t) * 2;
+          const double complex bn = B[k] + I * B[k + 1], cn = C[k] + I * C[k + 1];
+          hs[(t + 1) * dstate + n] = cexp(step * an) * hs[t * dstate + n] + step * bn * ut;
+          acc += cn * hs[(t + 1) * dstate + n];
+        }
+        pre[t] = 2.0 * creal(acc) + Dd * ut;
+      }
+      /* backward */
+      double complex lam[256];
+      for (int64_t n = 0; n < dstate; ++n)
+        lam[n] = dlast ? dlast[(ch * dstate + n) * 2] + I * dlast[(ch * dstate + n) * 2 + 1] : 0.0;
+      for (int64_t t = seqlen - 1; t >= 0; --t) {
+        const double ut = u[ch * seqlen + t], step = steps[t];
+        double g = dy[ch * seqlen + t];
+        if (z) {
+          const double zt = z[ch * seqlen + t];
+          const double sg = 1.0 / (1.0 + exp(-zt));
+          if (dz) dz[ch * seqlen + t] = g * pre[t] * sg * (1.0 + zt * (1.0 - sg));
+          g *= zt * sg;
+        }
+        partD[ch] += g * ut;
+        double du_t = g * Dd, dstep = 0.0;
+        for (int64_t n = 0; n < dstate; ++n) {
+          const double complex an = A[(d * dstate + n) * 2] + I * A[(d * dstate + n) * 2 + 1];
+          const int64_t k = ((b * dstate + n) * seqlen + t) * 2;
+          const double complex bn = B[k] + I * B[k + 1], cn = C[k] + I * C[k + 1];
+          const double complex abar = cexp(step * an);
+          const double complex q = abar * hs[t * dstate + n];
+          lam[n] += 2.0 * g * conj(cn);
+          const double complex dc = 2.0 * g * conj(hs[(t + 1) * dstate + n]);
+          const double complex db = lam[n] * step * ut;
+          dC[k] += creal(dc);
+          dC[k + 1] += cimag(dc);
+          dB[k] += creal(db);
+          dB[k + 1] += cimag(db);
+          du_t += step * creal(lam[n] * conj(bn));
+          dstep += creal(lam[n] * conj(an * q + bn * ut));
+          partA[ch * dstate + n] += lam[n] * conj(step * q);
+          lam[n] *= conj(abar);
+        }
+        du[ch * seqlen + t] = du_t;
+        const double x = delta[ch * seqlen + t] + bias;
+        const double dd = softplus_flag ? dstep / (1.0 + exp(-x)) : dstep;
+        ddelta[ch * seqlen + t] = dd;
+        partBias[ch] += dd;
+      }
+      if (dh0)
+        for (int64_t n = 0; n < dstate; ++n) {
+          dh0[(ch * dstate + n) * 2] = creal(lam[n]);
+          dh0[(ch * dstate + n) * 2 + 1] = cimag(lam[n]);
+        }
+    }
+    free(hs); free(steps); free(pre);
+  }
+  if (!fail) {
+    for (int64_t i = 0; i < dim * dstate * 2; ++i) dA[i] = 0.0;
+    for (int64_t d = 0; d < dim; ++d) {
+      if (dD) dD[d] = 0.0;
+      if (ddelta_bias) ddelta_bias[d] = 0.0;
+    }
+    for (int64_t b = 0; b < batch; ++b)
+      for (int64_t d = 0; d < dim; ++d) {
+        for (int64_t n = 0; n < dstate; ++n) {
+          dA[(d * dstate + n) * 2] += creal(partA[(b * dim + d) * dstate + n]);
+          dA[(d * dstate + n) * 2 + 1] += cimag(partA[(b * dim + d) * dstate + n]);
+        }
+        if (dD) dD[d] += partD[b * dim + d];
+        if (ddelta_bias) ddelta_bias[d] += partBias[b * dim + d];
+      }
+  }
+  free(partA); free(partD); free(partBias);
+  return fail ? -1 : 0;
 }
 
 /* Causal depthwise convolution of every (b, d) row, then silu if the flag is

@@ -51,6 +51,8 @@ deliberately broken copies of it (tests/test_oracle_mutants.py).
                     input (Re B, Im B) u and output 2 (Re C, -Im C)
   complex_lti       constant Delta, B, C: y = 2 Re(sum_k K_k u_{t-k}) + D u with
                     K_k = sum_n C_n Abar_n^k Delta B_n (numpy complex powers, np.convolve)
+  complex_bwd       the complex-A gradients (d/dRe + i d/dIm) against central finite
+                    differences of the complex forward and torch's complex autograd
 """
 import json
 import math
@@ -641,7 +643,78 @@ def complex_lti(o):
         _close(y[0, d], want, 1e-11, 1e-12, "complex LTI d=%d" % d)
 
 
+def _complex_loss_torch(p, softplus, dy, dlast):
+    import torch
+    c = {k: (None if p.get(k) is None else torch.tensor(p[k], dtype=torch.complex128 if np.iscomplexobj(p[k])
+                                                          else torch.float64, requires_grad=True))
+         for k in ("u", "delta", "A", "B", "C", "D", "z", "delta_bias", "h0")}
+    x = c["delta"] + (c["delta_bias"][None, :, None] if c["delta_bias"] is not None else 0.0)
+    step = torch.logaddexp(x, torch.zeros_like(x)) if softplus else x
+    batch, dim, seqlen = c["u"].shape
+    dstate = c["A"].shape[1]
+    h = c["h0"] if c["h0"] is not None else torch.zeros(batch, dim, dstate, dtype=torch.complex128)
+    loss = 0.0
+    for l in range(seqlen):
+        abar = torch.exp(step[:, :, l, None] * c["A"][None])
+        h = abar * h + step[:, :, l, None] * c["B"][:, None, :, l] * c["u"][:, :, l, None]
+        s_ = 2.0 * (c["C"][:, None, :, l] * h).sum(-1).real
+        if c["D"] is not None:
+            s_ = s_ + c["D"][None] * c["u"][:, :, l]
+        if c["z"] is not None:
+            zz = c["z"][:, :, l]
+            s_ = s_ * zz * torch.sigmoid(zz)
+        loss = loss + (torch.tensor(dy[:, :, l]) * s_).sum()
+    dl = torch.tensor(dlast)
+    loss = loss + (dl.real * h.real + dl.imag * h.imag).sum()
+    loss.backward()
+    return {k: (None if v is None else v.grad.numpy()) for k, v in c.items()}
+
+
+def complex_bwd(o):
+    rng = _rng(43)
+    batch, dim, dstate, seqlen = 2, 2, 3, 7
+    for flags in ((True, True, True, True, True), (False, False, False, False, True)):
+        zf, Df, bf, spf, hf = flags
+        p = _complex_problem(rng, batch, dim, dstate, seqlen, h0=hf)
+        if not zf:
+            p["z"] = None
+        if not Df:
+            p["D"] = None
+        if not bf:
+            p["delta_bias"] = None
+        dy = rng.standard_normal((batch, dim, seqlen))
+        dlast = rng.standard_normal((batch, dim, dstate)) + 1j * rng.standard_normal((batch, dim, dstate))
+        g = o.scan_complex_bwd_f64(softplus=spf, dy=dy, dlast=dlast, **p)
+
+        def loss(q):
+            y, h = o.scan_complex_f64(softplus=spf, **q)
+            return float((dy * y).sum() + (dlast.real * h.real + dlast.imag * h.imag).sum())
+
+        eps = 1e-6
+        for name, key in GRAD_OF.items():
+            if p.get(name) is None:
+                continue
+            base = p[name]
+            parts = (1.0, 1j) if np.iscomplexobj(base) else (1.0,)
+            num = np.zeros(base.shape, complex if np.iscomplexobj(base) else float)
+            for part in parts:
+                for i in range(base.size):
+                    up, dn = base.copy(), base.copy()
+                    up.flat[i] += eps * part
+                    dn.flat[i] -= eps * part
+                    dv = (loss(dict(p, **{name: up})) - loss(dict(p, **{name: dn}))) / (2 * eps)
+                    num.flat[i] += dv * part
+            scale = max(float(np.abs(num).max()), 1e-12)
+            _close(np.abs(g[key] - num) / scale, np.zeros(base.shape), 0.0, 1e-6, "complex d/d%s" % name)
+        ref = _complex_loss_torch(p, spf, dy, dlast)
+        for name, key in GRAD_OF.items():
+            if p.get(name) is None:
+                continue
+            _close(np.abs(g[key] - ref[name]), np.zeros(np.shape(ref[name])), 0.0,
+                   1e-11 * max(1.0, float(np.abs(ref[name]).max())), "complex autograd d/d%s" % name)
+
+
 ALL = [worked_examples, lti_closed_form, bruteforce, single_step, persistence, forgetting, split_carry, linearity,
        softplus_silu, decode_is_scan, channel_subset, conv_library, conv_taps, conv_causality, conv_split_carry,
        bwd_finite_diff, bwd_autograd, zoh_van_loan, zoh_fixed_point, zoh_limits, zoh_decode, zoh_bwd, complex_real_limit,
-       complex_block_expm, complex_lti]
+       complex_block_expm, complex_lti, complex_bwd]

@@ -64,6 +64,12 @@ MUTANTS = [
     ("cplx_C_conjugated", "acc += (cc[0] + I * cc[1]) * h[n];", "acc += (cc[0] - I * cc[1]) * h[n];"),
     ("cplx_h0_imag_dropped", "h0[(ch * dstate + n) * 2] + I * h0[(ch * dstate + n) * 2 + 1]",
      "h0[(ch * dstate + n) * 2] + 0.0 * I * h0[(ch * dstate + n) * 2 + 1]"),
+    ("cplx_bwd_adjoint_not_conj", "lam[n] *= conj(abar);", "lam[n] *= abar;"),
+    ("cplx_bwd_C_not_conj", "lam[n] += 2.0 * g * conj(cn);", "lam[n] += 2.0 * g * cn;"),
+    ("cplx_bwd_dC_factor", "const double complex dc = 2.0 * g * conj(hs[(t + 1) * dstate + n]);",
+     "const double complex dc = g * conj(hs[(t + 1) * dstate + n]);"),
+    ("cplx_bwd_dA_not_conj", "partA[ch * dstate + n] += lam[n] * conj(step * q);", "partA[ch * dstate + n] += lam[n] * step * q;"),
+    ("cplx_bwd_dstep_imag", "dstep += creal(lam[n] * conj(an * q + bn * ut));", "dstep += cimag(lam[n] * conj(an * q + bn * ut));"),
     ("bwd_dD_after_gate", "        partD[ch] += g * ut;", "        partD[ch] += dy[ch * seqlen + t] * ut;"),
 ]
 
