@@ -40,8 +40,8 @@ MUTANTS = [
     ("conv_silu_dropped", "u[ch * seqlen + l] = silu_flag ? oracle_silu(acc) : acc;", "u[ch * seqlen + l] = acc;"),
     ("bwd_lambda_not_decayed", "          lam[n] *= abar;", "          lam[n] *= 1.0;"),
     ("bwd_hprev_is_h", "const double hprev = hs[t * dstate + n];", "const double hprev = hs[(t + 1) * dstate + n];"),
-    ("bwd_softplus_grad_dropped", "softplus_flag ? dstep / (1.0 + exp(-x)) : dstep", "softplus_flag ? dstep : dstep"),
-    ("bwd_dz_sign", "(1.0 + zt * (1.0 - sg))", "(1.0 - zt * (1.0 - sg))"),
+    ("bwd_softplus_grad_dropped", "softplus_flag ? dstep / (1.0 + exp(-x)) : dstep", "softplus_flag ? dstep : dstep", 0),
+    ("bwd_dz_sign", "(1.0 + zt * (1.0 - sg))", "(1.0 - zt * (1.0 - sg))", 0),
     ("bwd_dB_missing_step", "+= lam[n] * phi * ut;", "+= lam[n] * ut;"),
     ("bwd_zoh_dphi_dstep", "const double dphi_dstep = zoh ? abar : 1.0;", "const double dphi_dstep = 1.0;"),
     ("bwd_zoh_dphi_da_dropped", "const double dphi_da = zoh ? oracle_zoh_b_da(step, Ar[n]) : 0.0;",
@@ -63,15 +63,24 @@ MUTANTS = [
     ("cplx_B_imag_dropped", "step * (bb[0] + I * bb[1]) * ul", "step * (bb[0] + 0.0 * I * bb[1]) * ul"),
     ("cplx_C_conjugated", "acc += (cc[0] + I * cc[1]) * h[n];", "acc += (cc[0] - I * cc[1]) * h[n];"),
     ("cplx_h0_imag_dropped", "h0[(ch * dstate + n) * 2] + I * h0[(ch * dstate + n) * 2 + 1]",
-     "h0[(ch * dstate + n) * 2] + 0.0 * I * h0[(ch * dstate + n) * 2 + 1]"),
+     "h0[(ch * dstate + n) * 2] + 0.0 * I * h0[(ch * dstate + n) * 2 + 1]", 0),
+    ("cplx_bwd_h0_imag_dropped", "h0[(ch * dstate + n) * 2] + I * h0[(ch * dstate + n) * 2 + 1]",
+     "h0[(ch * dstate + n) * 2] + 0.0 * I * h0[(ch * dstate + n) * 2 + 1]", 1),
     ("cplx_bwd_adjoint_not_conj", "lam[n] *= conj(abar);", "lam[n] *= abar;"),
     ("cplx_bwd_C_not_conj", "lam[n] += 2.0 * g * conj(cn);", "lam[n] += 2.0 * g * cn;"),
     ("cplx_bwd_dC_factor", "const double complex dc = 2.0 * g * conj(hs[(t + 1) * dstate + n]);",
      "const double complex dc = g * conj(hs[(t + 1) * dstate + n]);"),
     ("cplx_bwd_dA_not_conj", "partA[ch * dstate + n] += lam[n] * conj(step * q);", "partA[ch * dstate + n] += lam[n] * step * q;"),
     ("cplx_bwd_dstep_imag", "dstep += creal(lam[n] * conj(an * q + bn * ut));", "dstep += cimag(lam[n] * conj(an * q + bn * ut));"),
-    ("bwd_dD_after_gate", "        partD[ch] += g * ut;", "        partD[ch] += dy[ch * seqlen + t] * ut;"),
+    ("bwd_dD_after_gate", "        partD[ch] += g * ut;", "        partD[ch] += dy[ch * seqlen + t] * ut;", 0),
+    # Sites that the real and the complex backward share: the occurrence is named.
+    ("cplx_bwd_softplus_grad_dropped", "softplus_flag ? dstep / (1.0 + exp(-x)) : dstep", "softplus_flag ? dstep : dstep", 1),
+    ("cplx_bwd_dz_sign", "(1.0 + zt * (1.0 - sg))", "(1.0 - zt * (1.0 - sg))", 1),
+    ("cplx_bwd_dD_after_gate", "        partD[ch] += g * ut;", "        partD[ch] += dy[ch * seqlen + t] * ut;", 1),
 ]
+# A site written twice (the real and the complex backward) is mutated at the
+# named occurrence (0 = first); every other site must occur exactly once.
+MUTANTS = [m if len(m) == 4 else m + (None,) for m in MUTANTS]
 
 
 @pytest.fixture(scope="module")
@@ -79,11 +88,19 @@ def source():
     return open(oracle.SOURCE).read()
 
 
-@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
-def test_mutant_is_caught(tmp_path, source, name, old, new):
-    assert source.count(old) == 1, "mutation site for %s not found exactly once" % name
+def mutate(source, old, new, nth):
+    if nth is None:
+        assert source.count(old) == 1, "mutation site not found exactly once: %r" % old
+        return source.replace(old, new)
+    assert source.count(old) == 2, "shared mutation site not found exactly twice: %r" % old
+    at = source.index(old) if nth == 0 else source.index(old, source.index(old) + 1)
+    return source[:at] + new + source[at + len(old):]
+
+
+@pytest.mark.parametrize("name,old,new,nth", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(tmp_path, source, name, old, new, nth):
     src = tmp_path / ("mutant_%s.c" % name)
-    src.write_text(source.replace(old, new))
+    src.write_text(mutate(source, old, new, nth))
     lib = oracle.compile_oracle(str(src), str(tmp_path / ("libmutant_%s.so" % name)))
     o = oracle.Oracle(lib)
     caught = []
