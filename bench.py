@@ -241,11 +241,19 @@ def bench_complex(dev, x, t, steps, warmup):
     io_bytes = 2 if x.io == "bf16" else 4
     nbytes = algorithmic_bytes(b, d, n, l, io_bytes, has_z=x.z is not None) + d * n * 4  # A holds 2 numbers per state
     slots = CPLX_SLOTS_PER_ELEM_STATE * b * d * l * nc
+    dy = torch.from_numpy(inputs.grad_output(x)).to(dev, t["u"].dtype)
+
+    def bwd():
+        binding.scan_bwd_complex(t["u"], t["delta"], At, Bt, Ct, dy, D=t["D"], z=t["z"], delta_bias=t["delta_bias"],
+                                 delta_softplus=x.softplus)
+
+    _, bwd_ms, _ = time_calls(bwd, max(3, steps // 4), 2)
     return dict(workload="complex diagonal A (ssm_scan_fwd_complex), 8 complex states, same shape and flags",
                 us_per_call=round(avg_ms * 1e3, 2), us_median=round(med_ms * 1e3, 2),
                 algorithmic_gbs=round(nbytes / (avg_ms * 1e-3) / 1e9, 1),
                 alu_frac=round(slots / (avg_ms * 1e-3) / LANE_SLOTS_PEAK, 4),
-                lane_slots_per_elem_complex_state=CPLX_SLOTS_PER_ELEM_STATE)
+                lane_slots_per_elem_complex_state=CPLX_SLOTS_PER_ELEM_STATE,
+                backward_us_per_call=round(bwd_ms * 1e3, 2))
 
 
 BWD_SLOTS_PER_ELEM_STATE = 20  # 6 for the checkpointing forward + 14 for the adjoint walk

@@ -68,7 +68,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 8
+#define SSM_ABI_VERSION 9
 
 struct ihipStream_t; /* the same incomplete type as HIP's hipStream_t */
 
@@ -368,6 +368,31 @@ ssm_status_t ssm_scan_bwd_ex(int64_t batch, int64_t dim, int64_t dstate, int64_t
                              int softplus_flag, const float* h0, const void* dy, const float* dlast, void* du,
                              void* ddelta, float* dA, float* dB, float* dC, float* dD, void* dz, float* ddelta_bias,
                              float* dh0, struct ihipStream_t* stream);
+
+/*
+ * ssm_scan_bwd_complex -- gradients of ssm_scan_fwd_complex for a real loss
+ * with dL/dy = dy and dL/dlast_state = dlast.  The gradient with respect to a
+ * complex number w (a pair (Re w, Im w)) is returned as the pair
+ * (dL/dRe w, dL/dIm w).  With lambda that gradient for the state, q =
+ * Abar_t h_{t-1} and g = dL/d(pre-gate output):
+ *   lambda_t = 2 g_t conj(C_t) + conj(Abar_{t+1}) lambda_{t+1}   (+ dlast at the end)
+ *   dC += 2 g conj(h_t),  dB += lambda Delta u,  dA += lambda conj(Delta q)
+ *   du = g D + Delta sum_n Re(lambda conj(B)),  dDelta = sum_n Re(lambda conj(A q + B u))
+ *   dh0 = conj(Abar_0) lambda_0;  dz, dD, ddelta_bias as ssm_scan_bwd.
+ * Layouts: complex arrays as ssm_scan_fwd_complex ((re, im) last): dA
+ * [dim, dstate, 2], dB, dC [batch, dstate, seqlen, 2], dlast and dh0 [batch,
+ * dim, dstate, 2], all fp32; du, ddelta, dz as ssm_scan_bwd.  dstate counts
+ * complex states: 4 or 8 (other values up to 8 are SSM_ERR_UNSUPPORTED,
+ * above 8 SSM_ERR_DSTATE_UNSUPPORTED); seqlen a multiple of 8 and 16-byte
+ * aligned rows, as ssm_scan_bwd.  Unlike ssm_scan_fwd_complex it runs on any
+ * batch * dim (the checkpointing forward always takes the single-pass kernel).
+ */
+ssm_status_t ssm_scan_bwd_complex(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, ssm_dtype_t io,
+                                  const void* u, const void* delta, const float* A, const void* B, const void* C,
+                                  const float* D, const void* z, const float* delta_bias, int softplus_flag,
+                                  const float* h0, const void* dy, const float* dlast, void* du, void* ddelta,
+                                  float* dA, float* dB, float* dC, float* dD, void* dz, float* ddelta_bias,
+                                  float* dh0, struct ihipStream_t* stream);
 
 /* Kernel paths of ssm_scan_fwd (reported by ssm_scan_fwd_plan). */
 typedef enum {

@@ -8,7 +8,7 @@ generators) can be used without the library.
 """
 
 __all__ = ["scan_fwd", "scan_fwd_ex", "scan_fwd_complex", "conv_scan_fwd", "scan_bwd", "state_update", "state_update_ex",
-           "state_update_complex", "scan_fwd_save", "scan_bwd_saved", "scan_bwd_ex", "ckpt_shape", "scan_plan", "SsmError"]
+           "state_update_complex", "scan_fwd_save", "scan_bwd_saved", "scan_bwd_ex", "scan_bwd_complex", "ckpt_shape", "scan_plan", "SsmError"]
 
 
 def __getattr__(name):

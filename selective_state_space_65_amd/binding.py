@@ -49,6 +49,8 @@ SIGNATURES = {
                           _P, _P, _P, _P, _P]),
     "ssm_scan_bwd_ex": (_I, [_I64, _I64, _I64, _I64, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P,
                              _P, _P, _P, _P, _P, _P, _P]),
+    "ssm_scan_bwd_complex": (_I, [_I64, _I64, _I64, _I64, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P,
+                                  _P, _P, _P, _P, _P, _P, _P, _P]),
     "ssm_scan_ckpt_bytes": (_I, [_I64, _I64, _I64, _I64, _I, ctypes.POINTER(_I64)]),
     "ssm_scan_fwd_save": (_I, [_I64, _I64, _I64, _I64, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P]),
     "ssm_scan_bwd_saved": (_I, [_I64, _I64, _I64, _I64, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P,
@@ -265,6 +267,53 @@ def scan_fwd_complex(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_s
                                   _ptr(out), _ptr(last_state), _stream(dev, stream))
     _check("ssm_scan_fwd_complex", st)
     return out, last_state
+
+
+def scan_bwd_complex(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, delta_softplus=False, h0=None,
+                     dlast=None, need=("dD", "dz", "ddelta_bias", "dh0"), stream=None):
+    """Gradients for scan_fwd_complex (ssm_scan_bwd_complex); complex arrays as real tensors with a trailing
+    (re, im) dimension, their gradients as (d/dRe, d/dIm) pairs in the same layout.  Returns a dict as scan_bwd."""
+    import torch
+    if u.dim() != 3:
+        raise ValueError("u must be (batch, dim, seqlen)")
+    batch, dim, seqlen = u.shape
+    if A.dim() != 3 or A.shape[-1] != 2:
+        raise ValueError("A must be (dim, dstate, 2)")
+    dstate = A.shape[1]
+    dev = u.device
+    io = u.dtype
+    f32 = torch.float32
+    _need(u, "u", (batch, dim, seqlen), io, dev)
+    _need(delta, "delta", (batch, dim, seqlen), io, dev)
+    _need(A, "A", (dim, dstate, 2), f32, dev)
+    _need(B, "B", (batch, dstate, seqlen, 2), io, dev)
+    _need(C, "C", (batch, dstate, seqlen, 2), io, dev)
+    _need(dy, "dy", (batch, dim, seqlen), io, dev)
+    if D is not None:
+        _need(D, "D", (dim,), f32, dev)
+    if z is not None:
+        _need(z, "z", (batch, dim, seqlen), io, dev)
+    if delta_bias is not None:
+        _need(delta_bias, "delta_bias", (dim,), f32, dev)
+    if h0 is not None:
+        _need(h0, "h0", (batch, dim, dstate, 2), f32, dev)
+    if dlast is not None:
+        _need(dlast, "dlast", (batch, dim, dstate, 2), f32, dev)
+    g = dict(du=torch.empty_like(u), ddelta=torch.empty_like(u), dA=torch.empty((dim, dstate, 2), dtype=f32, device=dev),
+             dB=torch.empty((batch, dstate, seqlen, 2), dtype=f32, device=dev),
+             dC=torch.empty((batch, dstate, seqlen, 2), dtype=f32, device=dev),
+             dD=torch.empty(dim, dtype=f32, device=dev) if "dD" in need else None,
+             dz=torch.empty_like(u) if ("dz" in need and z is not None) else None,
+             ddelta_bias=torch.empty(dim, dtype=f32, device=dev) if "ddelta_bias" in need else None,
+             dh0=torch.empty((batch, dim, dstate, 2), dtype=f32, device=dev) if "dh0" in need else None)
+    lib = load_library()
+    st = lib.ssm_scan_bwd_complex(batch, dim, dstate, seqlen, _io_code(io), _ptr(u), _ptr(delta), _ptr(A), _ptr(B),
+                                  _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias), 1 if delta_softplus else 0, _ptr(h0),
+                                  _ptr(dy), _ptr(dlast), _ptr(g["du"]), _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]),
+                                  _ptr(g["dC"]), _ptr(g["dD"]), _ptr(g["dz"]), _ptr(g["ddelta_bias"]), _ptr(g["dh0"]),
+                                  _stream(dev, stream))
+    _check("ssm_scan_bwd_complex", st)
+    return g
 
 
 def state_update_complex(state, u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=False, out=None,

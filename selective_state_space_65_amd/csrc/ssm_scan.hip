@@ -1034,7 +1034,7 @@ __global__ __launch_bounds__(64 * S) void scan_split_kernel(ScanArgs a) {
           fetch_bc(s ^ 1, l + (k + 1) * kChunk);
         }
         __builtin_amdgcn_sched_barrier(0);
-        if (!kCplx && a.ckpt && (k * kChunk) % kCkptTokens == 0) {
+        if (a.ckpt && (k * kChunk) % kCkptTokens == 0) {
           // The state before token l + k*kChunk, for the backward's recompute.
           const int64_t c = (l + k * kChunk) / kCkptTokens;
 #pragma unroll
@@ -1256,7 +1256,15 @@ __device__ __forceinline__ float wave_sum_spread(float (&v)[NV], int lane) {
 }
 
 // kZoh: B discretized by exact zero-order hold; the staged x is then u itself.
-template <typename IoT, int N, int S, int SA, bool kZ, bool kSoftplus, bool kZoh = false>
+// kCplx: complex diagonal A, one complex state per wave (its NS = 2 slots hold
+// (re, im), as in the forward kernel); B, C, dB and dC rows are
+// (re, im)-interleaved.  With lambda the gradient with respect to the state
+// (d/dRe + i d/dIm), the adjoint is lambda_t = 2 g conj(C) + conj(Abar_{t+1})
+// lambda_{t+1}; dB += lambda Delta u, dC += 2 g conj(h), dA += lambda
+// conj(Delta Abar h_{t-1}), and du and dDelta take the real parts
+// Re(lambda conj(B)) and Re(lambda conj(A Abar h_{t-1})) in place of lambda B
+// and lambda A Abar h_{t-1}.
+template <typename IoT, int N, int S, int SA, bool kZ, bool kSoftplus, bool kZoh = false, bool kCplx = false>
 __global__ __launch_bounds__(64 * S) void scan_bwd_kernel(BwdArgs a) {
   constexpr int NS = N / S;
   constexpr int T = kCkptTokens;
@@ -1269,6 +1277,7 @@ __global__ __launch_bounds__(64 * S) void scan_bwd_kernel(BwdArgs a) {
   constexpr int PW = PI::kWords, ZW = kZ ? PI::kWords : 1, W = U::kWords;
   static_assert(N % S == 0 && NS <= 2 && S % SA == 0 && TS % 2 == 0 && kChunk % TS == 0 && KT == 2,
                 "backward tile shape");
+  static_assert(!kCplx || (NS == 2 && !kZoh), "complex: one complex state per wave, Delta * B rule");
   __shared__ float4 dxs[T / 2][64];  // (Delta_t, x_t, Delta_t+1, x_t+1)
   __shared__ float pch[S][T][64];    // per-wave partials of P1: C.h
   __shared__ float2 part[S][T][64];  // per-wave partials of P2: .x = sum lambda A q, .y = sum lambda B
@@ -1289,7 +1298,7 @@ __global__ __launch_bounds__(64 * S) void scan_bwd_kernel(BwdArgs a) {
   for (int j = 0; j < NS; ++j) {
     const int n = w * NS + j;
     Af[j] = a.A[d * N + n];
-    A2[j] = Af[j] * kLog2e;
+    A2[j] = (kCplx && j == 1) ? Af[j] * kInv2Pi : Af[j] * kLog2e;
     inva[j] = 1.0f / Af[j];
     carry[j] = a.dlast ? a.dlast[ch * N + n] : 0.0f;  // Abar_{t+1} lambda_{t+1} past the last token
     dA_acc[j] = 0.0f;
@@ -1340,7 +1349,9 @@ __global__ __launch_bounds__(64 * S) void scan_bwd_kernel(BwdArgs a) {
     for (int j = 0; j < NS; ++j)
 #pragma unroll
       for (int k = 0; k < KV; ++k) {
-        uint32_t off = (uint32_t)(w * NS + j) * row_bytes + (uint32_t)((l + k * kChunk) * sizeof(IoT));
+        // Complex rows: slot j holds tokens [4j, 4j + 4) of the sub-chunk as (re, im) pairs.
+        uint32_t off = kCplx ? (uint32_t)(w * NS) * row_bytes + (uint32_t)((2 * (l + k * kChunk) + 8 * j) * sizeof(IoT))
+                             : (uint32_t)(w * NS + j) * row_bytes + (uint32_t)((l + k * kChunk) * sizeof(IoT));
         asm volatile("" : "+s"(off));
         U::load8(Bb, off, Bt[j][k]);
         U::load8(Cb, off, Ct[j][k]);
@@ -1390,7 +1401,25 @@ __global__ __launch_bounds__(64 * S) void scan_bwd_kernel(BwdArgs a) {
     // the products) keeps them out of the lane sums of dB and dC.
 #pragma unroll
     for (int t = 0; t < VT; ++t) gv[t] = active ? gs[t][lane] : 0.0f;
-    float hs[NS][VT], ab[NS][VT];
+    float hs[NS][VT], ab[NS][VT];  // complex: [0] re, [1] im
+    if constexpr (kCplx) {
+      float hr = hck[0], hi = hck[1];
+#pragma unroll
+      for (int t = 0; t < VT; ++t) {
+        const int k = t / kChunk, jj = (t % kChunk) >> 2, q = 2 * (t & 3);
+        const float mag = exp2_hw(A2[0] * dlv[t]);
+        const float turn = __builtin_amdgcn_fractf(A2[1] * dlv[t]);
+        ab[0][t] = mag * __builtin_amdgcn_cosf(turn);
+        ab[1][t] = mag * __builtin_amdgcn_sinf(turn);
+        const float nr = __builtin_fmaf(ab[0][t], hr, __builtin_fmaf(-ab[1][t], hi, U::elem(Bt[jj][k], q) * xv[t]));
+        const float ni = __builtin_fmaf(ab[0][t], hi, __builtin_fmaf(ab[1][t], hr, U::elem(Bt[jj][k], q + 1) * xv[t]));
+        hr = nr;
+        hi = ni;
+        hs[0][t] = hr;
+        hs[1][t] = hi;
+        pch[w][t][lane] = __builtin_fmaf(U::elem(Ct[jj][k], q), hr, -(U::elem(Ct[jj][k], q + 1) * hi));  // Re(C h)
+      }
+    } else {
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
       float hc = hck[j];
@@ -1410,6 +1439,7 @@ __global__ __launch_bounds__(64 * S) void scan_bwd_kernel(BwdArgs a) {
       for (int j = 1; j < NS; ++j) ps = __builtin_fmaf(U::elem(Ct[j][t / kChunk], t % kChunk), hs[j][t], ps);
       pch[w][t][lane] = ps;
     }
+    }
 #pragma unroll
     for (int t = 0; t < VT; ++t) xv[t] = active ? xv[t] : 0.0f;
     // ---- P2: this wave's states backwards over the tile, one sub-chunk at a time
@@ -1420,6 +1450,30 @@ __global__ __launch_bounds__(64 * S) void scan_bwd_kernel(BwdArgs a) {
       for (int t = kChunk - 1; t >= 0; --t) {
         const int tt = k * kChunk + t;
         float sA = 0.0f, sB = 0.0f;
+        if constexpr (kCplx) {
+          // pv: [0, 8) dB re, [8, 16) dB im, [16, 24) dC re, [24, 32) dC im.
+          const int jj = t >> 2, q2 = 2 * (t & 3);
+          const float br = U::elem(Bt[jj][k], q2), bi = U::elem(Bt[jj][k], q2 + 1);
+          const float cr = U::elem(Ct[jj][k], q2), ci = U::elem(Ct[jj][k], q2 + 1);
+          const float g2 = 2.0f * gv[tt];
+          const float lr = __builtin_fmaf(g2, cr, carry[0]), li = __builtin_fmaf(-g2, ci, carry[1]);
+          const float hr = hs[0][tt], hi = hs[1][tt];
+          pv[t] = lr * xv[tt];
+          pv[kChunk + t] = li * xv[tt];
+          pv[2 * kChunk + t] = g2 * hr;
+          pv[3 * kChunk + t] = -(g2 * hi);
+          const float qr = __builtin_fmaf(-br, xv[tt], hr), qi = __builtin_fmaf(-bi, xv[tt], hi);  // Abar_t h_{t-1}
+          sB = __builtin_fmaf(lr, br, li * bi);                                                // Re(lambda conj(B))
+          // Re(lambda conj(A q)) with A q = (Ar qr - Ai qi, Ar qi + Ai qr)
+          const float aqr = __builtin_fmaf(Af[0], qr, -(Af[1] * qi)), aqi = __builtin_fmaf(Af[0], qi, Af[1] * qr);
+          sA = __builtin_fmaf(lr, aqr, li * aqi);
+          // dA += lambda conj(Delta q)
+          dA_acc[0] = __builtin_fmaf(dlv[tt], __builtin_fmaf(lr, qr, li * qi), dA_acc[0]);
+          dA_acc[1] = __builtin_fmaf(dlv[tt], __builtin_fmaf(li, qr, -(lr * qi)), dA_acc[1]);
+          // carry = conj(Abar) lambda
+          carry[0] = __builtin_fmaf(ab[0][tt], lr, ab[1][tt] * li);
+          carry[1] = __builtin_fmaf(ab[0][tt], li, -(ab[1][tt] * lr));
+        } else {
 #pragma unroll
         for (int j = 0; j < NS; ++j) {
           const float cv = U::elem(Ct[j][k], t);
@@ -1451,6 +1505,7 @@ __global__ __launch_bounds__(64 * S) void scan_bwd_kernel(BwdArgs a) {
           }
           carry[j] = ab[j][tt] * lam;
         }
+        }
         part[w][tt][lane] = make_float2(sA, sB);
       }
       // Sum the products over the wave's 64 channels.
@@ -1459,7 +1514,10 @@ __global__ __launch_bounds__(64 * S) void scan_bwd_kernel(BwdArgs a) {
       const int which = i / (NS * kChunk), jj = (i % (NS * kChunk)) / kChunk, t = i % kChunk;
       if (lane < NV) {
         float* dst = which ? a.dC_part : a.dB_part;
-        dst[((grp * a.batch + b) * N + w * NS + jj) * L + l + k * kChunk + t] = tot;
+        if constexpr (kCplx)  // the wave's complex row of 2 L floats, (re, im) interleaved
+          dst[((grp * a.batch + b) * N + w * NS) * L + 2 * (l + k * kChunk + t) + jj] = tot;
+        else
+          dst[((grp * a.batch + b) * N + w * NS + jj) * L + l + k * kChunk + t] = tot;
       }
     }
     lds_barrier();
@@ -1488,7 +1546,7 @@ __global__ __launch_bounds__(64 * S) void scan_bwd_kernel(BwdArgs a) {
         dbias_acc += ddv;
         float dzt = 0.0f;
         if constexpr (kZ) {
-          sv = __builtin_fmaf(Dd, ut, sv);
+          sv = __builtin_fmaf(Dd, ut, kCplx ? 2.0f * sv : sv);
           const float zt = LI::elem(qz, t), sg = sgz4[t];
           dzt = LI::elem(qy, t) * sv * sg * (1.0f + zt * (1.0f - sg));
         }
@@ -2099,6 +2157,21 @@ hipError_t launch_bwd_n(const BwdArgs& a, hipStream_t st, bool sp, bool zoh) {
   return zoh ? launch_bwd_z<IoT, N, true>(a, st, sp) : launch_bwd_z<IoT, N, false>(a, st, sp);
 }
 
+// Complex A: NC complex states (2 NC slots), one per wave.
+template <typename IoT, int NC>
+hipError_t launch_bwd_cplx(const BwdArgs& a, hipStream_t st, bool sp) {
+  constexpr int N = 2 * NC, S = NC, SA = 4;
+  const dim3 grid((unsigned)(a.batch * a.groups)), block(64 * S);
+  if (a.z) {
+    if (sp) hipLaunchKernelGGL((scan_bwd_kernel<IoT, N, S, SA, true, true, false, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((scan_bwd_kernel<IoT, N, S, SA, true, false, false, true>), grid, block, 0, st, a);
+  } else {
+    if (sp) hipLaunchKernelGGL((scan_bwd_kernel<IoT, N, S, SA, false, true, false, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((scan_bwd_kernel<IoT, N, S, SA, false, false, false, true>), grid, block, 0, st, a);
+  }
+  return hipGetLastError();
+}
+
 template <typename IoT>
 hipError_t launch_bwd(const BwdArgs& a, int N, hipStream_t st, bool sp, bool zoh) {
   if (N == 4) return launch_bwd_n<IoT, 4>(a, st, sp, zoh);
@@ -2449,7 +2522,7 @@ static ssm_status_t scan_bwd_impl(int64_t batch, int64_t dim, int64_t dstate, in
                                   const float* D, const void* z, const float* delta_bias, int softplus_flag,
                                   const float* h0, const float* saved, const void* dy, const float* dlast, void* du,
                                   void* ddelta, float* dA, float* dB, float* dC, float* dD, void* dz,
-                                  float* ddelta_bias, float* dh0, hipStream_t hs, bool zoh) {
+                                  float* ddelta_bias, float* dh0, hipStream_t hs, bool zoh, bool cplx = false) {
   Shape sh;
   ssm_status_t st = shape_of(batch, dim, dstate, seqlen, io, &sh);
   if (st != SSM_OK) return st;
@@ -2515,7 +2588,14 @@ static ssm_status_t scan_bwd_impl(int64_t batch, int64_t dim, int64_t dstate, in
     fa.zoh = zoh;
     Plan fp = plan;
     fp.split = true; fp.segments = 1; fp.seg_len = seqlen; fp.scratch_bytes = 0;
-    e = (io == SSM_BF16) ? launch_scan<bf16_t>(fa, fp, hs, true, sp) : launch_scan<float>(fa, fp, hs, true, sp);
+    if (cplx) {  // dstate counts slots here: two per complex state
+      if (io == SSM_BF16)
+        e = dstate == 8 ? launch_split_cplx<bf16_t, 4>(fa, fp, hs, sp) : launch_split_cplx<bf16_t, 8>(fa, fp, hs, sp);
+      else
+        e = dstate == 8 ? launch_split_cplx<float, 4>(fa, fp, hs, sp) : launch_split_cplx<float, 8>(fa, fp, hs, sp);
+    } else {
+      e = (io == SSM_BF16) ? launch_scan<bf16_t>(fa, fp, hs, true, sp) : launch_scan<float>(fa, fp, hs, true, sp);
+    }
   }
   // 2. Backward over the tiles in reverse.
   BwdArgs ba;
@@ -2527,9 +2607,17 @@ static ssm_status_t scan_bwd_impl(int64_t batch, int64_t dim, int64_t dstate, in
   ba.dD_part = ba.dA_part + sh.bdn;
   ba.dbias_part = ba.dD_part + batch * SA * dim;
   ba.batch = batch; ba.dim = dim; ba.seqlen = seqlen; ba.groups = groups;
-  if (e == hipSuccess)
-    e = (io == SSM_BF16) ? launch_bwd<bf16_t>(ba, (int)dstate, hs, sp, zoh)
-                         : launch_bwd<float>(ba, (int)dstate, hs, sp, zoh);
+  if (e == hipSuccess) {
+    if (cplx) {
+      if (io == SSM_BF16)
+        e = dstate == 8 ? launch_bwd_cplx<bf16_t, 4>(ba, hs, sp) : launch_bwd_cplx<bf16_t, 8>(ba, hs, sp);
+      else
+        e = dstate == 8 ? launch_bwd_cplx<float, 4>(ba, hs, sp) : launch_bwd_cplx<float, 8>(ba, hs, sp);
+    } else {
+      e = (io == SSM_BF16) ? launch_bwd<bf16_t>(ba, (int)dstate, hs, sp, zoh)
+                           : launch_bwd<float>(ba, (int)dstate, hs, sp, zoh);
+    }
+  }
   // 3. Fixed-order sums of the partials.
   if (e == hipSuccess) {
     const int64_t n = std::max(sh.bnl, std::max(sh.dn, dim));
@@ -2553,6 +2641,24 @@ ssm_status_t ssm_scan_bwd(int64_t batch, int64_t dim, int64_t dstate, int64_t se
   return scan_bwd_impl(batch, dim, dstate, seqlen, io, u, delta, A, B, C, D, z, delta_bias, softplus_flag, h0, nullptr,
                        dy, dlast, du, ddelta, dA, dB, dC, dD, dz, ddelta_bias, dh0,
                        reinterpret_cast<hipStream_t>(stream), false);
+}
+
+ssm_status_t ssm_scan_bwd_complex(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, ssm_dtype_t io,
+                                  const void* u, const void* delta, const float* A, const void* B, const void* C,
+                                  const float* D, const void* z, const float* delta_bias, int softplus_flag,
+                                  const float* h0, const void* dy, const float* dlast, void* du, void* ddelta,
+                                  float* dA, float* dB, float* dC, float* dD, void* dz, float* ddelta_bias,
+                                  float* dh0, struct ihipStream_t* stream) {
+  // The checks of ssm_scan_bwd on the real slots (two per complex state).
+  const int64_t slots = dstate < 1 ? dstate : (dstate > 8 ? 17 : 2 * dstate);
+  if (dstate >= 1 && dstate <= 8 && !(dstate == 4 || dstate == 8)) {
+    Shape sh;
+    ssm_status_t st = shape_of(batch, dim, slots, seqlen, io, &sh);
+    return st != SSM_OK ? st : SSM_ERR_UNSUPPORTED;
+  }
+  return scan_bwd_impl(batch, dim, slots, seqlen, io, u, delta, A, B, C, D, z, delta_bias, softplus_flag, h0, nullptr,
+                       dy, dlast, du, ddelta, dA, dB, dC, dD, dz, ddelta_bias, dh0,
+                       reinterpret_cast<hipStream_t>(stream), false, true);
 }
 
 ssm_status_t ssm_scan_bwd_ex(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, ssm_dtype_t io,

@@ -245,6 +245,22 @@ def test_bwd_ex_validation(lib):
         assert call(disc) == 8
 
 
+def test_bwd_complex_validation(lib):
+    def call(**over):
+        args = dict(batch=2, dstate=4, seqlen=16, u=addr(1), du=addr(14), dA=addr(16))
+        args.update(over)
+        return lib.ssm_scan_bwd_complex(args["batch"], 8, args["dstate"], args["seqlen"], 0, args["u"], addr(2), addr(3),
+                                        addr(4), addr(5), None, None, None, 1, None, addr(13), None, args["du"],
+                                        addr(15), args["dA"], addr(17), addr(18), None, None, None, None, None)
+    assert call(u=None) == 1
+    assert call(dstate=9) == 3
+    assert call(dstate=0) == 2
+    assert call(dstate=3) == 8                  # complex backward: 4 or 8 complex states
+    assert call(seqlen=12) == 8
+    assert call(du=addr(1)) == 6
+    assert call(dA=addr(3) + 8) == 6            # dA on A (dim x dstate x 2 floats)
+
+
 def cfwd(lib, batch=2, dim=8, dstate=4, seqlen=16, width=4, io=0, **over):
     args = dict(x=addr(1), w=addr(12), cb=addr(13), xp=addr(14), silu=1, delta=addr(2), A=addr(3), B=addr(4),
                 C=addr(5), D=addr(6), z=addr(7), bias=addr(8), sp=1, h0=addr(9), y=addr(10), last=addr(11),

@@ -224,3 +224,47 @@ def test_complex_decode_steps_equal_scan():
     torch.cuda.synchronize()
     check(np64(torch.stack(ys, -1)), np64(y_scan), 1e-5, "y")
     check(np64(st), np64(last), 1e-5, "state")
+
+
+CBWD_SHAPES = [(192, 64, 8, 64), (256, 33, 4, 16), (2, 8, 8, 40), (3, 130, 4, 24)]
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", CBWD_SHAPES, ids=["%dx%dx%dx%d" % s for s in CBWD_SHAPES])
+def test_complex_bwd_matches_oracle(io, shape):
+    """ssm_scan_bwd_complex against the oracle's complex gradients (d/dRe, d/dIm pairs)."""
+    b, d, n, l = shape
+    io_tol = TOL[io]
+    for mask in (31, 10):
+        zf, Df, bf, spf, hf = [(mask >> i) & 1 == 1 for i in range(5)]
+        say("complex bwd shape=%s io=%s mask=%d" % (shape, io, mask))
+        x, A, B, C, hh = complex_inputs(b, d, n, l, io, 4800 + mask, z=zf, D=Df, bias=bf, softplus=spf, h0=hf)
+        if not spf:
+            x.delta = inputs.round_bf16(np.abs(x.delta) * np.float32(0.2)) if io == "bf16" else \
+                np.abs(x.delta) * np.float32(0.2)
+            if bf:
+                x.delta_bias = np.full(d, 0.01, np.float32)
+        rng = np.random.default_rng([4801, mask])
+        dy = rng.standard_normal((b, d, l)).astype(np.float32)
+        if io == "bf16":
+            dy = inputs.round_bf16(dy)
+        dlast = rng.standard_normal((b, d, n, 2)).astype(np.float32)
+        t = inputs.to_torch(x, DEV)
+        dt = t["u"].dtype
+        g = binding.scan_bwd_complex(t["u"], t["delta"], torch.from_numpy(A).to(DEV), torch.from_numpy(B).to(DEV, dt),
+                                     torch.from_numpy(C).to(DEV, dt), torch.from_numpy(dy).to(DEV, dt), D=t["D"],
+                                     z=t["z"], delta_bias=t["delta_bias"], delta_softplus=spf,
+                                     h0=None if hh is None else torch.from_numpy(hh).to(DEV),
+                                     dlast=torch.from_numpy(dlast).to(DEV))
+        torch.cuda.synchronize()
+        r = oracle.scan_complex_bwd_f64(x.u, x.delta, cplx(A), cplx(B), cplx(C), x.D, x.z, x.delta_bias, spf,
+                                        cplx(hh), dy=dy, dlast=cplx(dlast))
+        for k in ("du", "ddelta", "dz"):
+            if g.get(k) is not None and r.get(k) is not None:
+                check(np64(g[k]), r[k], io_tol, "%s mask=%d" % (k, mask))
+        for k in ("dD", "ddelta_bias"):
+            if g.get(k) is not None and r.get(k) is not None:
+                check(np64(g[k]), r[k], TOL["f32"], "%s mask=%d" % (k, mask))
+        for k in ("dA", "dB", "dC", "dh0"):
+            want = np.stack([r[k].real, r[k].imag], -1)
+            check(np64(g[k]), want, TOL["f32"], "%s mask=%d" % (k, mask))
