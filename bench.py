@@ -151,9 +151,30 @@ def bench_decode(dev, steps, warmup):
                              delta_softplus=True, out=y)
 
     wall_ms, avg_ms, med_ms = time_calls(fn, steps, warmup)
+    # The same step captured once in a HIP graph and replayed back to back (no
+    # host launch between steps): the time per step of a decode loop.
+    graph_us = None
+    try:
+        stream = torch.cuda.Stream()
+        stream.wait_stream(torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        graph_us = round(e0.elapsed_time(e1) / steps * 1e3, 2)
+    except RuntimeError:
+        graph_us = None
     nbytes = decode_bytes(dec.batch, dec.dim, dec.dstate, 2)
     return dict(workload="decode state update, batch %d, dim %d, dstate %d, bf16 io, fp32 state"
                 % (dec.batch, dec.dim, dec.dstate), us_per_step=round(avg_ms * 1e3, 2),
+                graph_replay_us_per_step=graph_us,
                 effective_gbs=round(nbytes / (avg_ms * 1e-3) / 1e9, 1), bytes_per_step=nbytes,
                 note="algorithmic bytes per step / step time; the 84 MB state fits in the 256 MB Infinity "
                      "Cache, which sits behind the L2 and may serve part of it, so this is not pure HBM traffic")
