@@ -209,8 +209,9 @@ ssm_status_t ssm_conv_scan_fwd(int64_t batch, int64_t dim, int64_t dstate, int64
  *   dh0         [batch, dim, dstate]    fp32   written when not NULL (the gradient at h0 = 0 when h0 is NULL)
  *
  * Outputs must not overlap inputs or each other.  Supported: dstate in
- * {4, 8, 16}, seqlen a multiple of 8, and every (batch, dim, seqlen) and
- * (batch, dstate, seqlen) buffer 16-byte aligned; anything else returns
+ * {4, 8, 16}, seqlen a multiple of 8 and below 2^26 bytes per row (seqlen
+ * times the io element size), and every (batch, dim, seqlen) and (batch,
+ * dstate, seqlen) buffer 16-byte aligned; anything else returns
  * SSM_ERR_UNSUPPORTED.  Deterministic: partial sums are added in a fixed order.
  */
 ssm_status_t ssm_scan_bwd(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, ssm_dtype_t io,

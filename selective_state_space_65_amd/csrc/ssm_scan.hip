@@ -1137,31 +1137,34 @@ __global__ __launch_bounds__(64 * S) void scan_split_kernel(ScanArgs a) {
 //   lambda_t = g_t C_t + Abar_{t+1} lambda_{t+1}   (lambda = dL/dh, g = dL/d(pre-gate y))
 // and needs h_{t-1} at every token.  The forward states are not stored: the
 // single-pass forward kernel writes each wave's states every 16 tokens
-// (checkpoints, 1/16 of the expanded state for N = 16 ... and a 16th of the
-// tokens), and the backward recomputes a 16-token tile of states from its
-// checkpoint in registers before walking it backwards.  Same layout as the
-// forward: a block owns 64 channels of one batch row, its S waves split the
-// states, and the first SA waves (one per SIMD) handle the per-token work.
-// Per tile, in reverse order, with two barriers:
-//   P0  the first SA waves stage (Delta, x = Delta u) and g_t = dy_t silu(z_t)
-//       of their TS tokens in LDS (g does not depend on the state) and add
-//       g u into dD;                                              -- barrier
-//   P1  every wave recomputes its states over the tile from the checkpoint and
-//       publishes its partial C.h sums;
-//   P2  then walks its states backwards: lambda, dA in registers, the partial
-//       sums over its states of lambda B and lambda A (h_t - B x_t)
-//       (= lambda A Abar h_{t-1}) to LDS, and the per-lane products lambda x
-//       (dB) and g h (dC) summed over the wave's 64 channels;    -- barrier
-//   P3  the first SA waves sum the partials in wave order into the pre-gate
-//       output s_t = C.h + D u (for dz_t), du_t = g D + Delta sum(lambda B) and
-//       dDelta_t = sum(lambda A Abar h_{t-1}) + u sum(lambda B), with
-//       ddelta_t = dDelta_t sigmoid(delta_t + bias) under softplus.
-// The next tile's P0 follows P3 directly: every LDS buffer it writes was last
-// read before the second barrier, and every buffer P3 reads is next written
-// after the next tile's first barrier.
+// (checkpoints, 1/16 of the expanded state), and the backward recomputes a
+// 16-token tile of states from its checkpoint in registers before walking it
+// backwards.  A block owns 64 channels of one batch row and its S waves split
+// the states, as in the forward.  The work is cut into 8-token steps, taken
+// in reverse order with one LDS barrier each, and every wave runs every phase:
+//   token phases, lanes = 8 channels x 8 tokens (each global access then
+//   covers 8 rows with 16- or 32-byte runs):
+//     P0 of step s - 2: Delta (softplus), x = Delta u, g = dy silu(z), and the
+//        factors the output phase needs, into rings of four steps in LDS;
+//        dD accumulates g u;
+//     P3 of step s + 1: the per-wave partials of that step summed in wave
+//        order: the pre-gate output C.h + D u (for dz), du = g D + Delta
+//        sum(lambda B) and ddelta = (sum(lambda A Abar h_{t-1}) + u
+//        sum(lambda B)) times dDelta/d(raw delta); stored;
+//   state phases, lanes = channels:
+//     P1 at the upper step of a tile: the tile's states from the checkpoint;
+//     P2 of step s: the wave's states walked backwards: lambda and dA in
+//        registers; the partial sums over its states of C h, lambda A Abar
+//        h_{t-1} and lambda B to LDS; the per-lane products lambda x (dB) and
+//        g h (dC) summed over the wave's 64 channels.
+// P0 runs two steps ahead because P1 needs both steps of a tile; P3 runs one
+// step behind.  The partials alternate between two buffers by step parity and
+// the per-token values rotate through four, so every buffer is written only
+// after the barrier that follows its last read, and the token phases of one
+// wave overlap the state arithmetic of the others.
 // dB and dC are per-(group, batch row) partial sums over 64 channels, dA per
-// batch row, dD and dbias per (batch row, wave); bwd_reduce_kernel adds them
-// up in a fixed order, so the gradients are deterministic (no atomics).
+// batch row, dD and dbias per batch row; bwd_reduce_kernel adds them up in a
+// fixed order, so the gradients are deterministic (no atomics).
 struct BwdArgs {
   const void* u;
   const void* delta;
@@ -1181,8 +1184,8 @@ struct BwdArgs {
   float* dB_part;      // [groups][batch][N][seqlen]
   float* dC_part;      // [groups][batch][N][seqlen]
   float* dA_part;      // [batch][dim][N]
-  float* dD_part;      // [batch][SA][dim]
-  float* dbias_part;   // [batch][SA][dim]
+  float* dD_part;      // [batch][dim]
+  float* dbias_part;   // [batch][dim]
   int64_t batch, dim, seqlen, groups;
 };
 
@@ -1255,6 +1258,24 @@ __device__ __forceinline__ float wave_sum_spread(float (&v)[NV], int lane) {
   return r;
 }
 
+
+// LDS of the backward kernel.  The token phases access it with lanes spread
+// over 8 channels x 8 tokens (token = lane % 8).  On gfx950 a 4-byte access
+// is served 32 lanes at a time from 32 banks and an 8- or 16-byte access
+// from 64 banks, so rows of 68 floats (or 68 float2, 68 float4) put those
+// lanes on distinct banks; the channel-lane accesses of the state phases
+// are contiguous in every row.
+template <int S>
+struct BwdShared {
+  static constexpr int kRow = 68;
+  float pch[2][S][kChunk][kRow];       // per-wave partial C.h, by step parity
+  float2 part[2][S][kChunk][kRow];     // per-wave (sum lambda A Abar h_{t-1}, sum lambda B), by step parity
+  float4 dx[4][kChunk / 2][kRow];      // (Delta_t, x_t, Delta_t+1, x_t+1), ring of four steps
+  float2 us[4][kChunk][kRow];          // (u_t, dDelta_t / d(raw delta_t)), ring of four steps
+  float g[4][kChunk][kRow];            // g_t, ring of four steps
+  float kz[4][kChunk][kRow];           // dz_t / d(pre-gate output_t), ring of four steps
+};
+
 // kZoh: B discretized by exact zero-order hold; the staged x is then u itself.
 // kCplx: complex diagonal A, one complex state per wave (its NS = 2 slots hold
 // (re, im), as in the forward kernel); B, C, dB and dC rows are
@@ -1264,35 +1285,32 @@ __device__ __forceinline__ float wave_sum_spread(float (&v)[NV], int lane) {
 // conj(Delta Abar h_{t-1}), and du and dDelta take the real parts
 // Re(lambda conj(B)) and Re(lambda conj(A Abar h_{t-1})) in place of lambda B
 // and lambda A Abar h_{t-1}.
-template <typename IoT, int N, int S, int SA, bool kZ, bool kSoftplus, bool kZoh = false, bool kCplx = false>
+template <typename IoT, int N, int S, bool kZ, bool kSoftplus, bool kZoh = false, bool kCplx = false>
 __global__ __launch_bounds__(64 * S) void scan_bwd_kernel(BwdArgs a) {
   constexpr int NS = N / S;
   constexpr int T = kCkptTokens;
-  constexpr int KT = T / kChunk;
-  constexpr int TS = T / SA;
-  constexpr int NV = 2 * NS * kChunk;  // per-lane products summed over the wave per sub-chunk: dB, then dC
-  using LI = Line<IoT>;
-  using PI = Piece<IoT, TS>;
+  constexpr int NV = 2 * NS * kChunk;  // per-lane products summed over the wave per step: dB, then dC
+  constexpr int EPL = 8 / S;           // token-phase elements per lane (the block's 64 channels x 8 tokens)
   using U = Uni<IoT>;
-  constexpr int PW = PI::kWords, ZW = kZ ? PI::kWords : 1, W = U::kWords;
-  static_assert(N % S == 0 && NS <= 2 && S % SA == 0 && TS % 2 == 0 && kChunk % TS == 0 && KT == 2,
-                "backward tile shape");
+  constexpr int W = U::kWords;
+  static_assert(T == 2 * kChunk, "a checkpoint tile is two steps");
+  static_assert(N % S == 0 && NS <= 2 && (S == 4 || S == 8), "backward block shape");
   static_assert(!kCplx || (NS == 2 && !kZoh), "complex: one complex state per wave, Delta * B rule");
-  __shared__ float4 dxs[T / 2][64];  // (Delta_t, x_t, Delta_t+1, x_t+1)
-  __shared__ float pch[S][T][64];    // per-wave partials of P1: C.h
-  __shared__ float2 part[S][T][64];  // per-wave partials of P2: .x = sum lambda A q, .y = sum lambda B
-  __shared__ float gs[T][64];        // g_t
+  __shared__ BwdShared<S> sm;
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int64_t grp = blockIdx.x % a.groups;
   const int64_t b = blockIdx.x / a.groups;
+  const int64_t L = a.seqlen;
+  const int64_t nsteps = L / kChunk;
+
+  // State phases: lane = channel.  Lanes past the last channel run on a copy
+  // of it; P0 gives them zero g and x, which keeps them out of dB and dC.
   const int64_t d_raw = grp * kWaveThreads + lane;
   const bool active = d_raw < a.dim;
   const int64_t d = active ? d_raw : a.dim - 1;
-  const int64_t L = a.seqlen;
   const int64_t ch = b * a.dim + d;
-
   float Af[NS], A2[NS], inva[NS], carry[NS], dA_acc[NS];
 #pragma unroll
   for (int j = 0; j < NS; ++j) {
@@ -1303,104 +1321,168 @@ __global__ __launch_bounds__(64 * S) void scan_bwd_kernel(BwdArgs a) {
     carry[j] = a.dlast ? a.dlast[ch * N + n] : 0.0f;  // Abar_{t+1} lambda_{t+1} past the last token
     dA_acc[j] = 0.0f;
   }
-  const float Dd = a.D ? a.D[d] : 0.0f;
-  const float bias = a.bias ? a.bias[d] : 0.0f;
-  float dD_acc = 0.0f, dbias_acc = 0.0f;
 
-  const IoT* ur = static_cast<const IoT*>(a.u) + ch * L;
-  const IoT* dr = static_cast<const IoT*>(a.delta) + ch * L;
-  const IoT* zr = kZ ? static_cast<const IoT*>(a.z) + ch * L : nullptr;
-  const IoT* yr = static_cast<const IoT*>(a.dy) + ch * L;
-  IoT* dur = static_cast<IoT*>(a.du) + ch * L;
-  IoT* ddr = static_cast<IoT*>(a.ddelta) + ch * L;
-  IoT* dzr = (kZ && a.dz) ? static_cast<IoT*>(a.dz) + ch * L : nullptr;
+  // Token phases: element e of a lane is token tl of block channel tc[e],
+  // at byte offset toff[e] (+ the step's) from the block's first row (the
+  // host keeps 64 rows under 4 GiB, so one 32-bit lane offset serves the
+  // seven per-token arrays).
+  const int tl = lane & 7;
+  int tc[EPL];
+  bool tact[EPL];
+  uint32_t toff[EPL];
+  float tbias[EPL], tD[EPL], dD_acc[EPL], dbias_acc[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) {
+    tc[e] = w * (8 * EPL) + 8 * e + (lane >> 3);
+    const int64_t dg = grp * kWaveThreads + tc[e];
+    tact[e] = dg < a.dim;
+    const int64_t dgc = tact[e] ? dg : a.dim - 1;
+    toff[e] = (uint32_t)(((dgc - grp * kWaveThreads) * L + tl) * (int64_t)sizeof(IoT));
+    tbias[e] = a.bias ? a.bias[dgc] : 0.0f;
+    tD[e] = a.D ? a.D[dgc] : 0.0f;
+    dD_acc[e] = 0.0f;
+    dbias_acc[e] = 0.0f;
+  }
+  const int64_t row0 = (b * a.dim + grp * kWaveThreads) * L;
+  const char* up = reinterpret_cast<const char*>(static_cast<const IoT*>(a.u) + row0);
+  const char* dp = reinterpret_cast<const char*>(static_cast<const IoT*>(a.delta) + row0);
+  const char* zp = kZ ? reinterpret_cast<const char*>(static_cast<const IoT*>(a.z) + row0) : nullptr;
+  const char* yp = reinterpret_cast<const char*>(static_cast<const IoT*>(a.dy) + row0);
+  char* dup = reinterpret_cast<char*>(static_cast<IoT*>(a.du) + row0);
+  char* ddp = reinterpret_cast<char*>(static_cast<IoT*>(a.ddelta) + row0);
+  char* dzp = (kZ && a.dz) ? reinterpret_cast<char*>(static_cast<IoT*>(a.dz) + row0) : nullptr;
   const IoT* Bb = static_cast<const IoT*>(a.B) + b * N * L;
   const IoT* Cb = static_cast<const IoT*>(a.C) + b * N * L;
   const uint32_t row_bytes = (uint32_t)(L * sizeof(IoT));
 
-  // Inputs of a tile, loaded one tile ahead: the per-token pieces of the
-  // first SA waves and every wave's checkpointed states.
-  uint32_t qu[PW], qd[PW], qz[ZW], qy[PW], nqu[PW], nqd[PW], nqz[ZW], nqy[PW];
-  float hck[NS], nhck[NS];
-  auto load_tile = [&](int64_t c, uint32_t (&u_)[PW], uint32_t (&d_)[PW], uint32_t (&z_)[ZW], uint32_t (&y_)[PW],
-                       float (&h_)[NS]) {
-    const int64_t l = c * T;
-    if (w < SA && l + w * TS < L) {
-      PI::load(ur + l + w * TS, u_);
-      PI::load(dr + l + w * TS, d_);
-      if constexpr (kZ) PI::load(zr + l + w * TS, z_);
-      PI::load(yr + l + w * TS, y_);
+  // u, delta, z, dy of one step's token-phase elements as raw 32-bit words
+  // (for bf16, the aligned word that holds the token), so that nothing waits
+  // for the loads before P0 widens them one step later.  Two sets alternate
+  // by step.
+  uint32_t inA[EPL][4] = {}, inB[EPL][4] = {};
+  auto load_in = [&](int64_t s, uint32_t (&q)[EPL][4]) {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      const uint32_t o = (toff[e] + (uint32_t)(s * kChunk * (int64_t)sizeof(IoT))) & ~3u;
+      q[e][0] = *reinterpret_cast<const uint32_t*>(up + o);
+      q[e][1] = *reinterpret_cast<const uint32_t*>(dp + o);
+      if constexpr (kZ) q[e][2] = *reinterpret_cast<const uint32_t*>(zp + o);
+      q[e][3] = *reinterpret_cast<const uint32_t*>(yp + o);
     }
+  };
+  // bf16: the token's half of the word moved to the top (one byte permute;
+  // selector byte 0x0c gives zero).
+  const uint32_t half_sel = (tl & 1) ? 0x03020c0cu : 0x01000c0cu;
+  auto widen = [&](uint32_t w) {
+    if constexpr (sizeof(IoT) == 2) return __uint_as_float(__builtin_amdgcn_perm(0u, w, half_sel));
+    else return __uint_as_float(w);
+  };
+  // P0 of step s.
+  auto p0 = [&](int64_t s, const uint32_t (&q)[EPL][4]) {
+    const int r = (int)(s & 3);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      const float raw = widen(q[e][1]) + tbias[e];
+      const float dl = kSoftplus ? softplus_f32(raw) : raw;
+      const float sgd = kSoftplus ? sigmoid_f32(raw) : 1.0f;
+      const float ut = widen(q[e][0]);
+      float g = widen(q[e][3]), kz = 0.0f;
+      if constexpr (kZ) {
+        const float zt = widen(q[e][2]), sg = sigmoid_f32(zt);
+        kz = g * sg * (1.0f + zt * (1.0f - sg));
+        g *= zt * sg;
+      }
+      dD_acc[e] = __builtin_fmaf(g, ut, dD_acc[e]);
+      const float x = tact[e] ? (kZoh ? ut : dl * ut) : 0.0f;
+      reinterpret_cast<float2*>(&sm.dx[r][tl >> 1][tc[e]])[tl & 1] = make_float2(dl, x);
+      sm.us[r][tl][tc[e]] = make_float2(ut, sgd);
+      sm.g[r][tl][tc[e]] = tact[e] ? g : 0.0f;
+      sm.kz[r][tl][tc[e]] = kz;
+    }
+  };
+  // P3 of step s.
+  auto p3 = [&](int64_t s) {
+    const int r = (int)(s & 3), pb = (int)(s & 1);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      const int c = tc[e];
+      float sv = sm.pch[pb][0][tl][c];
+      float2 acc = sm.part[pb][0][tl][c];
+#pragma unroll
+      for (int s2 = 1; s2 < S; ++s2) {
+        sv += sm.pch[pb][s2][tl][c];
+        const float2 v = sm.part[pb][s2][tl][c];
+        acc.x += v.x;
+        acc.y += v.y;
+      }
+      const float dl = reinterpret_cast<const float2*>(&sm.dx[r][tl >> 1][c])[tl & 1].x;
+      const float2 us = sm.us[r][tl][c];
+      const float gt = sm.g[r][tl][c], kzt = sm.kz[r][tl][c];
+      // Under zero-order hold the partials already are the dDelta terms (.x)
+      // and sum lambda B phi (.y).
+      const float dstep = kZoh ? acc.x : __builtin_fmaf(us.x, acc.y, acc.x);
+      const float duv = kZoh ? __builtin_fmaf(gt, tD[e], acc.y) : __builtin_fmaf(dl, acc.y, gt * tD[e]);
+      const float ddv = dstep * us.y;
+      dbias_acc[e] += ddv;
+      if (tact[e]) {
+        const uint32_t o = toff[e] + (uint32_t)(s * kChunk * (int64_t)sizeof(IoT));
+        Io<IoT>::store1(reinterpret_cast<IoT*>(dup + o), duv);
+        Io<IoT>::store1(reinterpret_cast<IoT*>(ddp + o), ddv);
+        if (kZ && dzp)
+          Io<IoT>::store1(reinterpret_cast<IoT*>(dzp + o), __builtin_fmaf(tD[e], us.x, kCplx ? 2.0f * sv : sv) * kzt);
+      }
+    }
+  };
+  // The token phases that go with the state phases of step s: P0 reads cur
+  // (the inputs of step s - 2) and the inputs of step s - 3 go to nxt (the
+  // load is clamped to step 0 near the start, and its values then unused).
+  auto token_phases = [&](int64_t s, const uint32_t (&cur)[EPL][4], uint32_t (&nxt)[EPL][4]) {
+    load_in(s >= 3 ? s - 3 : 0, nxt);
+    if (s >= 2) p0(s - 2, cur);
+    if (s + 1 < nsteps) p3(s + 1);
+  };
+
+  // Checkpointed states of a tile, loaded one tile ahead.
+  float hck[NS] = {}, nhck[NS] = {};
+  auto load_ckpt = [&](int64_t c, float (&h_)[NS]) {
 #pragma unroll
     for (int j = 0; j < NS; ++j) h_[j] = a.ckpt[((c * a.batch + b) * N + w * NS + j) * a.dim + d];
   };
 
-  // One tile of KV sub-chunks of kChunk tokens (KV = KT, or 1 for a last
-  // tile of 8 tokens), so that every loop below has a static trip count.
+  // One tile of KV steps (KV = 2, or 1 for a last tile of 8 tokens), so that
+  // every loop below has a static trip count.
   auto tile = [&](int64_t c, auto kv_tag) {
     constexpr int KV = decltype(kv_tag)::value;
     constexpr int VT = KV * kChunk;
     const int64_t l = c * T;
-    const bool acw = w < SA && w * TS < VT;  // this wave's per-token share exists
-    // The B/C rows of this wave's states (scalar words), issued first so that
-    // P0 covers their latency.
-    uint32_t Bt[NS][KV][W], Ct[NS][KV][W];
+    const int64_t s_lo = 2 * c;
+    // The B rows of this wave's states over the tile and the C rows of the
+    // current step (scalar words), issued first so that the token phases
+    // cover their latency.
+    auto bc_off = [&](int j, int k) {
+      // Complex rows: slot j holds tokens [4j, 4j + 4) of the step as (re, im) pairs.
+      uint32_t off = kCplx ? (uint32_t)(w * NS) * row_bytes + (uint32_t)((2 * (l + k * kChunk) + 8 * j) * sizeof(IoT))
+                           : (uint32_t)(w * NS + j) * row_bytes + (uint32_t)((l + k * kChunk) * sizeof(IoT));
+      asm volatile("" : "+s"(off));
+      return off;
+    };
+    uint32_t Bt[NS][KV][W], Ct[NS][W];
 #pragma unroll
-    for (int j = 0; j < NS; ++j)
+    for (int j = 0; j < NS; ++j) {
 #pragma unroll
-      for (int k = 0; k < KV; ++k) {
-        // Complex rows: slot j holds tokens [4j, 4j + 4) of the sub-chunk as (re, im) pairs.
-        uint32_t off = kCplx ? (uint32_t)(w * NS) * row_bytes + (uint32_t)((2 * (l + k * kChunk) + 8 * j) * sizeof(IoT))
-                             : (uint32_t)(w * NS + j) * row_bytes + (uint32_t)((l + k * kChunk) * sizeof(IoT));
-        asm volatile("" : "+s"(off));
-        U::load8(Bb, off, Bt[j][k]);
-        U::load8(Cb, off, Ct[j][k]);
-      }
-    // The next tile's inputs (tiles run in reverse; every tile but the last is full).
-    if (c > 0) load_tile(c - 1, nqu, nqd, nqz, nqy, nhck);
-    // ---- P0: (Delta, x = Delta u) and g = dL/d(pre-gate output) of this
-    // wave's tokens.  g = dy silu(z) does not depend on the state, so every
-    // wave can start on the adjoint right after recomputing its states.
-    float dlv4[TS], sgd4[TS], g4[TS], sgz4[TS];
-    if (acw) {
-#pragma unroll
-      for (int t = 0; t < TS; t += 2) {
-        float dd[2];
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const float raw = LI::elem(qd, t + e) + bias;
-          dd[e] = kSoftplus ? softplus_f32(raw) : raw;
-          dlv4[t + e] = dd[e];
-          sgd4[t + e] = kSoftplus ? sigmoid_f32(raw) : 1.0f;
-        }
-        const float u0 = LI::elem(qu, t), u1 = LI::elem(qu, t + 1);
-        dxs[(w * TS + t) / 2][lane] = kZoh ? make_float4(dd[0], u0, dd[1], u1) : make_float4(dd[0], dd[0] * u0, dd[1], dd[1] * u1);
-      }
-#pragma unroll
-      for (int t = 0; t < TS; ++t) {
-        float g = LI::elem(qy, t);
-        if constexpr (kZ) {
-          const float zt = LI::elem(qz, t);
-          sgz4[t] = sigmoid_f32(zt);
-          g *= zt * sgz4[t];
-        }
-        dD_acc = __builtin_fmaf(g, LI::elem(qu, t), dD_acc);
-        g4[t] = g;
-        gs[w * TS + t][lane] = g;
-      }
+      for (int k = 0; k < KV; ++k) U::load8(Bb, bc_off(j, k), Bt[j][k]);
+      U::load8(Cb, bc_off(j, KV - 1), Ct[j]);
     }
-    lds_barrier();
+    load_ckpt(c > 0 ? c - 1 : 0, nhck);  // (clamped: unconditional loads keep the waits simple)
+    // A tile of two steps reads inA and fills inB, then the reverse.
+    token_phases(s_lo + KV - 1, inA, inB);
     // ---- P1: the tile's states from its checkpoint
-    float dlv[VT], xv[VT], gv[VT];
+    float dlv[VT], xv[VT];
 #pragma unroll
     for (int i = 0; i < VT / 2; ++i) {
-      const float4 v = dxs[i][lane];
+      const float4 v = sm.dx[(int)((s_lo + i / 4) & 3)][i % 4][lane];
       dlv[2 * i] = v.x; xv[2 * i] = v.y; dlv[2 * i + 1] = v.z; xv[2 * i + 1] = v.w;
     }
-    // Lanes past the last channel run on a copy of it; a zero g (and x in
-    // the products) keeps them out of the lane sums of dB and dC.
-#pragma unroll
-    for (int t = 0; t < VT; ++t) gv[t] = active ? gs[t][lane] : 0.0f;
     float hs[NS][VT], ab[NS][VT];  // complex: [0] re, [1] im
     if constexpr (kCplx) {
       float hr = hck[0], hi = hck[1];
@@ -1417,47 +1499,43 @@ __global__ __launch_bounds__(64 * S) void scan_bwd_kernel(BwdArgs a) {
         hi = ni;
         hs[0][t] = hr;
         hs[1][t] = hi;
-        pch[w][t][lane] = __builtin_fmaf(U::elem(Ct[jj][k], q), hr, -(U::elem(Ct[jj][k], q + 1) * hi));  // Re(C h)
       }
     } else {
 #pragma unroll
-    for (int j = 0; j < NS; ++j) {
-      float hc = hck[j];
+      for (int j = 0; j < NS; ++j) {
+        float hc = hck[j];
 #pragma unroll
-      for (int t = 0; t < VT; ++t) {
-        const float ta = A2[j] * dlv[t];
-        ab[j][t] = exp2_hw(ta);
-        const float bu = kZoh ? zoh_input(ta, ab[j][t], dlv[t] * xv[t], xv[t] * inva[j]) : xv[t];
-        hc = __builtin_fmaf(ab[j][t], hc, U::elem(Bt[j][t / kChunk], t % kChunk) * bu);
-        hs[j][t] = hc;
+        for (int t = 0; t < VT; ++t) {
+          const float ta = A2[j] * dlv[t];
+          ab[j][t] = exp2_hw(ta);
+          const float bu = kZoh ? zoh_input(ta, ab[j][t], dlv[t] * xv[t], xv[t] * inva[j]) : xv[t];
+          hc = __builtin_fmaf(ab[j][t], hc, U::elem(Bt[j][t / kChunk], t % kChunk) * bu);
+          hs[j][t] = hc;
+        }
       }
     }
+    // ---- P2 of the tile's step k (step s_lo + k): the wave's states backwards
+    auto p2 = [&](auto k_tag) {
+      constexpr int k = decltype(k_tag)::value;
+      const int64_t s = s_lo + k;
+      const int r = (int)(s & 3), pb = (int)(s & 1);
+      float gv[kChunk];
 #pragma unroll
-    for (int t = 0; t < VT; ++t) {
-      float ps = U::elem(Ct[0][t / kChunk], t % kChunk) * hs[0][t];
-#pragma unroll
-      for (int j = 1; j < NS; ++j) ps = __builtin_fmaf(U::elem(Ct[j][t / kChunk], t % kChunk), hs[j][t], ps);
-      pch[w][t][lane] = ps;
-    }
-    }
-#pragma unroll
-    for (int t = 0; t < VT; ++t) xv[t] = active ? xv[t] : 0.0f;
-    // ---- P2: this wave's states backwards over the tile, one sub-chunk at a time
-#pragma unroll
-    for (int k = KV - 1; k >= 0; --k) {
+      for (int t = 0; t < kChunk; ++t) gv[t] = sm.g[r][t][lane];
       float pv[NV];
 #pragma unroll
       for (int t = kChunk - 1; t >= 0; --t) {
         const int tt = k * kChunk + t;
-        float sA = 0.0f, sB = 0.0f;
+        float sA = 0.0f, sB = 0.0f, sC;
         if constexpr (kCplx) {
           // pv: [0, 8) dB re, [8, 16) dB im, [16, 24) dC re, [24, 32) dC im.
           const int jj = t >> 2, q2 = 2 * (t & 3);
           const float br = U::elem(Bt[jj][k], q2), bi = U::elem(Bt[jj][k], q2 + 1);
-          const float cr = U::elem(Ct[jj][k], q2), ci = U::elem(Ct[jj][k], q2 + 1);
-          const float g2 = 2.0f * gv[tt];
+          const float cr = U::elem(Ct[jj], q2), ci = U::elem(Ct[jj], q2 + 1);
+          const float g2 = 2.0f * gv[t];
           const float lr = __builtin_fmaf(g2, cr, carry[0]), li = __builtin_fmaf(-g2, ci, carry[1]);
           const float hr = hs[0][tt], hi = hs[1][tt];
+          sC = __builtin_fmaf(cr, hr, -(ci * hi));  // Re(C h)
           pv[t] = lr * xv[tt];
           pv[kChunk + t] = li * xv[tt];
           pv[2 * kChunk + t] = g2 * hr;
@@ -1474,39 +1552,43 @@ __global__ __launch_bounds__(64 * S) void scan_bwd_kernel(BwdArgs a) {
           carry[0] = __builtin_fmaf(ab[0][tt], lr, ab[1][tt] * li);
           carry[1] = __builtin_fmaf(ab[0][tt], li, -(ab[1][tt] * lr));
         } else {
+          sC = U::elem(Ct[0], t) * hs[0][tt];
 #pragma unroll
-        for (int j = 0; j < NS; ++j) {
-          const float cv = U::elem(Ct[j][k], t);
-          const float bv = U::elem(Bt[j][k], t);
-          const float lam = __builtin_fmaf(gv[tt], cv, carry[j]);
-          pv[NS * kChunk + j * kChunk + t] = gv[tt] * hs[j][tt];
-          if constexpr (kZoh) {
-            // Bbar u = phi u: dB gets lambda phi u, du lambda B phi, dDelta
-            // lambda (A Abar h_{t-1} + Abar B u) (d phi / d Delta = Abar), dA
-            // lambda (Delta Abar h_{t-1} + B u d phi / d A).  xv holds u.
-            const float ta = A2[j] * dlv[tt];
-            const float phi = zoh_factor(ta, ab[j][tt], dlv[tt], inva[j]);
-            const float bu = phi * xv[tt];
-            pv[j * kChunk + t] = lam * bu;
-            const float q = __builtin_fmaf(-bv, bu, hs[j][tt]);  // Abar_t h_{t-1}
-            const float m = lam * q;
-            const float lb = lam * bv, lbu = lb * xv[tt];
-            sB = __builtin_fmaf(lb, phi, sB);
-            sA = __builtin_fmaf(m, Af[j], __builtin_fmaf(lbu, ab[j][tt], sA));
-            dA_acc[j] = __builtin_fmaf(m, dlv[tt], __builtin_fmaf(lbu, zoh_factor_da(ta, ab[j][tt], dlv[tt], phi, inva[j]),
-                                                                  dA_acc[j]));
-          } else {
-            pv[j * kChunk + t] = lam * xv[tt];
-            const float q = __builtin_fmaf(-bv, xv[tt], hs[j][tt]);  // Abar_t h_{t-1} (active lanes)
-            const float m = lam * q;
-            sB = __builtin_fmaf(lam, bv, sB);
-            sA = __builtin_fmaf(m, Af[j], sA);
-            dA_acc[j] = __builtin_fmaf(m, dlv[tt], dA_acc[j]);
+          for (int j = 1; j < NS; ++j) sC = __builtin_fmaf(U::elem(Ct[j], t), hs[j][tt], sC);
+#pragma unroll
+          for (int j = 0; j < NS; ++j) {
+            const float cv = U::elem(Ct[j], t);
+            const float bv = U::elem(Bt[j][k], t);
+            const float lam = __builtin_fmaf(gv[t], cv, carry[j]);
+            pv[NS * kChunk + j * kChunk + t] = gv[t] * hs[j][tt];
+            if constexpr (kZoh) {
+              // Bbar u = phi u: dB gets lambda phi u, du lambda B phi, dDelta
+              // lambda (A Abar h_{t-1} + Abar B u) (d phi / d Delta = Abar), dA
+              // lambda (Delta Abar h_{t-1} + B u d phi / d A).  xv holds u.
+              const float ta = A2[j] * dlv[tt];
+              const float phi = zoh_factor(ta, ab[j][tt], dlv[tt], inva[j]);
+              const float bu = phi * xv[tt];
+              pv[j * kChunk + t] = lam * bu;
+              const float q = __builtin_fmaf(-bv, bu, hs[j][tt]);  // Abar_t h_{t-1}
+              const float m = lam * q;
+              const float lb = lam * bv, lbu = lb * xv[tt];
+              sB = __builtin_fmaf(lb, phi, sB);
+              sA = __builtin_fmaf(m, Af[j], __builtin_fmaf(lbu, ab[j][tt], sA));
+              dA_acc[j] = __builtin_fmaf(m, dlv[tt], __builtin_fmaf(lbu, zoh_factor_da(ta, ab[j][tt], dlv[tt], phi, inva[j]),
+                                                                    dA_acc[j]));
+            } else {
+              pv[j * kChunk + t] = lam * xv[tt];
+              const float q = __builtin_fmaf(-bv, xv[tt], hs[j][tt]);  // Abar_t h_{t-1} (active lanes)
+              const float m = lam * q;
+              sB = __builtin_fmaf(lam, bv, sB);
+              sA = __builtin_fmaf(m, Af[j], sA);
+              dA_acc[j] = __builtin_fmaf(m, dlv[tt], dA_acc[j]);
+            }
+            carry[j] = ab[j][tt] * lam;
           }
-          carry[j] = ab[j][tt] * lam;
         }
-        }
-        part[w][tt][lane] = make_float2(sA, sB);
+        sm.pch[pb][w][t][lane] = sC;
+        sm.part[pb][w][t][lane] = make_float2(sA, sB);
       }
       // Sum the products over the wave's 64 channels.
       const float tot = wave_sum_spread<NV>(pv, lane);
@@ -1519,94 +1601,71 @@ __global__ __launch_bounds__(64 * S) void scan_bwd_kernel(BwdArgs a) {
         else
           dst[((grp * a.batch + b) * N + w * NS + jj) * L + l + k * kChunk + t] = tot;
       }
-    }
+    };
+    p2(std::integral_constant<int, KV - 1>{});
     lds_barrier();
-    // ---- P3: the pre-gate output (for dz) and the partials of P2 (for du,
-    // ddelta), summed over the waves in order.
-    if (acw) {
-      uint32_t uw[PW], dw[PW], zw[PW];
+    if constexpr (KV == 2) {
 #pragma unroll
-      for (int t = 0; t < TS; ++t) {
-        const int tt = w * TS + t;
-        float sv = pch[0][tt][lane];
-        float2 acc = part[0][tt][lane];
-#pragma unroll
-        for (int s2 = 1; s2 < S; ++s2) {
-          sv += pch[s2][tt][lane];
-          const float2 v = part[s2][tt][lane];
-          acc.x += v.x;
-          acc.y += v.y;
-        }
-        const float ut = LI::elem(qu, t);
-        // Under zero-order hold the partials already are the dDelta terms
-        // (.x) and sum lambda B phi (.y).
-        const float dstep = kZoh ? acc.x : __builtin_fmaf(ut, acc.y, acc.x);
-        const float duv = kZoh ? __builtin_fmaf(g4[t], Dd, acc.y) : __builtin_fmaf(dlv4[t], acc.y, g4[t] * Dd);
-        const float ddv = dstep * sgd4[t];
-        dbias_acc += ddv;
-        float dzt = 0.0f;
-        if constexpr (kZ) {
-          sv = __builtin_fmaf(Dd, ut, kCplx ? 2.0f * sv : sv);
-          const float zt = LI::elem(qz, t), sg = sgz4[t];
-          dzt = LI::elem(qy, t) * sv * sg * (1.0f + zt * (1.0f - sg));
-        }
-        if constexpr (sizeof(IoT) == 4) {
-          uw[t] = __float_as_uint(duv);
-          dw[t] = __float_as_uint(ddv);
-          zw[t] = __float_as_uint(dzt);
-        } else if (t & 1) {
-          uw[t / 2] = Io<bf16_t>::pack2(__uint_as_float(uw[t / 2]), duv);
-          dw[t / 2] = Io<bf16_t>::pack2(__uint_as_float(dw[t / 2]), ddv);
-          zw[t / 2] = Io<bf16_t>::pack2(__uint_as_float(zw[t / 2]), dzt);
-        } else {
-          uw[t / 2] = __float_as_uint(duv);
-          dw[t / 2] = __float_as_uint(ddv);
-          zw[t / 2] = __float_as_uint(dzt);
-        }
-      }
-      if (active) {
-        PI::store(dur + l + w * TS, uw);
-        PI::store(ddr + l + w * TS, dw);
-        if (kZ && dzr) PI::store(dzr + l + w * TS, zw);
-      }
+      for (int j = 0; j < NS; ++j) U::load8(Cb, bc_off(j, 0), Ct[j]);
+      token_phases(s_lo, inB, inA);
+      p2(std::integral_constant<int, 0>{});
+      lds_barrier();
     }
-    // The prefetched inputs become the current ones.
+    if constexpr (KV == 1) {  // (once, at the start) the next tile's first step reads inA
 #pragma unroll
-    for (int q = 0; q < PW; ++q) {
-      qu[q] = nqu[q];
-      qd[q] = nqd[q];
-      if constexpr (kZ) qz[q] = nqz[q];
-      qy[q] = nqy[q];
+      for (int e = 0; e < EPL; ++e)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) inA[e][i] = inB[e][i];
     }
 #pragma unroll
     for (int j = 0; j < NS; ++j) hck[j] = nhck[j];
   };
 
+  // Prologue: P0 of the last two steps, and the inputs of the third-last.
   const int64_t ntiles = (L + T - 1) / T;
-  load_tile(ntiles - 1, qu, qd, qz, qy, hck);
-  for (int64_t c = ntiles - 1; c >= 0; --c) {
-    if (L - c * T >= T)
-      tile(c, std::integral_constant<int, KT>{});
-    else
-      tile(c, std::integral_constant<int, 1>{});  // a last tile of kChunk tokens
+  if (nsteps >= 1) {
+    load_in(nsteps - 1, inA);
+    p0(nsteps - 1, inA);
   }
+  if (nsteps >= 2) {
+    load_in(nsteps - 2, inA);
+    p0(nsteps - 2, inA);
+  }
+  load_in(nsteps >= 3 ? nsteps - 3 : 0, inA);
+  load_ckpt(ntiles - 1, hck);
+  lds_barrier();
+  int64_t c = ntiles - 1;
+  if (L - c * T < T) tile(c--, std::integral_constant<int, 1>{});  // a last tile of kChunk tokens
+  for (; c >= 0; --c) tile(c, std::integral_constant<int, 2>{});
+  if (nsteps >= 1) p3(0);
+
   if (active) {
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
       if (a.dh0) a.dh0[ch * N + w * NS + j] = carry[j];
       a.dA_part[ch * N + w * NS + j] = dA_acc[j];
     }
-    if (w < SA) {
-      a.dD_part[(b * SA + w) * a.dim + d] = dD_acc;
-      a.dbias_part[(b * SA + w) * a.dim + d] = dbias_acc;
+  }
+  // dD and dbias: each channel's 8 token lanes are adjacent; sum them.
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) {
+#pragma unroll
+    for (int m = 1; m < 8; m <<= 1) {
+      dD_acc[e] += __shfl_xor(dD_acc[e], m);
+      dbias_acc[e] += __shfl_xor(dbias_acc[e], m);
+    }
+    if (tact[e] && tl == 0) {
+      const int64_t dg = grp * kWaveThreads + tc[e];
+      a.dD_part[b * a.dim + dg] = dD_acc[e];
+      a.dbias_part[b * a.dim + dg] = dbias_acc[e];
     }
   }
 }
 
 // Adds the backward's partial sums in a fixed order: dB, dC over channel
-// groups; dA over batch rows; dD and dbias over batch rows and waves.
-__global__ __launch_bounds__(kBlockThreads) void bwd_reduce_kernel(BwdArgs a, int N, int SA, float* dB, float* dC,
-                                                                   float* dA, float* dD, float* dbias) {
+// groups; dA, dD and dbias over batch rows.
+__global__ __launch_bounds__(kBlockThreads) void bwd_reduce_kernel(BwdArgs a, int N, float* dB, float* dC, float* dA,
+                                                                   float* dD, float* dbias) {
   const int64_t i = (int64_t)blockIdx.x * kBlockThreads + threadIdx.x;
   const int64_t bnl = a.batch * N * a.seqlen;
   if (i < bnl) {
@@ -1625,11 +1684,10 @@ __global__ __launch_bounds__(kBlockThreads) void bwd_reduce_kernel(BwdArgs a, in
   }
   if (i < a.dim) {
     float sd = 0.0f, sb = 0.0f;
-    for (int64_t b = 0; b < a.batch; ++b)
-      for (int w = 0; w < SA; ++w) {
-        sd += a.dD_part[(b * SA + w) * a.dim + i];
-        sb += a.dbias_part[(b * SA + w) * a.dim + i];
-      }
+    for (int64_t b = 0; b < a.batch; ++b) {
+      sd += a.dD_part[b * a.dim + i];
+      sb += a.dbias_part[b * a.dim + i];
+    }
     if (dD) dD[i] = sd;
     if (dbias) dbias[i] = sb;
   }
@@ -2139,8 +2197,7 @@ hipError_t launch_conv(const ScanArgs& a, void* u, hipStream_t st) {
 template <typename IoT, int N, bool kZ, bool kSp, bool kZoh>
 hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
   constexpr int S = (N >= SSM_SPLIT_WAVES) ? SSM_SPLIT_WAVES : N;
-  constexpr int SA = (S > 4) ? 4 : S;
-  hipLaunchKernelGGL((scan_bwd_kernel<IoT, N, S, SA, kZ, kSp, kZoh>), dim3((unsigned)(a.batch * a.groups)),
+  hipLaunchKernelGGL((scan_bwd_kernel<IoT, N, S, kZ, kSp, kZoh>), dim3((unsigned)(a.batch * a.groups)),
                      dim3(64 * S), 0, st, a);
   return hipGetLastError();
 }
@@ -2160,14 +2217,14 @@ hipError_t launch_bwd_n(const BwdArgs& a, hipStream_t st, bool sp, bool zoh) {
 // Complex A: NC complex states (2 NC slots), one per wave.
 template <typename IoT, int NC>
 hipError_t launch_bwd_cplx(const BwdArgs& a, hipStream_t st, bool sp) {
-  constexpr int N = 2 * NC, S = NC, SA = 4;
+  constexpr int N = 2 * NC, S = NC;
   const dim3 grid((unsigned)(a.batch * a.groups)), block(64 * S);
   if (a.z) {
-    if (sp) hipLaunchKernelGGL((scan_bwd_kernel<IoT, N, S, SA, true, true, false, true>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((scan_bwd_kernel<IoT, N, S, SA, true, false, false, true>), grid, block, 0, st, a);
+    if (sp) hipLaunchKernelGGL((scan_bwd_kernel<IoT, N, S, true, true, false, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((scan_bwd_kernel<IoT, N, S, true, false, false, true>), grid, block, 0, st, a);
   } else {
-    if (sp) hipLaunchKernelGGL((scan_bwd_kernel<IoT, N, S, SA, false, true, false, true>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((scan_bwd_kernel<IoT, N, S, SA, false, false, false, true>), grid, block, 0, st, a);
+    if (sp) hipLaunchKernelGGL((scan_bwd_kernel<IoT, N, S, false, true, false, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((scan_bwd_kernel<IoT, N, S, false, false, false, true>), grid, block, 0, st, a);
   }
   return hipGetLastError();
 }
@@ -2177,12 +2234,6 @@ hipError_t launch_bwd(const BwdArgs& a, int N, hipStream_t st, bool sp, bool zoh
   if (N == 4) return launch_bwd_n<IoT, 4>(a, st, sp, zoh);
   if (N == 8) return launch_bwd_n<IoT, 8>(a, st, sp, zoh);
   return launch_bwd_n<IoT, 16>(a, st, sp, zoh);
-}
-
-// Waves of the backward (and forward) blocks that do the per-token work.
-int bwd_token_waves(int64_t dstate) {
-  const int S = dstate >= SSM_SPLIT_WAVES ? SSM_SPLIT_WAVES : (int)dstate;
-  return S > 4 ? 4 : S;
 }
 
 // Vector kernels exist for dstate in {4, 8, 16}; every other case runs the
@@ -2560,15 +2611,16 @@ static ssm_status_t scan_bwd_impl(int64_t batch, int64_t dim, int64_t dstate, in
   if (!vec_rows(sh, dstate, seqlen, io, u, delta, B, C, z, dy) || !aligned(du, 16) || !aligned(ddelta, 16) ||
       (dz && !aligned(dz, 16)))
     return SSM_ERR_UNSUPPORTED;
+  // The kernel addresses 64 rows of a block with 32-bit byte offsets.
+  if (seqlen * (int64_t)es >= ((int64_t)1 << 26)) return SSM_ERR_UNSUPPORTED;
 
   const Plan plan = make_plan(sh, batch, dim, dstate, seqlen, io);
   const int64_t groups = plan.groups;
-  const int SA = bwd_token_waves(dstate);
   // Scratch: checkpoints (unless saved), per-group dB/dC partials, per-batch
   // dA, dD, dbias partials.
   const int64_t n_own = saved ? 0 : n_ckpt;
   const int64_t n_part = groups * sh.bnl;
-  const int64_t n_small = sh.bdn + 2 * batch * SA * dim;
+  const int64_t n_small = sh.bdn + 2 * batch * dim;
   const int64_t scratch_floats = n_own + 2 * n_part + n_small;
   hipMemPool_t pool;
   hipError_t e = get_pool(&pool);
@@ -2605,7 +2657,7 @@ static ssm_status_t scan_bwd_impl(int64_t batch, int64_t dim, int64_t dstate, in
   ba.dC_part = ba.dB_part + n_part;
   ba.dA_part = ba.dC_part + n_part;
   ba.dD_part = ba.dA_part + sh.bdn;
-  ba.dbias_part = ba.dD_part + batch * SA * dim;
+  ba.dbias_part = ba.dD_part + batch * dim;
   ba.batch = batch; ba.dim = dim; ba.seqlen = seqlen; ba.groups = groups;
   if (e == hipSuccess) {
     if (cplx) {
@@ -2622,7 +2674,7 @@ static ssm_status_t scan_bwd_impl(int64_t batch, int64_t dim, int64_t dstate, in
   if (e == hipSuccess) {
     const int64_t n = std::max(sh.bnl, std::max(sh.dn, dim));
     const int64_t blocks = (n + kBlockThreads - 1) / kBlockThreads;
-    hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)blocks), dim3(kBlockThreads), 0, hs, ba, (int)dstate, SA, dB,
+    hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)blocks), dim3(kBlockThreads), 0, hs, ba, (int)dstate, dB,
                        dC, dA, dD, ddelta_bias);
     e = hipGetLastError();
   }
