@@ -1285,16 +1285,16 @@ struct BwdShared {
 // conj(Delta Abar h_{t-1}), and du and dDelta take the real parts
 // Re(lambda conj(B)) and Re(lambda conj(A Abar h_{t-1})) in place of lambda B
 // and lambda A Abar h_{t-1}.
-template <typename IoT, int N, int S, bool kZ, bool kSoftplus, bool kZoh = false, bool kCplx = false>
+template <typename IoT, int N, int S, int TW, bool kZ, bool kSoftplus, bool kZoh = false, bool kCplx = false>
 __global__ __launch_bounds__(64 * S) void scan_bwd_kernel(BwdArgs a) {
   constexpr int NS = N / S;
   constexpr int T = kCkptTokens;
   constexpr int NV = 2 * NS * kChunk;  // per-lane products summed over the wave per step: dB, then dC
-  constexpr int EPL = 8 / S;           // token-phase elements per lane (the block's 64 channels x 8 tokens)
+  constexpr int EPL = 8 / TW;          // token-phase elements per lane (the block's 64 channels x 8 tokens)
   using U = Uni<IoT>;
   constexpr int W = U::kWords;
   static_assert(T == 2 * kChunk, "a checkpoint tile is two steps");
-  static_assert(N % S == 0 && NS <= 2 && (S == 4 || S == 8), "backward block shape");
+  static_assert(N % S == 0 && NS <= 2 && (S == 4 || S == 8) && (TW == 4 || TW == 8) && TW <= S, "backward block shape");
   static_assert(!kCplx || (NS == 2 && !kZoh), "complex: one complex state per wave, Delta * B rule");
   __shared__ BwdShared<S> sm;
 
@@ -1333,7 +1333,7 @@ __global__ __launch_bounds__(64 * S) void scan_bwd_kernel(BwdArgs a) {
   float tbias[EPL], tD[EPL], dD_acc[EPL], dbias_acc[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) {
-    tc[e] = w * (8 * EPL) + 8 * e + (lane >> 3);
+    tc[e] = (w % TW) * (8 * EPL) + 8 * e + (lane >> 3);
     const int64_t dg = grp * kWaveThreads + tc[e];
     tact[e] = dg < a.dim;
     const int64_t dgc = tact[e] ? dg : a.dim - 1;
@@ -1400,46 +1400,66 @@ __global__ __launch_bounds__(64 * S) void scan_bwd_kernel(BwdArgs a) {
       sm.kz[r][tl][tc[e]] = kz;
     }
   };
-  // P3 of step s.
-  auto p3 = [&](int64_t s) {
+  // P3 of step s in two parts: the LDS reads, issued right after the
+  // barrier, and the sums and stores, after the step's state phases (so the
+  // reads have long returned).
+  struct P3In {
+    float pch[S];
+    float2 part[S];
+    float dl, u, sgd, g, kz;
+  };
+  auto p3_read = [&](int64_t s, P3In (&q)[EPL]) {
     const int r = (int)(s & 3), pb = (int)(s & 1);
 #pragma unroll
     for (int e = 0; e < EPL; ++e) {
       const int c = tc[e];
-      float sv = sm.pch[pb][0][tl][c];
-      float2 acc = sm.part[pb][0][tl][c];
+#pragma unroll
+      for (int s2 = 0; s2 < S; ++s2) {
+        q[e].pch[s2] = sm.pch[pb][s2][tl][c];
+        q[e].part[s2] = sm.part[pb][s2][tl][c];
+      }
+      q[e].dl = reinterpret_cast<const float2*>(&sm.dx[r][tl >> 1][c])[tl & 1].x;
+      const float2 us = sm.us[r][tl][c];
+      q[e].u = us.x;
+      q[e].sgd = us.y;
+      q[e].g = sm.g[r][tl][c];
+      q[e].kz = sm.kz[r][tl][c];
+    }
+  };
+  auto p3_finish = [&](int64_t s, const P3In (&q)[EPL]) {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      float sv = q[e].pch[0];
+      float2 acc = q[e].part[0];
 #pragma unroll
       for (int s2 = 1; s2 < S; ++s2) {
-        sv += sm.pch[pb][s2][tl][c];
-        const float2 v = sm.part[pb][s2][tl][c];
-        acc.x += v.x;
-        acc.y += v.y;
+        sv += q[e].pch[s2];
+        acc.x += q[e].part[s2].x;
+        acc.y += q[e].part[s2].y;
       }
-      const float dl = reinterpret_cast<const float2*>(&sm.dx[r][tl >> 1][c])[tl & 1].x;
-      const float2 us = sm.us[r][tl][c];
-      const float gt = sm.g[r][tl][c], kzt = sm.kz[r][tl][c];
       // Under zero-order hold the partials already are the dDelta terms (.x)
       // and sum lambda B phi (.y).
-      const float dstep = kZoh ? acc.x : __builtin_fmaf(us.x, acc.y, acc.x);
-      const float duv = kZoh ? __builtin_fmaf(gt, tD[e], acc.y) : __builtin_fmaf(dl, acc.y, gt * tD[e]);
-      const float ddv = dstep * us.y;
+      const float dstep = kZoh ? acc.x : __builtin_fmaf(q[e].u, acc.y, acc.x);
+      const float duv = kZoh ? __builtin_fmaf(q[e].g, tD[e], acc.y) : __builtin_fmaf(q[e].dl, acc.y, q[e].g * tD[e]);
+      const float ddv = dstep * q[e].sgd;
       dbias_acc[e] += ddv;
       if (tact[e]) {
         const uint32_t o = toff[e] + (uint32_t)(s * kChunk * (int64_t)sizeof(IoT));
         Io<IoT>::store1(reinterpret_cast<IoT*>(dup + o), duv);
         Io<IoT>::store1(reinterpret_cast<IoT*>(ddp + o), ddv);
         if (kZ && dzp)
-          Io<IoT>::store1(reinterpret_cast<IoT*>(dzp + o), __builtin_fmaf(tD[e], us.x, kCplx ? 2.0f * sv : sv) * kzt);
+          Io<IoT>::store1(reinterpret_cast<IoT*>(dzp + o),
+                          __builtin_fmaf(tD[e], q[e].u, kCplx ? 2.0f * sv : sv) * q[e].kz);
       }
     }
   };
-  // The token phases that go with the state phases of step s: P0 reads cur
-  // (the inputs of step s - 2) and the inputs of step s - 3 go to nxt (the
-  // load is clamped to step 0 near the start, and its values then unused).
-  auto token_phases = [&](int64_t s, const uint32_t (&cur)[EPL][4], uint32_t (&nxt)[EPL][4]) {
-    load_in(s >= 3 ? s - 3 : 0, nxt);
-    if (s >= 2) p0(s - 2, cur);
-    if (s + 1 < nsteps) p3(s + 1);
+  const bool tw = w < TW;  // this wave runs the token phases
+
+  // g of step s, for P2 (lanes = channels).
+  auto read_g = [&](int64_t s, float (&gv)[kChunk]) {
+    const int r = (int)(s & 3);
+#pragma unroll
+    for (int t = 0; t < kChunk; ++t) gv[t] = sm.g[r][t][lane];
   };
 
   // Checkpointed states of a tile, loaded one tile ahead.
@@ -1474,15 +1494,25 @@ __global__ __launch_bounds__(64 * S) void scan_bwd_kernel(BwdArgs a) {
       U::load8(Cb, bc_off(j, KV - 1), Ct[j]);
     }
     load_ckpt(c > 0 ? c - 1 : 0, nhck);  // (clamped: unconditional loads keep the waits simple)
-    // A tile of two steps reads inA and fills inB, then the reverse.
-    token_phases(s_lo + KV - 1, inA, inB);
-    // ---- P1: the tile's states from its checkpoint
-    float dlv[VT], xv[VT];
+    const int64_t s_hi = s_lo + KV - 1;
+    // Every LDS read of the upper step first: P1's (Delta, x), P2's g, P3's
+    // partials.
+    float dlv[VT], xv[VT], gv[kChunk];
 #pragma unroll
     for (int i = 0; i < VT / 2; ++i) {
       const float4 v = sm.dx[(int)((s_lo + i / 4) & 3)][i % 4][lane];
       dlv[2 * i] = v.x; xv[2 * i] = v.y; dlv[2 * i + 1] = v.z; xv[2 * i + 1] = v.w;
     }
+    read_g(s_hi, gv);
+    P3In p3q[EPL];
+    if (tw && s_hi + 1 < nsteps) p3_read(s_hi + 1, p3q);
+    // P0 of step s_hi - 2 (a tile of two steps reads inA and fills inB, then
+    // the reverse).
+    if (tw) {
+      load_in(s_hi >= 3 ? s_hi - 3 : 0, inB);
+      if (s_hi >= 2) p0(s_hi - 2, inA);
+    }
+    // ---- P1: the tile's states from its checkpoint
     float hs[NS][VT], ab[NS][VT];  // complex: [0] re, [1] im
     if constexpr (kCplx) {
       float hr = hck[0], hi = hck[1];
@@ -1518,10 +1548,7 @@ __global__ __launch_bounds__(64 * S) void scan_bwd_kernel(BwdArgs a) {
     auto p2 = [&](auto k_tag) {
       constexpr int k = decltype(k_tag)::value;
       const int64_t s = s_lo + k;
-      const int r = (int)(s & 3), pb = (int)(s & 1);
-      float gv[kChunk];
-#pragma unroll
-      for (int t = 0; t < kChunk; ++t) gv[t] = sm.g[r][t][lane];
+      const int pb = (int)(s & 1);
       float pv[NV];
 #pragma unroll
       for (int t = kChunk - 1; t >= 0; --t) {
@@ -1603,12 +1630,19 @@ __global__ __launch_bounds__(64 * S) void scan_bwd_kernel(BwdArgs a) {
       }
     };
     p2(std::integral_constant<int, KV - 1>{});
+    if (tw && s_hi + 1 < nsteps) p3_finish(s_hi + 1, p3q);
     lds_barrier();
     if constexpr (KV == 2) {
 #pragma unroll
       for (int j = 0; j < NS; ++j) U::load8(Cb, bc_off(j, 0), Ct[j]);
-      token_phases(s_lo, inB, inA);
+      read_g(s_lo, gv);
+      if (tw) {
+        p3_read(s_lo + 1, p3q);
+        load_in(s_lo >= 3 ? s_lo - 3 : 0, inA);
+        if (s_lo >= 2) p0(s_lo - 2, inB);
+      }
       p2(std::integral_constant<int, 0>{});
+      if (tw) p3_finish(s_lo + 1, p3q);
       lds_barrier();
     }
     if constexpr (KV == 1) {  // (once, at the start) the next tile's first step reads inA
@@ -1623,21 +1657,27 @@ __global__ __launch_bounds__(64 * S) void scan_bwd_kernel(BwdArgs a) {
 
   // Prologue: P0 of the last two steps, and the inputs of the third-last.
   const int64_t ntiles = (L + T - 1) / T;
-  if (nsteps >= 1) {
-    load_in(nsteps - 1, inA);
-    p0(nsteps - 1, inA);
+  if (w < TW) {
+    if (nsteps >= 1) {
+      load_in(nsteps - 1, inA);
+      p0(nsteps - 1, inA);
+    }
+    if (nsteps >= 2) {
+      load_in(nsteps - 2, inA);
+      p0(nsteps - 2, inA);
+    }
+    load_in(nsteps >= 3 ? nsteps - 3 : 0, inA);
   }
-  if (nsteps >= 2) {
-    load_in(nsteps - 2, inA);
-    p0(nsteps - 2, inA);
-  }
-  load_in(nsteps >= 3 ? nsteps - 3 : 0, inA);
   load_ckpt(ntiles - 1, hck);
   lds_barrier();
   int64_t c = ntiles - 1;
   if (L - c * T < T) tile(c--, std::integral_constant<int, 1>{});  // a last tile of kChunk tokens
   for (; c >= 0; --c) tile(c, std::integral_constant<int, 2>{});
-  if (nsteps >= 1) p3(0);
+  if (tw && nsteps >= 1) {
+    P3In q[EPL];
+    p3_read(0, q);
+    p3_finish(0, q);
+  }
 
   if (active) {
 #pragma unroll
@@ -1654,7 +1694,7 @@ __global__ __launch_bounds__(64 * S) void scan_bwd_kernel(BwdArgs a) {
       dD_acc[e] += __shfl_xor(dD_acc[e], m);
       dbias_acc[e] += __shfl_xor(dbias_acc[e], m);
     }
-    if (tact[e] && tl == 0) {
+    if (w < TW && tact[e] && tl == 0) {
       const int64_t dg = grp * kWaveThreads + tc[e];
       a.dD_part[b * a.dim + dg] = dD_acc[e];
       a.dbias_part[b * a.dim + dg] = dbias_acc[e];
@@ -2003,6 +2043,9 @@ constexpr int64_t kMinSegment = 256;    // tokens; keeps the aggregate pass amor
 #ifndef SSM_SPLIT_MIN_BLOCKS
 #define SSM_SPLIT_MIN_BLOCKS 192
 #endif
+#ifndef SSM_BWD_TOKEN_WAVES
+#define SSM_BWD_TOKEN_WAVES 8  // backward waves that run the token phases (4: only the older wave of each SIMD)
+#endif
 #ifndef SSM_SPLIT_WAVES
 #define SSM_SPLIT_WAVES 8
 #endif
@@ -2197,7 +2240,8 @@ hipError_t launch_conv(const ScanArgs& a, void* u, hipStream_t st) {
 template <typename IoT, int N, bool kZ, bool kSp, bool kZoh>
 hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
   constexpr int S = (N >= SSM_SPLIT_WAVES) ? SSM_SPLIT_WAVES : N;
-  hipLaunchKernelGGL((scan_bwd_kernel<IoT, N, S, kZ, kSp, kZoh>), dim3((unsigned)(a.batch * a.groups)),
+  constexpr int TW = (S < SSM_BWD_TOKEN_WAVES) ? S : SSM_BWD_TOKEN_WAVES;
+  hipLaunchKernelGGL((scan_bwd_kernel<IoT, N, S, TW, kZ, kSp, kZoh>), dim3((unsigned)(a.batch * a.groups)),
                      dim3(64 * S), 0, st, a);
   return hipGetLastError();
 }
@@ -2218,13 +2262,14 @@ hipError_t launch_bwd_n(const BwdArgs& a, hipStream_t st, bool sp, bool zoh) {
 template <typename IoT, int NC>
 hipError_t launch_bwd_cplx(const BwdArgs& a, hipStream_t st, bool sp) {
   constexpr int N = 2 * NC, S = NC;
+  constexpr int TW = (S < SSM_BWD_TOKEN_WAVES) ? S : SSM_BWD_TOKEN_WAVES;
   const dim3 grid((unsigned)(a.batch * a.groups)), block(64 * S);
   if (a.z) {
-    if (sp) hipLaunchKernelGGL((scan_bwd_kernel<IoT, N, S, true, true, false, true>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((scan_bwd_kernel<IoT, N, S, true, false, false, true>), grid, block, 0, st, a);
+    if (sp) hipLaunchKernelGGL((scan_bwd_kernel<IoT, N, S, TW, true, true, false, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((scan_bwd_kernel<IoT, N, S, TW, true, false, false, true>), grid, block, 0, st, a);
   } else {
-    if (sp) hipLaunchKernelGGL((scan_bwd_kernel<IoT, N, S, false, true, false, true>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((scan_bwd_kernel<IoT, N, S, false, false, false, true>), grid, block, 0, st, a);
+    if (sp) hipLaunchKernelGGL((scan_bwd_kernel<IoT, N, S, TW, false, true, false, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((scan_bwd_kernel<IoT, N, S, TW, false, false, false, true>), grid, block, 0, st, a);
   }
   return hipGetLastError();
 }
