@@ -1629,8 +1629,13 @@ __global__ __launch_bounds__(64 * S) void scan_bwd_kernel(BwdArgs a) {
           dst[((grp * a.batch + b) * N + w * NS + jj) * L + l + k * kChunk + t] = tot;
       }
     };
+    // Waves w and w + S/2 share a SIMD and the older one (w) wins issue
+    // ties, so it reaches the barrier first; from P2 on the younger one is
+    // given priority, which evens out their arrival.
+    if (w >= S / 2) __builtin_amdgcn_s_setprio(1);
     p2(std::integral_constant<int, KV - 1>{});
     if (tw && s_hi + 1 < nsteps) p3_finish(s_hi + 1, p3q);
+    __builtin_amdgcn_s_setprio(0);
     lds_barrier();
     if constexpr (KV == 2) {
 #pragma unroll
@@ -1641,8 +1646,10 @@ __global__ __launch_bounds__(64 * S) void scan_bwd_kernel(BwdArgs a) {
         load_in(s_lo >= 3 ? s_lo - 3 : 0, inA);
         if (s_lo >= 2) p0(s_lo - 2, inB);
       }
+      if (w >= S / 2) __builtin_amdgcn_s_setprio(1);
       p2(std::integral_constant<int, 0>{});
       if (tw) p3_finish(s_lo + 1, p3q);
+      __builtin_amdgcn_s_setprio(0);
       lds_barrier();
     }
     if constexpr (KV == 1) {  // (once, at the start) the next tile's first step reads inA
