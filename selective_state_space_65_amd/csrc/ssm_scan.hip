@@ -1505,7 +1505,10 @@ __global__ __launch_bounds__(64 * S) void scan_bwd_kernel(BwdArgs a) {
     }
     read_g(s_hi, gv);
     P3In p3q[EPL];
-    if (tw && s_hi + 1 < nsteps) p3_read(s_hi + 1, p3q);
+    // (Under zero-order hold P2 needs every register it can get: P3 reads
+    // its partials after P2 instead.)
+    constexpr bool kEarlyP3 = !kZoh;
+    if (kEarlyP3 && tw && s_hi + 1 < nsteps) p3_read(s_hi + 1, p3q);
     // P0 of step s_hi - 2 (a tile of two steps reads inA and fills inB, then
     // the reverse).
     if (tw) {
@@ -1634,6 +1637,7 @@ __global__ __launch_bounds__(64 * S) void scan_bwd_kernel(BwdArgs a) {
     // given priority, which evens out their arrival.
     if (w >= S / 2) __builtin_amdgcn_s_setprio(1);
     p2(std::integral_constant<int, KV - 1>{});
+    if (!kEarlyP3 && tw && s_hi + 1 < nsteps) p3_read(s_hi + 1, p3q);
     if (tw && s_hi + 1 < nsteps) p3_finish(s_hi + 1, p3q);
     __builtin_amdgcn_s_setprio(0);
     lds_barrier();
@@ -1642,12 +1646,13 @@ __global__ __launch_bounds__(64 * S) void scan_bwd_kernel(BwdArgs a) {
       for (int j = 0; j < NS; ++j) U::load8(Cb, bc_off(j, 0), Ct[j]);
       read_g(s_lo, gv);
       if (tw) {
-        p3_read(s_lo + 1, p3q);
+        if (kEarlyP3) p3_read(s_lo + 1, p3q);
         load_in(s_lo >= 3 ? s_lo - 3 : 0, inA);
         if (s_lo >= 2) p0(s_lo - 2, inB);
       }
       if (w >= S / 2) __builtin_amdgcn_s_setprio(1);
       p2(std::integral_constant<int, 0>{});
+      if (!kEarlyP3 && tw) p3_read(s_lo + 1, p3q);
       if (tw) p3_finish(s_lo + 1, p3q);
       __builtin_amdgcn_s_setprio(0);
       lds_barrier();
