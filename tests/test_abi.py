@@ -322,6 +322,8 @@ def test_bwd_validation(lib):
     assert bwd(lib, dstate=5) == 8                    # valid, but the backward takes dstate 4, 8, 16 only
     assert bwd(lib, seqlen=20) == 8                   # ... and seqlen a multiple of 8
     assert bwd(lib, u=addr(1) + 4) == 8               # ... and 16-byte aligned rows
+    assert bwd(lib, batch=1, dim=1, seqlen=1 << 25, io=1) == 8   # ... and rows under 2^26 bytes (bf16)
+    assert bwd(lib, batch=1, dim=1, seqlen=1 << 24) == 8         # (fp32)
 
 
 def test_plan(lib):
