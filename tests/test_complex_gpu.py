@@ -226,7 +226,7 @@ def test_complex_decode_steps_equal_scan():
     check(np64(st), np64(last), 1e-5, "state")
 
 
-CBWD_SHAPES = [(192, 64, 8, 64), (256, 33, 4, 16), (2, 8, 8, 40), (3, 130, 4, 24)]
+CBWD_SHAPES = [(192, 64, 8, 64), (256, 33, 4, 16), (2, 8, 8, 40), (3, 130, 4, 24), (3, 130, 8, 8)]
 
 
 @pytest.mark.parametrize("io", ["f32", "bf16"])

@@ -173,7 +173,7 @@ def test_saved_checkpoints_match_recompute(io):
                 assert torch.equal(g1[k], g2[k]), k
 
 
-ZOH_SHAPES = [(192, 64, 16, 64), (256, 33, 4, 16), (2, 8, 16, 40), (3, 130, 8, 24)]
+ZOH_SHAPES = [(192, 64, 16, 64), (256, 33, 4, 16), (2, 8, 16, 40), (3, 130, 8, 24), (3, 130, 16, 8)]
 
 
 @pytest.mark.parametrize("io", ["f32", "bf16"])
