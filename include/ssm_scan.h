@@ -281,10 +281,10 @@ ssm_status_t ssm_state_update_ex(int64_t batch, int64_t dim, int64_t dstate, ssm
  *   u, delta, z, y, D, delta_bias: as ssm_scan_fwd.
  *
  * Errors as ssm_scan_fwd (dstate above 8, i.e. above 16 real numbers per
- * channel, is SSM_ERR_DSTATE_UNSUPPORTED), plus SSM_ERR_UNSUPPORTED outside
- * the single-pass kernel: dstate must be 4 or 8, seqlen a multiple of 8, every
- * (batch, dim, seqlen) and B/C buffer 16-byte aligned, and batch *
- * ceil(dim / 64) at least 192 (enough 64-channel groups to fill the chip).
+ * channel, is SSM_ERR_DSTATE_UNSUPPORTED).  dstate 4 or 8 with seqlen a
+ * multiple of 8 and every (batch, dim, seqlen) and B/C buffer 16-byte aligned
+ * runs the single-pass kernel (one complex state per wave); every other shape
+ * a kernel that walks each channel a token at a time (correct, not fast).
  */
 ssm_status_t ssm_scan_fwd_complex(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, ssm_dtype_t io,
                                   const void* u, const void* delta, const float* A, const void* B, const void* C,

@@ -1998,6 +1998,68 @@ __global__ __launch_bounds__(kBlockThreads) void state_update_complex_generic_ke
   Io<IoT>::store1(static_cast<IoT*>(a.y) + ch, epilogue<kZ>(2.0f * acc, a.D ? a.D[d] : 0.0f, uv, zv));
 }
 
+// Complex A on any shape: one thread per (batch row, channel) walks the
+// sequence a token at a time with scalar loads (any seqlen, any alignment,
+// 1..8 complex states), with the per-token arithmetic of the single-pass
+// kernel.  The fallback for the shapes that kernel does not take.
+template <typename IoT, bool kZ, bool kSoftplus>
+__global__ __launch_bounds__(kBlockThreads) void scan_complex_generic_kernel(ScanArgs a, int64_t nc) {
+  const int64_t bd = a.batch * a.dim;
+  const int64_t ch = (int64_t)blockIdx.x * kBlockThreads + threadIdx.x;
+  if (ch >= bd) return;
+  const int64_t b = ch / a.dim, d = ch % a.dim;
+  const int64_t L = a.seqlen;
+  float a2r[8], a2i[8], hr[8], hi[8];
+#pragma unroll
+  for (int n = 0; n < 8; ++n) {
+    const bool on = n < nc;
+    // (Re A log2(e), Im A / 2 pi): the exp2 argument and the rotation in turns per unit of Delta.
+    a2r[n] = on ? a.A[(d * nc + n) * 2] * kLog2e : 0.0f;
+    a2i[n] = on ? a.A[(d * nc + n) * 2 + 1] * kInv2Pi : 0.0f;
+    hr[n] = (on && a.h0) ? a.h0[(ch * nc + n) * 2] : 0.0f;
+    hi[n] = (on && a.h0) ? a.h0[(ch * nc + n) * 2 + 1] : 0.0f;
+  }
+  const float Dd = a.D ? a.D[d] : 0.0f;
+  const float bias = a.bias ? a.bias[d] : 0.0f;
+  const IoT* ur = static_cast<const IoT*>(a.u) + ch * L;
+  const IoT* dr = static_cast<const IoT*>(a.delta) + ch * L;
+  const IoT* zr = kZ ? static_cast<const IoT*>(a.z) + ch * L : nullptr;
+  IoT* yr = static_cast<IoT*>(a.y) + ch * L;
+  const IoT* Bb = static_cast<const IoT*>(a.B) + b * nc * L * 2;  // [nc][seqlen][2] of this batch row
+  const IoT* Cb = static_cast<const IoT*>(a.C) + b * nc * L * 2;
+  for (int64_t l = 0; l < L; ++l) {
+    const float uv = Io<IoT>::load1(ur + l);
+    const float dl = discretize_delta<kSoftplus>(Io<IoT>::load1(dr + l), bias);
+    const float xl = dl * uv;
+    float acc = 0.0f;
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+      if (n < nc) {
+        const float mag = exp2_hw(a2r[n] * dl);
+        const float turn = __builtin_amdgcn_fractf(a2i[n] * dl);
+        const float pr = mag * __builtin_amdgcn_cosf(turn), pi = mag * __builtin_amdgcn_sinf(turn);
+        const int64_t o = (n * L + l) * 2;
+        const float br = Io<IoT>::load1(Bb + o), bi = Io<IoT>::load1(Bb + o + 1);
+        const float nr = __builtin_fmaf(pr, hr[n], __builtin_fmaf(-pi, hi[n], br * xl));
+        const float ni = __builtin_fmaf(pr, hi[n], __builtin_fmaf(pi, hr[n], bi * xl));
+        hr[n] = nr;
+        hi[n] = ni;
+        acc = __builtin_fmaf(Io<IoT>::load1(Cb + o), nr, __builtin_fmaf(-Io<IoT>::load1(Cb + o + 1), ni, acc));
+      }
+    }
+    Io<IoT>::store1(yr + l, epilogue<kZ>(2.0f * acc, Dd, uv, kZ ? Io<IoT>::load1(zr + l) : 0.0f));
+  }
+  if (a.last_state) {
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+      if (n < nc) {
+        a.last_state[(ch * nc + n) * 2] = hr[n];
+        a.last_state[(ch * nc + n) * 2 + 1] = hi[n];
+      }
+    }
+  }
+}
+
 // ----------------------------------------------------------------------------
 // Host side: validation, planning, dispatch
 // ----------------------------------------------------------------------------
@@ -2367,6 +2429,20 @@ hipError_t launch_update_cplx_t(const UpdateArgs& a, int64_t nc, hipStream_t st,
 }
 
 template <typename IoT>
+hipError_t launch_scan_cplx_generic(const ScanArgs& a, int64_t nc, hipStream_t st, bool sp) {
+  const int64_t bd = a.batch * a.dim;
+  const dim3 grid((unsigned)((bd + kBlockThreads - 1) / kBlockThreads)), block(kBlockThreads);
+  if (a.z) {
+    if (sp) hipLaunchKernelGGL((scan_complex_generic_kernel<IoT, true, true>), grid, block, 0, st, a, nc);
+    else hipLaunchKernelGGL((scan_complex_generic_kernel<IoT, true, false>), grid, block, 0, st, a, nc);
+  } else {
+    if (sp) hipLaunchKernelGGL((scan_complex_generic_kernel<IoT, false, true>), grid, block, 0, st, a, nc);
+    else hipLaunchKernelGGL((scan_complex_generic_kernel<IoT, false, false>), grid, block, 0, st, a, nc);
+  }
+  return hipGetLastError();
+}
+
+template <typename IoT>
 hipError_t launch_update_cplx(const UpdateArgs& a, int64_t nc, hipStream_t st, bool generic, bool sp) {
   if (a.z)
     return sp ? launch_update_cplx_t<IoT, true, true>(a, nc, st, generic)
@@ -2550,18 +2626,23 @@ ssm_status_t ssm_scan_fwd_complex(int64_t batch, int64_t dim, int64_t dstate, in
   if (!u || !delta || !A || !B || !C || !y) return SSM_ERR_NULL;
   st = check_scan_buffers(sh, dim, io, u, delta, A, B, C, D, z, delta_bias, h0, y, last_state, nullptr, 0, nullptr);
   if (st != SSM_OK) return st;
-  Plan plan = make_plan(sh, batch, dim, slots, seqlen, io);
-  if (!(dstate == 4 || dstate == 8) || !plan.split || !vec_rows(sh, slots, seqlen, io, u, delta, B, C, z, y))
-    return SSM_ERR_UNSUPPORTED;
   ScanArgs a = scan_args(sh, batch, dim, slots, seqlen, io, u, delta, A, B, C, D, z, delta_bias, h0, y, last_state);
-  a.groups = plan.groups; a.segments = 1; a.seg_len = seqlen;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   const bool sp = softplus_flag != 0;
   hipError_t e;
-  if (io == SSM_BF16)
-    e = dstate == 4 ? launch_split_cplx<bf16_t, 4>(a, plan, hs, sp) : launch_split_cplx<bf16_t, 8>(a, plan, hs, sp);
-  else
-    e = dstate == 4 ? launch_split_cplx<float, 4>(a, plan, hs, sp) : launch_split_cplx<float, 8>(a, plan, hs, sp);
+  if ((dstate == 4 || dstate == 8) && vec_rows(sh, slots, seqlen, io, u, delta, B, C, z, y)) {
+    // The single-pass kernel, on any number of 64-channel groups.
+    Plan plan = make_plan(sh, batch, dim, slots, seqlen, io);
+    plan.split = true; plan.segments = 1; plan.seg_len = seqlen; plan.scratch_bytes = 0;
+    a.groups = (dim + kWaveThreads - 1) / kWaveThreads; a.segments = 1; a.seg_len = seqlen;
+    if (io == SSM_BF16)
+      e = dstate == 4 ? launch_split_cplx<bf16_t, 4>(a, plan, hs, sp) : launch_split_cplx<bf16_t, 8>(a, plan, hs, sp);
+    else
+      e = dstate == 4 ? launch_split_cplx<float, 4>(a, plan, hs, sp) : launch_split_cplx<float, 8>(a, plan, hs, sp);
+  } else {
+    e = (io == SSM_BF16) ? launch_scan_cplx_generic<bf16_t>(a, dstate, hs, sp)
+                         : launch_scan_cplx_generic<float>(a, dstate, hs, sp);
+  }
   if (e != hipSuccess) return hip_fail(e);
   return SSM_OK;
 }

@@ -175,10 +175,7 @@ def test_complex_validation(lib):
     assert cplx(lib, y=addr(2) + 8) == 6
     # A is (dim, dstate, 2): last_state overlapping A's second half is an alias.
     assert cplx(lib, last=addr(3) + 8 * 4 * 4) == 6
-    # Valid calls outside the single-pass kernel are refused before any launch.
-    assert cplx(lib) == 8                      # 2 x 1 groups of 64 channels: too few blocks
-    assert cplx(lib, batch=192, dim=64, dstate=2) == 8
-    assert cplx(lib, batch=192, dim=64, seqlen=12) == 8
+    # (Every valid shape runs: the other complex shapes are tested on the GPU.)
 
 
 def cupd(lib, batch=2, dim=8, dstate=4, io=0, **over):

@@ -163,12 +163,62 @@ def test_complex_mamba1p4b_shape_sampled():
     check(np.stack([hg[bb, dd] for bb, dd in ch]), np.stack([hr.real, hr.imag], -1), TOL["f32"], "last_state")
 
 
-def test_complex_unsupported_shapes():
-    for shape in ((2, 64, 8, 64), (192, 64, 2, 64), (192, 64, 8, 60)):
-        x, A, B, C, hh = complex_inputs(*shape, "f32", 4500)
-        with pytest.raises(binding.SsmError) as e:
-            run(x, A, B, C, hh)
-        assert e.value.name == "SSM_ERR_UNSUPPORTED"
+# Shapes off the fast path: few 64-channel groups (the single-pass kernel on a
+# small grid), and dstate, seqlen or dim that only the per-token kernel takes.
+OTHER_SHAPES = [((2, 64, 8, 64), "single pass, 2 groups"), ((1, 130, 4, 40), "single pass, 3 groups"),
+                ((192, 64, 2, 64), "generic: 2 complex states"), ((96, 64, 8, 60), "generic: seqlen 60"),
+                ((3, 33, 5, 17), "generic: 5 states, seqlen 17"), ((2, 7, 1, 9), "generic: 1 state"),
+                ((4, 65, 7, 1), "generic: 7 states, one token")]
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("shape,what", OTHER_SHAPES, ids=[w for _, w in OTHER_SHAPES])
+def test_complex_other_shapes(io, shape, what):
+    b, d, n, l = shape
+    for mask in (31, 10):
+        zf, Df, bf, spf, hf = [(mask >> i) & 1 == 1 for i in range(5)]
+        say("complex other shape=%s (%s) io=%s mask=%d" % (shape, what, io, mask))
+        x, A, B, C, hh = complex_inputs(b, d, n, l, io, 4500 + mask, z=zf, D=Df, bias=bf, softplus=spf, h0=hf)
+        if not spf:
+            x.delta = inputs.round_bf16(np.abs(x.delta) * np.float32(0.2)) if io == "bf16" else \
+                np.abs(x.delta) * np.float32(0.2)
+            if bf:
+                x.delta_bias = np.full(d, 0.01, np.float32)
+        y, last = run(x, A, B, C, hh)
+        yr, hr = reference(x, A, B, C, hh)
+        check(np64(y), yr, TOL[io], "y mask=%d" % mask)
+        check(np64(last), np.stack([hr.real, hr.imag], -1), TOL["f32"], "last_state mask=%d" % mask)
+
+
+def test_complex_misaligned_rows_and_carry_in_place():
+    """Rows that are not 16-byte aligned take the per-token kernel; h0 == last_state carries the
+    state across two calls there too."""
+    x, A, B, C, hh = complex_inputs(8, 64, 4, 48, "f32", 4550)
+    yr, hr = reference(x, A, B, C, hh)
+    t = inputs.to_torch(x, DEV)
+    st = torch.from_numpy(hh).to(DEV)
+    At = torch.from_numpy(A).to(DEV)
+
+    def misaligned(src):  # a contiguous copy whose data starts 4 bytes past a 16-byte boundary
+        buf = torch.empty(src.numel() + 1, device=DEV, dtype=src.dtype)
+        v = buf[1:].view(src.shape)
+        v.copy_(src)
+        return v
+
+    ys = []
+    for lo, hi in ((0, 24), (24, 48)):
+        say("complex misaligned u, tokens %d..%d" % (lo, hi))
+        u = misaligned(t["u"][..., lo:hi].contiguous())
+        assert u.data_ptr() % 16 != 0
+        y, _ = binding.scan_fwd_complex(u, t["delta"][..., lo:hi].contiguous(), At,
+                                        torch.from_numpy(np.ascontiguousarray(B[:, :, lo:hi])).to(DEV),
+                                        torch.from_numpy(np.ascontiguousarray(C[:, :, lo:hi])).to(DEV), D=t["D"],
+                                        z=t["z"][..., lo:hi].contiguous(), delta_bias=t["delta_bias"],
+                                        delta_softplus=True, h0=st, last_state=st)
+        ys.append(y)
+    torch.cuda.synchronize()
+    check(np64(torch.cat(ys, -1)), yr, TOL["f32"], "y")
+    check(np64(st), np.stack([hr.real, hr.imag], -1), TOL["f32"], "state")
 
 
 @pytest.mark.parametrize("io", ["f32", "bf16"])
