@@ -318,3 +318,33 @@ def test_complex_bwd_matches_oracle(io, shape):
         for k in ("dA", "dB", "dC", "dh0"):
             want = np.stack([r[k].real, r[k].imag], -1)
             check(np64(g[k]), want, TOL["f32"], "%s mask=%d" % (k, mask))
+
+
+def test_complex_bwd_mamba1p4b_shape_sampled():
+    """The complex backward at the Mamba-1.4B shape (8 complex states, bf16); the per-channel
+    gradients and sums checked on sampled channels against the oracle's complex backward."""
+    b, d, n, l = 4, 4096, 8, 4096
+    x, A, B, C, hh = complex_inputs(b, d, n, l, "bf16", 4900, h0=True)
+    rng = np.random.default_rng([4901])
+    dy = inputs.round_bf16(rng.standard_normal((b, d, l)).astype(np.float32))
+    dlast = rng.standard_normal((b, d, n, 2)).astype(np.float32)
+    say("complex bwd 4x4096x8cx4096 bf16, sampled channels")
+    t = inputs.to_torch(x, DEV)
+    dt = t["u"].dtype
+    g = binding.scan_bwd_complex(t["u"], t["delta"], torch.from_numpy(A).to(DEV), torch.from_numpy(B).to(DEV, dt),
+                                 torch.from_numpy(C).to(DEV, dt), torch.from_numpy(dy).to(DEV, dt), D=t["D"], z=t["z"],
+                                 delta_bias=t["delta_bias"], delta_softplus=x.softplus,
+                                 h0=torch.from_numpy(hh).to(DEV), dlast=torch.from_numpy(dlast).to(DEV))
+    torch.cuda.synchronize()
+    for dd in (0, 2222, 4095):
+        sl = lambda a: None if a is None else a[:, dd:dd + 1]
+        r = oracle.scan_complex_bwd_f64(sl(x.u), sl(x.delta), cplx(A[dd:dd + 1]), cplx(B), cplx(C), x.D[dd:dd + 1],
+                                        sl(x.z), x.delta_bias[dd:dd + 1], x.softplus, cplx(hh[:, dd:dd + 1]), dy=sl(dy),
+                                        dlast=cplx(dlast[:, dd:dd + 1]))
+        for k in ("du", "ddelta", "dz"):
+            check(np64(g[k][:, dd:dd + 1]), r[k], TOL["bf16"], "channel %d %s" % (dd, k))
+        for k in ("dD", "ddelta_bias"):
+            check(np64(g[k][dd:dd + 1]), r[k], TOL["f32"], "channel %d %s" % (dd, k))
+        check(np64(g["dA"][dd:dd + 1]), np.stack([r["dA"].real, r["dA"].imag], -1), TOL["f32"], "channel %d dA" % dd)
+        check(np64(g["dh0"][:, dd:dd + 1]), np.stack([r["dh0"].real, r["dh0"].imag], -1), TOL["f32"],
+              "channel %d dh0" % dd)
