@@ -17,6 +17,7 @@ this module only marshals numpy arrays into it.
   .scan_bwd_f64(...)       gradients of the scan (reverse mode, written out by hand)
   .scan_complex_f64(...)   the scan with complex diagonal A (complex B, C, state)
   .conv1d_f64(...)         the causal depthwise conv (+ silu) in front of the scan
+  .conv1d_bwd_f64(...)     its gradients (reverse mode, written out by hand)
   .softplus_f64, .silu_f64 the scalar helpers the C oracle uses
 Module-level functions of the same names use the default oracle.
 """
@@ -71,6 +72,8 @@ class Oracle:
         L.oracle_scan_complex_bwd_f64.argtypes = [I64, I64, I64, I64] + [P] * 8 + [I] + [P] * 12
         L.oracle_conv1d_f64.restype = I
         L.oracle_conv1d_f64.argtypes = [I64, I64, I64, I64, P, P, P, P, I, P]
+        L.oracle_conv1d_bwd_f64.restype = I
+        L.oracle_conv1d_bwd_f64.argtypes = [I64, I64, I64, I64, P, P, P, P, I, P, P, P, P, P]
         L.oracle_softplus.restype = ctypes.c_double
         L.oracle_softplus.argtypes = [ctypes.c_double]
         L.oracle_silu.restype = ctypes.c_double
@@ -204,6 +207,22 @@ class Oracle:
             raise ValueError("oracle_conv1d_f64 rejected the arguments")
         return u
 
+    def conv1d_bwd_f64(self, x, weight, du, bias=None, x_prev=None, silu=True):
+        """Gradients of conv1d_f64 for a loss with dL/du = du: dict of dx (batch, dim, seqlen),
+        dweight (dim, K), dbias (dim,) and dx_prev (batch, dim, K-1), all float64."""
+        x, weight, bias, du = _f64(x), _f64(weight), _f64(bias), _f64(du)
+        batch, dim, seqlen = x.shape
+        width = weight.shape[1]
+        xp = None if x_prev is None or width == 1 else _f64(x_prev)
+        out = dict(dx=np.empty((batch, dim, seqlen), np.float64), dweight=np.empty((dim, width), np.float64),
+                   dbias=np.empty(dim, np.float64), dx_prev=np.zeros((batch, dim, width - 1), np.float64))
+        rc = self.lib.oracle_conv1d_bwd_f64(batch, dim, seqlen, width, _p(x), _p(weight), _p(bias), _p(xp),
+                                            1 if silu else 0, _p(du), _p(out["dx"]), _p(out["dweight"]),
+                                            _p(out["dbias"]), _p(out["dx_prev"]) if width > 1 else None)
+        if rc != 0:
+            raise ValueError("oracle_conv1d_bwd_f64 rejected the arguments")
+        return out
+
     def scan_channels_f64(self, channels, u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=False,
                           h0=None, zoh=False):
         """Scan only the listed (b, d) channels; returns (y[k, seqlen], last_state[k, dstate]).
@@ -299,6 +318,10 @@ def scan_complex_channels_f64(*args, **kw):
 
 def conv1d_f64(*args, **kw):
     return default().conv1d_f64(*args, **kw)
+
+
+def conv1d_bwd_f64(*args, **kw):
+    return default().conv1d_bwd_f64(*args, **kw)
 
 
 def zoh_b_f64(delta, a):

@@ -88,7 +88,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-#define ORACLE_ABI_VERSION 5
+#define ORACLE_ABI_VERSION 6
 
 int oracle_abi_version(void) { return ORACLE_ABI_VERSION; }
 
@@ -410,6 +410,60 @@ int oracle_conv1d_f64(int64_t batch, int64_t dim, int64_t seqlen, int64_t width,
       }
       u[ch * seqlen + l] = silu_flag ? oracle_silu(acc) : acc;
     }
+  }
+  return 0;
+}
+
+/* Gradients of oracle_conv1d_f64 for a scalar loss with dL/du = du, by
+ * reverse-mode differentiation of its loop (the chain rule written out; the
+ * pages give no backward):
+ *   v_l        = cb[d] + sum_k w[d,k] x_{l-(K-1)+k}               (pre-activation)
+ *   dv_l       = du_l silu'(v_l), silu'(v) = s (1 + v (1 - s)), s = sigmoid(v); du_l without silu
+ *   dx_p      += w[d,k] dv_l for every tap k of every token l that reads position p = l-(K-1)+k;
+ *               positions p < 0 are x_prev slot (K-1) + p and go to dx_prev
+ *   dw[d,k]   += dv_l x_{l-(K-1)+k};  dcb[d] += dv_l   (summed over batch rows and tokens)
+ * dx, dw, dcb are written; dx_prev is written when not NULL (zero when K = 1).
+ * Returns 0, or -1 on bad sizes or a missing required pointer. */
+int oracle_conv1d_bwd_f64(int64_t batch, int64_t dim, int64_t seqlen, int64_t width, const double* x,
+                          const double* w, const double* cb, const double* x_prev, int silu_flag,
+                          const double* du, double* dx, double* dw, double* dcb, double* dx_prev) {
+  if (batch < 1 || dim < 1 || seqlen < 1 || width < 1 || width > 4) return -1;
+  if (!x || !w || !du || !dx || !dw || !dcb) return -1;
+  const int64_t hist = width - 1;
+#pragma omp parallel for schedule(static)
+  for (int64_t d = 0; d < dim; ++d) {
+    double gw[4] = {0.0, 0.0, 0.0, 0.0}, gb = 0.0;
+    for (int64_t b = 0; b < batch; ++b) {
+      const int64_t ch = b * dim + d;
+      for (int64_t p = 0; p < seqlen; ++p) dx[ch * seqlen + p] = 0.0;
+      if (dx_prev)
+        for (int64_t j = 0; j < hist; ++j) dx_prev[ch * hist + j] = 0.0;
+      for (int64_t l = 0; l < seqlen; ++l) {
+        double v = cb ? cb[d] : 0.0;
+        double in[4];
+        for (int64_t k = 0; k < width; ++k) {
+          const int64_t src = l - hist + k;
+          in[k] = src >= 0 ? x[ch * seqlen + src] : (x_prev ? x_prev[ch * hist + hist + src] : 0.0);
+          v += w[d * width + k] * in[k];
+        }
+        double dv = du[ch * seqlen + l];
+        if (silu_flag) {
+          const double s = 1.0 / (1.0 + exp(-v));
+          dv *= s * (1.0 + v * (1.0 - s));
+        }
+        for (int64_t k = 0; k < width; ++k) {
+          const int64_t src = l - hist + k;
+          if (src >= 0)
+            dx[ch * seqlen + src] += w[d * width + k] * dv;
+          else if (dx_prev)
+            dx_prev[ch * hist + hist + src] += w[d * width + k] * dv;
+          gw[k] += dv * in[k];
+        }
+        gb += dv;
+      }
+    }
+    for (int64_t k = 0; k < width; ++k) dw[d * width + k] = gw[k];
+    dcb[d] = gb;
   }
   return 0;
 }

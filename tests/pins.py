@@ -53,6 +53,10 @@ deliberately broken copies of it (tests/test_oracle_mutants.py).
                     K_k = sum_n C_n Abar_n^k Delta B_n (numpy complex powers, np.convolve)
   complex_bwd       the complex-A gradients (d/dRe + i d/dIm) against central finite
                     differences of the complex forward and torch's complex autograd
+  conv_bwd_finite_diff  the conv's gradients (x, weight, bias, x_prev) against central
+                    finite differences of the conv oracle, every width, silu on and off
+  conv_bwd_autograd the same gradients against torch autograd (fp64, CPU) through
+                    torch.nn.functional.conv1d (groups = dim) over [x_prev, x]
 """
 import json
 import math
@@ -714,7 +718,58 @@ def complex_bwd(o):
                    1e-11 * max(1.0, float(np.abs(ref[name]).max())), "complex autograd d/d%s" % name)
 
 
+def conv_bwd_finite_diff(o):
+    rng = _rng(24)
+    batch, dim, seqlen = 2, 3, 9
+    eps = 1e-6
+    for width in (1, 2, 3, 4):
+        for silu in (False, True):
+            p = _conv_problem(rng, batch, dim, seqlen, width)
+            du = rng.standard_normal((batch, dim, seqlen))
+            g = o.conv1d_bwd_f64(p["x"], p["weight"], du, bias=p["bias"], x_prev=p["x_prev"], silu=silu)
+
+            def loss(q):
+                return float((du * o.conv1d_f64(q["x"], q["weight"], q["bias"], q["x_prev"], silu=silu)).sum())
+
+            for name, key in (("x", "dx"), ("weight", "dweight"), ("bias", "dbias"), ("x_prev", "dx_prev")):
+                base = p[name]
+                num = np.zeros(base.shape)
+                for i in range(base.size):
+                    up, dn = base.copy(), base.copy()
+                    up.flat[i] += eps
+                    dn.flat[i] -= eps
+                    num.flat[i] = (loss(dict(p, **{name: up})) - loss(dict(p, **{name: dn}))) / (2 * eps)
+                _close(g[key], num, 0.0, 2e-8, "conv K=%d silu=%s d/d%s" % (width, silu, name))
+    # No x_prev: the history is zero and its gradient is still reported (as what x_prev would get).
+    p = _conv_problem(rng, 1, 2, 6, 3)
+    du = rng.standard_normal((1, 2, 6))
+    g0 = o.conv1d_bwd_f64(p["x"], p["weight"], du, bias=p["bias"], x_prev=None, silu=True)
+    gz = o.conv1d_bwd_f64(p["x"], p["weight"], du, bias=p["bias"], x_prev=np.zeros((1, 2, 2)), silu=True)
+    for k in ("dx", "dweight", "dbias", "dx_prev"):
+        _close(g0[k], gz[k], 1e-15, 1e-15, "conv no x_prev %s" % k)
+
+
+def conv_bwd_autograd(o):
+    import torch
+    import torch.nn.functional as F
+    rng = _rng(25)
+    batch, dim, seqlen = 3, 4, 17
+    for width in (1, 2, 4):
+        for silu in (False, True):
+            p = _conv_problem(rng, batch, dim, seqlen, width)
+            du = rng.standard_normal((batch, dim, seqlen))
+            g = o.conv1d_bwd_f64(p["x"], p["weight"], du, bias=p["bias"], x_prev=p["x_prev"], silu=silu)
+            t = {k: torch.tensor(v, dtype=torch.float64, requires_grad=True) for k, v in p.items()}
+            xin = torch.cat([t["x_prev"], t["x"]], dim=-1)  # [x_prev, x]: the K-1 inputs before token 0 first
+            v = F.conv1d(xin, t["weight"].unsqueeze(1), t["bias"], groups=dim)
+            u = F.silu(v) if silu else v
+            (u * torch.tensor(du)).sum().backward()
+            for name, key in (("x", "dx"), ("weight", "dweight"), ("bias", "dbias"), ("x_prev", "dx_prev")):
+                _close(g[key], t[name].grad.numpy(), 1e-12, 1e-12, "conv autograd K=%d silu=%s d/d%s" %
+                       (width, silu, name))
+
+
 ALL = [worked_examples, lti_closed_form, bruteforce, single_step, persistence, forgetting, split_carry, linearity,
        softplus_silu, decode_is_scan, channel_subset, conv_library, conv_taps, conv_causality, conv_split_carry,
        bwd_finite_diff, bwd_autograd, zoh_van_loan, zoh_fixed_point, zoh_limits, zoh_decode, zoh_bwd, complex_real_limit,
-       complex_block_expm, complex_lti, complex_bwd]
+       complex_block_expm, complex_lti, complex_bwd, conv_bwd_finite_diff, conv_bwd_autograd]

@@ -77,6 +77,15 @@ MUTANTS = [
     ("cplx_bwd_softplus_grad_dropped", "softplus_flag ? dstep / (1.0 + exp(-x)) : dstep", "softplus_flag ? dstep : dstep", 1),
     ("cplx_bwd_dz_sign", "(1.0 + zt * (1.0 - sg))", "(1.0 - zt * (1.0 - sg))", 1),
     ("cplx_bwd_dD_after_gate", "        partD[ch] += g * ut;", "        partD[ch] += dy[ch * seqlen + t] * ut;", 1),
+    ("conv_bwd_silu_grad_dropped", "dv *= s * (1.0 + v * (1.0 - s));", "dv *= s;"),
+    ("conv_bwd_silu_at_no_bias", "        double v = cb ? cb[d] : 0.0;\n        double in[4];",
+     "        double v = 0.0;\n        double in[4];"),
+    ("conv_bwd_dx_taps_reversed", "dx[ch * seqlen + src] += w[d * width + k] * dv;",
+     "dx[ch * seqlen + src] += w[d * width + (width - 1 - k)] * dv;"),
+    ("conv_bwd_prev_grad_dropped", "dx_prev[ch * hist + hist + src] += w[d * width + k] * dv;",
+     "dx_prev[ch * hist + hist + src] += 0.0 * dv;"),
+    ("conv_bwd_dw_taps_reversed", "gw[k] += dv * in[k];", "gw[k] += dv * in[width - 1 - k];"),
+    ("conv_bwd_bias_grad_dropped", "        gb += dv;", "        gb += 0.0 * dv;"),
 ]
 # A site written twice (the real and the complex backward) is mutated at the
 # named occurrence (0 = first); every other site must occur exactly once.
