@@ -68,7 +68,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 9
+#define SSM_ABI_VERSION 10
 
 struct ihipStream_t; /* the same incomplete type as HIP's hipStream_t */
 
@@ -178,6 +178,38 @@ ssm_status_t ssm_conv_scan_fwd(int64_t batch, int64_t dim, int64_t dstate, int64
                                const void* B, const void* C, const float* D, const void* z,
                                const float* delta_bias, int softplus_flag, const float* h0, void* y,
                                float* last_state, void* u_out, struct ihipStream_t* stream);
+
+/*
+ * ssm_conv_bwd -- gradients of the conv that ssm_conv_scan_fwd fuses in front
+ * of the scan, for training: given du = dL/du (ssm_scan_bwd's du for the u the
+ * scan consumed), with v the pre-activation conv_bias[d] + sum_k
+ * conv_weight[d,k] x[b,d,l-(K-1)+k] (recomputed; the io rounding of u is
+ * passed through):
+ *
+ *   dv[b,d,l]         = du[b,d,l] * silu'(v[b,d,l])   (du itself when conv_silu is 0)
+ *   dx[b,d,p]         = sum_k conv_weight[d,k] * dv[b,d,p+(K-1)-k]   (dv past the end is 0)
+ *   dx_prev[b,d,j]    = sum_{k<=j} conv_weight[d,k] * dv[b,d,j-k]    (the history slots x_prev)
+ *   dconv_weight[d,k] = sum_{b,l} dv[b,d,l] * x[b,d,l-(K-1)+k]       (x before token 0 from x_prev)
+ *   dconv_bias[d]     = sum_{b,l} dv[b,d,l]
+ *
+ *   x, conv_weight, conv_bias, x_prev, conv_silu, conv_width: as ssm_conv_scan_fwd
+ *   du            [batch, dim, seqlen]         io    read
+ *   dx            [batch, dim, seqlen]         io    written
+ *   dconv_weight  [dim, conv_width]            fp32  written
+ *   dconv_bias    [dim]                        fp32  written when not NULL
+ *   dx_prev       [batch, dim, conv_width-1]   io    written when not NULL (ignored when conv_width == 1)
+ *
+ * Outputs must not overlap inputs or each other.  Errors: SSM_ERR_DTYPE,
+ * SSM_ERR_SHAPE (a size below 1, conv_width outside 1..4, sizes that
+ * overflow), SSM_ERR_NULL (x, conv_weight, du, dx, dconv_weight),
+ * SSM_ERR_ALIGN (io buffers to their element, fp32 buffers to 4 bytes),
+ * SSM_ERR_ALIAS.  Uses stream-ordered scratch from the library's pool for the
+ * per-block sums; deterministic (fixed summation order).
+ */
+ssm_status_t ssm_conv_bwd(int64_t batch, int64_t dim, int64_t seqlen, int64_t conv_width, ssm_dtype_t io,
+                          const void* x, const float* conv_weight, const float* conv_bias, const void* x_prev,
+                          int conv_silu, const void* du, void* dx, float* dconv_weight, float* dconv_bias,
+                          void* dx_prev, struct ihipStream_t* stream);
 
 /*
  * ssm_scan_bwd -- gradients of the scan for training: given dy = dL/dy and

@@ -45,6 +45,7 @@ SIGNATURES = {
     "ssm_state_update_complex": (_I, [_I64, _I64, _I64, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P]),
     "ssm_conv_scan_fwd": (_I, [_I64, _I64, _I64, _I64, _I64, _I, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _I, _P,
                                _P, _P, _P, _P]),
+    "ssm_conv_bwd": (_I, [_I64, _I64, _I64, _I64, _I, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P]),
     "ssm_scan_bwd": (_I, [_I64, _I64, _I64, _I64, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P,
                           _P, _P, _P, _P, _P]),
     "ssm_scan_bwd_ex": (_I, [_I64, _I64, _I64, _I64, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P,
@@ -412,6 +413,43 @@ def conv_scan_fwd(x, conv_weight, delta, A, B, C, D=None, z=None, delta_bias=Non
                                _ptr(out), _ptr(last_state), _ptr(u_out), _stream(dev, stream))
     _check("ssm_conv_scan_fwd", st)
     return out, last_state
+
+
+def conv_bwd(x, conv_weight, du, conv_bias=None, x_prev=None, conv_silu=True, stream=None):
+    """Gradients of the conv of conv_scan_fwd for dL/du = du (ssm_conv_bwd).
+
+    du is the gradient with respect to the u the scan consumed (scan_bwd's du).
+    Returns a dict: dx (io dtype, like x), dconv_weight (dim, K) float32,
+    dconv_bias (dim,) float32 and dx_prev (batch, dim, K-1) in the io dtype
+    (the gradient for the x_prev history; zeros-shaped (batch, dim, 0) when K == 1).
+    """
+    import torch
+    if x.dim() != 3:
+        raise ValueError("x must be (batch, dim, seqlen)")
+    batch, dim, seqlen = x.shape
+    dev = x.device
+    io = x.dtype
+    if conv_weight.dim() != 2:
+        raise ValueError("conv_weight must be (dim, K)")
+    width = conv_weight.shape[1]
+    _need(x, "x", (batch, dim, seqlen), io, dev)
+    _need(du, "du", (batch, dim, seqlen), io, dev)
+    _need(conv_weight, "conv_weight", (dim, width), torch.float32, dev)
+    if conv_bias is not None:
+        _need(conv_bias, "conv_bias", (dim,), torch.float32, dev)
+    if x_prev is not None and width > 1:
+        _need(x_prev, "x_prev", (batch, dim, width - 1), io, dev)
+    elif width == 1:
+        x_prev = None
+    g = dict(dx=torch.empty_like(x), dconv_weight=torch.empty((dim, width), dtype=torch.float32, device=dev),
+             dconv_bias=torch.empty(dim, dtype=torch.float32, device=dev),
+             dx_prev=torch.empty((batch, dim, width - 1), dtype=io, device=dev))
+    lib = load_library()
+    st = lib.ssm_conv_bwd(batch, dim, seqlen, width, _io_code(io), _ptr(x), _ptr(conv_weight), _ptr(conv_bias),
+                          _ptr(x_prev), 1 if conv_silu else 0, _ptr(du), _ptr(g["dx"]), _ptr(g["dconv_weight"]),
+                          _ptr(g["dconv_bias"]), _ptr(g["dx_prev"]) if width > 1 else None, _stream(dev, stream))
+    _check("ssm_conv_bwd", st)
+    return g
 
 
 def scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, delta_softplus=False, h0=None, dlast=None,

@@ -1745,6 +1745,168 @@ __global__ __launch_bounds__(kBlockThreads) void bwd_reduce_kernel(BwdArgs a, in
   }
 }
 
+// ----------------------------------------------------------------------------
+// Backward of the fused conv
+// ----------------------------------------------------------------------------
+//
+// Gradients of u = act(cb + sum_k w[k] x[l-(K-1)+k]) (the causal depthwise
+// conv, + silu, that ssm_conv_scan_fwd fuses in front of the scan) for a
+// loss with dL/du = du, the scan backward's du:
+//   dv_l = du_l silu'(v_l) (du_l without silu), v the recomputed pre-activation;
+//   dx_p = sum_k w[k] dv_{p+(K-1)-k};  dx_prev gets the taps that reach before token 0;
+//   dw[k] = sum over batch rows and tokens of dv_l x_{l-(K-1)+k};  dcb = sum of dv_l.
+// A block owns kConvChunk tokens of one (batch row, channel) row, kConvTok per
+// thread; x and dv are staged in LDS so that every thread sees its
+// neighbours' taps, and the K-1 tokens past the chunk are recomputed from
+// global memory.  dw and dcb are written per (row, chunk) and summed by
+// conv_bwd_reduce_kernel in a fixed order (deterministic, no atomics).
+constexpr int kConvTok = 8;
+constexpr int kConvChunk = kBlockThreads * kConvTok;
+
+struct ConvBwdArgs {
+  const void* x;
+  const float* w;       // [dim][K]
+  const float* cb;      // [dim], may be null
+  const void* x_prev;   // [batch][dim][K-1], may be null (zero history)
+  const void* du;
+  void* dx;
+  void* dx_prev;        // [batch][dim][K-1], may be null
+  float* part;          // [batch * dim][chunks][K + 1]: sums of dv x_{l-(K-1)+k}, then of dv
+  int64_t batch, dim, seqlen, chunks;
+  int silu;
+};
+
+template <typename IoT, int K>
+__global__ __launch_bounds__(kBlockThreads) void conv_bwd_kernel(ConvBwdArgs a) {
+  constexpr int H = K - 1;  // history taps
+  __shared__ float xs[kConvChunk + 4];   // x of the chunk at [4 + i]; the H inputs before it at [4 - H, 4)
+  __shared__ float dvs[kConvChunk + 4];  // dv of the chunk at [i]; of the H tokens after it at [kConvChunk, + H)
+  __shared__ float red[kWavesPerBlock][K + 1];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wv = tid >> 6;
+  const int64_t row = blockIdx.x / a.chunks, chunk = blockIdx.x % a.chunks;
+  const int64_t d = row % a.dim, L = a.seqlen;
+  const int64_t c0 = chunk * kConvChunk;
+  const int64_t t0 = c0 + tid * kConvTok;
+  const IoT* xr = static_cast<const IoT*>(a.x) + row * L;
+  const IoT* ur = static_cast<const IoT*>(a.du) + row * L;
+  IoT* dxr = static_cast<IoT*>(a.dx) + row * L;
+  float w[K];
+#pragma unroll
+  for (int k = 0; k < K; ++k) w[k] = a.w[d * K + k];
+  const float cb = a.cb ? a.cb[d] : 0.0f;
+  auto dact = [&](float v, float g) {
+    if (!a.silu) return g;
+    const float sg = rcp_hw(1.0f + exp2_hw(-v * kLog2e));
+    return g * sg * (1.0f + v * (1.0f - sg));
+  };
+
+  // 1. x and du of this thread's tokens (zero past the end); x to LDS, with
+  //    the H inputs before the chunk (x_prev before token 0).
+  float uv[kConvTok];
+#pragma unroll
+  for (int i = 0; i < kConvTok; ++i) {
+    const int64_t t = t0 + i;
+    const bool in = t < L;
+    xs[4 + tid * kConvTok + i] = in ? Io<IoT>::load1(xr + t) : 0.0f;
+    uv[i] = in ? Io<IoT>::load1(ur + t) : 0.0f;
+  }
+  if (tid < H) {
+    const int64_t p = c0 - H + tid;
+    float hv = 0.0f;
+    if (p >= 0)
+      hv = Io<IoT>::load1(xr + p);
+    else if (a.x_prev)
+      hv = Io<IoT>::load1(static_cast<const IoT*>(a.x_prev) + row * H + H + p);
+    xs[4 - H + tid] = hv;
+  }
+  __syncthreads();
+
+  // 2. dv of this thread's tokens, and of the H tokens after the chunk.
+  float dv[kConvTok];
+#pragma unroll
+  for (int i = 0; i < kConvTok; ++i) {
+    const int j = tid * kConvTok + i;
+    float v = cb;
+#pragma unroll
+    for (int k = 0; k < K; ++k) v = __builtin_fmaf(w[k], xs[4 + j - H + k], v);
+    dv[i] = (t0 + i < L) ? dact(v, uv[i]) : 0.0f;
+    dvs[j] = dv[i];
+  }
+  if (tid < H) {
+    const int64_t q = c0 + kConvChunk + tid;
+    float g = 0.0f;
+    if (q < L) {
+      float v = cb;
+#pragma unroll
+      for (int k = 0; k < K; ++k) v = __builtin_fmaf(w[k], Io<IoT>::load1(xr + q - H + k), v);
+      g = dact(v, Io<IoT>::load1(ur + q));
+    }
+    dvs[kConvChunk + tid] = g;
+  }
+  __syncthreads();
+
+  // 3. dx of this thread's tokens; dx_prev from the first chunk.
+#pragma unroll
+  for (int i = 0; i < kConvTok; ++i) {
+    const int j = tid * kConvTok + i;
+    if (t0 + i < L) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int k = 0; k < K; ++k) acc = __builtin_fmaf(w[k], dvs[j + H - k], acc);
+      Io<IoT>::store1(dxr + t0 + i, acc);
+    }
+  }
+  if (chunk == 0 && a.dx_prev && tid < H) {
+    // Slot m (position m - H) is read by tap k of token m - k.
+    float acc = 0.0f;
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+      if (k <= tid) acc = __builtin_fmaf(w[k], dvs[tid - k], acc);
+    Io<IoT>::store1(static_cast<IoT*>(a.dx_prev) + row * H + tid, acc);
+  }
+
+  // 4. This block's sums of dv x_{l-H+k} and of dv, in a fixed order.
+  float pw[K + 1];
+#pragma unroll
+  for (int k = 0; k <= K; ++k) pw[k] = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kConvTok; ++i) {
+    const int j = tid * kConvTok + i;
+#pragma unroll
+    for (int k = 0; k < K; ++k) pw[k] = __builtin_fmaf(dv[i], xs[4 + j - H + k], pw[k]);
+    pw[K] += dv[i];
+  }
+#pragma unroll
+  for (int k = 0; k <= K; ++k) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) pw[k] += __shfl_xor(pw[k], m);
+    if (lane == 0) red[wv][k] = pw[k];
+  }
+  __syncthreads();
+  if (tid <= K) {
+    float sacc = red[0][tid];
+#pragma unroll
+    for (int w2 = 1; w2 < kWavesPerBlock; ++w2) sacc += red[w2][tid];
+    a.part[(row * a.chunks + chunk) * (K + 1) + tid] = sacc;
+  }
+}
+
+// dw[d][k] and dcb[d]: the (row, chunk) sums of conv_bwd_kernel added over
+// batch rows and chunks in order.
+__global__ __launch_bounds__(kBlockThreads) void conv_bwd_reduce_kernel(ConvBwdArgs a, int K, float* dw, float* dcb) {
+  const int64_t d = (int64_t)blockIdx.x * kBlockThreads + threadIdx.x;
+  if (d >= a.dim) return;
+  float acc[5] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+  for (int64_t b = 0; b < a.batch; ++b)
+    for (int64_t c = 0; c < a.chunks; ++c) {
+      const float* p = a.part + ((b * a.dim + d) * a.chunks + c) * (K + 1);
+      for (int k = 0; k <= K; ++k) acc[k] += p[k];
+    }
+  for (int k = 0; k < K; ++k) dw[d * K + k] = acc[k];
+  if (dcb) dcb[d] = acc[K];
+}
+
 // Launch 1: every segment but the last scans from a zero state and records
 // (sum of Delta, end state).  The segment's decay is a = exp(A * sum Delta).
 template <typename IoT, int N, bool kSoftplus, bool kVec, bool kZoh>
@@ -2304,6 +2466,18 @@ __global__ __launch_bounds__(kBlockThreads) void conv1d_kernel(ScanArgs a, IoT* 
 }
 
 template <typename IoT>
+hipError_t launch_conv_bwd(const ConvBwdArgs& a, int K, hipStream_t st) {
+  const dim3 grid((unsigned)(a.batch * a.dim * a.chunks)), block(kBlockThreads);
+  switch (K) {
+    case 1: hipLaunchKernelGGL((conv_bwd_kernel<IoT, 1>), grid, block, 0, st, a); break;
+    case 2: hipLaunchKernelGGL((conv_bwd_kernel<IoT, 2>), grid, block, 0, st, a); break;
+    case 3: hipLaunchKernelGGL((conv_bwd_kernel<IoT, 3>), grid, block, 0, st, a); break;
+    default: hipLaunchKernelGGL((conv_bwd_kernel<IoT, 4>), grid, block, 0, st, a); break;
+  }
+  return hipGetLastError();
+}
+
+template <typename IoT>
 hipError_t launch_conv(const ScanArgs& a, void* u, hipStream_t st) {
   const int64_t total = a.batch * a.dim * a.seqlen;
   const int64_t blocks = (total + kBlockThreads - 1) / kBlockThreads;
@@ -2817,6 +2991,67 @@ static ssm_status_t scan_bwd_impl(int64_t batch, int64_t dim, int64_t dstate, in
     e = hipGetLastError();
   }
   hipError_t ef = hipFreeAsync(scratch, hs);
+  if (e == hipSuccess) e = ef;
+  if (e != hipSuccess) return hip_fail(e);
+  return SSM_OK;
+}
+
+ssm_status_t ssm_conv_bwd(int64_t batch, int64_t dim, int64_t seqlen, int64_t conv_width, ssm_dtype_t io,
+                          const void* x, const float* conv_weight, const float* conv_bias, const void* x_prev,
+                          int conv_silu, const void* du, void* dx, float* dconv_weight, float* dconv_bias,
+                          void* dx_prev, struct ihipStream_t* stream) {
+  if (io != SSM_F32 && io != SSM_BF16) return SSM_ERR_DTYPE;
+  if (batch < 1 || dim < 1 || seqlen < 1 || conv_width < 1 || conv_width > 4) return SSM_ERR_SHAPE;
+  if (!x || !conv_weight || !du || !dx || !dconv_weight) return SSM_ERR_NULL;
+  const int64_t K = conv_width, H = conv_width - 1;
+  if (H == 0) {  // no history to read or to differentiate
+    x_prev = nullptr;
+    dx_prev = nullptr;
+  }
+  int64_t bd, bdl, chunks = (seqlen + kConvChunk - 1) / kConvChunk, blocks, parts;
+  if (!mul_ok(batch, dim, &bd) || !mul_ok(bd, seqlen, &bdl) || !mul_ok(bdl, 8, &parts) || !mul_ok(bd, chunks, &blocks) ||
+      blocks >= ((int64_t)1 << 31) || !mul_ok(blocks, K + 1, &parts) || !mul_ok(parts, 4, &parts))
+    return SSM_ERR_SHAPE;
+  const size_t es = io_size(io);
+  const void* io_ptrs[] = {x, x_prev, du, dx, dx_prev};
+  for (const void* p : io_ptrs)
+    if (p && !aligned(p, es)) return SSM_ERR_ALIGN;
+  const void* f_ptrs[] = {conv_weight, conv_bias, dconv_weight, dconv_bias};
+  for (const void* p : f_ptrs)
+    if (p && !aligned(p, 4)) return SSM_ERR_ALIGN;
+  const int64_t row_bytes = bdl * (int64_t)es, hist_bytes = bd * H * (int64_t)es;
+  const Range ins[] = {span(x, row_bytes), span(du, row_bytes), span(conv_weight, dim * K * 4),
+                       conv_bias ? span(conv_bias, dim * 4) : Range{0, 0},
+                       x_prev ? span(x_prev, hist_bytes) : Range{0, 0}};
+  const Range outs[] = {span(dx, row_bytes), span(dconv_weight, dim * K * 4),
+                        dconv_bias ? span(dconv_bias, dim * 4) : Range{0, 0},
+                        dx_prev ? span(dx_prev, hist_bytes) : Range{0, 0}};
+  for (int o = 0; o < 4; ++o) {
+    if (outs[o].hi <= outs[o].lo) continue;
+    for (const Range& r : ins)
+      if (r.hi > r.lo && overlap(outs[o], r)) return SSM_ERR_ALIAS;
+    for (int q = o + 1; q < 4; ++q)
+      if (outs[q].hi > outs[q].lo && overlap(outs[o], outs[q])) return SSM_ERR_ALIAS;
+  }
+
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  hipMemPool_t pool;
+  hipError_t e = get_pool(&pool);
+  if (e != hipSuccess) return hip_fail(e);
+  void* part = nullptr;
+  e = hipMallocFromPoolAsync(&part, (size_t)parts, pool, hs);
+  if (e != hipSuccess) return hip_fail(e);
+  ConvBwdArgs a;
+  a.x = x; a.w = conv_weight; a.cb = conv_bias; a.x_prev = x_prev; a.du = du; a.dx = dx; a.dx_prev = dx_prev;
+  a.part = static_cast<float*>(part);
+  a.batch = batch; a.dim = dim; a.seqlen = seqlen; a.chunks = chunks; a.silu = conv_silu != 0;
+  e = (io == SSM_BF16) ? launch_conv_bwd<bf16_t>(a, (int)K, hs) : launch_conv_bwd<float>(a, (int)K, hs);
+  if (e == hipSuccess) {
+    hipLaunchKernelGGL(conv_bwd_reduce_kernel, dim3((unsigned)((dim + kBlockThreads - 1) / kBlockThreads)),
+                       dim3(kBlockThreads), 0, hs, a, (int)K, dconv_weight, dconv_bias);
+    e = hipGetLastError();
+  }
+  hipError_t ef = hipFreeAsync(part, hs);
   if (e == hipSuccess) e = ef;
   if (e != hipSuccess) return hip_fail(e);
   return SSM_OK;

@@ -268,6 +268,35 @@ def cfwd(lib, batch=2, dim=8, dstate=4, seqlen=16, width=4, io=0, **over):
                                  args["bias"], args["sp"], args["h0"], args["y"], args["last"], args["uo"], None)
 
 
+def cbwd(lib, batch=2, dim=8, seqlen=16, width=4, io=0, **over):
+    args = dict(x=addr(1), w=addr(2), cb=addr(3), xp=addr(4), silu=1, du=addr(5), dx=addr(6), dw=addr(7), db=addr(8),
+                dxp=addr(9))
+    args.update(over)
+    return lib.ssm_conv_bwd(batch, dim, seqlen, width, io, args["x"], args["w"], args["cb"], args["xp"], args["silu"],
+                            args["du"], args["dx"], args["dw"], args["db"], args["dxp"], None)
+
+
+@pytest.mark.parametrize("field", ["x", "w", "du", "dx", "dw"])
+def test_conv_bwd_null_required(lib, field):
+    assert cbwd(lib, **{field: None}) == 1
+
+
+def test_conv_bwd_validation(lib):
+    assert cbwd(lib, width=0) == 2
+    assert cbwd(lib, width=5) == 2
+    assert cbwd(lib, seqlen=0) == 2
+    assert cbwd(lib, batch=1 << 62) == 2                 # sizes that overflow
+    assert cbwd(lib, io=7) == 4
+    assert cbwd(lib, dx=addr(6) + 2) == 5               # fp32 dx needs 4-byte alignment
+    assert cbwd(lib, io=1, xp=addr(4) + 1) == 5         # bf16 x_prev needs 2-byte alignment
+    assert cbwd(lib, dw=addr(7) + 2) == 5
+    assert cbwd(lib, dx=addr(1)) == 6                   # dx on x
+    assert cbwd(lib, dx=addr(5) + 4) == 6               # dx overlapping du
+    assert cbwd(lib, dw=addr(2) + 4) == 6               # dconv_weight overlapping conv_weight
+    assert cbwd(lib, db=addr(6)) == 6                   # two outputs on one buffer
+    assert cbwd(lib, dxp=addr(4)) == 6                  # dx_prev on x_prev
+
+
 @pytest.mark.parametrize("field", ["x", "w", "delta", "A", "B", "C", "y"])
 def test_conv_scan_null_required(lib, field):
     assert cfwd(lib, **{field: None}) == 1
