@@ -14,7 +14,7 @@ the timed region.  Prints one JSON line:
   decode       the one-token state update at the decode workload (batch 256,
                dim 5120, dstate 16), per step
   conv_scan    ssm_conv_scan_fwd (causal conv of width 4 fused in front of the
-               scan) on the same workload
+               scan) on the same workload, and its backward ssm_conv_bwd
   zoh          ssm_scan_fwd_ex with exact zero-order hold for B, same workload
   complex      ssm_scan_fwd_complex, 8 complex states (16 real numbers per channel)
   backward     ssm_scan_bwd (every gradient) on the same workload
@@ -199,9 +199,25 @@ def bench_conv_scan(dev, x, t, steps, warmup):
     wall_ms, avg_ms, med_ms = time_calls(fn, steps, warmup)
     io_bytes = 2 if x.io == "bf16" else 4
     nbytes = algorithmic_bytes(b, d, n, l, io_bytes, has_z=x.z is not None) + d * 4 * 4 + d * 4
-    return dict(workload="causal conv (width 4, bias, silu) fused in front of the scan, same shape",
-                us_per_call=round(avg_ms * 1e3, 2), us_median=round(med_ms * 1e3, 2),
-                algorithmic_gbs=round(nbytes / (avg_ms * 1e-3) / 1e9, 1), algorithmic_bytes=nbytes)
+    out = dict(workload="causal conv (width 4, bias, silu) fused in front of the scan, same shape",
+               us_per_call=round(avg_ms * 1e3, 2), us_median=round(med_ms * 1e3, 2),
+               algorithmic_gbs=round(nbytes / (avg_ms * 1e-3) / 1e9, 1), algorithmic_bytes=nbytes)
+
+    # Its backward (ssm_conv_bwd) for dL/du = the scan backward's du: read x and
+    # du, write dx (3 io values per element); the filter, bias and their
+    # gradients are a few KB.
+    du = torch.from_numpy(inputs.grad_output(x)).to(dev, t["u"].dtype)
+
+    def bwd():
+        binding.conv_bwd(t["u"], wt, du, conv_bias=cbt, conv_silu=True)
+
+    _, b_ms, b_med = time_calls(bwd, steps, warmup)
+    bbytes = 3 * b * d * l * io_bytes + 2 * (d * 4 * 4 + d * 4)
+    out["backward"] = dict(workload="ssm_conv_bwd: dx, dconv_weight, dconv_bias, same shape",
+                           us_per_call=round(b_ms * 1e3, 2), us_median=round(b_med * 1e3, 2),
+                           algorithmic_gbs=round(bbytes / (b_ms * 1e-3) / 1e9, 1), algorithmic_bytes=bbytes,
+                           hbm_frac=round(bbytes / (b_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))
+    return out
 
 
 ZOH_SLOTS_PER_ELEM_STATE = 14  # the 6 of the Delta*B rule + u/A, the series (3 FMAs, 1 mul), e*iu - iu, select (2)
@@ -423,7 +439,7 @@ def main():
         from selective_state_space_65_amd import binding as _b
         try:
             out["complex"] = bench_complex(dev, x, t, args.steps, args.warmup)
-        except _b.SsmError as e:  # complex A runs on the single-pass kernel only
+        except _b.SsmError as e:
             out["complex"] = dict(skipped=str(e))
     if not args.no_backward:
         bw = bench_backward(dev, x, t, max(3, args.steps // 4), 2)

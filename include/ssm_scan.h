@@ -203,8 +203,10 @@ ssm_status_t ssm_conv_scan_fwd(int64_t batch, int64_t dim, int64_t dstate, int64
  * SSM_ERR_SHAPE (a size below 1, conv_width outside 1..4, sizes that
  * overflow), SSM_ERR_NULL (x, conv_weight, du, dx, dconv_weight),
  * SSM_ERR_ALIGN (io buffers to their element, fp32 buffers to 4 bytes),
- * SSM_ERR_ALIAS.  Uses stream-ordered scratch from the library's pool for the
- * per-block sums; deterministic (fixed summation order).
+ * SSM_ERR_ALIAS, SSM_ERR_UNSUPPORTED (rows of 2^31 bytes or more: seqlen
+ * times the io element size).  Uses stream-ordered scratch from the
+ * library's pool for the per-block sums; deterministic (fixed summation
+ * order).
  */
 ssm_status_t ssm_conv_bwd(int64_t batch, int64_t dim, int64_t seqlen, int64_t conv_width, ssm_dtype_t io,
                           const void* x, const float* conv_weight, const float* conv_bias, const void* x_prev,

@@ -1755,14 +1755,17 @@ __global__ __launch_bounds__(kBlockThreads) void bwd_reduce_kernel(BwdArgs a, in
 //   dv_l = du_l silu'(v_l) (du_l without silu), v the recomputed pre-activation;
 //   dx_p = sum_k w[k] dv_{p+(K-1)-k};  dx_prev gets the taps that reach before token 0;
 //   dw[k] = sum over batch rows and tokens of dv_l x_{l-(K-1)+k};  dcb = sum of dv_l.
-// A block owns kConvChunk tokens of one (batch row, channel) row, kConvTok per
-// thread; x and dv are staged in LDS so that every thread sees its
-// neighbours' taps, and the K-1 tokens past the chunk are recomputed from
-// global memory.  dw and dcb are written per (row, chunk) and summed by
+// An item is a chunk of 256 T consecutive tokens of one (batch row, channel)
+// row, T per thread (T = 8 or 16).  A thread reads x over its tokens with the
+// K-1 before and after them, and du over its tokens with the K-1 after, from
+// global memory (the neighbours' values come from the caches), and keeps
+// everything in registers: dv is recomputed for the K-1 tokens past its own,
+// so no thread waits on another before the item's sums.  A wave whose reads
+// all lie inside the row takes a path without checks; the others clamp their
+// loads into the row and zero what lies outside it.  One block takes one item;
+// rows that start 16-byte aligned with seqlen a multiple of 8 move the own
+// tokens as 16-byte vectors.  dw and dcb are written per item and summed by
 // conv_bwd_reduce_kernel in a fixed order (deterministic, no atomics).
-constexpr int kConvTok = 8;
-constexpr int kConvChunk = kBlockThreads * kConvTok;
-
 struct ConvBwdArgs {
   const void* x;
   const float* w;       // [dim][K]
@@ -1776,124 +1779,206 @@ struct ConvBwdArgs {
   int silu;
 };
 
-template <typename IoT, int K>
-__global__ __launch_bounds__(kBlockThreads) void conv_bwd_kernel(ConvBwdArgs a) {
-  constexpr int H = K - 1;  // history taps
-  __shared__ float xs[kConvChunk + 4];   // x of the chunk at [4 + i]; the H inputs before it at [4 - H, 4)
-  __shared__ float dvs[kConvChunk + 4];  // dv of the chunk at [i]; of the H tokens after it at [kConvChunk, + H)
-  __shared__ float red[kWavesPerBlock][K + 1];
+// Sum of v over the 64 lanes of the wave, in every lane: quad, half-row and
+// row DPP exchanges, then the 16- and 32-lane swaps (no LDS traffic).
+__device__ __forceinline__ float wave_sum1(float v) {
+  v += dpp_pair(v, 1);
+  v += dpp_pair(v, 2);
+  v += dpp_pair(v, 4);
+  v += dpp_pair(v, 8);
+  auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
+// Where one item's thread sits: its row, first token, and whether its wave
+// reads only inside the row.
+struct ConvPos {
+  uint32_t row, chunk;
+  int t0;
+  bool inner;
+};
+
+template <int K, int T>
+__device__ __forceinline__ ConvPos conv_pos(uint32_t item, uint32_t nch, int L) {
+  constexpr int H = K - 1;
+  ConvPos c;
+  c.row = item / nch;
+  c.chunk = item - c.row * nch;
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wv = tid >> 6;
-  const int64_t row = blockIdx.x / a.chunks, chunk = blockIdx.x % a.chunks;
-  const int64_t d = row % a.dim, L = a.seqlen;
-  const int64_t c0 = chunk * kConvChunk;
-  const int64_t t0 = c0 + tid * kConvTok;
-  const IoT* xr = static_cast<const IoT*>(a.x) + row * L;
-  const IoT* ur = static_cast<const IoT*>(a.du) + row * L;
-  IoT* dxr = static_cast<IoT*>(a.dx) + row * L;
-  float w[K];
-#pragma unroll
-  for (int k = 0; k < K; ++k) w[k] = a.w[d * K + k];
-  const float cb = a.cb ? a.cb[d] : 0.0f;
-  auto dact = [&](float v, float g) {
-    if (!a.silu) return g;
-    const float sg = rcp_hw(1.0f + exp2_hw(-v * kLog2e));
-    return g * sg * (1.0f + v * (1.0f - sg));
-  };
+  c.t0 = (int)c.chunk * (kBlockThreads * T) + tid * T;
+  const int w0 = (int)c.chunk * (kBlockThreads * T) + (tid >> 6) * kWaveThreads * T;
+  c.inner = w0 >= H && w0 + kWaveThreads * T + H <= L;  // the same in every lane of the wave
+  return c;
+}
 
-  // 1. x and du of this thread's tokens (zero past the end); x to LDS, with
-  //    the H inputs before the chunk (x_prev before token 0).
-  float uv[kConvTok];
+// One item for one thread, from x at t0 - H + i (xv) and du at t0 + i (uv),
+// already zero outside the row (x_prev before token 0): dv, dx, dx_prev and
+// the thread's sums pw[k] of dv x_{l-H+k} and pw[K] of dv.
+template <typename IoT, int K, int T, bool kVec, bool kSilu, bool kInner>
+__device__ __forceinline__ void conv_bwd_item(const float (&xv)[T + 2 * K - 2], const float (&uv)[T + K - 1],
+                                              const float (&w)[K], float cb, int t0, int L, IoT* dxr, IoT* dxp,
+                                              float (&pw)[K + 1]) {
+  constexpr int H = K - 1;
+  float dv[T + H];
 #pragma unroll
-  for (int i = 0; i < kConvTok; ++i) {
-    const int64_t t = t0 + i;
-    const bool in = t < L;
-    xs[4 + tid * kConvTok + i] = in ? Io<IoT>::load1(xr + t) : 0.0f;
-    uv[i] = in ? Io<IoT>::load1(ur + t) : 0.0f;
-  }
-  if (tid < H) {
-    const int64_t p = c0 - H + tid;
-    float hv = 0.0f;
-    if (p >= 0)
-      hv = Io<IoT>::load1(xr + p);
-    else if (a.x_prev)
-      hv = Io<IoT>::load1(static_cast<const IoT*>(a.x_prev) + row * H + H + p);
-    xs[4 - H + tid] = hv;
-  }
-  __syncthreads();
-
-  // 2. dv of this thread's tokens, and of the H tokens after the chunk.
-  float dv[kConvTok];
-#pragma unroll
-  for (int i = 0; i < kConvTok; ++i) {
-    const int j = tid * kConvTok + i;
+  for (int i = 0; i < T + H; ++i) {
     float v = cb;
 #pragma unroll
-    for (int k = 0; k < K; ++k) v = __builtin_fmaf(w[k], xs[4 + j - H + k], v);
-    dv[i] = (t0 + i < L) ? dact(v, uv[i]) : 0.0f;
-    dvs[j] = dv[i];
-  }
-  if (tid < H) {
-    const int64_t q = c0 + kConvChunk + tid;
-    float g = 0.0f;
-    if (q < L) {
-      float v = cb;
-#pragma unroll
-      for (int k = 0; k < K; ++k) v = __builtin_fmaf(w[k], Io<IoT>::load1(xr + q - H + k), v);
-      g = dact(v, Io<IoT>::load1(ur + q));
+    for (int k = 0; k < K; ++k) v = __builtin_fmaf(w[k], xv[i + k], v);
+    float g = uv[i];
+    if constexpr (kSilu) {
+      const float sg = rcp_hw(1.0f + exp2_hw(-v * kLog2e));
+      g = g * sg * (1.0f + v * (1.0f - sg));
     }
-    dvs[kConvChunk + tid] = g;
+    dv[i] = (kInner || t0 + i < L) ? g : 0.0f;
   }
-  __syncthreads();
-
-  // 3. dx of this thread's tokens; dx_prev from the first chunk.
+  float dxv[T];
 #pragma unroll
-  for (int i = 0; i < kConvTok; ++i) {
-    const int j = tid * kConvTok + i;
-    if (t0 + i < L) {
-      float acc = 0.0f;
-#pragma unroll
-      for (int k = 0; k < K; ++k) acc = __builtin_fmaf(w[k], dvs[j + H - k], acc);
-      Io<IoT>::store1(dxr + t0 + i, acc);
-    }
-  }
-  if (chunk == 0 && a.dx_prev && tid < H) {
-    // Slot m (position m - H) is read by tap k of token m - k.
+  for (int i = 0; i < T; ++i) {
     float acc = 0.0f;
 #pragma unroll
-    for (int k = 0; k < K; ++k)
-      if (k <= tid) acc = __builtin_fmaf(w[k], dvs[tid - k], acc);
-    Io<IoT>::store1(static_cast<IoT*>(a.dx_prev) + row * H + tid, acc);
+    for (int k = 0; k < K; ++k) acc = __builtin_fmaf(w[k], dv[i + H - k], acc);
+    dxv[i] = acc;
   }
-
-  // 4. This block's sums of dv x_{l-H+k} and of dv, in a fixed order.
-  float pw[K + 1];
+  if constexpr (kVec) {
+#pragma unroll
+    for (int g = 0; g < T; g += 8)
+      if (kInner || t0 + g < L) Io<IoT>::store8(dxr + t0 + g, dxv + g);
+  } else {
+#pragma unroll
+    for (int i = 0; i < T; ++i)
+      if (kInner || t0 + i < L) Io<IoT>::store1(dxr + t0 + i, dxv[i]);
+  }
+  if (!kInner && t0 == 0 && dxp) {
+    // Slot j (position j - H) is read by tap k of token j - k.
+#pragma unroll
+    for (int j = 0; j < H; ++j) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int k = 0; k <= j; ++k) acc = __builtin_fmaf(w[k], dv[j - k], acc);
+      Io<IoT>::store1(dxp + j, acc);
+    }
+  }
 #pragma unroll
   for (int k = 0; k <= K; ++k) pw[k] = 0.0f;
 #pragma unroll
-  for (int i = 0; i < kConvTok; ++i) {
-    const int j = tid * kConvTok + i;
+  for (int i = 0; i < T; ++i) {
 #pragma unroll
-    for (int k = 0; k < K; ++k) pw[k] = __builtin_fmaf(dv[i], xs[4 + j - H + k], pw[k]);
+    for (int k = 0; k < K; ++k) pw[k] = __builtin_fmaf(dv[i], xv[i + k], pw[k]);
     pw[K] += dv[i];
   }
+}
+
+// The block's sums of one item into part, in a fixed order.
+template <int K>
+__device__ __forceinline__ void conv_block_sums(float (&pw)[K + 1], float (*red)[K + 1], float* part) {
+  const int tid = threadIdx.x;
 #pragma unroll
   for (int k = 0; k <= K; ++k) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) pw[k] += __shfl_xor(pw[k], m);
-    if (lane == 0) red[wv][k] = pw[k];
+    pw[k] = wave_sum1(pw[k]);
+    if ((tid & 63) == 0) red[tid >> 6][k] = pw[k];
   }
-  __syncthreads();
+  lds_barrier();  // stores in flight are not waited for
   if (tid <= K) {
     float sacc = red[0][tid];
 #pragma unroll
     for (int w2 = 1; w2 < kWavesPerBlock; ++w2) sacc += red[w2][tid];
-    a.part[(row * a.chunks + chunk) * (K + 1) + tid] = sacc;
+    part[tid] = sacc;
   }
 }
 
-// dw[d][k] and dcb[d]: the (row, chunk) sums of conv_bwd_kernel added over
-// batch rows and chunks in order.
+// The channel's taps and bias; d is uniform over the block, so these are
+// scalar loads (not counted with the vector loads in flight).
+template <int K>
+__device__ __forceinline__ void conv_filter(const ConvBwdArgs& a, uint32_t d, float (&w)[K], float& cb) {
+  const_as4<float> wp = (const_as4<float>)a.w + d * K;
+#pragma unroll
+  for (int k = 0; k < K; ++k) w[k] = wp[k];
+  cb = a.cb ? ((const_as4<float>)a.cb)[d] : 0.0f;
+}
+
+// One item per block.  kVec: the rows start 16-byte aligned and seqlen is a
+// multiple of 8, so the thread's own tokens move as 8-element vectors (an
+// 8-aligned group of tokens is then wholly inside the row or wholly past it).
+template <typename IoT, int K, int T, bool kVec, bool kSilu>
+__global__ __launch_bounds__(kBlockThreads) void conv_bwd_kernel(ConvBwdArgs a) {
+  constexpr int H = K - 1;
+  __shared__ float red[kWavesPerBlock][K + 1];
+  // The grid and the row length fit in 31 bits (checked on the host).
+  const uint32_t nch = (uint32_t)a.chunks;
+  const int L = (int)a.seqlen;
+  const ConvPos c = conv_pos<K, T>(blockIdx.x, nch, L);
+  const int t0 = c.t0;
+  const IoT* xr = static_cast<const IoT*>(a.x) + (int64_t)c.row * L;
+  const IoT* ur = static_cast<const IoT*>(a.du) + (int64_t)c.row * L;
+  IoT* dxr = static_cast<IoT*>(a.dx) + (int64_t)c.row * L;
+  IoT* dxp = a.dx_prev ? static_cast<IoT*>(a.dx_prev) + (int64_t)c.row * H : nullptr;
+  float w[K], cb;
+  conv_filter<K>(a, c.row % (uint32_t)a.dim, w, cb);
+  float pw[K + 1];
+
+  // kInner: every token the wave reads lies inside the row, so nothing is
+  // checked.  Otherwise loads are clamped into the row and their values
+  // zeroed outside it (no divergent branch but the row's first thread
+  // reading x_prev).
+  auto run = [&](auto inner_tag) {
+    constexpr bool kInner = decltype(inner_tag)::value;
+    auto clamp = [&](int i) { return min(max(i, 0), L - 1); };
+    // x at t0 - H + i and du at t0 + i.
+    float xv[T + 2 * H], uv[T + H];
+    if constexpr (kVec) {
+#pragma unroll
+      for (int g = 0; g < T; g += 8) {
+        const bool in = kInner || t0 + g < L;
+        const int at = (kInner || in) ? t0 + g : L - 8;
+        Io<IoT>::load8(xr + at, xv + H + g);
+        Io<IoT>::load8(ur + at, uv + g);
+        if (!kInner) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            xv[H + g + i] = in ? xv[H + g + i] : 0.0f;
+            uv[g + i] = in ? uv[g + i] : 0.0f;
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < T; ++i) {
+        const bool in = kInner || t0 + i < L;
+        const int at = kInner ? t0 + i : clamp(t0 + i);
+        const float xa = Io<IoT>::load1(xr + at), ua = Io<IoT>::load1(ur + at);
+        xv[H + i] = in ? xa : 0.0f;
+        uv[i] = in ? ua : 0.0f;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < H; ++i) {
+      const int p = t0 - H + i, q = t0 + T + i;
+      const float xb = Io<IoT>::load1(xr + (kInner ? p : clamp(p)));
+      const float xa = Io<IoT>::load1(xr + (kInner ? q : clamp(q)));
+      const float ua = Io<IoT>::load1(ur + (kInner ? q : clamp(q)));
+      xv[i] = (kInner || (p >= 0 && p < L)) ? xb : 0.0f;
+      xv[H + T + i] = (kInner || q < L) ? xa : 0.0f;
+      uv[T + i] = (kInner || q < L) ? ua : 0.0f;
+    }
+    if (!kInner && t0 == 0 && a.x_prev) {
+#pragma unroll
+      for (int i = 0; i < H; ++i)
+        xv[i] = Io<IoT>::load1(static_cast<const IoT*>(a.x_prev) + (int64_t)c.row * H + i);
+    }
+    conv_bwd_item<IoT, K, T, kVec, kSilu, kInner>(xv, uv, w, cb, t0, L, dxr, dxp, pw);
+  };
+  if (c.inner)
+    run(std::true_type{});
+  else
+    run(std::false_type{});
+  conv_block_sums<K>(pw, red, a.part + ((int64_t)c.row * nch + c.chunk) * (K + 1));
+}
+
+// dw[d][k] and dcb[d]: the (row, chunk) sums of the conv backward kernels
+// added over batch rows and chunks in order.
 __global__ __launch_bounds__(kBlockThreads) void conv_bwd_reduce_kernel(ConvBwdArgs a, int K, float* dw, float* dcb) {
   const int64_t d = (int64_t)blockIdx.x * kBlockThreads + threadIdx.x;
   if (d >= a.dim) return;
@@ -2465,16 +2550,36 @@ __global__ __launch_bounds__(kBlockThreads) void conv1d_kernel(ScanArgs a, IoT* 
   Io<IoT>::store1(u + i, acc);
 }
 
-template <typename IoT>
-hipError_t launch_conv_bwd(const ConvBwdArgs& a, int K, hipStream_t st) {
+template <typename IoT, int T, bool kSilu>
+hipError_t launch_conv_bwd_t(const ConvBwdArgs& a, int K, bool vec, hipStream_t st) {
   const dim3 grid((unsigned)(a.batch * a.dim * a.chunks)), block(kBlockThreads);
-  switch (K) {
-    case 1: hipLaunchKernelGGL((conv_bwd_kernel<IoT, 1>), grid, block, 0, st, a); break;
-    case 2: hipLaunchKernelGGL((conv_bwd_kernel<IoT, 2>), grid, block, 0, st, a); break;
-    case 3: hipLaunchKernelGGL((conv_bwd_kernel<IoT, 3>), grid, block, 0, st, a); break;
-    default: hipLaunchKernelGGL((conv_bwd_kernel<IoT, 4>), grid, block, 0, st, a); break;
+  if (vec) {
+    switch (K) {
+      case 1: hipLaunchKernelGGL((conv_bwd_kernel<IoT, 1, T, true, kSilu>), grid, block, 0, st, a); break;
+      case 2: hipLaunchKernelGGL((conv_bwd_kernel<IoT, 2, T, true, kSilu>), grid, block, 0, st, a); break;
+      case 3: hipLaunchKernelGGL((conv_bwd_kernel<IoT, 3, T, true, kSilu>), grid, block, 0, st, a); break;
+      default: hipLaunchKernelGGL((conv_bwd_kernel<IoT, 4, T, true, kSilu>), grid, block, 0, st, a); break;
+    }
+  } else {
+    switch (K) {
+      case 1: hipLaunchKernelGGL((conv_bwd_kernel<IoT, 1, T, false, kSilu>), grid, block, 0, st, a); break;
+      case 2: hipLaunchKernelGGL((conv_bwd_kernel<IoT, 2, T, false, kSilu>), grid, block, 0, st, a); break;
+      case 3: hipLaunchKernelGGL((conv_bwd_kernel<IoT, 3, T, false, kSilu>), grid, block, 0, st, a); break;
+      default: hipLaunchKernelGGL((conv_bwd_kernel<IoT, 4, T, false, kSilu>), grid, block, 0, st, a); break;
+    }
   }
   return hipGetLastError();
+}
+
+// vec: rows 16-byte aligned and seqlen a multiple of 8.  T (tokens per
+// thread) is 16 where a 4096-token item pads the rows no more than a
+// 2048-token one, else 8; rows read element by element always take 8.
+template <typename IoT>
+hipError_t launch_conv_bwd(const ConvBwdArgs& a, int K, bool vec, int T, hipStream_t st) {
+  if (T == 16) {
+    return a.silu ? launch_conv_bwd_t<IoT, 16, true>(a, K, vec, st) : launch_conv_bwd_t<IoT, 16, false>(a, K, vec, st);
+  }
+  return a.silu ? launch_conv_bwd_t<IoT, 8, true>(a, K, vec, st) : launch_conv_bwd_t<IoT, 8, false>(a, K, vec, st);
 }
 
 template <typename IoT>
@@ -3008,11 +3113,15 @@ ssm_status_t ssm_conv_bwd(int64_t batch, int64_t dim, int64_t seqlen, int64_t co
     x_prev = nullptr;
     dx_prev = nullptr;
   }
-  int64_t bd, bdl, chunks = (seqlen + kConvChunk - 1) / kConvChunk, blocks, parts;
+  const bool vec = seqlen % 8 == 0 && aligned(x, 16) && aligned(du, 16) && aligned(dx, 16);
+  const int T = (vec && (seqlen + 4095) / 4096 * 4096 <= (seqlen + 2047) / 2048 * 2048) ? 16 : 8;
+  const int64_t item_tokens = (int64_t)kBlockThreads * T;
+  int64_t bd, bdl, chunks = (seqlen + item_tokens - 1) / item_tokens, blocks, parts;
   if (!mul_ok(batch, dim, &bd) || !mul_ok(bd, seqlen, &bdl) || !mul_ok(bdl, 8, &parts) || !mul_ok(bd, chunks, &blocks) ||
       blocks >= ((int64_t)1 << 31) || !mul_ok(blocks, K + 1, &parts) || !mul_ok(parts, 4, &parts))
     return SSM_ERR_SHAPE;
   const size_t es = io_size(io);
+  if (seqlen * (int64_t)es >= ((int64_t)1 << 31)) return SSM_ERR_UNSUPPORTED;
   const void* io_ptrs[] = {x, x_prev, du, dx, dx_prev};
   for (const void* p : io_ptrs)
     if (p && !aligned(p, es)) return SSM_ERR_ALIGN;
@@ -3045,7 +3154,7 @@ ssm_status_t ssm_conv_bwd(int64_t batch, int64_t dim, int64_t seqlen, int64_t co
   a.x = x; a.w = conv_weight; a.cb = conv_bias; a.x_prev = x_prev; a.du = du; a.dx = dx; a.dx_prev = dx_prev;
   a.part = static_cast<float*>(part);
   a.batch = batch; a.dim = dim; a.seqlen = seqlen; a.chunks = chunks; a.silu = conv_silu != 0;
-  e = (io == SSM_BF16) ? launch_conv_bwd<bf16_t>(a, (int)K, hs) : launch_conv_bwd<float>(a, (int)K, hs);
+  e = (io == SSM_BF16) ? launch_conv_bwd<bf16_t>(a, (int)K, vec, T, hs) : launch_conv_bwd<float>(a, (int)K, vec, T, hs);
   if (e == hipSuccess) {
     hipLaunchKernelGGL(conv_bwd_reduce_kernel, dim3((unsigned)((dim + kBlockThreads - 1) / kBlockThreads)),
                        dim3(kBlockThreads), 0, hs, a, (int)K, dconv_weight, dconv_bias);

@@ -287,6 +287,8 @@ def test_conv_bwd_validation(lib):
     assert cbwd(lib, seqlen=0) == 2
     assert cbwd(lib, batch=1 << 62) == 2                 # sizes that overflow
     assert cbwd(lib, io=7) == 4
+    assert cbwd(lib, batch=1, dim=1, seqlen=1 << 30, io=1) == 8   # rows of 2^31 bytes
+    assert cbwd(lib, batch=1, dim=1, seqlen=1 << 29, io=0) == 8
     assert cbwd(lib, dx=addr(6) + 2) == 5               # fp32 dx needs 4-byte alignment
     assert cbwd(lib, io=1, xp=addr(4) + 1) == 5         # bf16 x_prev needs 2-byte alignment
     assert cbwd(lib, dw=addr(7) + 2) == 5

@@ -76,9 +76,11 @@ def compare(g, want, io, what):
     check(np64(g["dx_prev"]), want["dx_prev"], IO_TOL[io], what + " dx_prev")
 
 
-# (batch, dim, seqlen): one token; less than one 2048-token chunk; a ragged
-# tail past one and two chunks; whole chunks; a dim that is not a multiple of 64.
-SHAPES = [(1, 1, 1), (2, 33, 17), (2, 64, 2051), (1, 5, 5000), (2, 3, 4096), (3, 70, 300)]
+# (batch, dim, seqlen): one token; part of one item; ragged tails past one
+# and two items (items of 2048 tokens, 8 per thread, for rows read element by
+# element and for 5000; 4096 tokens, 16 per thread, for 4096 and 8000); one
+# whole item; a dim that is not a multiple of 64.
+SHAPES = [(1, 1, 1), (2, 33, 17), (2, 64, 2051), (1, 5, 5000), (2, 3, 8000), (2, 3, 4096), (3, 70, 300)]
 
 
 @pytest.mark.parametrize("io", ["f32", "bf16"])
@@ -182,3 +184,26 @@ def test_conv_scan_training_chain():
         err = float(np.max(np.abs(gv - want)))
         bound = 1e-4 * float(np.max(np.abs(want))) + gain * du_err
         assert err <= bound, "%s: max err %.3e > %.3e" % (what, err, bound)
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_conv_bwd_misaligned_rows(io):
+    """x and du starting one element past a 16-byte boundary (seqlen a multiple
+    of 8): the element-wise load path, same results."""
+    b, d, l, width = 2, 24, 2056, 4
+    say("conv_bwd misaligned io=%s" % io)
+    x, w, cb, prev, du = draw(b, d, l, width, io, seed=65109)
+    dt = torch.bfloat16 if io == "bf16" else torch.float32
+    n = b * d * l
+
+    def shifted(a):
+        buf = torch.zeros(n + 1, dtype=dt, device=DEV)
+        buf[1:] = torch.from_numpy(a.reshape(-1)).to(DEV, dt)
+        return buf[1:].view(b, d, l)
+
+    xs, dus = shifted(x), shifted(du)
+    assert xs.data_ptr() % 16 != 0 and dus.data_ptr() % 16 != 0
+    wt, cbt, pt = torch.from_numpy(w).to(DEV), torch.from_numpy(cb).to(DEV), to_dev(prev, io)
+    g = binding.conv_bwd(xs, wt, dus, conv_bias=cbt, x_prev=pt, conv_silu=True)
+    torch.cuda.synchronize()
+    compare(g, oracle.conv1d_bwd_f64(x, w, du, cb, prev, silu=True), io, "misaligned")
