@@ -1792,6 +1792,23 @@ __device__ __forceinline__ float wave_sum1(float v) {
   return __uint_as_float(p[0]) + __uint_as_float(p[1]);
 }
 
+// Lane i gets v of lane i - 1, lane 0 keeps old (DPP wave_shr:1).
+__device__ __forceinline__ float from_lane_below(float v, float old) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(v), 0x138, 0xF, 0xF, false));
+}
+// Lane i gets v of lane i + 1, lane 63 keeps old (DPP wave_shl:1).
+__device__ __forceinline__ float from_lane_above(float v, float old) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(v), 0x130, 0xF, 0xF, false));
+}
+
+// Element idx of an fp32 row at a wave-uniform index, through the scalar
+// cache (the row is not written by the kernel).
+template <typename IoT>
+__device__ __forceinline__ float uni_load1(const IoT* row, int idx) {
+  static_assert(sizeof(IoT) == 4, "fp32 rows");
+  return *((const_as4<float>)row + idx);
+}
+
 // Where one item's thread sits: its row, first token, and whether its wave
 // reads only inside the row.
 struct ConvPos {
@@ -1821,9 +1838,9 @@ __device__ __forceinline__ void conv_bwd_item(const float (&xv)[T + 2 * K - 2], 
                                               const float (&w)[K], float cb, int t0, int L, IoT* dxr, IoT* dxp,
                                               float (&pw)[K + 1]) {
   constexpr int H = K - 1;
-  float dv[T + H];
-#pragma unroll
-  for (int i = 0; i < T + H; ++i) {
+  // dv at t0 + i, computed one token ahead of its last use, so that only a
+  // window of K values of dv is live: token i's dx needs dv at i .. i + H.
+  auto dv_at = [&](int i) {
     float v = cb;
 #pragma unroll
     for (int k = 0; k < K; ++k) v = __builtin_fmaf(w[k], xv[i + k], v);
@@ -1832,15 +1849,32 @@ __device__ __forceinline__ void conv_bwd_item(const float (&xv)[T + 2 * K - 2], 
       const float sg = rcp_hw(1.0f + exp2_hw(-v * kLog2e));
       g = g * sg * (1.0f + v * (1.0f - sg));
     }
-    dv[i] = (kInner || t0 + i < L) ? g : 0.0f;
-  }
+    return (kInner || t0 + i < L) ? g : 0.0f;
+  };
+  float win[K];  // dv at i .. i + H
+#pragma unroll
+  for (int j = 0; j < H; ++j) win[j + 1] = dv_at(j);
+#pragma unroll
+  for (int k = 0; k <= K; ++k) pw[k] = 0.0f;
   float dxv[T];
+  float head[K];  // dv at 0 .. H - 1, for dx_prev
 #pragma unroll
   for (int i = 0; i < T; ++i) {
+#pragma unroll
+    for (int j = 0; j < H; ++j) win[j] = win[j + 1];
+    win[H] = dv_at(i + H);
+    if (i == 0) {
+#pragma unroll
+      for (int j = 0; j < K; ++j) head[j] = win[j];
+    }
     float acc = 0.0f;
 #pragma unroll
-    for (int k = 0; k < K; ++k) acc = __builtin_fmaf(w[k], dv[i + H - k], acc);
+    for (int k = 0; k < K; ++k) acc = __builtin_fmaf(w[k], win[H - k], acc);
     dxv[i] = acc;
+    const float d = win[0];
+#pragma unroll
+    for (int k = 0; k < K; ++k) pw[k] = __builtin_fmaf(d, xv[i + k], pw[k]);
+    pw[K] += d;
   }
   if constexpr (kVec) {
 #pragma unroll
@@ -1857,17 +1891,9 @@ __device__ __forceinline__ void conv_bwd_item(const float (&xv)[T + 2 * K - 2], 
     for (int j = 0; j < H; ++j) {
       float acc = 0.0f;
 #pragma unroll
-      for (int k = 0; k <= j; ++k) acc = __builtin_fmaf(w[k], dv[j - k], acc);
+      for (int k = 0; k <= j; ++k) acc = __builtin_fmaf(w[k], head[j - k], acc);
       Io<IoT>::store1(dxp + j, acc);
     }
-  }
-#pragma unroll
-  for (int k = 0; k <= K; ++k) pw[k] = 0.0f;
-#pragma unroll
-  for (int i = 0; i < T; ++i) {
-#pragma unroll
-    for (int k = 0; k < K; ++k) pw[k] = __builtin_fmaf(dv[i], xv[i + k], pw[k]);
-    pw[K] += dv[i];
   }
 }
 
@@ -1911,6 +1937,9 @@ __global__ __launch_bounds__(kBlockThreads) void conv_bwd_kernel(ConvBwdArgs a) 
   const int L = (int)a.seqlen;
   const ConvPos c = conv_pos<K, T>(blockIdx.x, nch, L);
   const int t0 = c.t0;
+  // The wave's first token, in scalar registers.
+  const int wave0 = (int)c.chunk * (kBlockThreads * T) +
+                    __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) * kWaveThreads * T;
   const IoT* xr = static_cast<const IoT*>(a.x) + (int64_t)c.row * L;
   const IoT* ur = static_cast<const IoT*>(a.du) + (int64_t)c.row * L;
   IoT* dxr = static_cast<IoT*>(a.dx) + (int64_t)c.row * L;
@@ -1953,12 +1982,24 @@ __global__ __launch_bounds__(kBlockThreads) void conv_bwd_kernel(ConvBwdArgs a) 
         uv[i] = in ? ua : 0.0f;
       }
     }
+    // The H tokens before and after the thread's own.  fp32: they are the
+    // neighbouring lanes' own tokens, moved across lanes, and the wave's
+    // first and last lanes take those beyond the wave from wave-uniform
+    // scalar loads.  bf16: each lane loads them (measured faster there).
+    const int wb = wave0 - H, wa = wave0 + kWaveThreads * T;
 #pragma unroll
     for (int i = 0; i < H; ++i) {
       const int p = t0 - H + i, q = t0 + T + i;
-      const float xb = Io<IoT>::load1(xr + (kInner ? p : clamp(p)));
-      const float xa = Io<IoT>::load1(xr + (kInner ? q : clamp(q)));
-      const float ua = Io<IoT>::load1(ur + (kInner ? q : clamp(q)));
+      float xb, xa, ua;
+      if constexpr (sizeof(IoT) == 4) {
+        xb = from_lane_below(xv[T + i], uni_load1<IoT>(xr, kInner ? wb + i : clamp(wb + i)));
+        xa = from_lane_above(xv[H + i], uni_load1<IoT>(xr, kInner ? wa + i : clamp(wa + i)));
+        ua = from_lane_above(uv[i], uni_load1<IoT>(ur, kInner ? wa + i : clamp(wa + i)));
+      } else {
+        xb = Io<IoT>::load1(xr + (kInner ? p : clamp(p)));
+        xa = Io<IoT>::load1(xr + (kInner ? q : clamp(q)));
+        ua = Io<IoT>::load1(ur + (kInner ? q : clamp(q)));
+      }
       xv[i] = (kInner || (p >= 0 && p < L)) ? xb : 0.0f;
       xv[H + T + i] = (kInner || q < L) ? xa : 0.0f;
       uv[T + i] = (kInner || q < L) ? ua : 0.0f;
