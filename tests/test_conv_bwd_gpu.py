@@ -138,6 +138,21 @@ def test_conv_bwd_mamba1p4b_layer():
     compare(g, want, "bf16", "Mamba-1.4B layer")
 
 
+def test_conv_bwd_mamba130m_layer():
+    """The Mamba-130M layer (batch 8, dim 1536, seqlen 2048, K = 4, fp32 io), every output: the
+    fp32 rows that take their neighbouring tokens across lanes."""
+    x = inputs.scan_config(1)
+    batch, dim, _, _ = x.shape
+    w, cb = inputs.conv_params(dim, 4)
+    rng = np.random.default_rng(65110)
+    prev = rng.standard_normal((batch, dim, 3)).astype(np.float32)
+    du = inputs.grad_output(x)
+    say("conv_bwd Mamba-130M layer %s" % (x.u.shape,))
+    g = run(x.u, w, cb, prev, du, True, "f32")
+    want = oracle.conv1d_bwd_f64(x.u, w, du, cb, prev, silu=True)
+    compare(g, want, "f32", "Mamba-130M layer")
+
+
 def test_conv_scan_training_chain():
     """conv_scan_fwd, scan_bwd on the u it stored, then conv_bwd on that du, against
     the same three steps in fp64 (fp32 io).
