@@ -2136,11 +2136,17 @@ struct UpdateArgs {
   int zoh;  // B discretized by exact zero-order hold instead of Delta * B
 };
 
-// N in {4, 8, 16}: N/4 lanes per channel, four states per lane.  Groups of
-// N/4 lanes are aligned inside the wave, so the shuffle stays in the group.
+// N in {4, 8, 16}: SPL states per lane (8 for N = 8 and 16, so that every
+// lane keeps two 16-byte state loads in flight; 4 for N = 4), N/SPL lanes per
+// channel.  Groups of N/SPL lanes are aligned inside the wave, so the shuffle
+// stays in the group.
+template <int N>
+constexpr int update_states_per_lane() { return (N >= 8) ? 8 : 4; }
+
 template <typename IoT, int N, bool kZ, bool kSoftplus, bool kZoh>
 __global__ __launch_bounds__(kBlockThreads) void state_update_kernel(UpdateArgs a) {
-  constexpr int kLanes = N / 4;
+  constexpr int SPL = update_states_per_lane<N>();
+  constexpr int kLanes = N / SPL;
   const int64_t bd = a.batch * a.dim;
   const int64_t tid = (int64_t)blockIdx.x * kBlockThreads + threadIdx.x;
   const int64_t ch_raw = tid / kLanes;
@@ -2149,18 +2155,21 @@ __global__ __launch_bounds__(kBlockThreads) void state_update_kernel(UpdateArgs 
   const int64_t ch = active ? ch_raw : bd - 1;
   const int64_t b = ch / a.dim, d = ch % a.dim;
 
-  float h[4], A4[4], B4[4], C4[4];
-  Io<float>::load4(a.state + ch * N + 4 * q, h);
-  Io<float>::load4(a.A + d * N + 4 * q, A4);
-  Io<IoT>::load4(static_cast<const IoT*>(a.B) + b * N + 4 * q, B4);
-  Io<IoT>::load4(static_cast<const IoT*>(a.C) + b * N + 4 * q, C4);
+  float h[SPL], A4[SPL], B4[SPL], C4[SPL];
+#pragma unroll
+  for (int j = 0; j < SPL; j += 4) {
+    Io<float>::load4(a.state + ch * N + SPL * q + j, h + j);
+    Io<float>::load4(a.A + d * N + SPL * q + j, A4 + j);
+    Io<IoT>::load4(static_cast<const IoT*>(a.B) + b * N + SPL * q + j, B4 + j);
+    Io<IoT>::load4(static_cast<const IoT*>(a.C) + b * N + SPL * q + j, C4 + j);
+  }
   const float uv = Io<IoT>::load1(static_cast<const IoT*>(a.u) + ch);
   const float dl = discretize_delta<kSoftplus>(Io<IoT>::load1(static_cast<const IoT*>(a.delta) + ch),
                                                a.bias ? a.bias[d] : 0.0f);
   const float xl = dl * uv;
   float acc = 0.0f;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < SPL; ++j) {
     const float ta = A4[j] * kLog2e * dl;
     const float abar = exp2_hw(ta);
     const float bu = kZoh ? zoh_input(ta, abar, xl, uv * (1.0f / A4[j])) : xl;
@@ -2170,7 +2179,9 @@ __global__ __launch_bounds__(kBlockThreads) void state_update_kernel(UpdateArgs 
 #pragma unroll
   for (int off = 1; off < kLanes; off <<= 1) acc += __shfl_xor(acc, off, kLanes);
   if (active) {
-    *reinterpret_cast<float4*>(a.state + ch * N + 4 * q) = make_float4(h[0], h[1], h[2], h[3]);
+#pragma unroll
+    for (int j = 0; j < SPL; j += 4)
+      *reinterpret_cast<float4*>(a.state + ch * N + SPL * q + j) = make_float4(h[j], h[j + 1], h[j + 2], h[j + 3]);
     if (q == 0) {
       float zv = kZ ? Io<IoT>::load1(static_cast<const IoT*>(a.z) + ch) : 0.0f;
       Io<IoT>::store1(static_cast<IoT*>(a.y) + ch, epilogue<kZ>(acc, a.D ? a.D[d] : 0.0f, uv, zv));
@@ -2700,7 +2711,7 @@ hipError_t launch_update_t(const UpdateArgs& a, hipStream_t st, bool generic) {
     hipLaunchKernelGGL((state_update_generic_kernel<IoT, kZ, kSp, kZoh>), dim3((unsigned)blocks), dim3(kBlockThreads),
                        0, st, a);
   } else {
-    int64_t threads = bd * (N / 4);
+    int64_t threads = bd * (N / update_states_per_lane<N>());
     int64_t blocks = (threads + kBlockThreads - 1) / kBlockThreads;
     hipLaunchKernelGGL((state_update_kernel<IoT, N, kZ, kSp, kZoh>), dim3((unsigned)blocks), dim3(kBlockThreads), 0,
                        st, a);
