@@ -2215,13 +2215,20 @@ __global__ __launch_bounds__(kBlockThreads) void state_update_generic_kernel(Upd
   Io<IoT>::store1(static_cast<IoT*>(a.y) + ch, epilogue<kZ>(acc, a.D ? a.D[d] : 0.0f, uv, zv));
 }
 
+// Complex states per decode lane: four for 4 and 8 complex states (two
+// 16-byte state loads in flight per lane), two for 2.
+__host__ __device__ constexpr int complex_states_per_lane(int nc) { return (nc >= 4) ? 4 : 2; }
+
 // Complex A, one decode step (the recurrence of the single-pass kernel's
-// complex variant for one token): NC/2 lanes per channel, two complex states
-// (four floats, (re, im) pairs) per lane, so state, A, B and C rows are read
-// and written as whole vectors.  y = 2 Re(sum C h) + D u, gated.
+// complex variant for one token): CPL complex states ((re, im) pairs) per
+// lane, NC/CPL lanes per channel, so state, A, B and C rows are read and
+// written as whole 16-byte vectors.  y = 2 Re(sum C h) + D u, gated.
+
 template <typename IoT, int NC, bool kZ, bool kSoftplus>
 __global__ __launch_bounds__(kBlockThreads) void state_update_complex_kernel(UpdateArgs a) {
-  constexpr int kLanes = NC / 2;
+  constexpr int CPL = complex_states_per_lane(NC);
+  constexpr int F = 2 * CPL;  // floats per lane
+  constexpr int kLanes = NC / CPL;
   constexpr int N = 2 * NC;  // floats per channel
   const int64_t bd = a.batch * a.dim;
   const int64_t tid = (int64_t)blockIdx.x * kBlockThreads + threadIdx.x;
@@ -2231,18 +2238,21 @@ __global__ __launch_bounds__(kBlockThreads) void state_update_complex_kernel(Upd
   const int64_t ch = active ? ch_raw : bd - 1;
   const int64_t b = ch / a.dim, d = ch % a.dim;
 
-  float h[4], A4[4], B4[4], C4[4];
-  Io<float>::load4(a.state + ch * N + 4 * q, h);
-  Io<float>::load4(a.A + d * N + 4 * q, A4);
-  Io<IoT>::load4(static_cast<const IoT*>(a.B) + b * N + 4 * q, B4);
-  Io<IoT>::load4(static_cast<const IoT*>(a.C) + b * N + 4 * q, C4);
+  float h[F], A4[F], B4[F], C4[F];
+#pragma unroll
+  for (int k = 0; k < F; k += 4) {
+    Io<float>::load4(a.state + ch * N + F * q + k, h + k);
+    Io<float>::load4(a.A + d * N + F * q + k, A4 + k);
+    Io<IoT>::load4(static_cast<const IoT*>(a.B) + b * N + F * q + k, B4 + k);
+    Io<IoT>::load4(static_cast<const IoT*>(a.C) + b * N + F * q + k, C4 + k);
+  }
   const float uv = Io<IoT>::load1(static_cast<const IoT*>(a.u) + ch);
   const float dl = discretize_delta<kSoftplus>(Io<IoT>::load1(static_cast<const IoT*>(a.delta) + ch),
                                                a.bias ? a.bias[d] : 0.0f);
   const float xl = dl * uv;
   float acc = 0.0f;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
+  for (int j = 0; j < CPL; ++j) {
     const float mag = exp2_hw(A4[2 * j] * kLog2e * dl);
     const float turn = __builtin_amdgcn_fractf(A4[2 * j + 1] * kInv2Pi * dl);
     const float pr = mag * __builtin_amdgcn_cosf(turn), pi = mag * __builtin_amdgcn_sinf(turn);
@@ -2256,7 +2266,9 @@ __global__ __launch_bounds__(kBlockThreads) void state_update_complex_kernel(Upd
 #pragma unroll
   for (int off = 1; off < kLanes; off <<= 1) acc += __shfl_xor(acc, off, kLanes);
   if (active) {
-    *reinterpret_cast<float4*>(a.state + ch * N + 4 * q) = make_float4(h[0], h[1], h[2], h[3]);
+#pragma unroll
+    for (int k = 0; k < F; k += 4)
+      *reinterpret_cast<float4*>(a.state + ch * N + F * q + k) = make_float4(h[k], h[k + 1], h[k + 2], h[k + 3]);
     if (q == 0) {
       float zv = kZ ? Io<IoT>::load1(static_cast<const IoT*>(a.z) + ch) : 0.0f;
       Io<IoT>::store1(static_cast<IoT*>(a.y) + ch, epilogue<kZ>(2.0f * acc, a.D ? a.D[d] : 0.0f, uv, zv));
@@ -2751,7 +2763,7 @@ hipError_t launch_update_cplx_t(const UpdateArgs& a, int64_t nc, hipStream_t st,
                        dim3((unsigned)((bd + kBlockThreads - 1) / kBlockThreads)), dim3(kBlockThreads), 0, st, a, nc);
     return hipGetLastError();
   }
-  const int64_t threads = bd * (nc / 2);
+  const int64_t threads = bd * (nc / complex_states_per_lane((int)nc));
   const dim3 grid((unsigned)((threads + kBlockThreads - 1) / kBlockThreads));
   if (nc == 2) hipLaunchKernelGGL((state_update_complex_kernel<IoT, 2, kZ, kSp>), grid, dim3(kBlockThreads), 0, st, a);
   else if (nc == 4) hipLaunchKernelGGL((state_update_complex_kernel<IoT, 4, kZ, kSp>), grid, dim3(kBlockThreads), 0, st, a);
