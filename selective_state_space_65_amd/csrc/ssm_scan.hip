@@ -1720,23 +1720,37 @@ __global__ __launch_bounds__(kBlockThreads) void bwd_reduce_kernel(BwdArgs a, in
                                                                    float* dD, float* dbias) {
   const int64_t i = (int64_t)blockIdx.x * kBlockThreads + threadIdx.x;
   const int64_t bnl = a.batch * N * a.seqlen;
-  // Four consecutive (b, n, l) per thread as 16-byte loads of the partials
-  // (bnl is a multiple of 4 and the partials start 16-byte aligned), the
-  // groups added in order with several loads in flight.
-  if (4 * i < bnl) {
-    const float4* pb = reinterpret_cast<const float4*>(a.dB_part) + i;
-    const float4* pc = reinterpret_cast<const float4*>(a.dC_part) + i;
+  // Four consecutive (b, n, l) per quad of lanes, as 16-byte loads of the
+  // partials (bnl is a multiple of 4 and the partials start 16-byte
+  // aligned): lane q of the quad adds groups q, q + 4, ... in order, then the
+  // quad adds its four sums as (s0 + s1) + (s2 + s3), the same in every lane
+  // (a fixed order: deterministic), and lane q stores component q.
+  {
+    const int64_t e4 = i >> 2;  // which four (b, n, l)
+    const int q = (int)(i & 3);
+    const bool on = 4 * e4 < bnl;
     const int64_t stride = bnl / 4;
+    const float4* pb = reinterpret_cast<const float4*>(a.dB_part) + (on ? e4 : 0);
+    const float4* pc = reinterpret_cast<const float4*>(a.dC_part) + (on ? e4 : 0);
     float4 sb = make_float4(0.0f, 0.0f, 0.0f, 0.0f), sc = sb;
-#pragma unroll 8
-    for (int64_t g = 0; g < a.groups; ++g) {
-      const float4 vb = pb[g * stride], vc = pc[g * stride];
-      sb.x += vb.x; sb.y += vb.y; sb.z += vb.z; sb.w += vb.w;
-      sc.x += vc.x; sc.y += vc.y; sc.z += vc.z; sc.w += vc.w;
+    if (on) {
+#pragma unroll 4
+      for (int64_t g = q; g < a.groups; g += 4) {
+        const float4 vb = pb[g * stride], vc = pc[g * stride];
+        sb.x += vb.x; sb.y += vb.y; sb.z += vb.z; sb.w += vb.w;
+        sc.x += vc.x; sc.y += vc.y; sc.z += vc.z; sc.w += vc.w;
+      }
     }
-    // dB and dC are only 4-byte aligned.
-    dB[4 * i] = sb.x; dB[4 * i + 1] = sb.y; dB[4 * i + 2] = sb.z; dB[4 * i + 3] = sb.w;
-    dC[4 * i] = sc.x; dC[4 * i + 1] = sc.y; dC[4 * i + 2] = sc.z; dC[4 * i + 3] = sc.w;
+    float v[8] = {sb.x, sb.y, sb.z, sb.w, sc.x, sc.y, sc.z, sc.w};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      v[k] += dpp_pair(v[k], 1);  // s0 + s1, s2 + s3
+      v[k] += dpp_pair(v[k], 2);  // (s0 + s1) + (s2 + s3)
+    }
+    if (on) {
+      dB[4 * e4 + q] = q == 0 ? v[0] : q == 1 ? v[1] : q == 2 ? v[2] : v[3];
+      dC[4 * e4 + q] = q == 0 ? v[4] : q == 1 ? v[5] : q == 2 ? v[6] : v[7];
+    }
   }
   if (i < a.dim * N) {
     float s = 0.0f;
@@ -3162,7 +3176,7 @@ static ssm_status_t scan_bwd_impl(int64_t batch, int64_t dim, int64_t dstate, in
   }
   // 3. Fixed-order sums of the partials.
   if (e == hipSuccess) {
-    const int64_t n = std::max(sh.bnl / 4, std::max(sh.dn, dim));
+    const int64_t n = std::max(sh.bnl, std::max(sh.dn, dim));
     const int64_t blocks = (n + kBlockThreads - 1) / kBlockThreads;
     hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)blocks), dim3(kBlockThreads), 0, hs, ba, (int)dstate, dB,
                        dC, dA, dD, ddelta_bias);
