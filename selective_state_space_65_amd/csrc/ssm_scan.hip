@@ -1779,11 +1779,12 @@ __global__ __launch_bounds__(kBlockThreads) void bwd_reduce_kernel(BwdArgs a, in
 //   dx_p = sum_k w[k] dv_{p+(K-1)-k};  dx_prev gets the taps that reach before token 0;
 //   dw[k] = sum over batch rows and tokens of dv_l x_{l-(K-1)+k};  dcb = sum of dv_l.
 // An item is a chunk of 256 T consecutive tokens of one (batch row, channel)
-// row, T per thread (T = 8 or 16).  A thread reads x over its tokens with the
-// K-1 before and after them, and du over its tokens with the K-1 after, from
-// global memory (the neighbours' values come from the caches), and keeps
-// everything in registers: dv is recomputed for the K-1 tokens past its own,
-// so no thread waits on another before the item's sums.  A wave whose reads
+// row, T per thread (T = 8 or 16).  A thread holds x over its tokens with the
+// K-1 before and after them, and du over its tokens with the K-1 after, all in
+// registers (the K-1 neighbouring tokens are the adjacent lanes' own, moved
+// across lanes for fp32 rows and loaded again for bf16 rows); dv is recomputed
+// for the K-1 tokens past its own and kept as a sliding window, so no thread
+// waits on another before the item's sums.  A wave whose reads
 // all lie inside the row takes a path without checks; the others clamp their
 // loads into the row and zero what lies outside it.  One block takes one item;
 // rows that start 16-byte aligned with seqlen a multiple of 8 move the own
