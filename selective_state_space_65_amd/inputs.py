@@ -16,6 +16,16 @@ Draw order from numpy.random.default_rng(seed) (PCG64): dt, u, delta, z, B, C
 (then h0 when requested).  bf16 workloads draw in fp32 and round to nearest
 even; the stored float32 arrays then hold exactly the bf16 values, so the
 oracle sees exactly what the GPU reads.
+
+Test inputs (make_scan_inputs with channel_params_kind="varied", its default)
+give every channel its own A row and D, so that a kernel reading another
+channel's A or D cannot pass a parity test:
+  A[d, n]     = -(n + 1) * s[d],  s[d] = exp(U(ln 0.5, ln 2))
+  D[d]        ~ N(1, 0.5^2)
+drawn from numpy.random.default_rng([seed, 0xA]) (s for every channel, then
+D), a stream of its own, so the other tensors are those of the recipe above.
+The workloads themselves (scan_config, decode_config) keep A = -(n + 1) and
+D = 1 unless asked otherwise.
 """
 from dataclasses import dataclass, field
 
@@ -78,11 +88,27 @@ class ScanInputs:
         return b, d, self.A.shape[1], l
 
 
+def channel_params(seed, dim, dstate, kind="varied"):
+    """A (dim, dstate) and D (dim,), float32.  "workload": A = -(n + 1) in every
+    channel and D = 1; "varied": A = -(n + 1) * s[d] with s[d] log-uniform in
+    [1/2, 2] and D[d] ~ N(1, 0.5^2), from their own stream [seed, 0xA]."""
+    base = -(np.arange(dstate, dtype=np.float64) + 1.0)
+    if kind == "workload":
+        return np.broadcast_to(base.astype(np.float32), (dim, dstate)).copy(), np.ones(dim, np.float32)
+    if kind != "varied":
+        raise ValueError(kind)
+    rng = np.random.default_rng([seed, 0xA])
+    s = np.exp(rng.uniform(np.log(0.5), np.log(2.0), size=dim))
+    D = 1.0 + 0.5 * rng.standard_normal(dim)
+    return (base[None, :] * s[:, None]).astype(np.float32), D.astype(np.float32)
+
+
 def make_scan_inputs(batch, dim, dstate, seqlen, io="f32", seed=SEED_BASE, z=True, D=True, bias=True, softplus=True,
-                     h0=False, h0_scale=1.0):
-    """Seeded inputs with the workloads' distributions; optional pieces switch off."""
+                     h0=False, h0_scale=1.0, channel_params_kind="varied"):
+    """Seeded inputs with the workloads' distributions; optional pieces switch off.
+    A and D vary per channel unless channel_params_kind="workload"."""
     rng = np.random.default_rng(seed)
-    A = np.broadcast_to(-(np.arange(dstate, dtype=np.float32) + 1.0), (dim, dstate)).copy()
+    A, Dv = channel_params(seed, dim, dstate, channel_params_kind)
     db = _dt_bias(rng, dim)
     u = _normal(rng, (batch, dim, seqlen))
     dlt = _normal(rng, (batch, dim, seqlen), 0.5)
@@ -94,7 +120,7 @@ def make_scan_inputs(batch, dim, dstate, seqlen, io="f32", seed=SEED_BASE, z=Tru
         u, dlt, zz, B, C = (round_bf16(t) for t in (u, dlt, zz, B, C))
     elif io != "f32":
         raise ValueError(io)
-    return ScanInputs(u=u, delta=dlt, A=A, B=B, C=C, D=np.ones(dim, np.float32) if D else None,
+    return ScanInputs(u=u, delta=dlt, A=A, B=B, C=C, D=Dv if D else None,
                       z=zz if z else None, delta_bias=db if bias else None, h0=hh, io=io, softplus=softplus,
                       meta=dict(seed=seed, batch=batch, dim=dim, dstate=dstate, seqlen=seqlen))
 
@@ -104,6 +130,7 @@ def scan_config(i, **overrides):
     c = dict(SCAN_CONFIGS[i])
     name = c.pop("name")
     c["seed"] = SEED_BASE + i
+    c["channel_params_kind"] = "workload"
     c.update(overrides)
     x = make_scan_inputs(**c)
     x.meta["name"] = name
@@ -154,18 +181,19 @@ class DecodeInputs:
         return dict(u=u, delta=dlt, z=zz, B=B, C=C)
 
 
-def decode_config(batch=None, dim=None, steps=None):
-    """The recurrent-decode workload: persistent fp32 state ~ 0.1 * N(0, 1) (0.1 read as the standard deviation)."""
+def decode_config(batch=None, dim=None, steps=None, channel_params_kind="workload"):
+    """The recurrent-decode workload: persistent fp32 state ~ 0.1 * N(0, 1) (0.1 read as the standard deviation).
+    channel_params_kind="varied" gives every channel its own A row and D (as make_scan_inputs)."""
     c = dict(DECODE_CONFIG)
     batch = batch or c["batch"]
     dim = dim or c["dim"]
     steps = steps or c["steps"]
     n = c["dstate"]
     rng = np.random.default_rng(SEED_BASE + 4)
-    A = np.broadcast_to(-(np.arange(n, dtype=np.float32) + 1.0), (dim, n)).copy()
+    A, Dv = channel_params(SEED_BASE + 4, dim, n, channel_params_kind)
     db = _dt_bias(rng, dim)
     state0 = _normal(rng, (batch, dim, n), 0.1)
-    return DecodeInputs(state0=state0, A=A, D=np.ones(dim, np.float32), delta_bias=db, batch=batch, dim=dim,
+    return DecodeInputs(state0=state0, A=A, D=Dv, delta_bias=db, batch=batch, dim=dim,
                         dstate=n, steps=steps, io=c["io"], meta=dict(seed=SEED_BASE + 4, name=c["name"]))
 
 

@@ -3,8 +3,9 @@ the C ABI (needs an MI355X).
 
 Bar as for the real scan: max|got - want| <= tol * max|want|, tol = 1e-4 for
 fp32 io and 2e-2 for bf16 io; states (complex, compared as (re, im) pairs) at
-1e-4 for both.  Inputs: A = -1/2 + i pi n (a decaying rotation per state,
-n = 0 .. dstate-1), Delta from the workloads' recipe, B and C with standard
+1e-4 for both.  Inputs: A[d, n] = -r[d]/2 + i pi n q[d] (a decaying rotation
+per state, n = 0 .. dstate-1, with r, q log-uniform in [1/2, 2] per channel),
+Delta, u, z and a per-channel D from the test recipe, B and C with standard
 normal real and imaginary parts, complex h0.
 """
 import numpy as np
@@ -42,9 +43,13 @@ def complex_inputs(batch, dim, dstate, seqlen, io, seed, z=True, D=True, bias=Tr
     x = inputs.make_scan_inputs(batch, dim, dstate, seqlen, io=io, seed=seed, z=z, D=D, bias=bias,
                                 softplus=softplus)
     rng = np.random.default_rng([seed, 7])
-    n = np.arange(dstate, dtype=np.float32)
-    A = np.stack([np.full((dim, dstate), -0.5, np.float32), np.broadcast_to(np.float32(np.pi) * n, (dim, dstate))],
-                 -1).astype(np.float32)
+    n = np.arange(dstate, dtype=np.float64)
+    # Per channel: the decay scaled by r[d] and the rotation by q[d] (both
+    # log-uniform in [1/2, 2]), so that another channel's A row is visible.
+    cr = np.random.default_rng([seed, 0xC])
+    r = np.exp(cr.uniform(np.log(0.5), np.log(2.0), size=dim))[:, None]
+    q = np.exp(cr.uniform(np.log(0.5), np.log(2.0), size=dim))[:, None]
+    A = np.stack([np.broadcast_to(-0.5 * r, (dim, dstate)), np.pi * n[None, :] * q], -1).astype(np.float32)
     B = rng.standard_normal((batch, dstate, seqlen, 2)).astype(np.float32)
     C = rng.standard_normal((batch, dstate, seqlen, 2)).astype(np.float32)
     if io == "bf16":
@@ -131,7 +136,7 @@ def test_complex_state_carry_in_place():
 def test_complex_real_parameters_equal_real_scan():
     """Zero imaginary parts: the complex kernel equals the real scan with C doubled."""
     x, A, B, C, hh = complex_inputs(192, 64, 8, 64, "f32", 4300)
-    A[..., 0] = -(np.arange(8, dtype=np.float32) + 1.0)
+    A[..., 0] = x.A  # per-channel real rows of the test recipe
     A[..., 1] = 0.0
     B[..., 1] = 0.0
     C[..., 1] = 0.0

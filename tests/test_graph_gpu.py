@@ -19,7 +19,7 @@ def say(msg):
 
 
 def test_decode_steps_in_a_graph():
-    dec = inputs.decode_config(batch=16, dim=512, steps=4)
+    dec = inputs.decode_config(batch=16, dim=512, steps=4, channel_params_kind="varied")
     A = torch.from_numpy(dec.A).to(DEV)
     D = torch.from_numpy(dec.D).to(DEV)
     bias = torch.from_numpy(dec.delta_bias).to(DEV)

@@ -54,3 +54,19 @@ def test_decode_steps_are_seeded():
 def test_sample_channels():
     ch = inputs.sample_channels(4, 100, 10, seed=1)
     assert len(ch) == 10 and ch[0] == (0, 0) and ch[-1] == (3, 99) and len(set(ch)) == 10
+
+
+def test_test_recipe_varies_A_and_D_per_channel():
+    x = inputs.make_scan_inputs(2, 300, 16, 8, seed=9)
+    assert np.unique(x.A[:, 0]).size == 300 and np.unique(x.D).size == 300
+    # Each A row is a positive multiple of -(n + 1), the multiple in [1/2, 2].
+    s = x.A[:, 0] / -1.0
+    assert np.allclose(x.A, -(np.arange(16) + 1.0)[None, :] * s[:, None], rtol=1e-6)
+    assert s.min() >= 0.5 and s.max() <= 2.0
+    # The other tensors are those of the workload recipe with the same seed.
+    w = inputs.make_scan_inputs(2, 300, 16, 8, seed=9, channel_params_kind="workload")
+    for k in ("u", "delta", "z", "B", "C", "delta_bias"):
+        assert np.array_equal(getattr(x, k), getattr(w, k)), k
+    assert np.all(w.D == 1.0) and np.unique(w.A[:, 0]).size == 1
+    dec = inputs.decode_config(batch=2, dim=50, steps=1, channel_params_kind="varied")
+    assert np.unique(dec.D).size == 50 and np.unique(dec.A[:, 3]).size == 50

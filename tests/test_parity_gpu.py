@@ -80,6 +80,38 @@ def test_layer_configs_sampled(cfg, k):
     check(np64(last[bi, di]), hr, "f32", "last_state")
 
 
+@pytest.mark.parametrize("cfg,k", [(1, 24), (2, 24), (3, 4)])
+def test_ssm_part_alone_full_size(cfg, k):
+    """The workloads with D = null and z = null: y is then C.h alone, which the
+    D.u skip otherwise dominates.  Each output is normalised by its own max."""
+    x = inputs.scan_config(cfg, D=False, z=False)
+    b, d, n, l = x.shape
+    say("diagnostic config %d %dx%dx%dx%d %s, D and z null" % (cfg, b, d, n, l, x.io))
+    y, last = gpu_scan(x)
+    ch = inputs.sample_channels(b, d, k, seed=100 + cfg)
+    yr, hr = oracle.scan_channels_f64(ch, x.u, x.delta, x.A, x.B, x.C, x.D, x.z, x.delta_bias, x.softplus, x.h0)
+    bi = torch.tensor([c[0] for c in ch], device=DEV)
+    di = torch.tensor([c[1] for c in ch], device=DEV)
+    ey = check(np64(y[bi, di]), yr, x.io, "y (C.h alone)")
+    eh = check(np64(last[bi, di]), hr, "f32", "last_state")
+    say("diagnostic config %d: y rel err %.2e, last_state rel err %.2e" % (cfg, ey, eh))
+
+
+def test_layer_shape_varied_channels_sampled():
+    """The Mamba-1.4B layer shape with a per-channel A row and D (test recipe)."""
+    x = inputs.scan_config(2, channel_params_kind="varied")
+    b, d, n, l = x.shape
+    assert np.unique(x.D).size > 1000 and np.unique(x.A[:, 0]).size > 1000
+    say("config 2 shape with per-channel A and D")
+    y, last = gpu_scan(x)
+    ch = inputs.sample_channels(b, d, 32, seed=12)
+    yr, hr = oracle.scan_channels_f64(ch, x.u, x.delta, x.A, x.B, x.C, x.D, x.z, x.delta_bias, x.softplus, x.h0)
+    bi = torch.tensor([c[0] for c in ch], device=DEV)
+    di = torch.tensor([c[1] for c in ch], device=DEV)
+    check(np64(y[bi, di]), yr, x.io, "y")
+    check(np64(last[bi, di]), hr, "f32", "last_state")
+
+
 def test_long_sequence_sampled_and_carry():
     x = inputs.scan_config(3)
     b, d, n, l = x.shape
@@ -134,6 +166,27 @@ def test_decode_workload():
     for s in range(dec.steps):
         check(got[s], ys_ref[s], "bf16", "decode y step %d" % s)
     check(np64(state[bi, di]), ref_state, "f32", "decode final state")
+
+
+def test_decode_varied_channels():
+    """64 decode steps at 32x1024x16 with a per-channel A row and D."""
+    dec = inputs.decode_config(batch=32, dim=1024, steps=64, channel_params_kind="varied")
+    say("decode %dx%dx%d, %d steps, per-channel A and D" % (dec.batch, dec.dim, dec.dstate, dec.steps))
+    state = torch.from_numpy(dec.state0).to(DEV)
+    A = torch.from_numpy(dec.A).to(DEV)
+    D = torch.from_numpy(dec.D).to(DEV)
+    bias = torch.from_numpy(dec.delta_bias).to(DEV)
+    ref_state = dec.state0.astype(np.float64)
+    for s in range(dec.steps):
+        st = dec.step(s)
+        tt = {k: torch.from_numpy(v).to(DEV, torch.bfloat16) for k, v in st.items()}
+        y = binding.state_update(state, tt["u"], tt["delta"], A, tt["B"], tt["C"], D=D, z=tt["z"], delta_bias=bias,
+                                 delta_softplus=True)
+        yr = oracle.state_update_f64(ref_state, st["u"], st["delta"], dec.A, st["B"], st["C"], dec.D, st["z"],
+                                     dec.delta_bias, softplus=True)
+        check(np64(y), yr, "bf16", "decode y step %d" % s)
+    torch.cuda.synchronize()
+    check(np64(state), ref_state, "f32", "decode final state")
 
 
 # ---------------------------------------------------------------------------

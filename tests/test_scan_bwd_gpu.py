@@ -92,6 +92,29 @@ def test_bwd_matches_oracle(io, shape):
         compare(g, r, io, x, "mask=%d" % mask)
 
 
+# 5 and 6 channel groups of 64: the reduce kernel's lanes then sum unequal
+# numbers of groups (lane q takes groups q, q + 4, ...), which dB and dC see.
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", [(2, 320, 16, 32), (1, 384, 16, 48)], ids=["2x320x16x32", "1x384x16x48"])
+def test_bwd_group_counts_dB_dC(io, shape):
+    b, d, n, l = shape
+    for mask in (31, 6):
+        z, D, bias, sp, h0 = [(mask >> i) & 1 == 1 for i in range(5)]
+        x = inputs.make_scan_inputs(b, d, n, l, io=io, seed=1200 + mask, z=z, D=D, bias=bias, softplus=sp, h0=h0)
+        if not sp:
+            x.delta = inputs.round_bf16(np.abs(x.delta) * np.float32(0.2)) if io == "bf16" else \
+                np.abs(x.delta) * np.float32(0.2)
+            if bias:
+                x.delta_bias = np.full(d, 0.01, np.float32)
+        dy, dlast = grads_inputs(x, 1200 + mask)
+        say("bwd group counts shape=%s io=%s mask=%d" % (shape, io, mask))
+        g = gpu_bwd(x, dy, dlast)
+        r = oracle_bwd(x, dy, dlast)
+        compare(g, r, io, x, "groups mask=%d" % mask)
+        for k in ("dB", "dC"):
+            assert g[k] is not None and r[k] is not None, k
+
+
 def test_bwd_mamba130m_layer_full():
     x = inputs.scan_config(1)
     dy, dlast = grads_inputs(x, 1001)
