@@ -24,10 +24,16 @@ element), read B and C once per (batch, token), read A, D and the bias once,
 write the final state once.  The (batch, dim, seqlen, dstate) expanded state
 is not counted: the method never stores it.
 
-ALU roof: each (element, state) needs one exp2 and four fp32 VALU operations
-(Delta*A, B*x, the state FMA and the C.h FMA).  On gfx950 exp2 issues at half
-the fp32 rate, so the floor is 6 VALU lane-slots per (element, state), against
-256 CU x 64 lanes x 2.4 GHz = 39.3 T lane-slots/s.
+roofline: HBM is the roof the line is measured against: frac = algorithmic
+bytes / call time / 8 TB/s.  The path is in fact bound by plain ALU issue:
+each (element, state) needs one exp2 and four fp32 VALU operations (Delta*A,
+B*x, the state FMA and the C.h FMA).  The rate probe (csrc/rate_probe.hip)
+measures on the GPU at hand how many FMA issue slots an exp2 and the scan's
+per-(element, state) body take; alu_frac is the call's (element, state) rate
+against 256 CU x 64 lanes x 2.4 GHz = 39.3 T lane-slots/s at that cost.
+
+configs: the Mamba-130M-layer (fp32) and long-sequence (fp32) workloads
+timed the same way, one call per step.
 """
 import argparse
 import json
@@ -90,12 +96,27 @@ def cpu_cores():
         return os.cpu_count() or 1
 
 
-def cpu_baseline(x, budget_s):
-    """Time the fp64 oracle on whole batch rows of the workload until budget_s has elapsed."""
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(x, budget_s, one_thread_s=5.0):
+    """Time the fp64 oracle on whole batch rows of the workload until budget_s has elapsed,
+    then on one thread over a slice of channels of batch row 0."""
     import numpy as np
     import oracle
     b, d, n, l = x.shape
     o = oracle.default()
+    io_bytes = 2 if x.io == "bf16" else 4
+    cores = cpu_cores()
+    oracle.set_threads(cores)
     done = 0
     spent = 0.0
     rows = 0
@@ -109,10 +130,30 @@ def cpu_baseline(x, budget_s):
         rows += 1
         if spent >= budget_s:
             break
-    gbs = algorithmic_bytes(rows, d, n, l, 2 if x.io == "bf16" else 4) / spent / 1e9
-    return dict(value=round(gbs, 3), unit="GB/s", cores=cpu_cores(), kind="oracle",
-                sample="%d of %d batch rows (%d channels x %d tokens, dstate %d), fp64, OpenMP over channels"
-                % (rows, b, rows * d, l, n), seconds=round(spent, 3), elements_per_s=round(done / spent, 1))
+    gbs = algorithmic_bytes(rows, d, n, l, io_bytes) / spent / 1e9
+    out = dict(value=round(gbs, 3), unit="GB/s", cores=cores, kind="oracle", cpu_model=cpu_model(),
+               sample="%d of %d batch rows (%d channels x %d tokens, dstate %d), fp64, OpenMP over channels"
+               % (rows, b, rows * d, l, n), seconds=round(spent, 3), elements_per_s=round(done / spent, 1))
+    # One thread: channels of batch row 0, 64 at a time, until one_thread_s has elapsed.
+    oracle.set_threads(1)
+    spent1, ch1 = 0.0, 0
+    try:
+        while ch1 < d and spent1 < one_thread_s:
+            cs = slice(ch1, min(d, ch1 + 64))
+            args = [np.ascontiguousarray(a[0:1, cs], dtype=np.float64) for a in (x.u, x.delta, x.z)]
+            t0 = time.perf_counter()
+            o.scan_f64(args[0], args[1], x.A[cs], np.ascontiguousarray(x.B[0:1], dtype=np.float64),
+                       np.ascontiguousarray(x.C[0:1], dtype=np.float64), x.D[cs], args[2], x.delta_bias[cs],
+                       x.softplus, None)
+            spent1 += time.perf_counter() - t0
+            ch1 += cs.stop - cs.start
+    finally:
+        oracle.set_threads(cores)
+    el1 = ch1 * l
+    out["one_thread"] = dict(elements_per_s=round(el1 / spent1, 1), seconds=round(spent1, 3),
+                             sample="%d channels x %d tokens of batch row 0" % (ch1, l),
+                             gbs=round(el1 * (4 * io_bytes) / spent1 / 1e9, 4))
+    return out
 
 
 def time_calls(fn, steps, warmup):
@@ -352,6 +393,119 @@ def bench_backward(dev, x, t, steps, warmup):
     return out
 
 
+def rate_probe(dev):
+    """Issue rates of FMA, exp2 and the scan's per-(element, state) body on this GPU
+    (csrc/rate_probe.hip), each probe at 2 and at 8 waves per SIMD."""
+    import ctypes
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "selective_state_space_65_amd", "librate_probe.so"))
+    lib.rate_probe_launch.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.rate_probe_launch.restype = ctypes.c_int
+    lib.rate_probe_ops_per_iter.argtypes = [ctypes.c_int]
+    lib.rate_probe_ops_per_iter.restype = ctypes.c_int
+    names = {0: "fma", 1: "exp2", 2: "scan_body", 3: "exp2_plus_4fma"}
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    res = {}
+    for waves_per_simd in (2, 8):
+        blocks = cus * waves_per_simd  # blocks of 4 waves: one wave per SIMD each
+        sink = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+        stream = torch.cuda.current_stream().cuda_stream
+        rates = {}
+        for kind, name in names.items():
+            iters = 4000
+
+            def launch():
+                rc = lib.rate_probe_launch(kind, blocks, iters, ctypes.c_void_p(sink.data_ptr()),
+                                           ctypes.c_void_p(stream))
+                if rc != 0:
+                    raise RuntimeError("rate probe launch failed: %d" % rc)
+
+            launch()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(3):
+                launch()
+            e1.record()
+            torch.cuda.synchronize()
+            sec = e0.elapsed_time(e1) / 3 * 1e-3
+            ops = blocks * 256 * iters * lib.rate_probe_ops_per_iter(kind)
+            rates[name] = ops / sec
+        res[waves_per_simd] = rates
+    best = {k: max(res[w][k] for w in res) for k in names.values()}
+    fma = best["fma"]
+    return dict(
+        kernel="csrc/rate_probe.hip", compute_units=cus,
+        fma_lane_ops_per_s=round(fma, -9), exp2_lane_ops_per_s=round(best["exp2"], -9),
+        scan_units_per_s=round(best["scan_body"], -9), exp2_plus_4fma_units_per_s=round(best["exp2_plus_4fma"], -9),
+        exp2_cost_in_fma_slots=round(fma / best["exp2"], 3),
+        exp2_plus_4fma_cost_in_fma_slots=round(4.0 * fma / (4.0 * best["exp2_plus_4fma"]), 3),
+        scan_body_cost_in_fma_slots=round(fma / best["scan_body"], 3),
+        implied_clock_ghz=round(fma / (cus * 64) / 1e9, 3),
+        per_waves_per_simd={str(w): {k: round(v, -9) for k, v in r.items()} for w, r in res.items()},
+        note="costs are FMA issue slots per operation (clock-independent); exp2 does not co-issue with FMA if "
+             "exp2_plus_4fma costs 4 + exp2_cost")
+
+
+def bench_config(dev, cfg, steps, warmup):
+    """One scan workload (fp32 configs 1 and 3) timed call by call with HIP events."""
+    import torch
+    from selective_state_space_65_amd import binding, inputs
+    x = inputs.scan_config(cfg)
+    b, d, n, l = x.shape
+    io_bytes = 2 if x.io == "bf16" else 4
+    t = inputs.to_torch(x, dev)
+    y = torch.empty_like(t["u"])
+    last = torch.empty((b, d, n), dtype=torch.float32, device=dev)
+
+    def fn():
+        binding.scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"], delta_bias=t["delta_bias"],
+                         delta_softplus=x.softplus, h0=None, out=y, last_state=last)
+
+    wall_ms, avg_ms, med_ms = time_calls(fn, steps, warmup)
+    nbytes = algorithmic_bytes(b, d, n, l, io_bytes, has_z=x.z is not None)
+    path, seg, seglen, scratch = binding.scan_plan(b, d, n, l, t["u"].dtype, with_path=True)
+    del t, y, last
+    torch.cuda.empty_cache()
+    return dict(workload=x.meta["name"], batch=b, dim=d, dstate=n, seqlen=l, io=x.io, kernel_path=path,
+                segments=seg, us_per_call=round(avg_ms * 1e3, 2), us_median=round(med_ms * 1e3, 2),
+                algorithmic_bytes=nbytes, algorithmic_gbs=round(nbytes / (avg_ms * 1e-3) / 1e9, 1),
+                hbm_frac=round(nbytes / (avg_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                alu_frac=round(SLOTS_PER_ELEM_STATE * b * d * l * n / (avg_ms * 1e-3) / LANE_SLOTS_PEAK, 4),
+                elements_per_s=round(b * d * l / (avg_ms * 1e-3), 1))
+
+
+def sweep_seqlen(dev, steps, warmup, lengths):
+    """Time and algorithmic bytes at fixed channels (batch 1, dim 2560, dstate 16, fp32) over seqlen."""
+    import torch
+    from selective_state_space_65_amd import binding, inputs
+    lmax = max(lengths)
+    x = inputs.make_scan_inputs(1, 2560, 16, lmax, io="f32", seed=inputs.SEED_BASE + 3,
+                                channel_params_kind="workload")
+    full = inputs.to_torch(x, dev)
+    rows = []
+    for l in lengths:
+        t = {k: (None if v is None else (v[..., :l].contiguous() if k in ("u", "delta", "z", "B", "C") else v))
+             for k, v in full.items()}
+        y = torch.empty_like(t["u"])
+        last = torch.empty((1, 2560, 16), dtype=torch.float32, device=dev)
+
+        def fn():
+            binding.scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
+                             delta_bias=t["delta_bias"], delta_softplus=True, h0=None, out=y, last_state=last)
+
+        _, avg_ms, med_ms = time_calls(fn, steps, warmup)
+        nbytes = algorithmic_bytes(1, 2560, 16, l, 4)
+        path, seg, seglen, _ = binding.scan_plan(1, 2560, 16, l, torch.float32, with_path=True)
+        row = dict(seqlen=l, us_per_call=round(avg_ms * 1e3, 2), us_per_1k_tokens=round(avg_ms * 1e6 / l, 3),
+                   algorithmic_bytes=nbytes, algorithmic_gbs=round(nbytes / (avg_ms * 1e-3) / 1e9, 1),
+                   kernel_path=path, segments=seg)
+        print(json.dumps(row), flush=True)
+        rows.append(row)
+        del t, y, last
+    return rows
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -365,6 +519,11 @@ def main():
     ap.add_argument("--no-backward", action="store_true", help="skip the backward line")
     ap.add_argument("--no-zoh", action="store_true", help="skip the zero-order-hold line")
     ap.add_argument("--no-complex", action="store_true", help="skip the complex-A line")
+    ap.add_argument("--no-configs", action="store_true", help="skip the Mamba-130M and long-sequence sub-lines")
+    ap.add_argument("--no-probe", action="store_true", help="skip the instruction-rate probe")
+    ap.add_argument("--probe-only", action="store_true", help="only run the instruction-rate probe")
+    ap.add_argument("--sweep-seqlen", action="store_true",
+                    help="only time batch 1 x dim 2560 x dstate 16 fp32 over seqlen 1k .. 128k")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy 1 GiB three times (reference kernel for rocprofv3 FETCH_SIZE/WRITE_SIZE)")
     args = ap.parse_args()
@@ -388,6 +547,13 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps(dict(copy_bytes_per_launch=src.numel() * 4, launches=3)))
         return
+    if args.probe_only:
+        print(json.dumps(rate_probe(dev)), flush=True)
+        return
+    if args.sweep_seqlen:
+        rows = sweep_seqlen(dev, max(3, args.steps // 4), 2, [1024 << i for i in range(8)])
+        print(json.dumps(dict(sweep="seqlen", channels="batch 1 x dim 2560 x dstate 16, fp32", rows=rows)))
+        return
     x = inputs.scan_config(args.config)
     b, d, n, l = x.shape
     io_bytes = 2 if x.io == "bf16" else 4
@@ -410,17 +576,17 @@ def main():
     alu_rate = slots / (avg_ms * 1e-3)
     hbm_frac = call_gbs / HBM_PEAK_GBS
     alu_frac = alu_rate / LANE_SLOTS_PEAK
-    if alu_frac >= hbm_frac:
-        roof = dict(bound="alu", achieved=round(alu_rate / 1e12, 2), peak=round(LANE_SLOTS_PEAK / 1e12, 2),
-                    unit="T lane-slots/s", frac=round(alu_frac, 4))
-    else:
-        roof = dict(bound="hbm", achieved=round(call_gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s", frac=round(hbm_frac, 4))
     kernels = {"split": "scan_split_kernel", "segmented": "aggregate_kernel + carry_kernel + scan_kernel",
                "generic": "scan_kernel (per-token)"}
-    roof.update(traffic=measured_traffic(args.config), kernel="ssm_scan_fwd call: %s" % kernels[path],
-        call_us_avg=round(avg_ms * 1e3, 2), call_us_median=round(med_ms * 1e3, 2),
-        hbm_gbs=round(call_gbs, 1), hbm_frac=round(hbm_frac, 4), alu_frac=round(alu_frac, 4),
-        algorithmic_bytes=nbytes, algorithmic_lane_slots=slots)
+    roof = dict(bound="hbm", achieved=round(call_gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s", frac=round(hbm_frac, 4),
+                traffic=measured_traffic(args.config), kernel="ssm_scan_fwd call: %s" % kernels[path],
+                call_us_avg=round(avg_ms * 1e3, 2), call_us_median=round(med_ms * 1e3, 2),
+                algorithmic_bytes=nbytes,
+                alu=dict(frac=round(alu_frac, 4), achieved=round(alu_rate / 1e12, 2),
+                         peak=round(LANE_SLOTS_PEAK / 1e12, 2), unit="T lane-slots/s",
+                         lane_slots_per_elem_state=SLOTS_PER_ELEM_STATE, algorithmic_lane_slots=slots,
+                         note="the binding roof: exp2 (2 FMA slots, see rate_probe) + 4 fp32 ops per "
+                              "(element, state); packed FP32 is not used"))
 
     out = dict(metric=METRIC, value=round(gbs, 1), unit="GB/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
                ms_per_step=round(wall_ms, 4), higher_is_better=True, scaling="weak", vs_baseline=None, dtype="f32",
@@ -429,6 +595,12 @@ def main():
                            softplus=True, kernel_path=path, segments=seg, segment_len=seglen),
                hbm_frac_of_peak=round(gbs / HBM_PEAK_GBS, 4), elements_per_s=round(elems / (wall_ms * 1e-3), 1),
                roofline=roof)
+    if not args.no_probe:
+        out["rate_probe"] = rate_probe(dev)
+        roof["alu"]["probe_scan_body_cost_in_fma_slots"] = out["rate_probe"]["scan_body_cost_in_fma_slots"]
+    if not args.no_configs:
+        out["configs"] = {str(c): bench_config(dev, c, max(5, args.steps // 2), 2) for c in (1, 3)
+                          if c != args.config}
     if not args.no_decode:
         out["decode"] = bench_decode(dev, 50, 5)
     if not args.no_conv:

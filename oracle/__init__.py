@@ -44,6 +44,13 @@ def build():
     return compile_oracle()
 
 
+def set_threads(n):
+    """Thread count of the oracle's OpenMP channel loop (a call into the OpenMP
+    runtime the oracle library links; no arithmetic)."""
+    default()
+    ctypes.CDLL("libgomp.so.1").omp_set_num_threads(int(n))
+
+
 def _f64(a):
     return None if a is None else np.ascontiguousarray(a, dtype=np.float64)
 

@@ -675,35 +675,51 @@ __global__ __launch_bounds__(kBlockThreads) void scan_kernel(ScanArgs a, int64_t
 // ----------------------------------------------------------------------------
 //
 // A block owns 64 channels (one per lane) of one batch row and walks the
-// whole sequence once, in tiles of T = 32 tokens.  Its S waves split the N
-// states: wave w owns states [w*NS, (w+1)*NS).  The work on a tile:
-//   A. each of the first SA waves widens TS = T / SA tokens of the tile
-//      (Delta = softplus(delta + bias), x = Delta * u): wave w < SA owns
-//      tokens [w*TS, (w+1)*TS), and publishes (Delta, x) in LDS;
-//   B. every wave runs its NS states over all T tokens (B/C rows are wave-
-//      uniform scalar loads) and publishes its partial C.h sums in LDS;
-//   C. wave w < SA adds the S partials of its TS tokens in wave order (so the
-//      result is deterministic), applies the D skip and the silu gate and
-//      stores y.
-// Each state is therefore updated exactly once per token: no segment
-// aggregates, no rescans.  With two waves per SIMD (S = 8) phases A and C go
-// to the first four waves only: waves w and w + 4 share a SIMD and the older
-// one is issued first, so it finishes the common phase B early; giving it
-// the short, latency-bound softplus/silu chains lets them overlap the
-// partner's state arithmetic instead of leaving the partner to run alone.
-template <typename IoT, int N, int S, int SA>
+// whole sequence once, in tiles of T = 32 tokens.  Its waves have one of
+// three roles, and between two barriers each role works on its own tile:
+//   A (4 waves): Delta = softplus(delta + bias) and x = Delta * u of 8
+//      tokens of tile i+1 -- wave a owns tokens [8a, 8a + 8) of every tile --
+//      published in LDS (with the conv fused, u is first computed from the
+//      conv input);
+//   B (S waves): wave w runs the NS states [w*NS, (w+1)*NS) over the 32
+//      tokens of tile i (B/C rows are wave-uniform scalar loads) and
+//      publishes its partial sums C.h per token in LDS;
+//   C (4 waves): the S partials of 8 tokens of tile i-1 added in wave order
+//      (so the result is deterministic), the D skip and the silu gate, and
+//      the store of y.
+// Each state is updated exactly once per token: no segment aggregates, no
+// rescans.  The roles share every SIMD (for S = 8: two B waves, one A and one
+// C): the short, latency-bound softplus and silu chains of A and C fill the
+// issue slots the B waves leave open, and the B waves, whose work per tile
+// is equal, reach the barrier together.  A and C each keep two sets of
+// pieces (even and odd tiles, fetched two tiles ahead) and the loop is
+// unrolled by two, so no registers are copied and no load is waited for
+// early.
+//
+// Per dtype (each choice measured faster for its dtype): with bf16 rows the
+// B waves are the block's first waves (the older wave wins issue ties), the
+// B/C rows of the next tile's first sub-chunk are fetched during the last
+// sub-chunk (before the barrier), and y goes out two tiles at a time, so
+// that both halves of each 128-byte line are written together; with fp32
+// rows the A and C waves come first and the B/C rows of a tile are fetched
+// after its barrier (a 128-byte fp32 line is one tile, written by the four
+// C waves together).
+template <typename IoT, int N, int S>
 struct Split {
   static constexpr int NS = N / S;
   static constexpr int T = 32;
-  static constexpr int TS = T / SA;
+  static constexpr int TS = 8;         // tokens of a tile per A or C wave
+  static constexpr int RW = T / TS;    // A waves = C waves = 4
   static constexpr int KT = T / kChunk;
+  static constexpr int kWaves = S + 2 * RW;
+  static constexpr bool kBF = sizeof(IoT) == 2;
   static constexpr int kDxFloat4 = (T / 2) * 64;      // [T/2][64] of (Delta_t, x_t, Delta_t+1, x_t+1)
   static constexpr int kYpFloat4 = S * (T / 4) * 64;  // [S][T/4][64] of 4 partial sums
   static constexpr int kLdsBytes = 2 * 16 * (kDxFloat4 + kYpFloat4);  // double-buffered
   static_assert(kLdsBytes <= 160 * 1024, "LDS budget of a gfx950 workgroup");
   static_assert(N % S == 0 && NS <= 2, "state split: at most two states per wave");
-  static_assert(SA <= S && T % SA == 0 && TS % 4 == 0 && kChunk % TS == 0 && T % kChunk == 0, "tile shape");
-  static_assert(KT % 2 == 0, "an even number of sub-chunks per tile: sub-chunk k uses B/C buffer k % 2");
+  static_assert(T % kChunk == 0 && KT % 2 == 0, "an even number of sub-chunks per tile: sub-chunk k uses B/C buffer k % 2");
+  static_assert(kWaves * 64 <= 1024, "workgroup size");
 };
 
 // TS tokens of one row starting at p (TS * sizeof(IoT) bytes, aligned to that).
@@ -734,121 +750,71 @@ struct Piece {
 };
 
 // kCplx: complex diagonal A.  The N slots of a channel hold N/2 complex
-// states as (re, im) pairs (A, h0, last_state), and each wave owns one
+// states as (re, im) pairs (A, h0, last_state), and each B wave owns one
 // complex state (NS = 2 slots); B and C rows are (re, im)-interleaved
 // [batch][N/2][seqlen][2], and the output is 2 Re(sum C h) + D u (each
 // stored state stands for a conjugate pair).
-template <typename IoT, int N, int S, int SA, bool kZ, bool kSoftplus, bool kConv, bool kZoh, bool kCplx = false>
-__global__ __launch_bounds__(64 * S) void scan_split_kernel(ScanArgs a) {
-  using C = Split<IoT, N, S, SA>;
-  static_assert(!kCplx || (C::NS == 2 && !kConv && !kZoh), "one complex state per wave, Delta * B rule, no conv");
-  constexpr int TS = C::TS;
+template <typename IoT, int N, int S, bool kZ, bool kSoftplus, bool kConv, bool kZoh, bool kCplx = false>
+__global__ __launch_bounds__((64 * Split<IoT, N, S>::kWaves)) void scan_split_kernel(ScanArgs a) {
+  using SP = Split<IoT, N, S>;
+  static_assert(!kCplx || (SP::NS == 2 && !kConv && !kZoh), "one complex state per wave, Delta * B rule, no conv");
+  constexpr int NS = SP::NS, T = SP::T, TS = SP::TS, RW = SP::RW, KT = SP::KT;
+  constexpr bool kBFirst = SP::kBF, kAhead = SP::kBF, kPair = SP::kBF;
   using LI = Line<IoT>;
   using PI = Piece<IoT, TS>;
-  using HI = Piece<IoT, 4>;          // the 4 inputs in front of a piece (conv history)
-  constexpr int HW = HI::kWords;
+  using HI = Piece<IoT, 4>;  // the 4 inputs in front of a piece (conv history)
   using U = Uni<IoT>;
-  constexpr int NS = C::NS, T = C::T, KT = C::KT, PW = PI::kWords, ZW = kZ ? PI::kWords : 1, W = U::kWords;
+  constexpr int PW = PI::kWords, ZW = kZ ? PI::kWords : 1, W = U::kWords, HW = kConv ? HI::kWords : 1;
   // Double-buffered by tile parity: one barrier per tile (see below).
-  __shared__ float4 dx[2][C::kDxFloat4];
-  __shared__ float4 yp[2][C::kYpFloat4];
+  __shared__ float4 dx[2][SP::kDxFloat4];
+  __shared__ float4 yp[2][SP::kYpFloat4];
 
   const int lane = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  // role 0 = B, 1 = A, 2 = C; rw = the wave's index within its role.
+  int role, rw;
+  if (kBFirst) {
+    role = wv < S ? 0 : (wv < S + RW ? 1 : 2);
+    rw = wv < S ? wv : (wv < S + RW ? wv - S : wv - S - RW);
+  } else {
+    role = wv < RW ? 1 : (wv < 2 * RW ? 2 : 0);
+    rw = wv < RW ? wv : (wv < 2 * RW ? wv - RW : wv - 2 * RW);
+  }
   const int64_t g = blockIdx.x % a.groups;
   const int64_t b = blockIdx.x / a.groups;
   const int64_t d_raw = g * kWaveThreads + lane;
   const bool active = d_raw < a.dim;
-  const int64_t d = active ? d_raw : a.dim - 1;
+  const int64_t d = active ? d_raw : a.dim - 1;  // idle lanes shadow a valid channel, write nothing
   const int64_t L = a.seqlen;
   const int64_t ch = b * a.dim + d;
 
-  float A2[NS], inva[NS], h[NS];
-#pragma unroll
-  for (int j = 0; j < NS; ++j) {
-    const int n = w * NS + j;
-    const float an = a.A[d * N + n];
-    // Complex: A2 = (Re A log2(e), Im A / 2 pi), the exp2 argument and the
-    // rotation in turns per unit of Delta.
-    A2[j] = (kCplx && j == 1) ? an * kInv2Pi : an * kLog2e;
-    inva[j] = 1.0f / an;
-    h[j] = a.h0 ? a.h0[ch * N + n] : 0.0f;
-  }
-  const float Dd = a.D ? a.D[d] : 0.0f;
-  const float bias = a.bias ? a.bias[d] : 0.0f;
-  // Fused conv: the channel's filter taps, oldest first.
+  const IoT* ur = static_cast<const IoT*>(a.u) + ch * L;  // x when the conv is fused
+  const IoT* dr = static_cast<const IoT*>(a.delta) + ch * L;
+  const IoT* zr = kZ ? static_cast<const IoT*>(a.z) + ch * L : nullptr;
+  IoT* yr = static_cast<IoT*>(a.y) + ch * L;
+  // A and C waves own tokens [l + rw*TS, l + rw*TS + TS) of the tile at l; a
+  // tile holds a multiple of kChunk = TS tokens, so the share is all or none.
+  auto has = [&](int64_t l) { return l + rw * TS < L; };
+
+  // Fused conv (A and C waves): the channel's filter taps, oldest first.
   float cw[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   float cbias = 0.0f;
   const int K = kConv ? a.conv_width : 1;
   if constexpr (kConv) {
+    if (role != 0) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
-      if (k < K) cw[k] = a.conv_w[d * K + k];
-    cbias = a.conv_b ? a.conv_b[d] : 0.0f;
+      for (int k = 0; k < 4; ++k)
+        if (k < K) cw[k] = a.conv_w[d * K + k];
+      cbias = a.conv_b ? a.conv_b[d] : 0.0f;
+    }
   }
-
-  const IoT* ur = static_cast<const IoT*>(a.u) + ch * L;  // x when the conv is fused
-  IoT* uo = kConv && a.u_out ? static_cast<IoT*>(a.u_out) + ch * L : nullptr;
-  const IoT* dr = static_cast<const IoT*>(a.delta) + ch * L;
-  const IoT* zr = kZ ? static_cast<const IoT*>(a.z) + ch * L : nullptr;
-  IoT* yr = static_cast<IoT*>(a.y) + ch * L;
-
-  // B/C words of this wave's states for one sub-chunk of kChunk tokens, in
-  // two buffers: sub-chunk k of a tile uses buffer k % 2, and the next sub-
-  // chunk's rows are fetched while the current one computes (each fetch is
-  // issued only after the buffer it overwrites has been waited for).
-  const IoT* Bb = static_cast<const IoT*>(a.B) + b * N * L;
-  const IoT* Cb = static_cast<const IoT*>(a.C) + b * N * L;
-  const uint32_t row_bytes = (uint32_t)(L * sizeof(IoT));
-  uint32_t Bx[2][NS][W], Cx[2][NS][W];
-  auto fetch_bc = [&](int s, int64_t lt) {
-#pragma unroll
-    for (int j = 0; j < NS; ++j) {
-      // Complex rows are twice as long; slot j holds tokens [4j, 4j + 4) as (re, im) pairs.
-      uint32_t off = kCplx ? (uint32_t)(w * NS) * row_bytes + (uint32_t)((2 * lt + 8 * j) * sizeof(IoT))
-                           : (uint32_t)(w * NS + j) * row_bytes + (uint32_t)(lt * sizeof(IoT));
-      // Materialise the offset here: an address computed in another block
-      // is not merged into whole-row s_load_dwordx4/x8 loads.
-      asm volatile("" : "+s"(off));
-      U::load8(Bb, off, Bx[s][j]);
-      U::load8(Cb, off, Cx[s][j]);
-    }
-  };
-  // (Delta, x) of sub-chunk k of the tile in dx[buf].
-  auto read_dx = [&](int buf, int k, float (&dl)[kChunk], float (&xl)[kChunk]) {
-#pragma unroll
-    for (int i = 0; i < kChunk / 2; ++i) {
-      float4 v = dx[buf][(k * kChunk / 2 + i) * 64 + lane];
-      dl[2 * i] = v.x; xl[2 * i] = v.y; dl[2 * i + 1] = v.z; xl[2 * i + 1] = v.w;
-    }
-  };
-  // The S partial sums of this wave's TS tokens of the tile in yp[buf].
-  auto read_partials = [&](int buf, float4 (&part)[TS / 4][S]) {
-#pragma unroll
-    for (int q = 0; q < TS / 4; ++q)
-#pragma unroll
-      for (int s2 = 0; s2 < S; ++s2) part[q][s2] = yp[buf][(s2 * (T / 4) + (w * TS) / 4 + q) * 64 + lane];
-  };
-
-  // This wave's TS-token pieces of u, delta, z, four tiles in flight:
-  //   p*: tile i-1 (u, z for phase C of tile i-1)
-  //   c*: tile i   (u, z kept for phase C of tile i)
-  //   a*: tile i+1 (widened by phase A of tile i+1)
-  //   n*: tile i+2 (fetched during phase A of tile i+1)
-  // With the conv fused, the a* and n* pieces hold x (plus the four inputs in
-  // front of the piece, ah/nh) until phase A turns them into u.
-  uint32_t pu[PW], pz[ZW], cu[PW], cz[ZW], au[PW], ad[PW], az[ZW], nu[PW], nd[PW], nz[ZW];
-  uint32_t ah[HW], nh[HW];
-  auto fetch = [&](int64_t l, uint32_t (&qu)[PW], uint32_t (&qd)[PW], uint32_t (&qz)[ZW], uint32_t (&qh)[HW]) {
-    const int64_t p0 = l + w * TS;
-    PI::load(ur + p0, qu);
-    PI::load(dr + p0, qd);
-    if constexpr (kZ) PI::load(zr + p0, qz);
+  // The four conv inputs in front of the piece at p0: the row itself, or for
+  // p0 = 0 the last K-1 slots of x_prev (else zero).
+  auto fetch_history = [&](int64_t p0, uint32_t (&qh)[HW]) {
     if constexpr (kConv) {
       if (p0 > 0) {
         HI::load(ur + p0 - 4, qh);
       } else {
-        // Token 0: the history is x_prev (the last K-1 of its slots), else zero.
         float hv[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -907,225 +873,267 @@ __global__ __launch_bounds__(64 * S) void scan_split_kernel(ScanArgs a) {
       for (int t = 0; t < TS / 2; ++t) q[t] = Io<bf16_t>::pack2(uv[2 * t], uv[2 * t + 1]);
     }
   };
-  // Phase A prologue for the piece of the tile at lt: with the conv fused,
-  // x becomes u (stored to u_out when asked).
-  auto make_u = [&](int64_t lt) {
-    if constexpr (kConv) {
-      conv_piece(au, ah);
-      if (uo && active) PI::store(uo + lt + w * TS, au);
-    }
-  };
-  // Phase A: widen this wave's tokens of a tile and publish (Delta, x):
-  // x = Delta * u, or u itself under zero-order hold.
-  auto widen = [&](int buf, const uint32_t (&qu)[PW], const uint32_t (&qd)[PW]) {
-#pragma unroll
-    for (int t = 0; t < TS; t += 2) {
-      float d0 = discretize_delta<kSoftplus>(LI::elem(qd, t), bias);
-      float d1 = discretize_delta<kSoftplus>(LI::elem(qd, t + 1), bias);
-      const float u0 = LI::elem(qu, t), u1 = LI::elem(qu, t + 1);
-      dx[buf][((w * TS + t) / 2) * 64 + lane] =
-          kZoh ? make_float4(d0, u0, d1, u1) : make_float4(d0, d0 * u0, d1, d1 * u1);
-    }
-  };
-  // Phase C: sum the partials in wave order, gate, store the tile at lc.
-  auto finish = [&](const float4 (&part)[TS / 4][S], int64_t lc, const uint32_t (&qu)[PW],
-                    const uint32_t (&qz)[ZW]) {
-    float yo[TS];
-#pragma unroll
-    for (int q = 0; q < TS / 4; ++q) {
-      float4 acc = part[q][0];
-#pragma unroll
-      for (int s2 = 1; s2 < S; ++s2) {
-        acc.x += part[q][s2].x; acc.y += part[q][s2].y; acc.z += part[q][s2].z; acc.w += part[q][s2].w;
-      }
-      if constexpr (kCplx) {  // each state and its conjugate partner
-        acc.x *= 2.0f; acc.y *= 2.0f; acc.z *= 2.0f; acc.w *= 2.0f;
-      }
-      yo[4 * q] = acc.x; yo[4 * q + 1] = acc.y; yo[4 * q + 2] = acc.z; yo[4 * q + 3] = acc.w;
-    }
-#pragma unroll
-    for (int t = 0; t < TS; ++t) yo[t] = epilogue<kZ>(yo[t], Dd, LI::elem(qu, t), kZ ? LI::elem(qz, t) : 0.0f);
-    uint32_t yw[PW];
-    if constexpr (sizeof(IoT) == 4) {
-#pragma unroll
-      for (int t = 0; t < TS; ++t) yw[t] = __float_as_uint(yo[t]);
-    } else {
-#pragma unroll
-      for (int t = 0; t < TS / 2; ++t) yw[t] = Io<bf16_t>::pack2(yo[2 * t], yo[2 * t + 1]);
-    }
-    if (active) PI::store(yr + lc + w * TS, yw);
-  };
-  // A wave's share of a tile is all-or-nothing: tiles hold a multiple of
-  // kChunk tokens and TS divides kChunk.  Waves w >= SA own no tokens.
-  auto owns = [&](int64_t l) { return w < SA && l < L && l + w * TS < L; };
 
-  if (owns(0)) {
-    fetch(0, au, ad, az, ah);
-    if (owns(T)) fetch(T, nu, nd, nz, nh);
-    make_u(0);
-    widen(0, au, ad);
-#pragma unroll
-    for (int q = 0; q < PW; ++q) {
-      cu[q] = au[q];
-      if constexpr (kZ) cz[q] = az[q];
-      au[q] = nu[q];
-      ad[q] = nd[q];
-      if constexpr (kZ) az[q] = nz[q];
-    }
-    if constexpr (kConv) {
-#pragma unroll
-      for (int q = 0; q < HW; ++q) ah[q] = nh[q];
-    }
-  }
-  __syncthreads();
-
-  // Iteration i (tile i at l, buf = i % 2):
-  //   issue the B/C scalar loads and the dx[buf] LDS reads of sub-chunk 0,
-  //   and the LDS reads of the partials of tile i-1 in yp[buf^1];  A(i+1)
-  //   writes dx[buf^1];  C(i-1) consumes the partials;  B(i) reads dx[buf]
-  //   and B/C one sub-chunk ahead and writes yp[buf];  LDS barrier.
-  // The single barrier orders every cross-wave hand-off: B(i) needs all of
-  // A(i) (written before barrier i-1); C(i-1) needs all of B(i-1) (before
-  // barrier i-1); A(i+1) overwrites dx[buf^1], last read by B(i-1) before
-  // barrier i-1; B(i) overwrites yp[buf], last read at the start of
-  // iteration i-1, before barrier i-1.  Issuing the reads first lets phase A's
-  // arithmetic cover their latency instead of every wave stalling on them at
-  // once after the barrier.
-  int buf = 0;
-  for (int64_t l = 0; l < L; l += T, buf ^= 1) {
-    const int valid = (int)min((int64_t)T, L - l);  // a multiple of kChunk
-    float dl[KT][kChunk], xl[KT][kChunk];
-    float4 part[TS / 4][S];
-    const bool prev = l > 0 && owns(l - T);
-    fetch_bc(0, l);
-    read_dx(buf, 0, dl[0], xl[0]);
-    if (prev) read_partials(buf ^ 1, part);
-    __builtin_amdgcn_sched_barrier(0);
-    // ---- A of the next tile
-    if (owns(l + T)) {
-      if (owns(l + 2 * T)) fetch(l + 2 * T, nu, nd, nz, nh);
-      make_u(l + T);
-      widen(buf ^ 1, au, ad);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    // ---- C of the previous tile
-    if (prev) finish(part, l - T, pu, pz);
-    __builtin_amdgcn_sched_barrier(0);
-    // ---- B: this wave's states over the tile, one sub-chunk at a time.
-#pragma unroll
-    for (int k = 0; k < KT; ++k) {
-      if (k * kChunk < valid) {
-        const int s = k & 1;
-        // One wait covers this sub-chunk's (Delta, x) and B/C words.
-        settle_vgprs(dl[k]);
-        settle_vgprs(xl[k]);
-#pragma unroll
-        for (int j = 0; j < NS; ++j) {
-          settle_sgprs(Bx[s][j]);
-          settle_sgprs(Cx[s][j]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        // Prefetch the next sub-chunk of this tile.  (The first sub-chunk of
-        // the next tile is fetched after the barrier: a scalar load in flight
-        // would hold up the LDS wait in front of it.)
-        if (k + 1 < KT && (k + 1) * kChunk < valid) {
-          const int kn = (k + 1 < KT) ? k + 1 : k;  // (the clamp only keeps the index static)
-          read_dx(buf, kn, dl[kn], xl[kn]);
-          fetch_bc(s ^ 1, l + (k + 1) * kChunk);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        if (a.ckpt && (k * kChunk) % kCkptTokens == 0) {
-          // The state before token l + k*kChunk, for the backward's recompute.
-          const int64_t c = (l + k * kChunk) / kCkptTokens;
-#pragma unroll
-          for (int j = 0; j < NS; ++j)
-            if (active) a.ckpt[((c * a.batch + b) * N + w * NS + j) * a.dim + d] = h[j];
-        }
-        float yv[kChunk], du[kChunk];
-        if constexpr (kZoh) {
-#pragma unroll
-          for (int t = 0; t < kChunk; ++t) du[t] = dl[k][t] * xl[k][t];
-        }
-        if constexpr (kCplx) {
-          // h <- exp(Delta A) h + Delta B u in complex arithmetic; the partial
-          // is Re(C h) = Re C Re h - Im C Im h.
-          float hr = h[0], hi = h[1];
-#pragma unroll
-          for (int t = 0; t < kChunk; ++t) {
-            const int jj = t >> 2, q = 2 * (t & 3);
-            const float mag = exp2_hw(A2[0] * dl[k][t]);
-            const float turn = __builtin_amdgcn_fractf(A2[1] * dl[k][t]);
-            const float pr = mag * __builtin_amdgcn_cosf(turn), pi = mag * __builtin_amdgcn_sinf(turn);
-            const float x = xl[k][t];
-            const float nr = __builtin_fmaf(pr, hr, __builtin_fmaf(-pi, hi, U::elem(Bx[s][jj], q) * x));
-            const float ni = __builtin_fmaf(pr, hi, __builtin_fmaf(pi, hr, U::elem(Bx[s][jj], q + 1) * x));
-            hr = nr;
-            hi = ni;
-            yv[t] = __builtin_fmaf(U::elem(Cx[s][jj], q), hr, -(U::elem(Cx[s][jj], q + 1) * hi));
-          }
-          h[0] = hr;
-          h[1] = hi;
-          asm volatile("" : "+v"(h[0]), "+v"(h[1]));
-        } else {
-#pragma unroll
-        for (int j = 0; j < NS; ++j) {
-          float hn = h[j];
-#pragma unroll
-          for (int t = 0; t < kChunk; ++t) {
-            const float ta = A2[j] * dl[k][t];
-            const float abar = exp2_hw(ta);
-            const float bu = kZoh ? zoh_input(ta, abar, du[t], xl[k][t] * inva[j]) : xl[k][t];
-            hn = __builtin_fmaf(abar, hn, U::elem(Bx[s][j], t) * bu);
-            const float cv = U::elem(Cx[s][j], t);
-            yv[t] = (j == 0) ? cv * hn : __builtin_fmaf(cv, hn, yv[t]);
-          }
-          h[j] = hn;
-          // The state's results must exist here: the compiler may not sink
-          // the C.h accumulation below the next state's work.
-          asm volatile("" : "+v"(h[j]));
-        }
-        }
-        yp[buf][(w * (T / 4) + 2 * k) * 64 + lane] = make_float4(yv[0], yv[1], yv[2], yv[3]);
-        yp[buf][(w * (T / 4) + 2 * k + 1) * 64 + lane] = make_float4(yv[4], yv[5], yv[6], yv[7]);
-        __builtin_amdgcn_sched_barrier(0);
+  if (role == 1) {
+    // ---- A: (Delta, x) of tile i+1 into dx[(i+1) % 2] at iteration i.
+    const float bias = a.bias ? a.bias[d] : 0.0f;
+    IoT* uo = kConv && a.u_out ? static_cast<IoT*>(a.u_out) + ch * L : nullptr;
+    uint32_t eu[PW], ed[PW], ou[PW], od[PW], eh[HW], oh[HW];  // even / odd tiles
+    auto fetch = [&](int64_t l, uint32_t (&qu)[PW], uint32_t (&qd)[PW], uint32_t (&qh)[HW]) {
+      if (has(l)) {
+        const int64_t p0 = l + rw * TS;
+        PI::load(ur + p0, qu);
+        PI::load(dr + p0, qd);
+        fetch_history(p0, qh);
       }
-    }
-    // Rotate the pieces (only the waves that own tokens hold any).  The pins
-    // keep the compiler from deferring the copies (and the wait on the tile
-    // i+2 fetch) into the next phase A.
-    if (w < SA) {
-#pragma unroll
-      for (int q = 0; q < PW; ++q) {
-        pu[q] = cu[q];
-        if constexpr (kZ) pz[q] = cz[q];
-        cu[q] = au[q];
-        if constexpr (kZ) cz[q] = az[q];
-        au[q] = nu[q];
-        ad[q] = nd[q];
-        if constexpr (kZ) az[q] = nz[q];
-      }
+    };
+    // x = Delta * u, or u itself under zero-order hold.
+    auto produce = [&](int bf, int64_t l, uint32_t (&qu)[PW], const uint32_t (&qd)[PW], const uint32_t (&qh)[HW]) {
+      if (!has(l)) return;
       if constexpr (kConv) {
-#pragma unroll
-        for (int q = 0; q < HW; ++q) ah[q] = nh[q];
-        settle_vgprs(ah);
+        conv_piece(qu, qh);
+        if (uo && active) PI::store(uo + l + rw * TS, qu);
       }
-      settle_vgprs(au);
-      settle_vgprs(ad);
-      if constexpr (kZ) settle_vgprs(az);
-    }
-    lds_barrier();
-  }
-  // ---- C of the last tile (its partials are in yp[buf^1]).
-  const int64_t l_last = ((L - 1) / T) * T;
-  if (owns(l_last)) {
-    float4 part[TS / 4][S];
-    read_partials(buf ^ 1, part);
-    finish(part, l_last, pu, pz);
-  }
-
-  if (a.last_state && active) {
 #pragma unroll
-    for (int j = 0; j < NS; ++j) a.last_state[ch * N + w * NS + j] = h[j];
+      for (int t = 0; t < TS; t += 2) {
+        float d0 = discretize_delta<kSoftplus>(LI::elem(qd, t), bias);
+        float d1 = discretize_delta<kSoftplus>(LI::elem(qd, t + 1), bias);
+        const float u0 = LI::elem(qu, t), u1 = LI::elem(qu, t + 1);
+        dx[bf][((rw * TS + t) / 2) * 64 + lane] =
+            kZoh ? make_float4(d0, u0, d1, u1) : make_float4(d0, d0 * u0, d1, d1 * u1);
+      }
+    };
+    fetch(0, eu, ed, eh);
+    fetch(T, ou, od, oh);
+    produce(0, 0, eu, ed, eh);
+    fetch(2 * T, eu, ed, eh);
+    __syncthreads();
+    for (int64_t l = 0; l < L; l += 2 * T) {
+      produce(1, l + T, ou, od, oh);  // even iteration: the odd tile after it
+      fetch(l + 3 * T, ou, od, oh);
+      lds_barrier();
+      if (l + T < L) {
+        produce(0, l + 2 * T, eu, ed, eh);  // odd iteration: the even tile after it
+        fetch(l + 4 * T, eu, ed, eh);
+        lds_barrier();
+      }
+    }
+  } else if (role == 2) {
+    // ---- C: tile i-1 at iteration i, from its partials in yp[(i-1) % 2].
+    const float Dd = a.D ? a.D[d] : 0.0f;
+    uint32_t eu[PW], ez[ZW], ou[PW], oz[ZW], eh[HW], oh[HW];  // even / odd tiles (u, or x with the conv)
+    uint32_t ye[PW], yo[PW];
+    auto fetch = [&](int64_t l, uint32_t (&qu)[PW], uint32_t (&qz)[ZW], uint32_t (&qh)[HW]) {
+      if (has(l)) {
+        const int64_t p0 = l + rw * TS;
+        PI::load(ur + p0, qu);
+        if constexpr (kZ) PI::load(zr + p0, qz);
+        fetch_history(p0, qh);
+      }
+    };
+    auto finish = [&](int bf, int64_t lc, uint32_t (&qu)[PW], const uint32_t (&qz)[ZW], const uint32_t (&qh)[HW],
+                      uint32_t (&yw)[PW]) {
+      if (!has(lc)) return;
+      if constexpr (kConv) conv_piece(qu, qh);  // u again, bitwise as the A wave made it
+      float yv[TS];
+#pragma unroll
+      for (int q = 0; q < TS / 4; ++q) {
+        float4 part[S];
+#pragma unroll
+        for (int s2 = 0; s2 < S; ++s2) part[s2] = yp[bf][(s2 * (T / 4) + (rw * TS) / 4 + q) * 64 + lane];
+        float4 acc = part[0];
+#pragma unroll
+        for (int s2 = 1; s2 < S; ++s2) {
+          acc.x += part[s2].x; acc.y += part[s2].y; acc.z += part[s2].z; acc.w += part[s2].w;
+        }
+        if constexpr (kCplx) {  // each state and its conjugate partner
+          acc.x *= 2.0f; acc.y *= 2.0f; acc.z *= 2.0f; acc.w *= 2.0f;
+        }
+        yv[4 * q] = acc.x; yv[4 * q + 1] = acc.y; yv[4 * q + 2] = acc.z; yv[4 * q + 3] = acc.w;
+      }
+#pragma unroll
+      for (int t = 0; t < TS; ++t) yv[t] = epilogue<kZ>(yv[t], Dd, LI::elem(qu, t), kZ ? LI::elem(qz, t) : 0.0f);
+      if constexpr (sizeof(IoT) == 4) {
+#pragma unroll
+        for (int t = 0; t < TS; ++t) yw[t] = __float_as_uint(yv[t]);
+      } else {
+#pragma unroll
+        for (int t = 0; t < TS / 2; ++t) yw[t] = Io<bf16_t>::pack2(yv[2 * t], yv[2 * t + 1]);
+      }
+    };
+    auto put = [&](int64_t lc, const uint32_t (&yw)[PW]) {
+      if (active && has(lc)) PI::store(yr + lc + rw * TS, yw);
+    };
+    // kPair: an even tile's piece is kept until the odd tile after it is
+    // finished, and both pieces of the 128-byte line are stored together.
+    fetch(0, eu, ez, eh);
+    __syncthreads();
+    for (int64_t l = 0; l < L; l += 2 * T) {
+      if (l > 0) {  // even iteration: the odd tile before it
+        finish(1, l - T, ou, oz, oh, yo);
+        if (kPair) put(l - 2 * T, ye);
+        put(l - T, yo);
+      }
+      fetch(l + T, ou, oz, oh);
+      lds_barrier();
+      if (l + T < L) {  // odd iteration: the even tile before it
+        finish(0, l, eu, ez, eh, ye);
+        if (!kPair) put(l, ye);
+        fetch(l + 2 * T, eu, ez, eh);
+        lds_barrier();
+      }
+    }
+    // The last tile (its partials are in yp[jl % 2]).
+    const int64_t jl = (L - 1) / T;
+    if (jl & 1) {
+      finish(1, jl * T, ou, oz, oh, yo);
+      if (kPair) put((jl - 1) * T, ye);
+      put(jl * T, yo);
+    } else {
+      finish(0, jl * T, eu, ez, eh, ye);
+      put(jl * T, ye);
+    }
+  } else {
+    // ---- B: this wave's states over tile i, one sub-chunk of kChunk tokens at a time.
+    float A2[NS], inva[NS], h[NS];
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      const int n = rw * NS + j;
+      const float an = a.A[d * N + n];
+      // Complex: A2 = (Re A log2(e), Im A / 2 pi), the exp2 argument and the
+      // rotation in turns per unit of Delta.
+      A2[j] = (kCplx && j == 1) ? an * kInv2Pi : an * kLog2e;
+      inva[j] = 1.0f / an;
+      h[j] = a.h0 ? a.h0[ch * N + n] : 0.0f;
+    }
+    // B/C words of this wave's states for one sub-chunk, in two buffers:
+    // sub-chunk k of a tile uses buffer k % 2, and the next sub-chunk's rows
+    // are fetched while the current one computes (each fetch is issued only
+    // after the buffer it overwrites has been waited for).
+    const IoT* Bb = static_cast<const IoT*>(a.B) + b * N * L;
+    const IoT* Cb = static_cast<const IoT*>(a.C) + b * N * L;
+    const uint32_t row_bytes = (uint32_t)(L * sizeof(IoT));
+    uint32_t Bx[2][NS][W], Cx[2][NS][W];
+    auto fetch_bc = [&](int s, int64_t lt) {
+#pragma unroll
+      for (int j = 0; j < NS; ++j) {
+        // Complex rows are twice as long; slot j holds tokens [4j, 4j + 4) as (re, im) pairs.
+        uint32_t off = kCplx ? (uint32_t)(rw * NS) * row_bytes + (uint32_t)((2 * lt + 8 * j) * sizeof(IoT))
+                             : (uint32_t)(rw * NS + j) * row_bytes + (uint32_t)(lt * sizeof(IoT));
+        // Materialise the offset here: an address computed in another block
+        // is not merged into whole-row s_load_dwordx4/x8 loads.
+        asm volatile("" : "+s"(off));
+        U::load8(Bb, off, Bx[s][j]);
+        U::load8(Cb, off, Cx[s][j]);
+      }
+    };
+    // (Delta, x) of sub-chunk k of the tile in dx[bf].
+    auto read_dx = [&](int bf, int k, float (&dl)[kChunk], float (&xl)[kChunk]) {
+#pragma unroll
+      for (int i = 0; i < kChunk / 2; ++i) {
+        float4 v = dx[bf][(k * kChunk / 2 + i) * 64 + lane];
+        dl[2 * i] = v.x; xl[2 * i] = v.y; dl[2 * i + 1] = v.z; xl[2 * i + 1] = v.w;
+      }
+    };
+    __syncthreads();
+    if (kAhead) fetch_bc(0, 0);
+    // Iteration i (tile i at l, buf = i % 2): B(i) reads dx[buf], written by
+    // A(i) before barrier i-1, and writes yp[buf], last read by C(i-2)
+    // before barrier i-1; meanwhile A(i+1) writes dx[buf^1] (last read by
+    // B(i-1) before barrier i-1) and C(i-1) reads yp[buf^1] (written by
+    // B(i-1) before barrier i-1).  The single barrier per tile therefore
+    // orders every cross-wave hand-off.  It fences LDS only, so global loads
+    // and stores stay in flight across it.
+    int buf = 0;
+    for (int64_t l = 0; l < L; l += T, buf ^= 1) {
+      const int valid = (int)min((int64_t)T, L - l);  // a multiple of kChunk
+      float dl[KT][kChunk], xl[KT][kChunk];
+      if (!kAhead) fetch_bc(0, l);
+      read_dx(buf, 0, dl[0], xl[0]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int k = 0; k < KT; ++k) {
+        if (k * kChunk < valid) {
+          const int s = k & 1;
+          // One wait covers this sub-chunk's (Delta, x) and B/C words.
+          settle_vgprs(dl[k]);
+          settle_vgprs(xl[k]);
+#pragma unroll
+          for (int j = 0; j < NS; ++j) {
+            settle_sgprs(Bx[s][j]);
+            settle_sgprs(Cx[s][j]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          if (k + 1 < KT && (k + 1) * kChunk < valid) {
+            const int kn = (k + 1 < KT) ? k + 1 : k;  // (the clamp only keeps the index static)
+            read_dx(buf, kn, dl[kn], xl[kn]);
+            fetch_bc(s ^ 1, l + (k + 1) * kChunk);
+          } else if (kAhead && k + 1 == KT && l + T < L) {
+            fetch_bc(s ^ 1, l + T);  // the next tile's first sub-chunk (buffer 0: KT is even)
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          if (a.ckpt && (k * kChunk) % kCkptTokens == 0) {
+            // The state before token l + k*kChunk, for the backward's recompute.
+            const int64_t c = (l + k * kChunk) / kCkptTokens;
+#pragma unroll
+            for (int j = 0; j < NS; ++j)
+              if (active) a.ckpt[((c * a.batch + b) * N + rw * NS + j) * a.dim + d] = h[j];
+          }
+          float yv[kChunk], du[kChunk];
+          if constexpr (kZoh) {
+#pragma unroll
+            for (int t = 0; t < kChunk; ++t) du[t] = dl[k][t] * xl[k][t];
+          }
+          if constexpr (kCplx) {
+            // h <- exp(Delta A) h + Delta B u in complex arithmetic; the partial
+            // is Re(C h) = Re C Re h - Im C Im h.
+            float hr = h[0], hi = h[1];
+#pragma unroll
+            for (int t = 0; t < kChunk; ++t) {
+              const int jj = t >> 2, q = 2 * (t & 3);
+              const float mag = exp2_hw(A2[0] * dl[k][t]);
+              const float turn = __builtin_amdgcn_fractf(A2[1] * dl[k][t]);
+              const float pr = mag * __builtin_amdgcn_cosf(turn), pi = mag * __builtin_amdgcn_sinf(turn);
+              const float x = xl[k][t];
+              const float nr = __builtin_fmaf(pr, hr, __builtin_fmaf(-pi, hi, U::elem(Bx[s][jj], q) * x));
+              const float ni = __builtin_fmaf(pr, hi, __builtin_fmaf(pi, hr, U::elem(Bx[s][jj], q + 1) * x));
+              hr = nr;
+              hi = ni;
+              yv[t] = __builtin_fmaf(U::elem(Cx[s][jj], q), hr, -(U::elem(Cx[s][jj], q + 1) * hi));
+            }
+            h[0] = hr;
+            h[1] = hi;
+            asm volatile("" : "+v"(h[0]), "+v"(h[1]));
+          } else {
+#pragma unroll
+            for (int j = 0; j < NS; ++j) {
+              float hn = h[j];
+#pragma unroll
+              for (int t = 0; t < kChunk; ++t) {
+                const float ta = A2[j] * dl[k][t];
+                const float abar = exp2_hw(ta);
+                const float bu = kZoh ? zoh_input(ta, abar, du[t], xl[k][t] * inva[j]) : xl[k][t];
+                hn = __builtin_fmaf(abar, hn, U::elem(Bx[s][j], t) * bu);
+                const float cv = U::elem(Cx[s][j], t);
+                yv[t] = (j == 0) ? cv * hn : __builtin_fmaf(cv, hn, yv[t]);
+              }
+              h[j] = hn;
+              // The state's results must exist here: the compiler may not sink
+              // the C.h accumulation below the next state's work.
+              asm volatile("" : "+v"(h[j]));
+            }
+          }
+          yp[buf][(rw * (T / 4) + 2 * k) * 64 + lane] = make_float4(yv[0], yv[1], yv[2], yv[3]);
+          yp[buf][(rw * (T / 4) + 2 * k + 1) * 64 + lane] = make_float4(yv[4], yv[5], yv[6], yv[7]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      lds_barrier();
+    }
+    if (a.last_state && active) {
+#pragma unroll
+      for (int j = 0; j < NS; ++j) a.last_state[ch * N + rw * NS + j] = h[j];
+    }
   }
 }
 
@@ -2568,34 +2576,32 @@ hipError_t launch_scan_f(const ScanArgs& a, const Plan& p, hipStream_t st, bool 
   return a.zoh ? launch_scan_z<IoT, N, kVec, true>(a, p, st, sp) : launch_scan_z<IoT, N, kVec, false>(a, p, st, sp);
 }
 
-template <typename IoT, int N, int S, int SA, bool kZ, bool kSp, bool kConv, bool kZoh, bool kCplx = false>
+template <typename IoT, int N, int S, bool kZ, bool kSp, bool kConv, bool kZoh, bool kCplx = false>
 hipError_t launch_split_t(const ScanArgs& a, const Plan& p, hipStream_t st) {
-  hipLaunchKernelGGL((scan_split_kernel<IoT, N, S, SA, kZ, kSp, kConv, kZoh, kCplx>),
-                     dim3((unsigned)(a.batch * p.groups)), dim3(64 * S), 0, st, a);
+  hipLaunchKernelGGL((scan_split_kernel<IoT, N, S, kZ, kSp, kConv, kZoh, kCplx>),
+                     dim3((unsigned)(a.batch * p.groups)), dim3(64 * Split<IoT, N, S>::kWaves), 0, st, a);
   return hipGetLastError();
 }
 
 // Complex A: NC complex states (2 NC slots), one per wave.
 template <typename IoT, int NC>
 hipError_t launch_split_cplx(const ScanArgs& a, const Plan& p, hipStream_t st, bool sp) {
-  constexpr int N = 2 * NC, S = NC, SA = 4;
+  constexpr int N = 2 * NC, S = NC;
   if (a.z)
-    return sp ? launch_split_t<IoT, N, S, SA, true, true, false, false, true>(a, p, st)
-              : launch_split_t<IoT, N, S, SA, true, false, false, false, true>(a, p, st);
-  return sp ? launch_split_t<IoT, N, S, SA, false, true, false, false, true>(a, p, st)
-            : launch_split_t<IoT, N, S, SA, false, false, false, false, true>(a, p, st);
+    return sp ? launch_split_t<IoT, N, S, true, true, false, false, true>(a, p, st)
+              : launch_split_t<IoT, N, S, true, false, false, false, true>(a, p, st);
+  return sp ? launch_split_t<IoT, N, S, false, true, false, false, true>(a, p, st)
+            : launch_split_t<IoT, N, S, false, false, false, false, true>(a, p, st);
 }
 
 template <typename IoT, int N, bool kConv, bool kZoh>
 hipError_t launch_split(const ScanArgs& a, const Plan& p, hipStream_t st, bool sp) {
   constexpr int S = (N >= SSM_SPLIT_WAVES) ? SSM_SPLIT_WAVES : N;
-  // Phases A and C run on one wave per SIMD (the first four waves).
-  constexpr int SA = (S > 4) ? 4 : S;
   if (a.z)
-    return sp ? launch_split_t<IoT, N, S, SA, true, true, kConv, kZoh>(a, p, st)
-              : launch_split_t<IoT, N, S, SA, true, false, kConv, kZoh>(a, p, st);
-  return sp ? launch_split_t<IoT, N, S, SA, false, true, kConv, kZoh>(a, p, st)
-            : launch_split_t<IoT, N, S, SA, false, false, kConv, kZoh>(a, p, st);
+    return sp ? launch_split_t<IoT, N, S, true, true, kConv, kZoh>(a, p, st)
+              : launch_split_t<IoT, N, S, true, false, kConv, kZoh>(a, p, st);
+  return sp ? launch_split_t<IoT, N, S, false, true, kConv, kZoh>(a, p, st)
+            : launch_split_t<IoT, N, S, false, false, kConv, kZoh>(a, p, st);
 }
 
 // The fused conv runs with the Delta * B rule only (its entry point has no
