@@ -54,10 +54,20 @@
  *    output with an input) happens on the host before any HIP call, so an
  *    invalid call returns an error code without touching the device.
  *  - NaN and Inf propagate; nothing is clamped.
- *  - The library may take stream-ordered scratch memory from a pool of its
- *    own during ssm_scan_fwd (per-segment carries of long sequences); it is
- *    released on the same stream before the call returns.  Calls on different
- *    streams are independent; the library is re-entrant.
+ *  - The prefill and decode entry points (ssm_scan_fwd, ssm_scan_fwd_ex,
+ *    ssm_scan_fwd_complex, ssm_conv_scan_fwd, ssm_scan_fwd_save and the
+ *    ssm_state_update family) allocate no device memory and need no
+ *    workspace: a long sequence scanned in parallel segments keeps each
+ *    segment's aggregate and carry-in inside that segment's own range of y
+ *    before y is written there (y's prior contents are never read as data).
+ *    They can therefore be captured into a HIP graph as plain kernel launches.
+ *  - The backward entry points (ssm_scan_bwd, ssm_scan_bwd_ex,
+ *    ssm_scan_bwd_complex, ssm_scan_bwd_saved, ssm_conv_bwd) take stream-
+ *    ordered scratch from a per-device pool of the library (checkpoints and
+ *    partial sums), freed on the same stream within the call.  The pool's
+ *    release threshold is 0: freed blocks are reused by later calls on the
+ *    stream and returned to the device at the next synchronisation.
+ *  - Calls on different streams are independent; the library is re-entrant.
  */
 #ifndef SSM_SCAN_H
 #define SSM_SCAN_H
@@ -68,7 +78,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 10
+#define SSM_ABI_VERSION 11
 
 struct ihipStream_t; /* the same incomplete type as HIP's hipStream_t */
 
@@ -155,9 +165,8 @@ ssm_status_t ssm_state_update(int64_t batch, int64_t dim, int64_t dstate, ssm_dt
  * of the sequence) or zero, and act is silu when conv_silu is nonzero.  u is
  * rounded to the io dtype, as if it had been stored, and then the scan of
  * ssm_scan_fwd runs on it.  The result equals the conv written to memory
- * followed by ssm_scan_fwd on it; where the single-pass path applies, u never
- * touches memory (it is computed in the scan's prologue) unless u_out asks
- * for it.
+ * followed by ssm_scan_fwd on it; u never touches memory (every kernel path
+ * computes it from x in its own prologue) unless u_out asks for it.
  *
  *   x            [batch, dim, seqlen]         io    conv input
  *   conv_weight  [dim, conv_width]            fp32  conv_weight[d, K-1] multiplies the current token
@@ -169,8 +178,8 @@ ssm_status_t ssm_state_update(int64_t batch, int64_t dim, int64_t dstate, ssm_dt
  *                                u_out must not overlap any input or output)
  *
  * Errors as ssm_scan_fwd, plus SSM_ERR_SHAPE for conv_width outside 1..4.
- * Shapes that do not take the single-pass path run a separate conv kernel
- * into u_out or into stream-ordered scratch from the library's pool.
+ * Allocates nothing.  A u_out that is not 16-byte aligned sends the call to
+ * the per-token kernel (SSM_PATH_GENERIC).
  */
 ssm_status_t ssm_conv_scan_fwd(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int64_t conv_width,
                                ssm_dtype_t io, const void* x, const float* conv_weight, const float* conv_bias,
@@ -442,8 +451,9 @@ typedef enum {
  * ssm_scan_fwd_plan -- how ssm_scan_fwd would run a problem of this shape,
  * assuming 16-byte aligned buffers (misaligned rows fall back to
  * SSM_PATH_GENERIC at call time): the kernel path, the number of sequence
- * segments scanned in parallel per channel, the segment length in tokens, and
- * the scratch bytes the call takes from the library's pool.  Pure host
+ * segments scanned in parallel per channel, the segment length in tokens (the
+ * last segment ends at seqlen and holds at least 64 tokens), and the scratch
+ * bytes the call takes (always 0: the prefill allocates nothing).  Pure host
  * arithmetic; any output pointer may be NULL.  Returns the same status
  * ssm_scan_fwd would return for these sizes.
  */

@@ -285,15 +285,12 @@ struct ScanArgs {
   const float* h0;    // may be null
   void* y;
   float* last_state;  // may be null
-  float* agg_sum;     // [P-1][batch*dim]            scratch, P > 1
-  float* agg_h;       // [P-1][batch*dim][dstate]    scratch, P > 1
-  float* carry;       // [P][batch*dim][dstate]      scratch, P > 1
   int64_t batch, dim, dstate, seqlen;
   int64_t groups;    // ceil(dim / 64)
   int64_t segments;  // P
-  int64_t seg_len;   // tokens per segment, a multiple of kChunk
-  // Fused causal conv in front of the scan (single-pass kernel only): u
-  // then holds the conv input x.
+  int64_t seg_len;   // tokens per segment, a multiple of 64; the last segment ends at seqlen
+  // Fused causal conv in front of the scan (every prefill kernel): u then
+  // holds the conv input x.
   const float* conv_w;  // [dim][conv_width]
   const float* conv_b;  // [dim], may be null
   const void* x_prev;   // [batch][dim][conv_width - 1], may be null
@@ -307,6 +304,103 @@ struct ScanArgs {
 };
 
 constexpr int kCkptTokens = 16;  // tokens between backward checkpoints (one backward tile)
+
+// The segmented path keeps each segment's aggregate and carry-in in the
+// caller's y, inside the segment's own range of each row, before that range
+// is written: 4-byte slot 0 holds the segment's sum of Delta, slots 1..N its
+// end state (launch 1), then its carry-in (launch 2, in place); launch 3
+// reads the carry-in before its own y overwrites it.  A segment is at least
+// 64 tokens, so the N + 1 slots (68 bytes at N = 16) fit in its range for
+// either dtype.  bf16 rows may be only 2-byte aligned, so the slots move as
+// 16-bit halves there.
+template <typename IoT>
+__device__ __forceinline__ float seg_slot_load(const void* y, int64_t seg_elem, int slot) {
+  const char* p = static_cast<const char*>(y) + seg_elem * (int64_t)sizeof(IoT) + 4 * slot;
+  if constexpr (sizeof(IoT) == 4) {
+    return *reinterpret_cast<const float*>(p);
+  } else {
+    const uint16_t* q = reinterpret_cast<const uint16_t*>(p);
+    return __uint_as_float((uint32_t)q[0] | ((uint32_t)q[1] << 16));
+  }
+}
+template <typename IoT>
+__device__ __forceinline__ void seg_slot_store(void* y, int64_t seg_elem, int slot, float v) {
+  char* p = static_cast<char*>(y) + seg_elem * (int64_t)sizeof(IoT) + 4 * slot;
+  if constexpr (sizeof(IoT) == 4) {
+    *reinterpret_cast<float*>(p) = v;
+  } else {
+    uint16_t* q = reinterpret_cast<uint16_t*>(p);
+    const uint32_t w = __float_as_uint(v);
+    q[0] = (uint16_t)(w & 0xffffu);
+    q[1] = (uint16_t)(w >> 16);
+  }
+}
+
+// The causal depthwise conv of one channel with a runtime width K <= 4, for
+// the kernels that walk a row token by token: wl[j] is the tap of lag j
+// (w[K-1-j]), and a tap of lag K or more is skipped by a select (not
+// multiplied by zero), so a non-finite input reaches exactly the K outputs
+// that read it.  The FMAs run from the oldest input to the current one, as
+// conv_taps<K> does, so every path rounds u identically.
+struct ConvChan {
+  float wl[4];
+  float bias;
+  int K;
+  bool silu;
+};
+
+__device__ __forceinline__ ConvChan conv_chan(const float* conv_w, const float* conv_b, int K, int silu, int64_t d) {
+  ConvChan c;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) c.wl[j] = (j < K) ? conv_w[d * K + (K - 1 - j)] : 0.0f;
+  c.bias = conv_b ? conv_b[d] : 0.0f;
+  c.K = K;
+  c.silu = silu != 0;
+  return c;
+}
+
+// u at a token from x at lags 3, 2, 1 and 0 (x3 oldest), before rounding.
+__device__ __forceinline__ float conv_token(const ConvChan& c, float x3, float x2, float x1, float x0) {
+  float acc = c.bias;
+  acc = (c.K > 3) ? __builtin_fmaf(c.wl[3], x3, acc) : acc;
+  acc = (c.K > 2) ? __builtin_fmaf(c.wl[2], x2, acc) : acc;
+  acc = (c.K > 1) ? __builtin_fmaf(c.wl[1], x1, acc) : acc;
+  acc = __builtin_fmaf(c.wl[0], x0, acc);
+  return acc;
+}
+
+__device__ __forceinline__ float conv_silu(const ConvChan& c, float v) { return c.silu ? silu_f32(v) : v; }
+
+// v rounded to the io dtype (as a stored u would be), returned as fp32.
+template <typename IoT>
+__device__ __forceinline__ float round_io(float v) {
+  if constexpr (sizeof(IoT) == 4) {
+    return v;
+  } else {
+    const __bf16 r = (__bf16)v;  // round to nearest even
+    return __uint_as_float((uint32_t)__builtin_bit_cast(uint16_t, r) << 16);
+  }
+}
+
+// The conv inputs at positions l0-3 .. l0-1 of row ch (oldest first): the
+// row itself, or before the sequence start the last K-1 slots of x_prev
+// (else zero).
+template <typename IoT>
+__device__ __forceinline__ void conv_history(const ScanArgs& a, int64_t ch, int64_t l0, float xh[3]) {
+  const IoT* x = static_cast<const IoT*>(a.u) + ch * a.seqlen;
+  const int K = a.conv_width;
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    const int64_t pos = l0 - 3 + i;
+    if (pos >= 0) {
+      xh[i] = Io<IoT>::load1(x + pos);
+    } else {
+      const int64_t idx = (K - 1) + pos;  // x_prev slot of position pos
+      xh[i] = (a.x_prev && idx >= 0) ? Io<IoT>::load1(static_cast<const IoT*>(a.x_prev) + ch * (K - 1) + idx)
+                                     : 0.0f;
+    }
+  }
+}
 
 // The causal depthwise conv of one token: acc = bias, then one FMA per tap
 // from the oldest input (xs[4 - K]) to the current one (xs[3]); taps a
@@ -547,10 +641,14 @@ struct Line {
 
 // Scan [l0, l1) of one lane's channel row in line tiles (l0 line-aligned,
 // l1 - l0 a multiple of kChunk): h advances; with kEmit, y is written.
-template <typename IoT, int N, bool kEmit, bool kZ, bool kSoftplus, bool kZoh>
+// kConv: ur holds the conv input x; each line is turned into u in place
+// (rounded to IoT, and stored to uo when given) from its inputs and the three
+// before it, xh[0..2] (oldest first), which then advance to the line's last three.
+template <typename IoT, int N, bool kEmit, bool kZ, bool kSoftplus, bool kZoh, bool kConv = false>
 __device__ __forceinline__ void scan_lines(const IoT* ur, const IoT* dr, const IoT* zr, IoT* yr, bool active,
                                            const IoT* Bb, const IoT* Cb, uint32_t row_bytes, int64_t l0,
-                                           int64_t l1, const Channel<N>& c, float h[N], float* dsum) {
+                                           int64_t l1, const Channel<N>& c, float h[N], float* dsum,
+                                           const ConvChan* cc = nullptr, float* xh = nullptr, IoT* uo = nullptr) {
   using LI = Line<IoT>;
   BCPipe<IoT, N, kEmit> bc;
   bc.Bb = Bb;
@@ -565,6 +663,28 @@ __device__ __forceinline__ void scan_lines(const IoT* ur, const IoT* dr, const I
     LI::load(ur + l, pieces, ru);
     LI::load(dr + l, pieces, rd);
     if constexpr (kZ) LI::load(zr + l, pieces, rz);
+    if constexpr (kConv) {
+      float x3 = xh[0], x2 = xh[1], x1 = xh[2];
+#pragma unroll
+      for (int t = 0; t < LI::kTokens; t += 2) {
+        const float xa = LI::elem(ru, t), xb = LI::elem(ru, t + 1);
+        float ua = conv_token(*cc, x3, x2, x1, xa);
+        float ub = conv_token(*cc, x2, x1, xa, xb);
+        if (cc->silu) {
+          ua = silu_f32(ua);
+          ub = silu_f32(ub);
+        }
+        x3 = x1; x2 = xa; x1 = xb;
+        if constexpr (sizeof(IoT) == 4) {
+          ru[t] = __float_as_uint(ua);
+          ru[t + 1] = __float_as_uint(ub);
+        } else {
+          ru[t / 2] = Io<bf16_t>::pack2(ua, ub);
+        }
+      }
+      xh[0] = x3; xh[1] = x2; xh[2] = x1;  // only the last (possibly partial) line leaves stale values
+      if (kEmit && uo && active) LI::store(uo + l, pieces, ru);
+    }
 #pragma unroll 1
     for (int pass = 0; pass < LI::kPasses; ++pass) {
 #pragma unroll
@@ -617,7 +737,7 @@ __device__ __forceinline__ void scan_lines(const IoT* ur, const IoT* dr, const I
 //         every chunk is a full vector chunk with B/C in SGPRs.  Otherwise
 //         (N = 16 then bounds a runtime dstate) every token goes through the
 //         scalar path.
-template <typename IoT, int N, bool kZ, bool kSoftplus, bool kVec, bool kZoh>
+template <typename IoT, int N, bool kZ, bool kSoftplus, bool kVec, bool kZoh, bool kConv>
 __global__ __launch_bounds__(kBlockThreads) void scan_kernel(ScanArgs a, int64_t total_waves) {
   const int64_t wave = wave_index();
   if (wave >= total_waves) return;
@@ -627,19 +747,32 @@ __global__ __launch_bounds__(kBlockThreads) void scan_kernel(ScanArgs a, int64_t
   const bool active = d_raw < a.dim;
   const int64_t d = active ? d_raw : a.dim - 1;  // idle lanes shadow a valid channel, write nothing
   const int64_t L = a.seqlen;
-  const int64_t bd = a.batch * a.dim;
   const int64_t ch = wc.b * a.dim + d;
   const int64_t l0 = wc.s * a.seg_len;
-  const int64_t l1 = min(l0 + a.seg_len, L);
+  const int64_t l1 = (wc.s == a.segments - 1) ? L : l0 + a.seg_len;
 
   Channel<N> c;
   load_channel<N>(a, d, c);
 
+  // The carry-in: h0 for the first segment, else the slots launch 2 left in
+  // this segment's range of y (read before this wave overwrites them).
   float h[N];
-  const float* cin = (a.segments > 1) ? a.carry + (wc.s * bd + ch) * a.dstate
-                                      : (a.h0 ? a.h0 + ch * a.dstate : nullptr);
+  const float* cin = a.h0 ? a.h0 + ch * a.dstate : nullptr;
 #pragma unroll
-  for (int n = 0; n < N; ++n) h[n] = (cin && n < a.dstate) ? cin[n] : 0.0f;
+  for (int n = 0; n < N; ++n) {
+    if (a.segments > 1 && wc.s > 0)
+      h[n] = (n < a.dstate) ? seg_slot_load<IoT>(a.y, ch * L + l0, 1 + n) : 0.0f;
+    else
+      h[n] = (cin && n < a.dstate) ? cin[n] : 0.0f;
+  }
+  ConvChan cc;
+  float xh[3] = {0.0f, 0.0f, 0.0f};
+  IoT* uo = nullptr;
+  if constexpr (kConv) {
+    cc = conv_chan(a.conv_w, a.conv_b, a.conv_width, a.conv_silu, d);
+    conv_history<IoT>(a, ch, l0, xh);
+    if (a.u_out) uo = static_cast<IoT*>(a.u_out) + ch * L;
+  }
 
   const IoT* ur = static_cast<const IoT*>(a.u) + ch * L;
   const IoT* dr = static_cast<const IoT*>(a.delta) + ch * L;
@@ -651,10 +784,17 @@ __global__ __launch_bounds__(kBlockThreads) void scan_kernel(ScanArgs a, int64_t
 
   int64_t l = l0;
   if constexpr (kVec) {
-    scan_lines<IoT, N, true, kZ, kSoftplus, kZoh>(ur, dr, zr, yr, active, Bb, Cb, row_bytes, l, l1, c, h, nullptr);
+    scan_lines<IoT, N, true, kZ, kSoftplus, kZoh, kConv>(ur, dr, zr, yr, active, Bb, Cb, row_bytes, l, l1, c, h,
+                                                         nullptr, &cc, xh, uo);
   } else {
     for (; l < l1; ++l) {
       float uv = Io<IoT>::load1(ur + l);
+      if constexpr (kConv) {
+        const float x0 = uv;
+        uv = round_io<IoT>(conv_silu(cc, conv_token(cc, xh[0], xh[1], xh[2], x0)));
+        xh[0] = xh[1]; xh[1] = xh[2]; xh[2] = x0;
+        if (uo && active) Io<IoT>::store1(uo + l, uv);
+      }
       float dl = discretize_delta<kSoftplus>(Io<IoT>::load1(dr + l), c.bias);
       float acc = token_states<IoT, N, true, kZoh>(Bb + l, Cb + l, L, a.dstate, c, dl, uv, h);
       float v = epilogue<kZ>(acc, c.Dd, uv, kZ ? Io<IoT>::load1(zr + l) : 0.0f);
@@ -2067,7 +2207,7 @@ __global__ __launch_bounds__(kBlockThreads) void conv_bwd_reduce_kernel(ConvBwdA
 
 // Launch 1: every segment but the last scans from a zero state and records
 // (sum of Delta, end state).  The segment's decay is a = exp(A * sum Delta).
-template <typename IoT, int N, bool kSoftplus, bool kVec, bool kZoh>
+template <typename IoT, int N, bool kSoftplus, bool kVec, bool kZoh, bool kConv>
 __global__ __launch_bounds__(kBlockThreads) void aggregate_kernel(ScanArgs a, int64_t total_waves) {
   const int64_t wave = wave_index();
   if (wave >= total_waves) return;
@@ -2077,10 +2217,9 @@ __global__ __launch_bounds__(kBlockThreads) void aggregate_kernel(ScanArgs a, in
   const bool active = d_raw < a.dim;
   const int64_t d = active ? d_raw : a.dim - 1;
   const int64_t L = a.seqlen;
-  const int64_t bd = a.batch * a.dim;
   const int64_t ch = wc.b * a.dim + d;
   const int64_t l0 = wc.s * a.seg_len;
-  const int64_t l1 = min(l0 + a.seg_len, L);
+  const int64_t l1 = l0 + a.seg_len;  // never the last segment
 
   Channel<N> c;
   load_channel<N>(a, d, c);
@@ -2088,6 +2227,12 @@ __global__ __launch_bounds__(kBlockThreads) void aggregate_kernel(ScanArgs a, in
 #pragma unroll
   for (int n = 0; n < N; ++n) h[n] = 0.0f;
   float dsum = 0.0f;
+  ConvChan cc;
+  float xh[3] = {0.0f, 0.0f, 0.0f};
+  if constexpr (kConv) {
+    cc = conv_chan(a.conv_w, a.conv_b, a.conv_width, a.conv_silu, d);
+    conv_history<IoT>(a, ch, l0, xh);
+  }
 
   const IoT* ur = static_cast<const IoT*>(a.u) + ch * L;
   const IoT* dr = static_cast<const IoT*>(a.delta) + ch * L;
@@ -2096,35 +2241,46 @@ __global__ __launch_bounds__(kBlockThreads) void aggregate_kernel(ScanArgs a, in
 
   int64_t l = l0;
   if constexpr (kVec) {
-    scan_lines<IoT, N, false, false, kSoftplus, kZoh>(ur, dr, nullptr, nullptr, active, Bb, nullptr, row_bytes, l, l1,
-                                                      c, h, &dsum);
+    scan_lines<IoT, N, false, false, kSoftplus, kZoh, kConv>(ur, dr, nullptr, nullptr, active, Bb, nullptr, row_bytes,
+                                                             l, l1, c, h, &dsum, &cc, xh, nullptr);
   } else {
     for (; l < l1; ++l) {
       float uv = Io<IoT>::load1(ur + l);
+      if constexpr (kConv) {
+        const float x0 = uv;
+        uv = round_io<IoT>(conv_silu(cc, conv_token(cc, xh[0], xh[1], xh[2], x0)));
+        xh[0] = xh[1]; xh[1] = xh[2]; xh[2] = x0;
+      }
       float dl = discretize_delta<kSoftplus>(Io<IoT>::load1(dr + l), c.bias);
       dsum += dl;
       token_states<IoT, N, false, kZoh>(Bb + l, nullptr, L, a.dstate, c, dl, uv, h);
     }
   }
 
+  // The aggregate into this segment's range of y (see seg_slot_store).
   if (active) {
-    a.agg_sum[wc.s * bd + ch] = dsum;
+    seg_slot_store<IoT>(a.y, ch * L + l0, 0, dsum);
 #pragma unroll
     for (int n = 0; n < N; ++n)
-      if (n < a.dstate) a.agg_h[(wc.s * bd + ch) * a.dstate + n] = h[n];
+      if (n < a.dstate) seg_slot_store<IoT>(a.y, ch * L + l0, 1 + n, h[n]);
   }
 }
 
 // Launch 2: one thread per (channel, state) folds the segment aggregates in
-// sequence order: carry[0] = h0, carry[s+1] = a_s * carry[s] + b_s.
+// sequence order, carry[0] = h0, carry[s+1] = a_s * carry[s] + b_s with
+// a_s = exp(A * sum Delta_s), in place in y: segment s's slot 1 + n is read as
+// b_s before this thread overwrites it with carry[s] (slot 0, the sum, is
+// shared by the channel's threads and only read).
+template <typename IoT>
 __global__ __launch_bounds__(kBlockThreads) void carry_kernel(ScanArgs a) {
   const int64_t bd = a.batch * a.dim;
   const int64_t idx = (int64_t)blockIdx.x * kBlockThreads + threadIdx.x;
   if (idx >= bd * a.dstate) return;
   const int64_t ch = idx / a.dstate;
-  const int64_t n = idx % a.dstate;
+  const int n = (int)(idx % a.dstate);
   const int64_t d = ch % a.dim;
   const float A2 = a.A[d * a.dstate + n] * kLog2e;
+  const int64_t row = ch * a.seqlen;
   float h = a.h0 ? a.h0[idx] : 0.0f;
   const int64_t P = a.segments;
   int64_t s = 0;
@@ -2133,20 +2289,22 @@ __global__ __launch_bounds__(kBlockThreads) void carry_kernel(ScanArgs a) {
     float sums[8], hs[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      sums[j] = a.agg_sum[(s + j) * bd + ch];
-      hs[j] = a.agg_h[(s + j) * bd * a.dstate + idx];
+      sums[j] = seg_slot_load<IoT>(a.y, row + (s + j) * a.seg_len, 0);
+      hs[j] = seg_slot_load<IoT>(a.y, row + (s + j) * a.seg_len, 1 + n);
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      a.carry[(s + j) * bd * a.dstate + idx] = h;
+      seg_slot_store<IoT>(a.y, row + (s + j) * a.seg_len, 1 + n, h);
       h = __builtin_fmaf(exp2_hw(A2 * sums[j]), h, hs[j]);
     }
   }
   for (; s < P - 1; ++s) {
-    a.carry[s * bd * a.dstate + idx] = h;
-    h = __builtin_fmaf(exp2_hw(A2 * a.agg_sum[s * bd + ch]), h, a.agg_h[s * bd * a.dstate + idx]);
+    const float sum = seg_slot_load<IoT>(a.y, row + s * a.seg_len, 0);
+    const float hb = seg_slot_load<IoT>(a.y, row + s * a.seg_len, 1 + n);
+    seg_slot_store<IoT>(a.y, row + s * a.seg_len, 1 + n, h);
+    h = __builtin_fmaf(exp2_hw(A2 * sum), h, hb);
   }
-  a.carry[(P - 1) * bd * a.dstate + idx] = h;
+  seg_slot_store<IoT>(a.y, row + (P - 1) * a.seg_len, 1 + n, h);
 }
 
 // ----------------------------------------------------------------------------
@@ -2450,7 +2608,7 @@ ssm_status_t shape_of(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen
 
 struct Plan {
   int64_t groups, segments, seg_len;
-  int64_t scratch_bytes;
+  int64_t scratch_bytes;  // always 0: no path takes device memory beyond its inputs and outputs
   bool split;  // single-pass state-split kernel
 };
 
@@ -2487,24 +2645,30 @@ Plan make_plan(const Shape& s, int64_t batch, int64_t dim, int64_t dstate, int64
   int64_t seg = (seqlen + want - 1) / want;
   seg = ((seg + kSegAlign - 1) / kSegAlign) * kSegAlign;
   seg = std::max(seg, kMinSegment);
+  p.scratch_bytes = 0;  // the segment aggregates and carries live in y (seg_slot_store)
   if (seg >= seqlen) {
     p.segments = 1;
     p.seg_len = seqlen;
   } else {
+    // The last segment ends at seqlen; a remainder shorter than kSegAlign
+    // tokens joins the segment before it, so every segment's range of y
+    // holds its N + 1 slots.
     p.segments = (seqlen + seg - 1) / seg;
+    if (seqlen - (p.segments - 1) * seg < kSegAlign) p.segments -= 1;
     p.seg_len = seg;
-  }
-  if (p.segments > 1) {
-    int64_t P = p.segments;
-    p.scratch_bytes = 4 * ((P - 1) * s.bd + (P - 1) * s.bdn + P * s.bdn);
-  } else {
-    p.scratch_bytes = 0;
+    if (p.segments < 2) {
+      p.segments = 1;
+      p.seg_len = seqlen;
+    }
   }
   return p;
 }
 
-// Per-device pool for the scratch memory of segmented scans (stream ordered,
-// kept warm between calls).
+// Per-device stream-ordered pool for the scratch of the backward entry points
+// (checkpoints and partial sums).  Its release threshold is 0: blocks freed on
+// a stream are reused by later calls on that stream, and whatever is not in
+// use goes back to the device at the next synchronisation, so the library
+// holds no device memory between call sequences.
 struct PoolCache {
   std::mutex mu;
   hipMemPool_t pools[64] = {};
@@ -2531,7 +2695,7 @@ hipError_t get_pool(hipMemPool_t* out) {
     hipMemPool_t pool;
     e = hipMemPoolCreate(&pool, &props);
     if (e != hipSuccess) return e;
-    uint64_t keep = UINT64_MAX;
+    uint64_t keep = 0;
     e = hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep);
     if (e != hipSuccess) return e;
     c.pools[dev] = pool;
@@ -2540,40 +2704,44 @@ hipError_t get_pool(hipMemPool_t* out) {
   return hipSuccess;
 }
 
-template <typename IoT, int N, bool kZ, bool kSp, bool kVec, bool kZoh>
+template <typename IoT, int N, bool kZ, bool kSp, bool kVec, bool kZoh, bool kConv>
 hipError_t launch_scan_t(const ScanArgs& a, const Plan& p, hipStream_t st) {
   int64_t waves_scan = a.batch * p.groups * p.segments;
   if (p.segments > 1) {
     int64_t waves_agg = a.batch * p.groups * (p.segments - 1);
     int64_t blocks = (waves_agg + kWavesPerBlock - 1) / kWavesPerBlock;
-    hipLaunchKernelGGL((aggregate_kernel<IoT, N, kSp, kVec, kZoh>), dim3((unsigned)blocks), dim3(kBlockThreads), 0, st,
-                       a, waves_agg);
+    hipLaunchKernelGGL((aggregate_kernel<IoT, N, kSp, kVec, kZoh, kConv>), dim3((unsigned)blocks), dim3(kBlockThreads),
+                       0, st, a, waves_agg);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     int64_t threads = a.batch * a.dim * a.dstate;
-    hipLaunchKernelGGL(carry_kernel, dim3((unsigned)((threads + kBlockThreads - 1) / kBlockThreads)),
+    hipLaunchKernelGGL((carry_kernel<IoT>), dim3((unsigned)((threads + kBlockThreads - 1) / kBlockThreads)),
                        dim3(kBlockThreads), 0, st, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   int64_t blocks = (waves_scan + kWavesPerBlock - 1) / kWavesPerBlock;
-  hipLaunchKernelGGL((scan_kernel<IoT, N, kZ, kSp, kVec, kZoh>), dim3((unsigned)blocks), dim3(kBlockThreads), 0, st, a,
-                     waves_scan);
+  hipLaunchKernelGGL((scan_kernel<IoT, N, kZ, kSp, kVec, kZoh, kConv>), dim3((unsigned)blocks), dim3(kBlockThreads), 0,
+                     st, a, waves_scan);
   return hipGetLastError();
 }
 
-template <typename IoT, int N, bool kVec, bool kZoh>
+template <typename IoT, int N, bool kVec, bool kZoh, bool kConv>
 hipError_t launch_scan_z(const ScanArgs& a, const Plan& p, hipStream_t st, bool sp) {
   if (a.z)
-    return sp ? launch_scan_t<IoT, N, true, true, kVec, kZoh>(a, p, st)
-              : launch_scan_t<IoT, N, true, false, kVec, kZoh>(a, p, st);
-  return sp ? launch_scan_t<IoT, N, false, true, kVec, kZoh>(a, p, st)
-            : launch_scan_t<IoT, N, false, false, kVec, kZoh>(a, p, st);
+    return sp ? launch_scan_t<IoT, N, true, true, kVec, kZoh, kConv>(a, p, st)
+              : launch_scan_t<IoT, N, true, false, kVec, kZoh, kConv>(a, p, st);
+  return sp ? launch_scan_t<IoT, N, false, true, kVec, kZoh, kConv>(a, p, st)
+            : launch_scan_t<IoT, N, false, false, kVec, kZoh, kConv>(a, p, st);
 }
 
+// The fused conv runs with the Delta * B rule only (its entry point has no
+// discretization argument).
 template <typename IoT, int N, bool kVec>
-hipError_t launch_scan_f(const ScanArgs& a, const Plan& p, hipStream_t st, bool sp) {
-  return a.zoh ? launch_scan_z<IoT, N, kVec, true>(a, p, st, sp) : launch_scan_z<IoT, N, kVec, false>(a, p, st, sp);
+hipError_t launch_scan_f(const ScanArgs& a, const Plan& p, hipStream_t st, bool sp, bool conv) {
+  if (conv) return launch_scan_z<IoT, N, kVec, false, true>(a, p, st, sp);
+  return a.zoh ? launch_scan_z<IoT, N, kVec, true, false>(a, p, st, sp)
+               : launch_scan_z<IoT, N, kVec, false, false>(a, p, st, sp);
 }
 
 template <typename IoT, int N, int S, bool kZ, bool kSp, bool kConv, bool kZoh, bool kCplx = false>
@@ -2612,38 +2780,6 @@ hipError_t launch_split_c(const ScanArgs& a, const Plan& p, hipStream_t st, bool
   return a.zoh ? launch_split<IoT, N, false, true>(a, p, st, sp) : launch_split<IoT, N, false, false>(a, p, st, sp);
 }
 
-// The causal depthwise conv as a kernel of its own (shapes the single-pass
-// kernel does not take): one thread per output element, u rounded to IoT.
-template <typename IoT>
-__global__ __launch_bounds__(kBlockThreads) void conv1d_kernel(ScanArgs a, IoT* u) {
-  const int64_t i = (int64_t)blockIdx.x * kBlockThreads + threadIdx.x;
-  const int64_t L = a.seqlen;
-  if (i >= a.batch * a.dim * L) return;
-  const int64_t ch = i / L, l = i % L, d = ch % a.dim;
-  const int K = a.conv_width;
-  const IoT* x = static_cast<const IoT*>(a.u) + ch * L;
-  const IoT* xp = static_cast<const IoT*>(a.x_prev);
-  float w[4], xs[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) w[k] = k < K ? a.conv_w[d * K + k] : 0.0f;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {  // xs[j] = input at position l - 3 + j
-    const int64_t pos = l - 3 + j;
-    const int64_t slot = (K - 1) + pos;  // x_prev slot of a negative position
-    xs[j] = pos >= 0 ? Io<IoT>::load1(x + pos) : ((xp && slot >= 0) ? Io<IoT>::load1(xp + ch * (K - 1) + slot) : 0.0f);
-  }
-  const float cb = a.conv_b ? a.conv_b[d] : 0.0f;
-  float acc;
-  switch (K) {
-    case 1: acc = conv_taps<1>(xs, w, cb); break;
-    case 2: acc = conv_taps<2>(xs, w, cb); break;
-    case 3: acc = conv_taps<3>(xs, w, cb); break;
-    default: acc = conv_taps<4>(xs, w, cb); break;
-  }
-  if (a.conv_silu) acc = silu_f32(acc);
-  Io<IoT>::store1(u + i, acc);
-}
-
 template <typename IoT, int T, bool kSilu>
 hipError_t launch_conv_bwd_t(const ConvBwdArgs& a, int K, bool vec, hipStream_t st) {
   const dim3 grid((unsigned)(a.batch * a.dim * a.chunks)), block(kBlockThreads);
@@ -2676,13 +2812,6 @@ hipError_t launch_conv_bwd(const ConvBwdArgs& a, int K, bool vec, int T, hipStre
   return a.silu ? launch_conv_bwd_t<IoT, 8, true>(a, K, vec, st) : launch_conv_bwd_t<IoT, 8, false>(a, K, vec, st);
 }
 
-template <typename IoT>
-hipError_t launch_conv(const ScanArgs& a, void* u, hipStream_t st) {
-  const int64_t total = a.batch * a.dim * a.seqlen;
-  const int64_t blocks = (total + kBlockThreads - 1) / kBlockThreads;
-  hipLaunchKernelGGL((conv1d_kernel<IoT>), dim3((unsigned)blocks), dim3(kBlockThreads), 0, st, a, static_cast<IoT*>(u));
-  return hipGetLastError();
-}
 
 template <typename IoT, int N, bool kZ, bool kSp, bool kZoh>
 hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
@@ -2738,11 +2867,11 @@ hipError_t launch_scan(const ScanArgs& a, const Plan& p, hipStream_t st, bool ve
     return launch_split_c<IoT, 16>(a, p, st, sp, conv);
   }
   if (vec) {
-    if (a.dstate == 4) return launch_scan_f<IoT, 4, true>(a, p, st, sp);
-    if (a.dstate == 8) return launch_scan_f<IoT, 8, true>(a, p, st, sp);
-    if (a.dstate == 16) return launch_scan_f<IoT, 16, true>(a, p, st, sp);
+    if (a.dstate == 4) return launch_scan_f<IoT, 4, true>(a, p, st, sp, conv);
+    if (a.dstate == 8) return launch_scan_f<IoT, 8, true>(a, p, st, sp, conv);
+    if (a.dstate == 16) return launch_scan_f<IoT, 16, true>(a, p, st, sp, conv);
   }
-  return launch_scan_f<IoT, 16, false>(a, p, st, sp);
+  return launch_scan_f<IoT, 16, false>(a, p, st, sp, conv);
 }
 
 template <typename IoT, int N, bool kZ, bool kSp, bool kZoh>
@@ -2885,7 +3014,7 @@ ScanArgs scan_args(const Shape&, int64_t batch, int64_t dim, int64_t dstate, int
   (void)io;
   ScanArgs a;
   a.u = u; a.delta = delta; a.A = A; a.B = B; a.C = C; a.D = D; a.z = z; a.bias = delta_bias; a.h0 = h0;
-  a.y = y; a.last_state = last_state; a.agg_sum = nullptr; a.agg_h = nullptr; a.carry = nullptr;
+  a.y = y; a.last_state = last_state;
   a.batch = batch; a.dim = dim; a.dstate = dstate; a.seqlen = seqlen;
   a.groups = 0; a.segments = 0; a.seg_len = 0;
   a.conv_w = nullptr; a.conv_b = nullptr; a.x_prev = nullptr; a.u_out = nullptr; a.conv_width = 1; a.conv_silu = 0;
@@ -2894,32 +3023,14 @@ ScanArgs scan_args(const Shape&, int64_t batch, int64_t dim, int64_t dstate, int
   return a;
 }
 
-// Plans and launches the scan of a validated call, with the segment scratch
-// (if the plan needs it) taken from the pool and released on the stream.
-// conv: the conv is fused (a.u holds x); only the single-pass vector path
-// takes it, which the caller has checked.
+// Plans and launches the scan of a validated call.  Nothing is allocated:
+// the segmented path keeps its aggregates and carries in y (seg_slot_store).
+// conv: the conv is fused (a.u holds x).
 ssm_status_t run_scan(ScanArgs& a, const Shape& sh, ssm_dtype_t io, bool vec, bool sp, bool conv, hipStream_t hs) {
   const Plan plan = make_plan(sh, a.batch, a.dim, a.dstate, a.seqlen, io);
   a.groups = plan.groups; a.segments = plan.segments; a.seg_len = plan.seg_len;
-  void* scratch = nullptr;
-  if (plan.scratch_bytes > 0) {
-    hipMemPool_t pool;
-    hipError_t e = get_pool(&pool);
-    if (e != hipSuccess) return hip_fail(e);
-    e = hipMallocFromPoolAsync(&scratch, (size_t)plan.scratch_bytes, pool, hs);
-    if (e != hipSuccess) return hip_fail(e);
-    float* f = static_cast<float*>(scratch);
-    const int64_t P = plan.segments;
-    a.agg_sum = f;
-    a.agg_h = f + (P - 1) * sh.bd;
-    a.carry = a.agg_h + (P - 1) * sh.bdn;
-  }
   hipError_t e = (io == SSM_BF16) ? launch_scan<bf16_t>(a, plan, hs, vec, sp, conv)
                                   : launch_scan<float>(a, plan, hs, vec, sp, conv);
-  if (scratch) {
-    hipError_t ef = hipFreeAsync(scratch, hs);
-    if (e == hipSuccess) e = ef;
-  }
   if (e != hipSuccess) return hip_fail(e);
   return SSM_OK;
 }
@@ -3044,37 +3155,11 @@ ssm_status_t ssm_conv_scan_fwd(int64_t batch, int64_t dim, int64_t dstate, int64
   ScanArgs a = scan_args(sh, batch, dim, dstate, seqlen, io, x, delta, A, B, C, D, z, delta_bias, h0, y, last_state);
   a.conv_w = conv_weight; a.conv_b = conv_bias; a.x_prev = x_prev; a.u_out = u_out;
   a.conv_width = (int)conv_width; a.conv_silu = conv_silu != 0;
-  const Plan plan = make_plan(sh, batch, dim, dstate, seqlen, io);
-  const bool sp = softplus_flag != 0;
-  // Fused: the single-pass kernel computes u in its prologue.  Its u_out
-  // stores are whole 16- or 32-byte pieces, so they need 16-byte rows too.
-  if (plan.split && vec_rows(sh, dstate, seqlen, io, x, delta, B, C, z, y) && (!u_out || aligned(u_out, 16)))
-    return run_scan(a, sh, io, true, sp, true, hs);
-
-  // Otherwise the conv writes u (to u_out, else to pool scratch) and the
-  // plain scan reads it.
-  void* ubuf = u_out;
-  if (!ubuf) {
-    hipMemPool_t pool;
-    hipError_t e = get_pool(&pool);
-    if (e != hipSuccess) return hip_fail(e);
-    e = hipMallocFromPoolAsync(&ubuf, (size_t)(sh.bdl * (int64_t)es), pool, hs);
-    if (e != hipSuccess) return hip_fail(e);
-  }
-  hipError_t e = (io == SSM_BF16) ? launch_conv<bf16_t>(a, ubuf, hs) : launch_conv<float>(a, ubuf, hs);
-  ssm_status_t out = SSM_OK;
-  if (e != hipSuccess) {
-    out = hip_fail(e);
-  } else {
-    a.u = ubuf;
-    a.conv_w = nullptr; a.conv_b = nullptr; a.x_prev = nullptr; a.u_out = nullptr;
-    out = run_scan(a, sh, io, vec_rows(sh, dstate, seqlen, io, ubuf, delta, B, C, z, y), sp, false, hs);
-  }
-  if (!u_out) {
-    hipError_t ef = hipFreeAsync(ubuf, hs);
-    if (out == SSM_OK && ef != hipSuccess) out = hip_fail(ef);
-  }
-  return out;
+  // Every path computes u from x in its own prologue (no u round trip through
+  // memory).  The vector paths store u_out as whole 16-byte pieces, so it
+  // needs 16-byte rows like the other row arrays.
+  const bool vec = vec_rows(sh, dstate, seqlen, io, x, delta, B, C, z, y) && (!u_out || aligned(u_out, 16));
+  return run_scan(a, sh, io, vec, softplus_flag != 0, true, hs);
 }
 
 // The backward, with the checkpoints either saved by ssm_scan_fwd_save

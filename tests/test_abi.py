@@ -360,7 +360,12 @@ def test_plan(lib):
     assert (path, seg, seglen, scratch) == ("split", 1, 4096, 0)          # Mamba-1.4B layer: single pass
     assert binding.scan_plan(8, 1536, 16, 2048, torch.float32, with_path=True) == ("split", 1, 2048, 0)
     path, seg, seglen, scratch = binding.scan_plan(1, 2560, 16, 131072, torch.float32, with_path=True)
-    assert path == "segmented" and seg > 1 and (seg - 1) * seglen < 131072 <= seg * seglen and scratch > 0
+    # No path takes scratch: the segment aggregates and carries live in y.  The
+    # last segment ends at seqlen and holds at least 64 tokens.
+    assert path == "segmented" and seg > 1 and scratch == 0
+    assert (seg - 1) * seglen < 131072 and 131072 - (seg - 1) * seglen >= 64
+    path, seg, seglen, scratch = binding.scan_plan(1, 64, 16, 4097, torch.float32, with_path=True)
+    assert path == "generic" and seg == 16 and seglen == 256 and scratch == 0   # a 1-token remainder joins segment 15
     assert seglen % 64 == 0
     assert binding.scan_plan(1, 16, 4, 64, torch.float32, with_path=True) == ("segmented", 1, 64, 0)
     assert binding.scan_plan(1, 16, 4, 63, torch.float32, with_path=True)[0] == "generic"

@@ -94,15 +94,19 @@ def test_fused_path(io, shape):
             check(np64(last), hr, TOL["f32"], "last_state K=%d" % width)
 
 
-UNFUSED_SHAPES = [(1, 16, 4, 64), (2, 63, 16, 63), (1, 3, 16, 7), (1, 64, 16, 4097)]
+# Shapes off the single-pass kernel: the conv is fused into the segmented
+# and per-token kernels too (history carried across lines and segments).
+OTHER_SHAPES = [(1, 16, 4, 64), (2, 63, 16, 63), (1, 3, 16, 7), (1, 64, 16, 4097), (1, 64, 16, 4096),
+                (2, 100, 8, 1536)]
 
 
 @pytest.mark.parametrize("io", ["f32", "bf16"])
-@pytest.mark.parametrize("shape", UNFUSED_SHAPES, ids=["%dx%dx%dx%d" % s for s in UNFUSED_SHAPES])
-def test_unfused_paths(io, shape):
+@pytest.mark.parametrize("shape", OTHER_SHAPES, ids=["%dx%dx%dx%d" % s for s in OTHER_SHAPES])
+def test_other_paths(io, shape):
     b, d, n, l = shape
     for width in (2, 4):
-        say("conv unfused shape=%s io=%s K=%d" % (shape, io, width))
+        say("conv other path shape=%s io=%s K=%d plan=%s" % (shape, io, width, binding.scan_plan(
+            b, d, n, l, torch.float32 if io == "f32" else torch.bfloat16, with_path=True)))
         x, w, cb, prev = conv_inputs(b, d, n, l, io, width, 600 + width, h0=True)
         for u_out in (True, False):
             y, last, uo, _ = run(x, w, cb, prev, True, u_out=u_out)
@@ -116,8 +120,9 @@ def test_unfused_paths(io, shape):
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 def test_fused_equals_conv_then_scan(io):
     """The fused kernel's y is bitwise the plain scan of the u it reports, and
-    that u is bitwise the standalone conv kernel's (a misaligned u_out forces
-    it; the scan then takes the generic path, so y is held to the usual bar)."""
+    that u is bitwise the per-token kernel's conv (a misaligned u_out sends the
+    call there; its scan then differs in summation order, so y is held to the
+    usual bar)."""
     b, d, n, l = 192, 64, 16, 96
     x, w, cb, prev = conv_inputs(b, d, n, l, io, 4, 700, h0=True)
     say("conv fused vs conv+scan io=%s" % io)
@@ -132,8 +137,8 @@ def test_fused_equals_conv_then_scan(io):
     assert uo_mis.data_ptr() % 16 == es
     y3, last3, _, _ = run(x, w, cb, prev, True, uo=uo_mis)
     assert torch.equal(uo_mis, uo)
-    check(np64(y3), np64(y), TOL[io], "y via conv kernel + generic scan")
-    check(np64(last3), np64(last), TOL["f32"], "last_state via conv kernel + generic scan")
+    check(np64(y3), np64(y), TOL[io], "y via the per-token kernel")
+    check(np64(last3), np64(last), TOL["f32"], "last_state via the per-token kernel")
 
 
 @pytest.mark.parametrize("io", ["f32", "bf16"])

@@ -89,3 +89,46 @@ def test_split_prefill_in_a_graph(io):
         torch.cuda.synchronize()
         assert torch.equal(y, y_ref) and torch.equal(last, h_ref), "replay %d" % i
         _ = float(np.float64(y.float().abs().sum().item()))  # eager work between replays
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("conv", [False, True])
+def test_segmented_prefill_in_a_graph(io, conv):
+    """The segmented path (three launches, aggregates and carries in y) and the
+    conv fused into it allocate nothing, so a capture holds only launches."""
+    b, d, n, l = 1, 128, 16, 4096
+    dt = torch.float32 if io == "f32" else torch.bfloat16
+    assert binding.scan_plan(b, d, n, l, dt, with_path=True)[1] > 1
+    x = inputs.make_scan_inputs(b, d, n, l, io=io, seed=78, h0=True)
+    t = inputs.to_torch(x, DEV)
+    w = torch.from_numpy((0.5 * np.random.default_rng(79).standard_normal((d, 4))).astype(np.float32)).to(DEV)
+    kw = dict(D=t["D"], z=t["z"], delta_bias=t["delta_bias"], delta_softplus=True, h0=t["h0"])
+
+    def call(out, last):
+        if conv:
+            return binding.conv_scan_fwd(t["u"], w, t["delta"], t["A"], t["B"], t["C"], conv_silu=True, out=out,
+                                         last_state=last, **kw)
+        return binding.scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], out=out, last_state=last, **kw)
+
+    y_ref, h_ref = call(None, None)
+    torch.cuda.synchronize()
+    y = torch.empty_like(y_ref)
+    last = torch.empty_like(h_ref)
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        call(torch.empty_like(y), torch.empty_like(last))
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        call(y, last)
+    for i in range(3):
+        say("segmented prefill graph replay %d io=%s conv=%s" % (i, io, conv))
+        y.fill_(7.0)
+        last.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_ref) and torch.equal(last, h_ref), "replay %d" % i
+        _ = float(np.float64(y.float().abs().sum().item()))  # eager work between replays

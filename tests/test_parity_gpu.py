@@ -235,9 +235,10 @@ def test_odd_shapes(io, shape):
 
 
 def test_segmented_plan_is_exercised():
-    # The long-sequence workload must take the segmented (multi-launch) path.
+    # The long-sequence workload takes the segmented (multi-launch) path, which
+    # allocates nothing: its aggregates and carries live in y.
     seg, seglen, scratch = binding.scan_plan(1, 2560, 16, 131072, torch.float32)
-    assert seg > 1 and scratch > 0
+    assert seg > 1 and scratch == 0
 
 
 @pytest.mark.parametrize("io", ["f32", "bf16"])
@@ -303,6 +304,33 @@ def test_run_to_run_bitwise():
     y1, h1 = gpu_scan(x)
     y2, h2 = gpu_scan(x)
     assert torch.equal(y1, y2) and torch.equal(h1, h2)
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_misaligned_rows_segmented(io):
+    """Rows one element off 16-byte alignment on a segmented shape: the generic
+    kernel, with the segment slots in a y that is only element-aligned."""
+    b, d, n, l = 1, 70, 16, 2000
+    x = inputs.make_scan_inputs(b, d, n, l, io=io, seed=42, h0=True)
+    assert binding.scan_plan(b, d, n, l, torch.float32 if io == "f32" else torch.bfloat16)[0] > 1
+    t = inputs.to_torch(x, DEV)
+    say("misaligned segmented io=%s" % io)
+
+    def shifted(a):
+        flat = torch.empty(a.numel() + 1, dtype=a.dtype, device=DEV)
+        v = flat[1:].view(a.shape)
+        v.copy_(a)
+        return v
+
+    ybuf = torch.empty(b * d * l + 1, dtype=t["u"].dtype, device=DEV)
+    y = ybuf[1:].view(b, d, l)
+    _, last = binding.scan_fwd(shifted(t["u"]), shifted(t["delta"]), t["A"], shifted(t["B"]), shifted(t["C"]),
+                               D=t["D"], z=shifted(t["z"]), delta_bias=t["delta_bias"], delta_softplus=True,
+                               h0=t["h0"], out=y)
+    torch.cuda.synchronize()
+    yr, hr = oracle_full(x)
+    check(np64(y), yr, io, "y")
+    check(np64(last), hr, "f32", "last_state")
 
 
 def test_misaligned_rows_take_the_generic_path():
