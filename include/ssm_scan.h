@@ -78,7 +78,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 11
+#define SSM_ABI_VERSION 12
 
 struct ihipStream_t; /* the same incomplete type as HIP's hipStream_t */
 
@@ -96,7 +96,8 @@ typedef enum {
   SSM_ERR_ALIGN = 5,                /* a pointer is not element-aligned      */
   SSM_ERR_ALIAS = 6,                /* an output overlaps an input           */
   SSM_ERR_HIP = 7,                  /* a HIP runtime call failed             */
-  SSM_ERR_UNSUPPORTED = 8           /* valid, but outside what this entry point implements */
+  SSM_ERR_UNSUPPORTED = 8,          /* valid, but outside what this entry point implements */
+  SSM_ERR_WORKSPACE = 9             /* needs more scratch than the fixed device array holds */
 } ssm_status_t;
 
 /*
@@ -393,6 +394,32 @@ ssm_status_t ssm_scan_bwd_saved(int64_t batch, int64_t dim, int64_t dstate, int6
                                 const float* ckpt, const void* dy, const float* dlast, void* du, void* ddelta,
                                 float* dA, float* dB, float* dC, float* dD, void* dz, float* ddelta_bias, float* dh0,
                                 struct ihipStream_t* stream);
+
+/*
+ * ssm_scan_bwd_saved_noalloc -- ssm_scan_bwd_saved for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight training loops,
+ * harnesses that forbid allocation.  Same arguments, same kernels, bitwise
+ * the same gradients; it calls no allocating routine.  Its scratch (the
+ * per-group dB/dC partial sums and the per-batch-row partials of dA, dD and
+ * ddelta_bias: 4 * (2 * ceil(dim/64) * batch * dstate * seqlen
+ * + batch * dim * (dstate + 2)) bytes) comes from a fixed 64 MiB device
+ * array inside the library, one per device, held from the library's load
+ * until the process ends.  A call whose scratch is larger returns
+ * SSM_ERR_WORKSPACE before any HIP call (the Mamba-130M layer, batch 8 x
+ * dim 1536 x dstate 16 x seqlen 2048, takes 49 MiB; the Mamba-1.4B layer,
+ * batch 4 x 4096 x 16 x 4096, 129 MiB, does not fit).
+ *
+ * Every call on a device shares that device's array: calls that overlap on
+ * one device (different streams without ordering between them) race and
+ * must not be issued.  The first call on each device resolves the array's
+ * address (hipGetSymbolAddress); make it outside graph capture.
+ */
+ssm_status_t ssm_scan_bwd_saved_noalloc(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, ssm_dtype_t io,
+                                        const void* u, const void* delta, const float* A, const void* B,
+                                        const void* C, const float* D, const void* z, const float* delta_bias,
+                                        int softplus_flag, const float* ckpt, const void* dy, const float* dlast,
+                                        void* du, void* ddelta, float* dA, float* dB, float* dC, float* dD, void* dz,
+                                        float* ddelta_bias, float* dh0, struct ihipStream_t* stream);
 
 /*
  * ssm_scan_bwd_ex -- ssm_scan_bwd for either discretization of B (see

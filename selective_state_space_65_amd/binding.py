@@ -56,6 +56,8 @@ SIGNATURES = {
     "ssm_scan_fwd_save": (_I, [_I64, _I64, _I64, _I64, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P]),
     "ssm_scan_bwd_saved": (_I, [_I64, _I64, _I64, _I64, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P,
                                 _P, _P, _P, _P, _P, _P, _P]),
+    "ssm_scan_bwd_saved_noalloc": (_I, [_I64, _I64, _I64, _I64, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P,
+                                        _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "ssm_scan_fwd_plan": (_I, [_I64, _I64, _I64, _I64, _I, ctypes.POINTER(_I), ctypes.POINTER(_I64),
                               ctypes.POINTER(_I64), ctypes.POINTER(_I64)]),
     "ssm_status_string": (ctypes.c_char_p, [_I]),
@@ -479,6 +481,16 @@ def scan_bwd_saved(u, delta, A, B, C, dy, ckpt, D=None, z=None, delta_bias=None,
     return _scan_bwd(ckpt, u, delta, A, B, C, dy, D, z, delta_bias, delta_softplus, None, dlast, need, stream)
 
 
+def scan_bwd_saved_noalloc(u, delta, A, B, C, dy, ckpt, D=None, z=None, delta_bias=None, delta_softplus=False,
+                           dlast=None, need=("dD", "dz", "ddelta_bias", "dh0"), stream=None):
+    """scan_bwd_saved with its scratch in the library's fixed 64 MiB device array
+    (ssm_scan_bwd_saved_noalloc): no device allocation inside the call.  The
+    output tensors are still allocated here by torch unless the caller passes
+    the C ABI its own."""
+    return _scan_bwd(ckpt, u, delta, A, B, C, dy, D, z, delta_bias, delta_softplus, None, dlast, need, stream,
+                     noalloc=True)
+
+
 def ckpt_shape(batch, dim, dstate, seqlen):
     """Shape of the float32 checkpoint tensor of scan_fwd_save / scan_bwd_saved."""
     return ((seqlen + 15) // 16, batch, dstate, dim)
@@ -529,7 +541,8 @@ def scan_fwd_save(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_soft
     return out, last_state, ckpt
 
 
-def _scan_bwd(ckpt, u, delta, A, B, C, dy, D, z, delta_bias, delta_softplus, h0, dlast, need, stream, disc=None):
+def _scan_bwd(ckpt, u, delta, A, B, C, dy, D, z, delta_bias, delta_softplus, h0, dlast, need, stream, disc=None,
+              noalloc=False):
     import torch
     if u.dim() != 3:
         raise ValueError("u must be (batch, dim, seqlen)")
@@ -572,6 +585,8 @@ def _scan_bwd(ckpt, u, delta, A, B, C, dy, D, z, delta_bias, delta_softplus, h0,
         _check("ssm_scan_bwd_ex", lib.ssm_scan_bwd_ex(*head[:5], disc, *head[5:], _ptr(h0), *tail))
     elif ckpt is None:
         _check("ssm_scan_bwd", lib.ssm_scan_bwd(*head, _ptr(h0), *tail))
+    elif noalloc:
+        _check("ssm_scan_bwd_saved_noalloc", lib.ssm_scan_bwd_saved_noalloc(*head, _ptr(ckpt), *tail))
     else:
         _check("ssm_scan_bwd_saved", lib.ssm_scan_bwd_saved(*head, _ptr(ckpt), *tail))
     return g

@@ -2704,6 +2704,43 @@ hipError_t get_pool(hipMemPool_t* out) {
   return hipSuccess;
 }
 
+// The fixed device scratch of ssm_scan_bwd_saved_noalloc: 64 MiB on every
+// device the library runs on, held until the process ends.  In host code
+// this name is only a stand-in for the symbol: each device's copy lives at
+// its own address, resolved once per device with hipGetSymbolAddress (with
+// that device current) and kept in fixed_scratch_ptr's table.
+constexpr int64_t kFixedScratchFloats = (int64_t)16 << 20;
+static __device__ __align__(256) float scratch[kFixedScratchFloats];
+
+struct FixedScratch {
+  std::mutex mu;
+  float* ptr[64] = {};
+};
+
+FixedScratch& fixed_scratch() {
+  static FixedScratch f;
+  return f;
+}
+
+// The current device's copy of scratch.
+hipError_t fixed_scratch_ptr(float** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  FixedScratch& f = fixed_scratch();
+  std::lock_guard<std::mutex> lock(f.mu);
+  if (!f.ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    f.ptr[dev] = static_cast<float*>(p);
+  }
+  *out = f.ptr[dev];
+  return hipSuccess;
+}
+
 template <typename IoT, int N, bool kZ, bool kSp, bool kVec, bool kZoh, bool kConv>
 hipError_t launch_scan_t(const ScanArgs& a, const Plan& p, hipStream_t st) {
   int64_t waves_scan = a.batch * p.groups * p.segments;
@@ -3052,6 +3089,7 @@ const char* ssm_status_string(ssm_status_t s) {
     case SSM_ERR_ALIAS: return "an output buffer overlaps an input buffer";
     case SSM_ERR_HIP: return "a HIP runtime call failed (see ssm_last_hip_error)";
     case SSM_ERR_UNSUPPORTED: return "valid arguments outside what this entry point implements (see the header)";
+    case SSM_ERR_WORKSPACE: return "the call needs more scratch than the entry point's fixed device array holds";
   }
   return "unknown status";
 }
@@ -3169,7 +3207,8 @@ static ssm_status_t scan_bwd_impl(int64_t batch, int64_t dim, int64_t dstate, in
                                   const float* D, const void* z, const float* delta_bias, int softplus_flag,
                                   const float* h0, const float* saved, const void* dy, const float* dlast, void* du,
                                   void* ddelta, float* dA, float* dB, float* dC, float* dD, void* dz,
-                                  float* ddelta_bias, float* dh0, hipStream_t hs, bool zoh, bool cplx = false) {
+                                  float* ddelta_bias, float* dh0, hipStream_t hs, bool zoh, bool cplx = false,
+                                  bool fixed = false) {
   Shape sh;
   ssm_status_t st = shape_of(batch, dim, dstate, seqlen, io, &sh);
   if (st != SSM_OK) return st;
@@ -3218,13 +3257,24 @@ static ssm_status_t scan_bwd_impl(int64_t batch, int64_t dim, int64_t dstate, in
   const int64_t n_part = groups * sh.bnl;
   const int64_t n_small = sh.bdn + 2 * batch * dim;
   const int64_t scratch_floats = n_own + 2 * n_part + n_small;
-  hipMemPool_t pool;
-  hipError_t e = get_pool(&pool);
-  if (e != hipSuccess) return hip_fail(e);
-  void* scratch = nullptr;
-  e = hipMallocFromPoolAsync(&scratch, (size_t)scratch_floats * 4, pool, hs);
-  if (e != hipSuccess) return hip_fail(e);
-  float* f = static_cast<float*>(scratch);
+  // fixed: the library's fixed device array, nothing allocated; else the pool.
+  // Every float of it that the kernels read they have written first in the
+  // same call, so nothing needs clearing between calls.
+  float* f = nullptr;
+  void* work = nullptr;
+  hipError_t e = hipSuccess;
+  if (fixed) {
+    if (scratch_floats > kFixedScratchFloats) return SSM_ERR_WORKSPACE;
+    e = fixed_scratch_ptr(&f);
+    if (e != hipSuccess) return hip_fail(e);
+  } else {
+    hipMemPool_t pool;
+    e = get_pool(&pool);
+    if (e != hipSuccess) return hip_fail(e);
+    e = hipMallocFromPoolAsync(&work, (size_t)scratch_floats * 4, pool, hs);
+    if (e != hipSuccess) return hip_fail(e);
+    f = static_cast<float*>(work);
+  }
 
   const bool sp = softplus_flag != 0;
   // 1. Unless saved: the forward with checkpoints (single-pass kernel; y goes
@@ -3274,8 +3324,10 @@ static ssm_status_t scan_bwd_impl(int64_t batch, int64_t dim, int64_t dstate, in
                        dC, dA, dD, ddelta_bias);
     e = hipGetLastError();
   }
-  hipError_t ef = hipFreeAsync(scratch, hs);
-  if (e == hipSuccess) e = ef;
+  if (work) {
+    hipError_t ef = hipFreeAsync(work, hs);
+    if (e == hipSuccess) e = ef;
+  }
   if (e != hipSuccess) return hip_fail(e);
   return SSM_OK;
 }
@@ -3404,6 +3456,22 @@ ssm_status_t ssm_scan_bwd_saved(int64_t batch, int64_t dim, int64_t dstate, int6
   return scan_bwd_impl(batch, dim, dstate, seqlen, io, u, delta, A, B, C, D, z, delta_bias, softplus_flag, nullptr,
                        ckpt, dy, dlast, du, ddelta, dA, dB, dC, dD, dz, ddelta_bias, dh0,
                        reinterpret_cast<hipStream_t>(stream), false);
+}
+
+ssm_status_t ssm_scan_bwd_saved_noalloc(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, ssm_dtype_t io,
+                                        const void* u, const void* delta, const float* A, const void* B,
+                                        const void* C, const float* D, const void* z, const float* delta_bias,
+                                        int softplus_flag, const float* ckpt, const void* dy, const float* dlast,
+                                        void* du, void* ddelta, float* dA, float* dB, float* dC, float* dD, void* dz,
+                                        float* ddelta_bias, float* dh0, struct ihipStream_t* stream) {
+  if (!ckpt) {
+    Shape sh;
+    ssm_status_t st = shape_of(batch, dim, dstate, seqlen, io, &sh);
+    return st != SSM_OK ? st : SSM_ERR_NULL;
+  }
+  return scan_bwd_impl(batch, dim, dstate, seqlen, io, u, delta, A, B, C, D, z, delta_bias, softplus_flag, nullptr,
+                       ckpt, dy, dlast, du, ddelta, dA, dB, dC, dD, dz, ddelta_bias, dh0,
+                       reinterpret_cast<hipStream_t>(stream), false, false, true);
 }
 
 ssm_status_t ssm_scan_ckpt_bytes(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, ssm_dtype_t io,

@@ -42,7 +42,7 @@ def test_abi_version(lib):
 
 
 def test_status_strings(lib):
-    for code in range(9):
+    for code in range(10):
         s = lib.ssm_status_string(code)
         assert s and s != b"unknown status"
     assert lib.ssm_status_string(99) == b"unknown status"
@@ -381,3 +381,21 @@ def test_product_never_uses_the_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in text and "from oracle" not in text, f
                 assert "ssm_oracle" not in text and "oracle_scan" not in text, f
+
+
+def test_noalloc_backward_limit(lib):
+    """ssm_scan_bwd_saved_noalloc refuses, on the host, a call whose scratch exceeds
+    its fixed 64 MiB device array (the Mamba-1.4B layer: 129 MiB); its other checks
+    are ssm_scan_bwd_saved's."""
+    big = 1 << 36  # far-apart fake addresses: the arrays of a large call must not overlap
+
+    def call(batch, dim, dstate, seqlen, ck=True):
+        a = [big * (k + 1) for k in range(20)]
+        return lib.ssm_scan_bwd_saved_noalloc(batch, dim, dstate, seqlen, 1, a[1], a[2], a[3], a[4], a[5], None, None,
+                                              None, 1, a[12] if ck else None, a[13], None, a[14], a[15], a[16], a[17],
+                                              a[18], None, None, None, None, None)
+    assert call(4, 4096, 16, 4096) == 9                  # SSM_ERR_WORKSPACE
+    assert lib.ssm_status_string(9).startswith(b"the call needs more scratch")
+    assert call(4, 4096, 16, 4096, ck=False) == 1        # SSM_ERR_NULL first
+    assert call(0, 4096, 16, 4096) == 2
+    assert call(4, 4096, 5, 4096) == 8                   # outside the backward kernel, as ssm_scan_bwd_saved
