@@ -545,6 +545,103 @@ struct BCPipe {
   }
 };
 
+// fp32 rows: B and C in VGPRs, applied through DPP row broadcasts.  An fp32
+// sub-chunk of 16 states is 16 rows x 32 bytes per array, which as SGPR
+// groups (BCPipe) needs 64 SGPRs for two groups of two states and still
+// waits on every group (the scalar-load counter is shared and out of order).
+// Here lane k of every 16-lane row loads, with one 16-byte vector load per
+// 8 states, the 4 tokens 4 (k % 2) .. 4 (k % 2) + 3 of state 8u + k / 2; a
+// VALU operand `row_newbcast:k` then hands lane k's value to the whole row,
+// so every channel (lane) multiplies by the same B or C at no extra
+// instruction.  Vector loads complete in order, so the next sub-chunk's
+// rows are fetched while the current one computes and waited for exactly.
+template <int K>
+__device__ __forceinline__ float bcast_mul(float b, float x) {  // b from lane K of the row, times x
+  float r;
+  asm("v_mul_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf" : "=v"(r) : "v"(b), "v"(x), "n"(K));
+  return r;
+}
+template <int K>
+__device__ __forceinline__ float bcast_fmac(float acc, float c, float h) {  // acc + (c from lane K) * h, fused
+  asm("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf" : "+v"(acc) : "v"(c), "v"(h), "n"(K));
+  return acc;
+}
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+__device__ __forceinline__ float f4c(const float4& v, int j) { return j == 0 ? v.x : (j == 1 ? v.y : (j == 2 ? v.z : v.w)); }
+
+template <int NST, bool kEmit>
+struct BCVec {
+  static constexpr int NG = 1;              // one buffer per sub-chunk
+  static constexpr int NQ = (NST + 7) / 8;  // 16-byte quads per array
+  const float* Bb;
+  const float* Cb;
+  uint32_t row_bytes;
+  int n0;
+  float4 Bq[2][NQ], Cq[2][NQ];
+
+  __device__ __forceinline__ void fetch(int buf, uint32_t l_bytes) {
+    const int k = threadIdx.x & 15;
+    const uint32_t L = row_bytes / 4;
+#pragma unroll
+    for (int u = 0; u < NQ; ++u) {
+      const int n = 8 * u + (k >> 1);
+      if (n < NST) {  // lanes past the last state load nothing (their values are never broadcast)
+        const uint32_t off = (uint32_t)n * L + l_bytes / 4 + 4 * (k & 1);
+        Bq[buf][u] = *reinterpret_cast<const float4*>(Bb + off);
+        if (kEmit) Cq[buf][u] = *reinterpret_cast<const float4*>(Cb + off);
+      }
+    }
+  }
+  __device__ __forceinline__ void prime(uint32_t l_bytes) { fetch(0, l_bytes); }
+
+  // As BCPipe::chunk: one sub-chunk of kChunk tokens for all NST states.
+  template <int P0, bool kZoh>
+  __device__ __forceinline__ void chunk(uint32_t l_bytes, bool has_next, uint32_t next_l_bytes, const float A2[NST],
+                                        const float inva[NST], const float dl[kChunk], const float xl[kChunk],
+                                        float h[NST], float yv[kChunk]) {
+    constexpr int cur = P0;
+    (void)l_bytes;
+    __builtin_amdgcn_sched_barrier(0);
+    if (has_next) fetch(cur ^ 1, next_l_bytes);
+    __builtin_amdgcn_sched_barrier(0);
+    float du[kChunk];
+    if constexpr (kZoh) {
+#pragma unroll
+      for (int t = 0; t < kChunk; ++t) du[t] = dl[t] * xl[t];
+    }
+    static_for<0, NST>([&](auto nc) {
+      constexpr int n = decltype(nc)::value;
+      float hn = h[n];
+      static_for<0, kChunk>([&](auto tc) {
+        constexpr int t = decltype(tc)::value;
+        constexpr int k = 2 * (n % 8) + t / 4;  // the lane that holds (state n, token t)
+        const float ta = A2[n] * dl[t];
+        const float abar = exp2_hw(ta);
+        const float bu = kZoh ? zoh_input(ta, abar, du[t], xl[t] * inva[n]) : xl[t];
+        hn = __builtin_fmaf(abar, hn, bcast_mul<k>(f4c(Bq[cur][n / 8], t % 4), bu));
+        if constexpr (kEmit) {
+          const float cv = f4c(Cq[cur][n / 8], t % 4);
+          if constexpr (n == 0) yv[t] = bcast_mul<k>(cv, hn);
+          else yv[t] = bcast_fmac<k>(yv[t], cv, hn);
+        }
+      });
+      h[n] = hn;
+      asm volatile("" : "+v"(h[n]));
+      if constexpr ((n & 1) == 1 && kEmit) {
+#pragma unroll
+        for (int t = 0; t < kChunk; ++t) asm volatile("" : "+v"(yv[t]));
+      }
+    });
+    __builtin_amdgcn_sched_barrier(0);
+  }
+};
+
 // One token with scalar loads (tails, unaligned shapes).
 // uv is u; the input term is Delta * u, or its zero-order-hold form (kZoh).
 template <typename IoT, int N, bool kEmit, bool kZoh>
@@ -650,7 +747,8 @@ __device__ __forceinline__ void scan_lines(const IoT* ur, const IoT* dr, const I
                                            int64_t l1, const Channel<N>& c, float h[N], float* dsum,
                                            const ConvChan* cc = nullptr, float* xh = nullptr, IoT* uo = nullptr) {
   using LI = Line<IoT>;
-  BCPipe<IoT, N, kEmit> bc;
+  using BCT = typename std::conditional<sizeof(IoT) == 4, BCVec<N, kEmit>, BCPipe<IoT, N, kEmit>>::type;
+  BCT bc;
   bc.Bb = Bb;
   bc.Cb = Cb;
   bc.row_bytes = row_bytes;
@@ -703,10 +801,11 @@ __device__ __forceinline__ void scan_lines(const IoT* ur, const IoT* dr, const I
           }
           const int64_t lt = l + t0;
           // Each pass runs kChunksPerPass (even) chunks, so the buffer parity
-          // of chunk k's first group is (k * NG) mod 2 on every pass and tile.
+          // of chunk k's first group is (k * NG) mod 2 on every pass and tile
+          // (NG = 1 for BCVec: one buffer per chunk).
           // (The branch folds away once the chunk loop is unrolled.)
           const uint32_t lb = (uint32_t)(lt * sizeof(IoT)), nb = (uint32_t)((lt + kChunk) * sizeof(IoT));
-          if (((k * BCPipe<IoT, N, kEmit>::NG) & 1) == 0)
+          if (((k * BCT::NG) & 1) == 0)
             bc.template chunk<0, kZoh>(lb, lt + kChunk < l1, nb, c.A2, c.inva, dl, xl, h, yv);
           else
             bc.template chunk<1, kZoh>(lb, lt + kChunk < l1, nb, c.A2, c.inva, dl, xl, h, yv);
