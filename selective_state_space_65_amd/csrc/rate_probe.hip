@@ -8,9 +8,11 @@
 //   kind 0  fp32 FMA only        8 independent v_fma_f32 chains per lane
 //   kind 1  exp2 only            8 independent v_exp_f32 chains per lane
 //   kind 2  the scan's body      per (token, state): Delta*A mul, exp2,
-//                                B*x mul (B a wave-uniform SGPR operand),
-//                                the state FMA and the C.h FMA -- 2 states
-//                                x 8 tokens per iteration, as in the scan
+//                                B*x mul (B a wave-uniform SGPR operand, one
+//                                per state), the state FMA and the C.h FMA
+//                                (a mul for the first state) -- 2 states x
+//                                8 tokens per iteration, as in the scan:
+//                                5 VALU instructions per unit, one an exp2
 //   kind 3  exp2 and FMA mixed   1 exp2 + 4 FMA per unit, independent
 //
 // Ops per lane per iteration: kind 0: 64 FMA; kind 1: 64 exp2; kind 2: 16
@@ -61,8 +63,8 @@ __global__ __launch_bounds__(kThreads) void exp_kernel(int iters, float* sink) {
 // The scan's per-(token, state) body: 2 states over 8 tokens per iteration.
 // A2, B and C are wave-uniform (SGPR operands); dl and x are made opaque each
 // iteration so the exp2 arguments cannot be hoisted out of the loop.
-__global__ __launch_bounds__(kThreads) void scan_body_kernel(int iters, float a0, float a1, float bsc, float csc,
-                                                             float* sink) {
+__global__ __launch_bounds__(kThreads) void scan_body_kernel(int iters, float a0, float a1, float b0, float b1,
+                                                             float csc, float* sink) {
   float dl[8], xl[8];
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
@@ -71,6 +73,7 @@ __global__ __launch_bounds__(kThreads) void scan_body_kernel(int iters, float a0
   }
   float h0 = 0.0f, h1 = 0.0f, yacc = 0.0f;
   const float A2[2] = {a0, a1};
+  const float Bs[2] = {b0, b1};
   for (int it = 0; it < iters; ++it) {
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
@@ -85,7 +88,7 @@ __global__ __launch_bounds__(kThreads) void scan_body_kernel(int iters, float a0
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
         const float abar = __builtin_amdgcn_exp2f(A2[j] * dl[t]);
-        hn = __builtin_fmaf(abar, hn, bsc * xl[t]);
+        hn = __builtin_fmaf(abar, hn, Bs[j] * xl[t]);
         yv[t] = (j == 0) ? csc * hn : __builtin_fmaf(csc, hn, yv[t]);
       }
       h[j] = hn;
@@ -147,7 +150,7 @@ int rate_probe_launch(int kind, int blocks, int iters, float* sink, hipStream_t 
       break;
     case 2:
       hipLaunchKernelGGL(scan_body_kernel, dim3(blocks), dim3(kThreads), 0, stream, iters, -1.4427f, -2.8854f,
-                         0.5f, 0.25f, sink);
+                         0.5f, 0.375f, 0.25f, sink);
       break;
     case 3:
       hipLaunchKernelGGL(mix_kernel, dim3(blocks), dim3(kThreads), 0, stream, iters, 0.999f, 1e-4f, sink);

@@ -1019,9 +1019,17 @@ __global__ __launch_bounds__((64 * Split<IoT, N, S>::kWaves)) void scan_split_ke
     role = wv < RW ? 1 : (wv < 2 * RW ? 2 : 0);
     rw = wv < RW ? wv : (wv < 2 * RW ? wv - RW : wv - 2 * RW);
   }
+  // Channels of the block: B waves put lane l on channel l.  A and C waves
+  // put lane l on channel 16 rw + l % 16 and piece l / 16 of every tile (TS
+  // tokens), so that each of their global accesses covers 16 rows with 4
+  // consecutive pieces each: whole 128-byte lines of y per wave (two tiles'
+  // stores in a row for bf16), not 64 rows of one piece.
+  static_assert(RW * 16 == kWaveThreads && T / TS == 4, "A and C waves: 16 channels x 4 pieces");
+  const int lch = role == 0 ? lane : rw * 16 + (lane & 15);  // the lane's channel in the block
+  const int pc = lane >> 4;                                  // A and C: the lane's piece of a tile
   const int64_t g = blockIdx.x % a.groups;
   const int64_t b = blockIdx.x / a.groups;
-  const int64_t d_raw = g * kWaveThreads + lane;
+  const int64_t d_raw = g * kWaveThreads + lch;
   const bool active = d_raw < a.dim;
   const int64_t d = active ? d_raw : a.dim - 1;  // idle lanes shadow a valid channel, write nothing
   const int64_t L = a.seqlen;
@@ -1031,9 +1039,9 @@ __global__ __launch_bounds__((64 * Split<IoT, N, S>::kWaves)) void scan_split_ke
   const IoT* dr = static_cast<const IoT*>(a.delta) + ch * L;
   const IoT* zr = kZ ? static_cast<const IoT*>(a.z) + ch * L : nullptr;
   IoT* yr = static_cast<IoT*>(a.y) + ch * L;
-  // A and C waves own tokens [l + rw*TS, l + rw*TS + TS) of the tile at l; a
+  // A and C lanes own tokens [l + pc*TS, l + pc*TS + TS) of the tile at l; a
   // tile holds a multiple of kChunk = TS tokens, so the share is all or none.
-  auto has = [&](int64_t l) { return l + rw * TS < L; };
+  auto has = [&](int64_t l) { return l + pc * TS < L; };
 
   // Fused conv (A and C waves): the channel's filter taps, oldest first.
   float cw[4] = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -1120,7 +1128,7 @@ __global__ __launch_bounds__((64 * Split<IoT, N, S>::kWaves)) void scan_split_ke
     uint32_t eu[PW], ed[PW], ou[PW], od[PW], eh[HW], oh[HW];  // even / odd tiles
     auto fetch = [&](int64_t l, uint32_t (&qu)[PW], uint32_t (&qd)[PW], uint32_t (&qh)[HW]) {
       if (has(l)) {
-        const int64_t p0 = l + rw * TS;
+        const int64_t p0 = l + pc * TS;
         PI::load(ur + p0, qu);
         PI::load(dr + p0, qd);
         fetch_history(p0, qh);
@@ -1131,14 +1139,14 @@ __global__ __launch_bounds__((64 * Split<IoT, N, S>::kWaves)) void scan_split_ke
       if (!has(l)) return;
       if constexpr (kConv) {
         conv_piece(qu, qh);
-        if (uo && active) PI::store(uo + l + rw * TS, qu);
+        if (uo && active) PI::store(uo + l + pc * TS, qu);
       }
 #pragma unroll
       for (int t = 0; t < TS; t += 2) {
         float d0 = discretize_delta<kSoftplus>(LI::elem(qd, t), bias);
         float d1 = discretize_delta<kSoftplus>(LI::elem(qd, t + 1), bias);
         const float u0 = LI::elem(qu, t), u1 = LI::elem(qu, t + 1);
-        dx[bf][((rw * TS + t) / 2) * 64 + lane] =
+        dx[bf][((pc * TS + t) / 2) * 64 + lch] =
             kZoh ? make_float4(d0, u0, d1, u1) : make_float4(d0, d0 * u0, d1, d1 * u1);
       }
     };
@@ -1164,7 +1172,7 @@ __global__ __launch_bounds__((64 * Split<IoT, N, S>::kWaves)) void scan_split_ke
     uint32_t ye[PW], yo[PW];
     auto fetch = [&](int64_t l, uint32_t (&qu)[PW], uint32_t (&qz)[ZW], uint32_t (&qh)[HW]) {
       if (has(l)) {
-        const int64_t p0 = l + rw * TS;
+        const int64_t p0 = l + pc * TS;
         PI::load(ur + p0, qu);
         if constexpr (kZ) PI::load(zr + p0, qz);
         fetch_history(p0, qh);
@@ -1179,7 +1187,7 @@ __global__ __launch_bounds__((64 * Split<IoT, N, S>::kWaves)) void scan_split_ke
       for (int q = 0; q < TS / 4; ++q) {
         float4 part[S];
 #pragma unroll
-        for (int s2 = 0; s2 < S; ++s2) part[s2] = yp[bf][(s2 * (T / 4) + (rw * TS) / 4 + q) * 64 + lane];
+        for (int s2 = 0; s2 < S; ++s2) part[s2] = yp[bf][(s2 * (T / 4) + (pc * TS) / 4 + q) * 64 + lch];
         float4 acc = part[0];
 #pragma unroll
         for (int s2 = 1; s2 < S; ++s2) {
@@ -1201,7 +1209,7 @@ __global__ __launch_bounds__((64 * Split<IoT, N, S>::kWaves)) void scan_split_ke
       }
     };
     auto put = [&](int64_t lc, const uint32_t (&yw)[PW]) {
-      if (active && has(lc)) PI::store(yr + lc + rw * TS, yw);
+      if (active && has(lc)) PI::store(yr + lc + pc * TS, yw);
     };
     // kPair: an even tile's piece is kept until the odd tile after it is
     // finished, and both pieces of the 128-byte line are stored together.
