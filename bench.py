@@ -47,19 +47,26 @@ if ROOT not in sys.path:
 
 METRIC = "selective-scan HBM GB/s (% of MI355X peak) + (B·D·L)/s at Mamba-1.4B shape"
 
-# HBM bytes per call of the Mamba-1.4B-layer scan measured with rocprofv3
-# (FETCH_SIZE x 2 + WRITE_SIZE x 1, the factors a 1 GiB copy gives these
-# counters), valid only for the kernel source they were measured on: when
-# csrc/ssm_scan.hip changes, the figure is reported as null until re-measured.
+# HBM bytes per call of the scan workloads measured with rocprofv3
+# (FETCH_SIZE x 1.9999 + WRITE_SIZE x 1.0, the factors a 1 GiB copy gives these
+# counters in the same run), valid only for the kernel source they were
+# measured on: when csrc/ssm_scan.hip changes, the figures are reported as null
+# until re-measured.  Keys are the workload indices of inputs.scan_config.
 MEASURED_TRAFFIC = {
-    "source_sha256": "e3994abc2435a6778c76299a4fc6f19914d607c33187ebaf06aa53b5cac8378d",
-    "config": 2,
-    "read_bytes": 464_025_281,
-    "write_bytes": 221_480_512,
+    "source_sha256": "9dafa598393370974b6b904dffbdcc281d609c9b400d158943fede42f3bb24d8",
+    "per_call": {
+        2: {"read_bytes": 487_350_644, "write_bytes": 138_488_816},
+        1: {"read_bytes": 365_598_764, "write_bytes": 101_628_768},
+        3: {"read_bytes": 7_057_509_975, "write_bytes": 1_371_739_032},
+    },
 }
 HBM_PEAK_GBS = 8000.0
 LANE_SLOTS_PEAK = 256 * 64 * 2.4e9  # fp32 VALU lane-slots per second
 SLOTS_PER_ELEM_STATE = 6            # exp2 (2 slots, half rate) + 4 fp32 ops
+
+
+KERNELS = {"split": "scan_split_kernel", "segmented": "aggregate_kernel + carry_kernel + scan_kernel",
+           "generic": "scan_kernel (per-token)"}
 
 
 def algorithmic_bytes(batch, dim, dstate, seqlen, io_bytes, has_z=True, has_h0=False):
@@ -76,14 +83,15 @@ def decode_bytes(batch, dim, dstate, io_bytes):
 
 
 def measured_traffic(config):
-    """Counter-measured HBM bytes per call, or None if the kernel changed since."""
+    """Counter-measured HBM bytes per call (read + written), or None if the
+    kernel source changed since the measurement or the workload has none."""
     import hashlib
     src = os.path.join(ROOT, "selective_state_space_65_amd", "csrc", "ssm_scan.hip")
     digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
     m = MEASURED_TRAFFIC
-    if digest != m["source_sha256"] or config != m["config"]:
+    if digest != m["source_sha256"] or config not in m["per_call"]:
         return None
-    return m["read_bytes"] + m["write_bytes"]
+    return m["per_call"][config]["read_bytes"] + m["per_call"][config]["write_bytes"]
 
 
 def cpu_cores():
@@ -467,12 +475,18 @@ def bench_config(dev, cfg, steps, warmup):
     path, seg, seglen, scratch = binding.scan_plan(b, d, n, l, t["u"].dtype, with_path=True)
     del t, y, last
     torch.cuda.empty_cache()
+    gbs = nbytes / (avg_ms * 1e-3) / 1e9
+    traffic = measured_traffic(cfg)
+    alu_frac = SLOTS_PER_ELEM_STATE * b * d * l * n / (avg_ms * 1e-3) / LANE_SLOTS_PEAK
     return dict(workload=x.meta["name"], batch=b, dim=d, dstate=n, seqlen=l, io=x.io, kernel_path=path,
                 segments=seg, us_per_call=round(avg_ms * 1e3, 2), us_median=round(med_ms * 1e3, 2),
-                algorithmic_bytes=nbytes, algorithmic_gbs=round(nbytes / (avg_ms * 1e-3) / 1e9, 1),
-                hbm_frac=round(nbytes / (avg_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                alu_frac=round(SLOTS_PER_ELEM_STATE * b * d * l * n / (avg_ms * 1e-3) / LANE_SLOTS_PEAK, 4),
-                elements_per_s=round(b * d * l / (avg_ms * 1e-3), 1))
+                algorithmic_bytes=nbytes, algorithmic_gbs=round(gbs, 1), hbm_frac=round(gbs / HBM_PEAK_GBS, 4),
+                alu_frac=round(alu_frac, 4), elements_per_s=round(b * d * l / (avg_ms * 1e-3), 1),
+                roofline=dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                              frac=round(gbs / HBM_PEAK_GBS, 4), traffic=traffic,
+                              traffic_ratio=None if traffic is None else round(traffic / nbytes, 3),
+                              kernel="ssm_scan_fwd call: %s" % KERNELS[path],
+                              alu=dict(frac=round(alu_frac, 4), lane_slots_per_elem_state=SLOTS_PER_ELEM_STATE)))
 
 
 def sweep_seqlen(dev, steps, warmup, lengths):
@@ -576,10 +590,10 @@ def main():
     alu_rate = slots / (avg_ms * 1e-3)
     hbm_frac = call_gbs / HBM_PEAK_GBS
     alu_frac = alu_rate / LANE_SLOTS_PEAK
-    kernels = {"split": "scan_split_kernel", "segmented": "aggregate_kernel + carry_kernel + scan_kernel",
-               "generic": "scan_kernel (per-token)"}
+    traffic = measured_traffic(args.config)
     roof = dict(bound="hbm", achieved=round(call_gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s", frac=round(hbm_frac, 4),
-                traffic=measured_traffic(args.config), kernel="ssm_scan_fwd call: %s" % kernels[path],
+                traffic=traffic, traffic_ratio=None if traffic is None else round(traffic / nbytes, 3),
+                kernel="ssm_scan_fwd call: %s" % KERNELS[path],
                 call_us_avg=round(avg_ms * 1e3, 2), call_us_median=round(med_ms * 1e3, 2),
                 algorithmic_bytes=nbytes,
                 alu=dict(frac=round(alu_frac, 4), achieved=round(alu_rate / 1e12, 2),
