@@ -289,6 +289,8 @@ struct ScanArgs {
   int64_t groups;    // ceil(dim / 64)
   int64_t segments;  // P
   int64_t seg_len;   // tokens per segment, a multiple of 64; the last segment ends at seqlen
+  int64_t agg_len = 0;      // tokens per aggregate piece: seg_len / agg_per_seg, a multiple of 64
+  int64_t agg_per_seg = 1;  // aggregate pieces per segment (launch 1 runs one wave per piece)
   // Fused causal conv in front of the scan (every prefill kernel): u then
   // holds the conv input x.
   const float* conv_w;  // [dim][conv_width]
@@ -305,13 +307,15 @@ struct ScanArgs {
 
 constexpr int kCkptTokens = 16;  // tokens between backward checkpoints (one backward tile)
 
-// The segmented path keeps each segment's aggregate and carry-in in the
-// caller's y, inside the segment's own range of each row, before that range
-// is written: 4-byte slot 0 holds the segment's sum of Delta, slots 1..N its
-// end state (launch 1), then its carry-in (launch 2, in place); launch 3
-// reads the carry-in before its own y overwrites it.  A segment is at least
-// 64 tokens, so the N + 1 slots (68 bytes at N = 16) fit in its range for
-// either dtype.  bf16 rows may be only 2-byte aligned, so the slots move as
+// The segmented path keeps its aggregates and carry-ins in the caller's y,
+// before y is written.  Launch 1 scans each aggregate piece (a segment, or a
+// part of one) from zero and stores, at the start of the piece's range of
+// each row, its sum of Delta in 4-byte slot 0 and its end state in slots
+// 1..N; launch 2 folds the pieces in order and overwrites slots 1..N at the
+// start of each segment with the segment's carry-in (in place: the piece that
+// starts there is read first); launch 3 reads the carry-in before its own y
+// overwrites it.  A piece is at least 64 tokens, so the N + 1 slots (68 bytes
+// at N = 16) fit in its range for either dtype.  bf16 rows may be only 2-byte aligned, so the slots move as
 // 16-bit halves there.
 template <typename IoT>
 __device__ __forceinline__ float seg_slot_load(const void* y, int64_t seg_elem, int slot) {
@@ -2312,8 +2316,11 @@ __global__ __launch_bounds__(kBlockThreads) void conv_bwd_reduce_kernel(ConvBwdA
   if (dcb) dcb[d] = acc[K];
 }
 
-// Launch 1: every segment but the last scans from a zero state and records
-// (sum of Delta, end state).  The segment's decay is a = exp(A * sum Delta).
+// Launch 1: every aggregate piece of the segments but the last scans from a
+// zero state and records (sum of Delta, end state); the piece's decay is
+// a = exp(A * sum Delta).  Pieces are segments cut into agg_per_seg parts, so
+// that this launch has as many waves as the chip holds at its register use,
+// more than launch 3 (whose waves need more registers).
 template <typename IoT, int N, bool kSoftplus, bool kVec, bool kZoh, bool kConv>
 __global__ __launch_bounds__(kBlockThreads) void aggregate_kernel(ScanArgs a, int64_t total_waves) {
   const int64_t wave = wave_index();
@@ -2325,8 +2332,8 @@ __global__ __launch_bounds__(kBlockThreads) void aggregate_kernel(ScanArgs a, in
   const int64_t d = active ? d_raw : a.dim - 1;
   const int64_t L = a.seqlen;
   const int64_t ch = wc.b * a.dim + d;
-  const int64_t l0 = wc.s * a.seg_len;
-  const int64_t l1 = l0 + a.seg_len;  // never the last segment
+  const int64_t l0 = wc.s * a.agg_len;  // wc.s: the piece
+  const int64_t l1 = l0 + a.agg_len;     // never in the last segment
 
   Channel<N> c;
   load_channel<N>(a, d, c);
@@ -2373,11 +2380,12 @@ __global__ __launch_bounds__(kBlockThreads) void aggregate_kernel(ScanArgs a, in
   }
 }
 
-// Launch 2: one thread per (channel, state) folds the segment aggregates in
-// sequence order, carry[0] = h0, carry[s+1] = a_s * carry[s] + b_s with
-// a_s = exp(A * sum Delta_s), in place in y: segment s's slot 1 + n is read as
-// b_s before this thread overwrites it with carry[s] (slot 0, the sum, is
-// shared by the channel's threads and only read).
+// Launch 2: one thread per (channel, state) folds the pieces' aggregates in
+// sequence order, h <- a_j * h + b_j with a_j = exp(A * sum Delta_j), from
+// h = h0; the value of h at the start of segment s is that segment's
+// carry-in.  In place in y: the piece that starts segment s has its slot
+// 1 + n read as b_j before this thread overwrites it with the carry-in (slot
+// 0, the sum, is shared by the channel's threads and only read).
 template <typename IoT>
 __global__ __launch_bounds__(kBlockThreads) void carry_kernel(ScanArgs a) {
   const int64_t bd = a.batch * a.dim;
@@ -2389,29 +2397,30 @@ __global__ __launch_bounds__(kBlockThreads) void carry_kernel(ScanArgs a) {
   const float A2 = a.A[d * a.dstate + n] * kLog2e;
   const int64_t row = ch * a.seqlen;
   float h = a.h0 ? a.h0[idx] : 0.0f;
-  const int64_t P = a.segments;
-  int64_t s = 0;
-  // Aggregates do not depend on the running carry: fetch 8 segments ahead.
-  for (; s + 8 <= P - 1; s += 8) {
+  const int64_t J = (a.segments - 1) * a.agg_per_seg;  // pieces
+  const int64_t R = a.agg_per_seg;
+  int64_t j = 0;
+  // Aggregates do not depend on the running carry: fetch 8 pieces ahead.
+  for (; j + 8 <= J; j += 8) {
     float sums[8], hs[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      sums[j] = seg_slot_load<IoT>(a.y, row + (s + j) * a.seg_len, 0);
-      hs[j] = seg_slot_load<IoT>(a.y, row + (s + j) * a.seg_len, 1 + n);
+    for (int k = 0; k < 8; ++k) {
+      sums[k] = seg_slot_load<IoT>(a.y, row + (j + k) * a.agg_len, 0);
+      hs[k] = seg_slot_load<IoT>(a.y, row + (j + k) * a.agg_len, 1 + n);
     }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      seg_slot_store<IoT>(a.y, row + (s + j) * a.seg_len, 1 + n, h);
-      h = __builtin_fmaf(exp2_hw(A2 * sums[j]), h, hs[j]);
+    for (int k = 0; k < 8; ++k) {
+      if ((j + k) % R == 0) seg_slot_store<IoT>(a.y, row + (j + k) * a.agg_len, 1 + n, h);
+      h = __builtin_fmaf(exp2_hw(A2 * sums[k]), h, hs[k]);
     }
   }
-  for (; s < P - 1; ++s) {
-    const float sum = seg_slot_load<IoT>(a.y, row + s * a.seg_len, 0);
-    const float hb = seg_slot_load<IoT>(a.y, row + s * a.seg_len, 1 + n);
-    seg_slot_store<IoT>(a.y, row + s * a.seg_len, 1 + n, h);
+  for (; j < J; ++j) {
+    const float sum = seg_slot_load<IoT>(a.y, row + j * a.agg_len, 0);
+    const float hb = seg_slot_load<IoT>(a.y, row + j * a.agg_len, 1 + n);
+    if (j % R == 0) seg_slot_store<IoT>(a.y, row + j * a.agg_len, 1 + n, h);
     h = __builtin_fmaf(exp2_hw(A2 * sum), h, hb);
   }
-  seg_slot_store<IoT>(a.y, row + (P - 1) * a.seg_len, 1 + n, h);
+  seg_slot_store<IoT>(a.y, row + (a.segments - 1) * a.seg_len, 1 + n, h);
 }
 
 // ----------------------------------------------------------------------------
@@ -2715,6 +2724,7 @@ ssm_status_t shape_of(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen
 
 struct Plan {
   int64_t groups, segments, seg_len;
+  int64_t agg_per_seg = 1;  // aggregate pieces per segment (1, 2 or 4)
   int64_t scratch_bytes;  // always 0: no path takes device memory beyond its inputs and outputs
   bool split;  // single-pass state-split kernel
 };
@@ -2722,6 +2732,7 @@ struct Plan {
 constexpr int64_t kTargetWaves = 2048;  // two waves per SIMD on 256 CUs
 constexpr int64_t kSegAlign = 64;       // segments start on a 128-byte line for bf16 and fp32 rows
 constexpr int64_t kMinSegment = 256;    // tokens; keeps the aggregate pass amortised
+constexpr int64_t kAggWaves = 4096;     // four waves per SIMD: what the aggregate kernel's registers allow
 #ifndef SSM_SPLIT_MIN_BLOCKS
 #define SSM_SPLIT_MIN_BLOCKS 192
 #endif
@@ -2742,6 +2753,7 @@ Plan make_plan(const Shape& s, int64_t batch, int64_t dim, int64_t dstate, int64
   p.groups = (dim + kWaveThreads - 1) / kWaveThreads;
   int64_t base = batch * p.groups;
   p.split = base >= kSplitMinBlocks && (dstate == 4 || dstate == 8 || dstate == 16) && seqlen % kChunk == 0;
+  p.agg_per_seg = 1;
   if (p.split) {
     p.segments = 1;
     p.seg_len = seqlen;
@@ -2766,6 +2778,18 @@ Plan make_plan(const Shape& s, int64_t batch, int64_t dim, int64_t dstate, int64
     if (p.segments < 2) {
       p.segments = 1;
       p.seg_len = seqlen;
+    }
+  }
+  // Aggregate pieces: cut each segment into 2 or 4 when the aggregate launch
+  // would otherwise leave room for more waves, keeping pieces whole 128-byte
+  // lines and at least kMinSegment tokens.
+  if (p.segments > 1) {
+    const int64_t waves = base * (p.segments - 1);
+    for (int64_t r = 4; r >= 2; r /= 2) {
+      if (p.seg_len % (r * kSegAlign) == 0 && p.seg_len / r >= kMinSegment && waves * r <= kAggWaves) {
+        p.agg_per_seg = r;
+        break;
+      }
     }
   }
   return p;
@@ -2852,7 +2876,7 @@ template <typename IoT, int N, bool kZ, bool kSp, bool kVec, bool kZoh, bool kCo
 hipError_t launch_scan_t(const ScanArgs& a, const Plan& p, hipStream_t st) {
   int64_t waves_scan = a.batch * p.groups * p.segments;
   if (p.segments > 1) {
-    int64_t waves_agg = a.batch * p.groups * (p.segments - 1);
+    int64_t waves_agg = a.batch * p.groups * (p.segments - 1) * p.agg_per_seg;
     int64_t blocks = (waves_agg + kWavesPerBlock - 1) / kWavesPerBlock;
     hipLaunchKernelGGL((aggregate_kernel<IoT, N, kSp, kVec, kZoh, kConv>), dim3((unsigned)blocks), dim3(kBlockThreads),
                        0, st, a, waves_agg);
@@ -3160,7 +3184,7 @@ ScanArgs scan_args(const Shape&, int64_t batch, int64_t dim, int64_t dstate, int
   a.u = u; a.delta = delta; a.A = A; a.B = B; a.C = C; a.D = D; a.z = z; a.bias = delta_bias; a.h0 = h0;
   a.y = y; a.last_state = last_state;
   a.batch = batch; a.dim = dim; a.dstate = dstate; a.seqlen = seqlen;
-  a.groups = 0; a.segments = 0; a.seg_len = 0;
+  a.groups = 0; a.segments = 0; a.seg_len = 0; a.agg_len = 0; a.agg_per_seg = 1;
   a.conv_w = nullptr; a.conv_b = nullptr; a.x_prev = nullptr; a.u_out = nullptr; a.conv_width = 1; a.conv_silu = 0;
   a.ckpt = nullptr;
   a.zoh = 0;
@@ -3173,6 +3197,7 @@ ScanArgs scan_args(const Shape&, int64_t batch, int64_t dim, int64_t dstate, int
 ssm_status_t run_scan(ScanArgs& a, const Shape& sh, ssm_dtype_t io, bool vec, bool sp, bool conv, hipStream_t hs) {
   const Plan plan = make_plan(sh, a.batch, a.dim, a.dstate, a.seqlen, io);
   a.groups = plan.groups; a.segments = plan.segments; a.seg_len = plan.seg_len;
+  a.agg_per_seg = plan.agg_per_seg; a.agg_len = plan.seg_len / plan.agg_per_seg;
   hipError_t e = (io == SSM_BF16) ? launch_scan<bf16_t>(a, plan, hs, vec, sp, conv)
                                   : launch_scan<float>(a, plan, hs, vec, sp, conv);
   if (e != hipSuccess) return hip_fail(e);
