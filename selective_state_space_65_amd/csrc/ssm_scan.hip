@@ -920,16 +920,19 @@ __global__ __launch_bounds__(kBlockThreads) void scan_kernel(ScanArgs a, int64_t
 // A block owns 64 channels (one per lane) of one batch row and walks the
 // whole sequence once, in tiles of T = 32 tokens.  Its waves have one of
 // three roles, and between two barriers each role works on its own tile:
-//   A (4 waves): Delta = softplus(delta + bias) and x = Delta * u of 8
-//      tokens of tile i+1 -- wave a owns tokens [8a, 8a + 8) of every tile --
-//      published in LDS (with the conv fused, u is first computed from the
-//      conv input);
+//   A (4 waves): Delta = softplus(delta + bias) and x = Delta * u of tile
+//      i+1 -- wave a owns channels [16a, 16a + 16) of the block, lane l of it
+//      channel 16a + l % 16 and tokens [8 (l / 16), 8 (l / 16) + 8) of every
+//      tile -- published in LDS (with the conv fused, u is first computed
+//      from the conv input);
 //   B (S waves): wave w runs the NS states [w*NS, (w+1)*NS) over the 32
 //      tokens of tile i (B/C rows are wave-uniform scalar loads) and
 //      publishes its partial sums C.h per token in LDS;
-//   C (4 waves): the S partials of 8 tokens of tile i-1 added in wave order
-//      (so the result is deterministic), the D skip and the silu gate, and
-//      the store of y.
+//   C (4 waves): for the same channels and tokens as the A waves, the S
+//      partials of tile i-1 added in wave order (so the result is
+//      deterministic), the D skip and the silu gate, and the store of y: each
+//      store instruction of a wave covers 16 rows with 64 (bf16) or 128
+//      (fp32) contiguous bytes.
 // Each state is updated exactly once per token: no segment aggregates, no
 // rescans.  The roles share every SIMD (for S = 8: two B waves, one A and one
 // C): the short, latency-bound softplus and silu chains of A and C fill the
@@ -943,15 +946,15 @@ __global__ __launch_bounds__(kBlockThreads) void scan_kernel(ScanArgs a, int64_t
 // B waves are the block's first waves (the older wave wins issue ties), the
 // B/C rows of the next tile's first sub-chunk are fetched during the last
 // sub-chunk (before the barrier), and y goes out two tiles at a time, so
-// that both halves of each 128-byte line are written together; with fp32
-// rows the A and C waves come first and the B/C rows of a tile are fetched
-// after its barrier (a 128-byte fp32 line is one tile, written by the four
-// C waves together).
+// that each C wave writes both halves of its 128-byte lines back to back;
+// with fp32 rows the A and C waves come first and the B/C rows of a tile are
+// fetched after its barrier (a 128-byte fp32 line is one tile, written by
+// one C wave).
 template <typename IoT, int N, int S>
 struct Split {
   static constexpr int NS = N / S;
   static constexpr int T = 32;
-  static constexpr int TS = 8;         // tokens of a tile per A or C wave
+  static constexpr int TS = 8;         // tokens of a tile per A or C lane
   static constexpr int RW = T / TS;    // A waves = C waves = 4
   static constexpr int KT = T / kChunk;
   static constexpr int kWaves = S + 2 * RW;
@@ -2729,7 +2732,12 @@ struct Plan {
   bool split;  // single-pass state-split kernel
 };
 
-constexpr int64_t kTargetWaves = 2048;  // two waves per SIMD on 256 CUs
+// Scan waves the segmented plan aims at: two per SIMD on 256 CUs, what the
+// scan kernel's registers allow at once.  Measured on the long-sequence
+// workload (1 x 2560 x 16 x 131072, fp32): 2048 (52 segments of 2560 tokens,
+// the last 512) 2669 us per call; at most 2048 resident (49 of 2688) 2708 us;
+// 2560 3126 us; 3072 2722 us; 4096 2687 us.
+constexpr int64_t kTargetWaves = 2048;
 constexpr int64_t kSegAlign = 64;       // segments start on a 128-byte line for bf16 and fp32 rows
 constexpr int64_t kMinSegment = 256;    // tokens; keeps the aggregate pass amortised
 constexpr int64_t kAggWaves = 4096;     // four waves per SIMD: what the aggregate kernel's registers allow
