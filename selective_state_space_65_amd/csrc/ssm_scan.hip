@@ -1777,8 +1777,12 @@ __global__ __launch_bounds__(64 * S) void scan_bwd_kernel(BwdArgs a) {
       load_in(s_hi >= 3 ? s_hi - 3 : 0, inB);
       if (s_hi >= 2) p0(s_hi - 2, inA);
     }
-    // ---- P1: the tile's states from its checkpoint
+    // ---- P1: the tile's states from its checkpoint, and (real A, Delta * B
+    // rule) the decayed previous states Abar_t h_{t-1} that P2's dA and dDelta
+    // terms need (under zero-order hold P2 forms them from h_t, for registers)
+    constexpr bool kQ = !kCplx && !kZoh;
     float hs[NS][VT], ab[NS][VT];  // complex: [0] re, [1] im
+    float qs[kQ ? NS : 1][kQ ? VT : 1];
     if constexpr (kCplx) {
       float hr = hck[0], hi = hck[1];
 #pragma unroll
@@ -1804,7 +1808,12 @@ __global__ __launch_bounds__(64 * S) void scan_bwd_kernel(BwdArgs a) {
           const float ta = A2[j] * dlv[t];
           ab[j][t] = exp2_hw(ta);
           const float bu = kZoh ? zoh_input(ta, ab[j][t], dlv[t] * xv[t], xv[t] * inva[j]) : xv[t];
-          hc = __builtin_fmaf(ab[j][t], hc, U::elem(Bt[j][t / kChunk], t % kChunk) * bu);
+          if constexpr (kQ) {
+            qs[j][t] = ab[j][t] * hc;
+            hc = __builtin_fmaf(U::elem(Bt[j][t / kChunk], t % kChunk), bu, qs[j][t]);
+          } else {
+            hc = __builtin_fmaf(ab[j][t], hc, U::elem(Bt[j][t / kChunk], t % kChunk) * bu);
+          }
           hs[j][t] = hc;
         }
       }
@@ -1870,8 +1879,7 @@ __global__ __launch_bounds__(64 * S) void scan_bwd_kernel(BwdArgs a) {
                                                                     dA_acc[j]));
             } else {
               pv[j * kChunk + t] = lam * xv[tt];
-              const float q = __builtin_fmaf(-bv, xv[tt], hs[j][tt]);  // Abar_t h_{t-1} (active lanes)
-              const float m = lam * q;
+              const float m = lam * qs[j][tt];  // lambda Abar_t h_{t-1}
               sB = __builtin_fmaf(lam, bv, sB);
               sA = __builtin_fmaf(m, Af[j], sA);
               dA_acc[j] = __builtin_fmaf(m, dlv[tt], dA_acc[j]);

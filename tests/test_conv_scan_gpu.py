@@ -118,6 +118,31 @@ def test_other_paths(io, shape):
 
 
 @pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_segmented_aggregate_pieces_with_conv(io):
+    """A segmented plan whose aggregate launch runs each segment in two pieces
+    (52 segments of 640 tokens at 1 x 2560 x 32768): each piece starts its
+    conv from the four inputs before it.  Checked on sampled channels."""
+    b, d, n, l = 1, 2560, 16, 32768
+    dt = torch.float32 if io == "f32" else torch.bfloat16
+    assert binding.scan_plan(b, d, n, l, dt, with_path=True) == ("segmented", 52, 640, 0)
+    say("conv with aggregate pieces io=%s" % io)
+    x, w, cb, prev = conv_inputs(b, d, n, l, io, 4, 700, h0=True)
+    y, last, uo, _ = run(x, w, cb, prev, True)
+    ch = inputs.sample_channels(b, d, 6, seed=5)
+    di = [c[1] for c in ch]
+    u64 = oracle.conv1d_f64(x.u[:, di], w[di], None if cb is None else cb[di], None if prev is None else prev[:, di],
+                            silu=True)
+    ur = io_round(u64, io)
+    sub = lambda a: None if a is None else a[:, di]
+    yr, hr = oracle.scan_f64(ur, sub(x.delta), x.A[di], x.B, x.C, None if x.D is None else x.D[di], sub(x.z),
+                             None if x.delta_bias is None else x.delta_bias[di], x.softplus, sub(x.h0))
+    dti = torch.tensor(di, device=DEV)
+    check(np64(uo[:, dti]), u64, U_TOL[io], "u_out")
+    check(np64(y[:, dti]), yr, TOL[io], "y")
+    check(np64(last[:, dti]), hr, TOL["f32"], "last_state")
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
 def test_fused_equals_conv_then_scan(io):
     """The fused kernel's y is bitwise the plain scan of the u it reports, and
     that u is bitwise the per-token kernel's conv (a misaligned u_out sends the

@@ -112,6 +112,35 @@ def test_layer_shape_varied_channels_sampled():
     check(np64(last[bi, di]), hr, "f32", "last_state")
 
 
+# Segmented plans whose aggregate launch cuts each segment into pieces: 1 x
+# 2560 channels x 32768 tokens gives 52 segments of 640 tokens, a multiple of
+# 128 whose halves are >= 256 tokens, and 40 groups x 51 segments x 2 pieces
+# fit the aggregate launch's 4096 waves, so every segment but the last is
+# aggregated in two pieces and the carry launch folds 102 pieces.
+PIECE_CASES = [("f32", 16, "delta_b"), ("bf16", 16, "delta_b"), ("f32", 5, "delta_b"), ("f32", 16, "zoh"),
+               ("bf16", 8, "zoh")]
+
+
+@pytest.mark.parametrize("io,n,disc", PIECE_CASES, ids=["%s-n%d-%s" % c for c in PIECE_CASES])
+def test_segmented_aggregate_pieces(io, n, disc):
+    b, d, l = 1, 2560, 32768
+    dt = torch.float32 if io == "f32" else torch.bfloat16
+    path, seg, seglen, scratch = binding.scan_plan(b, d, n, l, dt, with_path=True)
+    assert (seg, seglen, scratch) == (52, 640, 0) and path == ("segmented" if n in (4, 8, 16) else "generic")
+    x = inputs.make_scan_inputs(b, d, n, l, io=io, seed=2100 + n, h0=True)
+    say("aggregate pieces %s n=%d %s path=%s" % (io, n, disc, path))
+    t = inputs.to_torch(x, DEV)
+    y, last = binding.scan_fwd_ex(t["u"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
+                                  delta_bias=t["delta_bias"], delta_softplus=True, h0=t["h0"], disc=disc)
+    torch.cuda.synchronize()
+    ch = inputs.sample_channels(b, d, 6, seed=n)
+    yr, hr = oracle.scan_channels_f64(ch, x.u, x.delta, x.A, x.B, x.C, x.D, x.z, x.delta_bias, True, x.h0,
+                                      zoh=disc == "zoh")
+    di = torch.tensor([c[1] for c in ch], device=DEV)
+    check(np64(y[0, di]), yr, io, "y")
+    check(np64(last[0, di]), hr, "f32", "last_state")
+
+
 def test_long_sequence_sampled_and_carry():
     x = inputs.scan_config(3)
     b, d, n, l = x.shape
