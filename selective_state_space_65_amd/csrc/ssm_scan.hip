@@ -993,6 +993,23 @@ struct Piece {
         reinterpret_cast<uint4*>(p)[j] = make_uint4(w[4 * j], w[4 * j + 1], w[4 * j + 2], w[4 * j + 3]);
     }
   }
+  // load() as a streaming (non-temporal) access: for data read for the last
+  // time, which L2 then lets go first, keeping the B/C rows that every block
+  // of a batch row shares resident.
+  typedef uint32_t V2 __attribute__((ext_vector_type(2)));
+  typedef uint32_t V4 __attribute__((ext_vector_type(4)));
+  __device__ static __forceinline__ void load_stream(const IoT* p, uint32_t w[kWords]) {
+    if constexpr (kWords == 2) {
+      const V2 v = __builtin_nontemporal_load(reinterpret_cast<const V2*>(p));
+      w[0] = v.x; w[1] = v.y;
+    } else {
+#pragma unroll
+      for (int j = 0; j < kWords / 4; ++j) {
+        const V4 v = __builtin_nontemporal_load(reinterpret_cast<const V4*>(p) + j);
+        w[4 * j] = v.x; w[4 * j + 1] = v.y; w[4 * j + 2] = v.z; w[4 * j + 3] = v.w;
+      }
+    }
+  }
 };
 
 // kCplx: complex diagonal A.  The N slots of a channel hold N/2 complex
@@ -1137,7 +1154,11 @@ __global__ __launch_bounds__((64 * Split<IoT, N, S>::kWaves)) void scan_split_ke
       if (has(l)) {
         const int64_t p0 = l + pc * TS;
         PI::load(ur + p0, qu);
-        PI::load(dr + p0, qd);
+        // Delta is read once: streamed for fp32 rows, where a tile is a whole
+        // 128-byte line; a bf16 tile is half a line, and streaming the two
+        // halves a tile apart fetches lines twice.
+        if constexpr (sizeof(IoT) == 4) PI::load_stream(dr + p0, qd);
+        else PI::load(dr + p0, qd);
         fetch_history(p0, qh);
       }
     };
@@ -1180,8 +1201,13 @@ __global__ __launch_bounds__((64 * Split<IoT, N, S>::kWaves)) void scan_split_ke
     auto fetch = [&](int64_t l, uint32_t (&qu)[PW], uint32_t (&qz)[ZW], uint32_t (&qh)[HW]) {
       if (has(l)) {
         const int64_t p0 = l + pc * TS;
-        PI::load(ur + p0, qu);
-        if constexpr (kZ) PI::load(zr + p0, qz);
+        // The last reads of u (the A waves read it two tiles earlier) and of z,
+        // streamed as the A waves' Delta is.
+        PI::load_stream(ur + p0, qu);
+        if constexpr (kZ) {
+          if constexpr (sizeof(IoT) == 4) PI::load_stream(zr + p0, qz);
+          else PI::load(zr + p0, qz);
+        }
         fetch_history(p0, qh);
       }
     };
