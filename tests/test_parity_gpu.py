@@ -141,6 +141,26 @@ def test_segmented_aggregate_pieces(io, n, disc):
     check(np64(last[0, di]), hr, "f32", "last_state")
 
 
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_segmented_aggregate_pieces_batch_rows_ragged_dim(io):
+    """Two batch rows of 1300 channels (21 groups, the last 20 channels wide)
+    over 31360 tokens: 49 segments of 640 tokens, each aggregated in two
+    pieces (42 x 48 x 2 = 4032 waves), with an initial state; sampled
+    channels of both rows, the ragged group included."""
+    b, d, n, l = 2, 1300, 16, 31360
+    dt = torch.float32 if io == "f32" else torch.bfloat16
+    assert binding.scan_plan(b, d, n, l, dt, with_path=True) == ("segmented", 49, 640, 0)
+    x = inputs.make_scan_inputs(b, d, n, l, io=io, seed=2200, h0=True)
+    say("aggregate pieces, 2 batch rows, ragged dim, io=%s" % io)
+    y, last = gpu_scan(x)
+    ch = inputs.sample_channels(b, d, 8, seed=22) + [(0, d - 1), (1, d - 20), (0, d - 21)]
+    yr, hr = oracle.scan_channels_f64(ch, x.u, x.delta, x.A, x.B, x.C, x.D, x.z, x.delta_bias, x.softplus, x.h0)
+    bi = torch.tensor([c[0] for c in ch], device=DEV)
+    di = torch.tensor([c[1] for c in ch], device=DEV)
+    check(np64(y[bi, di]), yr, io, "y")
+    check(np64(last[bi, di]), hr, "f32", "last_state")
+
+
 def test_long_sequence_sampled_and_carry():
     x = inputs.scan_config(3)
     b, d, n, l = x.shape
