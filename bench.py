@@ -474,6 +474,24 @@ def rate_probe(dev):
              "exp2_plus_4fma costs 4 + exp2_cost")
 
 
+def device_copy(dev, nbytes=1 << 30):
+    """A plain device-to-device copy of nbytes (torch copy_): the HBM rate a
+    streaming kernel reaches on this GPU, beside the 8 TB/s peak."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+
+    def fn():
+        dst.copy_(src)
+
+    _, avg_ms, med_ms = time_calls(fn, 5, 2)
+    del src, dst
+    torch.cuda.empty_cache()
+    moved = 2 * nbytes
+    return dict(bytes_per_copy=moved, us_per_copy=round(avg_ms * 1e3, 1),
+                gbs=round(moved / (avg_ms * 1e-3) / 1e9, 1), frac_of_peak=round(moved / (avg_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))
+
+
 def bench_config(dev, cfg, steps, warmup):
     """One scan workload (fp32 configs 1 and 3) timed call by call with HIP events."""
     import torch
@@ -630,6 +648,7 @@ def main():
                roofline=roof)
     if not args.no_probe:
         out["rate_probe"] = rate_probe(dev)
+        out["device_copy"] = device_copy(dev)
         roof["alu"]["probe_scan_body_cost_in_fma_slots"] = out["rate_probe"]["scan_body_cost_in_fma_slots"]
     if not args.no_configs:
         out["configs"] = {str(c): bench_config(dev, c, max(5, args.steps // 2), 2) for c in (1, 3)
