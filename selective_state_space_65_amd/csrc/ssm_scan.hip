@@ -1353,11 +1353,14 @@ __global__ __launch_bounds__((64 * Split<IoT, N, S>::kWaves)) void scan_split_ke
           }
           __builtin_amdgcn_sched_barrier(0);
           if (a.ckpt && (k * kChunk) % kCkptTokens == 0) {
-            // The state before token l + k*kChunk, for the backward's recompute.
+            // The state before token l + k*kChunk, for the backward's recompute
+            // (a streaming store: it is not read again in this kernel).
             const int64_t c = (l + k * kChunk) / kCkptTokens;
 #pragma unroll
             for (int j = 0; j < NS; ++j)
-              if (active) a.ckpt[((c * a.batch + b) * N + rw * NS + j) * a.dim + d] = h[j];
+              if (active) {
+                __builtin_nontemporal_store(h[j], &a.ckpt[((c * a.batch + b) * N + rw * NS + j) * a.dim + d]);
+              }
           }
           float yv[kChunk], du[kChunk];
           if constexpr (kZoh) {
@@ -1479,17 +1482,10 @@ struct BwdArgs {
 
 __device__ __forceinline__ float sigmoid_f32(float x) { return rcp_hw(1.0f + exp2_hw(-x * kLog2e)); }
 
-// Sum of NV values over the 64 lanes of a wave, all at once: log2(NV)
-// exchange-and-add halvings.  At the halving of distance m every lane keeps
-// the half of its values selected by lane bit m and adds the partner lane's
-// copy of that half; the partner differs in bit m (and, for the mirror
-// patterns, in lower bits only), so after the last halving lane i holds the
-// sum over the wave of value i mod NV.  Distances 32 and 16 are one
-// v_permlane32/16_swap per pair of registers (whichever order the pair comes
-// back in, lo + hi is the pair sum in each half); 8 and 4 are the DPP
-// row_mirror / row_half_mirror patterns, 2 and 1 quad permutes, each fused
-// into an add (both halves are added, the lane keeps one).  NV is 16, 32 or
-// 64.
+// The DPP partner patterns of the wave sums below, as a move of the
+// partner's value: 8 = row_mirror (lane l ^ 15 within a row of 16), 4 =
+// row_half_mirror (l ^ 7), 2 = quad_perm [2,3,0,1] (l ^ 2), 1 = quad_perm
+// [1,0,3,2] (l ^ 1).
 __device__ __forceinline__ float dpp_pair(float send, int ctrl_id) {
   const uint32_t s = __float_as_uint(send);
   uint32_t r;
@@ -1502,48 +1498,86 @@ __device__ __forceinline__ float dpp_pair(float send, int ctrl_id) {
   return __uint_as_float(r);
 }
 
+
+// Lanes of the upper half of the distance-m pair keep values [m, 2m), the
+// others [0, m), both in registers [0, m): two DPP adds with complementary
+// bank masks (lanes a bank mask leaves out keep their register), m <= 4.
+// Distance 8 pairs lane l with l ^ 15 (row_mirror; banks 2, 3 hold bit 3
+// set), distance 4 with l ^ 7 (row_half_mirror; banks 1, 3 hold bit 2 set).
+// The first add reads the partner's register i before the second overwrites
+// it in the upper lanes.  One s_nop 1 before and after gives the two wait
+// states a DPP read needs after a VALU write of its source.
+template <int M, int D>
+__device__ __forceinline__ void dpp_keep_halves(float (&v)[2 * M]) {
+#define SSM_KEEP(ctrl, lo, hi)                                                                        \
+  if constexpr (M == 4)                                                                               \
+    asm("s_nop 1\n"                                                                                   \
+        "v_add_f32_dpp %0, %0, %0 " ctrl " row_mask:0xf bank_mask:" lo "\n"                           \
+        "v_add_f32_dpp %0, %4, %4 " ctrl " row_mask:0xf bank_mask:" hi "\n"                           \
+        "v_add_f32_dpp %1, %1, %1 " ctrl " row_mask:0xf bank_mask:" lo "\n"                           \
+        "v_add_f32_dpp %1, %5, %5 " ctrl " row_mask:0xf bank_mask:" hi "\n"                           \
+        "v_add_f32_dpp %2, %2, %2 " ctrl " row_mask:0xf bank_mask:" lo "\n"                           \
+        "v_add_f32_dpp %2, %6, %6 " ctrl " row_mask:0xf bank_mask:" hi "\n"                           \
+        "v_add_f32_dpp %3, %3, %3 " ctrl " row_mask:0xf bank_mask:" lo "\n"                           \
+        "v_add_f32_dpp %3, %7, %7 " ctrl " row_mask:0xf bank_mask:" hi "\n"                           \
+        "s_nop 1"                                                                                     \
+        : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3])                                              \
+        : "v"(v[4]), "v"(v[5]), "v"(v[6]), "v"(v[7]));                                                \
+  else if constexpr (M == 2)                                                                          \
+    asm("s_nop 1\n"                                                                                   \
+        "v_add_f32_dpp %0, %0, %0 " ctrl " row_mask:0xf bank_mask:" lo "\n"                           \
+        "v_add_f32_dpp %0, %2, %2 " ctrl " row_mask:0xf bank_mask:" hi "\n"                           \
+        "v_add_f32_dpp %1, %1, %1 " ctrl " row_mask:0xf bank_mask:" lo "\n"                           \
+        "v_add_f32_dpp %1, %3, %3 " ctrl " row_mask:0xf bank_mask:" hi "\n"                           \
+        "s_nop 1"                                                                                     \
+        : "+v"(v[0]), "+v"(v[1])                                                                      \
+        : "v"(v[2]), "v"(v[3]));                                                                      \
+  else                                                                                                \
+    asm("s_nop 1\n"                                                                                   \
+        "v_add_f32_dpp %0, %0, %0 " ctrl " row_mask:0xf bank_mask:" lo "\n"                           \
+        "v_add_f32_dpp %0, %1, %1 " ctrl " row_mask:0xf bank_mask:" hi "\n"                           \
+        "s_nop 1"                                                                                     \
+        : "+v"(v[0])                                                                                  \
+        : "v"(v[1]));
+  static_assert(M == 1 || M == 2 || M == 4, "1, 2 or 4 kept values");
+  static_assert(D == 8 || D == 4, "distance 8 or 4");
+  if constexpr (D == 8) {
+    SSM_KEEP("row_mirror", "0x3", "0xc")
+  } else {
+    SSM_KEEP("row_half_mirror", "0x5", "0xa")
+  }
+#undef SSM_KEEP
+}
+
+// Sum of NV (16 or 32) values over the 64 lanes of a wave.  Lane bits 5, 4,
+// 3, 2 (and 1 for 32 values) each halve the values a lane keeps: bits 5 and 4
+// with v_permlane32/16_swap and an add per pair, bits 3 and 2 with
+// dpp_keep_halves, bit 1 with a DPP add of each half and a select; the bits
+// left add the one value over the remaining lanes.  Lane l returns the sum of
+// value l >> (6 - log2 NV).
 template <int NV>
-__device__ __forceinline__ float wave_sum_spread(float (&v)[NV], int lane) {
-  constexpr int kStages = NV == 64 ? 6 : (NV == 32 ? 5 : 4);
-  // (Counted loops: a shift-stepped loop is not fully unrolled, and a
-  // run-time m would turn every v[] access into a select chain.)
+__device__ __forceinline__ float wave_sum_halves(float (&v)[NV], int lane) {
+  static_assert(NV == 16 || NV == 32, "16 or 32 values");
 #pragma unroll
-  for (int st = 0; st < kStages; ++st) {
-    const int m = NV >> (st + 1);
-    if (m >= 16) {
-#pragma unroll
-      for (int i = 0; i < m; ++i) {
-        const auto r = (m == 32) ? __builtin_amdgcn_permlane32_swap(__float_as_uint(v[i]), __float_as_uint(v[m + i]),
-                                                                    false, false)
-                                 : __builtin_amdgcn_permlane16_swap(__float_as_uint(v[i]), __float_as_uint(v[m + i]),
-                                                                    false, false);
-        v[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-      }
-    } else {
-      // Both halves are summed with the partner and the lane keeps one: a
-      // select between two loaded values would be folded into one load at a
-      // lane-dependent index, which cannot stay in registers.
-      const bool hi = (lane & m) != 0;
-#pragma unroll
-      for (int i = 0; i < m; ++i) {
-        const float lo_sum = v[i] + dpp_pair(v[i], m);
-        const float hi_sum = v[m + i] + dpp_pair(v[m + i], m);
-        v[i] = hi ? hi_sum : lo_sum;
-      }
-    }
+  for (int i = 0; i < NV / 2; ++i) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[i]), __float_as_uint(v[NV / 2 + i]), false, false);
+    v[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
   }
-  static_assert(NV >= 16 && NV <= 64 && (NV & (NV - 1)) == 0, "16, 32 or 64 values");
-  // Below 64 values each 16- or 32-lane part of the wave holds sums over
-  // itself only: add the parts (a register swapped with itself).
-  float r = v[0];
 #pragma unroll
-  for (int st = kStages; st < 6; ++st) {
-    const int m = 1 << st;
-    const auto p = (m == 32) ? __builtin_amdgcn_permlane32_swap(__float_as_uint(r), __float_as_uint(r), false, false)
-                             : __builtin_amdgcn_permlane16_swap(__float_as_uint(r), __float_as_uint(r), false, false);
-    r = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  for (int i = 0; i < NV / 4; ++i) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[i]), __float_as_uint(v[NV / 4 + i]), false, false);
+    v[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
   }
-  return r;
+  dpp_keep_halves<NV / 8, 8>(*reinterpret_cast<float(*)[NV / 4]>(&v[0]));
+  dpp_keep_halves<NV / 16, 4>(*reinterpret_cast<float(*)[NV / 8]>(&v[0]));
+  float r;
+  if constexpr (NV == 32) {
+    const float lo_sum = v[0] + dpp_pair(v[0], 2), hi_sum = v[1] + dpp_pair(v[1], 2);
+    r = (lane & 2) ? hi_sum : lo_sum;
+  } else {
+    r = v[0] + dpp_pair(v[0], 2);
+  }
+  return r + dpp_pair(r, 1);
 }
 
 
@@ -1750,11 +1784,14 @@ __global__ __launch_bounds__(64 * S) void scan_bwd_kernel(BwdArgs a) {
     for (int t = 0; t < kChunk; ++t) gv[t] = sm.g[r][t][lane];
   };
 
-  // Checkpointed states of a tile, loaded one tile ahead.
+  // Checkpointed states of a tile, loaded one tile ahead (read once: a
+  // streaming load).
   float hck[NS] = {}, nhck[NS] = {};
   auto load_ckpt = [&](int64_t c, float (&h_)[NS]) {
 #pragma unroll
-    for (int j = 0; j < NS; ++j) h_[j] = a.ckpt[((c * a.batch + b) * N + w * NS + j) * a.dim + d];
+    for (int j = 0; j < NS; ++j) {
+      h_[j] = __builtin_nontemporal_load(&a.ckpt[((c * a.batch + b) * N + w * NS + j) * a.dim + d]);
+    }
   };
 
   // One tile of KV steps (KV = 2, or 1 for a last tile of 8 tokens), so that
@@ -1916,16 +1953,21 @@ __global__ __launch_bounds__(64 * S) void scan_bwd_kernel(BwdArgs a) {
         sm.pch[pb][w][t][lane] = sC;
         sm.part[pb][w][t][lane] = make_float2(sA, sB);
       }
-      // Sum the products over the wave's 64 channels.
-      const float tot = wave_sum_spread<NV>(pv, lane);
-      const int i = lane % NV;
+      // Sum the products over the wave's 64 channels; each sum is written
+      // once and read by the reduction kernel only (a streaming store, as
+      // for the checkpoints, keeps L2 for the token rows, whose lines are
+      // touched in eight steps).
+      constexpr int kSh = NV == 32 ? 1 : 2;
+      const float tot = wave_sum_halves<NV>(pv, lane);
+      const int i = lane >> kSh;
+      const bool wr = (lane & ((1 << kSh) - 1)) == 0;
       const int which = i / (NS * kChunk), jj = (i % (NS * kChunk)) / kChunk, t = i % kChunk;
-      if (lane < NV) {
+      if (wr) {
         float* dst = which ? a.dC_part : a.dB_part;
         if constexpr (kCplx)  // the wave's complex row of 2 L floats, (re, im) interleaved
-          dst[((grp * a.batch + b) * N + w * NS) * L + 2 * (l + k * kChunk + t) + jj] = tot;
+          __builtin_nontemporal_store(tot, &dst[((grp * a.batch + b) * N + w * NS) * L + 2 * (l + k * kChunk + t) + jj]);
         else
-          dst[((grp * a.batch + b) * N + w * NS + jj) * L + l + k * kChunk + t] = tot;
+          __builtin_nontemporal_store(tot, &dst[((grp * a.batch + b) * N + w * NS + jj) * L + l + k * kChunk + t]);
       }
     };
     // Waves w and w + S/2 share a SIMD and the older one (w) wins issue
