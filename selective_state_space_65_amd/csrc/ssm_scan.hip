@@ -1581,6 +1581,20 @@ __device__ __forceinline__ float wave_sum_halves(float (&v)[NV], int lane) {
 }
 
 
+// Makes the compiler wait for the loads of these registers at this point.
+template <int K>
+__device__ __forceinline__ void settle_vgprs(const float (&v)[K]) {
+#pragma unroll
+  for (int i = 0; i < K; ++i) asm volatile("" : : "v"(v[i]));
+}
+template <int E, int K>
+__device__ __forceinline__ void settle_vgprs(const uint32_t (&v)[E][K]) {
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+#pragma unroll
+    for (int i = 0; i < K; ++i) asm volatile("" : : "v"(v[e][i]));
+}
+
 // LDS of the backward kernel.  The token phases access it with lanes spread
 // over 8 channels x 8 tokens (token = lane % 8).  On gfx950 a 4-byte access
 // is served 32 lanes at a time from 32 banks and an 8- or 16-byte access
@@ -1775,7 +1789,7 @@ __global__ __launch_bounds__(64 * S) void scan_bwd_kernel(BwdArgs a) {
       }
     }
   };
-  const bool tw = w < TW;  // this wave runs the token phases
+  const bool tw = TW == S || w < TW;  // this wave runs the token phases
 
   // g of step s, for P2 (lanes = channels).
   auto read_g = [&](int64_t s, float (&gv)[kChunk]) {
@@ -1960,21 +1974,27 @@ __global__ __launch_bounds__(64 * S) void scan_bwd_kernel(BwdArgs a) {
       constexpr int kSh = NV == 32 ? 1 : 2;
       const float tot = wave_sum_halves<NV>(pv, lane);
       const int i = lane >> kSh;
-      const bool wr = (lane & ((1 << kSh) - 1)) == 0;
       const int which = i / (NS * kChunk), jj = (i % (NS * kChunk)) / kChunk, t = i % kChunk;
-      if (wr) {
-        float* dst = which ? a.dC_part : a.dB_part;
-        if constexpr (kCplx)  // the wave's complex row of 2 L floats, (re, im) interleaved
-          __builtin_nontemporal_store(tot, &dst[((grp * a.batch + b) * N + w * NS) * L + 2 * (l + k * kChunk + t) + jj]);
-        else
-          __builtin_nontemporal_store(tot, &dst[((grp * a.batch + b) * N + w * NS + jj) * L + l + k * kChunk + t]);
-      }
+      // The 2 (or 4) lanes that hold sum i store the same bits to the same
+      // place: an unconditional store keeps the later waits for loads exact.
+      float* dst = which ? a.dC_part : a.dB_part;
+      if constexpr (kCplx)  // the wave's complex row of 2 L floats, (re, im) interleaved
+        __builtin_nontemporal_store(tot, &dst[((grp * a.batch + b) * N + w * NS) * L + 2 * (l + k * kChunk + t) + jj]);
+      else
+        __builtin_nontemporal_store(tot, &dst[((grp * a.batch + b) * N + w * NS + jj) * L + l + k * kChunk + t]);
     };
     // Waves w and w + S/2 share a SIMD and the older one (w) wins issue
     // ties, so it reaches the barrier first; from P2 on the younger one is
     // given priority, which evens out their arrival.
     if (w >= S / 2) __builtin_amdgcn_s_setprio(1);
     p2(std::integral_constant<int, KV - 1>{});
+    // The token loads of this half (and, in a one-step tile, the next
+    // checkpoint) are waited for here, before P3's stores: the compiler's
+    // count for a later wait would leave out stores under a condition, and
+    // vmcnt, which stores also decrement, would then hold the wait until
+    // those just-issued stores complete.
+    if (tw) settle_vgprs(inB);
+    if constexpr (KV == 1) settle_vgprs(nhck);
     if (!kEarlyP3 && tw && s_hi + 1 < nsteps) p3_read(s_hi + 1, p3q);
     if (tw && s_hi + 1 < nsteps) p3_finish(s_hi + 1, p3q);
     __builtin_amdgcn_s_setprio(0);
@@ -1990,6 +2010,8 @@ __global__ __launch_bounds__(64 * S) void scan_bwd_kernel(BwdArgs a) {
       }
       if (w >= S / 2) __builtin_amdgcn_s_setprio(1);
       p2(std::integral_constant<int, 0>{});
+      if (tw) settle_vgprs(inA);
+      settle_vgprs(nhck);
       if (!kEarlyP3 && tw) p3_read(s_lo + 1, p3q);
       if (tw) p3_finish(s_lo + 1, p3q);
       __builtin_amdgcn_s_setprio(0);
