@@ -1017,6 +1017,12 @@ struct Piece {
 // complex state (NS = 2 slots); B and C rows are (re, im)-interleaved
 // [batch][N/2][seqlen][2], and the output is 2 Re(sum C h) + D u (each
 // stored state stands for a conjugate pair).
+// Where the C waves' lanes with no output (an idle channel, or a piece past
+// the end of the row) put their stores: every y store is then issued
+// unconditionally, as every A and C load is (clamped into the row), so the
+// compiler counts them all and a wait for one tile's loads does not also
+// wait for the loads and stores issued after them.
+static __device__ __align__(16) uint32_t y_sink[64 * 8];
 template <typename IoT, int N, int S, bool kZ, bool kSoftplus, bool kConv, bool kZoh, bool kCplx = false>
 __global__ __launch_bounds__((64 * Split<IoT, N, S>::kWaves)) void scan_split_kernel(ScanArgs a) {
   using SP = Split<IoT, N, S>;
@@ -1151,6 +1157,13 @@ __global__ __launch_bounds__((64 * Split<IoT, N, S>::kWaves)) void scan_split_ke
     IoT* uo = kConv && a.u_out ? static_cast<IoT*>(a.u_out) + ch * L : nullptr;
     uint32_t eu[PW], ed[PW], ou[PW], od[PW], eh[HW], oh[HW];  // even / odd tiles
     auto fetch = [&](int64_t l, uint32_t (&qu)[PW], uint32_t (&qd)[PW], uint32_t (&qh)[HW]) {
+      if constexpr (!kConv) {  // (the split path has L >= TS: a multiple of kChunk)
+        const int64_t p0 = l + pc * TS < L ? l + pc * TS : L - TS;
+        PI::load(ur + p0, qu);
+        if constexpr (sizeof(IoT) == 4) PI::load_stream(dr + p0, qd);
+        else PI::load(dr + p0, qd);
+        return;
+      }
       if (has(l)) {
         const int64_t p0 = l + pc * TS;
         PI::load(ur + p0, qu);
@@ -1199,6 +1212,15 @@ __global__ __launch_bounds__((64 * Split<IoT, N, S>::kWaves)) void scan_split_ke
     uint32_t eu[PW], ez[ZW], ou[PW], oz[ZW], eh[HW], oh[HW];  // even / odd tiles (u, or x with the conv)
     uint32_t ye[PW], yo[PW];
     auto fetch = [&](int64_t l, uint32_t (&qu)[PW], uint32_t (&qz)[ZW], uint32_t (&qh)[HW]) {
+      if constexpr (!kConv) {
+        const int64_t p0 = l + pc * TS < L ? l + pc * TS : L - TS;
+        PI::load_stream(ur + p0, qu);
+        if constexpr (kZ) {
+          if constexpr (sizeof(IoT) == 4) PI::load_stream(zr + p0, qz);
+          else PI::load(zr + p0, qz);
+        }
+        return;
+      }
       if (has(l)) {
         const int64_t p0 = l + pc * TS;
         // The last reads of u (the A waves read it two tiles earlier) and of z,
@@ -1242,7 +1264,9 @@ __global__ __launch_bounds__((64 * Split<IoT, N, S>::kWaves)) void scan_split_ke
       }
     };
     auto put = [&](int64_t lc, const uint32_t (&yw)[PW]) {
-      if (active && has(lc)) PI::store(yr + lc + pc * TS, yw);
+      static_assert(PW <= 8, "a lane's piece fits its 32-byte slot of the sink");
+      IoT* dst = (active && has(lc)) ? yr + lc + pc * TS : reinterpret_cast<IoT*>(y_sink + lane * 8);
+      PI::store(dst, yw);
     };
     // kPair: an even tile's piece is kept until the odd tile after it is
     // finished, and both pieces of the 128-byte line are stored together.
