@@ -66,7 +66,7 @@ SLOTS_PER_ELEM_STATE = 6            # exp2 (2 slots, half rate) + 4 fp32 ops
 
 
 KERNELS = {"split": "scan_split_kernel", "segmented": "aggregate_kernel + carry_kernel + scan_kernel",
-           "generic": "scan_kernel (per-token)"}
+           "generic": "scan_kernel (per-token)", "chunked": "scan_chunked_kernel"}
 
 
 def algorithmic_bytes(batch, dim, dstate, seqlen, io_bytes, has_z=True, has_h0=False):

@@ -78,7 +78,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 12
+#define SSM_ABI_VERSION 13
 
 struct ihipStream_t; /* the same incomplete type as HIP's hipStream_t */
 
@@ -470,8 +470,13 @@ typedef enum {
   SSM_PATH_SPLIT = 0,     /* one pass; a block owns 64 channels, its waves split the states */
   SSM_PATH_SEGMENTED = 1, /* the sequence is cut into segments scanned in parallel, then
                              combined (segment aggregates -> carries -> rescan)            */
-  SSM_PATH_GENERIC = 2    /* one token at a time with scalar loads: any dstate <= 16, any
+  SSM_PATH_GENERIC = 2,   /* one token at a time with scalar loads: any dstate <= 16, any
                              seqlen, any element-aligned pointers                          */
+  SSM_PATH_CHUNKED = 3    /* one pass, lanes along the sequence: a wave owns one channel, its
+                             lanes 16-token chunks of a tile, combined by a lane scan of the
+                             chunks' affine maps and a running carry (dstate 16, plain
+                             Delta*B rule, no fused conv; shapes with too few channels for
+                             SSM_PATH_SPLIT)                                               */
 } ssm_path_t;
 
 /*
@@ -487,6 +492,18 @@ typedef enum {
 ssm_status_t ssm_scan_fwd_plan(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
                                ssm_dtype_t io, int* path, int64_t* segments, int64_t* segment_len,
                                int64_t* scratch_bytes);
+
+/*
+ * ssm_scan_fwd_plan_ex -- ssm_scan_fwd_plan for the other prefill entry
+ * points: disc is the discretization of B (ssm_scan_fwd_ex), conv_width the
+ * width of the conv fused in front (ssm_conv_scan_fwd; 0 for none).  The
+ * chunked path runs only the plain Delta*B rule without a conv; the other
+ * calls of such a shape run segmented.  SSM_ERR_UNSUPPORTED for an unknown
+ * disc or a conv_width outside 0..4.
+ */
+ssm_status_t ssm_scan_fwd_plan_ex(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
+                                  ssm_dtype_t io, ssm_disc_t disc, int64_t conv_width, int* path,
+                                  int64_t* segments, int64_t* segment_len, int64_t* scratch_bytes);
 
 /* Static English text for a status code (never NULL). */
 const char* ssm_status_string(ssm_status_t status);

@@ -60,6 +60,8 @@ SIGNATURES = {
                                         _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "ssm_scan_fwd_plan": (_I, [_I64, _I64, _I64, _I64, _I, ctypes.POINTER(_I), ctypes.POINTER(_I64),
                               ctypes.POINTER(_I64), ctypes.POINTER(_I64)]),
+    "ssm_scan_fwd_plan_ex": (_I, [_I64, _I64, _I64, _I64, _I, _I, _I64, ctypes.POINTER(_I), ctypes.POINTER(_I64),
+                                 ctypes.POINTER(_I64), ctypes.POINTER(_I64)]),
     "ssm_status_string": (ctypes.c_char_p, [_I]),
     "ssm_last_hip_error": (_I, []),
     "ssm_abi_version": (_I, []),
@@ -139,20 +141,21 @@ def _stream(device, stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-PATH_NAMES = {0: "split", 1: "segmented", 2: "generic"}
+PATH_NAMES = {0: "split", 1: "segmented", 2: "generic", 3: "chunked"}
 
 
-def scan_plan(batch, dim, dstate, seqlen, io_dtype, with_path=False):
+def scan_plan(batch, dim, dstate, seqlen, io_dtype, with_path=False, disc="delta_b", conv_width=0):
     """(segments, segment_len, scratch_bytes) the library uses for this shape.
 
-    With with_path=True the kernel path name ("split", "segmented" or
-    "generic") is prepended to the tuple.
+    With with_path=True the kernel path name ("split", "chunked", "segmented" or
+    "generic") is prepended to the tuple.  disc and conv_width name the entry
+    point: ssm_scan_fwd_ex's discretization, ssm_conv_scan_fwd's conv width.
     """
     lib = load_library()
     path, seg, seglen, scratch = _I(), _I64(), _I64(), _I64()
-    st = lib.ssm_scan_fwd_plan(batch, dim, dstate, seqlen, _io_code(io_dtype), ctypes.byref(path), ctypes.byref(seg),
-                               ctypes.byref(seglen), ctypes.byref(scratch))
-    _check("ssm_scan_fwd_plan", st)
+    st = lib.ssm_scan_fwd_plan_ex(batch, dim, dstate, seqlen, _io_code(io_dtype), DISC_CODES[disc], conv_width,
+                                  ctypes.byref(path), ctypes.byref(seg), ctypes.byref(seglen), ctypes.byref(scratch))
+    _check("ssm_scan_fwd_plan_ex", st)
     if with_path:
         return PATH_NAMES[path.value], seg.value, seglen.value, scratch.value
     return seg.value, seglen.value, scratch.value

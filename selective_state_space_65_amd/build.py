@@ -1,8 +1,10 @@
 """Builds the HIP library libssm_scan.so in-tree for gfx950 with hipcc.
 
 The library is the whole product path: C ABI + kernels in one shared object
-(csrc/ssm_scan.hip, header include/ssm_scan.h).  Packed FP32 instructions are
-disabled for every HIP compile (-packed-fp32-ops).
+(csrc/ssm_scan.hip: the ABI and most kernels; csrc/scan_chunked.hip: the
+chunked prefill scan; header include/ssm_scan.h).  The translation units are
+compiled in parallel and linked.  Packed FP32 instructions are disabled for
+every HIP compile (-packed-fp32-ops).
 """
 import os
 import subprocess
@@ -10,7 +12,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SRC = os.path.join(HERE, "csrc", "ssm_scan.hip")
+SRCS = [os.path.join(HERE, "csrc", "ssm_scan.hip"), os.path.join(HERE, "csrc", "scan_chunked.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libssm_scan.so")
 # Instruction-rate probes for the roofline (bench.py only; not the scan path).
@@ -22,7 +24,6 @@ HIPCC_FLAGS = [
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     "-Wall",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
@@ -33,24 +34,40 @@ def hipcc():
     return os.path.join(rocm, "bin", "hipcc")
 
 
-def _compile(src, lib, verbose):
+def _run(cmds, verbose):
+    """Runs the hipcc command lines in parallel; raises if any fails."""
+    procs = []
+    for cmd in cmds:
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append(subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True))
+    failed = []
+    for cmd, proc in zip(cmds, procs):
+        out, _ = proc.communicate()
+        if proc.returncode != 0:
+            sys.stderr.write(out)
+            failed.append(cmd[-1])
+    if failed:
+        raise RuntimeError("hipcc failed on %s" % ", ".join(failed))
+
+
+def _link(srcs, lib, verbose):
+    """Compiles each source to an object (in parallel) and links them into lib."""
+    objs = [lib + ".%d.o" % i for i in range(len(srcs))]
+    _run([[hipcc()] + HIPCC_FLAGS + ["-I", INCLUDE, "-c", "-o", o, s] for s, o in zip(srcs, objs)], verbose)
     tmp = lib + ".tmp"
-    cmd = [hipcc()] + HIPCC_FLAGS + ["-I", INCLUDE, "-o", tmp, src]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    proc = subprocess.run(cmd, capture_output=True, text=True)
-    if proc.returncode != 0:
-        sys.stderr.write(proc.stdout + proc.stderr)
-        raise RuntimeError("hipcc failed building %s" % lib)
+    _run([[hipcc()] + HIPCC_FLAGS + ["-shared", "-o", tmp] + objs], verbose)
+    for o in objs:
+        os.remove(o)
     os.replace(tmp, lib)
     return lib
 
 
 def build(verbose=False):
-    """Compile csrc/ssm_scan.hip into libssm_scan.so and csrc/rate_probe.hip into
-    librate_probe.so (always recompiles)."""
-    _compile(PROBE_SRC, PROBE_LIB, verbose)
-    return _compile(SRC, LIB, verbose)
+    """Compile the library sources into libssm_scan.so and csrc/rate_probe.hip
+    into librate_probe.so (always recompiles)."""
+    _link([PROBE_SRC], PROBE_LIB, verbose)
+    return _link(SRCS, LIB, verbose)
 
 
 if __name__ == "__main__":

@@ -1,0 +1,108 @@
+// device_common.h -- device helpers shared by the kernel translation units of
+// libssm_scan.so (fp32 transcendentals on the hardware units, the softplus and
+// silu used by every prefill kernel, bf16 conversions, row loads and stores,
+// and the LDS-only workgroup barrier).  Internal: not part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+typedef uint16_t bf16_t;  // bit pattern of a bfloat16
+
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float log2_hw(float x) { return __builtin_amdgcn_logf(x); }
+__device__ __forceinline__ float rcp_hw(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// softplus(x) = log(1 + e^x) = max(x, 0) + log1p(e), e = e^-|x| in (0, 1].
+// w = 1 + e is rounded, but for w in [1, 2] its rounding error c = (w - 1) - e
+// is exact (w - 1 is exact there, and so is the difference of two nearby
+// floats), and log1p(e) = log(w) - c / w + O(c^2).  Using c for c / w errs by
+// at most c / 2 <= 2^-25 absolute, which is below the rounding of the result
+// except where the result is below 2^-24 -- and there (w == 1, so c = -e)
+// the formula returns e itself.  Emulated in fp32 with correctly rounded
+// exp2/log2 over x in [-40, 40] it stays within 2e-6 relative of the fp64
+// log1p(exp(x)), like the Kahan form log(w) * e / (w - 1), with one
+// transcendental and four VALU ops fewer.
+__device__ __forceinline__ float softplus_f32(float x) {
+  const float e = exp2_hw(-__builtin_fabsf(x) * kLog2e);  // in (0, 1]
+  const float w = 1.0f + e;                               // in [1, 2]
+  const float c = (w - 1.0f) - e;                         // rounding error of w, exact
+  return __builtin_fmaf(log2_hw(w), kLn2, __builtin_fmaxf(x, 0.0f) - c);
+}
+
+// silu(z) = z * sigmoid(z) = z / (1 + e^-z)
+__device__ __forceinline__ float silu_f32(float z) { return z * rcp_hw(1.0f + exp2_hw(-z * kLog2e)); }
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+template <typename IoT>
+struct Io;
+
+template <>
+struct Io<float> {
+  __device__ static __forceinline__ float load1(const float* p) { return *p; }
+  __device__ static __forceinline__ void store1(float* p, float v) { *p = v; }
+  // 8 consecutive elements; p is 16-byte aligned.
+  __device__ static __forceinline__ void load8(const float* p, float out[8]) {
+    float4 a = reinterpret_cast<const float4*>(p)[0];
+    float4 b = reinterpret_cast<const float4*>(p)[1];
+    out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
+    out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
+  }
+  __device__ static __forceinline__ void store8(float* p, const float v[8]) {
+    reinterpret_cast<float4*>(p)[0] = make_float4(v[0], v[1], v[2], v[3]);
+    reinterpret_cast<float4*>(p)[1] = make_float4(v[4], v[5], v[6], v[7]);
+  }
+  // 4 consecutive elements; p is 16-byte aligned.
+  __device__ static __forceinline__ void load4(const float* p, float out[4]) {
+    float4 a = *reinterpret_cast<const float4*>(p);
+    out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
+  }
+};
+
+template <>
+struct Io<bf16_t> {
+  __device__ static __forceinline__ float load1(const bf16_t* p) { return __uint_as_float((uint32_t)*p << 16); }
+  __device__ static __forceinline__ void store1(bf16_t* p, float v) {
+    __bf16 r = (__bf16)v;  // round to nearest even (v_cvt_pk_bf16_f32)
+    *p = __builtin_bit_cast(bf16_t, r);
+  }
+  __device__ static __forceinline__ void load8(const bf16_t* p, float out[8]) {
+    uint4 w = *reinterpret_cast<const uint4*>(p);
+    out[0] = bf16_lo(w.x); out[1] = bf16_hi(w.x); out[2] = bf16_lo(w.y); out[3] = bf16_hi(w.y);
+    out[4] = bf16_lo(w.z); out[5] = bf16_hi(w.z); out[6] = bf16_lo(w.w); out[7] = bf16_hi(w.w);
+  }
+  __device__ static __forceinline__ uint32_t pack2(float lo, float hi) {
+    uint32_t a = __builtin_bit_cast(bf16_t, (__bf16)lo);
+    uint32_t b = __builtin_bit_cast(bf16_t, (__bf16)hi);
+    return a | (b << 16);
+  }
+  __device__ static __forceinline__ void store8(bf16_t* p, const float v[8]) {
+    uint4 w;
+    w.x = pack2(v[0], v[1]); w.y = pack2(v[2], v[3]); w.z = pack2(v[4], v[5]); w.w = pack2(v[6], v[7]);
+    *reinterpret_cast<uint4*>(p) = w;
+  }
+  // 4 consecutive elements; p is 8-byte aligned.
+  __device__ static __forceinline__ void load4(const bf16_t* p, float out[4]) {
+    uint2 w = *reinterpret_cast<const uint2*>(p);
+    out[0] = bf16_lo(w.x); out[1] = bf16_hi(w.x); out[2] = bf16_lo(w.y); out[3] = bf16_hi(w.y);
+  }
+};
+
+// Workgroup barrier that orders LDS only: the LDS writes before it are
+// visible to every wave after it, while global loads and stores stay in
+// flight (a full __syncthreads would also wait for those).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+}  // namespace

@@ -1,0 +1,33 @@
+// scan_chunked.h -- internal interface between the C ABI (ssm_scan.hip) and
+// the chunked prefill scan (scan_chunked.hip).  Not part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+// One prefill call on the chunked path: pointers and sizes as validated by
+// ssm_scan_fwd (dstate 16, seqlen a multiple of 8, rows 16-byte aligned).
+struct ChunkedScanArgs {
+  const void* u;
+  const void* delta;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* D;     // may be null
+  const void* z;      // may be null
+  const float* bias;  // may be null
+  const float* h0;    // may be null; may equal last_state
+  void* y;
+  float* last_state;  // may be null
+  int64_t batch, dim, seqlen;
+};
+
+// Channels per block (waves of one block) the launch uses for batch * dim
+// channels: 8 to 16, chosen so that the blocks cover the 256 compute units
+// as evenly as possible.
+int ssmi_chunked_block_waves(int64_t channels);
+
+// Enqueues the chunked scan on st.  bf16: io dtype bf16 (else fp32);
+// softplus: Delta = softplus(delta + bias).
+hipError_t ssmi_chunked_launch(const ChunkedScanArgs& a, bool bf16, bool softplus, hipStream_t st);

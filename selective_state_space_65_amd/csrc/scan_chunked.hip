@@ -1,0 +1,346 @@
+// scan_chunked.hip -- the chunked prefill scan: lanes along the sequence.
+//
+// The selective scan h_t = Abar_t h_{t-1} + Bbar_t u_t is, token by token,
+// the affine map h -> a h + b.  Maps compose associatively,
+//   (a1, b1) o (a2, b2) = (a1 a2, a2 b1 + b2)     (first 1, then 2),
+// so a sequence may be cut into chunks that are run separately and then
+// combined in any grouping (the Chinese explainer's parallel-scan section,
+// "硬件感知的设计：并行扫描(parallel scan)且借鉴Flash Attention").  This kernel
+// is that combine done on chip, for shapes with too few (batch, channel)
+// rows for the one-lane-per-channel kernels to fill the GPU (long sequences
+// over few channels):
+//
+//   * A wave owns ONE channel of one batch row.  Its 64 lanes own
+//     consecutive 16-token chunks of a 1024-token tile, so a tile of a row
+//     is read with contiguous 16-byte loads and nothing is re-read.
+//   * Per state n (the 16 states one after another), each lane
+//       1. discretizes its 16 tokens -- Abar = exp(Delta A[n]),
+//          Bbar u = Delta u B[n] -- keeps them in registers, and runs its
+//          chunk from a zero state: the chunk's map is (a, b) with
+//          a = exp(A[n] sum Delta) and b the end state;
+//       2. scans these maps over the 64 lanes with DPP lane shifts
+//          (row_shr 1, 2, 4, 8 inside each row of 16 lanes, then row_bcast
+//          15 and 31 across rows) and shifts the result by one lane
+//          (wave_shr 1): each lane now holds the map of the tile before its
+//          chunk; applied to the running carry (the state before the tile,
+//          wave-uniform, kept in SGPRs) it is the lane's true state before
+//          its chunk;
+//       3. runs its chunk again from that state with the kept Abar and
+//          Bbar u, adding C[n] h to each token's output.
+//     The carry then advances by the whole tile's map (lane 63's scan).
+//   * B and C are shared by every channel of a batch row: a block of 8 to 16
+//     waves (consecutive channels of one row) stages them through LDS, 8
+//     states x 1024 tokens of B and C (64 KB) per stage, double-buffered,
+//     one LDS barrier per stage.  The next stage is loaded one state row at
+//     a time by the first waves while the current one is computed.
+//   * Nothing but y and last_state is written: no aggregate, carry or
+//     expanded state reaches memory, and the sequence is read once.
+//
+// Per (token, state) the lane spends the plain recurrence's work (the exp,
+// two products and the state FMA) plus one FMA for the rerun and one for
+// C h; the lane scan adds about 20 instructions per state per 16 tokens.
+#include <hip/hip_runtime.h>
+
+#include "device_common.h"
+#include "scan_chunked.h"
+
+namespace {
+
+constexpr int kN = 16;                   // states (dstate)
+constexpr int kTok = 16;                 // tokens per lane
+constexpr int kTile = 64 * kTok;         // tokens per wave tile
+constexpr int kStageStates = 8;          // states per LDS stage
+constexpr int kRowF4 = kTile / 4;        // float4 slots per staged row
+constexpr int kMinWaves = 8;             // the fp32 stager needs 512 threads
+constexpr int kMaxWaves = 12;
+
+// DPP controls (GFX9 encoding).
+constexpr int kDppWaveShr1 = 0x138;
+
+// v moved from the lane the control names; lanes with no such lane (or
+// outside row_mask) keep `old`.
+template <int Ctrl, int RowMask>
+__device__ __forceinline__ float dpp(float old, float v) {
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(v), Ctrl, RowMask, 0xf, false));
+}
+
+// Inclusive scan of the chunk maps (a, b) over the 64 lanes: lane i ends
+// with the composition of the maps of lanes 0..i.  Each step composes the
+// map this lane holds (the later chunks) after the map of the lane the DPP
+// control names (the earlier chunks): b += b' a, a = a' a.  A lane with no
+// such lane (the first lanes of a row for row_shr, the rows outside
+// row_mask for row_bcast) is not written, i.e. composes with the identity.
+// Written as DPP-operand VALU instructions (one per half-step); each is
+// preceded by the two wait states a DPP read needs after a VALU write of its
+// register.
+__device__ __forceinline__ void lane_scan(float& a, float& b) {
+  asm volatile(
+      "s_nop 1\n\t"
+      "v_fmac_f32_dpp %0, %0, %1 row_shr:1 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %1, %1, %1 row_shr:1 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_fmac_f32_dpp %0, %0, %1 row_shr:2 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %1, %1, %1 row_shr:2 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_fmac_f32_dpp %0, %0, %1 row_shr:4 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %1, %1, %1 row_shr:4 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_fmac_f32_dpp %0, %0, %1 row_shr:8 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %1, %1, %1 row_shr:8 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_fmac_f32_dpp %0, %0, %1 row_bcast:15 row_mask:0xa bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %1, %1, %1 row_bcast:15 row_mask:0xa bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_fmac_f32_dpp %0, %0, %1 row_bcast:31 row_mask:0xc bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %1, %1, %1 row_bcast:31 row_mask:0xc bank_mask:0xf"
+      : "+v"(b), "+v"(a));
+}
+
+// Staged B/C row layout: slot q * 64 + i holds tokens 4q .. 4q + 3 of lane
+// i's chunk (16 i + 4q ...), so each lane reads its chunk with four
+// conflict-free 16-byte LDS reads.
+__device__ __forceinline__ int stage_slot(int q4) { return (q4 & 3) * 64 + (q4 >> 2); }
+
+// Loads and stores one state's B and C rows of a stage.  Thread p < kPieces
+// moves one piece; pieces past the end of the sequence are zeros.
+template <typename IoT>
+struct Stager;
+
+template <>
+struct Stager<float> {
+  static constexpr int kPieces = 2 * kRowF4;  // float4 pieces of the B and C rows
+  float4 v;
+  __device__ __forceinline__ void load(const float* Bb, const float* Cb, int n, int64_t t0, int64_t L, int p) {
+    const float* row = ((p < kRowF4) ? Bb : Cb) + (int64_t)n * L;
+    const int q4 = p & (kRowF4 - 1);
+    const int64_t t = t0 + 4 * q4;
+    const float4 w = *reinterpret_cast<const float4*>(row + (t < L ? t : L - 4));
+    v = t < L ? w : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  }
+  __device__ __forceinline__ void store(float4 (*rows)[kRowF4], int p) const {
+    rows[p >= kRowF4][stage_slot(p & (kRowF4 - 1))] = v;
+  }
+};
+
+template <>
+struct Stager<bf16_t> {
+  static constexpr int kPieces = 2 * kTile / 8;  // 8-token pieces of the B and C rows
+  uint4 w;
+  bool in;
+  __device__ __forceinline__ void load(const bf16_t* Bb, const bf16_t* Cb, int n, int64_t t0, int64_t L, int p) {
+    const bf16_t* row = ((p < kTile / 8) ? Bb : Cb) + (int64_t)n * L;
+    const int q8 = p & (kTile / 8 - 1);
+    const int64_t t = t0 + 8 * q8;
+    in = t < L;
+    w = *reinterpret_cast<const uint4*>(row + (in ? t : L - 8));
+  }
+  __device__ __forceinline__ void store(float4 (*rows)[kRowF4], int p) const {
+    const int q8 = p & (kTile / 8 - 1);
+    float4* dst = rows[p >= kTile / 8];
+    float4 lo = make_float4(bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y));
+    float4 hi = make_float4(bf16_lo(w.z), bf16_hi(w.z), bf16_lo(w.w), bf16_hi(w.w));
+    if (!in) lo = hi = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    dst[stage_slot(2 * q8)] = lo;
+    dst[stage_slot(2 * q8 + 1)] = hi;
+  }
+};
+
+// The lane's 16 tokens of one row, as two 8-token halves; a half past the end
+// of the sequence (seqlen is a multiple of 8) reads the row's last 8 tokens
+// instead and is flagged out.
+template <typename IoT>
+__device__ __forceinline__ void load_chunk(const IoT* row, int64_t tl, int64_t L, float (&v)[kTok]) {
+  Io<IoT>::load8(row + (tl < L ? tl : L - 8), v);
+  Io<IoT>::load8(row + (tl + 8 < L ? tl + 8 : L - 8), v + 8);
+}
+
+template <typename IoT, bool kZ, bool kSp>
+__global__ void __launch_bounds__(64 * kMaxWaves) scan_chunked_kernel(ChunkedScanArgs a) {
+  // [state of the stage][buffer][B, C][slot]: 128 KB.  One state's B and C
+  // rows of both buffers lie within 16 KB, so its reads take immediate
+  // offsets from one address.
+  __shared__ float4 stage[kStageStates][2][2][kRowF4];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int W = blockDim.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t L = a.seqlen;
+  const int64_t groups = (a.dim + W - 1) / W;
+  const int64_t bb = blockIdx.x / groups;
+  const int64_t d = (blockIdx.x % groups) * W + wave;
+  const bool live = d < a.dim;              // a ragged block's extra waves compute a real channel, store nothing
+  const int64_t dc = live ? d : a.dim - 1;
+  const int64_t row = (bb * a.dim + dc) * L;
+  const IoT* u = static_cast<const IoT*>(a.u) + row;
+  const IoT* dlt = static_cast<const IoT*>(a.delta) + row;
+  const IoT* zr = kZ ? static_cast<const IoT*>(a.z) + row : nullptr;
+  IoT* yr = static_cast<IoT*>(a.y) + row;
+  const IoT* Bb = static_cast<const IoT*>(a.B) + bb * kN * L;
+  const IoT* Cb = static_cast<const IoT*>(a.C) + bb * kN * L;
+  const bool stager = tid < Stager<IoT>::kPieces;
+
+  // Lane n < 16 holds A[n] log2(e) and the running carry of state n; the
+  // state loop reads them with readlane and updates the carry with writelane.
+  const int ln = lane < kN ? lane : 0;
+  const float A2v = a.A[dc * kN + ln] * kLog2e;
+  float carry_v = a.h0 ? a.h0[(bb * a.dim + dc) * kN + ln] : 0.0f;
+  const float bias = a.bias ? a.bias[dc] : 0.0f;
+  const float Dd = a.D ? a.D[dc] : 0.0f;
+  const int64_t ntiles = (L + kTile - 1) / kTile;
+
+  // Stage 0: tile 0, states 0..7, into buffer 0.
+  if (stager) {
+#pragma unroll 1
+    for (int i = 0; i < kStageStates; ++i) {
+      Stager<IoT> s;
+      s.load(Bb, Cb, i, 0, L, tid);
+      s.store(stage[i][0], tid);
+    }
+  }
+  lds_barrier();
+
+  // The lane's rows of u and delta for the next tile, and of z for this one,
+  // are loaded two states before the end of each tile (tile 0's before the
+  // loop), so their latency is covered by the last two states' work.
+  float un[kTok], rn[kTok], zc[kTok];
+  load_chunk(u, lane * kTok, L, un);
+  load_chunk(dlt, lane * kTok, L, rn);
+
+#pragma unroll 1
+  for (int64_t tile = 0; tile < ntiles; ++tile) {
+    const int64_t t0 = tile * kTile;
+    const int64_t tl = t0 + lane * kTok;
+    const bool in0 = tl < L, in1 = tl + 8 < L;
+
+    float x[kTok], dv[kTok], yv[kTok];
+#pragma unroll
+    for (int j = 0; j < kTok; ++j) {
+      const float v = rn[j] + bias;
+      float dj = kSp ? softplus_f32(v) : v;
+      if (!(j < 8 ? in0 : in1)) dj = 0.0f;  // tokens past the end: the identity map
+      dv[j] = dj;
+      x[j] = dj * un[j];
+      yv[j] = Dd * un[j];
+    }
+    float sd = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kTok; ++j) sd += dv[j];
+
+    // State n of stage h (buffer h; its B/C rows are entry i of the stage).
+    // While it runs, the stager threads move entry i of the next stage (this
+    // tile's states 8..15, or the next tile's 0..7) into buffer 1 - h.
+    auto run_state = [&](const int h, const int i) {
+      const int n = h * kStageStates + i;
+      const bool next = h == 0 || tile + 1 < ntiles;
+      const int64_t nt0 = h == 0 ? t0 : t0 + kTile;
+      Stager<IoT> s;
+      if (next && stager) s.load(Bb, Cb, (1 - h) * kStageStates + i, nt0, L, tid);
+
+      float Bv[kTok];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 t = stage[i][h][0][q * 64 + lane];
+        Bv[4 * q] = t.x; Bv[4 * q + 1] = t.y; Bv[4 * q + 2] = t.z; Bv[4 * q + 3] = t.w;
+      }
+      const float An = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(A2v), n));
+      const float cn = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(carry_v), n));
+      float dA[kTok], dBu[kTok];
+#pragma unroll
+      for (int j = 0; j < kTok; ++j) {
+        dA[j] = exp2_hw(An * dv[j]);
+        dBu[j] = Bv[j] * x[j];
+      }
+      float b = dBu[0];
+#pragma unroll
+      for (int j = 1; j < kTok; ++j) b = __builtin_fmaf(dA[j], b, dBu[j]);
+      float ag = exp2_hw(An * sd);
+      lane_scan(ag, b);
+      // State after this lane's chunk; shifted one lane up it is the state
+      // before the chunk (lane 0: the carry), and lane 63's is the carry
+      // of the next tile.
+      const float hend = __builtin_fmaf(ag, cn, b);
+      float hc = dpp<kDppWaveShr1, 0xf>(cn, hend);
+      const float cnew = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(hend), 63));
+      carry_v = lane == n ? cnew : carry_v;
+
+      float Cv[kTok];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 t = stage[i][h][1][q * 64 + lane];
+        Cv[4 * q] = t.x; Cv[4 * q + 1] = t.y; Cv[4 * q + 2] = t.z; Cv[4 * q + 3] = t.w;
+      }
+#pragma unroll
+      for (int j = 0; j < kTok; ++j) {
+        hc = __builtin_fmaf(dA[j], hc, dBu[j]);
+        yv[j] = __builtin_fmaf(Cv[j], hc, yv[j]);
+      }
+      if (next && stager) s.store(stage[i][1 - h], tid);
+    };
+
+#pragma unroll 1
+    for (int i = 0; i < kStageStates; ++i) run_state(0, i);
+    lds_barrier();
+#pragma unroll 1
+    for (int i = 0; i < kStageStates - 2; ++i) run_state(1, i);
+    {
+      const int64_t tn = (tile + 1 < ntiles ? t0 + kTile : t0) + lane * kTok;
+      load_chunk(u, tn, L, un);
+      load_chunk(dlt, tn, L, rn);
+      if (kZ) load_chunk(zr, tl, L, zc);
+    }
+#pragma unroll 1
+    for (int i = kStageStates - 2; i < kStageStates; ++i) run_state(1, i);
+    lds_barrier();
+
+    if (kZ) {
+#pragma unroll
+      for (int j = 0; j < kTok; ++j) yv[j] *= silu_f32(zc[j]);
+    }
+    if (live) {
+      if (in0) Io<IoT>::store8(yr + tl, yv);
+      if (in1) Io<IoT>::store8(yr + tl + 8, yv + 8);
+    }
+  }
+
+  if (live && a.last_state && lane < kN) a.last_state[(bb * a.dim + dc) * kN + lane] = carry_v;
+}
+
+template <typename IoT, bool kZ, bool kSp>
+hipError_t launch_t(const ChunkedScanArgs& a, hipStream_t st) {
+  const int W = ssmi_chunked_block_waves(a.batch * a.dim);
+  const int64_t blocks = a.batch * ((a.dim + W - 1) / W);
+  hipLaunchKernelGGL((scan_chunked_kernel<IoT, kZ, kSp>), dim3((unsigned)blocks), dim3(64 * W), 0, st, a);
+  return hipGetLastError();
+}
+
+template <typename IoT>
+hipError_t launch_io(const ChunkedScanArgs& a, bool sp, hipStream_t st) {
+  if (a.z) return sp ? launch_t<IoT, true, true>(a, st) : launch_t<IoT, true, false>(a, st);
+  return sp ? launch_t<IoT, false, true>(a, st) : launch_t<IoT, false, false>(a, st);
+}
+
+}  // namespace
+
+int ssmi_chunked_block_waves(int64_t channels) {
+  // One block per CU (its LDS is 128 KB): pick the block size whose blocks
+  // fill the 256 CUs most evenly, the larger on ties.
+  constexpr int64_t kCUs = 256;
+  int best = kMaxWaves;
+  double best_use = -1.0;
+  for (int w = kMaxWaves; w >= kMinWaves; --w) {
+    const int64_t blocks = (channels + w - 1) / w;
+    const int64_t rounds = (blocks + kCUs - 1) / kCUs;
+    const double use = (double)channels / (double)(rounds * kCUs * w);
+    if (use > best_use + 1e-9) {
+      best_use = use;
+      best = w;
+    }
+  }
+  return best;
+}
+
+hipError_t ssmi_chunked_launch(const ChunkedScanArgs& a, bool bf16, bool softplus, hipStream_t st) {
+  return bf16 ? launch_io<bf16_t>(a, softplus, st) : launch_io<float>(a, softplus, st);
+}

@@ -49,6 +49,8 @@
 #include <mutex>
 
 #include "ssm_scan.h"
+#include "device_common.h"
+#include "scan_chunked.h"
 
 namespace {
 
@@ -56,39 +58,13 @@ namespace {
 // Device helpers
 // ----------------------------------------------------------------------------
 
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kInv2Pi = 0.15915494309189535f;  // 1 / (2 pi): radians to turns
 constexpr int kChunk = 8;           // tokens per lane per inner iteration
 constexpr int kWaveThreads = 64;
 constexpr int kBlockThreads = 256;  // 4 independent waves per block
 constexpr int kWavesPerBlock = kBlockThreads / kWaveThreads;
 
-typedef uint16_t bf16_t;  // bit pattern of a bfloat16
 
-__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
-__device__ __forceinline__ float log2_hw(float x) { return __builtin_amdgcn_logf(x); }
-__device__ __forceinline__ float rcp_hw(float x) { return __builtin_amdgcn_rcpf(x); }
-
-// softplus(x) = log(1 + e^x) = max(x, 0) + log1p(e), e = e^-|x| in (0, 1].
-// w = 1 + e is rounded, but for w in [1, 2] its rounding error c = (w - 1) - e
-// is exact (w - 1 is exact there, and so is the difference of two nearby
-// floats), and log1p(e) = log(w) - c / w + O(c^2).  Using c for c / w errs by
-// at most c / 2 <= 2^-25 absolute, which is below the rounding of the result
-// except where the result is below 2^-24 -- and there (w == 1, so c = -e)
-// the formula returns e itself.  Emulated in fp32 with correctly rounded
-// exp2/log2 over x in [-40, 40] it stays within 2e-6 relative of the fp64
-// log1p(exp(x)), like the Kahan form log(w) * e / (w - 1), with one
-// transcendental and four VALU ops fewer.
-__device__ __forceinline__ float softplus_f32(float x) {
-  const float e = exp2_hw(-__builtin_fabsf(x) * kLog2e);  // in (0, 1]
-  const float w = 1.0f + e;                               // in [1, 2]
-  const float c = (w - 1.0f) - e;                         // rounding error of w, exact
-  return __builtin_fmaf(log2_hw(w), kLn2, __builtin_fmaxf(x, 0.0f) - c);
-}
-
-// silu(z) = z * sigmoid(z) = z / (1 + e^-z)
-__device__ __forceinline__ float silu_f32(float z) { return z * rcp_hw(1.0f + exp2_hw(-z * kLog2e)); }
 
 // Exact zero-order hold for B.  Holding u over a step of length Delta and
 // solving dh/dt = a h + B u exactly gives the input term (e^{Delta a} - 1)/a * u
@@ -139,62 +115,6 @@ __device__ __forceinline__ float zoh_factor_da(float t, float e, float dl, float
   return __builtin_fabsf(t) < kZohDaSeriesT ? series : closed;
 }
 
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
-template <typename IoT>
-struct Io;
-
-template <>
-struct Io<float> {
-  __device__ static __forceinline__ float load1(const float* p) { return *p; }
-  __device__ static __forceinline__ void store1(float* p, float v) { *p = v; }
-  // 8 consecutive elements; p is 16-byte aligned.
-  __device__ static __forceinline__ void load8(const float* p, float out[8]) {
-    float4 a = reinterpret_cast<const float4*>(p)[0];
-    float4 b = reinterpret_cast<const float4*>(p)[1];
-    out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
-    out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
-  }
-  __device__ static __forceinline__ void store8(float* p, const float v[8]) {
-    reinterpret_cast<float4*>(p)[0] = make_float4(v[0], v[1], v[2], v[3]);
-    reinterpret_cast<float4*>(p)[1] = make_float4(v[4], v[5], v[6], v[7]);
-  }
-  // 4 consecutive elements; p is 16-byte aligned.
-  __device__ static __forceinline__ void load4(const float* p, float out[4]) {
-    float4 a = *reinterpret_cast<const float4*>(p);
-    out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
-  }
-};
-
-template <>
-struct Io<bf16_t> {
-  __device__ static __forceinline__ float load1(const bf16_t* p) { return __uint_as_float((uint32_t)*p << 16); }
-  __device__ static __forceinline__ void store1(bf16_t* p, float v) {
-    __bf16 r = (__bf16)v;  // round to nearest even (v_cvt_pk_bf16_f32)
-    *p = __builtin_bit_cast(bf16_t, r);
-  }
-  __device__ static __forceinline__ void load8(const bf16_t* p, float out[8]) {
-    uint4 w = *reinterpret_cast<const uint4*>(p);
-    out[0] = bf16_lo(w.x); out[1] = bf16_hi(w.x); out[2] = bf16_lo(w.y); out[3] = bf16_hi(w.y);
-    out[4] = bf16_lo(w.z); out[5] = bf16_hi(w.z); out[6] = bf16_lo(w.w); out[7] = bf16_hi(w.w);
-  }
-  __device__ static __forceinline__ uint32_t pack2(float lo, float hi) {
-    uint32_t a = __builtin_bit_cast(bf16_t, (__bf16)lo);
-    uint32_t b = __builtin_bit_cast(bf16_t, (__bf16)hi);
-    return a | (b << 16);
-  }
-  __device__ static __forceinline__ void store8(bf16_t* p, const float v[8]) {
-    uint4 w;
-    w.x = pack2(v[0], v[1]); w.y = pack2(v[2], v[3]); w.z = pack2(v[4], v[5]); w.w = pack2(v[6], v[7]);
-    *reinterpret_cast<uint4*>(p) = w;
-  }
-  // 4 consecutive elements; p is 8-byte aligned.
-  __device__ static __forceinline__ void load4(const bf16_t* p, float out[4]) {
-    uint2 w = *reinterpret_cast<const uint2*>(p);
-    out[0] = bf16_lo(w.x); out[1] = bf16_hi(w.x); out[2] = bf16_lo(w.y); out[3] = bf16_hi(w.y);
-  }
-};
 
 // Wave-uniform loads through the scalar data cache.  Reading through the
 // constant address space tells the compiler the memory is not written by this
@@ -227,14 +147,6 @@ __device__ __forceinline__ void settle_vgprs(uint32_t (&v)[K]) {
   for (int i = 0; i < K; ++i) asm volatile("" : "+v"(v[i]));
 }
 
-// Workgroup barrier that orders LDS only: the LDS writes before it are
-// visible to every wave after it, while global loads and stores stay in
-// flight (a full __syncthreads would also wait for those).
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
 
 template <typename IoT>
 struct Uni;
@@ -3324,8 +3236,24 @@ ScanArgs scan_args(const Shape&, int64_t batch, int64_t dim, int64_t dstate, int
 // Plans and launches the scan of a validated call.  Nothing is allocated:
 // the segmented path keeps its aggregates and carries in y (seg_slot_store).
 // conv: the conv is fused (a.u holds x).
+// The chunked kernel (scan_chunked.hip) takes the shapes the single-pass
+// kernel leaves to the segmented path, when it implements them: dstate 16,
+// whole 16-byte rows, the Delta * B rule, no fused conv.
+bool use_chunked(const Plan& p, int64_t dstate, bool vec, bool conv, bool zoh) {
+  return !p.split && vec && dstate == 16 && !conv && !zoh;
+}
+
 ssm_status_t run_scan(ScanArgs& a, const Shape& sh, ssm_dtype_t io, bool vec, bool sp, bool conv, hipStream_t hs) {
   const Plan plan = make_plan(sh, a.batch, a.dim, a.dstate, a.seqlen, io);
+  if (use_chunked(plan, a.dstate, vec, conv, a.zoh != 0)) {
+    ChunkedScanArgs c;
+    c.u = a.u; c.delta = a.delta; c.A = a.A; c.B = a.B; c.C = a.C; c.D = a.D; c.z = a.z; c.bias = a.bias;
+    c.h0 = a.h0; c.y = a.y; c.last_state = a.last_state;
+    c.batch = a.batch; c.dim = a.dim; c.seqlen = a.seqlen;
+    hipError_t e = ssmi_chunked_launch(c, io == SSM_BF16, sp, hs);
+    if (e != hipSuccess) return hip_fail(e);
+    return SSM_OK;
+  }
   a.groups = plan.groups; a.segments = plan.segments; a.seg_len = plan.seg_len;
   a.agg_per_seg = plan.agg_per_seg; a.agg_len = plan.seg_len / plan.agg_per_seg;
   hipError_t e = (io == SSM_BF16) ? launch_scan<bf16_t>(a, plan, hs, vec, sp, conv)
@@ -3356,19 +3284,29 @@ const char* ssm_status_string(ssm_status_t s) {
   return "unknown status";
 }
 
-ssm_status_t ssm_scan_fwd_plan(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, ssm_dtype_t io,
-                               int* path, int64_t* segments, int64_t* segment_len, int64_t* scratch_bytes) {
+ssm_status_t ssm_scan_fwd_plan_ex(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, ssm_dtype_t io,
+                                  ssm_disc_t disc, int64_t conv_width, int* path, int64_t* segments,
+                                  int64_t* segment_len, int64_t* scratch_bytes) {
   Shape sh;
   ssm_status_t st = shape_of(batch, dim, dstate, seqlen, io, &sh);
   if (st != SSM_OK) return st;
+  if ((disc != SSM_DISC_DELTA_B && disc != SSM_DISC_ZOH) || conv_width < 0 || conv_width > 4)
+    return SSM_ERR_UNSUPPORTED;
   Plan p = make_plan(sh, batch, dim, dstate, seqlen, io);
   const bool vec = seqlen % kChunk == 0 && (dstate == 4 || dstate == 8 || dstate == 16) &&
                    dstate * seqlen * (int64_t)io_size(io) < ((int64_t)1 << 31);
-  if (path) *path = p.split && vec ? SSM_PATH_SPLIT : (vec ? SSM_PATH_SEGMENTED : SSM_PATH_GENERIC);
-  if (segments) *segments = p.segments;
-  if (segment_len) *segment_len = p.seg_len;
+  const bool chunked = use_chunked(p, dstate, vec, conv_width > 0, disc == SSM_DISC_ZOH);
+  if (path) *path = p.split && vec ? SSM_PATH_SPLIT : (chunked ? SSM_PATH_CHUNKED : (vec ? SSM_PATH_SEGMENTED : SSM_PATH_GENERIC));
+  if (segments) *segments = chunked ? 1 : p.segments;
+  if (segment_len) *segment_len = chunked ? seqlen : p.seg_len;
   if (scratch_bytes) *scratch_bytes = p.scratch_bytes;
   return SSM_OK;
+}
+
+ssm_status_t ssm_scan_fwd_plan(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, ssm_dtype_t io,
+                               int* path, int64_t* segments, int64_t* segment_len, int64_t* scratch_bytes) {
+  return ssm_scan_fwd_plan_ex(batch, dim, dstate, seqlen, io, SSM_DISC_DELTA_B, 0, path, segments, segment_len,
+                              scratch_bytes);
 }
 
 ssm_status_t ssm_scan_fwd_ex(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, ssm_dtype_t io,

@@ -359,9 +359,15 @@ def test_plan(lib):
     path, seg, seglen, scratch = binding.scan_plan(4, 4096, 16, 4096, torch.bfloat16, with_path=True)
     assert (path, seg, seglen, scratch) == ("split", 1, 4096, 0)          # Mamba-1.4B layer: single pass
     assert binding.scan_plan(8, 1536, 16, 2048, torch.float32, with_path=True) == ("split", 1, 2048, 0)
-    path, seg, seglen, scratch = binding.scan_plan(1, 2560, 16, 131072, torch.float32, with_path=True)
-    # No path takes scratch: the segment aggregates and carries live in y.  The
-    # last segment ends at seqlen and holds at least 64 tokens.
+    # Long sequence: the chunked kernel for the plain scan; exact zero-order
+    # hold and the fused conv run segmented.  No path takes scratch: the
+    # segment aggregates and carries live in y.  The last segment ends at
+    # seqlen and holds at least 64 tokens.
+    assert binding.scan_plan(1, 2560, 16, 131072, torch.float32, with_path=True) == ("chunked", 1, 131072, 0)
+    assert binding.scan_plan(1, 2560, 16, 131072, torch.bfloat16, with_path=True) == ("chunked", 1, 131072, 0)
+    assert binding.scan_plan(1, 2560, 8, 131072, torch.float32, with_path=True)[0] == "segmented"
+    assert binding.scan_plan(1, 2560, 16, 131072, torch.float32, with_path=True, conv_width=4)[0] == "segmented"
+    path, seg, seglen, scratch = binding.scan_plan(1, 2560, 16, 131072, torch.float32, with_path=True, disc="zoh")
     assert path == "segmented" and seg > 1 and scratch == 0
     assert (seg - 1) * seglen < 131072 and 131072 - (seg - 1) * seglen >= 64
     path, seg, seglen, scratch = binding.scan_plan(1, 64, 16, 4097, torch.float32, with_path=True)
@@ -371,6 +377,10 @@ def test_plan(lib):
     assert binding.scan_plan(1, 16, 4, 63, torch.float32, with_path=True)[0] == "generic"
     assert binding.scan_plan(256, 64, 5, 64, torch.float32, with_path=True)[0] == "generic"
     assert binding.scan_plan(2, 8, 16, 16, torch.float32) == (1, 16, 0)
+    path, seg = ctypes.c_int(), ctypes.c_int64()
+    for disc, width in ((2, 0), (-1, 0), (0, 5), (0, -1)):
+        st = lib.ssm_scan_fwd_plan_ex(1, 64, 16, 64, 0, disc, width, ctypes.byref(path), ctypes.byref(seg), None, None)
+        assert st == 8   # SSM_ERR_UNSUPPORTED
 
 
 def test_product_never_uses_the_oracle():

@@ -124,7 +124,7 @@ def test_segmented_aggregate_pieces_with_conv(io):
     conv from the four inputs before it.  Checked on sampled channels."""
     b, d, n, l = 1, 2560, 16, 32768
     dt = torch.float32 if io == "f32" else torch.bfloat16
-    assert binding.scan_plan(b, d, n, l, dt, with_path=True) == ("segmented", 52, 640, 0)
+    assert binding.scan_plan(b, d, n, l, dt, with_path=True, conv_width=4) == ("segmented", 52, 640, 0)
     say("conv with aggregate pieces io=%s" % io)
     x, w, cb, prev = conv_inputs(b, d, n, l, io, 4, 700, h0=True)
     y, last, uo, _ = run(x, w, cb, prev, True)

@@ -94,11 +94,13 @@ def test_split_prefill_in_a_graph(io):
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 @pytest.mark.parametrize("conv", [False, True])
 def test_segmented_prefill_in_a_graph(io, conv):
-    """The segmented path (three launches, aggregates and carries in y) and the
-    conv fused into it allocate nothing, so a capture holds only launches."""
+    """The chunked path (the plain scan) and the segmented path with the conv
+    fused into it (three launches, aggregates and carries in y) allocate
+    nothing, so a capture holds only launches."""
     b, d, n, l = 1, 128, 16, 4096
     dt = torch.float32 if io == "f32" else torch.bfloat16
-    assert binding.scan_plan(b, d, n, l, dt, with_path=True)[1] > 1
+    path, seg = binding.scan_plan(b, d, n, l, dt, with_path=True, conv_width=4 if conv else 0)[:2]
+    assert (path, seg > 1) == (("segmented", True) if conv else ("chunked", False))
     x = inputs.make_scan_inputs(b, d, n, l, io=io, seed=78, h0=True)
     t = inputs.to_torch(x, DEV)
     w = torch.from_numpy((0.5 * np.random.default_rng(79).standard_normal((d, 4))).astype(np.float32)).to(DEV)

@@ -125,8 +125,11 @@ PIECE_CASES = [("f32", 16, "delta_b"), ("bf16", 16, "delta_b"), ("f32", 5, "delt
 def test_segmented_aggregate_pieces(io, n, disc):
     b, d, l = 1, 2560, 32768
     dt = torch.float32 if io == "f32" else torch.bfloat16
-    path, seg, seglen, scratch = binding.scan_plan(b, d, n, l, dt, with_path=True)
-    assert (seg, seglen, scratch) == (52, 640, 0) and path == ("segmented" if n in (4, 8, 16) else "generic")
+    path, seg, seglen, scratch = binding.scan_plan(b, d, n, l, dt, with_path=True, disc=disc)
+    if n == 16 and disc == "delta_b":   # the plain rule at dstate 16 runs the chunked kernel instead
+        assert (path, seg, seglen, scratch) == ("chunked", 1, l, 0)
+    else:
+        assert (seg, seglen, scratch) == (52, 640, 0) and path == ("segmented" if n in (4, 8, 16) else "generic")
     x = inputs.make_scan_inputs(b, d, n, l, io=io, seed=2100 + n, h0=True)
     say("aggregate pieces %s n=%d %s path=%s" % (io, n, disc, path))
     t = inputs.to_torch(x, DEV)
@@ -141,20 +144,27 @@ def test_segmented_aggregate_pieces(io, n, disc):
     check(np64(last[0, di]), hr, "f32", "last_state")
 
 
-@pytest.mark.parametrize("io", ["f32", "bf16"])
-def test_segmented_aggregate_pieces_batch_rows_ragged_dim(io):
-    """Two batch rows of 1300 channels (21 groups, the last 20 channels wide)
-    over 31360 tokens: 49 segments of 640 tokens, each aggregated in two
-    pieces (42 x 48 x 2 = 4032 waves), with an initial state; sampled
-    channels of both rows, the ragged group included."""
+@pytest.mark.parametrize("io,disc", [("f32", "delta_b"), ("bf16", "delta_b"), ("f32", "zoh"), ("bf16", "zoh")])
+def test_long_rows_two_batch_rows_ragged_dim(io, disc):
+    """Two batch rows of 1300 channels over 31360 tokens, with an initial
+    state; sampled channels of both rows, the ragged channel blocks included.
+    The Delta*B rule runs the chunked kernel (31 tiles, the last 640 tokens
+    long; the last block of each row only partly filled); exact zero-order
+    hold runs segmented: 49 segments of 640 tokens, each aggregated in two
+    pieces (42 x 48 x 2 = 4032 waves, the last group 20 channels wide)."""
     b, d, n, l = 2, 1300, 16, 31360
     dt = torch.float32 if io == "f32" else torch.bfloat16
-    assert binding.scan_plan(b, d, n, l, dt, with_path=True) == ("segmented", 49, 640, 0)
+    want = ("chunked", 1, l, 0) if disc == "delta_b" else ("segmented", 49, 640, 0)
+    assert binding.scan_plan(b, d, n, l, dt, with_path=True, disc=disc) == want
     x = inputs.make_scan_inputs(b, d, n, l, io=io, seed=2200, h0=True)
-    say("aggregate pieces, 2 batch rows, ragged dim, io=%s" % io)
-    y, last = gpu_scan(x)
-    ch = inputs.sample_channels(b, d, 8, seed=22) + [(0, d - 1), (1, d - 20), (0, d - 21)]
-    yr, hr = oracle.scan_channels_f64(ch, x.u, x.delta, x.A, x.B, x.C, x.D, x.z, x.delta_bias, x.softplus, x.h0)
+    say("long rows, 2 batch rows, ragged dim, io=%s disc=%s path=%s" % (io, disc, want[0]))
+    t = inputs.to_torch(x, DEV)
+    y, last = binding.scan_fwd_ex(t["u"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
+                                  delta_bias=t["delta_bias"], delta_softplus=x.softplus, h0=t["h0"], disc=disc)
+    torch.cuda.synchronize()
+    ch = inputs.sample_channels(b, d, 8, seed=22) + [(0, d - 1), (1, d - 2), (1, d - 20), (0, d - 21)]
+    yr, hr = oracle.scan_channels_f64(ch, x.u, x.delta, x.A, x.B, x.C, x.D, x.z, x.delta_bias, x.softplus, x.h0,
+                                      zoh=disc == "zoh")
     bi = torch.tensor([c[0] for c in ch], device=DEV)
     di = torch.tensor([c[1] for c in ch], device=DEV)
     check(np64(y[bi, di]), yr, io, "y")
@@ -242,7 +252,7 @@ def test_decode_varied_channels():
 # Flags, shapes, edge cases
 
 
-FLAG_SHAPES = [(2, 80, 16, 200), (1, 70, 16, 1000)]
+FLAG_SHAPES = [(2, 80, 16, 200), (1, 70, 16, 1000), (1, 70, 8, 1000)]   # chunked, chunked, segmented
 
 
 @pytest.mark.parametrize("io", ["f32", "bf16"])
@@ -283,20 +293,23 @@ def test_odd_shapes(io, shape):
     check(np64(last), hr, "f32", "last_state")
 
 
-def test_segmented_plan_is_exercised():
-    # The long-sequence workload takes the segmented (multi-launch) path, which
-    # allocates nothing: its aggregates and carries live in y.
-    seg, seglen, scratch = binding.scan_plan(1, 2560, 16, 131072, torch.float32)
-    assert seg > 1 and scratch == 0
+def test_long_sequence_plans():
+    # The long-sequence workload runs the chunked kernel (one launch, nothing
+    # but y and last_state written); under exact zero-order hold it runs
+    # segmented, with its aggregates and carries in y.  Neither takes scratch.
+    assert binding.scan_plan(1, 2560, 16, 131072, torch.float32, with_path=True) == ("chunked", 1, 131072, 0)
+    path, seg, seglen, scratch = binding.scan_plan(1, 2560, 16, 131072, torch.float32, with_path=True, disc="zoh")
+    assert path == "segmented" and seg > 1 and scratch == 0
 
 
 @pytest.mark.parametrize("io", ["f32", "bf16"])
-def test_h0_aliases_last_state(io):
-    b, d, n, l = 1, 96, 16, 4096
+@pytest.mark.parametrize("n,path", [(16, "chunked"), (8, "segmented")])
+def test_h0_aliases_last_state(io, n, path):
+    b, d, l = 1, 96, 4096
     x = inputs.make_scan_inputs(b, d, n, l, io=io, seed=9, h0=True)
-    assert binding.scan_plan(b, d, n, l, torch.float32)[0] > 1
+    assert binding.scan_plan(b, d, n, l, torch.float32, with_path=True)[0] == path
     t = inputs.to_torch(x, DEV)
-    say("h0 aliasing last_state io=%s" % io)
+    say("h0 aliasing last_state io=%s n=%d path=%s" % (io, n, path))
     state = t["h0"].clone()
     y, last = binding.scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
                                delta_bias=t["delta_bias"], delta_softplus=True, h0=state, last_state=state)
@@ -361,7 +374,9 @@ def test_misaligned_rows_segmented(io):
     kernel, with the segment slots in a y that is only element-aligned."""
     b, d, n, l = 1, 70, 16, 2000
     x = inputs.make_scan_inputs(b, d, n, l, io=io, seed=42, h0=True)
-    assert binding.scan_plan(b, d, n, l, torch.float32 if io == "f32" else torch.bfloat16)[0] > 1
+    # The plan (for aligned rows) is the chunked kernel; rows that are not
+    # 16-byte aligned run the per-token kernel over the segmented plan.
+    assert binding.scan_plan(b, d, n, l, torch.float32 if io == "f32" else torch.bfloat16, disc="zoh")[0] > 1
     t = inputs.to_torch(x, DEV)
     say("misaligned segmented io=%s" % io)
 
