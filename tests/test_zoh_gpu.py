@@ -85,7 +85,7 @@ SHAPES = [((192, 64, 16, 96), "split"), ((200, 64, 8, 40), "split"), ((256, 33, 
 def test_zoh_scan_paths(io, shape, path):
     b, d, n, l = shape
     dt = torch.float32 if io == "f32" else torch.bfloat16
-    assert binding.scan_plan(b, d, n, l, dt, with_path=True)[0] == path
+    assert binding.scan_plan(b, d, n, l, dt, with_path=True, disc="zoh")[0] == path
     for variant in ("workload", "awkward_A", "wide_steps"):
         say("zoh shape=%s io=%s path=%s variant=%s" % (shape, io, path, variant))
         x = inputs.make_scan_inputs(b, d, n, l, io=io, seed=3000 + n + l, h0=True)
