@@ -48,16 +48,17 @@ if ROOT not in sys.path:
 METRIC = "selective-scan HBM GB/s (% of MI355X peak) + (B·D·L)/s at Mamba-1.4B shape"
 
 # HBM bytes per call of the scan workloads measured with rocprofv3
-# (FETCH_SIZE x 1.9999 + WRITE_SIZE x 1.0, the factors a 1 GiB copy gives these
-# counters in the same run), valid only for the kernel source they were
-# measured on: when csrc/ssm_scan.hip changes, the figures are reported as null
-# until re-measured.  Keys are the workload indices of inputs.scan_config.
+# (FETCH_SIZE and WRITE_SIZE scaled by the factors a 1 GiB copy gives these
+# counters in the same run), valid only for the kernel sources they were
+# measured on (KERNEL_SOURCES, hashed together): when one changes, the figures
+# are reported as null until re-measured.  Keys are the workload indices of
+# inputs.scan_config.
 MEASURED_TRAFFIC = {
-    "source_sha256": "d6f7afa25ba9af40d8ff14f511c0f07faac5d8bfe5a00999ce588fdff5984fec",
+    "source_sha256": "8302f10fccfd77768ffbde0013b0442dbbf980e96c2bfabfd952588cc52b782b",
     "per_call": {
-        2: {"read_bytes": 485_540_677, "write_bytes": 138_099_072},
-        1: {"read_bytes": 359_717_095, "write_bytes": 103_020_656},
-        3: {"read_bytes": 7_089_722_783, "write_bytes": 1_384_078_840},
+        2: {"read_bytes": 485_954_709, "write_bytes": 137_361_104},
+        1: {"read_bytes": 359_336_816, "write_bytes": 102_650_480},
+        3: {"read_bytes": 4_515_520_357, "write_bytes": 1_344_975_200},
     },
 }
 HBM_PEAK_GBS = 8000.0
@@ -82,12 +83,22 @@ def decode_bytes(batch, dim, dstate, io_bytes):
             + dim * dstate * 4 + 2 * dim * 4)
 
 
+KERNEL_SOURCES = ("ssm_scan.hip", "scan_chunked.hip", "device_common.h")
+
+
+def kernel_source_digest():
+    """sha256 over the kernel sources (csrc/, in KERNEL_SOURCES order)."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, "selective_state_space_65_amd", "csrc", name), "rb").read())
+    return h.hexdigest()
+
+
 def measured_traffic(config):
     """Counter-measured HBM bytes per call (read + written), or None if the
-    kernel source changed since the measurement or the workload has none."""
-    import hashlib
-    src = os.path.join(ROOT, "selective_state_space_65_amd", "csrc", "ssm_scan.hip")
-    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    kernel sources changed since the measurement or the workload has none."""
+    digest = kernel_source_digest()
     m = MEASURED_TRAFFIC
     if digest != m["source_sha256"] or config not in m["per_call"]:
         return None
