@@ -24,7 +24,7 @@ struct ChunkedScanArgs {
 };
 
 // Channels per block (waves of one block) the launch uses for batch * dim
-// channels: 8 to 16, chosen so that the blocks cover the 256 compute units
+// channels: 8 to 12, chosen so that the blocks cover the 256 compute units
 // as evenly as possible.
 int ssmi_chunked_block_waves(int64_t channels);
 

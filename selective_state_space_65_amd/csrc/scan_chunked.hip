@@ -28,11 +28,14 @@
 //       3. runs its chunk again from that state with the kept Abar and
 //          Bbar u, adding C[n] h to each token's output.
 //     The carry then advances by the whole tile's map (lane 63's scan).
-//   * B and C are shared by every channel of a batch row: a block of 8 to 16
+//   * B and C are shared by every channel of a batch row: a block of 8 to 12
 //     waves (consecutive channels of one row) stages them through LDS, 8
-//     states x 1024 tokens of B and C (64 KB) per stage, double-buffered,
+//     states x 1024 tokens of B and C (68 KB with padding) per stage, double-buffered,
 //     one LDS barrier per stage.  The next stage is loaded one state row at
 //     a time by the first waves while the current one is computed.
+//   * Each lane's u and delta for the next tile, and z for this one, are
+//     loaded two states before the end of the tile, so their latency is
+//     covered by the last two states' work.
 //   * Nothing but y and last_state is written: no aggregate, carry or
 //     expanded state reaches memory, and the sequence is read once.
 //
@@ -50,7 +53,9 @@ constexpr int kN = 16;                   // states (dstate)
 constexpr int kTok = 16;                 // tokens per lane
 constexpr int kTile = 64 * kTok;         // tokens per wave tile
 constexpr int kStageStates = 8;          // states per LDS stage
-constexpr int kRowF4 = kTile / 4;        // float4 slots per staged row
+constexpr int kRowF4 = kTile / 4;        // float4 pieces of one row of a tile
+constexpr int kPartF4 = 64 + 4;          // float4 slots per part of a staged row (64 lanes + 64 B pad)
+constexpr int kSlotsF4 = 4 * kPartF4;    // float4 slots per staged row
 constexpr int kMinWaves = 8;             // the fp32 stager needs 512 threads
 constexpr int kMaxWaves = 12;
 
@@ -97,10 +102,13 @@ __device__ __forceinline__ void lane_scan(float& a, float& b) {
       : "+v"(b), "+v"(a));
 }
 
-// Staged B/C row layout: slot q * 64 + i holds tokens 4q .. 4q + 3 of lane
-// i's chunk (16 i + 4q ...), so each lane reads its chunk with four
-// conflict-free 16-byte LDS reads.
-__device__ __forceinline__ int stage_slot(int q4) { return (q4 & 3) * 64 + (q4 >> 2); }
+// Staged B/C row layout: slot q * kPartF4 + i holds tokens 4q .. 4q + 3 of
+// lane i's chunk (16 i + 4q ...), so each lane reads its chunk with four
+// conflict-free 16-byte LDS reads.  The 64-byte pad after each part puts the
+// four parts of one 16-token piece in different banks, so the stager's
+// writes (consecutive threads: consecutive 16-byte pieces of the row) are
+// conflict-free too.
+__device__ __forceinline__ int stage_slot(int q4) { return (q4 & 3) * kPartF4 + (q4 >> 2); }
 
 // Loads and stores one state's B and C rows of a stage.  Thread p < kPieces
 // moves one piece; pieces past the end of the sequence are zeros.
@@ -118,7 +126,7 @@ struct Stager<float> {
     const float4 w = *reinterpret_cast<const float4*>(row + (t < L ? t : L - 4));
     v = t < L ? w : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   }
-  __device__ __forceinline__ void store(float4 (*rows)[kRowF4], int p) const {
+  __device__ __forceinline__ void store(float4 (*rows)[kSlotsF4], int p) const {
     rows[p >= kRowF4][stage_slot(p & (kRowF4 - 1))] = v;
   }
 };
@@ -135,7 +143,7 @@ struct Stager<bf16_t> {
     in = t < L;
     w = *reinterpret_cast<const uint4*>(row + (in ? t : L - 8));
   }
-  __device__ __forceinline__ void store(float4 (*rows)[kRowF4], int p) const {
+  __device__ __forceinline__ void store(float4 (*rows)[kSlotsF4], int p) const {
     const int q8 = p & (kTile / 8 - 1);
     float4* dst = rows[p >= kTile / 8];
     float4 lo = make_float4(bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y));
@@ -157,10 +165,10 @@ __device__ __forceinline__ void load_chunk(const IoT* row, int64_t tl, int64_t L
 
 template <typename IoT, bool kZ, bool kSp>
 __global__ void __launch_bounds__(64 * kMaxWaves) scan_chunked_kernel(ChunkedScanArgs a) {
-  // [state of the stage][buffer][B, C][slot]: 128 KB.  One state's B and C
+  // [state of the stage][buffer][B, C][slot]: 136 KB.  One state's B and C
   // rows of both buffers lie within 16 KB, so its reads take immediate
   // offsets from one address.
-  __shared__ float4 stage[kStageStates][2][2][kRowF4];
+  __shared__ float4 stage[kStageStates][2][2][kSlotsF4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -241,7 +249,7 @@ __global__ void __launch_bounds__(64 * kMaxWaves) scan_chunked_kernel(ChunkedSca
       float Bv[kTok];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const float4 t = stage[i][h][0][q * 64 + lane];
+        const float4 t = stage[i][h][0][q * kPartF4 + lane];
         Bv[4 * q] = t.x; Bv[4 * q + 1] = t.y; Bv[4 * q + 2] = t.z; Bv[4 * q + 3] = t.w;
       }
       const float An = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(A2v), n));
@@ -268,7 +276,7 @@ __global__ void __launch_bounds__(64 * kMaxWaves) scan_chunked_kernel(ChunkedSca
       float Cv[kTok];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const float4 t = stage[i][h][1][q * 64 + lane];
+        const float4 t = stage[i][h][1][q * kPartF4 + lane];
         Cv[4 * q] = t.x; Cv[4 * q + 1] = t.y; Cv[4 * q + 2] = t.z; Cv[4 * q + 3] = t.w;
       }
 #pragma unroll
@@ -324,7 +332,7 @@ hipError_t launch_io(const ChunkedScanArgs& a, bool sp, hipStream_t st) {
 }  // namespace
 
 int ssmi_chunked_block_waves(int64_t channels) {
-  // One block per CU (its LDS is 128 KB): pick the block size whose blocks
+  // One block per CU (its LDS is 136 KB): pick the block size whose blocks
   // fill the 256 CUs most evenly, the larger on ties.
   constexpr int64_t kCUs = 256;
   int best = kMaxWaves;
