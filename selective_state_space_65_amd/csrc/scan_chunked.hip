@@ -32,7 +32,9 @@
 //     waves (consecutive channels of one row) stages them through LDS, 8
 //     states x 1024 tokens of B and C (68 KB with padding) per stage, double-buffered,
 //     one LDS barrier per stage.  The next stage is loaded one state row at
-//     a time by the first waves while the current one is computed.
+//     a time while the current one is computed: fp32 rows by four waves
+//     straight from global memory into LDS (no VGPRs, no VALU), bf16 rows
+//     through the VGPRs of the first four waves, widened on the way.
 //   * Each lane's u and delta for the next tile, and z for this one, are
 //     loaded two states before the end of the tile, so their latency is
 //     covered by the last two states' work.
@@ -43,6 +45,8 @@
 // two products and the state FMA) plus one FMA for the rerun and one for
 // C h; the lane scan adds about 20 instructions per state per 16 tokens.
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "device_common.h"
 #include "scan_chunked.h"
@@ -56,7 +60,7 @@ constexpr int kStageStates = 8;          // states per LDS stage
 constexpr int kRowF4 = kTile / 4;        // float4 pieces of one row of a tile
 constexpr int kPartF4 = 64 + 4;          // float4 slots per part of a staged row (64 lanes + 64 B pad)
 constexpr int kSlotsF4 = 4 * kPartF4;    // float4 slots per staged row
-constexpr int kMinWaves = 8;             // the fp32 stager needs 512 threads
+constexpr int kMinWaves = 8;             // the fp32 stagers are waves 2, 3, 6 and 7
 constexpr int kMaxWaves = 12;
 
 // DPP controls (GFX9 encoding).
@@ -110,29 +114,39 @@ __device__ __forceinline__ void lane_scan(float& a, float& b) {
 // conflict-free too.
 __device__ __forceinline__ int stage_slot(int q4) { return (q4 & 3) * kPartF4 + (q4 >> 2); }
 
-// Loads and stores one state's B and C rows of a stage.  Thread p < kPieces
-// moves one piece; pieces past the end of the sequence are zeros.
-template <typename IoT>
-struct Stager;
-
-template <>
-struct Stager<float> {
-  static constexpr int kPieces = 2 * kRowF4;  // float4 pieces of the B and C rows
-  float4 v;
-  __device__ __forceinline__ void load(const float* Bb, const float* Cb, int n, int64_t t0, int64_t L, int p) {
-    const float* row = ((p < kRowF4) ? Bb : Cb) + (int64_t)n * L;
-    const int q4 = p & (kRowF4 - 1);
-    const int64_t t = t0 + 4 * q4;
-    const float4 w = *reinterpret_cast<const float4*>(row + (t < L ? t : L - 4));
-    v = t < L ? w : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+// fp32 rows of a stage go straight from global memory into LDS
+// (global_load_lds_dwordx4: lane l's 16 bytes land at the LDS base + 16 l),
+// one 1 KB part of a row per instruction: part q of row `mat` holds tokens
+// 4q .. 4q + 3 of every lane's chunk.  Four waves (si = 0..3) issue two
+// parts per state each, so staging spends no VGPRs and no VALU stores.
+// Tokens past the end of the sequence are read from the row's last four and
+// zeroed in LDS once the parts have landed (a partial tile only).
+struct DmaStager {
+  __device__ static __forceinline__ void issue(const float* Bb, const float* Cb, int n, int64_t t0, int64_t L,
+                                               int si, int lane, float4 (*rows)[kSlotsF4]) {
+#pragma unroll
+    for (int k = 2 * si; k < 2 * si + 2; ++k) {
+      const int mat = k >> 2, q = k & 3;
+      const float* row = (mat ? Cb : Bb) + (int64_t)n * L;
+      const int64_t t = t0 + 16 * lane + 4 * q;
+      __builtin_amdgcn_global_load_lds(row + (t < L ? t : L - 4),
+                                       (__attribute__((address_space(3))) void*)&rows[mat][q * kPartF4], 16, 0, 0);
+    }
   }
-  __device__ __forceinline__ void store(float4 (*rows)[kSlotsF4], int p) const {
-    rows[p >= kRowF4][stage_slot(p & (kRowF4 - 1))] = v;
+  __device__ static __forceinline__ void zero_tail(int64_t t0, int64_t L, int si, int lane,
+                                                   float4 (*rows)[kSlotsF4]) {
+#pragma unroll
+    for (int k = 2 * si; k < 2 * si + 2; ++k) {
+      const int mat = k >> 2, q = k & 3;
+      if (t0 + 16 * lane + 4 * q >= L) rows[mat][q * kPartF4 + lane] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    }
   }
 };
 
-template <>
-struct Stager<bf16_t> {
+// bf16 rows of a stage are widened to fp32 on the way: thread p < kPieces
+// loads one 8-token piece of one state's B or C row into VGPRs and stores it
+// to LDS as two float4 slots; pieces past the end of the sequence are zeros.
+struct Bf16Stager {
   static constexpr int kPieces = 2 * kTile / 8;  // 8-token pieces of the B and C rows
   uint4 w;
   bool in;
@@ -165,10 +179,14 @@ __device__ __forceinline__ void load_chunk(const IoT* row, int64_t tl, int64_t L
 
 template <typename IoT, bool kZ, bool kSp>
 __global__ void __launch_bounds__(64 * kMaxWaves) scan_chunked_kernel(ChunkedScanArgs a) {
-  // [state of the stage][buffer][B, C][slot]: 136 KB.  One state's B and C
-  // rows of both buffers lie within 16 KB, so its reads take immediate
-  // offsets from one address.
-  __shared__ float4 stage[kStageStates][2][2][kSlotsF4];
+  // The two stage buffers, [state of the stage][B, C][slot], 68 KB each.  One
+  // state's B and C rows lie within 9 KB, so its reads take immediate offsets
+  // from one address.  Two arrays rather than one: the compiler can then tell
+  // the buffer being read from the one the DMA writes, and does not wait for
+  // the DMA before each read.
+  __shared__ float4 stage0[kStageStates][2][kSlotsF4];
+  __shared__ float4 stage1[kStageStates][2][kSlotsF4];
+  auto buf = [&](int b, int i) -> float4 (*)[kSlotsF4] { return b ? stage1[i] : stage0[i]; };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -187,7 +205,14 @@ __global__ void __launch_bounds__(64 * kMaxWaves) scan_chunked_kernel(ChunkedSca
   IoT* yr = static_cast<IoT*>(a.y) + row;
   const IoT* Bb = static_cast<const IoT*>(a.B) + bb * kN * L;
   const IoT* Cb = static_cast<const IoT*>(a.C) + bb * kN * L;
-  const bool stager = tid < Stager<IoT>::kPieces;
+  constexpr bool kDma = std::is_same<IoT, float>::value;
+  const bool stager = !kDma && tid < Bf16Stager::kPieces;          // bf16: waves 0..3
+  const bool dma = kDma && (wave & 3) >= 2 && wave < 8;            // fp32: waves 2, 3, 6, 7
+  const int si = ((wave >> 2) << 1) | (wave & 1);
+  const float* Bf = reinterpret_cast<const float*>(Bb);
+  const float* Cf = reinterpret_cast<const float*>(Cb);
+  const bf16_t* Bh = reinterpret_cast<const bf16_t*>(Bb);
+  const bf16_t* Ch = reinterpret_cast<const bf16_t*>(Cb);
 
   // Lane n < 16 holds A[n] log2(e) and the running carry of state n; the
   // state loop reads them with readlane and updates the carry with writelane.
@@ -199,12 +224,21 @@ __global__ void __launch_bounds__(64 * kMaxWaves) scan_chunked_kernel(ChunkedSca
   const int64_t ntiles = (L + kTile - 1) / kTile;
 
   // Stage 0: tile 0, states 0..7, into buffer 0.
+  if (dma) {
+#pragma unroll 1
+    for (int i = 0; i < kStageStates; ++i) DmaStager::issue(Bf, Cf, i, 0, L, si, lane, stage0[i]);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (kTile > L) {
+#pragma unroll 1
+      for (int i = 0; i < kStageStates; ++i) DmaStager::zero_tail(0, L, si, lane, stage0[i]);
+    }
+  }
   if (stager) {
 #pragma unroll 1
     for (int i = 0; i < kStageStates; ++i) {
-      Stager<IoT> s;
-      s.load(Bb, Cb, i, 0, L, tid);
-      s.store(stage[i][0], tid);
+      Bf16Stager s;
+      s.load(Bh, Ch, i, 0, L, tid);
+      s.store(stage0[i], tid);
     }
   }
   lds_barrier();
@@ -237,19 +271,20 @@ __global__ void __launch_bounds__(64 * kMaxWaves) scan_chunked_kernel(ChunkedSca
     for (int j = 0; j < kTok; ++j) sd += dv[j];
 
     // State n of stage h (buffer h; its B/C rows are entry i of the stage).
-    // While it runs, the stager threads move entry i of the next stage (this
-    // tile's states 8..15, or the next tile's 0..7) into buffer 1 - h.
+    // While it runs, the stagers move entry i of the next stage (this tile's
+    // states 8..15, or the next tile's 0..7) into buffer 1 - h.
     auto run_state = [&](const int h, const int i) {
       const int n = h * kStageStates + i;
       const bool next = h == 0 || tile + 1 < ntiles;
       const int64_t nt0 = h == 0 ? t0 : t0 + kTile;
-      Stager<IoT> s;
-      if (next && stager) s.load(Bb, Cb, (1 - h) * kStageStates + i, nt0, L, tid);
+      Bf16Stager s;
+      if (next && stager) s.load(Bh, Ch, (1 - h) * kStageStates + i, nt0, L, tid);
+      if (next && dma) DmaStager::issue(Bf, Cf, (1 - h) * kStageStates + i, nt0, L, si, lane, buf(1 - h, i));
 
       float Bv[kTok];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const float4 t = stage[i][h][0][q * kPartF4 + lane];
+        const float4 t = buf(h, i)[0][q * kPartF4 + lane];
         Bv[4 * q] = t.x; Bv[4 * q + 1] = t.y; Bv[4 * q + 2] = t.z; Bv[4 * q + 3] = t.w;
       }
       const float An = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(A2v), n));
@@ -276,7 +311,7 @@ __global__ void __launch_bounds__(64 * kMaxWaves) scan_chunked_kernel(ChunkedSca
       float Cv[kTok];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const float4 t = stage[i][h][1][q * kPartF4 + lane];
+        const float4 t = buf(h, i)[1][q * kPartF4 + lane];
         Cv[4 * q] = t.x; Cv[4 * q + 1] = t.y; Cv[4 * q + 2] = t.z; Cv[4 * q + 3] = t.w;
       }
 #pragma unroll
@@ -284,11 +319,16 @@ __global__ void __launch_bounds__(64 * kMaxWaves) scan_chunked_kernel(ChunkedSca
         hc = __builtin_fmaf(dA[j], hc, dBu[j]);
         yv[j] = __builtin_fmaf(Cv[j], hc, yv[j]);
       }
-      if (next && stager) s.store(stage[i][1 - h], tid);
+      if (next && stager) s.store(buf(1 - h, i), tid);
+      if (next && dma && nt0 + kTile > L) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        DmaStager::zero_tail(nt0, L, si, lane, buf(1 - h, i));
+      }
     };
 
 #pragma unroll 1
     for (int i = 0; i < kStageStates; ++i) run_state(0, i);
+    if (kDma) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's DMA parts have landed
     lds_barrier();
 #pragma unroll 1
     for (int i = 0; i < kStageStates - 2; ++i) run_state(1, i);
@@ -300,6 +340,7 @@ __global__ void __launch_bounds__(64 * kMaxWaves) scan_chunked_kernel(ChunkedSca
     }
 #pragma unroll 1
     for (int i = kStageStates - 2; i < kStageStates; ++i) run_state(1, i);
+    if (kDma) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     lds_barrier();
 
     if (kZ) {
