@@ -61,7 +61,9 @@ constexpr int kRowF4 = kTile / 4;        // float4 pieces of one row of a tile
 constexpr int kPartF4 = 64 + 4;          // float4 slots per part of a staged row (64 lanes + 64 B pad)
 constexpr int kSlotsF4 = 4 * kPartF4;    // float4 slots per staged row
 constexpr int kMinWaves = 8;             // the fp32 stagers are waves 2, 3, 6 and 7
-constexpr int kMaxWaves = 12;
+constexpr int kMaxWaves = 12;            // waves per block (channels per block plus split channels)
+constexpr int kMaxSplit = 2;             // channels split by state between two waves
+constexpr int kWaitVmcnt0 = 0x0F70;      // s_waitcnt vmcnt(0) expcnt(7) lgkmcnt(15): vector memory only
 
 // DPP controls (GFX9 encoding).
 constexpr int kDppWaveShr1 = 0x138;
@@ -178,7 +180,7 @@ __device__ __forceinline__ void load_chunk(const IoT* row, int64_t tl, int64_t L
 }
 
 template <typename IoT, bool kZ, bool kSp>
-__global__ void __launch_bounds__(64 * kMaxWaves) scan_chunked_kernel(ChunkedScanArgs a) {
+__global__ void __launch_bounds__(64 * kMaxWaves) scan_chunked_kernel(ChunkedScanArgs a, int wc, int nsplit) {
   // The two stage buffers, [state of the stage][B, C][slot], 68 KB each.  One
   // state's B and C rows lie within 9 KB, so its reads take immediate offsets
   // from one address.  Two arrays rather than one: the compiler can then tell
@@ -187,15 +189,30 @@ __global__ void __launch_bounds__(64 * kMaxWaves) scan_chunked_kernel(ChunkedSca
   __shared__ float4 stage0[kStageStates][2][kSlotsF4];
   __shared__ float4 stage1[kStageStates][2][kSlotsF4];
   auto buf = [&](int b, int i) -> float4 (*)[kSlotsF4] { return b ? stage1[i] : stage0[i]; };
+  // y of the split channels' second halves, [split channel][q][lane]: 8 KB.
+  __shared__ float4 ypart[kMaxSplit][4][64];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int W = blockDim.x >> 6;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // The block owns wc consecutive channels of one batch row.  Waves
+  // 0 .. nfull-1 own one channel each with all 16 states; the remaining
+  // 2 * nsplit waves split the last nsplit channels by state, half 0 taking
+  // states 0..3 and 8..11 (entries 0..3 of each stage), half 1 states 4..7
+  // and 12..15, so that every SIMD of the CU gets the same share of the
+  // state work (10 channels: waves 8 and 10 share channel 8, 9 and 11
+  // channel 9, one of each pair on each SIMD).  Half 1 hands its part of y
+  // to half 0 through LDS at the end of each tile.
+  const int nfull = wc - nsplit;
+  const bool split = wave >= nfull;
+  const int ch = split ? nfull + (wave - nfull) % nsplit : wave;
+  const int half = split ? (wave - nfull) / nsplit : -1;
+  const int i0 = half == 1 ? kStageStates / 2 : 0;
+  const int i1 = half == 0 ? kStageStates / 2 : kStageStates;
   const int64_t L = a.seqlen;
-  const int64_t groups = (a.dim + W - 1) / W;
+  const int64_t groups = (a.dim + wc - 1) / wc;
   const int64_t bb = blockIdx.x / groups;
-  const int64_t d = (blockIdx.x % groups) * W + wave;
+  const int64_t d = (blockIdx.x % groups) * wc + ch;
   const bool live = d < a.dim;              // a ragged block's extra waves compute a real channel, store nothing
   const int64_t dc = live ? d : a.dim - 1;
   const int64_t row = (bb * a.dim + dc) * L;
@@ -264,7 +281,7 @@ __global__ void __launch_bounds__(64 * kMaxWaves) scan_chunked_kernel(ChunkedSca
       if (!(j < 8 ? in0 : in1)) dj = 0.0f;  // tokens past the end: the identity map
       dv[j] = dj;
       x[j] = dj * un[j];
-      yv[j] = Dd * un[j];
+      yv[j] = half == 1 ? 0.0f : Dd * un[j];
     }
     float sd = 0.0f;
 #pragma unroll
@@ -279,7 +296,6 @@ __global__ void __launch_bounds__(64 * kMaxWaves) scan_chunked_kernel(ChunkedSca
       const int64_t nt0 = h == 0 ? t0 : t0 + kTile;
       Bf16Stager s;
       if (next && stager) s.load(Bh, Ch, (1 - h) * kStageStates + i, nt0, L, tid);
-      if (next && dma) DmaStager::issue(Bf, Cf, (1 - h) * kStageStates + i, nt0, L, si, lane, buf(1 - h, i));
 
       float Bv[kTok];
 #pragma unroll
@@ -320,28 +336,67 @@ __global__ void __launch_bounds__(64 * kMaxWaves) scan_chunked_kernel(ChunkedSca
         yv[j] = __builtin_fmaf(Cv[j], hc, yv[j]);
       }
       if (next && stager) s.store(buf(1 - h, i), tid);
-      if (next && dma && nt0 + kTile > L) {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        DmaStager::zero_tail(nt0, L, si, lane, buf(1 - h, i));
-      }
+    };
+    // fp32: the whole next stage is requested from the DMA stagers when a
+    // stage begins (its buffer was last read in the stage before, which
+    // ended with a barrier), so it has a whole stage to land; a partial
+    // tile's tail is zeroed once it has.
+    auto dma_next = [&](const int h) {
+      const bool next = h == 0 || tile + 1 < ntiles;
+      const int64_t nt0 = h == 0 ? t0 : t0 + kTile;
+      if (!(next && dma)) return;
+      // Unrolled, so the compiler counts these requests and waits for older
+      // loads with vmcnt(16) rather than vmcnt(0).
+#pragma unroll
+      for (int k = 0; k < kStageStates; ++k) DmaStager::issue(Bf, Cf, (1 - h) * kStageStates + k, nt0, L, si, lane, buf(1 - h, k));
+    };
+    auto dma_tail = [&](const int h) {
+      const bool next = h == 0 || tile + 1 < ntiles;
+      const int64_t nt0 = h == 0 ? t0 : t0 + kTile;
+      if (!(next && dma && nt0 + kTile > L)) return;
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll 1
+      for (int k = 0; k < kStageStates; ++k) DmaStager::zero_tail(nt0, L, si, lane, buf(1 - h, k));
     };
 
+    // The u and delta loads of this tile (in flight since two states before
+    // the previous tile ended) are waited for here, before the DMA requests:
+    // the compiler cannot count requests issued on some waves only, and
+    // would otherwise wait for those too before the first use of u.
+    if (kDma) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    dma_next(0);
 #pragma unroll 1
-    for (int i = 0; i < kStageStates; ++i) run_state(0, i);
+    for (int i = i0; i < i1; ++i) run_state(0, i);
+    dma_tail(0);
     if (kDma) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's DMA parts have landed
     lds_barrier();
+    dma_next(1);
 #pragma unroll 1
-    for (int i = 0; i < kStageStates - 2; ++i) run_state(1, i);
+    for (int i = i0; i < (i1 < kStageStates - 2 ? i1 : kStageStates - 2); ++i) run_state(1, i);
     {
       const int64_t tn = (tile + 1 < ntiles ? t0 + kTile : t0) + lane * kTok;
       load_chunk(u, tn, L, un);
       load_chunk(dlt, tn, L, rn);
-      if (kZ) load_chunk(zr, tl, L, zc);
+      if (kZ && half != 1) load_chunk(zr, tl, L, zc);
     }
 #pragma unroll 1
-    for (int i = kStageStates - 2; i < kStageStates; ++i) run_state(1, i);
+    for (int i = (i0 > kStageStates - 2 ? i0 : kStageStates - 2); i < i1; ++i) run_state(1, i);
+    dma_tail(1);
+    if (half == 1) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        ypart[ch - nfull][q][lane] = make_float4(yv[4 * q], yv[4 * q + 1], yv[4 * q + 2], yv[4 * q + 3]);
+    }
     if (kDma) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     lds_barrier();
+    if (half == 1) continue;  // half 0 finishes the tile's y
+    if (half == 0) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 t = ypart[ch - nfull][q][lane];
+        yv[4 * q] += t.x; yv[4 * q + 1] += t.y; yv[4 * q + 2] += t.z; yv[4 * q + 3] += t.w;
+      }
+    }
 
     if (kZ) {
 #pragma unroll
@@ -353,14 +408,22 @@ __global__ void __launch_bounds__(64 * kMaxWaves) scan_chunked_kernel(ChunkedSca
     }
   }
 
-  if (live && a.last_state && lane < kN) a.last_state[(bb * a.dim + dc) * kN + lane] = carry_v;
+  // Each wave stores the final states it ran (half 0: 0..3, 8..11; half 1: 4..7, 12..15).
+  const bool own = lane < kN && (half < 0 || ((lane >> 2) & 1) == half);
+  if (live && a.last_state && own) a.last_state[(bb * a.dim + dc) * kN + lane] = carry_v;
 }
 
 template <typename IoT, bool kZ, bool kSp>
 hipError_t launch_t(const ChunkedScanArgs& a, hipStream_t st) {
-  const int W = ssmi_chunked_block_waves(a.batch * a.dim);
-  const int64_t blocks = a.batch * ((a.dim + W - 1) / W);
-  hipLaunchKernelGGL((scan_chunked_kernel<IoT, kZ, kSp>), dim3((unsigned)blocks), dim3(64 * W), 0, st, a);
+  const int wc = ssmi_chunked_block_waves(a.batch * a.dim);
+  // 10 channels on 4 SIMDs would put 3 waves on two SIMDs and 2 on the
+  // others; splitting 2 channels by state gives 12 waves and every SIMD the
+  // same state work.  (8 and 12 channels divide evenly; 9 and 11 gain
+  // nothing from a split that keeps the stagers on whole channels.)
+  const int nsplit = wc == 10 ? 2 : 0;
+  const int64_t blocks = a.batch * ((a.dim + wc - 1) / wc);
+  hipLaunchKernelGGL((scan_chunked_kernel<IoT, kZ, kSp>), dim3((unsigned)blocks), dim3(64 * (wc + nsplit)),
+                     0, st, a, wc, nsplit);
   return hipGetLastError();
 }
 
