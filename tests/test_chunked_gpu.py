@@ -156,3 +156,18 @@ def test_chunked_nonfinite_propagates():
     assert not np.isfinite(yy[0, 7, 1500]).all()
     others = np.delete(yy[0], 7, axis=0)
     assert np.isfinite(others).all()
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_chunked_split_channels_every_channel(io):
+    """2560 channels run in blocks of 10 channels on 12 waves: channels 8 and 9
+    of every block are split by state between two waves, which hand y over
+    through LDS and each store their own final states.  Every channel of every
+    block against the oracle, over a partial last tile, with an initial state."""
+    b, d, l = 1, 2560, 1048
+    x = inputs.make_scan_inputs(b, d, 16, l, io=io, seed=5700, h0=True)
+    say("chunked split channels, every channel, io=%s" % io)
+    y, last = run(x)
+    yr, hr = oracle.scan_f64(x.u, x.delta, x.A, x.B, x.C, x.D, x.z, x.delta_bias, x.softplus, x.h0)
+    check(np64(y), yr, io, "y")
+    check(np64(last), hr, "f32", "last_state")
