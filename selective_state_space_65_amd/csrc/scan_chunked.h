@@ -7,7 +7,8 @@
 #include <cstdint>
 
 // One prefill call on the chunked path: pointers and sizes as validated by
-// ssm_scan_fwd (dstate 16, seqlen a multiple of 8, rows 16-byte aligned).
+// ssm_scan_fwd / ssm_scan_fwd_ex (dstate 16, seqlen a multiple of 8, rows
+// 16-byte aligned).
 struct ChunkedScanArgs {
   const void* u;
   const void* delta;
@@ -21,6 +22,7 @@ struct ChunkedScanArgs {
   void* y;
   float* last_state;  // may be null
   int64_t batch, dim, seqlen;
+  int zoh;  // B discretized by exact zero-order hold instead of Delta * B
 };
 
 // Channels per block (waves of one block) the launch uses for batch * dim

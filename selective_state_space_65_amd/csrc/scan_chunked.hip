@@ -179,7 +179,7 @@ __device__ __forceinline__ void load_chunk(const IoT* row, int64_t tl, int64_t L
   Io<IoT>::load8(row + (tl + 8 < L ? tl + 8 : L - 8), v + 8);
 }
 
-template <typename IoT, bool kZ, bool kSp>
+template <typename IoT, bool kZ, bool kSp, bool kZoh>
 __global__ void __launch_bounds__(64 * kMaxWaves) scan_chunked_kernel(ChunkedScanArgs a, int wc, int nsplit) {
   // The two stage buffers, [state of the stage][B, C][slot], 68 KB each.  One
   // state's B and C rows lie within 9 KB, so its reads take immediate offsets
@@ -235,6 +235,7 @@ __global__ void __launch_bounds__(64 * kMaxWaves) scan_chunked_kernel(ChunkedSca
   // state loop reads them with readlane and updates the carry with writelane.
   const int ln = lane < kN ? lane : 0;
   const float A2v = a.A[dc * kN + ln] * kLog2e;
+  const float invA_v = kZoh ? 1.0f / a.A[dc * kN + ln] : 0.0f;  // exact zero-order hold: 1 / A[n]
   float carry_v = a.h0 ? a.h0[(bb * a.dim + dc) * kN + ln] : 0.0f;
   const float bias = a.bias ? a.bias[dc] : 0.0f;
   const float Dd = a.D ? a.D[dc] : 0.0f;
@@ -280,7 +281,7 @@ __global__ void __launch_bounds__(64 * kMaxWaves) scan_chunked_kernel(ChunkedSca
       float dj = kSp ? softplus_f32(v) : v;
       if (!(j < 8 ? in0 : in1)) dj = 0.0f;  // tokens past the end: the identity map
       dv[j] = dj;
-      x[j] = dj * un[j];
+      x[j] = kZoh ? un[j] : dj * un[j];  // exact zero-order hold: B u phi instead of B (Delta u)
       yv[j] = half == 1 ? 0.0f : Dd * un[j];
     }
     float sd = 0.0f;
@@ -306,10 +307,20 @@ __global__ void __launch_bounds__(64 * kMaxWaves) scan_chunked_kernel(ChunkedSca
       const float An = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(A2v), n));
       const float cn = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(carry_v), n));
       float dA[kTok], dBu[kTok];
+      if (kZoh) {
+        const float inva = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(invA_v), n));
 #pragma unroll
-      for (int j = 0; j < kTok; ++j) {
-        dA[j] = exp2_hw(An * dv[j]);
-        dBu[j] = Bv[j] * x[j];
+        for (int j = 0; j < kTok; ++j) {
+          const float t = An * dv[j];
+          dA[j] = exp2_hw(t);
+          dBu[j] = Bv[j] * x[j] * zoh_factor(t, dA[j], dv[j], inva);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < kTok; ++j) {
+          dA[j] = exp2_hw(An * dv[j]);
+          dBu[j] = Bv[j] * x[j];
+        }
       }
       float b = dBu[0];
 #pragma unroll
@@ -413,7 +424,7 @@ __global__ void __launch_bounds__(64 * kMaxWaves) scan_chunked_kernel(ChunkedSca
   if (live && a.last_state && own) a.last_state[(bb * a.dim + dc) * kN + lane] = carry_v;
 }
 
-template <typename IoT, bool kZ, bool kSp>
+template <typename IoT, bool kZ, bool kSp, bool kZoh>
 hipError_t launch_t(const ChunkedScanArgs& a, hipStream_t st) {
   const int wc = ssmi_chunked_block_waves(a.batch * a.dim);
   // 10 channels on 4 SIMDs would put 3 waves on two SIMDs and 2 on the
@@ -422,15 +433,20 @@ hipError_t launch_t(const ChunkedScanArgs& a, hipStream_t st) {
   // nothing from a split that keeps the stagers on whole channels.)
   const int nsplit = wc == 10 ? 2 : 0;
   const int64_t blocks = a.batch * ((a.dim + wc - 1) / wc);
-  hipLaunchKernelGGL((scan_chunked_kernel<IoT, kZ, kSp>), dim3((unsigned)blocks), dim3(64 * (wc + nsplit)),
+  hipLaunchKernelGGL((scan_chunked_kernel<IoT, kZ, kSp, kZoh>), dim3((unsigned)blocks), dim3(64 * (wc + nsplit)),
                      0, st, a, wc, nsplit);
   return hipGetLastError();
 }
 
+template <typename IoT, bool kZoh>
+hipError_t launch_zoh(const ChunkedScanArgs& a, bool sp, hipStream_t st) {
+  if (a.z) return sp ? launch_t<IoT, true, true, kZoh>(a, st) : launch_t<IoT, true, false, kZoh>(a, st);
+  return sp ? launch_t<IoT, false, true, kZoh>(a, st) : launch_t<IoT, false, false, kZoh>(a, st);
+}
+
 template <typename IoT>
 hipError_t launch_io(const ChunkedScanArgs& a, bool sp, hipStream_t st) {
-  if (a.z) return sp ? launch_t<IoT, true, true>(a, st) : launch_t<IoT, true, false>(a, st);
-  return sp ? launch_t<IoT, false, true>(a, st) : launch_t<IoT, false, false>(a, st);
+  return a.zoh ? launch_zoh<IoT, true>(a, sp, st) : launch_zoh<IoT, false>(a, sp, st);
 }
 
 }  // namespace

@@ -66,16 +66,9 @@ constexpr int kWavesPerBlock = kBlockThreads / kWaveThreads;
 
 
 
-// Exact zero-order hold for B.  Holding u over a step of length Delta and
-// solving dh/dt = a h + B u exactly gives the input term (e^{Delta a} - 1)/a * u
-// per state (times B).  t = Delta a log2(e) is the exp2 argument, e = exp2(t)
-// is Abar, du = Delta u and iu = u / a.  Where |Delta a| >= 1/16 the term is
-// (e - 1) iu: the rounding of e (about 6e-8 near 1) is then at most 1e-6 of
-// e - 1.  Below that, e - 1 would cancel, and the term is
-// du (1 + x/2 + x^2/6 + x^3/24), x = Delta a, whose first dropped term is
-// under 1.3e-7 of the sum.  At a = 0 (iu infinite, the other side not taken)
-// it is exactly du.
-constexpr float kZohSeriesT = 0.0625f * kLog2e;  // |t| below this: the series
+// Exact zero-order hold for B, the input term phi u (phi: zoh_factor in the
+// device helpers), with du = Delta u and iu = u / a in the places of Delta
+// and 1 / a.
 __device__ __forceinline__ float zoh_input(float t, float e, float du, float iu) {
   constexpr float c1 = kLn2 / 2.0f, c2 = kLn2 * kLn2 / 6.0f, c3 = kLn2 * kLn2 * kLn2 / 24.0f;
   float q = __builtin_fmaf(t, c3, c2);
@@ -83,18 +76,6 @@ __device__ __forceinline__ float zoh_input(float t, float e, float du, float iu)
   q = __builtin_fmaf(t, q, 1.0f);
   const float series = du * q;
   const float held = __builtin_fmaf(e, iu, -iu);
-  return __builtin_fabsf(t) < kZohSeriesT ? series : held;
-}
-
-// The zero-order-hold factor alone, phi = (e^{Delta a} - 1) / a (zoh_input
-// without u): t, e as there, dl = Delta, inva = 1 / a.
-__device__ __forceinline__ float zoh_factor(float t, float e, float dl, float inva) {
-  constexpr float c1 = kLn2 / 2.0f, c2 = kLn2 * kLn2 / 6.0f, c3 = kLn2 * kLn2 * kLn2 / 24.0f;
-  float q = __builtin_fmaf(t, c3, c2);
-  q = __builtin_fmaf(t, q, c1);
-  q = __builtin_fmaf(t, q, 1.0f);
-  const float series = dl * q;
-  const float held = __builtin_fmaf(e, inva, -inva);
   return __builtin_fabsf(t) < kZohSeriesT ? series : held;
 }
 
@@ -3238,18 +3219,18 @@ ScanArgs scan_args(const Shape&, int64_t batch, int64_t dim, int64_t dstate, int
 // conv: the conv is fused (a.u holds x).
 // The chunked kernel (scan_chunked.hip) takes the shapes the single-pass
 // kernel leaves to the segmented path, when it implements them: dstate 16,
-// whole 16-byte rows, the Delta * B rule, no fused conv.
-bool use_chunked(const Plan& p, int64_t dstate, bool vec, bool conv, bool zoh) {
-  return !p.split && vec && dstate == 16 && !conv && !zoh;
+// whole 16-byte rows, no fused conv (either discretization of B).
+bool use_chunked(const Plan& p, int64_t dstate, bool vec, bool conv) {
+  return !p.split && vec && dstate == 16 && !conv;
 }
 
 ssm_status_t run_scan(ScanArgs& a, const Shape& sh, ssm_dtype_t io, bool vec, bool sp, bool conv, hipStream_t hs) {
   const Plan plan = make_plan(sh, a.batch, a.dim, a.dstate, a.seqlen, io);
-  if (use_chunked(plan, a.dstate, vec, conv, a.zoh != 0)) {
+  if (use_chunked(plan, a.dstate, vec, conv)) {
     ChunkedScanArgs c;
     c.u = a.u; c.delta = a.delta; c.A = a.A; c.B = a.B; c.C = a.C; c.D = a.D; c.z = a.z; c.bias = a.bias;
     c.h0 = a.h0; c.y = a.y; c.last_state = a.last_state;
-    c.batch = a.batch; c.dim = a.dim; c.seqlen = a.seqlen;
+    c.batch = a.batch; c.dim = a.dim; c.seqlen = a.seqlen; c.zoh = a.zoh;
     hipError_t e = ssmi_chunked_launch(c, io == SSM_BF16, sp, hs);
     if (e != hipSuccess) return hip_fail(e);
     return SSM_OK;
@@ -3295,7 +3276,7 @@ ssm_status_t ssm_scan_fwd_plan_ex(int64_t batch, int64_t dim, int64_t dstate, in
   Plan p = make_plan(sh, batch, dim, dstate, seqlen, io);
   const bool vec = seqlen % kChunk == 0 && (dstate == 4 || dstate == 8 || dstate == 16) &&
                    dstate * seqlen * (int64_t)io_size(io) < ((int64_t)1 << 31);
-  const bool chunked = use_chunked(p, dstate, vec, conv_width > 0, disc == SSM_DISC_ZOH);
+  const bool chunked = use_chunked(p, dstate, vec, conv_width > 0);
   if (path) *path = p.split && vec ? SSM_PATH_SPLIT : (chunked ? SSM_PATH_CHUNKED : (vec ? SSM_PATH_SEGMENTED : SSM_PATH_GENERIC));
   if (segments) *segments = chunked ? 1 : p.segments;
   if (segment_len) *segment_len = chunked ? seqlen : p.seg_len;

@@ -126,7 +126,7 @@ def test_segmented_aggregate_pieces(io, n, disc):
     b, d, l = 1, 2560, 32768
     dt = torch.float32 if io == "f32" else torch.bfloat16
     path, seg, seglen, scratch = binding.scan_plan(b, d, n, l, dt, with_path=True, disc=disc)
-    if n == 16 and disc == "delta_b":   # the plain rule at dstate 16 runs the chunked kernel instead
+    if n == 16:   # dstate 16 runs the chunked kernel instead
         assert (path, seg, seglen, scratch) == ("chunked", 1, l, 0)
     else:
         assert (seg, seglen, scratch) == (52, 640, 0) and path == ("segmented" if n in (4, 8, 16) else "generic")
@@ -144,20 +144,23 @@ def test_segmented_aggregate_pieces(io, n, disc):
     check(np64(last[0, di]), hr, "f32", "last_state")
 
 
-@pytest.mark.parametrize("io,disc", [("f32", "delta_b"), ("bf16", "delta_b"), ("f32", "zoh"), ("bf16", "zoh")])
-def test_long_rows_two_batch_rows_ragged_dim(io, disc):
+LONG_ROWS = [("f32", "delta_b", 16), ("bf16", "zoh", 16), ("f32", "zoh", 8), ("bf16", "delta_b", 8)]
+
+
+@pytest.mark.parametrize("io,disc,n", LONG_ROWS, ids=["%s-%s-n%d" % c for c in LONG_ROWS])
+def test_long_rows_two_batch_rows_ragged_dim(io, disc, n):
     """Two batch rows of 1300 channels over 31360 tokens, with an initial
     state; sampled channels of both rows, the ragged channel blocks included.
-    The Delta*B rule runs the chunked kernel (31 tiles, the last 640 tokens
-    long; the last block of each row only partly filled); exact zero-order
-    hold runs segmented: 49 segments of 640 tokens, each aggregated in two
-    pieces (42 x 48 x 2 = 4032 waves, the last group 20 channels wide)."""
-    b, d, n, l = 2, 1300, 16, 31360
+    dstate 16 runs the chunked kernel (31 tiles, the last 640 tokens long;
+    the last block of each row only partly filled); dstate 8 runs segmented:
+    49 segments of 640 tokens, each aggregated in two pieces (42 x 48 x 2 =
+    4032 waves, the last group 20 channels wide)."""
+    b, d, l = 2, 1300, 31360
     dt = torch.float32 if io == "f32" else torch.bfloat16
-    want = ("chunked", 1, l, 0) if disc == "delta_b" else ("segmented", 49, 640, 0)
+    want = ("chunked", 1, l, 0) if n == 16 else ("segmented", 49, 640, 0)
     assert binding.scan_plan(b, d, n, l, dt, with_path=True, disc=disc) == want
-    x = inputs.make_scan_inputs(b, d, n, l, io=io, seed=2200, h0=True)
-    say("long rows, 2 batch rows, ragged dim, io=%s disc=%s path=%s" % (io, disc, want[0]))
+    x = inputs.make_scan_inputs(b, d, n, l, io=io, seed=2200 + n, h0=True)
+    say("long rows, 2 batch rows, ragged dim, io=%s disc=%s n=%d path=%s" % (io, disc, n, want[0]))
     t = inputs.to_torch(x, DEV)
     y, last = binding.scan_fwd_ex(t["u"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
                                   delta_bias=t["delta_bias"], delta_softplus=x.softplus, h0=t["h0"], disc=disc)
@@ -295,10 +298,13 @@ def test_odd_shapes(io, shape):
 
 def test_long_sequence_plans():
     # The long-sequence workload runs the chunked kernel (one launch, nothing
-    # but y and last_state written); under exact zero-order hold it runs
-    # segmented, with its aggregates and carries in y.  Neither takes scratch.
+    # but y and last_state written), under either discretization of B; with
+    # the conv fused in front it runs segmented, with its aggregates and
+    # carries in y.  Neither takes scratch.
     assert binding.scan_plan(1, 2560, 16, 131072, torch.float32, with_path=True) == ("chunked", 1, 131072, 0)
-    path, seg, seglen, scratch = binding.scan_plan(1, 2560, 16, 131072, torch.float32, with_path=True, disc="zoh")
+    assert binding.scan_plan(1, 2560, 16, 131072, torch.float32, with_path=True, disc="zoh") == \
+        ("chunked", 1, 131072, 0)
+    path, seg, seglen, scratch = binding.scan_plan(1, 2560, 16, 131072, torch.float32, with_path=True, conv_width=4)
     assert path == "segmented" and seg > 1 and scratch == 0
 
 
@@ -376,7 +382,7 @@ def test_misaligned_rows_segmented(io):
     x = inputs.make_scan_inputs(b, d, n, l, io=io, seed=42, h0=True)
     # The plan (for aligned rows) is the chunked kernel; rows that are not
     # 16-byte aligned run the per-token kernel over the segmented plan.
-    assert binding.scan_plan(b, d, n, l, torch.float32 if io == "f32" else torch.bfloat16, disc="zoh")[0] > 1
+    assert binding.scan_plan(b, d, n, l, torch.float32 if io == "f32" else torch.bfloat16, conv_width=4)[0] > 1
     t = inputs.to_torch(x, DEV)
     say("misaligned segmented io=%s" % io)
 

@@ -73,11 +73,12 @@ def oracle_zoh(x):
     return oracle.scan_f64(x.u, x.delta, x.A, x.B, x.C, x.D, x.z, x.delta_bias, x.softplus, x.h0, zoh=True)
 
 
-# (shape, expected path): the single-pass kernel, the segmented path, the
+# (shape, expected path): the single-pass kernel, the chunked kernel (the
+# second shape ends in a partial tile), the segmented path (dstate 8), the
 # generic path (dstate 12; seqlen 63).
 SHAPES = [((192, 64, 16, 96), "split"), ((200, 64, 8, 40), "split"), ((256, 33, 4, 24), "split"),
-          ((1, 64, 16, 4096), "segmented"), ((2, 96, 8, 1536), "segmented"), ((2, 63, 12, 72), "generic"),
-          ((3, 40, 16, 63), "generic")]
+          ((1, 64, 16, 4096), "chunked"), ((1, 64, 16, 2056), "chunked"), ((2, 96, 8, 1536), "segmented"),
+          ((2, 63, 12, 72), "generic"), ((3, 40, 16, 63), "generic")]
 
 
 @pytest.mark.parametrize("io", ["f32", "bf16"])
