@@ -475,8 +475,8 @@ typedef enum {
   SSM_PATH_CHUNKED = 3    /* one pass, lanes along the sequence: a wave owns one channel, its
                              lanes 16-token chunks of a tile, combined by a lane scan of the
                              chunks' affine maps and a running carry (dstate 16, either
-                             discretization of B, no fused conv; shapes with too few
-                             channels for SSM_PATH_SPLIT)                                  */
+                             discretization of B, with or without the fused conv; shapes
+                             with too few channels for SSM_PATH_SPLIT)                     */
 } ssm_path_t;
 
 /*
@@ -496,10 +496,8 @@ ssm_status_t ssm_scan_fwd_plan(int64_t batch, int64_t dim, int64_t dstate, int64
 /*
  * ssm_scan_fwd_plan_ex -- ssm_scan_fwd_plan for the other prefill entry
  * points: disc is the discretization of B (ssm_scan_fwd_ex), conv_width the
- * width of the conv fused in front (ssm_conv_scan_fwd; 0 for none).  The
- * chunked path runs no fused conv; a conv call of such a shape runs
- * segmented.  SSM_ERR_UNSUPPORTED for an unknown disc or a conv_width
- * outside 0..4.
+ * width of the conv fused in front (ssm_conv_scan_fwd; 0 for none).
+ * SSM_ERR_UNSUPPORTED for an unknown disc or a conv_width outside 0..4.
  */
 ssm_status_t ssm_scan_fwd_plan_ex(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
                                   ssm_dtype_t io, ssm_disc_t disc, int64_t conv_width, int* path,

@@ -117,6 +117,30 @@ struct Io<bf16_t> {
   }
 };
 
+// v rounded to the io dtype (as a stored u would be), returned as fp32.
+template <typename IoT>
+__device__ __forceinline__ float round_io(float v) {
+  if constexpr (sizeof(IoT) == 4) {
+    return v;
+  } else {
+    const __bf16 r = (__bf16)v;  // round to nearest even
+    return __uint_as_float((uint32_t)__builtin_bit_cast(uint16_t, r) << 16);
+  }
+}
+
+// The causal depthwise conv of one token: acc = bias, then one FMA per tap
+// from the oldest input (xs[4 - K]) to the current one (xs[3]); taps a
+// narrower filter does not have are skipped, not multiplied by zero, so a
+// non-finite input reaches exactly the K outputs that read it.  The standalone
+// conv kernel and the fused prologue both use this, so they agree bitwise.
+template <int K>
+__device__ __forceinline__ float conv_taps(const float* xs, const float* w, float bias) {
+  float acc = bias;
+#pragma unroll
+  for (int k = 0; k < K; ++k) acc = __builtin_fmaf(w[k], xs[4 - K + k], acc);
+  return acc;
+}
+
 // Workgroup barrier that orders LDS only: the LDS writes before it are
 // visible to every wave after it, while global loads and stores stay in
 // flight (a full __syncthreads would also wait for those).

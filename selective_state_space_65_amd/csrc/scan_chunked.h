@@ -23,6 +23,14 @@ struct ChunkedScanArgs {
   float* last_state;  // may be null
   int64_t batch, dim, seqlen;
   int zoh;  // B discretized by exact zero-order hold instead of Delta * B
+  // Causal depthwise conv fused in front (ssm_conv_scan_fwd): u then holds the
+  // conv input x.  conv_width 0: no conv.
+  const float* conv_w;  // [dim][conv_width]
+  const float* conv_b;  // [dim], may be null
+  const void* x_prev;   // [batch][dim][conv_width - 1], may be null
+  void* u_out;          // [batch][dim][seqlen], may be null
+  int conv_width;       // 0 (no conv) or 1..4
+  int conv_silu;
 };
 
 // Channels per block (waves of one block) the launch uses for batch * dim

@@ -179,8 +179,12 @@ __device__ __forceinline__ void load_chunk(const IoT* row, int64_t tl, int64_t L
   Io<IoT>::load8(row + (tl + 8 < L ? tl + 8 : L - 8), v + 8);
 }
 
-template <typename IoT, bool kZ, bool kSp, bool kZoh>
+// kConvK: width of the conv fused in front (1..4), 0 for none.  The width is
+// a template argument: with a runtime width the taps' selects keep every
+// token's candidate sums live and the kernel spills.
+template <typename IoT, bool kZ, bool kSp, bool kZoh, int kConvK>
 __global__ void __launch_bounds__(64 * kMaxWaves) scan_chunked_kernel(ChunkedScanArgs a, int wc, int nsplit) {
+  constexpr bool kConv = kConvK > 0;
   // The two stage buffers, [state of the stage][B, C][slot], 68 KB each.  One
   // state's B and C rows lie within 9 KB, so its reads take immediate offsets
   // from one address.  Two arrays rather than one: the compiler can then tell
@@ -239,6 +243,25 @@ __global__ void __launch_bounds__(64 * kMaxWaves) scan_chunked_kernel(ChunkedSca
   float carry_v = a.h0 ? a.h0[(bb * a.dim + dc) * kN + ln] : 0.0f;
   const float bias = a.bias ? a.bias[dc] : 0.0f;
   const float Dd = a.D ? a.D[dc] : 0.0f;
+  // Fused conv: u holds the conv input x; the taps, and the three inputs
+  // before the tile (x_prev's last slots for tile 0, then the previous
+  // tile's last three), are wave-uniform.
+  constexpr int K = kConv ? kConvK : 1;
+  float wl[4] = {0.0f, 0.0f, 0.0f, 0.0f}, cbias = 0.0f, xtail[3] = {0.0f, 0.0f, 0.0f};  // wl[j]: tap of lag j
+  if constexpr (kConv) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (j < K) wl[j] = a.conv_w[dc * K + (K - 1 - j)];
+    cbias = a.conv_b ? a.conv_b[dc] : 0.0f;
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      const int idx = K - 4 + k;  // x_prev slot of position k - 3
+      xtail[k] = (a.x_prev && idx >= 0)
+                     ? Io<IoT>::load1(static_cast<const IoT*>(a.x_prev) + (bb * a.dim + dc) * (K - 1) + idx)
+                     : 0.0f;
+    }
+  }
+  IoT* uo = kConv && a.u_out ? static_cast<IoT*>(a.u_out) + row : nullptr;
   const int64_t ntiles = (L + kTile - 1) / kTile;
 
   // Stage 0: tile 0, states 0..7, into buffer 0.
@@ -273,6 +296,36 @@ __global__ void __launch_bounds__(64 * kMaxWaves) scan_chunked_kernel(ChunkedSca
     const int64_t t0 = tile * kTile;
     const int64_t tl = t0 + lane * kTok;
     const bool in0 = tl < L, in1 = tl + 8 < L;
+
+    if constexpr (kConv) {
+      // u from x: the lane's 16 inputs and the 3 before them (the lane
+      // below's last three, or for lane 0 the tile's history).  One FMA per
+      // tap from the oldest input to the current one, a tap beyond the width
+      // skipped (the order and rounding of conv_taps on the other paths),
+      // then the optional silu and the rounding to the io dtype.  Outputs run
+      // from the last token down, so each input is overwritten only after
+      // its last use.
+      float hx[3];
+#pragma unroll
+      for (int k = 0; k < 3; ++k) {
+        hx[k] = dpp<kDppWaveShr1, 0xf>(xtail[k], un[kTok - 3 + k]);
+        xtail[k] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(un[kTok - 3 + k]), 63));
+      }
+      auto xin = [&](int p) { return p >= 0 ? un[p] : hx[3 + p]; };  // input at lane position p (p >= -3)
+#pragma unroll
+      for (int j = kTok - 1; j >= 0; --j) {
+        float acc = cbias;
+        if (K > 3) acc = __builtin_fmaf(wl[3], xin(j - 3), acc);
+        if (K > 2) acc = __builtin_fmaf(wl[2], xin(j - 2), acc);
+        if (K > 1) acc = __builtin_fmaf(wl[1], xin(j - 1), acc);
+        acc = __builtin_fmaf(wl[0], xin(j), acc);
+        un[j] = round_io<IoT>(a.conv_silu ? silu_f32(acc) : acc);
+      }
+      if (uo && live && half != 1) {
+        if (in0) Io<IoT>::store8(uo + tl, un);
+        if (in1) Io<IoT>::store8(uo + tl + 8, un + 8);
+      }
+    }
 
     float x[kTok], dv[kTok], yv[kTok];
 #pragma unroll
@@ -424,7 +477,7 @@ __global__ void __launch_bounds__(64 * kMaxWaves) scan_chunked_kernel(ChunkedSca
   if (live && a.last_state && own) a.last_state[(bb * a.dim + dc) * kN + lane] = carry_v;
 }
 
-template <typename IoT, bool kZ, bool kSp, bool kZoh>
+template <typename IoT, bool kZ, bool kSp, bool kZoh, int kConvK>
 hipError_t launch_t(const ChunkedScanArgs& a, hipStream_t st) {
   const int wc = ssmi_chunked_block_waves(a.batch * a.dim);
   // 10 channels on 4 SIMDs would put 3 waves on two SIMDs and 2 on the
@@ -433,20 +486,29 @@ hipError_t launch_t(const ChunkedScanArgs& a, hipStream_t st) {
   // nothing from a split that keeps the stagers on whole channels.)
   const int nsplit = wc == 10 ? 2 : 0;
   const int64_t blocks = a.batch * ((a.dim + wc - 1) / wc);
-  hipLaunchKernelGGL((scan_chunked_kernel<IoT, kZ, kSp, kZoh>), dim3((unsigned)blocks), dim3(64 * (wc + nsplit)),
+  hipLaunchKernelGGL((scan_chunked_kernel<IoT, kZ, kSp, kZoh, kConvK>), dim3((unsigned)blocks), dim3(64 * (wc + nsplit)),
                      0, st, a, wc, nsplit);
   return hipGetLastError();
 }
 
-template <typename IoT, bool kZoh>
-hipError_t launch_zoh(const ChunkedScanArgs& a, bool sp, hipStream_t st) {
-  if (a.z) return sp ? launch_t<IoT, true, true, kZoh>(a, st) : launch_t<IoT, true, false, kZoh>(a, st);
-  return sp ? launch_t<IoT, false, true, kZoh>(a, st) : launch_t<IoT, false, false, kZoh>(a, st);
+template <typename IoT, bool kZoh, int kConvK>
+hipError_t launch_zc(const ChunkedScanArgs& a, bool sp, hipStream_t st) {
+  if (a.z) return sp ? launch_t<IoT, true, true, kZoh, kConvK>(a, st) : launch_t<IoT, true, false, kZoh, kConvK>(a, st);
+  return sp ? launch_t<IoT, false, true, kZoh, kConvK>(a, st) : launch_t<IoT, false, false, kZoh, kConvK>(a, st);
 }
 
+// The fused conv runs with the Delta * B rule only (its entry point has no
+// discretization argument).
 template <typename IoT>
 hipError_t launch_io(const ChunkedScanArgs& a, bool sp, hipStream_t st) {
-  return a.zoh ? launch_zoh<IoT, true>(a, sp, st) : launch_zoh<IoT, false>(a, sp, st);
+  switch (a.conv_width) {
+    case 1: return launch_zc<IoT, false, 1>(a, sp, st);
+    case 2: return launch_zc<IoT, false, 2>(a, sp, st);
+    case 3: return launch_zc<IoT, false, 3>(a, sp, st);
+    case 4: return launch_zc<IoT, false, 4>(a, sp, st);
+    default: break;
+  }
+  return a.zoh ? launch_zc<IoT, true, 0>(a, sp, st) : launch_zc<IoT, false, 0>(a, sp, st);
 }
 
 }  // namespace

@@ -268,16 +268,6 @@ __device__ __forceinline__ float conv_token(const ConvChan& c, float x3, float x
 
 __device__ __forceinline__ float conv_silu(const ConvChan& c, float v) { return c.silu ? silu_f32(v) : v; }
 
-// v rounded to the io dtype (as a stored u would be), returned as fp32.
-template <typename IoT>
-__device__ __forceinline__ float round_io(float v) {
-  if constexpr (sizeof(IoT) == 4) {
-    return v;
-  } else {
-    const __bf16 r = (__bf16)v;  // round to nearest even
-    return __uint_as_float((uint32_t)__builtin_bit_cast(uint16_t, r) << 16);
-  }
-}
 
 // The conv inputs at positions l0-3 .. l0-1 of row ch (oldest first): the
 // row itself, or before the sequence start the last K-1 slots of x_prev
@@ -297,19 +287,6 @@ __device__ __forceinline__ void conv_history(const ScanArgs& a, int64_t ch, int6
                                      : 0.0f;
     }
   }
-}
-
-// The causal depthwise conv of one token: acc = bias, then one FMA per tap
-// from the oldest input (xs[4 - K]) to the current one (xs[3]); taps a
-// narrower filter does not have are skipped, not multiplied by zero, so a
-// non-finite input reaches exactly the K outputs that read it.  The standalone
-// conv kernel and the fused prologue both use this, so they agree bitwise.
-template <int K>
-__device__ __forceinline__ float conv_taps(const float* xs, const float* w, float bias) {
-  float acc = bias;
-#pragma unroll
-  for (int k = 0; k < K; ++k) acc = __builtin_fmaf(w[k], xs[4 - K + k], acc);
-  return acc;
 }
 
 // Wave-uniform decomposition of a wave index into (segment, batch row, group).
@@ -3218,19 +3195,19 @@ ScanArgs scan_args(const Shape&, int64_t batch, int64_t dim, int64_t dstate, int
 // the segmented path keeps its aggregates and carries in y (seg_slot_store).
 // conv: the conv is fused (a.u holds x).
 // The chunked kernel (scan_chunked.hip) takes the shapes the single-pass
-// kernel leaves to the segmented path, when it implements them: dstate 16,
-// whole 16-byte rows, no fused conv (either discretization of B).
-bool use_chunked(const Plan& p, int64_t dstate, bool vec, bool conv) {
-  return !p.split && vec && dstate == 16 && !conv;
-}
+// kernel leaves to the segmented path, when it implements them: dstate 16 and
+// whole 16-byte rows (either discretization of B, with or without the conv).
+bool use_chunked(const Plan& p, int64_t dstate, bool vec) { return !p.split && vec && dstate == 16; }
 
 ssm_status_t run_scan(ScanArgs& a, const Shape& sh, ssm_dtype_t io, bool vec, bool sp, bool conv, hipStream_t hs) {
   const Plan plan = make_plan(sh, a.batch, a.dim, a.dstate, a.seqlen, io);
-  if (use_chunked(plan, a.dstate, vec, conv)) {
+  if (use_chunked(plan, a.dstate, vec)) {
     ChunkedScanArgs c;
     c.u = a.u; c.delta = a.delta; c.A = a.A; c.B = a.B; c.C = a.C; c.D = a.D; c.z = a.z; c.bias = a.bias;
     c.h0 = a.h0; c.y = a.y; c.last_state = a.last_state;
     c.batch = a.batch; c.dim = a.dim; c.seqlen = a.seqlen; c.zoh = a.zoh;
+    c.conv_w = a.conv_w; c.conv_b = a.conv_b; c.x_prev = a.x_prev; c.u_out = a.u_out;
+    c.conv_width = conv ? a.conv_width : 0; c.conv_silu = a.conv_silu;
     hipError_t e = ssmi_chunked_launch(c, io == SSM_BF16, sp, hs);
     if (e != hipSuccess) return hip_fail(e);
     return SSM_OK;
@@ -3276,7 +3253,7 @@ ssm_status_t ssm_scan_fwd_plan_ex(int64_t batch, int64_t dim, int64_t dstate, in
   Plan p = make_plan(sh, batch, dim, dstate, seqlen, io);
   const bool vec = seqlen % kChunk == 0 && (dstate == 4 || dstate == 8 || dstate == 16) &&
                    dstate * seqlen * (int64_t)io_size(io) < ((int64_t)1 << 31);
-  const bool chunked = use_chunked(p, dstate, vec, conv_width > 0);
+  const bool chunked = use_chunked(p, dstate, vec);
   if (path) *path = p.split && vec ? SSM_PATH_SPLIT : (chunked ? SSM_PATH_CHUNKED : (vec ? SSM_PATH_SEGMENTED : SSM_PATH_GENERIC));
   if (segments) *segments = chunked ? 1 : p.segments;
   if (segment_len) *segment_len = chunked ? seqlen : p.seg_len;

@@ -359,16 +359,15 @@ def test_plan(lib):
     path, seg, seglen, scratch = binding.scan_plan(4, 4096, 16, 4096, torch.bfloat16, with_path=True)
     assert (path, seg, seglen, scratch) == ("split", 1, 4096, 0)          # Mamba-1.4B layer: single pass
     assert binding.scan_plan(8, 1536, 16, 2048, torch.float32, with_path=True) == ("split", 1, 2048, 0)
-    # Long sequence: the chunked kernel for the scan under either
-    # discretization; the fused conv runs segmented.  No path takes scratch: the
-    # segment aggregates and carries live in y.  The last segment ends at
-    # seqlen and holds at least 64 tokens.
+    # Long sequence: the chunked kernel at dstate 16 (under either
+    # discretization, with or without the conv); dstate 8 runs segmented.  No
+    # path takes scratch: the segment aggregates and carries live in y.  The
+    # last segment ends at seqlen and holds at least 64 tokens.
     assert binding.scan_plan(1, 2560, 16, 131072, torch.float32, with_path=True) == ("chunked", 1, 131072, 0)
     assert binding.scan_plan(1, 2560, 16, 131072, torch.bfloat16, with_path=True) == ("chunked", 1, 131072, 0)
-    assert binding.scan_plan(1, 2560, 8, 131072, torch.float32, with_path=True)[0] == "segmented"
-    assert binding.scan_plan(1, 2560, 16, 131072, torch.float32, with_path=True, conv_width=4)[0] == "segmented"
+    assert binding.scan_plan(1, 2560, 16, 131072, torch.float32, with_path=True, conv_width=4)[0] == "chunked"
     assert binding.scan_plan(1, 2560, 16, 131072, torch.float32, with_path=True, disc="zoh")[0] == "chunked"
-    path, seg, seglen, scratch = binding.scan_plan(1, 2560, 16, 131072, torch.float32, with_path=True, conv_width=4)
+    path, seg, seglen, scratch = binding.scan_plan(1, 2560, 8, 131072, torch.float32, with_path=True, conv_width=4)
     assert path == "segmented" and seg > 1 and scratch == 0
     assert (seg - 1) * seglen < 131072 and 131072 - (seg - 1) * seglen >= 64
     path, seg, seglen, scratch = binding.scan_plan(1, 64, 16, 4097, torch.float32, with_path=True)

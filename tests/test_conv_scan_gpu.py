@@ -94,10 +94,13 @@ def test_fused_path(io, shape):
             check(np64(last), hr, TOL["f32"], "last_state K=%d" % width)
 
 
-# Shapes off the single-pass kernel: the conv is fused into the segmented
-# and per-token kernels too (history carried across lines and segments).
+# Shapes off the single-pass kernel: the conv is fused into the chunked,
+# segmented and per-token kernels too (history carried across lanes, tiles,
+# lines and segments).  Chunked: 1x64x16x4096, 1x40x16x24 (lane 1 half past
+# the end), 2x37x16x2064 (three tiles, the last partial; ragged blocks),
+# 1x2560x16x1048 (channels split by state).
 OTHER_SHAPES = [(1, 16, 4, 64), (2, 63, 16, 63), (1, 3, 16, 7), (1, 64, 16, 4097), (1, 64, 16, 4096),
-                (2, 100, 8, 1536)]
+                (2, 100, 8, 1536), (1, 40, 16, 24), (2, 37, 16, 2064), (1, 2560, 16, 1048)]
 
 
 @pytest.mark.parametrize("io", ["f32", "bf16"])
@@ -118,17 +121,21 @@ def test_other_paths(io, shape):
 
 
 @pytest.mark.parametrize("io", ["f32", "bf16"])
-def test_segmented_aggregate_pieces_with_conv(io):
-    """A segmented plan whose aggregate launch runs each segment in two pieces
-    (52 segments of 640 tokens at 1 x 2560 x 32768): each piece starts its
-    conv from the four inputs before it.  Checked on sampled channels."""
-    b, d, n, l = 1, 2560, 16, 32768
+@pytest.mark.parametrize("n", [16, 8])
+def test_long_rows_with_conv(io, n):
+    """1 x 2560 x 32768 with the conv in front.  dstate 16 runs the chunked
+    kernel (32 tiles, two channels of each block split by state); dstate 8 a
+    segmented plan whose aggregate launch runs each segment in two pieces (52
+    segments of 640 tokens), each piece starting its conv from the four
+    inputs before it.  Checked on sampled channels."""
+    b, d, l = 1, 2560, 32768
     dt = torch.float32 if io == "f32" else torch.bfloat16
-    assert binding.scan_plan(b, d, n, l, dt, with_path=True, conv_width=4) == ("segmented", 52, 640, 0)
-    say("conv with aggregate pieces io=%s" % io)
+    want = ("chunked", 1, l, 0) if n == 16 else ("segmented", 52, 640, 0)
+    assert binding.scan_plan(b, d, n, l, dt, with_path=True, conv_width=4) == want
+    say("conv on long rows io=%s n=%d path=%s" % (io, n, want[0]))
     x, w, cb, prev = conv_inputs(b, d, n, l, io, 4, 700, h0=True)
     y, last, uo, _ = run(x, w, cb, prev, True)
-    ch = inputs.sample_channels(b, d, 6, seed=5)
+    ch = inputs.sample_channels(b, d, 6, seed=5) + [(0, 8), (0, 2559)]   # two split channels of the chunked plan
     di = [c[1] for c in ch]
     u64 = oracle.conv1d_f64(x.u[:, di], w[di], None if cb is None else cb[di], None if prev is None else prev[:, di],
                             silu=True)
@@ -143,14 +150,15 @@ def test_segmented_aggregate_pieces_with_conv(io):
 
 
 @pytest.mark.parametrize("io", ["f32", "bf16"])
-def test_fused_equals_conv_then_scan(io):
+@pytest.mark.parametrize("shape", [(192, 64, 16, 96), (1, 64, 16, 2056)], ids=["split", "chunked"])
+def test_fused_equals_conv_then_scan(io, shape):
     """The fused kernel's y is bitwise the plain scan of the u it reports, and
     that u is bitwise the per-token kernel's conv (a misaligned u_out sends the
     call there; its scan then differs in summation order, so y is held to the
     usual bar)."""
-    b, d, n, l = 192, 64, 16, 96
+    b, d, n, l = shape
     x, w, cb, prev = conv_inputs(b, d, n, l, io, 4, 700, h0=True)
-    say("conv fused vs conv+scan io=%s" % io)
+    say("conv fused vs conv+scan io=%s shape=%s" % (io, shape))
     y, last, uo, t = run(x, w, cb, prev, True)
     y2, last2 = binding.scan_fwd(uo, t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"], delta_bias=t["delta_bias"],
                                  delta_softplus=True, h0=t["h0"])
@@ -167,10 +175,11 @@ def test_fused_equals_conv_then_scan(io):
 
 
 @pytest.mark.parametrize("io", ["f32", "bf16"])
-def test_conv_carry_across_calls(io):
+@pytest.mark.parametrize("shape", [(192, 64, 16, 160, 72), (1, 48, 16, 3072, 1040)], ids=["split", "chunked"])
+def test_conv_carry_across_calls(io, shape):
     """Two calls, the second fed the first's last K-1 inputs and final state,
     equal one call over the whole sequence."""
-    b, d, n, l, cut = 192, 64, 16, 160, 72
+    b, d, n, l, cut = shape
     x, w, cb, prev = conv_inputs(b, d, n, l, io, 4, 800, h0=True)
     say("conv carry io=%s" % io)
     y, last, uo, t = run(x, w, cb, prev, True)
@@ -189,15 +198,23 @@ def test_conv_carry_across_calls(io):
     check(np64(h2), np64(last), 1e-6, "carried state")
 
 
-def test_conv_nonfinite_reaches_exactly_k_outputs():
-    b, d, n, l = 192, 64, 16, 48
+# (shape, (batch, channel, token) of the Inf): the single-pass kernel; the
+# chunked kernel with the Inf two tokens before a lane boundary (its taps
+# reach the next lane's first outputs) and two before a tile boundary.
+NONFINITE = [((192, 64, 16, 48), (3, 5, 17)), ((1, 40, 16, 2048), (0, 7, 30)), ((1, 40, 16, 2048), (0, 9, 1022))]
+
+
+@pytest.mark.parametrize("shape,at", NONFINITE, ids=["split", "chunked-lane", "chunked-tile"])
+def test_conv_nonfinite_reaches_exactly_k_outputs(shape, at):
+    b, d, n, l = shape
+    bi, di, li = at
     for width in (1, 2, 4):
         x, w, cb, prev = conv_inputs(b, d, n, l, "f32", width, 900 + width, h0=True)
         x.u = x.u.copy()
-        x.u[3, 5, 17] = np.inf
-        say("conv inf K=%d" % width)
+        x.u[bi, di, li] = np.inf
+        say("conv inf K=%d shape=%s at=%s" % (width, shape, at))
         _, _, uo, _ = run(x, w, cb, prev, False)
         bad = ~torch.isfinite(uo.cpu())
         want = torch.zeros_like(bad)
-        want[3, 5, 17:17 + width] = True
+        want[bi, di, li:li + width] = True
         assert torch.equal(bad, want), "K=%d non-finite at %s" % (width, torch.nonzero(bad).tolist()[:8])

@@ -94,10 +94,11 @@ def test_split_prefill_in_a_graph(io):
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 @pytest.mark.parametrize("conv", [False, True])
 def test_segmented_prefill_in_a_graph(io, conv):
-    """The chunked path (the plain scan) and the segmented path with the conv
-    fused into it (three launches, aggregates and carries in y) allocate
-    nothing, so a capture holds only launches."""
-    b, d, n, l = 1, 128, 16, 4096
+    """The chunked path (dstate 16, the plain scan) and the segmented path
+    (dstate 8, the conv fused into it; three launches, aggregates and carries
+    in y) allocate nothing, so a capture holds only launches."""
+    b, d, l = 1, 128, 4096
+    n = 8 if conv else 16
     dt = torch.float32 if io == "f32" else torch.bfloat16
     path, seg = binding.scan_plan(b, d, n, l, dt, with_path=True, conv_width=4 if conv else 0)[:2]
     assert (path, seg > 1) == (("segmented", True) if conv else ("chunked", False))

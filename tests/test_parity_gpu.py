@@ -298,13 +298,15 @@ def test_odd_shapes(io, shape):
 
 def test_long_sequence_plans():
     # The long-sequence workload runs the chunked kernel (one launch, nothing
-    # but y and last_state written), under either discretization of B; with
-    # the conv fused in front it runs segmented, with its aggregates and
+    # but y and last_state written), under either discretization of B and
+    # with the conv; at dstate 8 it runs segmented, with its aggregates and
     # carries in y.  Neither takes scratch.
     assert binding.scan_plan(1, 2560, 16, 131072, torch.float32, with_path=True) == ("chunked", 1, 131072, 0)
     assert binding.scan_plan(1, 2560, 16, 131072, torch.float32, with_path=True, disc="zoh") == \
         ("chunked", 1, 131072, 0)
-    path, seg, seglen, scratch = binding.scan_plan(1, 2560, 16, 131072, torch.float32, with_path=True, conv_width=4)
+    assert binding.scan_plan(1, 2560, 16, 131072, torch.float32, with_path=True, conv_width=4) == \
+        ("chunked", 1, 131072, 0)
+    path, seg, seglen, scratch = binding.scan_plan(1, 2560, 8, 131072, torch.float32, with_path=True)
     assert path == "segmented" and seg > 1 and scratch == 0
 
 
@@ -381,8 +383,9 @@ def test_misaligned_rows_segmented(io):
     b, d, n, l = 1, 70, 16, 2000
     x = inputs.make_scan_inputs(b, d, n, l, io=io, seed=42, h0=True)
     # The plan (for aligned rows) is the chunked kernel; rows that are not
-    # 16-byte aligned run the per-token kernel over the segmented plan.
-    assert binding.scan_plan(b, d, n, l, torch.float32 if io == "f32" else torch.bfloat16, conv_width=4)[0] > 1
+    # 16-byte aligned run the per-token kernel over the segmented plan (the
+    # one dstate 8 would take).
+    assert binding.scan_plan(b, d, 8, l, torch.float32 if io == "f32" else torch.bfloat16)[0] > 1
     t = inputs.to_torch(x, DEV)
     say("misaligned segmented io=%s" % io)
 
