@@ -54,11 +54,11 @@ METRIC = "selective-scan HBM GB/s (% of MI355X peak) + (B·D·L)/s at Mamba-1.4B
 # are reported as null until re-measured.  Keys are the workload indices of
 # inputs.scan_config.
 MEASURED_TRAFFIC = {
-    "source_sha256": "4ec78a68d9341df5f51defdcded4e3c236bbeff2aa90372298695c757be6102c",
+    "source_sha256": "1ae6a298e4268be2da070d513547fbe6c8c44200eda4dbc3097c1ecdcee26777",
     "per_call": {
-        2: {"read_bytes": 482_756_245, "write_bytes": 137_473_248},
-        1: {"read_bytes": 359_322_449, "write_bytes": 102_479_952},
-        3: {"read_bytes": 4_183_332_839, "write_bytes": 1_354_432_064},
+        2: {"read_bytes": 463_734_732, "write_bytes": 136_778_720},
+        1: {"read_bytes": 362_545_520, "write_bytes": 103_089_600},
+        3: {"read_bytes": 4_184_593_576, "write_bytes": 1_353_897_296},
     },
 }
 HBM_PEAK_GBS = 8000.0
@@ -521,6 +521,29 @@ def bench_config(dev, cfg, steps, warmup):
     wall_ms, avg_ms, med_ms = time_calls(fn, steps, warmup)
     nbytes = algorithmic_bytes(b, d, n, l, io_bytes, has_z=x.z is not None)
     path, seg, seglen, scratch = binding.scan_plan(b, d, n, l, t["u"].dtype, with_path=True)
+    variants = {}
+    if cfg == 3:
+        # The same long rows under exact zero-order hold and with the width-4
+        # conv (+ silu) fused in front: the other two entry points the
+        # one-pass kernel serves.
+        def fn_zoh():
+            binding.scan_fwd_ex(t["u"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
+                                delta_bias=t["delta_bias"], delta_softplus=x.softplus, h0=None, out=y, last_state=last,
+                                disc="zoh")
+
+        cw = inputs.conv_params(d, 4)
+        cwt = torch.from_numpy(cw[0]).to(dev)
+        cbt = torch.from_numpy(cw[1]).to(dev)
+
+        def fn_conv():
+            binding.conv_scan_fwd(t["u"], cwt, t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
+                                  delta_bias=t["delta_bias"], delta_softplus=x.softplus, conv_bias=cbt, conv_silu=True,
+                                  out=y, last_state=last)
+
+        for name, f, kw in (("zoh", fn_zoh, {"disc": "zoh"}), ("conv_scan", fn_conv, {"conv_width": 4})):
+            _, v_ms, v_med = time_calls(f, max(3, steps // 2), 1)
+            variants[name] = dict(us_per_call=round(v_ms * 1e3, 2), us_median=round(v_med * 1e3, 2),
+                                  kernel_path=binding.scan_plan(b, d, n, l, t["u"].dtype, with_path=True, **kw)[0])
     del t, y, last
     torch.cuda.empty_cache()
     gbs = nbytes / (avg_ms * 1e-3) / 1e9
@@ -534,7 +557,8 @@ def bench_config(dev, cfg, steps, warmup):
                               frac=round(gbs / HBM_PEAK_GBS, 4), traffic=traffic,
                               traffic_ratio=None if traffic is None else round(traffic / nbytes, 3),
                               kernel="ssm_scan_fwd call: %s" % KERNELS[path],
-                              alu=dict(frac=round(alu_frac, 4), lane_slots_per_elem_state=SLOTS_PER_ELEM_STATE)))
+                              alu=dict(frac=round(alu_frac, 4), lane_slots_per_elem_state=SLOTS_PER_ELEM_STATE)),
+                **variants)
 
 
 def sweep_seqlen(dev, steps, warmup, lengths):
