@@ -1561,6 +1561,12 @@ __global__ __launch_bounds__(64 * S) void scan_bwd_kernel(BwdArgs a) {
   bool tact[EPL];
   uint32_t toff[EPL];
   float tbias[EPL], tD[EPL], dD_acc[EPL], dbias_acc[EPL];
+  // du, dDelta and dz of the last kHold steps, held until the group of steps
+  // that fills a 128-byte line of a row is complete (8 steps of bf16, 4 of
+  // fp32; the zero-order-hold and complex variants, short of registers,
+  // store every step).
+  constexpr int kHold = (kZoh || kCplx) ? 1 : 128 / (kChunk * (int)sizeof(IoT));
+  float hdu[EPL][kHold] = {}, hdd[EPL][kHold] = {}, hdz[EPL][kZ ? kHold : 1] = {};
 #pragma unroll
   for (int e = 0; e < EPL; ++e) {
     tc[e] = (w % TW) * (8 * EPL) + 8 * e + (lane >> 3);
@@ -1672,14 +1678,45 @@ __global__ __launch_bounds__(64 * S) void scan_bwd_kernel(BwdArgs a) {
       const float dstep = kZoh ? acc.x : __builtin_fmaf(q[e].u, acc.y, acc.x);
       const float duv = kZoh ? __builtin_fmaf(q[e].g, tD[e], acc.y) : __builtin_fmaf(q[e].dl, acc.y, q[e].g * tD[e]);
       const float ddv = dstep * q[e].sgd;
-      dbias_acc[e] += ddv;
-      if (tact[e]) {
-        const uint32_t o = toff[e] + (uint32_t)(s * kChunk * (int64_t)sizeof(IoT));
-        Io<IoT>::store1(reinterpret_cast<IoT*>(dup + o), duv);
-        Io<IoT>::store1(reinterpret_cast<IoT*>(ddp + o), ddv);
-        if (kZ && dzp)
-          Io<IoT>::store1(reinterpret_cast<IoT*>(dzp + o),
-                          __builtin_fmaf(tD[e], q[e].u, kCplx ? 2.0f * sv : sv) * q[e].kz);
+      // An explicit FMA: the compiler's own choice would hang on ddv's other uses.
+      dbias_acc[e] = __builtin_fmaf(dstep, q[e].sgd, dbias_acc[e]);
+      const float dzv = (kZ && dzp) ? __builtin_fmaf(tD[e], q[e].u, kCplx ? 2.0f * sv : sv) * q[e].kz : 0.0f;
+      if constexpr (kHold == 1) {
+        if (tact[e]) {
+          const uint32_t o = toff[e] + (uint32_t)(s * kChunk * (int64_t)sizeof(IoT));
+          Io<IoT>::store1(reinterpret_cast<IoT*>(dup + o), duv);
+          Io<IoT>::store1(reinterpret_cast<IoT*>(ddp + o), ddv);
+          if (kZ && dzp) Io<IoT>::store1(reinterpret_cast<IoT*>(dzp + o), dzv);
+        }
+      } else {
+        const int slot = (int)(s & (kHold - 1));
+#pragma unroll
+        for (int k = 0; k < kHold; ++k) {
+          hdu[e][k] = k == slot ? duv : hdu[e][k];
+          hdd[e][k] = k == slot ? ddv : hdd[e][k];
+          if constexpr (kZ) hdz[e][k] = k == slot ? dzv : hdz[e][k];
+        }
+      }
+    }
+    // Steps s .. s + kHold - 1 are complete once step s (slot 0) is: their
+    // stores go out together, so L2 merges each line's pieces before it can
+    // be evicted.
+    if constexpr (kHold > 1) {
+      if ((s & (kHold - 1)) == 0) {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+          if (!tact[e]) continue;
+#pragma unroll
+          for (int k = 0; k < kHold; ++k) {
+            if (s + k >= nsteps) break;
+            const uint32_t o = toff[e] + (uint32_t)((s + k) * kChunk * (int64_t)sizeof(IoT));
+            Io<IoT>::store1(reinterpret_cast<IoT*>(dup + o), hdu[e][k]);
+            Io<IoT>::store1(reinterpret_cast<IoT*>(ddp + o), hdd[e][k]);
+            if constexpr (kZ) {
+              if (dzp) Io<IoT>::store1(reinterpret_cast<IoT*>(dzp + o), hdz[e][k]);
+            }
+          }
+        }
       }
     }
   };
